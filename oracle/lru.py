@@ -1,0 +1,155 @@
+"""The shared expert-slot cache, one layer call at a time (oracle; test infrastructure).
+
+What the pages fix:
+* [FT] "语义感知专家缓存": one LRU residency space shared by every MoE layer;
+  a hit refreshes the expert's recency, a fill admits a newly chosen expert,
+  eviction takes the expert least recently needed.
+* [FT] "FTW 权重格式与平台适配" and [FTK] (two-level memory paragraph): an
+  expert's identity is the flat logical id l*E + e; one slot holds every
+  tensor of one (layer, expert).
+* [FT] "Device-side 缓存控制": per layer one pass does dedup of the routed
+  experts -> hit/miss against the residency table -> the fill count q from
+  the bandwidth ratio -> victim slots -> rewrite of each route to a physical
+  slot or to a "run on host" flag; victims are the K least recently used
+  slots found in one scan, of which the miss path takes the first q.
+* [FT] "q* 策略": fills F (|F| = q) enter the cache and run on the GPU; the
+  host set C runs from the host pool and leaves residency untouched; the
+  choice of F is left to the replacement policy.
+* [FT] "执行顺序与工程细节": GPU order is cache update, copy of F, grouped
+  evaluation of G = H u F.
+
+Readings adopted where the pages are silent (all listed in the design notes):
+* dedup order and the hit / miss lists are ascending logical id;
+* recency: one global tick per layer call; inside a call the touch order is
+  the hits (ascending id) then the fills (ascending id), stamped
+  (tick << 16) | (1 + rank); seeded slot i has stamp 1 + i, empty slots 0;
+* slots holding a hit of this call are never victims (their bytes are read
+  by the grouped evaluation after the copy), so q = min(q*, #non-hit slots);
+* victims: ascending (stamp, slot) among non-hit, non-reserved slots; F is
+  the first q misses by ascending id and fill i goes to victim i;
+* slots reserved by the prefill double buffer are outside the LRU.
+"""
+import numpy as np
+
+from .qsplit import q_star as _q_star
+
+EMPTY = -1
+RESERVED = -2
+
+
+class StepResult:
+    """Decisions of one layer call (plain lists / arrays, for comparison)."""
+
+    __slots__ = ("uniq", "is_hit", "q_star", "q", "fill_id", "fill_slot", "fill_evicted",
+                 "host_id", "pick_slot", "hits", "misses", "g_slots")
+
+    def __repr__(self):
+        return ("StepResult(u=%d, hits=%s, misses=%s, q*=%d, q=%d, fill=%s, host=%s)"
+                % (len(self.uniq), self.hits, self.misses, self.q_star, self.q,
+                   list(zip(self.fill_id, self.fill_slot, self.fill_evicted)), self.host_id))
+
+
+class ExpertCache:
+    def __init__(self, L: int, E: int, C: int, bp: int, bh: int):
+        if C <= 0 or L <= 0 or E <= 0:
+            raise ValueError("bad shape")
+        self.L, self.E, self.C, self.bp, self.bh = L, E, C, bp, bh
+        self.slot_id = [EMPTY] * C
+        self.ts = [0] * C
+        self.id_slot = [EMPTY] * (L * E)
+        self.tick = 1
+        # running counters: layer calls, unique, hits, misses, fills, host
+        self.counters = dict(calls=0, uniq=0, hits=0, misses=0, fills=0, host=0)
+
+    # -- set-up ---------------------------------------------------------------
+    def seed(self, ids):
+        """Slot i <- logical id ids[i], stamp 1 + i (older than any call)."""
+        for i, lid in enumerate(ids):
+            old = self.slot_id[i]
+            if old >= 0:
+                self.id_slot[old] = EMPTY
+            self.slot_id[i] = int(lid)
+            self.ts[i] = 1 + i
+            self.id_slot[int(lid)] = i
+
+    def reserve(self, first: int, count: int):
+        """Take slots [first, first+count) out of the LRU (prefill buffers)."""
+        for s in range(first, first + count):
+            old = self.slot_id[s]
+            if old >= 0:
+                self.id_slot[old] = EMPTY
+            self.slot_id[s] = RESERVED
+            self.ts[s] = 0
+
+    def release(self, first: int, count: int):
+        for s in range(first, first + count):
+            self.slot_id[s] = EMPTY
+            self.ts[s] = 0
+
+    # -- one layer call --------------------------------------------------------
+    def step(self, layer: int, ids, copy: bool = True) -> StepResult:
+        ids = np.asarray(ids, dtype=np.int64)
+        T, k = ids.shape
+        E = self.E
+        if ids.size and (ids.min() < 0 or ids.max() >= E):
+            raise ValueError("expert id out of range")
+        logical = layer * E + ids
+
+        uniq = sorted(set(int(v) for v in logical.reshape(-1)))
+        hits = [i for i in uniq if self.id_slot[i] >= 0]
+        misses = [i for i in uniq if self.id_slot[i] < 0]
+        m = len(misses)
+        qs = _q_star(m, self.bp, self.bh)
+
+        hit_slots = set(self.id_slot[i] for i in hits)
+        cand = [s for s in range(self.C) if s not in hit_slots and self.slot_id[s] != RESERVED]
+        cand.sort(key=lambda s: (self.ts[s], s))
+        q = min(qs, len(cand))
+        victims = cand[:q]
+        fills = misses[:q]
+        host = misses[q:]
+
+        evicted = []
+        for f, v in zip(fills, victims):
+            old = self.slot_id[v]
+            evicted.append(old)
+            if old >= 0:
+                self.id_slot[old] = EMPTY
+            self.slot_id[v] = f
+            self.id_slot[f] = v
+
+        for rank, lid in enumerate(hits + fills):
+            self.ts[self.id_slot[lid]] = (self.tick << 16) | (1 + rank)
+        self.tick += 1
+
+        gset = set(hits) | set(fills)
+        pick_slot = np.full((T, k), -1, np.int32)
+        for t in range(T):
+            for j in range(k):
+                lid = int(logical[t, j])
+                if lid in gset:
+                    pick_slot[t, j] = self.id_slot[lid]
+
+        c = self.counters
+        c["calls"] += 1
+        c["uniq"] += len(uniq)
+        c["hits"] += len(hits)
+        c["misses"] += m
+        c["fills"] += q
+        c["host"] += len(host)
+
+        r = StepResult()
+        r.uniq = uniq
+        r.is_hit = [1 if i in set(hits) else 0 for i in uniq]
+        r.q_star, r.q = qs, q
+        r.fill_id, r.fill_slot, r.fill_evicted = fills, victims, evicted
+        r.host_id = host
+        r.pick_slot = pick_slot
+        r.hits, r.misses = hits, misses
+        r.g_slots = [self.id_slot[i] for i in hits + fills]
+        return r
+
+    # -- views -----------------------------------------------------------------
+    def tables(self):
+        return (np.array(self.slot_id, np.int32), np.array(self.ts, np.uint64),
+                np.array(self.id_slot, np.int32), self.tick)
