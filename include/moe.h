@@ -1,0 +1,290 @@
+/*
+ * moe.h — C ABI of the MI355X (gfx950) routed-MoE-layer library with a shared
+ * expert-slot cache.
+ *
+ * Sources (cited by page title and section):
+ *   [FT]   "FreeToken 完全拆解" (pinghaoyang.com.cn/aigc/posts/freetoken/)
+ *   [FTK]  "개인 장치에서 MoE 모델을 서빙하는 FreeToken" (aitrends.kr/articles/99620)
+ *   [OSDI] "OSDI'26 | 双路 CPU + 两张 5090 ..." (marsggbo.github.io, 2026-07-23)
+ *
+ * Conventions for every call:
+ *   - Returns moe_status: MOE_OK (0) or a negative error.  Arguments are
+ *     validated on the host before anything is enqueued; on an error nothing
+ *     is enqueued.  moe_last_error() returns a message for the calling thread.
+ *   - Pointers named d_* / "device" are device memory (hipMalloc or torch
+ *     CUDA tensors) owned by the caller.  "host" pointers are ordinary host
+ *     memory.  "pinned" pointers are page-locked host memory from hipHostMalloc
+ *     (torch pin_memory); the library reads them from kernels and DMA.
+ *   - The caller owns every buffer, the pinned host pool and the streams.  The
+ *     library owns only its opaque handles (small host structs), and the
+ *     events of a prefill pool.  Device state of a cache lives in a caller
+ *     workspace whose size moe_cache_workspace_bytes() reports.
+ *   - Work is enqueued on the given stream, in stream order, and the calls
+ *     marked "capturable" neither allocate, synchronise the host nor copy
+ *     device data to the host, so they may be recorded into a hipGraph.
+ *   - BF16 values are passed as uint16_t bit patterns; FP8 values as uint8_t
+ *     OCP E4M3FN codes.
+ *   - A handle is used by one host thread and one stream at a time.
+ */
+#ifndef MOE_H_
+#define MOE_H_
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_ARG = -1,        /* null pointer, bad enum, misaligned pointer        */
+  MOE_ERR_SHAPE = -2,      /* a size outside the supported range                */
+  MOE_ERR_NO_SPACE = -3,   /* not enough slots / workspace                      */
+  MOE_ERR_NOT_PINNED = -4, /* a host-pool pointer is not device-accessible      */
+  MOE_ERR_HIP = -5,        /* a HIP runtime call failed (see moe_last_error)    */
+  MOE_ERR_STATE = -6,      /* call out of order (e.g. acquire before prefetch)  */
+  MOE_ERR_DEVICE = -7      /* a kernel flagged bad data (see moe_cache_error)   */
+} moe_status;
+
+/* Stored weight formats of one expert. */
+typedef enum {
+  MOE_W_BF16 = 0,          /* BF16 weights                                        */
+  MOE_W_FP8_B128 = 1       /* E4M3FN codes + one float32 scale per 128x128 tile   */
+} moe_wtype;
+
+/*
+ * Slot pool: every tensor of one (layer, expert) in one slot ([FT] section
+ * "全层双缓冲"; [FTK] paragraph on the elastic expert cache).  One bank per
+ * tensor, slot-major, matrices stored [out, in] row-major:
+ *   w_gate, w_up : [n_slots][I][H]   (uint16 BF16 or uint8 E4M3)
+ *   w_down       : [n_slots][H][I]
+ *   s_gate, s_up : [n_slots][I/128][H/128] float32   (FP8 only, else NULL)
+ *   s_down       : [n_slots][H/128][I/128] float32   (FP8 only, else NULL)
+ * All bases 16-byte aligned.  A view of slots [a, a+n) is the same struct with
+ * every base advanced by a slots and n_slots = n.
+ */
+typedef struct moe_slots {
+  int32_t wtype;           /* moe_wtype */
+  int32_t H, I;            /* hidden and SwiGLU intermediate sizes */
+  int32_t n_slots;
+  void* w_gate;
+  void* w_up;
+  void* w_down;
+  float* s_gate;
+  float* s_up;
+  float* s_down;
+} moe_slots;
+
+/*
+ * Host expert pool: the ground truth of every routed expert, addressed by
+ * logical id l*E + e ([FT] section "FTW 权重格式与平台适配": banks keyed by
+ * lE+e, the rows of one id across banks form one expert).  Each field is a
+ * HOST array of L*E pointers into PINNED host memory, one per logical id
+ * (aliasing allowed: several ids may point at the same bytes).  Scale tables
+ * are NULL for BF16.  The arrays are copied at moe_cache_create; the pinned
+ * memory they point to must outlive the cache.
+ */
+typedef struct moe_host_pool {
+  const void* const* w_gate;
+  const void* const* w_up;
+  const void* const* w_down;
+  const float* const* s_gate;
+  const float* const* s_up;
+  const float* const* s_down;
+} moe_host_pool;
+
+typedef struct moe_cache_cfg {
+  int32_t L;               /* MoE layers sharing the cache                       */
+  int32_t E;               /* routed experts per layer (<= 4096)                 */
+  int32_t k;               /* picks per token                                    */
+  int32_t T_max;           /* max tokens per moe_cache_step call (T_max*k<=1024) */
+  int32_t C;               /* cache slots (<= 16384, == slots->n_slots)          */
+  uint32_t bp, bh;         /* B_P and B_H in one unit (e.g. 0.1 GB/s); bh > 0    */
+} moe_cache_cfg;
+
+typedef struct moe_cache* moe_cache_t;
+typedef struct moe_prefill* moe_prefill_t;
+
+/* Indices into moe_step_out.counts. */
+enum {
+  MOE_CNT_UNIQ = 0,        /* u: distinct logical ids routed this call            */
+  MOE_CNT_HIT = 1,         /* h                                                   */
+  MOE_CNT_MISS = 2,        /* m                                                   */
+  MOE_CNT_QSTAR = 3,       /* q*: the split's fill count before the victim clamp  */
+  MOE_CNT_FILL = 4,        /* q = min(q*, free victims): valid entries of fill_*  */
+  MOE_CNT_HOST = 5,        /* m - q: valid entries of host_id                     */
+  MOE_CNT_N = 8
+};
+
+/*
+ * Fixed-shape outputs of one cache step, all DEVICE arrays owned by the
+ * caller ([FT] section "Device-side 缓存控制": fixed-shape work buffers plus a
+ * device-resident valid count).  U_max = min(T_max*k, E).  Entries past the
+ * valid count are written -1.
+ */
+typedef struct moe_step_out {
+  int32_t* pick_slot;      /* [T_max*k] slot of each pick, or -1 = host set       */
+  int32_t* uniq;           /* [U_max] distinct logical ids, ascending             */
+  int32_t* is_hit;         /* [U_max] 1 if uniq[i] was resident                   */
+  int32_t* fill_id;        /* [U_max] logical ids filled, ascending               */
+  int32_t* fill_slot;      /* [U_max] their victim slots                          */
+  int32_t* fill_evicted;   /* [U_max] id evicted from that slot, -1 if empty      */
+  int32_t* host_id;        /* [U_max] logical ids left to the host, ascending     */
+  int32_t* counts;         /* [MOE_CNT_N]                                         */
+} moe_step_out;
+
+#define MOE_STEP_NO_COPY 1u   /* decisions and tables only; skip the fill copy  */
+
+#define MOE_FWD_DECODE 0u     /* grouped GEMV, T <= 16                           */
+#define MOE_FWD_PREFILL 1u    /* sorted grouped GEMM on MFMA                     */
+
+/* Message of the last failed call on this thread ("" if none). */
+const char* moe_last_error(void);
+
+/*
+ * Top-k router ([FTK] paragraphs on MoE routing and the GPU router).
+ * logits: device float32 [T, E]; ids: device int32 [T, k]; w: device float32
+ * [T, k].  Per token, experts are ranked by logit descending, ties to the
+ * lower index; ids are written in rank order and w = softmax over the k kept
+ * logits.  1 <= k <= min(E, 32), 1 <= E <= 1024, T >= 0.  Capturable.
+ */
+moe_status moe_route_topk(const float* logits, int32_t T, int32_t E, int32_t k,
+                          int32_t* ids, float* w, hipStream_t stream);
+
+/* Bytes of device workspace a cache with this configuration needs. */
+moe_status moe_cache_workspace_bytes(const moe_cache_cfg* cfg, size_t* bytes);
+
+/*
+ * Create a cache over `slots` (which must have n_slots == cfg->C) and the host
+ * pool `host` (L*E ids).  dev_ws: device workspace of at least
+ * moe_cache_workspace_bytes, 256-byte aligned, owned by the caller and kept
+ * alive until moe_cache_destroy.  Every host-pool pointer is checked to be
+ * pinned and device-accessible (else MOE_ERR_NOT_PINNED).  Initialises the
+ * tables to empty on `stream` (not capturable).
+ */
+moe_status moe_cache_create(const moe_cache_cfg* cfg, const moe_slots* slots,
+                            const moe_host_pool* host, void* dev_ws, size_t ws_bytes,
+                            hipStream_t stream, moe_cache_t* out);
+
+/*
+ * Reset the cache to empty, then place logical id host_ids[i] in slot i with
+ * recency older than any step (stamp 1 + i), copying its bytes from the host
+ * pool unless flags has MOE_STEP_NO_COPY.  host_ids: host array of n distinct
+ * ids, n <= C.  Not capturable.
+ */
+moe_status moe_cache_seed(moe_cache_t c, const int32_t* host_ids, int32_t n,
+                          uint32_t flags, hipStream_t stream);
+
+/*
+ * One layer call of the cache ([FT] sections "Device-side 缓存控制", "q* 策略",
+ * "语义感知专家缓存"; [FTK] decode and dynamic-LRU paragraphs).  One kernel:
+ * dedup of the routed experts -> hit/miss against the residency table ->
+ * q* = clamp(round(m*bp/bh), 1, m) -> one scan selecting the least recently
+ * used non-hit slots -> table update and recency stamps -> rewrite of every
+ * pick to its slot or -1 (host set).  Then, unless MOE_STEP_NO_COPY, one
+ * fixed-grid copy kernel moves every bank of each filled expert from the
+ * pinned host pool into its slot, masked by the device fill count ([FT]
+ * section "Device-side 缓存控制": one fused transfer over all banks).
+ * ids: device int32 [T, k] expert indices of `layer` (0 <= layer < L).
+ * 1 <= T <= T_max.  An id outside [0, E) sets the cache's device error word
+ * and is treated as routed to the host.  Capturable.
+ */
+moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t* ids, int32_t T,
+                          uint32_t flags, const moe_step_out* out, hipStream_t stream);
+
+/*
+ * Copy the residency tables to HOST arrays (any pointer may be NULL):
+ * slot_id [C] (-1 empty, -2 reserved by a prefill pool), stamp [C] (0 empty,
+ * (tick << 16) | (1 + rank) otherwise), id_slot [L*E], tick, and counters[6] =
+ * calls, uniq, hits, misses, fills, host summed over all steps.  Synchronises
+ * `stream`; not capturable.
+ */
+moe_status moe_cache_read_state(moe_cache_t c, int32_t* slot_id, uint64_t* stamp,
+                                int32_t* id_slot, uint64_t* tick, uint64_t* counters,
+                                hipStream_t stream);
+
+/* Read and clear the device error word (0 = none).  Synchronises; not capturable. */
+moe_status moe_cache_error(moe_cache_t c, int32_t* code, hipStream_t stream);
+
+moe_status moe_cache_destroy(moe_cache_t c);
+
+/* Bytes of device workspace moe_expert_forward needs for these sizes. */
+moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int32_t H, int32_t I,
+                                       int32_t n_slots, uint32_t mode, size_t* bytes);
+
+/*
+ * Grouped SwiGLU expert evaluation of G = H u F ([FT] section "执行顺序与工程细节":
+ * grouped evaluation of the hits and fills; [OSDI] section 4.3 expert
+ * structure; [OSDI] section 4.2 FP8 expansion and post-scaling).
+ *   y[t] = sum over picks j with pick_slot[t,j] >= 0 of
+ *          w[t,j] * W_down (silu(W_gate x_t) * (W_up x_t))   (slot's weights)
+ * x: device BF16 [T, H]; pick_slot: device int32 [T, k] (slot index in
+ * `slots`, -1 = skip); w: device float32 [T, k]; y: device float32 [T, H],
+ * fully overwritten.  FP8 weights are expanded to BF16 in registers by
+ * integer bit operations (exact for all 256 codes) and each 128x128 tile's
+ * scale is applied once to its block partial sum.  Accumulation is FP32; the
+ * SwiGLU activations h are rounded to BF16 before the down projection.
+ *   mode MOE_FWD_DECODE: T <= 16 (grouped GEMV streaming each slot once).
+ *   mode MOE_FWD_PREFILL: any T (tokens sorted by slot, grouped GEMM).
+ * ws: device workspace of moe_forward_workspace_bytes(T_max >= T, ...).
+ * Requires H, I multiples of 128 (FP8) or of 32 (BF16).  Capturable.
+ */
+moe_status moe_expert_forward(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,
+                              const float* w, int32_t T, int32_t k, float* y,
+                              void* ws, size_t ws_bytes, uint32_t mode, hipStream_t stream);
+
+/*
+ * Merge of the GPU and host partial sums ([FT] section "q* 策略": the two
+ * partial sums are combined exactly; [FT] "Graph 内的 CPU 执行分支").
+ * y_out[i] = y_gpu[i] + y_host[i] over T*H floats; if y_out_bf16 != NULL it
+ * also receives the BF16 (round-to-nearest-even) of y_out.  y_host may be
+ * device memory or pinned host memory.  y_out may alias y_gpu.  Capturable.
+ */
+moe_status moe_merge_partial(const float* y_gpu, const float* y_host, int32_t T, int32_t H,
+                             float* y_out, uint16_t* y_out_bf16, hipStream_t stream);
+
+/*
+ * Full-layer double buffer for prefill ([FT] section "全层双缓冲"; [FTK]
+ * prefill paragraph).  Reserves the last 2E slots of the cache's pool as two
+ * full-layer buffers (evicting what they held; they leave the LRU), else
+ * MOE_ERR_NO_SPACE.  Layer l uses buffer l % 2.
+ */
+moe_status moe_prefill_create(moe_cache_t c, moe_prefill_t* out);
+
+/*
+ * Enqueue on copy_stream: wait until buffer (layer % 2) is released, copy ALL
+ * E experts of `layer` (every bank) from the pinned host pool into it
+ * (without waiting for routing), then mark it ready.
+ */
+moe_status moe_prefill_prefetch(moe_prefill_t p, int32_t layer, hipStream_t copy_stream);
+
+/*
+ * Make `compute` wait until layer's buffer is ready and return its view: a
+ * moe_slots of E slots whose slot e holds expert e of `layer` (pick_slot in
+ * prefill mode is then the expert index).  MOE_ERR_STATE if `layer` was not
+ * prefetched into that buffer.
+ */
+moe_status moe_prefill_acquire(moe_prefill_t p, int32_t layer, hipStream_t compute,
+                               moe_slots* view);
+
+/* Record on `compute` that layer's buffer may be overwritten by a later prefetch. */
+moe_status moe_prefill_release(moe_prefill_t p, int32_t layer, hipStream_t compute);
+
+/* Return the 2E slots to the LRU as empty slots and free the events. */
+moe_status moe_prefill_destroy(moe_prefill_t p, hipStream_t stream);
+
+
+/*
+ * Expand n E4M3FN codes to BF16 bit patterns with the exact integer routine
+ * the FP8 kernels use ([OSDI] section 4.2: exponent moved by the bias
+ * difference 120, mantissa zero-filled; zero, subnormal and NaN codes
+ * patched).  codes: device uint8 [n]; out: device uint16 [n].  Capturable.
+ */
+moe_status moe_e4m3_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_H_ */

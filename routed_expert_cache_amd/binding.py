@@ -1,0 +1,290 @@
+"""ctypes binding of libmoe_gfx950.so (argument marshalling only).
+
+Every step of the layer runs in the library's HIP kernels; torch is used here
+only to allocate device / pinned memory and to name the current stream.  If
+the shared library is missing this module raises at import: there is no
+fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_gfx950.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError("routed_expert_cache_amd: %s is not built; run "
+                      "`python -m routed_expert_cache_amd.build` (hipcc, gfx950)" % LIB_PATH)
+_lib = ctypes.CDLL(LIB_PATH)
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_NO_SPACE",
+          -4: "MOE_ERR_NOT_PINNED", -5: "MOE_ERR_HIP", -6: "MOE_ERR_STATE", -7: "MOE_ERR_DEVICE"}
+W_BF16, W_FP8_B128 = 0, 1
+STEP_NO_COPY = 1
+FWD_DECODE, FWD_PREFILL = 0, 1
+CNT_UNIQ, CNT_HIT, CNT_MISS, CNT_QSTAR, CNT_FILL, CNT_HOST, CNT_N = 0, 1, 2, 3, 4, 5, 8
+
+EXPORTS = [
+    "moe_last_error", "moe_route_topk", "moe_cache_workspace_bytes", "moe_cache_create",
+    "moe_cache_seed", "moe_cache_step", "moe_cache_read_state", "moe_cache_error",
+    "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_merge_partial",
+    "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
+    "moe_prefill_destroy", "moe_e4m3_to_bf16",
+]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        msg = _lib.moe_last_error().decode(errors="replace")
+        super().__init__("%s: %s (%d) %s" % (where, STATUS.get(status, "?"), status, msg))
+
+
+class Slots(ctypes.Structure):
+    _fields_ = [("wtype", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
+                ("n_slots", ctypes.c_int32),
+                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
+
+
+class HostPool(ctypes.Structure):
+    _fields_ = [(n, ctypes.POINTER(ctypes.c_void_p)) for n in
+                ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")]
+
+
+class CacheCfg(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int32), ("E", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("T_max", ctypes.c_int32), ("C", ctypes.c_int32),
+                ("bp", ctypes.c_uint32), ("bh", ctypes.c_uint32)]
+
+
+class StepOutC(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in
+                ("pick_slot", "uniq", "is_hit", "fill_id", "fill_slot", "fill_evicted", "host_id", "counts")]
+
+
+_vp, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
+_P = ctypes.POINTER
+_sig = {
+    "moe_last_error": (ctypes.c_char_p, []),
+    "moe_route_topk": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
+    "moe_cache_workspace_bytes": (_i32, [_P(CacheCfg), _P(_sz)]),
+    "moe_cache_create": (_i32, [_P(CacheCfg), _P(Slots), _P(HostPool), _vp, _sz, _vp, _P(_vp)]),
+    "moe_cache_seed": (_i32, [_vp, _P(_i32), _i32, _u32, _vp]),
+    "moe_cache_step": (_i32, [_vp, _i32, _vp, _i32, _u32, _P(StepOutC), _vp]),
+    "moe_cache_read_state": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_cache_error": (_i32, [_vp, _P(_i32), _vp]),
+    "moe_cache_destroy": (_i32, [_vp]),
+    "moe_forward_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, _u32, _P(_sz)]),
+    "moe_expert_forward": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _u32, _vp]),
+    "moe_merge_partial": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "moe_prefill_create": (_i32, [_vp, _P(_vp)]),
+    "moe_prefill_prefetch": (_i32, [_vp, _i32, _vp]),
+    "moe_prefill_acquire": (_i32, [_vp, _i32, _vp, _P(Slots)]),
+    "moe_prefill_release": (_i32, [_vp, _i32, _vp]),
+    "moe_prefill_destroy": (_i32, [_vp, _vp]),
+    "moe_e4m3_to_bf16": (_i32, [_vp, _vp, ctypes.c_int64, _vp]),
+}
+for _name, (_res, _args) in _sig.items():
+    _f = getattr(_lib, _name)
+    _f.restype, _f.argtypes = _res, _args
+
+
+def _check(st, where):
+    if st != MOE_OK:
+        raise MoeError(st, where)
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+# ---------------------------------------------------------------- router
+def route_topk(logits, k, ids=None, w=None, stream=None):
+    """logits float32 [T, E] (cuda) -> (ids int32 [T, k], w float32 [T, k])."""
+    assert logits.is_cuda and logits.dtype == torch.float32 and logits.is_contiguous()
+    T, E = logits.shape
+    if ids is None:
+        ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
+    if w is None:
+        w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
+    _check(_lib.moe_route_topk(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream)), "moe_route_topk")
+    return ids, w
+
+
+# ---------------------------------------------------------------- slot pools
+class SlotPool:
+    """Device banks of n_slots experts (torch tensors) and their moe_slots view."""
+
+    def __init__(self, n_slots, H, I, wtype=W_BF16, device="cuda"):
+        self.n_slots, self.H, self.I, self.wtype = n_slots, H, I, wtype
+        dt = torch.uint16 if wtype == W_BF16 else torch.uint8
+        self.w_gate = torch.empty((n_slots, I, H), dtype=dt, device=device)
+        self.w_up = torch.empty((n_slots, I, H), dtype=dt, device=device)
+        self.w_down = torch.empty((n_slots, H, I), dtype=dt, device=device)
+        if wtype == W_FP8_B128:
+            self.s_gate = torch.empty((n_slots, I // 128, H // 128), dtype=torch.float32, device=device)
+            self.s_up = torch.empty((n_slots, I // 128, H // 128), dtype=torch.float32, device=device)
+            self.s_down = torch.empty((n_slots, H // 128, I // 128), dtype=torch.float32, device=device)
+        else:
+            self.s_gate = self.s_up = self.s_down = None
+        self.c = Slots(wtype, H, I, n_slots, *[None if t is None else t.data_ptr() for t in
+                                                (self.w_gate, self.w_up, self.w_down,
+                                                 self.s_gate, self.s_up, self.s_down)])
+
+    def banks(self):
+        out = [self.w_gate, self.w_up, self.w_down]
+        if self.wtype == W_FP8_B128:
+            out += [self.s_gate, self.s_up, self.s_down]
+        return out
+
+
+class HostPoolTables:
+    """Per-logical-id pointers into pinned host tensors (aliasing allowed).
+
+    `banks` is a list (gate, up, down[, s_gate, s_up, s_down]) of pinned host
+    tensors whose first dim indexes *base* experts; `base_of` maps a logical
+    id to its base expert row."""
+
+    def __init__(self, banks, base_of, n_ids):
+        self.banks = banks
+        self._arrays = []
+        ptrs = []
+        for t in banks:
+            assert t.is_pinned(), "host pool banks must be pinned"
+            row = t[0].numel() * t.element_size()
+            arr = (ctypes.c_void_p * n_ids)(*[t.data_ptr() + int(base_of(i)) * row for i in range(n_ids)])
+            self._arrays.append(arr)
+            ptrs.append(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)))
+        while len(ptrs) < 6:
+            ptrs.append(None)
+        self.c = HostPool(*ptrs)
+
+
+class StepOut:
+    """Fixed-shape device outputs of one cache step."""
+
+    def __init__(self, T_max, k, E, device="cuda"):
+        self.U_max = min(T_max * k, E)
+        mk = lambda n: torch.full((n,), -1, dtype=torch.int32, device=device)
+        self.pick_slot = mk(T_max * k)
+        self.uniq, self.is_hit = mk(self.U_max), mk(self.U_max)
+        self.fill_id, self.fill_slot, self.fill_evicted = mk(self.U_max), mk(self.U_max), mk(self.U_max)
+        self.host_id = mk(self.U_max)
+        self.counts = torch.zeros((CNT_N,), dtype=torch.int32, device=device)
+        self.c = StepOutC(*[t.data_ptr() for t in (self.pick_slot, self.uniq, self.is_hit, self.fill_id,
+                                                   self.fill_slot, self.fill_evicted, self.host_id, self.counts)])
+
+
+class Cache:
+    """The shared LRU expert-slot cache (device tables in a torch workspace)."""
+
+    def __init__(self, L, E, k, T_max, slots: SlotPool, host: HostPoolTables, bp, bh, stream=None):
+        self.cfg = CacheCfg(L, E, k, T_max, slots.n_slots, bp, bh)
+        nbytes = ctypes.c_size_t(0)
+        _check(_lib.moe_cache_workspace_bytes(ctypes.byref(self.cfg), ctypes.byref(nbytes)), "workspace_bytes")
+        self.ws = torch.empty((nbytes.value,), dtype=torch.uint8, device="cuda")
+        self.slots, self.host = slots, host
+        h = ctypes.c_void_p()
+        _check(_lib.moe_cache_create(ctypes.byref(self.cfg), ctypes.byref(slots.c), ctypes.byref(host.c),
+                                     _ptr(self.ws), nbytes.value, _stream(stream), ctypes.byref(h)),
+               "moe_cache_create")
+        self.h = h
+
+    def seed(self, ids, copy=True, stream=None):
+        arr = (ctypes.c_int32 * max(1, len(ids)))(*[int(i) for i in ids])
+        _check(_lib.moe_cache_seed(self.h, arr, len(ids), 0 if copy else STEP_NO_COPY, _stream(stream)),
+               "moe_cache_seed")
+
+    def step(self, layer, ids, out: StepOut, copy=True, stream=None):
+        T = ids.shape[0]
+        _check(_lib.moe_cache_step(self.h, layer, _ptr(ids), T, 0 if copy else STEP_NO_COPY,
+                                   ctypes.byref(out.c), _stream(stream)), "moe_cache_step")
+
+    def read_state(self, stream=None):
+        import numpy as np
+        C, LE = self.cfg.C, self.cfg.L * self.cfg.E
+        slot_id = np.empty(C, np.int32)
+        stamp = np.empty(C, np.uint64)
+        id_slot = np.empty(LE, np.int32)
+        tick = np.empty(1, np.uint64)
+        counters = np.empty(6, np.uint64)
+        _check(_lib.moe_cache_read_state(self.h, slot_id.ctypes.data, stamp.ctypes.data, id_slot.ctypes.data,
+                                         tick.ctypes.data, counters.ctypes.data, _stream(stream)), "read_state")
+        return slot_id, stamp, id_slot, int(tick[0]), counters
+
+    def error(self, stream=None):
+        code = ctypes.c_int32(0)
+        _check(_lib.moe_cache_error(self.h, ctypes.byref(code), _stream(stream)), "moe_cache_error")
+        return code.value
+
+    def destroy(self):
+        if self.h:
+            _check(_lib.moe_cache_destroy(self.h), "moe_cache_destroy")
+            self.h = None
+
+
+# ---------------------------------------------------------------- forward / merge
+def forward_workspace(T_max, k, H, I, n_slots, mode, device="cuda"):
+    n = ctypes.c_size_t(0)
+    _check(_lib.moe_forward_workspace_bytes(T_max, k, H, I, n_slots, mode, ctypes.byref(n)),
+           "moe_forward_workspace_bytes")
+    return torch.empty((max(n.value, 256),), dtype=torch.uint8, device=device)
+
+
+def expert_forward(slots_c, x, pick_slot, w, mode, ws, y=None, stream=None):
+    """slots_c: Slots struct; x uint16 [T, H]; pick_slot int32 [T, k]; w float32 [T, k]."""
+    T, k = pick_slot.shape
+    if y is None:
+        y = torch.empty((T, slots_c.H), dtype=torch.float32, device=x.device)
+    _check(_lib.moe_expert_forward(ctypes.byref(slots_c), _ptr(x), _ptr(pick_slot), _ptr(w), T, k, _ptr(y),
+                                   _ptr(ws), ws.numel(), mode, _stream(stream)), "moe_expert_forward")
+    return y
+
+
+def merge_partial(y_gpu, y_host, y_out=None, y_out_bf16=None, stream=None):
+    T, H = y_gpu.shape
+    if y_out is None:
+        y_out = torch.empty_like(y_gpu)
+    _check(_lib.moe_merge_partial(_ptr(y_gpu), _ptr(y_host), T, H, _ptr(y_out), _ptr(y_out_bf16),
+                                  _stream(stream)), "moe_merge_partial")
+    return y_out
+
+
+def e4m3_to_bf16(codes, out=None, stream=None):
+    """Exact expansion of E4M3FN codes (uint8, cuda) to BF16 bits with the kernels' routine."""
+    if out is None:
+        out = torch.empty(codes.shape, dtype=torch.uint16, device=codes.device)
+    _check(_lib.moe_e4m3_to_bf16(_ptr(codes), _ptr(out), codes.numel(), _stream(stream)), "moe_e4m3_to_bf16")
+    return out
+
+
+# ---------------------------------------------------------------- prefill double buffer
+class PrefillPool:
+    def __init__(self, cache: Cache):
+        h = ctypes.c_void_p()
+        _check(_lib.moe_prefill_create(cache.h, ctypes.byref(h)), "moe_prefill_create")
+        self.h, self.cache = h, cache
+
+    def prefetch(self, layer, copy_stream):
+        _check(_lib.moe_prefill_prefetch(self.h, layer, _stream(copy_stream)), "moe_prefill_prefetch")
+
+    def acquire(self, layer, compute=None):
+        v = Slots()
+        _check(_lib.moe_prefill_acquire(self.h, layer, _stream(compute), ctypes.byref(v)), "moe_prefill_acquire")
+        return v
+
+    def release(self, layer, compute=None):
+        _check(_lib.moe_prefill_release(self.h, layer, _stream(compute)), "moe_prefill_release")
+
+    def destroy(self, stream=None):
+        if self.h:
+            _check(_lib.moe_prefill_destroy(self.h, _stream(stream)), "moe_prefill_destroy")
+            self.h = None

@@ -22,3 +22,17 @@ def golden(name):
 @pytest.fixture
 def golden_loader():
     return golden
+
+
+def pytest_collection_modifyitems(config, items):
+    try:
+        import torch
+        has_gpu = torch.cuda.is_available()
+    except Exception:
+        has_gpu = False
+    if has_gpu:
+        return
+    skip = pytest.mark.skip(reason="needs a GPU")
+    for it in items:
+        if "gpu" in it.keywords:
+            it.add_marker(skip)

@@ -1,0 +1,254 @@
+"""GPU parity of the grouped expert evaluation and the merge against the
+float64 oracle: rel-L2 <= 5e-3 and max-abs <= 2e-2 max|ref| on the layer
+outputs, at sizes spanning several tiles with ragged tails and at the
+workloads' full shapes (sampled tokens where the oracle is slow)."""
+import numpy as np
+import pytest
+import torch
+
+from harness import gen, CONFIGS
+from oracle import route, lru, numerics, ffn
+from tests.layer_setup import binding, dev, pinned, check_layer, Bf16Bank, Fp8Bank, oracle_partials
+
+pytestmark = pytest.mark.gpu
+
+
+def _slots_identity(b, bank, wtype):
+    pool = b.SlotPool(bank.E, bank.H, bank.I, wtype)
+    bank.load_slots(pool, {e: e for e in range(bank.E)})
+    return pool
+
+
+def _run_forward(b, pool, x_bits, pick_slot, w, mode, T_max=None):
+    T, k = pick_slot.shape
+    ws = b.forward_workspace(T_max or T, k, pool.H, pool.I, pool.n_slots, mode)
+    y = b.expert_forward(pool.c, dev(x_bits), dev(pick_slot.astype(np.int32)), dev(w.astype(np.float32)), mode, ws)
+    torch.cuda.synchronize()
+    return y.cpu().numpy()
+
+
+# ---------------------------------------------------------------- decode, BF16
+@pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 128), (3, 8, 2, 256, 128), (16, 32, 4, 512, 256),
+                                       (1, 128, 8, 2048, 768), (5, 24, 8, 1024, 384)])
+def test_decode_bf16(T, E, k, H, I):
+    b = binding()
+    bank = Bf16Bank(90 + T, E, H, I)
+    pool = _slots_identity(b, bank, b.W_BF16)
+    rng = np.random.default_rng(T + E)
+    x = gen.activations_bf16(rng, T, H)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    ids, w = route.topk_softmax(lg, k)
+    pick = ids.copy()
+    on_gpu = rng.random(ids.shape) < 0.75
+    pick[~on_gpu] = -1                                   # some picks to the host set
+    y = _run_forward(b, pool, x, pick, w, b.FWD_DECODE)
+    yg, _ = oracle_partials(x, ids, w, bank.expert64, on_gpu)
+    check_layer(y, yg, "decode bf16")
+
+
+def test_decode_shared_slots_across_tokens():
+    """Several tokens routed to the same slots: each slot streamed once."""
+    b = binding()
+    bank = Bf16Bank(77, 4, 256, 128)
+    pool = _slots_identity(b, bank, b.W_BF16)
+    T, k = 16, 2
+    ids = np.array([[t % 4, (t + 1) % 4] for t in range(T)])
+    w = np.full((T, k), 0.5)
+    x = gen.activations_bf16(np.random.default_rng(0), T, 256)
+    y = _run_forward(b, pool, x, ids, w, b.FWD_DECODE)
+    yg, _ = oracle_partials(x, ids, w, bank.expert64, np.ones(ids.shape, bool))
+    check_layer(y, yg)
+
+
+def test_decode_all_host_gives_zero():
+    b = binding()
+    bank = Bf16Bank(78, 4, 256, 128)
+    pool = _slots_identity(b, bank, b.W_BF16)
+    x = gen.activations_bf16(np.random.default_rng(1), 2, 256)
+    y = _run_forward(b, pool, x, np.full((2, 2), -1), np.full((2, 2), 0.5), b.FWD_DECODE)
+    assert np.all(y == 0)
+
+
+# ---------------------------------------------------------------- decode, FP8
+@pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 256), (4, 16, 4, 512, 384), (16, 24, 8, 1024, 256)])
+def test_decode_fp8(T, E, k, H, I):
+    b = binding()
+    bank = Fp8Bank(60 + T, E, H, I)
+    pool = _slots_identity(b, bank, b.W_FP8_B128)
+    rng = np.random.default_rng(5 * T)
+    x = gen.activations_bf16(rng, T, H)
+    ids, w = route.topk_softmax(rng.standard_normal((T, E)).astype(np.float32), k)
+    y = _run_forward(b, pool, x, ids, w, b.FWD_DECODE)
+    yg, _ = oracle_partials(x, ids, w, bank.expert64, np.ones(ids.shape, bool))
+    check_layer(y, yg, "decode fp8")
+
+
+def test_decode_fp8_special_codes():
+    """Subnormal, zero and sign codes in the weights decode exactly."""
+    b = binding()
+    bank = Fp8Bank(61, 2, 256, 128)
+    rng = np.random.default_rng(9)
+    for n in ("gate", "up", "down"):
+        t = bank.t[n]
+        mask = torch.from_numpy(rng.random(t.shape) < 0.2)
+        sub = torch.from_numpy(rng.integers(0, 8, t.shape).astype(np.uint8) | (rng.integers(0, 2, t.shape).astype(np.uint8) << 7))
+        t[mask] = sub[mask]
+    pool = _slots_identity(b, bank, b.W_FP8_B128)
+    x = gen.activations_bf16(rng, 3, 256)
+    ids = np.array([[0, 1]] * 3)
+    w = np.array([[0.7, 0.3]] * 3)
+    y = _run_forward(b, pool, x, ids, w, b.FWD_DECODE)
+    yg, _ = oracle_partials(x, ids, w, bank.expert64, np.ones(ids.shape, bool))
+    check_layer(y, yg)
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_decode_fp8_full_shape(T):
+    """Decode FP8 workload shape (H 7168, I 2048, top-8), sampled tokens."""
+    b = binding()
+    c = CONFIGS["decode_fp8"]
+    E = min(c.E, T * c.k)                               # only the routed experts need slots
+    bank = Fp8Bank(c.cfg_id, E, c.H, c.I, layer=T, device="cuda")
+    pool = _slots_identity(b, bank, b.W_FP8_B128)
+    rng = np.random.default_rng(100 + T)
+    x = gen.activations_bf16(rng, T, c.H)
+    ids = np.stack([rng.choice(E, size=c.k, replace=False) for _ in range(T)])
+    w = np.exp(rng.standard_normal((T, c.k)))
+    w /= w.sum(1, keepdims=True)
+    y = _run_forward(b, pool, x, ids, w, b.FWD_DECODE)
+    tok = [T - 1]                                       # last token (a ragged position)
+    yg, _ = oracle_partials(x[tok], ids[tok], w[tok], bank.expert64, np.ones((len(tok), c.k), bool))
+    check_layer(y[tok], yg, "decode fp8 full")
+
+
+# ---------------------------------------------------------------- prefill
+@pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 128), (300, 8, 2, 256, 128), (1000, 16, 4, 512, 192)])
+def test_prefill_bf16(T, E, k, H, I):
+    b = binding()
+    bank = Bf16Bank(50 + E, E, H, I)
+    pool = _slots_identity(b, bank, b.W_BF16)
+    rng = np.random.default_rng(T)
+    x = gen.activations_bf16(rng, T, H)
+    ids, w = route.topk_softmax(rng.standard_normal((T, E)).astype(np.float32), k)
+    y = _run_forward(b, pool, x, ids, w, b.FWD_PREFILL)
+    ref = ffn.moe_output(numerics.bf16_to_f64(x), ids, w, bank.expert64)
+    check_layer(y, ref, "prefill bf16")
+
+
+def test_prefill_bf16_skewed_segments():
+    """One expert gets most pairs (many tiles), one gets none."""
+    b = binding()
+    E, k, H, I, T = 6, 2, 256, 128, 700
+    bank = Bf16Bank(41, E, H, I)
+    pool = _slots_identity(b, bank, b.W_BF16)
+    rng = np.random.default_rng(2)
+    ids = np.stack([[0, 1 + (t % 4)] for t in range(T)])
+    w = rng.random((T, k))
+    x = gen.activations_bf16(rng, T, H)
+    y = _run_forward(b, pool, x, ids, w, b.FWD_PREFILL)
+    ref = ffn.moe_output(numerics.bf16_to_f64(x), ids, w, bank.expert64)
+    check_layer(y, ref)
+
+
+@pytest.mark.parametrize("T,E,k,H,I", [(130, 8, 2, 256, 128), (700, 16, 4, 512, 256)])
+def test_prefill_fp8(T, E, k, H, I):
+    b = binding()
+    bank = Fp8Bank(70 + E, E, H, I)
+    pool = _slots_identity(b, bank, b.W_FP8_B128)
+    rng = np.random.default_rng(T + 1)
+    x = gen.activations_bf16(rng, T, H)
+    ids, w = route.topk_softmax(rng.standard_normal((T, E)).astype(np.float32), k)
+    y = _run_forward(b, pool, x, ids, w, b.FWD_PREFILL)
+    ref = ffn.moe_output(numerics.bf16_to_f64(x), ids, w, bank.expert64)
+    check_layer(y, ref, "prefill fp8")
+
+
+def test_prefill_bf16_full_shape_sampled():
+    """Prefill BF16 workload (8192 tokens, H 2048, E 128, top-8, I 768), 64 sampled rows."""
+    b = binding()
+    c = CONFIGS["prefill_bf16"]
+    bank = Bf16Bank(c.cfg_id, c.E, c.H, c.I)
+    pool = _slots_identity(b, bank, b.W_BF16)
+    x = gen.activations_bf16(gen.np_rng(c.cfg_id, gen.S_ACT), c.T, c.H)
+    wr = gen.router_matrix(gen.np_rng(c.cfg_id, gen.S_ROUTER), c.H, c.E, c.router_std)
+    lg = gen.router_logits(x, wr)
+    ids_d, w_d = b.route_topk(dev(lg), c.k)
+    ids, w = route.topk_softmax(lg, c.k)
+    assert np.array_equal(ids_d.cpu().numpy(), ids)
+    ws = b.forward_workspace(c.T, c.k, c.H, c.I, c.E, b.FWD_PREFILL)
+    y = b.expert_forward(pool.c, dev(x), ids_d, w_d, b.FWD_PREFILL, ws).cpu().numpy()
+    rows = np.random.default_rng(0).choice(c.T, 64, replace=False)
+    ref = ffn.moe_output(numerics.bf16_to_f64(x[rows]), ids[rows], w[rows], bank.expert64)
+    check_layer(y[rows], ref, "prefill bf16 full")
+
+
+def test_prefill_equals_decode_small_batch():
+    b = binding()
+    bank = Bf16Bank(43, 8, 256, 128)
+    pool = _slots_identity(b, bank, b.W_BF16)
+    rng = np.random.default_rng(4)
+    x = gen.activations_bf16(rng, 8, 256)
+    ids, w = route.topk_softmax(rng.standard_normal((8, 8)).astype(np.float32), 2)
+    y1 = _run_forward(b, pool, x, ids, w, b.FWD_DECODE)
+    y2 = _run_forward(b, pool, x, ids, w, b.FWD_PREFILL)
+    ref = ffn.moe_output(numerics.bf16_to_f64(x), ids, w, bank.expert64)
+    check_layer(y1, ref)
+    check_layer(y2, ref)
+
+
+# ---------------------------------------------------------------- merge
+def test_merge_partial():
+    b = binding()
+    rng = np.random.default_rng(0)
+    for T, H in [(1, 2048), (3, 7), (32, 256)]:
+        yg = rng.standard_normal((T, H)).astype(np.float32)
+        yh = rng.standard_normal((T, H)).astype(np.float32)
+        yb = torch.empty((T, H), dtype=torch.uint16, device="cuda")
+        out = b.merge_partial(dev(yg), dev(yh), y_out_bf16=yb).cpu().numpy()
+        assert np.array_equal(out, yg + yh)                    # one float32 add: exact
+        ref_b = torch.from_numpy(yg + yh).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+        assert np.array_equal(yb.cpu().numpy().view(np.uint16), ref_b)
+    # host partial in pinned memory
+    yh = pinned(np.ones((2, 64), np.float32))
+    out = b.merge_partial(dev(np.zeros((2, 64), np.float32)), yh).cpu().numpy()
+    assert np.all(out == 1)
+
+
+# ---------------------------------------------------------------- the tiny workload end to end
+def test_tiny_layer_end_to_end():
+    """Route -> cache step (with fills) -> grouped evaluation -> merge with the
+    host partial; compared to the oracle's exact layer output."""
+    b = binding()
+    c = CONFIGS["tiny"]
+    bank = Bf16Bank(c.cfg_id, c.E, c.H, c.I)
+    x = gen.activations_bf16(gen.np_rng(c.cfg_id, gen.S_ACT), c.T, c.H)
+    wr = gen.router_matrix(gen.np_rng(c.cfg_id, gen.S_ROUTER), c.H, c.E, c.router_std)
+    lg = gen.router_logits(x, wr)
+    for T_step in (c.T, 1):                                # one 32-token step; 32 one-token steps
+        pool = b.SlotPool(c.C, c.H, c.I, b.W_BF16)
+        host = b.HostPoolTables(bank.host, lambda i: i, c.E)
+        cache = b.Cache(c.L, c.E, c.k, T_step, pool, host, c.bp, c.bh)
+        cache.seed(list(c.seed_slots))
+        out = b.StepOut(T_step, c.k, c.E)
+        orc = lru.ExpertCache(c.L, c.E, c.C, c.bp, c.bh)
+        orc.seed(list(c.seed_slots))
+        ws = b.forward_workspace(T_step, c.k, c.H, c.I, c.C, b.FWD_DECODE)
+        ys = []
+        for t0 in range(0, c.T, T_step):
+            lg_d = dev(lg[t0:t0 + T_step])
+            ids_d, w_d = b.route_topk(lg_d, c.k)
+            cache.step(0, ids_d, out)
+            y_gpu = b.expert_forward(pool.c, dev(x[t0:t0 + T_step]), out.pick_slot.view(T_step, c.k), w_d,
+                                     b.FWD_DECODE, ws)
+            ids, w = route.topk_softmax(lg[t0:t0 + T_step], c.k)
+            r = orc.step(0, ids)
+            assert np.array_equal(out.pick_slot.cpu().numpy(), r.pick_slot.reshape(-1))
+            yg_ref, yh_ref = oracle_partials(x[t0:t0 + T_step], ids, w, bank.expert64, r.pick_slot >= 0)
+            check_layer(y_gpu.cpu().numpy(), yg_ref, "y_gpu")
+            y = b.merge_partial(y_gpu, dev(yh_ref.astype(np.float32))).cpu().numpy()
+            ys.append(y)
+        y = np.concatenate(ys)
+        ref = ffn.moe_output(numerics.bf16_to_f64(x), route.topk_softmax(lg, c.k)[0],
+                             route.topk_softmax(lg, c.k)[1], bank.expert64)
+        check_layer(y, ref, "tiny end to end")
+        cache.destroy()
