@@ -168,6 +168,7 @@ __global__ __launch_bounds__(kThreads) void cache_decide_kernel(CacheDev cd, Ste
     if (f) uniq[u + pos] = e;
     u += tot;
   }
+  __syncthreads();   // uniq[] is read below by threads of other waves
 
   // 2. classify against the residency table
   bool is_hit = false;
@@ -192,6 +193,7 @@ __global__ __launch_bounds__(kThreads) void cache_decide_kernel(CacheDev cd, Ste
       uslot[tid] = -1;
     }
   }
+  __syncthreads();   // hit_list / miss_list / uslot are read by other waves
 
   // 3. q* = clamp(round(m bp / bh), 1, m)
   int qs = 0;

@@ -27,7 +27,7 @@ def test_e4m3_expansion_all_codes():
 
 
 # ---------------------------------------------------------------- router
-@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (33, 8, 2), (64, 128, 8), (300, 256, 8), (17, 1000, 32), (5, 64, 64)])
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (33, 8, 2), (64, 128, 8), (300, 256, 8), (17, 1000, 32), (5, 64, 32)])
 def test_route_topk(T, E, k):
     b = binding()
     rng = np.random.default_rng(T * 1000 + E)
@@ -192,6 +192,8 @@ def test_sticky_decode_trace_short():
         for l in range(c.L):
             ids, _ = route.topk_softmax(logits[s, l], c.k)
             hz.step(l, ids)
+            if s >= 10:
+                hz.compare_tables()
     hz.compare_tables()
 
 

@@ -232,14 +232,15 @@ def test_tiny_layer_end_to_end():
         out = b.StepOut(T_step, c.k, c.E)
         orc = lru.ExpertCache(c.L, c.E, c.C, c.bp, c.bh)
         orc.seed(list(c.seed_slots))
-        ws = b.forward_workspace(T_step, c.k, c.H, c.I, c.C, b.FWD_DECODE)
+        mode = b.FWD_DECODE if T_step <= 16 else b.FWD_PREFILL   # decode mode serves T <= 16
+        ws = b.forward_workspace(T_step, c.k, c.H, c.I, c.C, mode)
         ys = []
         for t0 in range(0, c.T, T_step):
             lg_d = dev(lg[t0:t0 + T_step])
             ids_d, w_d = b.route_topk(lg_d, c.k)
             cache.step(0, ids_d, out)
             y_gpu = b.expert_forward(pool.c, dev(x[t0:t0 + T_step]), out.pick_slot.view(T_step, c.k), w_d,
-                                     b.FWD_DECODE, ws)
+                                     mode, ws)
             ids, w = route.topk_softmax(lg[t0:t0 + T_step], c.k)
             r = orc.step(0, ids)
             assert np.array_equal(out.pick_slot.cpu().numpy(), r.pick_slot.reshape(-1))
