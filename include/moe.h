@@ -195,6 +195,16 @@ moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t* ids, int3
                           uint32_t flags, const moe_step_out* out, hipStream_t stream);
 
 /*
+ * The fused fill copy alone: copy every bank of the out->counts[MOE_CNT_FILL]
+ * experts listed in out->fill_id / out->fill_slot from the pinned host pool
+ * into their slots, with one fixed-grid launch masked by the device count
+ * ([FT] section "Device-side 缓存控制").  moe_cache_step with
+ * MOE_STEP_NO_COPY followed by this call equals moe_cache_step without the
+ * flag.  Capturable.
+ */
+moe_status moe_cache_fill(moe_cache_t c, const moe_step_out* out, hipStream_t stream);
+
+/*
  * Copy the residency tables to HOST arrays (any pointer may be NULL):
  * slot_id [C] (-1 empty, -2 reserved by a prefill pool), stamp [C] (0 empty,
  * (tick << 16) | (1 + rank) otherwise), id_slot [L*E], tick, and counters[6] =

@@ -28,7 +28,7 @@ CNT_UNIQ, CNT_HIT, CNT_MISS, CNT_QSTAR, CNT_FILL, CNT_HOST, CNT_N = 0, 1, 2, 3, 
 
 EXPORTS = [
     "moe_last_error", "moe_route_topk", "moe_cache_workspace_bytes", "moe_cache_create",
-    "moe_cache_seed", "moe_cache_step", "moe_cache_read_state", "moe_cache_error",
+    "moe_cache_seed", "moe_cache_step", "moe_cache_fill", "moe_cache_read_state", "moe_cache_error",
     "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_e4m3_to_bf16",
@@ -74,6 +74,7 @@ _sig = {
     "moe_cache_create": (_i32, [_P(CacheCfg), _P(Slots), _P(HostPool), _vp, _sz, _vp, _P(_vp)]),
     "moe_cache_seed": (_i32, [_vp, _P(_i32), _i32, _u32, _vp]),
     "moe_cache_step": (_i32, [_vp, _i32, _vp, _i32, _u32, _P(StepOutC), _vp]),
+    "moe_cache_fill": (_i32, [_vp, _P(StepOutC), _vp]),
     "moe_cache_read_state": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_cache_error": (_i32, [_vp, _P(_i32), _vp]),
     "moe_cache_destroy": (_i32, [_vp]),
@@ -207,6 +208,9 @@ class Cache:
         T = ids.shape[0]
         _check(_lib.moe_cache_step(self.h, layer, _ptr(ids), T, 0 if copy else STEP_NO_COPY,
                                    ctypes.byref(out.c), _stream(stream)), "moe_cache_step")
+
+    def fill(self, out: StepOut, stream=None):
+        _check(_lib.moe_cache_fill(self.h, ctypes.byref(out.c), _stream(stream)), "moe_cache_fill")
 
     def read_state(self, stream=None):
         import numpy as np

@@ -750,6 +750,12 @@ extern "C" moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t
   return MOE_OK;
 }
 
+extern "C" moe_status moe_cache_fill(moe_cache_t c, const moe_step_out* out, hipStream_t stream) {
+  clear_error();
+  if (!c || !out || !out->fill_id || !out->fill_slot || !out->counts) MOE_FAIL(MOE_ERR_ARG, "null argument");
+  return launch_fill(c, out->fill_id, out->fill_slot, out->counts + MOE_CNT_FILL, stream);
+}
+
 extern "C" moe_status moe_cache_read_state(moe_cache_t c, int32_t* slot_id, uint64_t* stamp, int32_t* id_slot,
                                            uint64_t* tick, uint64_t* counters, hipStream_t stream) {
   clear_error();

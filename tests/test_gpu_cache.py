@@ -207,6 +207,17 @@ def test_fill_copies_every_bank():
     hz.check_slot_bytes()
 
 
+def test_separate_fill_call_equals_step_with_copy():
+    hz = Harness(2, 8, 6, 2, 2, 900, 475, H=64, I=32, copy=False)
+    rng = np.random.default_rng(4)
+    for s in range(30):
+        ids = np.stack([rng.choice(8, size=2, replace=False) for _ in range(2)])
+        hz.step(int(rng.integers(0, 2)), ids)
+        hz.cache.fill(hz.out)
+    hz.compare_tables()
+    hz.check_slot_bytes()
+
+
 def test_bad_expert_id_sets_error_word():
     hz = Harness(1, 8, 4, 1, 2, 118, 475)
     ids = dev(np.array([[3, 11]], np.int32))
