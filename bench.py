@@ -58,7 +58,8 @@ def run_decode(b, K, W):
     log("decode: generating trace and weights")
     picks, logits = gen.decode_trace(c.cfg_id, L, n, E, k, c.p_keep)
     wg, wu, wd = gen.bank_bf16(c.cfg_id, E, H, I, c.w_std)
-    host_banks = [torch.from_numpy(a).pin_memory() for a in (wg, wu, wd)]
+    host_banks = [t.cpu().pin_memory() for t in
+                  b.pack_weights(b.W_BF16, *[torch.from_numpy(a).cuda() for a in (wg, wu, wd)])]
     host = b.HostPoolTables(host_banks, lambda i: gen.alias_base_expert(i // E, i % E, E, c.alias_stride), L * E)
     pool = b.SlotPool(C, H, I, b.W_BF16)
     cache = b.Cache(L, E, k, 1, pool, host, c.bp, c.bh)
@@ -144,9 +145,8 @@ def run_prefill(b, reps):
     log("prefill: generating weights and activations")
     wg, wu, wd = gen.bank_bf16(c.cfg_id, E, H, I, c.w_std)
     pool = b.SlotPool(E, H, I, b.W_BF16)
-    pool.w_gate.copy_(torch.from_numpy(wg))
-    pool.w_up.copy_(torch.from_numpy(wu))
-    pool.w_down.copy_(torch.from_numpy(wd))
+    b.pack_weights(b.W_BF16, *[torch.from_numpy(a).cuda() for a in (wg, wu, wd)], out_gu=pool.w_gu,
+                   out_down=pool.w_down)
     xb = gen.activations_bf16(gen.np_rng(c.cfg_id, gen.S_ACT), T, H)
     wr = gen.router_matrix(gen.np_rng(c.cfg_id, gen.S_ROUTER), H, E, c.router_std)
     lg = torch.from_numpy(gen.router_logits(xb, wr)).cuda()

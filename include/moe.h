@@ -57,20 +57,28 @@ typedef enum {
 /*
  * Slot pool: every tensor of one (layer, expert) in one slot ([FT] section
  * "全层双缓冲"; [FTK] paragraph on the elastic expert cache).  One bank per
- * tensor, slot-major, matrices stored [out, in] row-major:
- *   w_gate, w_up : [n_slots][I][H]   (uint16 BF16 or uint8 E4M3)
- *   w_down       : [n_slots][H][I]
- *   s_gate, s_up : [n_slots][I/128][H/128] float32   (FP8 only, else NULL)
- *   s_down       : [n_slots][H/128][I/128] float32   (FP8 only, else NULL)
- * All bases 16-byte aligned.  A view of slots [a, a+n) is the same struct with
- * every base advanced by a slots and n_slots = n.
+ * tensor kind, slot-major, 16-byte aligned:
+ *   w_gate_up : [n_slots][2*I*H] elements, gate and up weights in the packed
+ *               brick format below (BF16 bits or E4M3 codes)
+ *   w_down    : [n_slots][H*I] elements, down weights in the brick format
+ *   s_gate, s_up : [n_slots][I/128][H/128] float32  (FP8 only, else NULL)
+ *   s_down       : [n_slots][H/128][I/128] float32  (FP8 only, else NULL)
+ * Brick format of a matrix W [N][K] (stored [out, in]): 1 KB bricks, one per
+ * 16 rows x KB columns (KB = 32 for BF16, 64 for FP8), brick (t, kt) at
+ * element offset (t * (K/KB) + kt) * 16*KB; inside a brick the 64 lanes of an
+ * MFMA operand follow each other, lane l = 16*j + r holding W[16t + r][KB*kt
+ * + (KB/4)*j + e] for e < KB/4.  The gate/up bank is the brick format of the
+ * 2I-row matrix whose row 16t + r is W_gate row 8t + r (r < 8) or W_up row
+ * 8t + r - 8 (r >= 8).  moe_pack_weights produces both banks from row-major
+ * matrices.  Scales stay row-major per 128 x 128 tile of the original
+ * matrices.  A view of slots [a, a+n) is the same struct with every base
+ * advanced by a slots and n_slots = n.
  */
 typedef struct moe_slots {
   int32_t wtype;           /* moe_wtype */
   int32_t H, I;            /* hidden and SwiGLU intermediate sizes */
   int32_t n_slots;
-  void* w_gate;
-  void* w_up;
+  void* w_gate_up;
   void* w_down;
   float* s_gate;
   float* s_up;
@@ -87,9 +95,8 @@ typedef struct moe_slots {
  * memory they point to must outlive the cache.
  */
 typedef struct moe_host_pool {
-  const void* const* w_gate;
-  const void* const* w_up;
-  const void* const* w_down;
+  const void* const* w_gate_up;   /* packed gate/up bank rows, per logical id */
+  const void* const* w_down;      /* packed down bank rows                    */
   const float* const* s_gate;
   const float* const* s_up;
   const float* const* s_down;
@@ -219,6 +226,16 @@ moe_status moe_cache_read_state(moe_cache_t c, int32_t* slot_id, uint64_t* stamp
 moe_status moe_cache_error(moe_cache_t c, int32_t* code, hipStream_t stream);
 
 moe_status moe_cache_destroy(moe_cache_t c);
+
+/*
+ * Pack n experts from row-major device matrices into the brick format of the
+ * slot pool (see moe_slots): w_gate, w_up [n][I][H] and w_down [n][H][I]
+ * (BF16 bits or E4M3 codes) -> w_gate_up [n][2*I*H], w_down_packed [n][H*I].
+ * Requires I % 8 == 0 and H, I multiples of 32 (BF16) or 128 (FP8).  The
+ * outputs must not overlap the inputs.  Device pointers; enqueued on stream.
+ */
+moe_status moe_pack_weights(int32_t wtype, int32_t H, int32_t I, int32_t n, const void* w_gate, const void* w_up,
+                            const void* w_down, void* w_gate_up, void* w_down_packed, hipStream_t stream);
 
 /* Bytes of device workspace moe_expert_forward needs for these sizes. */
 moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int32_t H, int32_t I,

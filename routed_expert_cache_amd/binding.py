@@ -31,7 +31,7 @@ EXPORTS = [
     "moe_cache_seed", "moe_cache_step", "moe_cache_fill", "moe_cache_read_state", "moe_cache_error",
     "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
-    "moe_prefill_destroy", "moe_e4m3_to_bf16",
+    "moe_prefill_destroy", "moe_e4m3_to_bf16", "moe_pack_weights",
 ]
 
 
@@ -45,13 +45,13 @@ class MoeError(RuntimeError):
 class Slots(ctypes.Structure):
     _fields_ = [("wtype", ctypes.c_int32), ("H", ctypes.c_int32), ("I", ctypes.c_int32),
                 ("n_slots", ctypes.c_int32),
-                ("w_gate", ctypes.c_void_p), ("w_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
+                ("w_gate_up", ctypes.c_void_p), ("w_down", ctypes.c_void_p),
                 ("s_gate", ctypes.c_void_p), ("s_up", ctypes.c_void_p), ("s_down", ctypes.c_void_p)]
 
 
 class HostPool(ctypes.Structure):
     _fields_ = [(n, ctypes.POINTER(ctypes.c_void_p)) for n in
-                ("w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down")]
+                ("w_gate_up", "w_down", "s_gate", "s_up", "s_down")]
 
 
 class CacheCfg(ctypes.Structure):
@@ -87,6 +87,7 @@ _sig = {
     "moe_prefill_release": (_i32, [_vp, _i32, _vp]),
     "moe_prefill_destroy": (_i32, [_vp, _vp]),
     "moe_e4m3_to_bf16": (_i32, [_vp, _vp, ctypes.c_int64, _vp]),
+    "moe_pack_weights": (_i32, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -122,14 +123,13 @@ def route_topk(logits, k, ids=None, w=None, stream=None):
 
 # ---------------------------------------------------------------- slot pools
 class SlotPool:
-    """Device banks of n_slots experts (torch tensors) and their moe_slots view."""
+    """Device banks of n_slots experts (torch tensors, brick format) and their moe_slots view."""
 
     def __init__(self, n_slots, H, I, wtype=W_BF16, device="cuda"):
         self.n_slots, self.H, self.I, self.wtype = n_slots, H, I, wtype
         dt = torch.uint16 if wtype == W_BF16 else torch.uint8
-        self.w_gate = torch.empty((n_slots, I, H), dtype=dt, device=device)
-        self.w_up = torch.empty((n_slots, I, H), dtype=dt, device=device)
-        self.w_down = torch.empty((n_slots, H, I), dtype=dt, device=device)
+        self.w_gu = torch.empty((n_slots, 2 * I * H), dtype=dt, device=device)
+        self.w_down = torch.empty((n_slots, H * I), dtype=dt, device=device)
         if wtype == W_FP8_B128:
             self.s_gate = torch.empty((n_slots, I // 128, H // 128), dtype=torch.float32, device=device)
             self.s_up = torch.empty((n_slots, I // 128, H // 128), dtype=torch.float32, device=device)
@@ -137,20 +137,31 @@ class SlotPool:
         else:
             self.s_gate = self.s_up = self.s_down = None
         self.c = Slots(wtype, H, I, n_slots, *[None if t is None else t.data_ptr() for t in
-                                                (self.w_gate, self.w_up, self.w_down,
-                                                 self.s_gate, self.s_up, self.s_down)])
+                                                (self.w_gu, self.w_down, self.s_gate, self.s_up, self.s_down)])
 
     def banks(self):
-        out = [self.w_gate, self.w_up, self.w_down]
+        out = [self.w_gu, self.w_down]
         if self.wtype == W_FP8_B128:
             out += [self.s_gate, self.s_up, self.s_down]
         return out
 
 
+def pack_weights(wtype, w_gate, w_up, w_down, out_gu=None, out_down=None, stream=None):
+    """Row-major device weights [n, I, H], [n, I, H], [n, H, I] -> brick banks [n, 2IH], [n, HI]."""
+    n, I, H = w_gate.shape
+    if out_gu is None:
+        out_gu = torch.empty((n, 2 * I * H), dtype=w_gate.dtype, device=w_gate.device)
+    if out_down is None:
+        out_down = torch.empty((n, H * I), dtype=w_gate.dtype, device=w_gate.device)
+    _check(_lib.moe_pack_weights(wtype, H, I, n, _ptr(w_gate), _ptr(w_up), _ptr(w_down), _ptr(out_gu),
+                                 _ptr(out_down), _stream(stream)), "moe_pack_weights")
+    return out_gu, out_down
+
+
 class HostPoolTables:
     """Per-logical-id pointers into pinned host tensors (aliasing allowed).
 
-    `banks` is a list (gate, up, down[, s_gate, s_up, s_down]) of pinned host
+    `banks` is a list (gate_up, down[, s_gate, s_up, s_down]) of pinned host
     tensors whose first dim indexes *base* experts; `base_of` maps a logical
     id to its base expert row."""
 
@@ -164,7 +175,7 @@ class HostPoolTables:
             arr = (ctypes.c_void_p * n_ids)(*[t.data_ptr() + int(base_of(i)) * row for i in range(n_ids)])
             self._arrays.append(arr)
             ptrs.append(ctypes.cast(arr, ctypes.POINTER(ctypes.c_void_p)))
-        while len(ptrs) < 6:
+        while len(ptrs) < 5:
             ptrs.append(None)
         self.c = HostPool(*ptrs)
 

@@ -43,8 +43,9 @@ moe_status check_slots(const moe_slots* s) {
   if (s->H <= 0 || s->I <= 0 || s->n_slots <= 0) MOE_FAIL(MOE_ERR_SHAPE, "bad slot shape");
   int q = s->wtype == MOE_W_FP8_B128 ? 128 : 32;
   if (s->H % q || s->I % q) MOE_FAIL(MOE_ERR_SHAPE, "H and I must be multiples of %d (H=%d I=%d)", q, s->H, s->I);
-  if (!s->w_gate || !s->w_up || !s->w_down) MOE_FAIL(MOE_ERR_ARG, "null weight bank");
-  if (!aligned16(s->w_gate) || !aligned16(s->w_up) || !aligned16(s->w_down))
+  if (s->I % 8) MOE_FAIL(MOE_ERR_SHAPE, "I must be a multiple of 8");
+  if (!s->w_gate_up || !s->w_down) MOE_FAIL(MOE_ERR_ARG, "null weight bank");
+  if (!aligned16(s->w_gate_up) || !aligned16(s->w_down))
     MOE_FAIL(MOE_ERR_ARG, "weight banks must be 16-byte aligned");
   if (s->wtype == MOE_W_FP8_B128) {
     if (!s->s_gate || !s->s_up || !s->s_down) MOE_FAIL(MOE_ERR_ARG, "null scale bank");
@@ -54,12 +55,10 @@ moe_status check_slots(const moe_slots* s) {
   return MOE_OK;
 }
 
-constexpr int kThreads = 1024;        // decision kernel: one workgroup
+constexpr int kDT = 256;              // decision kernel: one workgroup of 4 waves
 constexpr int kUMax = 1024;           // T_max * k <= 1024
 constexpr int kEMax = 4096;
 constexpr int kCMax = 16384;
-constexpr uint64_t kSent = ~0ull;
-constexpr int kSmallQ = 32;           // tournament selection up to this many victims
 
 enum { ERR_BAD_ID = 1, ERR_TICK = 2, ERR_TABLE = 3 };
 
@@ -67,6 +66,8 @@ struct CacheDev {
   int32_t* id_slot;     // [L*E]
   int32_t* slot_id;     // [C]   -1 empty, -2 reserved, else logical id
   uint64_t* stamp;      // [C]
+  int32_t* order;       // [C]   non-reserved slots in ascending (stamp, slot): the LRU order
+  int32_t* n_ord;       // [1]   entries of `order`
   uint64_t* tick;       // [1]
   uint64_t* counters;   // [8]
   int32_t* error;       // [1]
@@ -88,300 +89,206 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
-__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int m) {
-  uint32_t lo = __shfl_xor((uint32_t)v, m, 64);
-  uint32_t hi = __shfl_xor((uint32_t)(v >> 32), m, 64);
-  return ((uint64_t)hi << 32) | lo;
-}
-
-__device__ __forceinline__ uint64_t wave_min_u64(uint64_t v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) {
-    uint64_t o = shfl_xor_u64(v, m);
-    v = o < v ? o : v;
-  }
-  return v;
-}
-
-// Block-wide stable compaction step: every thread offers `flag`; returns the
-// thread's output position (valid if flag) and writes the total to *total.
-// `wsum` is LDS scratch of 16 ints.  Contains two barriers.
-__device__ int block_compact(bool flag, int* wsum, int* total) {
+// Ordered compaction over [0, N) by the 4 waves of the workgroup: each wave
+// walks a contiguous range in 64-element steps with ballots; pass 1 counts,
+// one barrier shares the wave totals, pass 2 emits (i, rank) in index order.
+// `pred` is evaluated twice and must be pure.  Ends with a barrier.
+template <class Pred, class Emit>
+__device__ int ordered_compact(int N, Pred pred, Emit emit, int* wtot) {
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  uint64_t b = __ballot(flag);
-  int pre = __popcll(b & lanemask_lt());
-  if (lane == 0) wsum[wv] = __popcll(b);
+  const int per = ((N + kDT - 1) / kDT) * 64;
+  const int beg = wv * per, end = min(N, beg + per);
+  int cnt = 0;
+  for (int i0 = beg; i0 < end; i0 += 64) {
+    const int i = i0 + lane;
+    cnt += __popcll(__ballot(i < end && pred(i)));
+  }
+  if (lane == 0) wtot[wv] = cnt;
   __syncthreads();
-  int base = 0, tot = 0;
-  for (int i = 0; i < kThreads / 64; ++i) {
-    int c = wsum[i];
-    base += (i < wv) ? c : 0;
-    tot += c;
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kDT / 64; ++w) {
+    const int t = wtot[w];
+    base += (w < wv) ? t : 0;
+    total += t;
+  }
+  for (int i0 = beg; i0 < end; i0 += 64) {
+    const int i = i0 + lane;
+    const bool f = i < end && pred(i);
+    const uint64_t b = __ballot(f);
+    if (f) emit(i, base + __popcll(b & lanemask_lt()));
+    base += __popcll(b);
   }
   __syncthreads();
-  *total = tot;
-  return base + pre;
+  return total;
 }
 
 // ---------------------------------------------------------------- decision kernel
-__global__ __launch_bounds__(kThreads) void cache_decide_kernel(CacheDev cd, StepArgs a) {
-  extern __shared__ uint64_t keys[];          // [C]
-  __shared__ uint32_t bm[kEMax / 32];
+// LRU order array: the slots sorted by (stamp, slot), reserved slots left out.
+// Victims are the first q entries that hold no hit of this call, found in one
+// ordered scan; the new order is the other entries in place, then the hits
+// (rank order), then the filled victims: exactly the (stamp, slot) order after
+// the new stamps, since every new stamp exceeds all older ones.
+__global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs a) {
+  extern __shared__ int dyn[];                // ord [C] then hitbm [C/32]
+  __shared__ uint32_t bm[kEMax / 32];         // routed experts of this layer
   __shared__ int uniq[kUMax];                 // local expert index, ascending
   __shared__ int uslot[kUMax];                // slot of uniq[i] after the step, -1 = host
   __shared__ int hit_list[kUMax];             // positions into uniq
   __shared__ int miss_list[kUMax];
   __shared__ int victims[kUMax];
-  __shared__ uint64_t cand[16 * kSmallQ];
-  __shared__ int hist[256];
-  __shared__ int wsum[16];
-  __shared__ int sh[8];                       // 0 u, 1 h, 2 m, 3 q*, 4 q, 5 n_cand
-  __shared__ uint64_t sh64[4];                // 0 tick, 1 radix prefix, 2 key OR
+  __shared__ int wtot[kDT / 64];
+  __shared__ uint64_t s_tick;
+  __shared__ int s_nord;
 
   const int tid = threadIdx.x;
   const int E = cd.E, C = cd.C, layer = a.layer;
   const int P = a.T * a.k;
   const int lbase = layer * E;
+  int* ord = dyn;
+  uint32_t* hitbm = reinterpret_cast<uint32_t*>(dyn + C);
 
-  for (int i = tid; i < (E + 31) / 32; i += kThreads) bm[i] = 0;
+  for (int i = tid; i < (E + 31) / 32; i += kDT) bm[i] = 0;
+  for (int i = tid; i < (C + 31) / 32; i += kDT) hitbm[i] = 0;
   if (tid == 0) {
-    sh64[0] = *cd.tick;
-    sh64[2] = 0;
+    s_tick = *cd.tick;
+    s_nord = *cd.n_ord;
   }
   __syncthreads();
+  const int n_ord = s_nord;
+  for (int i = tid; i < n_ord; i += kDT) ord[i] = cd.order[i];   // staged: the new order overwrites it
 
-  // 1. dedup: bitmap of the routed experts of this layer
-  for (int p = tid; p < P; p += kThreads) {
-    int e = a.ids[p];
+  // 1. dedup: bitmap of the routed experts, compacted in ascending order
+  for (int p = tid; p < P; p += kDT) {
+    const int e = a.ids[p];
     if (e < 0 || e >= E)
       atomicOr(cd.error, 1 << ERR_BAD_ID);
     else
       atomicOr(&bm[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
-  int u = 0;
-  for (int base = 0; base < E; base += kThreads) {
-    int e = base + tid;
-    bool f = e < E && ((bm[e >> 5] >> (e & 31)) & 1u);
-    int tot;
-    int pos = block_compact(f, wsum, &tot);
-    if (f) uniq[u + pos] = e;
-    u += tot;
-  }
-  __syncthreads();   // uniq[] is read below by threads of other waves
+  const int u = ordered_compact(
+      E, [&](int e) { return ((bm[e >> 5] >> (e & 31)) & 1u) != 0; }, [&](int e, int r) { uniq[r] = e; }, wtot);
 
   // 2. classify against the residency table
-  bool is_hit = false;
-  int my_slot = -1;
-  if (tid < u) {
-    my_slot = cd.id_slot[lbase + uniq[tid]];
-    if (my_slot >= C) {
+  for (int i = tid; i < u; i += kDT) {
+    int s = cd.id_slot[lbase + uniq[i]];
+    if (s >= C || (s >= 0 && cd.slot_id[s] != lbase + uniq[i])) {
       atomicOr(cd.error, 1 << ERR_TABLE);
-      my_slot = -1;
+      s = -1;
     }
-    is_hit = my_slot >= 0;
+    uslot[i] = s;
+    a.out.is_hit[i] = s >= 0 ? 1 : 0;
   }
-  int h, m;
-  int hp = block_compact(tid < u && is_hit, wsum, &h);
-  int mp = block_compact(tid < u && !is_hit, wsum, &m);
-  if (tid < u) {
-    if (is_hit) {
-      hit_list[hp] = tid;
-      uslot[tid] = my_slot;
-    } else {
-      miss_list[mp] = tid;
-      uslot[tid] = -1;
-    }
-  }
-  __syncthreads();   // hit_list / miss_list / uslot are read by other waves
+  for (int i = u + tid; i < a.U_max; i += kDT) a.out.is_hit[i] = -1;
+  __syncthreads();
+  const int h = ordered_compact(
+      u, [&](int i) { return uslot[i] >= 0; }, [&](int i, int r) { hit_list[r] = i; }, wtot);
+  const int m = ordered_compact(
+      u, [&](int i) { return uslot[i] < 0; }, [&](int i, int r) { miss_list[r] = i; }, wtot);
 
   // 3. q* = clamp(round(m bp / bh), 1, m)
   int qs = 0;
   if (m > 0) {
-    uint64_t q0 = (2ull * (uint64_t)m * cd.bp + cd.bh) / (2ull * cd.bh);
+    const uint64_t q0 = (2ull * (uint64_t)m * cd.bp + cd.bh) / (2ull * cd.bh);
     qs = (int)(q0 < 1 ? 1 : (q0 > (uint64_t)m ? (uint64_t)m : q0));
   }
 
-  // 4. one scan over the slots: keys (stamp << 20 | slot) of the candidates
-  int q = 0;
-  if (qs > 0) {
-    int ncand = 0;
-    uint64_t kor = 0;
-    for (int s = tid; s < C; s += kThreads) {
-      int sid = cd.slot_id[s];
-      bool pinned_hit = false;
-      if (sid >= 0) {
-        int sl = sid - lbase;
-        pinned_hit = sl >= 0 && sl < E && ((bm[sl >> 5] >> (sl & 31)) & 1u);
-      }
-      uint64_t key = kSent;
-      if (sid != -2 && !pinned_hit) {
-        key = (cd.stamp[s] << 20) | (uint64_t)s;
-        ++ncand;
-        kor |= key;
-      }
-      keys[s] = key;
-    }
-    if (tid == 0) sh[5] = 0;
-    __syncthreads();
-    atomicAdd(&sh[5], ncand);
-    if (kor) atomicOr((unsigned long long*)&sh64[2], (unsigned long long)kor);
-    __syncthreads();
-    q = qs < sh[5] ? qs : sh[5];
-
-    if (q > 0 && q <= kSmallQ) {
-      // tournament: each wave extracts its q smallest keys, then wave 0 merges
-      const int lane = tid & 63, wv = tid >> 6;
-      for (int r = 0; r < q; ++r) {
-        uint64_t best = kSent;
-        int bs = -1;
-        for (int s = tid; s < C; s += kThreads) {
-          uint64_t kk = keys[s];
-          if (kk < best) {
-            best = kk;
-            bs = s;
-          }
-        }
-        uint64_t wmin = wave_min_u64(best);
-        if (wmin != kSent && best == wmin) keys[bs] = kSent;   // keys are unique
-        if (lane == 0) cand[wv * kSmallQ + r] = wmin;
-      }
-      __syncthreads();
-      if (wv == 0) {
-        const int NC = 16 * q;
-        for (int r = 0; r < q; ++r) {
-          uint64_t best = kSent;
-          int bi = -1;
-          for (int i = lane; i < NC; i += 64) {
-            int idx = (i / q) * kSmallQ + (i % q);
-            uint64_t kk = cand[idx];
-            if (kk < best) {
-              best = kk;
-              bi = idx;
-            }
-          }
-          uint64_t wmin = wave_min_u64(best);
-          if (wmin != kSent && best == wmin) cand[bi] = kSent;
-          if (lane == 0) victims[r] = (int)(wmin & 0xFFFFFull);
-        }
-      }
-      __syncthreads();
-    } else if (q > 0) {
-      // MSD radix select of the q-th smallest key, 8 bits per pass
-      uint64_t kor_all = sh64[2];
-      int top = 63 - __builtin_clzll(kor_all | 1ull);
-      int start = (top / 8) * 8;
-      if (tid == 0) {
-        sh64[1] = 0;
-        sh[6] = q;
-      }
-      __syncthreads();
-      for (int shift = start; shift >= 0; shift -= 8) {
-        for (int i = tid; i < 256; i += kThreads) hist[i] = 0;
-        __syncthreads();
-        const uint64_t prefix = sh64[1];
-        const uint64_t himask = (shift + 8 >= 64) ? 0ull : (~0ull << (shift + 8));
-        for (int s = tid; s < C; s += kThreads) {
-          uint64_t kk = keys[s];
-          if (kk != kSent && (kk & himask) == prefix) atomicAdd(&hist[(kk >> shift) & 255], 1);
-        }
-        __syncthreads();
-        if (tid < 64) {
-          // wave 0: inclusive scan over 256 bins, 4 per lane
-          int c0 = hist[4 * tid], c1 = hist[4 * tid + 1], c2 = hist[4 * tid + 2], c3 = hist[4 * tid + 3];
-          int lsum = c0 + c1 + c2 + c3;
-          int incl = lsum;
-#pragma unroll
-          for (int d = 1; d < 64; d <<= 1) {
-            int o = __shfl_up(incl, d, 64);
-            if (tid >= d) incl += o;
-          }
-          int excl = incl - lsum;
-          int need = sh[6];
-          if (excl < need && incl >= need) {
-            int c[4] = {c0, c1, c2, c3};
-            int cum = excl, dgt = 0;
-            for (int j = 0; j < 4; ++j) {
-              if (cum + c[j] >= need) {
-                dgt = 4 * tid + j;
-                break;
-              }
-              cum += c[j];
-            }
-            sh[6] = need - cum;
-            sh64[1] = prefix | ((uint64_t)dgt << shift);
-          }
-        }
-        __syncthreads();
-      }
-      const uint64_t thr = sh64[1];   // exactly the q-th smallest key
-      if (tid == 0) sh[7] = 0;
-      __syncthreads();
-      for (int s = tid; s < C; s += kThreads) {
-        uint64_t kk = keys[s];
-        if (kk != kSent && kk <= thr) {
-          int pos = atomicAdd(&sh[7], 1);   // exactly q keys are <= thr
-          if (pos < q) victims[pos] = s;
-        }
-      }
-      __syncthreads();
-      // order the q victims by key: rank sort
-      int myv = -1;
-      int myrank = 0;
-      if (tid < q) {
-        myv = victims[tid];
-        uint64_t mk = keys[myv];
-        for (int j = 0; j < q; ++j) myrank += keys[victims[j]] < mk;
-      }
-      __syncthreads();
-      if (tid < q) victims[myrank] = myv;
-      __syncthreads();
-    }
+  // 4. one ordered scan of the LRU order: the first q non-hit entries are the
+  //    victims; the others keep their relative order in the new order.
+  for (int r = tid; r < h; r += kDT) {
+    const int s = uslot[hit_list[r]];
+    atomicOr(&hitbm[s >> 5], 1u << (s & 31));
   }
+  __syncthreads();
+  const auto is_cand = [&](int i) {
+    const int s = ord[i];
+    return ((hitbm[s >> 5] >> (s & 31)) & 1u) == 0;
+  };
+  // pass 1 of the compaction is also the candidate count, needed for q
+  int n_cand;
+  {
+    const int lane = tid & 63, wv = tid >> 6;
+    const int per = ((n_ord + kDT - 1) / kDT) * 64;
+    const int beg = wv * per, end = min(n_ord, beg + per);
+    int cnt = 0;
+    for (int i0 = beg; i0 < end; i0 += 64) {
+      const int i = i0 + lane;
+      cnt += __popcll(__ballot(i < end && is_cand(i)));
+    }
+    if (lane == 0) wtot[wv] = cnt;
+    __syncthreads();
+    int base = 0;
+    n_cand = 0;
+#pragma unroll
+    for (int w = 0; w < kDT / 64; ++w) {
+      const int t = wtot[w];
+      base += (w < wv) ? t : 0;
+      n_cand += t;
+    }
+    const int q_ = qs < n_cand ? qs : n_cand;
+    for (int i0 = beg; i0 < end; i0 += 64) {
+      const int i = i0 + lane;
+      const bool f = i < end && is_cand(i);
+      const uint64_t b = __ballot(f);
+      if (f) {
+        const int r = base + __popcll(b & lanemask_lt());
+        if (r < q_)
+          victims[r] = ord[i];
+        else
+          cd.order[r - q_] = ord[i];
+      }
+      base += __popcll(b);
+    }
+    __syncthreads();
+  }
+  const int q = qs < n_cand ? qs : n_cand;
 
-  // 5. table update: fill i -> victim i
-  const uint64_t tick = sh64[0];
-  if (tid < q) {
-    int v = victims[tid];
-    int f = lbase + uniq[miss_list[tid]];
-    int old = cd.slot_id[v];
+  // 5. table update: fill i -> victim i; stamps; tail of the new order
+  const uint64_t tick = s_tick;
+  for (int i = tid; i < q; i += kDT) {
+    const int v = victims[i];
+    const int f = lbase + uniq[miss_list[i]];
+    const int old = cd.slot_id[v];
     if (old >= 0) cd.id_slot[old] = -1;
     cd.slot_id[v] = f;
     cd.id_slot[f] = v;
-    uslot[miss_list[tid]] = v;
-    a.out.fill_id[tid] = f;
-    a.out.fill_slot[tid] = v;
-    a.out.fill_evicted[tid] = old;
-    cd.stamp[v] = (tick << 16) | (uint64_t)(1 + h + tid);
+    uslot[miss_list[i]] = v;
+    a.out.fill_id[i] = f;
+    a.out.fill_slot[i] = v;
+    a.out.fill_evicted[i] = old;
+    cd.stamp[v] = (tick << 16) | (uint64_t)(1 + h + i);
+    cd.order[n_cand - q + h + i] = v;
   }
-  if (tid < h) cd.stamp[uslot[hit_list[tid]]] = (tick << 16) | (uint64_t)(1 + tid);
+  for (int r = tid; r < h; r += kDT) {
+    const int s = uslot[hit_list[r]];
+    cd.stamp[s] = (tick << 16) | (uint64_t)(1 + r);
+    cd.order[n_cand - q + r] = s;
+  }
   __syncthreads();
 
   // 6. outputs: rewrite picks, lists, counts
-  for (int p = tid; p < P; p += kThreads) {
-    int e = a.ids[p];
+  for (int p = tid; p < P; p += kDT) {
+    const int e = a.ids[p];
     int slot = -1;
     if (e >= 0 && e < E) {
       int lo = 0, hi = u - 1;
       while (lo < hi) {
-        int mid = (lo + hi) >> 1;
+        const int mid = (lo + hi) >> 1;
         if (uniq[mid] < e) lo = mid + 1; else hi = mid;
       }
       slot = uslot[lo];
     }
     a.out.pick_slot[p] = slot;
   }
-  if (tid < a.U_max) {
-    a.out.uniq[tid] = tid < u ? lbase + uniq[tid] : -1;
-    a.out.is_hit[tid] = tid < u ? (is_hit ? 1 : 0) : -1;
-  }
-  for (int i = tid; i < a.U_max; i += kThreads) {
+  for (int i = tid; i < a.U_max; i += kDT) {
+    a.out.uniq[i] = i < u ? lbase + uniq[i] : -1;
     if (i >= q) {
       a.out.fill_id[i] = -1;
       a.out.fill_slot[i] = -1;
       a.out.fill_evicted[i] = -1;
     }
-    int hi = i + q;
+    const int hi = i + q;
     a.out.host_id[i] = (hi < m) ? lbase + uniq[miss_list[hi]] : -1;
   }
   if (tid == 0) {
@@ -405,6 +312,28 @@ __global__ __launch_bounds__(kThreads) void cache_decide_kernel(CacheDev cd, Ste
   }
 }
 
+// Rebuild the LRU order from the stamps (set-up paths only: reset, seed,
+// reserve, release): rank of each non-reserved slot by (stamp, slot).
+__global__ __launch_bounds__(1024) void cache_order_kernel(CacheDev cd) {
+  __shared__ int cnt;
+  if (threadIdx.x == 0) cnt = 0;
+  __syncthreads();
+  for (int s = threadIdx.x; s < cd.C; s += 1024) {
+    if (cd.slot_id[s] == -2) continue;
+    const uint64_t ks = cd.stamp[s];
+    int rank = 0;
+    for (int t = 0; t < cd.C; ++t) {
+      if (cd.slot_id[t] == -2) continue;
+      const uint64_t kt = cd.stamp[t];
+      rank += (kt < ks) || (kt == ks && t < s);
+    }
+    cd.order[rank] = s;
+    atomicAdd(&cnt, 1);
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) *cd.n_ord = cnt;
+}
+
 // ---------------------------------------------------------------- fused fill copy
 struct FillArgs {
   const int32_t* fill_id;
@@ -412,8 +341,8 @@ struct FillArgs {
   const int32_t* n_fill;        // device count
   const uint64_t* host_tab;     // [nb][LE]
   int LE, C, nb;
-  char* dst[6];
-  uint64_t bytes[6];
+  char* dst[5];
+  uint64_t bytes[5];
 };
 
 __global__ __launch_bounds__(256) void cache_fill_kernel(FillArgs a) {
@@ -508,7 +437,7 @@ struct moe_cache {
   moe::CacheDev dev;
   int nb;
   moe::BankBytes bb;
-  std::vector<const void*> host_ptr[6];   // host-visible pool pointers (for DMA)
+  std::vector<const void*> host_ptr[5];   // host-visible pool pointers (for DMA)
   int lds_bytes;
   int U_max;
   bool has_prefill;
@@ -519,7 +448,7 @@ using namespace moe;
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t id_slot, slot_id, stamp, tick, counters, error, seed, host_tab, total;
+  size_t id_slot, slot_id, stamp, order, n_ord, tick, counters, error, seed, host_tab, total;
 };
 static WsLayout ws_layout(const moe_cache_cfg* c, int nb) {
   WsLayout w{};
@@ -528,6 +457,8 @@ static WsLayout ws_layout(const moe_cache_cfg* c, int nb) {
   w.id_slot = off; off = align_up(off + 4 * LE, 256);
   w.slot_id = off; off = align_up(off + 4 * (size_t)c->C, 256);
   w.stamp = off; off = align_up(off + 8 * (size_t)c->C, 256);
+  w.order = off; off = align_up(off + 4 * (size_t)c->C, 256);
+  w.n_ord = off; off = align_up(off + 4, 256);
   w.tick = off; off = align_up(off + 8, 256);
   w.counters = off; off = align_up(off + 64, 256);
   w.error = off; off = align_up(off + 4, 256);
@@ -555,7 +486,7 @@ extern "C" moe_status moe_cache_workspace_bytes(const moe_cache_cfg* cfg, size_t
   moe_status st = check_cfg(cfg);
   if (st) return st;
   if (!bytes) MOE_FAIL(MOE_ERR_ARG, "bytes is NULL");
-  *bytes = ws_layout(cfg, 6).total;
+  *bytes = ws_layout(cfg, 5).total;
   return MOE_OK;
 }
 
@@ -570,24 +501,23 @@ extern "C" moe_status moe_cache_create(const moe_cache_cfg* cfg, const moe_slots
   if ((st = check_slots(slots))) return st;
   if (slots->n_slots != cfg->C) MOE_FAIL(MOE_ERR_SHAPE, "slots->n_slots (%d) != cfg->C (%d)", slots->n_slots, cfg->C);
   if (reinterpret_cast<uintptr_t>(dev_ws) & 255) MOE_FAIL(MOE_ERR_ARG, "workspace must be 256-byte aligned");
-  const int nb = slots->wtype == MOE_W_FP8_B128 ? 6 : 3;
-  WsLayout L = ws_layout(cfg, 6);
+  const int nb = slots->wtype == MOE_W_FP8_B128 ? 5 : 2;
+  WsLayout L = ws_layout(cfg, 5);
   if (ws_bytes < L.total) MOE_FAIL(MOE_ERR_NO_SPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
 
   int dev = 0;
   MOE_HIP(hipGetDevice(&dev));
   int lds_max = 0;
   MOE_HIP(hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
-  const int lds_static = 32 * 1024;   // bound on the kernel's static LDS (about 26 KB)
-  const int lds_dyn = 8 * cfg->C;
+  const int lds_static = 32 * 1024;   // bound on the kernel's static LDS (about 21 KB)
+  const int lds_dyn = 4 * cfg->C + 4 * ((cfg->C + 31) / 32);
   if (lds_dyn + lds_static > lds_max)
     MOE_FAIL(MOE_ERR_SHAPE, "C=%d needs %d B of LDS; device allows %d", cfg->C, lds_dyn + lds_static, lds_max);
 
-  const void* const* tabs[6] = {host->w_gate, host->w_up, host->w_down,
-                                (const void* const*)host->s_gate, (const void* const*)host->s_up,
-                                (const void* const*)host->s_down};
+  const void* const* tabs[5] = {host->w_gate_up, host->w_down, (const void* const*)host->s_gate,
+                                (const void* const*)host->s_up, (const void* const*)host->s_down};
   const size_t LE = (size_t)cfg->L * cfg->E;
-  std::vector<uint64_t> htab((size_t)nb * LE);
+  std::vector<uint64_t> htab((size_t)nb * LE);  // nb <= 5
   moe_cache* c = new moe_cache();
   for (int b = 0; b < nb; ++b) {
     if (!tabs[b]) {
@@ -645,6 +575,8 @@ extern "C" moe_status moe_cache_create(const moe_cache_cfg* cfg, const moe_slots
   d.id_slot = (int32_t*)(ws + L.id_slot);
   d.slot_id = (int32_t*)(ws + L.slot_id);
   d.stamp = (uint64_t*)(ws + L.stamp);
+  d.order = (int32_t*)(ws + L.order);
+  d.n_ord = (int32_t*)(ws + L.n_ord);
   d.tick = (uint64_t*)(ws + L.tick);
   d.counters = (uint64_t*)(ws + L.counters);
   d.error = (int32_t*)(ws + L.error);
@@ -665,6 +597,7 @@ extern "C" moe_status moe_cache_create(const moe_cache_cfg* cfg, const moe_slots
   e = hipMemcpyAsync((void*)d.host_tab, htab.data(), htab.size() * 8, hipMemcpyHostToDevice, stream);
   if (e == hipSuccess) {
     cache_reset_kernel<<<64, 256, 0, stream>>>(d, 0);
+    cache_order_kernel<<<1, 1024, 0, stream>>>(d);
     e = hipGetLastError();
   }
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
@@ -686,8 +619,7 @@ static moe_status launch_fill(moe_cache* c, const int32_t* fill_id, const int32_
   f.LE = c->cfg.L * c->cfg.E;
   f.C = c->cfg.C;
   f.nb = c->nb;
-  void* bases[6] = {c->slots.w_gate, c->slots.w_up, c->slots.w_down,
-                    c->slots.s_gate, c->slots.s_up, c->slots.s_down};
+  void* bases[5] = {c->slots.w_gate_up, c->slots.w_down, c->slots.s_gate, c->slots.s_up, c->slots.s_down};
   for (int b = 0; b < c->nb; ++b) {
     f.dst[b] = (char*)bases[b];
     f.bytes[b] = c->bb.b[b];
@@ -718,6 +650,7 @@ extern "C" moe_status moe_cache_seed(moe_cache_t c, const int32_t* host_ids, int
   MOE_LAUNCHED();
   if (n > 0) MOE_HIP(hipMemcpyAsync(d.seed_list, host_ids, 4 * (size_t)n, hipMemcpyHostToDevice, stream));
   cache_seed_kernel<<<(n + 255) / 256 + 1, 256, 0, stream>>>(d, n);
+  cache_order_kernel<<<1, 1024, 0, stream>>>(d);
   MOE_LAUNCHED();
   if (!(flags & MOE_STEP_NO_COPY) && n > 0) {
     moe_status st = launch_fill(c, d.seed_list, d.seed_list + c->cfg.C, d.seed_list + 2 * c->cfg.C, stream);
@@ -743,7 +676,7 @@ extern "C" moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t
   a.k = c->cfg.k;
   a.U_max = c->U_max;
   a.out = *out;
-  cache_decide_kernel<<<1, kThreads, c->lds_bytes, stream>>>(c->dev, a);
+  cache_decide_kernel<<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
   MOE_LAUNCHED();
   if (!(flags & MOE_STEP_NO_COPY))
     return launch_fill(c, out->fill_id, out->fill_slot, out->counts + MOE_CNT_FILL, stream);
@@ -821,6 +754,7 @@ extern "C" moe_status moe_prefill_create(moe_cache_t c, moe_prefill_t* out) {
     }
   }
   cache_mark_kernel<<<(2 * E + 255) / 256, 256, 0, 0>>>(c->dev, p->first, 2 * E, -2);
+  cache_order_kernel<<<1, 1024, 0, 0>>>(c->dev);
   MOE_LAUNCHED();
   MOE_HIP(hipDeviceSynchronize());
   c->has_prefill = true;
@@ -837,8 +771,7 @@ extern "C" moe_status moe_prefill_prefetch(moe_prefill_t p, int32_t layer, hipSt
   if (p->released_recorded[b]) MOE_HIP(hipStreamWaitEvent(copy_stream, p->released[b], 0));
   const int E = p->E;
   const int slot0 = p->first + b * E;
-  void* bases[6] = {c->slots.w_gate, c->slots.w_up, c->slots.w_down,
-                    c->slots.s_gate, c->slots.s_up, c->slots.s_down};
+  void* bases[5] = {c->slots.w_gate_up, c->slots.w_down, c->slots.s_gate, c->slots.s_up, c->slots.s_down};
   for (int k = 0; k < c->nb; ++k) {
     const size_t sz = c->bb.b[k];
     char* dst = (char*)bases[k] + (size_t)slot0 * sz;
@@ -869,13 +802,12 @@ extern "C" moe_status moe_prefill_acquire(moe_prefill_t p, int32_t layer, hipStr
   const int slot0 = p->first + b * p->E;
   moe_slots v = c->slots;
   v.n_slots = p->E;
-  v.w_gate = (char*)c->slots.w_gate + (size_t)slot0 * c->bb.b[0];
-  v.w_up = (char*)c->slots.w_up + (size_t)slot0 * c->bb.b[1];
-  v.w_down = (char*)c->slots.w_down + (size_t)slot0 * c->bb.b[2];
-  if (c->nb == 6) {
-    v.s_gate = (float*)((char*)c->slots.s_gate + (size_t)slot0 * c->bb.b[3]);
-    v.s_up = (float*)((char*)c->slots.s_up + (size_t)slot0 * c->bb.b[4]);
-    v.s_down = (float*)((char*)c->slots.s_down + (size_t)slot0 * c->bb.b[5]);
+  v.w_gate_up = (char*)c->slots.w_gate_up + (size_t)slot0 * c->bb.b[0];
+  v.w_down = (char*)c->slots.w_down + (size_t)slot0 * c->bb.b[1];
+  if (c->nb == 5) {
+    v.s_gate = (float*)((char*)c->slots.s_gate + (size_t)slot0 * c->bb.b[2]);
+    v.s_up = (float*)((char*)c->slots.s_up + (size_t)slot0 * c->bb.b[3]);
+    v.s_down = (float*)((char*)c->slots.s_down + (size_t)slot0 * c->bb.b[4]);
   }
   *view = v;
   return MOE_OK;
@@ -897,6 +829,7 @@ extern "C" moe_status moe_prefill_destroy(moe_prefill_t p, hipStream_t stream) {
   moe_cache* c = p->c;
   MOE_HIP(hipDeviceSynchronize());
   cache_mark_kernel<<<(2 * p->E + 255) / 256, 256, 0, stream>>>(c->dev, p->first, 2 * p->E, -1);
+  cache_order_kernel<<<1, 1024, 0, stream>>>(c->dev);
   MOE_LAUNCHED();
   MOE_HIP(hipStreamSynchronize(stream));
   for (int b = 0; b < 2; ++b) {

@@ -41,21 +41,22 @@ void clear_error();
 
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Bytes of one slot in each bank: gate, up, down, s_gate, s_up, s_down.
+// Bytes of one slot in each bank, in moe_slots order: gate_up, down, s_gate,
+// s_up, s_down (the scale banks only for FP8).
 struct BankBytes {
-  size_t b[6];
+  size_t b[5];
   int nb;
 };
 inline BankBytes bank_bytes(int wtype, int H, int I) {
   BankBytes r{};
   size_t el = (wtype == MOE_W_BF16) ? 2 : 1;
-  r.b[0] = r.b[1] = el * (size_t)I * H;
-  r.b[2] = el * (size_t)H * I;
+  r.b[0] = el * 2 * (size_t)I * H;
+  r.b[1] = el * (size_t)H * I;
   if (wtype == MOE_W_FP8_B128) {
-    r.b[3] = r.b[4] = r.b[5] = sizeof(float) * (size_t)(I / 128) * (H / 128);
-    r.nb = 6;
+    r.b[2] = r.b[3] = r.b[4] = sizeof(float) * (size_t)(I / 128) * (H / 128);
+    r.nb = 5;
   } else {
-    r.nb = 3;
+    r.nb = 2;
   }
   return r;
 }

@@ -1,4 +1,5 @@
-// Grouped SwiGLU expert evaluation of G = H u F, and the partial-sum merge.
+// Grouped SwiGLU expert evaluation of G = H u F, the weight packing, and the
+// partial-sum merge.
 //
 // [FT] section "执行顺序与工程细节": after the cache update and the copy of F the
 // GPU evaluates all of G as one grouped computation.  [OSDI] section 4.3: an
@@ -7,19 +8,12 @@
 // dotted first and multiplied by the shared block scale once per block
 // (post-scaling: scale * sum(w x) = sum(scale * w * x)).
 //
-// Decode (T <= 16): every slot in G is streamed once from HBM.  The MFMA
-// 16x16x32 BF16 tile takes 16 weight rows as A and the (up to 16) tokens as
-// B, so one weight read serves every token of the batch; tokens that did not
-// pick a slot carry gate weight 0 in the down projection.
-//   plan kernel    : groups = distinct slots of pick_slot (ascending), per
-//                    token gate weight of each group; x padded to 16 rows
-//                    (for FP8: K permuted even/odd inside each 16-group to
-//                    match the register expansion of the codes)
-//   gate/up kernel : one workgroup per (16-row tile of I, group); waves split
-//                    K; h = silu(gate) * up rounded to BF16
-//   down kernel    : one workgroup per 16-row tile of H; loops over the
-//                    groups in order (deterministic), weights each group's
-//                    block by its per-token gate weight
+// Weights live in 1 KB MFMA bricks (see below), so every weight load of a
+// wave is one contiguous 1 KB segment.
+// Decode (T <= 16): every slot in G is streamed once from HBM; the brick is
+// the MFMA A operand and the (up to 16) tokens are B, so one read of a slot
+// serves the whole batch.  Two launches: gate/up + SwiGLU into h, then down
+// with the per-token gate weights.
 // Prefill (any T): (token, pick) pairs counting-sorted by slot, a grouped
 // MFMA GEMM for gate/up with the SwiGLU epilogue, a grouped MFMA GEMM for
 // down with the gate-weight epilogue into per-pair rows, and a combine that
@@ -48,12 +42,52 @@ __device__ __forceinline__ void split_even_odd(const u32x4& a, const u32x4& b, u
   od[3] = (b[2] >> 16) | (b[3] & 0xFFFF0000u);
 }
 
+// ================================================================ brick format
+// A matrix W [N][K] is stored as 1 KB bricks of 16 rows x KB columns (KB = 32
+// BF16 or 64 E4M3): brick (t, kt) at byte offset (t * (K/KB) + kt) * 1024,
+// lane l = 16 j + r of an MFMA operand at l * 16 within it, holding
+// W[16t + r][KB kt + (KB/4) j + e].  A brick is therefore one MFMA 16x16x32
+// operand (A for weights-as-rows, B for weights-as-columns) read with one
+// contiguous 1 KB wave load.  The gate/up bank packs the 2I-row matrix whose
+// row 16t + r is gate row 8t + r (r < 8) or up row 8t + r - 8 (r >= 8).
+
+__global__ __launch_bounds__(256) void pack_kernel(int fp8, int H, int I, int n, const char* __restrict__ wg,
+                                                   const char* __restrict__ wu, const char* __restrict__ wd,
+                                                   char* __restrict__ gu, char* __restrict__ dp) {
+  const int el = fp8 ? 1 : 2, KB = fp8 ? 64 : 32;
+  const size_t gu_chunks = (size_t)2 * I * H * el / 16, d_chunks = (size_t)H * I * el / 16;
+  const size_t per = gu_chunks + d_chunks;
+  const size_t c = (size_t)blockIdx.x * 256 + threadIdx.x;
+  if (c >= per * n) return;
+  const size_t e = c / per;
+  size_t rem = c % per;
+  const int lane = (int)(rem & 63), r = lane & 15, j = lane >> 4;
+  const size_t brick = rem >> 6;
+  if (rem < gu_chunks) {
+    const int nkt = H / KB;
+    const int t = (int)(brick / nkt), kt = (int)(brick % nkt);
+    const int row = 8 * t + (r & 7);
+    const int col = KB * kt + (KB / 4) * j;
+    const char* src = (r < 8 ? wg : wu) + ((e * I + row) * (size_t)H + col) * el;
+    *reinterpret_cast<u32x4*>(gu + e * gu_chunks * 16 + rem * 16) = ld16(src);
+  } else {
+    rem -= gu_chunks;
+    const size_t b2 = rem >> 6;
+    const int nkt = I / KB;
+    const int t = (int)(b2 / nkt), kt = (int)(b2 % nkt);
+    const int row = 16 * t + r;
+    const int col = KB * kt + (KB / 4) * j;
+    const char* src = wd + ((e * H + row) * (size_t)I + col) * el;
+    *reinterpret_cast<u32x4*>(dp + e * d_chunks * 16 + rem * 16) = ld16(src);
+  }
+}
+
 // ================================================================ decode
-constexpr int kDecTok = 16;
+constexpr int kDecTok = 16;     // MFMA N: tokens of one decode call
+constexpr int kDecPmax = 512;   // T * k picks
 
 struct DecArgs {
-  const void* w_gate;
-  const void* w_up;
+  const void* w_gu;
   const void* w_down;
   const float* s_gate;
   const float* s_up;
@@ -63,215 +97,268 @@ struct DecArgs {
   const int32_t* pick_slot;  // [T*k]
   const float* w;            // [T*k]
   float* y;                  // [T][H]
-  // workspace
-  int32_t* nG;               // [1]
-  int32_t* gslot;            // [G_max]
-  float* gw;                 // [G_max][16]
-  uint16_t* xpad;            // [16][H]
-  uint16_t* h;               // [G_max][16][I]
+  const uint16_t* xb;        // B-operand source [T][H]: x (BF16) or x permuted even/odd (FP8)
+  uint16_t* xperm;           // workspace [T][H] (FP8 only)
+  uint16_t* h;               // workspace [G_max][16][I]
   int G_max;
+  int kp2;                   // K-parts of the down projection per expert
 };
 
-template <bool FP8>
-__global__ __launch_bounds__(256) void dec_plan_kernel(DecArgs a) {
-  if (blockIdx.x == 0) {
-    __shared__ int s_slot[512];
-    __shared__ int s_first[512];
-    __shared__ float s_gw[512 * kDecTok];
-    __shared__ int s_n;
-    const int P = a.T * a.k;
-    for (int i = threadIdx.x; i < a.G_max * kDecTok; i += 256) s_gw[i] = 0.f;
-    for (int p = threadIdx.x; p < P; p += 256) {
-      int s = a.pick_slot[p];
-      s_slot[p] = (s >= 0 && s < a.n_slots) ? s : -1;
-    }
-    if (threadIdx.x == 0) s_n = 0;
-    __syncthreads();
-    for (int p = threadIdx.x; p < P; p += 256) {
-      int s = s_slot[p];
-      bool first = s >= 0;
-      for (int q = 0; q < p && first; ++q) first = s_slot[q] != s;
-      s_first[p] = first;
-      if (first) atomicAdd(&s_n, 1);
-    }
-    __syncthreads();
-    for (int p = threadIdx.x; p < P; p += 256) {
-      int s = s_slot[p];
-      if (s < 0) continue;
-      int rank = 0;
-      for (int q = 0; q < P; ++q) rank += (s_first[q] && s_slot[q] < s);
-      if (s_first[p]) a.gslot[rank] = s;
-      s_gw[rank * kDecTok + p / a.k] = a.w[p];
-    }
-    __syncthreads();
-    for (int i = threadIdx.x; i < a.G_max * kDecTok; i += 256) a.gw[i] = s_gw[i];
-    if (threadIdx.x == 0) *a.nG = s_n;
-  } else {
-    // x -> xpad [16][H], 16 elements per thread
-    const int c = (blockIdx.x - 1) * 256 + threadIdx.x;
-    const int per_row = a.H / 16;
-    if (c >= kDecTok * per_row) return;
-    const int t = c / per_row, kc = (c % per_row) * 16;
-    u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-    if (t < a.T) {
-      v0 = ld16(a.x + (size_t)t * a.H + kc);
-      v1 = ld16(a.x + (size_t)t * a.H + kc + 8);
-    }
-    uint16_t* dst = a.xpad + (size_t)t * a.H + kc;
-    if (FP8) {
-      u32x4 ev, od;
-      split_even_odd(v0, v1, ev, od);
-      *reinterpret_cast<u32x4*>(dst) = ev;
-      *reinterpret_cast<u32x4*>(dst + 8) = od;
-    } else {
-      *reinterpret_cast<u32x4*>(dst) = v0;
-      *reinterpret_cast<u32x4*>(dst + 8) = v1;
-    }
+// Group plan in LDS: groups are the distinct valid slots of pick_slot in
+// order of first appearance.  s_gslot[g] = slot of group g; if s_gw is not
+// NULL, s_gw[g*16 + t] = gate weight of token t's pick of group g (0 if
+// none).  Returns the number of groups.  Contains barriers; all threads call.
+template <int NT>
+__device__ int plan_groups(const DecArgs& a, int* s_ps, int* s_first, int* s_gslot, float* s_gw, int* s_n) {
+  const int P = a.T * a.k, tid = threadIdx.x;
+  for (int p = tid; p < P; p += NT) {
+    const int s = a.pick_slot[p];
+    s_ps[p] = (s >= 0 && s < a.n_slots) ? s : -1;
   }
+  if (s_gw)
+    for (int i = tid; i < a.G_max * kDecTok; i += NT) s_gw[i] = 0.f;
+  if (tid == 0) *s_n = 0;
+  __syncthreads();
+  for (int p = tid; p < P; p += NT) {
+    const int s = s_ps[p];
+    bool first = s >= 0;
+    for (int q = 0; q < p && first; ++q) first = s_ps[q] != s;
+    s_first[p] = first;
+    if (first) atomicAdd(s_n, 1);
+  }
+  __syncthreads();
+  for (int p = tid; p < P; p += NT) {
+    const int s = s_ps[p];
+    if (s < 0) continue;
+    int fq = p;
+    if (!s_first[p])
+      for (int q = 0; q < p; ++q)
+        if (s_ps[q] == s) { fq = q; break; }
+    int g = 0;
+    for (int q = 0; q < fq; ++q) g += s_first[q];
+    if (fq == p) s_gslot[g] = s;
+    if (s_gw) s_gw[g * kDecTok + p / a.k] = a.w[p];
+  }
+  __syncthreads();
+  return *s_n;
 }
 
+// FP8 only: x -> x permuted even/odd inside each 16-group, 16 elements per thread
+__global__ __launch_bounds__(256) void dec_xperm_kernel(DecArgs a) {
+  const int c = blockIdx.x * 256 + threadIdx.x;
+  const int per_row = a.H / 16;
+  if (c >= a.T * per_row) return;
+  const int t = c / per_row, kc = (c % per_row) * 16;
+  const u32x4 v0 = ld16(a.x + (size_t)t * a.H + kc);
+  const u32x4 v1 = ld16(a.x + (size_t)t * a.H + kc + 8);
+  u32x4 ev, od;
+  split_even_odd(v0, v1, ev, od);
+  uint16_t* dst = a.xperm + (size_t)t * a.H + kc;
+  *reinterpret_cast<u32x4*>(dst) = ev;
+  *reinterpret_cast<u32x4*>(dst + 8) = od;
+}
+
+// gate/up + SwiGLU.  One workgroup per (gate/up brick row t = 8 rows of I,
+// group).  The brick's A rows 0..7 are gate rows and 8..15 the same up rows,
+// so one fragment holds gate and up of the same outputs.  Waves split K and
+// issue a batch of contiguous 1 KB brick loads (plus the matching x loads)
+// before its MFMAs.  Workgroups of group 0 also zero y for the down launch.
 template <bool FP8, int NW>
 __global__ __launch_bounds__(NW * 64) void dec_gateup_kernel(DecArgs a) {
+  __shared__ int s_ps[kDecPmax], s_first[kDecPmax], s_gslot[kDecPmax];
+  __shared__ int s_n;
+  __shared__ f32x4 red[NW][64];
+  if (blockIdx.y == 0)
+    for (int i = blockIdx.x * NW * 64 + threadIdx.x; i < a.T * a.H; i += gridDim.x * NW * 64) a.y[i] = 0.f;
+  const int nG = plan_groups<NW * 64>(a, s_ps, s_first, s_gslot, nullptr, &s_n);
   const int g = blockIdx.y;
-  if (g >= *a.nG) return;
-  const int slot = a.gslot[g];
-  const int row0 = blockIdx.x * 16;
+  if (g >= nG) return;
+  const int slot = s_gslot[g];
+  const int t = blockIdx.x;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int r = lane & 15, j = lane >> 4;
   const int H = a.H, I = a.I;
-  f32x4 accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+  const bool tok = r < a.T;
+  f32x4 acc = {0, 0, 0, 0};
   if (!FP8) {
-    const uint16_t* wg = (const uint16_t*)a.w_gate + ((size_t)slot * I + row0 + r) * H + j * 8;
-    const uint16_t* wu = (const uint16_t*)a.w_up + ((size_t)slot * I + row0 + r) * H + j * 8;
-    const uint16_t* xb = a.xpad + (size_t)r * H + j * 8;
-    const int nk = H / 32;
-    const int kb = wv * nk / NW, ke = (wv + 1) * nk / NW;
-#pragma unroll 4
-    for (int kk = kb; kk < ke; ++kk) {
-      u32x4 ag = ld16_nt(wg + kk * 32);
-      u32x4 au = ld16_nt(wu + kk * 32);
-      u32x4 b = ld16(xb + kk * 32);
-      accg = mfma16x16x32(ag, b, accg);
-      accu = mfma16x16x32(au, b, accu);
+    const int nkt = H / 32;
+    const uint16_t* gu = (const uint16_t*)a.w_gu + (size_t)slot * 2 * I * H + (size_t)t * nkt * 512 + lane * 8;
+    const uint16_t* xr = a.xb + (size_t)(tok ? r : 0) * H + j * 8;
+    const int kb = wv * nkt / NW, ke = (wv + 1) * nkt / NW;
+    constexpr int CH = 8;
+    for (int k0 = kb; k0 < ke; k0 += CH) {
+      u32x4 av[CH], bv[CH];
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (k0 + c < ke) av[c] = ld16_nt(gu + (size_t)(k0 + c) * 512);
+#pragma unroll
+      for (int c = 0; c < CH; ++c) bv[c] = (tok && k0 + c < ke) ? ld16(xr + (k0 + c) * 32) : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int c = 0; c < CH; ++c)
+        if (k0 + c < ke) acc = mfma16x16x32(av[c], bv[c], acc);
     }
   } else {
-    const uint8_t* wg = (const uint8_t*)a.w_gate + ((size_t)slot * I + row0 + r) * H + j * 16;
-    const uint8_t* wu = (const uint8_t*)a.w_up + ((size_t)slot * I + row0 + r) * H + j * 16;
-    const uint16_t* xb = a.xpad + (size_t)r * H + j * 16;
-    const int nbk = H / 128;
-    const float* sg = a.s_gate + ((size_t)slot * (I / 128) + row0 / 128) * nbk;
-    const float* su = a.s_up + ((size_t)slot * (I / 128) + row0 / 128) * nbk;
+    const int nkt = H / 64, nbk = H / 128;
+    const uint8_t* gu = (const uint8_t*)a.w_gu + (size_t)slot * 2 * I * H + (size_t)t * nkt * 1024 + lane * 16;
+    const uint16_t* xr = a.xb + (size_t)(tok ? r : 0) * H + j * 16;
+    // C rows 4j+i: j < 2 are gate rows, j >= 2 up rows, each with its scale row
+    const float* sc = (j < 2 ? a.s_gate : a.s_up) + ((size_t)slot * (I / 128) + (8 * t) / 128) * nbk;
     const int bb = wv * nbk / NW, be = (wv + 1) * nbk / NW;
-#pragma unroll 2
-    for (int kb = bb; kb < be; ++kb) {
-      f32x4 pg = {0, 0, 0, 0}, pu = {0, 0, 0, 0};
+    constexpr int CB = 4;   // 128-K blocks per batch: 8 brick loads in flight per lane
+    for (int b0 = bb; b0 < be; b0 += CB) {
+      u32x4 q[CB][2], xv[CB][4];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int ko = kb * 128 + hh * 64;
-        u32x4 qg = ld16_nt(wg + ko);
-        u32x4 qu = ld16_nt(wu + ko);
-        u32x4 xe = ld16(xb + ko), xo = ld16(xb + ko + 8);
-        u32x4 ge, go, ue, uo;
-        e4m3x16_to_bf16(qg, ge, go);
-        e4m3x16_to_bf16(qu, ue, uo);
-        pg = mfma16x16x32(ge, xe, pg);
-        pg = mfma16x16x32(go, xo, pg);
-        pu = mfma16x16x32(ue, xe, pu);
-        pu = mfma16x16x32(uo, xo, pu);
-      }
-      const float cg = sg[kb], cu = su[kb];
+      for (int c = 0; c < CB; ++c)
+        if (b0 + c < be) {
+          q[c][0] = ld16_nt(gu + (size_t)(2 * (b0 + c)) * 1024);
+          q[c][1] = ld16_nt(gu + (size_t)(2 * (b0 + c) + 1) * 1024);
+        }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        accg[i] += cg * pg[i];
-        accu[i] += cu * pu[i];
-      }
-    }
-  }
-  __shared__ f32x4 red[NW][2][64];
-  red[wv][0][lane] = accg;
-  red[wv][1][lane] = accu;
-  __syncthreads();
-  if (wv == 0) {
-    f32x4 G = red[0][0][lane], U = red[0][1][lane];
+      for (int c = 0; c < CB; ++c)
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      G += red[w][0][lane];
-      U += red[w][1][lane];
-    }
-    uint16_t* hrow = a.h + ((size_t)g * kDecTok + r) * I;
+        for (int v = 0; v < 4; ++v)
+          xv[c][v] = (tok && b0 + c < be) ? ld16(xr + (b0 + c) * 128 + (v >> 1) * 64 + (v & 1) * 8) : u32x4{0, 0, 0, 0};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = row0 + 4 * j + i;
-      const float hv = silu_f32(G[i]) * U[i];
-      const int pos = FP8 ? ((row & ~15) + perm16(row & 15)) : row;
-      hrow[pos] = f32_to_bf16_rne(hv);
-    }
-  }
-}
-
-template <bool FP8, int NW>
-__global__ __launch_bounds__(NW * 64) void dec_down_kernel(DecArgs a) {
-  const int row0 = blockIdx.x * 16;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int r = lane & 15, j = lane >> 4;
-  const int H = a.H, I = a.I;
-  const int nG = *a.nG;
-  f32x4 acc = {0, 0, 0, 0};
-  for (int g = 0; g < nG; ++g) {
-    const int slot = a.gslot[g];
-    const float wgt = a.gw[g * kDecTok + r];
-    f32x4 blk = {0, 0, 0, 0};
-    if (!FP8) {
-      const uint16_t* wd = (const uint16_t*)a.w_down + ((size_t)slot * H + row0 + r) * I + j * 8;
-      const uint16_t* hb = a.h + ((size_t)g * kDecTok + r) * I + j * 8;
-      const int nk = I / 32;
-      const int kb = wv * nk / NW, ke = (wv + 1) * nk / NW;
-#pragma unroll 4
-      for (int kk = kb; kk < ke; ++kk) blk = mfma16x16x32(ld16_nt(wd + kk * 32), ld16(hb + kk * 32), blk);
-    } else {
-      const uint8_t* wd = (const uint8_t*)a.w_down + ((size_t)slot * H + row0 + r) * I + j * 16;
-      const uint16_t* hb = a.h + ((size_t)g * kDecTok + r) * I + j * 16;
-      const int nbk = I / 128;
-      const float* sd = a.s_down + ((size_t)slot * (H / 128) + row0 / 128) * nbk;
-      const int bb = wv * nbk / NW, be = (wv + 1) * nbk / NW;
-      for (int kb = bb; kb < be; ++kb) {
+      for (int c = 0; c < CB; ++c) {
+        if (b0 + c >= be) break;
         f32x4 p = {0, 0, 0, 0};
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int ko = kb * 128 + hh * 64;
-          u32x4 q = ld16_nt(wd + ko);
-          u32x4 he = ld16(hb + ko), ho = ld16(hb + ko + 8);
-          u32x4 de, dd;
-          e4m3x16_to_bf16(q, de, dd);
-          p = mfma16x16x32(de, he, p);
-          p = mfma16x16x32(dd, ho, p);
+          u32x4 ae, ao;
+          e4m3x16_to_bf16(q[c][hh], ae, ao);
+          p = mfma16x16x32(ae, xv[c][2 * hh], p);
+          p = mfma16x16x32(ao, xv[c][2 * hh + 1], p);
         }
-        const float c = sd[kb];
+        const float s = sc[b0 + c];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) blk[i] += c * p[i];
+        for (int i = 0; i < 4; ++i) acc[i] += s * p[i];
+      }
+    }
+  }
+  red[wv][lane] = acc;
+  __syncthreads();
+  if (wv == 0 && j < 2) {
+    f32x4 G = red[0][lane], U = red[0][lane + 32];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      G += red[w][lane];
+      U += red[w][lane + 32];
+    }
+    if (tok) {
+      uint16_t* hrow = a.h + ((size_t)g * kDecTok + r) * I;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int o = 8 * t + 4 * j + i;
+        const int pos = FP8 ? ((o & ~15) + perm16(o & 15)) : o;
+        hrow[pos] = f32_to_bf16_rne(silu_f32(G[i]) * U[i]);
+      }
+    }
+  }
+}
+
+// down projection + gate weights.  Workgroup (16-row brick row t of H, half):
+// half 0 takes the even groups, half 1 the odd ones; its waves take
+// (group, K-part) units round-robin, sums are added in wave order, and each
+// half adds its 16 x T partial into the zeroed y once.  Two additions into 0
+// commute exactly, so y is the same bits whichever half lands first.
+template <bool FP8, int NW>
+__global__ __launch_bounds__(NW * 64) void dec_down_kernel(DecArgs a) {
+  __shared__ int s_ps[kDecPmax], s_first[kDecPmax], s_gslot[kDecPmax];
+  __shared__ float s_gw[kDecPmax * kDecTok];
+  __shared__ int s_n;
+  __shared__ f32x4 red[NW][64];
+  const int nG = plan_groups<NW * 64>(a, s_ps, s_first, s_gslot, s_gw, &s_n);
+  const int t = blockIdx.x, hf = blockIdx.y;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int r = lane & 15, j = lane >> 4;
+  const int H = a.H, I = a.I;
+  const bool tok = r < a.T;
+  const int KP = a.kp2;
+  const int ngh = (nG - hf + 1) / 2;
+  f32x4 acc = {0, 0, 0, 0};
+  for (int u = wv; u < ngh * KP; u += NW) {
+    const int g = 2 * (u / KP) + hf, part = u % KP;
+    const int slot = s_gslot[g];
+    const float wgt = s_gw[g * kDecTok + r];
+    f32x4 blk = {0, 0, 0, 0};
+    if (!FP8) {
+      const int nkt = I / 32;
+      const int kb = part * nkt / KP, ke = (part + 1) * nkt / KP;
+      const uint16_t* wd = (const uint16_t*)a.w_down + (size_t)slot * H * I + (size_t)t * nkt * 512 + lane * 8;
+      const uint16_t* hr = a.h + ((size_t)g * kDecTok + (tok ? r : 0)) * I + j * 8;
+      constexpr int CH = 12;
+      for (int k0 = kb; k0 < ke; k0 += CH) {
+        u32x4 av[CH], bv[CH];
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+          if (k0 + c < ke) av[c] = ld16_nt(wd + (size_t)(k0 + c) * 512);
+#pragma unroll
+        for (int c = 0; c < CH; ++c) bv[c] = (tok && k0 + c < ke) ? ld16(hr + (k0 + c) * 32) : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < CH; ++c)
+          if (k0 + c < ke) blk = mfma16x16x32(av[c], bv[c], blk);
+      }
+    } else {
+      const int nkt = I / 64, nbk = I / 128;
+      const int bb = part * nbk / KP, be = (part + 1) * nbk / KP;
+      const uint8_t* wd = (const uint8_t*)a.w_down + (size_t)slot * H * I + (size_t)t * nkt * 1024 + lane * 16;
+      const uint16_t* hr = a.h + ((size_t)g * kDecTok + (tok ? r : 0)) * I + j * 16;
+      const float* sc = a.s_down + ((size_t)slot * (H / 128) + (16 * t) / 128) * nbk;
+      constexpr int CB = 4;
+      for (int b0 = bb; b0 < be; b0 += CB) {
+        u32x4 qv[CB][2], hv[CB][4];
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          if (b0 + c < be) {
+            qv[c][0] = ld16_nt(wd + (size_t)(2 * (b0 + c)) * 1024);
+            qv[c][1] = ld16_nt(wd + (size_t)(2 * (b0 + c) + 1) * 1024);
+          }
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+#pragma unroll
+          for (int v = 0; v < 4; ++v)
+            hv[c][v] = (tok && b0 + c < be) ? ld16(hr + (b0 + c) * 128 + (v >> 1) * 64 + (v & 1) * 8)
+                                             : u32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < CB; ++c) {
+          if (b0 + c >= be) break;
+          f32x4 p = {0, 0, 0, 0};
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            u32x4 de, dd;
+            e4m3x16_to_bf16(qv[c][hh], de, dd);
+            p = mfma16x16x32(de, hv[c][2 * hh], p);
+            p = mfma16x16x32(dd, hv[c][2 * hh + 1], p);
+          }
+          const float s = sc[b0 + c];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) blk[i] += s * p[i];
+        }
       }
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[i] += wgt * blk[i];
   }
-  __shared__ f32x4 red[NW][64];
   red[wv][lane] = acc;
   __syncthreads();
   if (wv == 0) {
     f32x4 Y = red[0][lane];
 #pragma unroll
     for (int w = 1; w < NW; ++w) Y += red[w][lane];
-    if (r < a.T) *reinterpret_cast<f32x4*>(a.y + (size_t)r * H + row0 + 4 * j) = Y;
+    if (tok) {
+      float* yr = a.y + (size_t)r * H + 16 * t + 4 * j;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) atomicAdd(yr + i, Y[i]);
+    }
   }
 }
 
 // ================================================================ prefill
 constexpr int kBM = 128;          // rows (pairs) per tile
-constexpr int kPfThreads = 256;   // 4 waves, 2 x 2
+constexpr int kPfThreads = 256;   // 4 waves, 2 x 2, 64 x 64 each
 
 struct PfArgs {
-  const void* w_gate;
-  const void* w_up;
+  const void* w_gu;
   const void* w_down;
   const float* s_gate;
   const float* s_up;
@@ -371,19 +458,26 @@ __global__ __launch_bounds__(1024) void pf_sort_kernel(PfArgs a) {
   }
 }
 
-// Grouped GEMM tile: C[128 x 128] = A[128 x K] * B[128 x K]^T over one slot's
-// segment.  GATEUP: A = gathered x rows, B rows 0..63 = W_gate rows n0..n0+63,
-// rows 64..127 = W_up rows n0..n0+63, epilogue h = silu(g) * u (BF16).
-// DOWN: A = h rows of the segment, B = W_down rows n0..n0+127, epilogue
-// o = w_pair * acc (FP32).  FP8 B operands are expanded exactly to BF16 when
-// read from LDS; their 128 x 128 scale multiplies the block partial once.
+// Grouped GEMM tile C[128 pairs x 128 weight rows] over one slot's segment;
+// weights are bricks read as MFMA B operands.  GATEUP: A = gathered x rows,
+// B = gate/up brick rows (16 B-rows = 8 gate + 8 up of the same outputs),
+// epilogue h = silu(g) * u (BF16).  DOWN: A = h rows of the segment, B =
+// W_down bricks, epilogue o = w_pair * acc (FP32).  Global -> register ->
+// LDS staging is double-buffered: the next K step's loads are in flight while
+// the current one computes.  FP8 bricks are expanded exactly to BF16 when
+// read from LDS; the 128 x 128 scale multiplies the block partial once.
 template <bool FP8, bool GATEUP>
 __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(PfArgs a) {
-  constexpr int BK = FP8 ? 128 : 64;
-  constexpr int ASTR = BK + 8;                 // LDS row stride, BF16 elements
-  constexpr int BSTR = FP8 ? (BK + 16) : (BK + 8);   // bytes (FP8) or elements (BF16)
-  __shared__ __attribute__((aligned(16))) uint16_t As[kBM * ASTR];
-  __shared__ __attribute__((aligned(16))) uint16_t Bs[FP8 ? (128 * BSTR / 2) : (128 * BSTR)];
+  constexpr int BK = FP8 ? 128 : 64;           // one FP8 scale block per step; 2 bricks per 16 B-rows
+  constexpr int KB = FP8 ? 64 : 32;            // brick K width
+  constexpr int ASTR = BK + 8;                 // A row stride in LDS (BF16 elements)
+  constexpr int A_ELEMS = kBM * ASTR;
+  constexpr int B_BYTES = 16 * 1024;           // 8 groups of 16 B-rows x 2 bricks
+  constexpr int ACH = kBM * BK / 16;           // 16-element A chunks per step
+  constexpr int ACT = ACH / kPfThreads;        // per thread
+  constexpr int BCT = (B_BYTES / 16) / kPfThreads;
+  __shared__ __attribute__((aligned(16))) uint16_t As[2][A_ELEMS];
+  __shared__ __attribute__((aligned(16))) char Bs[2][B_BYTES];
   __shared__ int rowtok[kBM];
 
   const int tile = blockIdx.x;
@@ -393,118 +487,124 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(PfArgs a) {
   const int seg = a.off[slot];
   const int mrows = min(kBM, a.cnt[slot] - m0);
   const int K = GATEUP ? a.H : a.I;
-  const int N = GATEUP ? a.I : a.H;
-  const int n0 = blockIdx.y * (GATEUP ? 64 : 128);
+  const int nkt = K / KB;
+  const int n0 = blockIdx.y * 128;             // first B row (gate/up rows or H rows)
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;          // wave tile: rows wm*64.., cols wn*64..
+  const int wm = wv >> 1, wn = wv & 1;
   const int r = lane & 15, j = lane >> 4;
 
   if (tid < kBM) {
     int pr = -1;
-    if (tid < mrows) {
-      pr = a.sorted_pair[seg + m0 + tid];
-      if (GATEUP) pr = pr / a.k;               // token row of x
-      else pr = seg + m0 + tid;                // row of h
-    }
+    if (tid < mrows) pr = GATEUP ? a.sorted_pair[seg + m0 + tid] / a.k : seg + m0 + tid;
     rowtok[tid] = pr;
   }
-
-  // B source rows
-  const char* bsrc[2];
-  const float* bscale[2] = {nullptr, nullptr};
-  const size_t el = FP8 ? 1 : 2;
-  if (GATEUP) {
-    bsrc[0] = (const char*)a.w_gate + ((size_t)slot * N + n0) * K * el;
-    bsrc[1] = (const char*)a.w_up + ((size_t)slot * N + n0) * K * el;
-    if (FP8) {
-      bscale[0] = a.s_gate + ((size_t)slot * (N / 128) + n0 / 128) * (K / 128);
-      bscale[1] = a.s_up + ((size_t)slot * (N / 128) + n0 / 128) * (K / 128);
-    }
-  } else {
-    bsrc[0] = (const char*)a.w_down + ((size_t)slot * N + n0) * K * el;
-    bsrc[1] = bsrc[0] + (size_t)64 * K * el;
-    if (FP8) bscale[0] = bscale[1] = a.s_down + ((size_t)slot * (N / 128) + n0 / 128) * (K / 128);
+  const char* bbase = (const char*)(GATEUP ? a.w_gu : a.w_down) +
+                      (size_t)slot * (GATEUP ? 2 : 1) * a.I * a.H * (FP8 ? 1 : 2) + (size_t)(n0 / 16) * nkt * 1024;
+  float sc_lane = 1.f;
+  const float* scp = nullptr;
+  if (FP8) {
+    const int nbk = K / 128;
+    if (GATEUP)   // B column r of a 16-row group: gate (r < 8) or up; all 64 outputs share one scale row block
+      scp = (r < 8 ? a.s_gate : a.s_up) + ((size_t)slot * (a.I / 128) + (n0 / 2) / 128) * nbk;
+    else
+      scp = a.s_down + ((size_t)slot * (a.H / 128) + n0 / 128) * nbk;
   }
+  const uint16_t* asrc = GATEUP ? a.x : a.h;
+  const int astride = GATEUP ? a.H : a.I;
   __syncthreads();
 
+  u32x4 ra[ACT][2], rb[BCT];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int c = 0; c < ACT; ++c) {
+      const int ch = tid + c * kPfThreads;
+      const int row = ch / (BK / 16), kc = (ch % (BK / 16)) * 16;
+      const int src = rowtok[row];
+      if (src >= 0) {
+        const uint16_t* p = asrc + (size_t)src * astride + k0 + kc;
+        ra[c][0] = ld16(p);
+        ra[c][1] = ld16(p + 8);
+      } else {
+        ra[c][0] = u32x4{0, 0, 0, 0};
+        ra[c][1] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < BCT; ++c) {
+      const int ch = tid + c * kPfThreads;     // brick bi = ch / 64 (group bi/2, sub bi%2), lane ch % 64
+      const int bi = ch >> 6, gi = bi >> 1, sub = bi & 1;
+      rb[c] = ld16_nt(bbase + ((size_t)gi * nkt + k0 / KB + sub) * 1024 + (ch & 63) * 16);
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int c = 0; c < ACT; ++c) {
+      const int ch = tid + c * kPfThreads;
+      const int row = ch / (BK / 16), kc = (ch % (BK / 16)) * 16;
+      uint16_t* d = &As[buf][row * ASTR + kc];
+      if (FP8) {
+        u32x4 ev, od;
+        split_even_odd(ra[c][0], ra[c][1], ev, od);
+        *reinterpret_cast<u32x4*>(d) = ev;
+        *reinterpret_cast<u32x4*>(d + 8) = od;
+      } else {
+        *reinterpret_cast<u32x4*>(d) = ra[c][0];
+        *reinterpret_cast<u32x4*>(d + 8) = ra[c][1];
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < BCT; ++c) {
+      const int ch = tid + c * kPfThreads;
+      *reinterpret_cast<u32x4*>(&Bs[buf][ch * 16]) = rb[c];
+    }
+  };
+
   f32x4 acc[4][4];
-  f32x4 part[4][4];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
     for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0, 0, 0, 0};
 
-  const uint16_t* asrc = GATEUP ? a.x : a.h;
-  const int arow_stride = GATEUP ? a.H : a.I;
-
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    // ---- A tile: 128 rows x BK bf16, 16-element chunks (FP8: even/odd permuted)
-    constexpr int ACH = kBM * BK / 16;
-    for (int c = tid; c < ACH; c += kPfThreads) {
-      const int row = c / (BK / 16), kc = (c % (BK / 16)) * 16;
-      const int src = rowtok[row];
-      u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-      if (src >= 0) {
-        const uint16_t* p = asrc + (size_t)src * arow_stride + k0 + kc;
-        v0 = ld16(p);
-        v1 = ld16(p + 8);
-      }
-      uint16_t* d = As + row * ASTR + kc;
-      if (FP8) {
-        u32x4 ev, od;
-        split_even_odd(v0, v1, ev, od);
-        *reinterpret_cast<u32x4*>(d) = ev;
-        *reinterpret_cast<u32x4*>(d + 8) = od;
-      } else {
-        *reinterpret_cast<u32x4*>(d) = v0;
-        *reinterpret_cast<u32x4*>(d + 8) = v1;
-      }
-    }
-    // ---- B tile: 128 rows x BK (raw codes or bf16)
-    constexpr int BROWB = BK * (FP8 ? 1 : 2);   // bytes per row in global
-    constexpr int BCH = 128 * BROWB / 16;
-    for (int c = tid; c < BCH; c += kPfThreads) {
-      const int row = c / (BROWB / 16), cb = (c % (BROWB / 16)) * 16;
-      const char* p = bsrc[row >> 6] + ((size_t)(row & 63) * K + k0) * el + cb;
-      u32x4 v = ld16_nt(p);
-      char* d = (char*)Bs + (size_t)row * (FP8 ? BSTR : BSTR * 2) + cb;
-      *reinterpret_cast<u32x4*>(d) = v;
-    }
-    __syncthreads();
-
+  gload(0);
+  lstore(0);
+  __syncthreads();
+  const int nsteps = K / BK;
+  for (int st = 0; st < nsteps; ++st) {
+    const int buf = st & 1;
+    if (st + 1 < nsteps) gload((st + 1) * BK);
     if (!FP8) {
 #pragma unroll
-      for (int ks = 0; ks < BK; ks += 32) {
+      for (int ks = 0; ks < 2; ++ks) {
         u32x4 af[4], bfr[4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
-          af[mi] = *reinterpret_cast<const u32x4*>(As + (wm * 64 + mi * 16 + r) * ASTR + ks + j * 8);
+          af[mi] = *reinterpret_cast<const u32x4*>(&As[buf][(wm * 64 + mi * 16 + r) * ASTR + ks * 32 + j * 8]);
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
-          bfr[ni] = *reinterpret_cast<const u32x4*>(Bs + (wn * 64 + ni * 16 + r) * BSTR + ks + j * 8);
+          bfr[ni] = *reinterpret_cast<const u32x4*>(&Bs[buf][((wn * 4 + ni) * 2 + ks) * 1024 + lane * 16]);
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
           for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16x16x32(af[mi], bfr[ni], acc[mi][ni]);
       }
     } else {
+      f32x4 part[4][4];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) part[mi][ni] = f32x4{0, 0, 0, 0};
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh) {
-        const int ko = hh * 64 + j * 16;
         u32x4 ae[4], ao[4], be[4], bo[4];
 #pragma unroll
         for (int mi = 0; mi < 4; ++mi) {
-          const uint16_t* p = As + (wm * 64 + mi * 16 + r) * ASTR + ko;
+          const uint16_t* p = &As[buf][(wm * 64 + mi * 16 + r) * ASTR + hh * 64 + j * 16];
           ae[mi] = *reinterpret_cast<const u32x4*>(p);
           ao[mi] = *reinterpret_cast<const u32x4*>(p + 8);
         }
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) {
-          const u32x4 q = *reinterpret_cast<const u32x4*>((const char*)Bs + (wn * 64 + ni * 16 + r) * BSTR + ko);
+          const u32x4 q = *reinterpret_cast<const u32x4*>(&Bs[buf][((wn * 4 + ni) * 2 + hh) * 1024 + lane * 16]);
           e4m3x16_to_bf16(q, be[ni], bo[ni]);
         }
 #pragma unroll
@@ -515,47 +615,37 @@ __global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(PfArgs a) {
             part[mi][ni] = mfma16x16x32(ao[mi], bo[ni], part[mi][ni]);
           }
       }
-      const int kb = k0 / 128;
-      const float sc = bscale[wn][kb];
+      sc_lane = scp[st];
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mi][ni][i] += sc * part[mi][ni][i];
+          for (int i = 0; i < 4; ++i) acc[mi][ni][i] += sc_lane * part[mi][ni][i];
+    }
+    if (st + 1 < nsteps) {
+      lstore(buf ^ 1);
     }
     __syncthreads();
   }
 
   // ---- epilogue.  Lane holds C[row = 4j + i][col = r] of each 16x16 tile.
   if (GATEUP) {
-    // wave (wm, 0) has gate cols 0..63 (B rows 0..63), wave (wm, 1) up cols 0..63
-    __shared__ float ups[kBM * 65];
-    if (wn == 1) {
+    // col r < 8: gate, r >= 8: up of output 8*(n0/16 + wn*4 + ni) + (r & 7)
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+    for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ups[(wm * 64 + mi * 16 + 4 * j + i) * 65 + ni * 16 + r] = acc[mi][ni][i];
-    }
-    __syncthreads();
-    if (wn == 0) {
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
+      for (int ni = 0; ni < 4; ++ni)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          const float v = acc[mi][ni][i];
+          const float u = __shfl_xor(v, 8, 64);
           const int row = wm * 64 + mi * 16 + 4 * j + i;
-          if (row < mrows) {
-            uint16_t* hrow = a.h + (size_t)(seg + m0 + row) * a.I + n0;
-#pragma unroll
-            for (int ni = 0; ni < 4; ++ni) {
-              const float u = ups[row * 65 + ni * 16 + r];
-              hrow[ni * 16 + r] = f32_to_bf16_rne(silu_f32(acc[mi][ni][i]) * u);
-            }
+          if (r < 8 && row < mrows) {
+            const int io = n0 / 2 + (wn * 4 + ni) * 8 + r;
+            a.h[(size_t)(seg + m0 + row) * a.I + io] = f32_to_bf16_rne(silu_f32(v) * u);
           }
         }
-    }
   } else {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi)
@@ -633,16 +723,13 @@ __global__ __launch_bounds__(256) void e4m3_expand_kernel(const uint8_t* __restr
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct DecWs {
-  size_t nG, gslot, gw, xpad, h, total;
+  size_t xperm, h, total;
 };
 static DecWs dec_ws(int T_max, int k, int H, int I, int n_slots) {
   DecWs w{};
   int G = T_max * k < n_slots ? T_max * k : n_slots;
   size_t off = 0;
-  w.nG = off; off = align256(off + 4);
-  w.gslot = off; off = align256(off + 4 * (size_t)G);
-  w.gw = off; off = align256(off + 4 * (size_t)G * kDecTok);
-  w.xpad = off; off = align256(off + 2 * (size_t)kDecTok * H);
+  w.xperm = off; off = align256(off + 2 * (size_t)T_max * H);
   w.h = off; off = align256(off + 2 * (size_t)G * kDecTok * I);
   w.total = off;
   return w;
@@ -692,6 +779,27 @@ extern "C" moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int3
   return MOE_OK;
 }
 
+extern "C" moe_status moe_pack_weights(int32_t wtype, int32_t H, int32_t I, int32_t n, const void* w_gate,
+                                      const void* w_up, const void* w_down, void* w_gate_up, void* w_down_packed,
+                                      hipStream_t stream) {
+  clear_error();
+  if (wtype != MOE_W_BF16 && wtype != MOE_W_FP8_B128) MOE_FAIL(MOE_ERR_ARG, "bad wtype %d", wtype);
+  const int q = wtype == MOE_W_FP8_B128 ? 128 : 32;
+  if (H <= 0 || I <= 0 || n < 0 || H % q || I % q || I % 8)
+    MOE_FAIL(MOE_ERR_SHAPE, "pack needs H, I multiples of %d and I %% 8 == 0 (H=%d I=%d n=%d)", q, H, I, n);
+  if (n == 0) return MOE_OK;
+  if (!w_gate || !w_up || !w_down || !w_gate_up || !w_down_packed) MOE_FAIL(MOE_ERR_ARG, "null argument");
+  if (!aligned16(w_gate) || !aligned16(w_up) || !aligned16(w_down) || !aligned16(w_gate_up) || !aligned16(w_down_packed))
+    MOE_FAIL(MOE_ERR_ARG, "pack buffers must be 16-byte aligned");
+  const size_t el = wtype == MOE_W_FP8_B128 ? 1 : 2;
+  const size_t chunks = (size_t)n * 3 * I * H * el / 16;
+  pack_kernel<<<(unsigned)((chunks + 255) / 256), 256, 0, stream>>>(wtype == MOE_W_FP8_B128, H, I, n, (const char*)w_gate,
+                                                                      (const char*)w_up, (const char*)w_down,
+                                                                      (char*)w_gate_up, (char*)w_down_packed);
+  MOE_LAUNCHED();
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,
                                          const float* w, int32_t T, int32_t k, float* y, void* ws, size_t ws_bytes,
                                          uint32_t mode, hipStream_t stream) {
@@ -708,41 +816,45 @@ extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t*
   char* wsb = (char*)ws;
 
   if (mode == MOE_FWD_DECODE) {
-    if (T > kDecTok || T * k > 512) MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T <= 16 and T*k <= 512 (T=%d k=%d)", T, k);
+    if (T > kDecTok || T * k > kDecPmax)
+      MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T <= 16 and T*k <= 512 (T=%d k=%d)", T, k);
     DecWs L = dec_ws(T, k, H, I, slots->n_slots);
     if (ws_bytes < L.total) MOE_FAIL(MOE_ERR_NO_SPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
     DecArgs a{};
-    a.w_gate = slots->w_gate; a.w_up = slots->w_up; a.w_down = slots->w_down;
+    a.w_gu = slots->w_gate_up; a.w_down = slots->w_down;
     a.s_gate = slots->s_gate; a.s_up = slots->s_up; a.s_down = slots->s_down;
     a.H = H; a.I = I; a.n_slots = slots->n_slots; a.T = T; a.k = k;
     a.x = x; a.pick_slot = pick_slot; a.w = w; a.y = y;
-    a.nG = (int32_t*)(wsb + L.nG);
-    a.gslot = (int32_t*)(wsb + L.gslot);
-    a.gw = (float*)(wsb + L.gw);
-    a.xpad = (uint16_t*)(wsb + L.xpad);
+    a.xperm = (uint16_t*)(wsb + L.xperm);
     a.h = (uint16_t*)(wsb + L.h);
+    a.xb = fp8 ? a.xperm : x;
     a.G_max = T * k < slots->n_slots ? T * k : slots->n_slots;
-    const int xblocks = (kDecTok * (H / 16) + 255) / 256;
+    // K-parts of the down projection: a unit keeps >= 12 bricks (BF16) / 4 blocks (FP8) of loads in flight
+    const int ksteps = fp8 ? I / 128 : I / 32;
+    const int unit = fp8 ? 4 : 12;
+    int kp2 = 1;
+    while (kp2 < 8 && ksteps % (2 * kp2) == 0 && ksteps / (2 * kp2) >= unit) kp2 *= 2;
+    a.kp2 = kp2;
     constexpr int NW = 8;
+    const dim3 g1(I / 8, a.G_max), g2(H / 16, 2);
     if (fp8) {
-      dec_plan_kernel<true><<<1 + xblocks, 256, 0, stream>>>(a);
-      dec_gateup_kernel<true, NW><<<dim3(I / 16, a.G_max), NW * 64, 0, stream>>>(a);
-      dec_down_kernel<true, NW><<<H / 16, NW * 64, 0, stream>>>(a);
+      dec_xperm_kernel<<<(T * (H / 16) + 255) / 256, 256, 0, stream>>>(a);
+      dec_gateup_kernel<true, NW><<<g1, NW * 64, 0, stream>>>(a);
+      dec_down_kernel<true, NW><<<g2, NW * 64, 0, stream>>>(a);
     } else {
-      dec_plan_kernel<false><<<1 + xblocks, 256, 0, stream>>>(a);
-      dec_gateup_kernel<false, NW><<<dim3(I / 16, a.G_max), NW * 64, 0, stream>>>(a);
-      dec_down_kernel<false, NW><<<H / 16, NW * 64, 0, stream>>>(a);
+      dec_gateup_kernel<false, NW><<<g1, NW * 64, 0, stream>>>(a);
+      dec_down_kernel<false, NW><<<g2, NW * 64, 0, stream>>>(a);
     }
     MOE_LAUNCHED();
     return MOE_OK;
   }
   if (mode != MOE_FWD_PREFILL) MOE_FAIL(MOE_ERR_ARG, "bad mode %u", mode);
   if (slots->n_slots > 4096) MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs n_slots <= 4096");
-  if (H % 128 || I % 64) MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs H % 128 == 0 and I % 64 == 0");
+  if (H % 128 || I % 64) MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs H %% 128 == 0 and I %% 64 == 0");
   PfWs L = pf_ws(T, k, H, I, slots->n_slots);
   if (ws_bytes < L.total) MOE_FAIL(MOE_ERR_NO_SPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   PfArgs a{};
-  a.w_gate = slots->w_gate; a.w_up = slots->w_up; a.w_down = slots->w_down;
+  a.w_gu = slots->w_gate_up; a.w_down = slots->w_down;
   a.s_gate = slots->s_gate; a.s_up = slots->s_up; a.s_down = slots->s_down;
   a.H = H; a.I = I; a.n_slots = slots->n_slots; a.T = T; a.k = k; a.P = T * k;
   a.max_tiles = L.max_tiles;

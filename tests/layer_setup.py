@@ -38,13 +38,31 @@ def check_layer(y, ref, what=""):
     return rel
 
 
+def pack_to_host(wtype, wg, wu, wd, chunk=16, pin=True):
+    """Pack row-major expert weights (torch, any device) into brick banks with
+    the library's pack call; returns host tensors (pinned) [E, 2IH], [E, HI]."""
+    b = binding()
+    E, I, H = wg.shape
+    gu = torch.empty((E, 2 * I * H), dtype=wg.dtype, pin_memory=pin)
+    dp = torch.empty((E, H * I), dtype=wg.dtype, pin_memory=pin)
+    for e0 in range(0, E, chunk):
+        e1 = min(E, e0 + chunk)
+        g_d, u_d, d_d = (t[e0:e1].cuda() for t in (wg, wu, wd))
+        pg, pd = b.pack_weights(wtype, g_d, u_d, d_d)
+        gu[e0:e1].copy_(pg)
+        dp[e0:e1].copy_(pd)
+    torch.cuda.synchronize()
+    return gu, dp
+
+
 class Bf16Bank:
-    """E experts in BF16 (numpy bits), their pinned host copy and the oracle view."""
+    """E experts in BF16: row-major bits for the oracle, packed pinned banks for the library."""
 
     def __init__(self, cfg_id, E, H, I, std=0.02, layer=0):
         self.E, self.H, self.I = E, H, I
         self.wg, self.wu, self.wd = gen.bank_bf16(cfg_id, E, H, I, std, layer)
-        self.host = [pinned(a) for a in (self.wg, self.wu, self.wd)]
+        t = [torch.from_numpy(a) for a in (self.wg, self.wu, self.wd)]
+        self.host = list(pack_to_host(0, *t))
         self._cache = {}
 
     def expert64(self, e):
@@ -54,15 +72,15 @@ class Bf16Bank:
         return self._cache[e]
 
     def load_slots(self, pool, slot_of_expert):
-        """Copy expert e's bytes into slot slot_of_expert[e] of a SlotPool."""
+        """Copy expert e's packed bytes into slot slot_of_expert[e] of a SlotPool."""
         for e, s in slot_of_expert.items():
-            pool.w_gate[s].copy_(torch.from_numpy(self.wg[e]))
-            pool.w_up[s].copy_(torch.from_numpy(self.wu[e]))
-            pool.w_down[s].copy_(torch.from_numpy(self.wd[e]))
+            pool.w_gu[s].copy_(self.host[0][e])
+            pool.w_down[s].copy_(self.host[1][e])
 
 
 class Fp8Bank:
-    """E FP8 experts (codes + 128x128 scales) drawn on `device`, pinned host copy."""
+    """E FP8 experts (codes + 128x128 scales) drawn on `device`; row-major for the
+    oracle, packed pinned banks (+ scales) for the library."""
 
     def __init__(self, cfg_id, E, H, I, std=0.02, layer=0, device="cpu", pin=True):
         self.E, self.H, self.I = E, H, I
@@ -76,8 +94,12 @@ class Fp8Bank:
             ex = gen.expert_fp8_torch(gen.torch_seed(cfg_id, gen.S_WEIGHTS, layer, e), H, I, std, device=device)
             for n in names:
                 self.t[n][e].copy_(ex[n])
-        self.host = [self.t[n] for n in names]
+        self.repack(pin)
         self._cache = {}
+
+    def repack(self, pin=True):
+        gu, dp = pack_to_host(1, self.t["gate"], self.t["up"], self.t["down"], pin=pin)
+        self.host = [gu, dp, self.t["s_gate"], self.t["s_up"], self.t["s_down"]]
 
     def expert64(self, e):
         if e not in self._cache:
@@ -92,9 +114,8 @@ class Fp8Bank:
 
     def load_slots(self, pool, slot_of_expert):
         for e, s in slot_of_expert.items():
-            pool.w_gate[s].copy_(self.t["gate"][e])
-            pool.w_up[s].copy_(self.t["up"][e])
-            pool.w_down[s].copy_(self.t["down"][e])
+            pool.w_gu[s].copy_(self.host[0][e])
+            pool.w_down[s].copy_(self.host[1][e])
             pool.s_gate[s].copy_(self.t["s_gate"][e])
             pool.s_up[s].copy_(self.t["s_up"][e])
             pool.s_down[s].copy_(self.t["s_down"][e])

@@ -48,7 +48,7 @@ def test_struct_layouts_match_header():
 #include "moe.h"
 int main(void) {
   printf("%zu %zu %zu %zu\n", sizeof(moe_slots), sizeof(moe_host_pool), sizeof(moe_cache_cfg), sizeof(moe_step_out));
-  printf("%zu %zu %zu\n", offsetof(moe_slots, w_gate), offsetof(moe_slots, s_down), offsetof(moe_cache_cfg, bh));
+  printf("%zu %zu %zu\n", offsetof(moe_slots, w_gate_up), offsetof(moe_slots, s_down), offsetof(moe_cache_cfg, bh));
   printf("%zu\n", offsetof(moe_step_out, counts));
   return 0;
 }
@@ -64,7 +64,7 @@ int main(void) {
     vals = [int(v) for v in out]
     assert vals[:4] == [ctypes.sizeof(b.Slots), ctypes.sizeof(b.HostPool), ctypes.sizeof(b.CacheCfg),
                         ctypes.sizeof(b.StepOutC)]
-    assert vals[4:] == [b.Slots.w_gate.offset, b.Slots.s_down.offset, b.CacheCfg.bh.offset,
+    assert vals[4:] == [b.Slots.w_gate_up.offset, b.Slots.s_down.offset, b.CacheCfg.bh.offset,
                         b.StepOutC.counts.offset]
 
 

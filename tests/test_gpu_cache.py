@@ -73,9 +73,8 @@ class Harness:
         # host banks: one distinct row per logical id so copies are checkable
         rng = np.random.default_rng(L * 7 + E)
         n = L * E
-        self.hb = [pinned(rng.integers(0, 1 << 16, size=(n, I, H), dtype=np.uint16)),
-                   pinned(rng.integers(0, 1 << 16, size=(n, I, H), dtype=np.uint16)),
-                   pinned(rng.integers(0, 1 << 16, size=(n, H, I), dtype=np.uint16))]
+        self.hb = [pinned(rng.integers(0, 1 << 16, size=(n, 2 * I * H), dtype=np.uint16)),
+                   pinned(rng.integers(0, 1 << 16, size=(n, H * I), dtype=np.uint16))]
         self.host = b.HostPoolTables(self.hb, lambda i: i, n)
         self.cache = b.Cache(L, E, k, T_max, self.pool, self.host, bp, bh)
         self.out = b.StepOut(T_max, k, E)
@@ -124,7 +123,7 @@ class Harness:
         slot_id = self.cache.read_state()[0]
         for s, lid in enumerate(slot_id):
             if lid >= 0:
-                for k, bank in enumerate((self.pool.w_gate, self.pool.w_up, self.pool.w_down)):
+                for k, bank in enumerate((self.pool.w_gu, self.pool.w_down)):
                     assert torch.equal(bank[s].cpu(), self.hb[k][lid]), (s, lid, k)
 
 
@@ -235,7 +234,7 @@ def test_argument_errors():
         hz.cache.step(1, dev(np.zeros((1, 2), np.int32)), hz.out)        # layer out of range
     with pytest.raises(b.MoeError):
         hz.cache.step(0, dev(np.zeros((3, 2), np.int32)), hz.out)        # T > T_max
-    pageable = [torch.zeros((8, 32, 32), dtype=torch.uint16) for _ in range(3)]
+    pageable = [torch.zeros((8, 2 * 32 * 32), dtype=torch.uint16), torch.zeros((8, 32 * 32), dtype=torch.uint16)]
     tabs = b.HostPoolTables.__new__(b.HostPoolTables)
     import ctypes
     arrs = [(ctypes.c_void_p * 8)(*[t.data_ptr()] * 8) for t in pageable]

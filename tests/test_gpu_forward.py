@@ -93,6 +93,7 @@ def test_decode_fp8_special_codes():
         mask = torch.from_numpy(rng.random(t.shape) < 0.2)
         sub = torch.from_numpy(rng.integers(0, 8, t.shape).astype(np.uint8) | (rng.integers(0, 2, t.shape).astype(np.uint8) << 7))
         t[mask] = sub[mask]
+    bank.repack()
     pool = _slots_identity(b, bank, b.W_FP8_B128)
     x = gen.activations_bf16(rng, 3, 256)
     ids = np.array([[0, 1]] * 3)
@@ -253,3 +254,36 @@ def test_tiny_layer_end_to_end():
                              route.topk_softmax(lg, c.k)[1], bank.expert64)
         check_layer(y, ref, "tiny end to end")
         cache.destroy()
+
+
+@pytest.mark.parametrize("wtype,H,I", [(0, 64, 32), (0, 256, 96), (1, 256, 128)])
+def test_pack_matches_brick_format(wtype, H, I):
+    """moe_pack_weights against the brick format stated in include/moe.h."""
+    b = binding()
+    rng = np.random.default_rng(H + I)
+    dt = np.uint16 if wtype == 0 else np.uint8
+    hi = 1 << 16 if wtype == 0 else 1 << 8
+    n = 2
+    wg = rng.integers(0, hi, (n, I, H), dtype=dt)
+    wu = rng.integers(0, hi, (n, I, H), dtype=dt)
+    wd = rng.integers(0, hi, (n, H, I), dtype=dt)
+    gu, dp = b.pack_weights(wtype, dev(wg), dev(wu), dev(wd))
+    gu, dp = gu.cpu().numpy(), dp.cpu().numpy()
+    KB = 32 if wtype == 0 else 64
+    per = KB // 4
+
+    def brick_elem(N, K, t, kt, lane, e):
+        return ((t * (K // KB) + kt) * 64 + lane) * per + e
+
+    for ex in range(n):
+        for row in range(0, 2 * I, 7):
+            for col in range(0, H, 5):
+                t, rr = row // 16, row % 16
+                kt, j, e = col // KB, (col % KB) // per, col % per
+                src = wg[ex, 8 * t + rr, col] if rr < 8 else wu[ex, 8 * t + rr - 8, col]
+                assert gu[ex, brick_elem(2 * I, H, t, kt, 16 * j + rr, e)] == src
+        for row in range(0, H, 3):
+            for col in range(0, I, 7):
+                t, rr = row // 16, row % 16
+                kt, j, e = col // KB, (col % KB) // per, col % per
+                assert dp[ex, brick_elem(H, I, t, kt, 16 * j + rr, e)] == wd[ex, row, col]

@@ -6,7 +6,7 @@ import torch
 
 from harness import gen
 from oracle import route, lru, numerics, ffn
-from tests.layer_setup import binding, dev, pinned, check_layer, oracle_partials
+from tests.layer_setup import binding, dev, pinned, check_layer, oracle_partials, pack_to_host
 
 pytestmark = pytest.mark.gpu
 
@@ -19,7 +19,8 @@ def _layer_banks(L, E, H, I, cfg_id=55):
     wd = np.empty((L * E, H, I), np.uint16)
     for i in range(L * E):
         wg[i], wu[i], wd[i] = gen.expert_bf16(rng, H, I, 0.02)
-    return (wg, wu, wd), [pinned(a) for a in (wg, wu, wd)]
+    packed = pack_to_host(0, *[torch.from_numpy(a) for a in (wg, wu, wd)])
+    return (wg, wu, wd), list(packed)
 
 
 def test_prefill_double_buffer_overlap():
@@ -66,8 +67,8 @@ def test_prefill_double_buffer_overlap():
         v = pf.acquire(l, compute)
         base = C - 2 * E + (l % 2) * E
         for e in range(E):
-            assert torch.equal(pool.w_gate[base + e].cpu(), host_t[0][l * E + e])
-            assert torch.equal(pool.w_down[base + e].cpu(), host_t[2][l * E + e])
+            assert torch.equal(pool.w_gu[base + e].cpu(), host_t[0][l * E + e])
+            assert torch.equal(pool.w_down[base + e].cpu(), host_t[1][l * E + e])
     pf.destroy()
     assert np.all(cache.read_state()[0][C - 2 * E:] == -1)
     cache.destroy()
@@ -167,7 +168,7 @@ def test_graph_capture_replays_equal_eager():
     sa, sb = A["cache"].read_state(), B["cache"].read_state()
     for u, v in zip(sa[:3], sb[:3]):
         assert np.array_equal(u, v)
-    assert torch.equal(A["pool"].w_gate, B["pool"].w_gate)
+    assert torch.equal(A["pool"].w_gu, B["pool"].w_gu)
 
 
 def test_forward_deterministic():
