@@ -34,6 +34,40 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+class HipEvents:
+    """Timing events created with hipEventDisableSystemFence: a record on a busy
+    stream costs far less GPU time than torch's default events (no
+    system-scope cache release), so the brackets disturb the path less."""
+
+    def __init__(self, n):
+        import ctypes
+        import torch
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.lib.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) == 0
+            self.ev.append(e)
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self._f = ctypes.c_float()
+
+    def record(self, i):
+        self.lib.hipEventRecord(self.ev[i], self.stream)
+
+    def ms(self, a, b):
+        import ctypes
+        assert self.lib.hipEventElapsedTime(ctypes.byref(self._f), self.ev[a], self.ev[b]) == 0
+        return self._f.value
+
+    def close(self):
+        for e in self.ev:
+            self.lib.hipEventDestroy(e)
+
+
 def parse():
     p = argparse.ArgumentParser()
     p.add_argument("--gpus", type=int, default=1)
@@ -43,6 +77,9 @@ def parse():
     p.add_argument("--cpu-seconds", type=float, default=15.0)
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-fp8", action="store_true", help="skip the FP8 decode and FP8 double-buffered prefill runs")
+    p.add_argument("--fp8-steps", type=int, default=64)
+    p.add_argument("--fp8-warmup", type=int, default=32)
     return p.parse_args()
 
 
@@ -75,17 +112,17 @@ def run_decode(b, K, W):
     y = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
     pick = out.pick_slot.view(1, k)
 
-    def layer_step(s, l, ev=None):
+    def layer_step(s, l, ev=None, i=0):
         b.route_topk(lg[s, l], k, ids, w)
         cache.step(l, ids, out, copy=False)
         if ev:
-            ev[0].record()
+            ev.record(3 * i)
         cache.fill(out)
         if ev:
-            ev[1].record()
+            ev.record(3 * i + 1)
         b.expert_forward(pool.c, x[s, l], pick, w, b.FWD_DECODE, ws, y=yg)
         if ev:
-            ev[2].record()
+            ev.record(3 * i + 2)
         b.merge_partial(yg, yh[l], y_out=y[l])
 
     log("decode: warmup %d steps" % W)
@@ -94,28 +131,29 @@ def run_decode(b, K, W):
             layer_step(s, l)
     torch.cuda.synchronize()
     c0 = cache.read_state()[4].astype(np.int64)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(K * L)]
+    ev = HipEvents(3 * K * L)
     log("decode: timing %d steps" % K)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     i = 0
     for s in range(W, W + K):
         for l in range(L):
-            layer_step(s, l, evs[i])
+            layer_step(s, l, ev, i)
             i += 1
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     c1 = cache.read_state()[4].astype(np.int64)
     d = c1 - c0                                          # calls, uniq, hits, misses, fills, host
-    fill_s = sum(e[0].elapsed_time(e[1]) for e in evs) / 1e3
-    fwd_s = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3
+    fill_s = sum(ev.ms(3 * i, 3 * i + 1) for i in range(K * L)) / 1e3
+    fwd_s = sum(ev.ms(3 * i + 1, 3 * i + 2) for i in range(K * L)) / 1e3
+    ev.close()
     n_g = int(d[2] + d[4])
     gpu_bytes = n_g * S
     hbm_s = wall - fill_s
     res = dict(
         value=gpu_bytes / hbm_s / 1e9,
         ms_per_step=hbm_s / K * 1e3,
-        roofline=dict(kernel="moe_expert_forward decode (grouped GEMV: plan + gate/up + down launches)",
+        roofline=dict(kernel="moe_expert_forward decode (grouped GEMV: gate/up + down launches)",
                       bound="hbm", achieved=gpu_bytes / fwd_s / 1e9, peak=PEAK_HBM_GBPS, unit="GB/s",
                       bytes_per_launch=gpu_bytes / (K * L), launches=K * L,
                       avg_launch_us=fwd_s / (K * L) * 1e6, traffic=None),
@@ -157,27 +195,28 @@ def run_prefill(b, reps):
     y = torch.empty((T, H), dtype=torch.float32, device="cuda")
     flops = 6.0 * H * I * T * k
 
-    def run(ev=None):
+    def run(ev=None, r=0):
         if ev:
-            ev[0].record()
+            ev.record(3 * r)
         b.route_topk(lg, k, ids, w)
         if ev:
-            ev[1].record()
+            ev.record(3 * r + 1)
         b.expert_forward(pool.c, x, ids, w, b.FWD_PREFILL, ws, y=y)
         if ev:
-            ev[2].record()
+            ev.record(3 * r + 2)
 
     for _ in range(3):
         run()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+    ev = HipEvents(3 * reps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for r in range(reps):
-        run(evs[r])
+        run(ev, r)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    fwd_s = sum(e[1].elapsed_time(e[2]) for e in evs) / 1e3 / reps
-    layer_s = sum(e[0].elapsed_time(e[2]) for e in evs) / 1e3 / reps
+    fwd_s = sum(ev.ms(3 * r + 1, 3 * r + 2) for r in range(reps)) / 1e3 / reps
+    layer_s = sum(ev.ms(3 * r, 3 * r + 2) for r in range(reps)) / 1e3 / reps
+    ev.close()
     ach = flops / fwd_s / 1e12
     return dict(
         workload="prefill_bf16: 8192 tokens, hidden 2048, 128 experts, top-8 of x.W_r, SwiGLU I 768, BF16, all experts resident",
@@ -187,6 +226,189 @@ def run_prefill(b, reps):
                       bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                       frac=ach / PEAK_BF16_TFLOPS, avg_launch_us=fwd_s * 1e6, traffic=None),
     )
+
+
+# ---------------------------------------------------------------- FP8 pools
+def fp8_bank_packed(b, cfg_id, E, H, I, std, layer, out_gu, out_dp, out_s):
+    """Draw E FP8 experts on the GPU, pack them, copy into the host tensors at rows [0, E)."""
+    import torch
+    from harness import gen
+    for e in range(E):
+        ex = gen.expert_fp8_torch(gen.torch_seed(cfg_id, gen.S_WEIGHTS, layer, e), H, I, std, device="cuda")
+        gu, dp = b.pack_weights(b.W_FP8_B128, ex["gate"][None], ex["up"][None], ex["down"][None])
+        out_gu[e].copy_(gu[0])
+        out_dp[e].copy_(dp[0])
+        for i, n in enumerate(("s_gate", "s_up", "s_down")):
+            out_s[i][e].copy_(ex[n])
+    torch.cuda.synchronize()
+
+
+def run_decode_fp8(b, K, W, Ts=(1, 4, 16)):
+    """Decode FP8 workload: 58-layer pool (layer 0 real, layers 1-57 metadata
+    only), H 7168, E 256, top-8, I 2048, 1633 slots, 11.8:47.5; one step = the
+    58 layer calls of one token step; the MALL is flushed before layer 0's GEMV."""
+    import torch
+    from harness import gen, CONFIGS
+    c = CONFIGS["decode_fp8"]
+    L, E, k, H, I, C = c.L, c.E, c.k, c.H, c.I, c.C
+    S = 3 * H * I + 3 * (I // 128) * (H // 128) * 4
+    log("decode fp8: drawing and packing layer 0 (%d experts)" % E)
+    gu_h = torch.empty((E, 2 * I * H), dtype=torch.uint8, pin_memory=True)
+    dp_h = torch.empty((E, H * I), dtype=torch.uint8, pin_memory=True)
+    s_h = [torch.empty((E, I // 128, H // 128), dtype=torch.float32, pin_memory=True),
+           torch.empty((E, I // 128, H // 128), dtype=torch.float32, pin_memory=True),
+           torch.empty((E, H // 128, I // 128), dtype=torch.float32, pin_memory=True)]
+    fp8_bank_packed(b, c.cfg_id, E, H, I, c.w_std, 0, gu_h, dp_h, s_h)
+    host = b.HostPoolTables([gu_h, dp_h] + s_h, lambda i: i % E, L * E)   # layers >= 1 never copy
+    pool = b.SlotPool(C, H, I, b.W_FP8_B128)
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+    out_all = {}
+    n = W + K
+    for T in Ts:
+        picks, logits = gen.decode_trace(c.cfg_id, L, n, E, k, c.p_keep, T=T, salt=T)
+        lg = torch.from_numpy(logits).cuda()                        # [n, L, T, E]
+        x = torch.from_numpy(gen.activations_bf16(gen.np_rng(c.cfg_id, gen.S_ACT, T), n * T, H)).cuda().view(n, T, H)
+        cache = b.Cache(L, E, k, T, pool, host, c.bp, c.bh)
+        out = b.StepOut(T, k, E)
+        ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+        ws = b.forward_workspace(T, k, H, I, C, b.FWD_DECODE)
+        yg = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        yh = torch.zeros((T, H), dtype=torch.float32, device="cuda")
+        y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+        pick = out.pick_slot.view(T, k)
+        ev = HipEvents(3 * K)
+        fwd_counts = np.zeros(2, np.int64)
+
+        def step(s, i=None):
+            for l in range(L):
+                b.route_topk(lg[s, l], k, ids, w)
+                cache.step(l, ids, out, copy=False)
+                if l == 0:
+                    flush.add_(1.0)                                  # evict the MALL (512 MB read + write)
+                    if i is not None:
+                        ev.record(3 * i)
+                    cache.fill(out)
+                    if i is not None:
+                        ev.record(3 * i + 1)
+                    b.expert_forward(pool.c, x[s], pick, w, b.FWD_DECODE, ws, y=yg)
+                    if i is not None:
+                        ev.record(3 * i + 2)
+                    b.merge_partial(yg, yh, y_out=y)
+                    if i is not None:
+                        cnt = out.counts                                # read after the run
+                        fwd_counts_dev.append(cnt.clone())
+
+        fwd_counts_dev = []
+        for s in range(W):
+            step(s)
+        torch.cuda.synchronize()
+        c0 = cache.read_state()[4].astype(np.int64)
+        fwd_counts_dev.clear()
+        t0 = time.perf_counter()
+        for i, s in enumerate(range(W, n)):
+            step(s, i)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        c1 = cache.read_state()[4].astype(np.int64)
+        cnts = torch.stack(fwd_counts_dev).cpu().numpy()
+        n_g = int(cnts[:, 1].sum() + cnts[:, 4].sum())                  # layer-0 hits + fills
+        fill_s = sum(ev.ms(3 * i, 3 * i + 1) for i in range(K)) / 1e3
+        fwd_s = sum(ev.ms(3 * i + 1, 3 * i + 2) for i in range(K)) / 1e3
+        ev.close()
+        d = c1 - c0
+        ach = n_g * S / fwd_s / 1e9
+        out_all["T%d" % T] = dict(
+            expert_GBps=ach, frac_hbm=ach / PEAK_HBM_GBPS, experts_per_forward=n_g / K,
+            avg_forward_us=fwd_s / K * 1e6, bytes_per_expert=S,
+            layer0_fill_GBps=(cnts[:, 4].sum() * S / fill_s / 1e9) if fill_s > 0 else None,
+            miss_rate_all_layers=float(d[3] / d[1]), wall_ms_per_step=wall / K * 1e3)
+        cache.destroy()
+        del lg, x, ws
+    return dict(workload="decode_fp8: 58-layer pool (layer 0 real, 1-57 metadata only), H 7168, E 256, top-8, "
+                         "I 2048, FP8 E4M3 + 128x128 scales, 1633 slots (11%), B_P:B_H 11.8:47.5, sticky p 0.5",
+                steps=K, warmup=W, by_T=out_all)
+
+
+def run_prefill_fp8(b):
+    """Prefill FP8 workload: 8192 tokens x 4 layers, H 7168, E 256, top-8,
+    I 2048; all 4 x 256 experts in a pinned host pool; two full-layer buffers
+    of the slot pool alternate; run once overlapped and once serial."""
+    import torch
+    from harness import gen, CONFIGS
+    c = CONFIGS["prefill_fp8"]
+    T, NL, H, I, E, k = c.T, c.layers, c.H, c.I, c.E, c.k
+    log("prefill fp8: drawing and packing %d x %d experts" % (NL, E))
+    gu_h = torch.empty((NL * E, 2 * I * H), dtype=torch.uint8, pin_memory=True)
+    dp_h = torch.empty((NL * E, H * I), dtype=torch.uint8, pin_memory=True)
+    s_h = [torch.empty((NL * E, I // 128, H // 128), dtype=torch.float32, pin_memory=True),
+           torch.empty((NL * E, I // 128, H // 128), dtype=torch.float32, pin_memory=True),
+           torch.empty((NL * E, H // 128, I // 128), dtype=torch.float32, pin_memory=True)]
+    for l in range(NL):
+        fp8_bank_packed(b, c.cfg_id, E, H, I, c.w_std, l, gu_h[l * E:(l + 1) * E], dp_h[l * E:(l + 1) * E],
+                        [t[l * E:(l + 1) * E] for t in s_h])
+    host = b.HostPoolTables([gu_h, dp_h] + s_h, lambda i: i, NL * E)
+    pool = b.SlotPool(2 * E, H, I, b.W_FP8_B128)
+    cache = b.Cache(NL, E, k, 1, pool, host, 118, 475)
+    pf = b.PrefillPool(cache)
+    log("prefill fp8: activations and router logits")
+    xs, lgs = [], []
+    for l in range(NL):
+        xb = gen.activations_bf16(gen.np_rng(c.cfg_id, gen.S_ACT, l), T, H)
+        wr = torch.from_numpy(gen.router_matrix(gen.np_rng(c.cfg_id, gen.S_ROUTER, l), H, E, c.router_std))
+        xf = torch.from_numpy(xb).cuda().view(torch.bfloat16).to(torch.float64)
+        lgs.append((xf @ wr.cuda().to(torch.float64)).to(torch.float32).contiguous())
+        xs.append(torch.from_numpy(xb).cuda())
+        del xf
+    ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    ws = b.forward_workspace(T, k, H, I, E, b.FWD_PREFILL)
+    y = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    flops = 6.0 * H * I * T * k
+    layer_bytes = E * (3 * H * I + 3 * (I // 128) * (H // 128) * 4)
+    compute = torch.cuda.current_stream()
+    copy = torch.cuda.Stream()
+
+    def run(serial):
+        ev = HipEvents(2 * NL)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        pf.prefetch(0, copy)
+        if not serial:
+            pf.prefetch(1, copy)
+        for l in range(NL):
+            if serial and l > 0:
+                copy.wait_stream(compute)
+                pf.prefetch(l, copy)
+            view = pf.acquire(l, compute)
+            b.route_topk(lgs[l], k, ids, w)
+            ev.record(2 * l)
+            b.expert_forward(view, xs[l], ids, w, b.FWD_PREFILL, ws, y=y)
+            ev.record(2 * l + 1)
+            pf.release(l, compute)
+            if not serial and l + 2 < NL:
+                pf.prefetch(l + 2, copy)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        fwd = [ev.ms(2 * l, 2 * l + 1) / 1e3 for l in range(NL)]
+        ev.close()
+        return wall, fwd
+
+    run(False)                                                       # warm-up
+    wall_o, fwd_o = run(False)
+    wall_s, fwd_s = run(True)
+    pf.destroy()
+    cache.destroy()
+    ach = flops / (sum(fwd_o) / NL) / 1e12
+    return dict(workload="prefill_fp8: 8192 tokens x 4 layers, H 7168, E 256, top-8 of x.W_r, I 2048, FP8 E4M3 + "
+                         "128x128 scales, pinned host pool, two full-layer slot buffers",
+                ms_per_layer_overlapped=wall_o / NL * 1e3, ms_per_layer_serial=wall_s / NL * 1e3,
+                overlap_gain=wall_s / wall_o, h2d_bytes_per_layer=layer_bytes,
+                h2d_GBps_bound=layer_bytes / (wall_o / NL) / 1e9,
+                forward_ms_per_layer=sum(fwd_o) / NL * 1e3,
+                roofline=dict(kernel="moe_expert_forward prefill FP8 (sort + gate/up GEMM + down GEMM + combine)",
+                              bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                              frac=ach / PEAK_BF16_TFLOPS))
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
@@ -261,6 +483,12 @@ def main():
     }
     if not a.no_prefill:
         line["prefill"] = run_prefill(b, a.prefill_reps)
+    if not a.no_fp8:
+        line["decode_fp8"] = run_decode_fp8(b, a.fp8_steps, a.fp8_warmup)
+        torch.cuda.empty_cache()
+        if not a.no_prefill:
+            line["prefill_fp8"] = run_prefill_fp8(b)
+            torch.cuda.empty_cache()
     if not a.no_cpu_baseline:
         log("cpu baseline: oracle for %.0f s" % a.cpu_seconds)
         line["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
