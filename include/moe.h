@@ -249,11 +249,13 @@ moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int32_t H, int3
  *          w[t,j] * W_down (silu(W_gate x_t) * (W_up x_t))   (slot's weights)
  * x: device BF16 [T, H]; pick_slot: device int32 [T, k] (slot index in
  * `slots`, -1 = skip); w: device float32 [T, k]; y: device float32 [T, H],
- * fully overwritten.  FP8 weights are expanded to BF16 in registers by
- * integer bit operations (exact for all 256 codes) and each 128x128 tile's
- * scale is applied once to its block partial sum.  Accumulation is FP32; the
+ * fully overwritten.  FP8 weights are expanded exactly to BF16 in registers
+ * (decode: the gfx950 two-codes-per-instruction E4M3 -> BF16 conversion with
+ * unit scale; prefill: integer bit operations) and each 128x128 tile's scale
+ * is applied once to its block partial sum.  Accumulation is FP32; the
  * SwiGLU activations h are rounded to BF16 before the down projection.
- *   mode MOE_FWD_DECODE: T <= 16 (grouped GEMV streaming each slot once).
+ *   mode MOE_FWD_DECODE: T <= 16 and T*k <= 256 (grouped GEMV streaming each
+ *     slot once; y is the same bits on every run).
  *   mode MOE_FWD_PREFILL: any T (tokens sorted by slot, grouped GEMM).
  * ws: device workspace of moe_forward_workspace_bytes(T_max >= T, ...).
  * Requires H, I multiples of 128 (FP8) or of 32 (BF16).  Capturable.
@@ -304,10 +306,11 @@ moe_status moe_prefill_destroy(moe_prefill_t p, hipStream_t stream);
 
 
 /*
- * Expand n E4M3FN codes to BF16 bit patterns with the exact integer routine
- * the FP8 kernels use ([OSDI] section 4.2: exponent moved by the bias
- * difference 120, mantissa zero-filled; zero, subnormal and NaN codes
- * patched).  codes: device uint8 [n]; out: device uint16 [n].  Capturable.
+ * Expand n E4M3FN codes to BF16 bit patterns with the conversion the decode
+ * kernels run in registers ([OSDI] section 4.2: every E4M3 value is exactly a
+ * BF16 value; here gfx950's E4M3 -> BF16 pack conversion with unit scale,
+ * NaN codes give a BF16 NaN).  codes: device uint8 [n]; out: device uint16
+ * [n].  Capturable.
  */
 moe_status moe_e4m3_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream);
 

@@ -143,6 +143,21 @@ __device__ __forceinline__ void e4m3x16_to_bf16(const u32x4& q, u32x4& ev, u32x4
   od = u32x4{o0, o1, o2, o3};
 }
 
+// 16 codes (one 128-bit load) -> 16 BF16 in their natural order: `lo` holds
+// codes 0..7 and `hi` codes 8..15.  gfx950 converts two OCP E4M3 codes to two
+// BF16 per instruction; with the scale operand 1.0 the result is the code's
+// exact value (every finite E4M3 value is a BF16 value), NaN codes give NaN.
+template <bool HIGH>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t d) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(d, 1.0f, HIGH));
+}
+__device__ __forceinline__ void e4m3x16_to_bf16_nat(const u32x4& q, u32x4& lo, u32x4& hi) {
+  lo = u32x4{e4m3x2_to_bf16x2<false>(q[0]), e4m3x2_to_bf16x2<true>(q[0]), e4m3x2_to_bf16x2<false>(q[1]),
+             e4m3x2_to_bf16x2<true>(q[1])};
+  hi = u32x4{e4m3x2_to_bf16x2<false>(q[2]), e4m3x2_to_bf16x2<true>(q[2]), e4m3x2_to_bf16x2<false>(q[3]),
+             e4m3x2_to_bf16x2<true>(q[3])};
+}
+
 __device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
 
 }  // namespace moe

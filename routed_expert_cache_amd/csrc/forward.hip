@@ -20,6 +20,9 @@
 // sums each token's k rows in pick order.
 #include "common.h"
 
+#include <algorithm>
+#include <mutex>
+
 namespace moe {
 
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *reinterpret_cast<const u32x4*>(p); }
@@ -83,8 +86,16 @@ __global__ __launch_bounds__(256) void pack_kernel(int fp8, int H, int I, int n,
 }
 
 // ================================================================ decode
+// Both launches are grids of resident workgroups that walk a task list
+// round-robin.  Every weight and activation load is a raw buffer load whose
+// offset is pushed past the buffer's end when the step does not exist, so the
+// hardware returns zeros without touching memory: each wave issues one fixed
+// sequence of loads, kept D steps (2 bricks each) ahead of the MFMAs in a
+// register ring, with no branch around any load.
 constexpr int kDecTok = 16;     // MFMA N: tokens of one decode call
-constexpr int kDecPmax = 512;   // T * k picks
+constexpr int kDecPmax = 256;   // T * k picks
+constexpr int kDecPPL = kDecPmax / 64;
+constexpr uint32_t kOOB = 0x80000000u;   // buffer offset past the end of every decode buffer
 
 struct DecArgs {
   const void* w_gu;
@@ -97,258 +108,342 @@ struct DecArgs {
   const int32_t* pick_slot;  // [T*k]
   const float* w;            // [T*k]
   float* y;                  // [T][H]
-  const uint16_t* xb;        // B-operand source [T][H]: x (BF16) or x permuted even/odd (FP8)
-  uint16_t* xperm;           // workspace [T][H] (FP8 only)
-  uint16_t* h;               // workspace [G_max][16][I]
+  uint16_t* h;               // workspace [G_max][16][I] BF16
   int G_max;
-  int kp2;                   // K-parts of the down projection per expert
 };
 
-// Group plan in LDS: groups are the distinct valid slots of pick_slot in
-// order of first appearance.  s_gslot[g] = slot of group g; if s_gw is not
-// NULL, s_gw[g*16 + t] = gate weight of token t's pick of group g (0 if
-// none).  Returns the number of groups.  Contains barriers; all threads call.
-template <int NT>
-__device__ int plan_groups(const DecArgs& a, int* s_ps, int* s_first, int* s_gslot, float* s_gw, int* s_n) {
-  const int P = a.T * a.k, tid = threadIdx.x;
-  for (int p = tid; p < P; p += NT) {
-    const int s = a.pick_slot[p];
-    s_ps[p] = (s >= 0 && s < a.n_slots) ? s : -1;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+__device__ __forceinline__ u32x4 bload_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
+}
+// Offset v if c, else past the end of the buffer.  The empty asm keeps the
+// choice a register select: without it the compiler may split the load into
+// two branches writing one register, and order them with a full wait on all
+// loads in flight.
+__device__ __forceinline__ uint32_t oob_sel(bool c, uint32_t v) {
+  uint32_t o = c ? v : kOOB;
+  asm volatile("" : "+v"(o));
+  return o;
+}
+__device__ __forceinline__ float lane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
+// Group plan, computed by one wave: groups are the distinct valid slots of
+// pick_slot in order of first appearance.  s_gslot[g] = slot of group g; if
+// s_gw is not NULL, s_gw[g*16 + t] = gate weight of token t's pick of group g
+// (0 if token t did not pick it).  Writes *s_G.  s_tab is LDS scratch of
+// kPlanTab words: an open-addressing table slot -> earliest pick holding it
+// (key in the high half, pick index in the low half, so atomicMin keeps the
+// earliest pick).  No barrier inside.
+constexpr int kPlanTab = 2 * kDecPmax;
+__device__ void wave_plan(const int32_t* __restrict__ pick_slot, const float* __restrict__ w, int P, int k,
+                          int n_slots, int G_max, int* s_gslot, float* s_gw, int* s_G, unsigned long long* s_tab) {
+  const int lane = threadIdx.x & 63;
+  constexpr unsigned long long kEmpty = ~0ull;
+  int sl[kDecPPL], hs[kDecPPL];
+#pragma unroll
+  for (int h = 0; h < kDecPPL; ++h) {
+    const int p = lane + 64 * h;
+    const int s = p < P ? pick_slot[p] : -1;
+    sl[h] = (s >= 0 && s < n_slots) ? s : -1;
   }
+  for (int i = lane; i < kPlanTab; i += 64) s_tab[i] = kEmpty;
   if (s_gw)
-    for (int i = tid; i < a.G_max * kDecTok; i += NT) s_gw[i] = 0.f;
-  if (tid == 0) *s_n = 0;
-  __syncthreads();
-  for (int p = tid; p < P; p += NT) {
-    const int s = s_ps[p];
-    bool first = s >= 0;
-    for (int q = 0; q < p && first; ++q) first = s_ps[q] != s;
-    s_first[p] = first;
-    if (first) atomicAdd(s_n, 1);
+    for (int i = lane; i < G_max * kDecTok; i += 64) s_gw[i] = 0.f;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+#pragma unroll
+  for (int h = 0; h < kDecPPL; ++h) {
+    hs[h] = -1;
+    if (sl[h] < 0) continue;
+    const unsigned long long want = ((unsigned long long)(uint32_t)sl[h] << 32) | (uint32_t)(lane + 64 * h);
+    int pos = (int)(((uint32_t)sl[h] * 2654435761u) >> 23) & (kPlanTab - 1);
+    for (int probe = 0; probe < kPlanTab; ++probe) {
+      unsigned long long cur = atomicCAS(&s_tab[pos], kEmpty, want);
+      if (cur == kEmpty || (cur >> 32) == (uint32_t)sl[h]) {
+        if (cur != kEmpty) atomicMin(&s_tab[pos], want);
+        hs[h] = pos;
+        break;
+      }
+      pos = (pos + 1) & (kPlanTab - 1);
+    }
   }
-  __syncthreads();
-  for (int p = tid; p < P; p += NT) {
-    const int s = s_ps[p];
-    if (s < 0) continue;
-    int fq = p;
-    if (!s_first[p])
-      for (int q = 0; q < p; ++q)
-        if (s_ps[q] == s) { fq = q; break; }
+  __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+  int fq[kDecPPL];
+  bool first[kDecPPL];
+#pragma unroll
+  for (int h = 0; h < kDecPPL; ++h) {
+    fq[h] = hs[h] >= 0 ? (int)(uint32_t)s_tab[hs[h]] : lane + 64 * h;
+    first[h] = hs[h] >= 0 && fq[h] == lane + 64 * h;
+  }
+  uint64_t m[kDecPPL];
+  int base[kDecPPL + 1];
+  base[0] = 0;
+#pragma unroll
+  for (int h = 0; h < kDecPPL; ++h) {
+    m[h] = __ballot(first[h]);
+    base[h + 1] = base[h] + __popcll(m[h]);
+  }
+#pragma unroll
+  for (int h = 0; h < kDecPPL; ++h) {
+    if (hs[h] < 0) continue;
+    const int f = fq[h];
     int g = 0;
-    for (int q = 0; q < fq; ++q) g += s_first[q];
-    if (fq == p) s_gslot[g] = s;
-    if (s_gw) s_gw[g * kDecTok + p / a.k] = a.w[p];
+#pragma unroll
+    for (int h2 = 0; h2 < kDecPPL; ++h2)
+      if ((f >> 6) == h2) g = base[h2] + __popcll(m[h2] & ((1ull << (f & 63)) - 1ull));
+    if (first[h]) s_gslot[g] = sl[h];
+    if (s_gw) s_gw[g * kDecTok + (lane + 64 * h) / k] = w[lane + 64 * h];
   }
-  __syncthreads();
-  return *s_n;
+  if (lane == 0) *s_G = base[kDecPPL];
 }
 
-// FP8 only: x -> x permuted even/odd inside each 16-group, 16 elements per thread
-__global__ __launch_bounds__(256) void dec_xperm_kernel(DecArgs a) {
-  const int c = blockIdx.x * 256 + threadIdx.x;
-  const int per_row = a.H / 16;
-  if (c >= a.T * per_row) return;
-  const int t = c / per_row, kc = (c % per_row) * 16;
-  const u32x4 v0 = ld16(a.x + (size_t)t * a.H + kc);
-  const u32x4 v1 = ld16(a.x + (size_t)t * a.H + kc + 8);
-  u32x4 ev, od;
-  split_even_odd(v0, v1, ev, od);
-  uint16_t* dst = a.xperm + (size_t)t * a.H + kc;
-  *reinterpret_cast<u32x4*>(dst) = ev;
-  *reinterpret_cast<u32x4*>(dst + 8) = od;
-}
-
-// gate/up + SwiGLU.  One workgroup per (gate/up brick row t = 8 rows of I,
-// group).  The brick's A rows 0..7 are gate rows and 8..15 the same up rows,
-// so one fragment holds gate and up of the same outputs.  Waves split K and
-// issue a batch of contiguous 1 KB brick loads (plus the matching x loads)
-// before its MFMAs.  Workgroups of group 0 also zero y for the down launch.
-template <bool FP8, int NW>
-__global__ __launch_bounds__(NW * 64) void dec_gateup_kernel(DecArgs a) {
-  __shared__ int s_ps[kDecPmax], s_first[kDecPmax], s_gslot[kDecPmax];
-  __shared__ int s_n;
-  __shared__ f32x4 red[NW][64];
-  if (blockIdx.y == 0)
-    for (int i = blockIdx.x * NW * 64 + threadIdx.x; i < a.T * a.H; i += gridDim.x * NW * 64) a.y[i] = 0.f;
-  const int nG = plan_groups<NW * 64>(a, s_ps, s_first, s_gslot, nullptr, &s_n);
-  const int g = blockIdx.y;
-  if (g >= nG) return;
-  const int slot = s_gslot[g];
-  const int t = blockIdx.x;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+// gate/up + SwiGLU.  Task (group g, brick row t): 16 rows of the gate/up bank
+// (gate rows 8t..8t+7 above the same up rows) over all H.  The NW waves take
+// 1/NW of the row's 2-brick steps each and meet in LDS, where wave 0 forms
+// h[g][token][8t..8t+7] = silu(gate) * up in BF16.  A workgroup's tasks form
+// one continuous step sequence per wave, so the loads of the next task are in
+// flight while the current one is reduced.  The first pass of workgroups also
+// zeroes y for the down launch.
+template <bool FP8, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void dec_gu_kernel(DecArgs a) {
+  __shared__ int s_gslot[kDecPmax];
+  __shared__ int s_G;
+  __shared__ unsigned long long s_tab[kPlanTab];
+  __shared__ f32x4 red[2][NW][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int r = lane & 15, j = lane >> 4;
-  const int H = a.H, I = a.I;
-  const bool tok = r < a.T;
-  f32x4 acc = {0, 0, 0, 0};
-  if (!FP8) {
-    const int nkt = H / 32;
-    const uint16_t* gu = (const uint16_t*)a.w_gu + (size_t)slot * 2 * I * H + (size_t)t * nkt * 512 + lane * 8;
-    const uint16_t* xr = a.xb + (size_t)(tok ? r : 0) * H + j * 8;
-    const int kb = wv * nkt / NW, ke = (wv + 1) * nkt / NW;
-    constexpr int CH = 8;
-    for (int k0 = kb; k0 < ke; k0 += CH) {
-      u32x4 av[CH], bv[CH];
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (k0 + c < ke) av[c] = ld16_nt(gu + (size_t)(k0 + c) * 512);
-#pragma unroll
-      for (int c = 0; c < CH; ++c) bv[c] = (tok && k0 + c < ke) ? ld16(xr + (k0 + c) * 32) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int c = 0; c < CH; ++c)
-        if (k0 + c < ke) acc = mfma16x16x32(av[c], bv[c], acc);
-    }
-  } else {
-    const int nkt = H / 64, nbk = H / 128;
-    const uint8_t* gu = (const uint8_t*)a.w_gu + (size_t)slot * 2 * I * H + (size_t)t * nkt * 1024 + lane * 16;
-    const uint16_t* xr = a.xb + (size_t)(tok ? r : 0) * H + j * 16;
-    // C rows 4j+i: j < 2 are gate rows, j >= 2 up rows, each with its scale row
-    const float* sc = (j < 2 ? a.s_gate : a.s_up) + ((size_t)slot * (I / 128) + (8 * t) / 128) * nbk;
-    const int bb = wv * nbk / NW, be = (wv + 1) * nbk / NW;
-    constexpr int CB = 4;   // 128-K blocks per batch: 8 brick loads in flight per lane
-    for (int b0 = bb; b0 < be; b0 += CB) {
-      u32x4 q[CB][2], xv[CB][4];
-#pragma unroll
-      for (int c = 0; c < CB; ++c)
-        if (b0 + c < be) {
-          q[c][0] = ld16_nt(gu + (size_t)(2 * (b0 + c)) * 1024);
-          q[c][1] = ld16_nt(gu + (size_t)(2 * (b0 + c) + 1) * 1024);
-        }
-#pragma unroll
-      for (int c = 0; c < CB; ++c)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          xv[c][v] = (tok && b0 + c < be) ? ld16(xr + (b0 + c) * 128 + (v >> 1) * 64 + (v & 1) * 8) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int c = 0; c < CB; ++c) {
-        if (b0 + c >= be) break;
-        f32x4 p = {0, 0, 0, 0};
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          u32x4 ae, ao;
-          e4m3x16_to_bf16(q[c][hh], ae, ao);
-          p = mfma16x16x32(ae, xv[c][2 * hh], p);
-          p = mfma16x16x32(ao, xv[c][2 * hh + 1], p);
-        }
-        const float s = sc[b0 + c];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += s * p[i];
-      }
-    }
-  }
-  red[wv][lane] = acc;
+  const int H = a.H, I = a.I, T = a.T;
+  for (int i = blockIdx.x * NW * 64 + tid; i < T * H; i += gridDim.x * NW * 64) a.y[i] = 0.f;
+  if (wv == 0) wave_plan(a.pick_slot, a.w, T * a.k, a.k, a.n_slots, a.G_max, s_gslot, nullptr, &s_G, s_tab);
   __syncthreads();
-  if (wv == 0 && j < 2) {
-    f32x4 G = red[0][lane], U = red[0][lane + 32];
+  const int G = s_G;
+  const int RA = I / 8;
+  const int nkt = FP8 ? H / 64 : H / 32;     // bricks per row
+  const int S = (nkt + 1) >> 1;              // 2-brick steps per row
+  const int SW = (S + NW - 1) / NW;          // steps per wave per task
+  const int s_lo = wv * SW;
+  const size_t gu_bytes = (size_t)2 * I * H * (FP8 ? 1 : 2);
+  const int ntask = G * RA;
+  const int ntk = ntask > (int)blockIdx.x ? (ntask - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+  const int nsteps = ntk * SW;
+  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)(T * H * 2));
+  const bool tok = r < T;
+  constexpr int XN = FP8 ? 4 : 2;
+  u32x4 wb[D][2], xb[D][XN];
+  float sb[D][2];
+  int i_tk = 0, i_l = 0;   // issue position: task of this workgroup, step within the wave's share
+  auto issue = [&](int d) {
+    const int task = (int)blockIdx.x + i_tk * (int)gridDim.x;
+    const int s = s_lo + i_l;
+    const bool ok = i_tk < ntk && s < S;
+    const int tt = ok ? task : 0;
+    const int g = tt / RA, t = tt - g * RA;
+    const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;   // slot 0 always exists
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc((const char*)a.w_gu + (size_t)slot * gu_bytes + (size_t)t * nkt * 1024, (uint32_t)(nkt * 1024));
+    const uint32_t wo = oob_sel(ok, (uint32_t)s * 2048u + lane * 16u);
+    wb[d][0] = bload_nt(wr, wo);
+    wb[d][1] = bload_nt(wr, oob_sel(ok, wo + 1024u));
 #pragma unroll
-    for (int w = 1; w < NW; ++w) {
-      G += red[w][lane];
-      U += red[w][lane + 32];
-    }
-    if (tok) {
-      uint16_t* hrow = a.h + ((size_t)g * kDecTok + r) * I;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int o = 8 * t + 4 * j + i;
-        const int pos = FP8 ? ((o & ~15) + perm16(o & 15)) : o;
-        hrow[pos] = f32_to_bf16_rne(silu_f32(G[i]) * U[i]);
+    for (int b = 0; b < 2; ++b) {
+      const int k0 = FP8 ? 128 * s + 64 * b : 64 * s + 32 * b;
+      const bool xo = ok && tok && k0 < H;
+      const uint32_t off = oob_sel(xo, (uint32_t)(r * H + k0 + (FP8 ? 16 : 8) * j) * 2u);
+      if (FP8) {
+        xb[d][2 * b] = bload(xr, off);
+        xb[d][2 * b + 1] = bload(xr, oob_sel(xo, off + 16u));
+      } else {
+        xb[d][b] = bload(xr, off);
       }
     }
-  }
-}
-
-// down projection + gate weights.  Workgroup (16-row brick row t of H, half):
-// half 0 takes the even groups, half 1 the odd ones; its waves take
-// (group, K-part) units round-robin, sums are added in wave order, and each
-// half adds its 16 x T partial into the zeroed y once.  Two additions into 0
-// commute exactly, so y is the same bits whichever half lands first.
-template <bool FP8, int NW>
-__global__ __launch_bounds__(NW * 64) void dec_down_kernel(DecArgs a) {
-  __shared__ int s_ps[kDecPmax], s_first[kDecPmax], s_gslot[kDecPmax];
-  __shared__ float s_gw[kDecPmax * kDecTok];
-  __shared__ int s_n;
-  __shared__ f32x4 red[NW][64];
-  const int nG = plan_groups<NW * 64>(a, s_ps, s_first, s_gslot, s_gw, &s_n);
-  const int t = blockIdx.x, hf = blockIdx.y;
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int r = lane & 15, j = lane >> 4;
-  const int H = a.H, I = a.I;
-  const bool tok = r < a.T;
-  const int KP = a.kp2;
-  const int ngh = (nG - hf + 1) / 2;
+    if (FP8) {   // block scales of the gate rows and of the up rows at this K step (scalar loads)
+      const size_t si = ((size_t)slot * (I / 128) + (8 * t) / 128) * (H / 128) + (ok ? s : 0);
+      sb[d][0] = a.s_gate[si];
+      sb[d][1] = a.s_up[si];
+    }
+    if (++i_l == SW) {
+      i_l = 0;
+      ++i_tk;
+    }
+  };
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d);
   f32x4 acc = {0, 0, 0, 0};
-  for (int u = wv; u < ngh * KP; u += NW) {
-    const int g = 2 * (u / KP) + hf, part = u % KP;
-    const int slot = s_gslot[g];
-    const float wgt = s_gw[g * kDecTok + r];
-    f32x4 blk = {0, 0, 0, 0};
-    if (!FP8) {
-      const int nkt = I / 32;
-      const int kb = part * nkt / KP, ke = (part + 1) * nkt / KP;
-      const uint16_t* wd = (const uint16_t*)a.w_down + (size_t)slot * H * I + (size_t)t * nkt * 512 + lane * 8;
-      const uint16_t* hr = a.h + ((size_t)g * kDecTok + (tok ? r : 0)) * I + j * 8;
-      constexpr int CH = 12;
-      for (int k0 = kb; k0 < ke; k0 += CH) {
-        u32x4 av[CH], bv[CH];
+  int c_tk = 0, c_l = 0;
+  for (int i0 = 0; i0 < nsteps; i0 += D) {
 #pragma unroll
-        for (int c = 0; c < CH; ++c)
-          if (k0 + c < ke) av[c] = ld16_nt(wd + (size_t)(k0 + c) * 512);
-#pragma unroll
-        for (int c = 0; c < CH; ++c) bv[c] = (tok && k0 + c < ke) ? ld16(hr + (k0 + c) * 32) : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < CH; ++c)
-          if (k0 + c < ke) blk = mfma16x16x32(av[c], bv[c], blk);
-      }
-    } else {
-      const int nkt = I / 64, nbk = I / 128;
-      const int bb = part * nbk / KP, be = (part + 1) * nbk / KP;
-      const uint8_t* wd = (const uint8_t*)a.w_down + (size_t)slot * H * I + (size_t)t * nkt * 1024 + lane * 16;
-      const uint16_t* hr = a.h + ((size_t)g * kDecTok + (tok ? r : 0)) * I + j * 16;
-      const float* sc = a.s_down + ((size_t)slot * (H / 128) + (16 * t) / 128) * nbk;
-      constexpr int CB = 4;
-      for (int b0 = bb; b0 < be; b0 += CB) {
-        u32x4 qv[CB][2], hv[CB][4];
-#pragma unroll
-        for (int c = 0; c < CB; ++c)
-          if (b0 + c < be) {
-            qv[c][0] = ld16_nt(wd + (size_t)(2 * (b0 + c)) * 1024);
-            qv[c][1] = ld16_nt(wd + (size_t)(2 * (b0 + c) + 1) * 1024);
-          }
-#pragma unroll
-        for (int c = 0; c < CB; ++c)
-#pragma unroll
-          for (int v = 0; v < 4; ++v)
-            hv[c][v] = (tok && b0 + c < be) ? ld16(hr + (b0 + c) * 128 + (v >> 1) * 64 + (v & 1) * 8)
-                                             : u32x4{0, 0, 0, 0};
-#pragma unroll
-        for (int c = 0; c < CB; ++c) {
-          if (b0 + c >= be) break;
+    for (int d = 0; d < D; ++d) {
+      if (i0 + d < nsteps) {
+        if (!FP8) {
+          acc = mfma16x16x32(wb[d][0], xb[d][0], acc);
+          acc = mfma16x16x32(wb[d][1], xb[d][1], acc);
+        } else {
           f32x4 p = {0, 0, 0, 0};
 #pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            u32x4 de, dd;
-            e4m3x16_to_bf16(qv[c][hh], de, dd);
-            p = mfma16x16x32(de, hv[c][2 * hh], p);
-            p = mfma16x16x32(dd, hv[c][2 * hh + 1], p);
+          for (int b = 0; b < 2; ++b) {
+            u32x4 lo, hi;
+            e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
+            p = mfma16x16x32(lo, xb[d][2 * b], p);
+            p = mfma16x16x32(hi, xb[d][2 * b + 1], p);
           }
-          const float s = sc[b0 + c];
+          const float sc = j < 2 ? sb[d][0] : sb[d][1];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) blk[i] += s * p[i];
+          for (int q = 0; q < 4; ++q) acc[q] += sc * p[q];
+        }
+        if (c_l == SW - 1) {   // end of a task: reduce over the waves, SwiGLU, h
+          const int task = (int)blockIdx.x + c_tk * (int)gridDim.x;
+          const int g = task / RA, t = task - g * RA;
+          f32x4(&rb)[NW][64] = red[c_tk & 1];
+          rb[wv][lane] = acc;
+          __syncthreads();
+          if (wv == 0 && j < 2 && tok) {
+            f32x4 Gv = rb[0][lane], Uv = rb[0][lane + 32];
+#pragma unroll
+            for (int w2 = 1; w2 < NW; ++w2) {
+              Gv += rb[w2][lane];
+              Uv += rb[w2][lane + 32];
+            }
+            uint16_t* hrow = a.h + ((size_t)g * kDecTok + r) * I + 8 * t + 4 * j;
+            const uint32_t h01 = f32_to_bf16_rne(silu_f32(Gv[0]) * Uv[0]) | ((uint32_t)f32_to_bf16_rne(silu_f32(Gv[1]) * Uv[1]) << 16);
+            const uint32_t h23 = f32_to_bf16_rne(silu_f32(Gv[2]) * Uv[2]) | ((uint32_t)f32_to_bf16_rne(silu_f32(Gv[3]) * Uv[3]) << 16);
+            *reinterpret_cast<u32x2*>(hrow) = u32x2{h01, h23};
+          }
+          acc = f32x4{0, 0, 0, 0};
+          c_l = 0;
+          ++c_tk;
+        } else {
+          ++c_l;
         }
       }
+      issue(d);
     }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += wgt * blk[i];
   }
-  red[wv][lane] = acc;
+}
+
+// down projection + gate weights.  Task (brick row t of H, half): the output
+// row's steps over (group, 2-brick K step) are split in two halves; the NW
+// waves take 1/NW of the half each, scale each step's sum by the token's gate
+// weight (and the FP8 block scale), meet in LDS, and wave 0 adds the 16 x T
+// partial into y, zeroed by the gate/up launch.  Exactly two additions land on
+// each y element and two additions into 0 commute exactly, so y has the same
+// bits whichever half lands first.  Continuous per-wave step sequence as in
+// the gate/up launch.
+template <bool FP8, int D, int NW>
+__global__ __launch_bounds__(NW * 64) void dec_dn_kernel(DecArgs a) {
+  __shared__ int s_gslot[kDecPmax];
+  __shared__ float s_gw[kDecPmax * kDecTok];
+  __shared__ int s_G;
+  __shared__ unsigned long long s_tab[kPlanTab];
+  __shared__ f32x4 red[2][NW][64];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int r = lane & 15, j = lane >> 4;
+  const int H = a.H, I = a.I, T = a.T;
+  if (wv == 0) wave_plan(a.pick_slot, a.w, T * a.k, a.k, a.n_slots, a.G_max, s_gslot, s_gw, &s_G, s_tab);
   __syncthreads();
-  if (wv == 0) {
-    f32x4 Y = red[0][lane];
+  const int G = s_G;
+  const int nkt = FP8 ? I / 64 : I / 32;     // bricks per (row, slot)
+  const int SB = (nkt + 1) >> 1;             // steps per (row, group)
+  const int n = G * SB;                      // steps per output row
+  const int SWB = ((n + 1) / 2 + NW - 1) / NW;   // steps per wave per task (larger half)
+  const size_t dn_bytes = (size_t)H * I * (FP8 ? 1 : 2);
+  const int ntask = 2 * (H / 16);
+  const int ntk = ntask > (int)blockIdx.x ? (ntask - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
+  const int nsteps = ntk * SWB;
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.h, (uint32_t)(2u * a.G_max * kDecTok * I));
+  const bool tok = r < T;
+  constexpr int XN = FP8 ? 4 : 2;
+  u32x4 wb[D][2], hb[D][XN];
+  float fb[D];
+  int i_tk = 0, i_l = 0;
+  auto issue = [&](int d) {
+    const int task = (int)blockIdx.x + i_tk * (int)gridDim.x;
+    const int t = task >> 1, half = task & 1;
+    const int lo = half ? n / 2 : 0, hi = half ? n : n / 2;
+    const int q = lo + wv * SWB + i_l;
+    const bool ok = i_tk < ntk && i_l < SWB && wv * SWB + i_l < hi - lo;
+    (void)q;
+    const int qq = ok ? q : 0;
+    const int g = qq / SB, s = qq - g * SB;
+    const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;   // slot 0 always exists
+    const int tr = ok ? t : 0;
+    const __amdgpu_buffer_rsrc_t wr =
+        make_rsrc((const char*)a.w_down + (size_t)slot * dn_bytes + (size_t)tr * nkt * 1024, (uint32_t)(nkt * 1024));
+    const uint32_t wo = oob_sel(ok, (uint32_t)s * 2048u + lane * 16u);
+    wb[d][0] = bload_nt(wr, wo);
+    wb[d][1] = bload_nt(wr, oob_sel(ok, wo + 1024u));
+    const uint32_t hrow = (uint32_t)((g * kDecTok + r) * I);
 #pragma unroll
-    for (int w = 1; w < NW; ++w) Y += red[w][lane];
-    if (tok) {
-      float* yr = a.y + (size_t)r * H + 16 * t + 4 * j;
+    for (int b = 0; b < 2; ++b) {
+      const int k0 = FP8 ? 128 * s + 64 * b : 64 * s + 32 * b;
+      const bool ho = ok && tok && k0 < I;
+      const uint32_t off = oob_sel(ho, (hrow + k0 + (FP8 ? 16 : 8) * j) * 2u);
+      if (FP8) {
+        hb[d][2 * b] = bload(hr, off);
+        hb[d][2 * b + 1] = bload(hr, oob_sel(ho, off + 16u));
+      } else {
+        hb[d][b] = bload(hr, off);
+      }
+    }
+    float f = ok ? s_gw[g * kDecTok + r] : 0.f;
+    if (FP8) f *= a.s_down[((size_t)slot * (H / 128) + (16 * tr) / 128) * (I / 128) + s];
+    fb[d] = f;
+    if (++i_l == SWB) {
+      i_l = 0;
+      ++i_tk;
+    }
+  };
 #pragma unroll
-      for (int i = 0; i < 4; ++i) atomicAdd(yr + i, Y[i]);
+  for (int d = 0; d < D; ++d) issue(d);
+  f32x4 acc = {0, 0, 0, 0};
+  int c_tk = 0, c_l = 0;
+  for (int i0 = 0; i0 < nsteps; i0 += D) {
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      if (i0 + d < nsteps) {
+        f32x4 p = {0, 0, 0, 0};
+        if (!FP8) {
+          p = mfma16x16x32(wb[d][0], hb[d][0], p);
+          p = mfma16x16x32(wb[d][1], hb[d][1], p);
+        } else {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {
+            u32x4 lo, hi;
+            e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
+            p = mfma16x16x32(lo, hb[d][2 * b], p);
+            p = mfma16x16x32(hi, hb[d][2 * b + 1], p);
+          }
+        }
+        const float f = fb[d];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[q] += f * p[q];
+        if (c_l == SWB - 1) {   // end of a task: reduce over the waves, add into y
+          const int task = (int)blockIdx.x + c_tk * (int)gridDim.x;
+          const int t = task >> 1;
+          f32x4(&rb)[NW][64] = red[c_tk & 1];
+          rb[wv][lane] = acc;
+          __syncthreads();
+          if (wv == 0 && tok) {
+            f32x4 Y = rb[0][lane];
+#pragma unroll
+            for (int w2 = 1; w2 < NW; ++w2) Y += rb[w2][lane];
+            float* yr = a.y + (size_t)r * H + 16 * t + 4 * j;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) atomicAdd(yr + q, Y[q]);
+          }
+          acc = f32x4{0, 0, 0, 0};
+          c_l = 0;
+          ++c_tk;
+        } else {
+          ++c_l;
+        }
+      }
+      issue(d);
     }
   }
 }
@@ -700,6 +795,8 @@ __global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ yg
 }
 
 // ================================================================ E4M3 expansion utility
+// The same conversion the decode path runs in registers, exposed so that it
+// can be checked code by code.
 __global__ __launch_bounds__(256) void e4m3_expand_kernel(const uint8_t* __restrict__ codes, uint16_t* __restrict__ out,
                                                           int64_t n) {
   const int64_t i = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 16;
@@ -710,12 +807,12 @@ __global__ __launch_bounds__(256) void e4m3_expand_kernel(const uint8_t* __restr
   for (int t = 0; t < 4; ++t)
     q[t] = (uint32_t)b[4 * t] | ((uint32_t)b[4 * t + 1] << 8) | ((uint32_t)b[4 * t + 2] << 16) |
            ((uint32_t)b[4 * t + 3] << 24);
-  u32x4 ev, od;
-  e4m3x16_to_bf16(q, ev, od);
+  u32x4 lo, hi;
+  e4m3x16_to_bf16_nat(q, lo, hi);
   for (int t = 0; t < 16; ++t) {
     if (i + t >= n) break;
-    const uint32_t v = (t & 1) ? od[t >> 2] : ev[t >> 2];
-    out[i + t] = (uint16_t)(((t >> 1) & 1) ? (v >> 16) : (v & 0xFFFFu));
+    const uint32_t v = t < 8 ? lo[t >> 1] : hi[(t - 8) >> 1];
+    out[i + t] = (uint16_t)((t & 1) ? (v >> 16) : (v & 0xFFFFu));
   }
 }
 
@@ -723,16 +820,48 @@ __global__ __launch_bounds__(256) void e4m3_expand_kernel(const uint8_t* __restr
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct DecWs {
-  size_t xperm, h, total;
+  size_t h, total;
 };
 static DecWs dec_ws(int T_max, int k, int H, int I, int n_slots) {
   DecWs w{};
   int G = T_max * k < n_slots ? T_max * k : n_slots;
   size_t off = 0;
-  w.xperm = off; off = align256(off + 2 * (size_t)T_max * H);
   w.h = off; off = align256(off + 2 * (size_t)G * kDecTok * I);
   w.total = off;
   return w;
+}
+
+// Resident workgroups per CU of each decode kernel, and the CU count, per device.
+struct DecOcc {
+  int cus = 0;
+  int gu[2] = {0, 0}, dn[2] = {0, 0};
+};
+constexpr int kDecD_BF16 = 4, kDecD_FP8 = 4;   // register-ring depth in 2-brick steps (gate/up)
+constexpr int kDnD_BF16 = 4, kDnD_FP8 = 4;     // (down)
+constexpr int kGuW = 4, kDnW = 16;              // waves per workgroup
+static std::mutex g_occ_mu;
+static DecOcc g_occ[64];
+static moe_status dec_occupancy(DecOcc* out) {
+  int dev = 0;
+  MOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) MOE_FAIL(MOE_ERR_ARG, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_occ_mu);
+  DecOcc& o = g_occ[dev];
+  if (!o.cus) {
+    int cus = 0;
+    MOE_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.gu[0], dec_gu_kernel<false, kDecD_BF16, kGuW>, kGuW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.gu[1], dec_gu_kernel<true, kDecD_FP8, kGuW>, kGuW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.dn[0], dec_dn_kernel<false, kDnD_BF16, kDnW>, kDnW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.dn[1], dec_dn_kernel<true, kDnD_FP8, kDnW>, kDnW * 64, 0));
+    for (int i = 0; i < 2; ++i) {
+      if (o.gu[i] < 1) o.gu[i] = 1;
+      if (o.dn[i] < 1) o.dn[i] = 1;
+    }
+    o.cus = cus > 0 ? cus : 1;
+  }
+  *out = o;
+  return MOE_OK;
 }
 
 struct PfWs {
@@ -767,8 +896,8 @@ extern "C" moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int3
   if (!bytes) MOE_FAIL(MOE_ERR_ARG, "bytes is NULL");
   if (T_max < 1 || k < 1 || H < 1 || I < 1 || n_slots < 1) MOE_FAIL(MOE_ERR_SHAPE, "bad sizes");
   if (mode == MOE_FWD_DECODE) {
-    if (T_max > kDecTok || T_max * k > 512)
-      MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T_max <= %d and T_max*k <= 512", kDecTok);
+    if (T_max > kDecTok || T_max * k > kDecPmax)
+      MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T_max <= %d and T_max*k <= %d", kDecTok, kDecPmax);
     *bytes = dec_ws(T_max, k, H, I, n_slots).total;
   } else if (mode == MOE_FWD_PREFILL) {
     if (n_slots > 4096) MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs n_slots <= 4096");
@@ -817,33 +946,30 @@ extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t*
 
   if (mode == MOE_FWD_DECODE) {
     if (T > kDecTok || T * k > kDecPmax)
-      MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T <= 16 and T*k <= 512 (T=%d k=%d)", T, k);
+      MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T <= %d and T*k <= %d (T=%d k=%d)", kDecTok, kDecPmax, T, k);
+    if (fp8 && H > 16384) MOE_FAIL(MOE_ERR_SHAPE, "FP8 decode mode needs H <= 16384 (H=%d)", H);
     DecWs L = dec_ws(T, k, H, I, slots->n_slots);
     if (ws_bytes < L.total) MOE_FAIL(MOE_ERR_NO_SPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+    DecOcc occ;
+    moe_status os = dec_occupancy(&occ);
+    if (os) return os;
     DecArgs a{};
     a.w_gu = slots->w_gate_up; a.w_down = slots->w_down;
     a.s_gate = slots->s_gate; a.s_up = slots->s_up; a.s_down = slots->s_down;
     a.H = H; a.I = I; a.n_slots = slots->n_slots; a.T = T; a.k = k;
     a.x = x; a.pick_slot = pick_slot; a.w = w; a.y = y;
-    a.xperm = (uint16_t*)(wsb + L.xperm);
     a.h = (uint16_t*)(wsb + L.h);
-    a.xb = fp8 ? a.xperm : x;
     a.G_max = T * k < slots->n_slots ? T * k : slots->n_slots;
-    // K-parts of the down projection: a unit keeps >= 12 bricks (BF16) / 4 blocks (FP8) of loads in flight
-    const int ksteps = fp8 ? I / 128 : I / 32;
-    const int unit = fp8 ? 4 : 12;
-    int kp2 = 1;
-    while (kp2 < 8 && ksteps % (2 * kp2) == 0 && ksteps / (2 * kp2) >= unit) kp2 *= 2;
-    a.kp2 = kp2;
-    constexpr int NW = 8;
-    const dim3 g1(I / 8, a.G_max), g2(H / 16, 2);
+    const int f = fp8 ? 1 : 0;
+    const long gu_tasks = (long)a.G_max * (I / 8), dn_tasks = 2L * (H / 16);
+    const unsigned g1 = (unsigned)std::min<long>(gu_tasks, (long)occ.cus * occ.gu[f]);
+    const unsigned g2 = (unsigned)std::min<long>(dn_tasks, (long)occ.cus * occ.dn[f]);
     if (fp8) {
-      dec_xperm_kernel<<<(T * (H / 16) + 255) / 256, 256, 0, stream>>>(a);
-      dec_gateup_kernel<true, NW><<<g1, NW * 64, 0, stream>>>(a);
-      dec_down_kernel<true, NW><<<g2, NW * 64, 0, stream>>>(a);
+      dec_gu_kernel<true, kDecD_FP8, kGuW><<<g1, kGuW * 64, 0, stream>>>(a);
+      dec_dn_kernel<true, kDnD_FP8, kDnW><<<g2, kDnW * 64, 0, stream>>>(a);
     } else {
-      dec_gateup_kernel<false, NW><<<g1, NW * 64, 0, stream>>>(a);
-      dec_down_kernel<false, NW><<<g2, NW * 64, 0, stream>>>(a);
+      dec_gu_kernel<false, kDecD_BF16, kGuW><<<g1, kGuW * 64, 0, stream>>>(a);
+      dec_dn_kernel<false, kDnD_BF16, kDnW><<<g2, kDnW * 64, 0, stream>>>(a);
     }
     MOE_LAUNCHED();
     return MOE_OK;

@@ -29,7 +29,9 @@ def _run_forward(b, pool, x_bits, pick_slot, w, mode, T_max=None):
 
 # ---------------------------------------------------------------- decode, BF16
 @pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 128), (3, 8, 2, 256, 128), (16, 32, 4, 512, 256),
-                                       (1, 128, 8, 2048, 768), (5, 24, 8, 1024, 384)])
+                                       (1, 128, 8, 2048, 768), (5, 24, 8, 1024, 384),
+                                       (16, 24, 16, 256, 128),      # 256 picks, many shared slots
+                                       (2, 8, 2, 96, 96)])          # odd brick counts along H and I
 def test_decode_bf16(T, E, k, H, I):
     b = binding()
     bank = Bf16Bank(90 + T, E, H, I)
@@ -58,6 +60,17 @@ def test_decode_shared_slots_across_tokens():
     y = _run_forward(b, pool, x, ids, w, b.FWD_DECODE)
     yg, _ = oracle_partials(x, ids, w, bank.expert64, np.ones(ids.shape, bool))
     check_layer(y, yg)
+
+
+def test_decode_pick_limit():
+    b = binding()
+    pool = b.SlotPool(4, 256, 128, b.W_BF16)
+    ws = b.forward_workspace(16, 16, 256, 128, 4, b.FWD_DECODE)
+    x = torch.zeros((16, 256), dtype=torch.uint16, device="cuda")
+    with pytest.raises(b.MoeError) as ei:
+        b.expert_forward(pool.c, x, torch.zeros((16, 17), dtype=torch.int32, device="cuda"),
+                         torch.zeros((16, 17), device="cuda"), b.FWD_DECODE, ws)
+    assert ei.value.status == -2                  # MOE_ERR_SHAPE: T*k > 256
 
 
 def test_decode_all_host_gives_zero():
