@@ -66,10 +66,10 @@ moe_status check_slots(const moe_slots* s);
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)(((u >> 16) & 0x8000u) | 0x7fc0u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+  const uint32_t nan = ((u >> 16) & 0x8000u) | 0x7fc0u;
+  return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? nan : r);
 }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
@@ -158,6 +158,8 @@ __device__ __forceinline__ void e4m3x16_to_bf16_nat(const u32x4& q, u32x4& lo, u
              e4m3x2_to_bf16x2<true>(q[3])};
 }
 
-__device__ __forceinline__ float silu_f32(float a) { return a / (1.0f + __expf(-a)); }
+// a * sigmoid(a); the reciprocal is the hardware one (about 1 ulp), far
+// below the BF16 rounding that h receives next.
+__device__ __forceinline__ float silu_f32(float a) { return a * __builtin_amdgcn_rcpf(1.0f + __expf(-a)); }
 
 }  // namespace moe

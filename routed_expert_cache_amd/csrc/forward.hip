@@ -449,8 +449,20 @@ __global__ __launch_bounds__(NW * 64) void dec_dn_kernel(DecArgs a) {
 }
 
 // ================================================================ prefill
-constexpr int kBM = 128;          // rows (pairs) per tile
-constexpr int kPfThreads = 256;   // 4 waves, 2 x 2, 64 x 64 each
+// (token, pick) pairs are counting-sorted by slot in three launches (per
+// workgroup histograms, one scan, scatter), then two grouped GEMMs walk a
+// tile list: tile = (slot, 128 or 64 sorted pairs) x (512 bank rows).  The
+// weight bricks are the MFMA A operand, streamed from memory straight into
+// registers; the tokens' rows are the B operand, staged in LDS.  Each wave
+// owns 128 bank rows, so the accumulator of a lane holds 4 consecutive bank
+// rows of one token: SwiGLU pairs a gate lane with the up lane 32 away, and
+// the outputs leave registers as 8-byte stores.  Gate/up writes h [P][I]
+// (BF16); down writes the gate-weighted rows o [P][H] (BF16); a last launch
+// sums each token's k rows in pick order.
+constexpr int kSortChunk = 2048;   // least pairs per counting workgroup
+constexpr int kSortMaxChunks = 32; // counting workgroups at most
+constexpr int kSortMaxSlots = 4096;
+constexpr int kPfRows = 512;       // bank rows per tile (4 waves x 128)
 
 struct PfArgs {
   const void* w_gu;
@@ -458,52 +470,69 @@ struct PfArgs {
   const float* s_gate;
   const float* s_up;
   const float* s_down;
-  int H, I, n_slots, T, k, P, max_tiles;
+  int H, I, n_slots, T, k, P, tm, max_mtiles, chunk;
   const uint16_t* x;
   const int32_t* pick_slot;
   const float* w;
   float* y;
   // workspace
+  int32_t* hist;         // [n_chunks][n_slots] counts, then bases
   int32_t* cnt;          // [n_slots]
   int32_t* off;          // [n_slots]
-  int32_t* n_tiles;      // [1]
-  int32_t* tile_slot;    // [max_tiles]
-  int32_t* tile_m0;      // [max_tiles]
+  int32_t* mtoff;        // [n_slots] first M tile of each slot
+  int32_t* n_mtiles;     // [1]
+  int32_t* tile_slot;    // [max_mtiles]
+  int32_t* tile_m0;      // [max_mtiles]
   int32_t* sorted_pair;  // [P]
   int32_t* pair_pos;     // [P]
-  uint16_t* h;           // [P][I]
-  float* o;              // [P][H]
+  uint16_t* h;           // [P][I] BF16
+  uint16_t* o;           // [P][H] BF16
 };
 
-// counting sort of the (token, pick) pairs by slot; one workgroup
-__global__ __launch_bounds__(1024) void pf_sort_kernel(PfArgs a) {
-  __shared__ int cnt[4096];
-  __shared__ int base[4096];
-  __shared__ int wsum[16];
-  __shared__ int wsum2[16];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int S = a.n_slots;
-  for (int s = tid; s < S; s += 1024) cnt[s] = 0;
+// pass 1: histogram of the chunk's pairs by slot
+__global__ __launch_bounds__(256) void pf_count_kernel(PfArgs a) {
+  __shared__ int hs[kSortMaxSlots];
+  const int tid = threadIdx.x, S = a.n_slots;
+  for (int s = tid; s < S; s += 256) hs[s] = 0;
   __syncthreads();
-  for (int p = tid; p < a.P; p += 1024) {
-    int s = a.pick_slot[p];
-    if (s >= 0 && s < S) atomicAdd(&cnt[s], 1);
+  const int p0 = blockIdx.x * a.chunk, p1 = min(a.P, p0 + a.chunk);
+  for (int p = p0 + tid; p < p1; p += 256) {
+    const int s = a.pick_slot[p];
+    if (s >= 0 && s < S) atomicAdd(&hs[s], 1);
   }
   __syncthreads();
-  // exclusive scans of counts and of tile counts; thread handles 4 slots
-  int c[4], tcount[4], ls = 0, lt = 0;
+  int32_t* row = a.hist + (size_t)blockIdx.x * S;
+  for (int s = tid; s < S; s += 256) row[s] = hs[s];
+}
+
+// pass 2 (one workgroup): slot totals and segment offsets, per-chunk bases
+// (hist is overwritten with the first sorted position of each chunk's pairs
+// of each slot), and the list of M tiles (slot, first row) in slot order.
+// A thread takes 4 slots; each slot's column of chunk counts is loaded into
+// registers at once (at most kSortMaxChunks), so no load waits on another.
+__global__ __launch_bounds__(1024) void pf_scan_kernel(PfArgs a, int n_chunks) {
+  __shared__ int wsum[16], wsum2[16];
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int S = a.n_slots, TM = a.tm;
+  int c[4], tc[4], ls = 0, lt = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int s = tid * 4 + i;
-    c[i] = s < S ? cnt[s] : 0;
-    tcount[i] = (c[i] + kBM - 1) / kBM;
-    ls += c[i];
-    lt += tcount[i];
+    const int s = tid * 4 + i;
+    int col[kSortMaxChunks];
+#pragma unroll
+    for (int w = 0; w < kSortMaxChunks; ++w) col[w] = (s < S && w < n_chunks) ? a.hist[(size_t)w * S + s] : 0;
+    int v = 0;
+#pragma unroll
+    for (int w = 0; w < kSortMaxChunks; ++w) v += col[w];
+    c[i] = v;
+    tc[i] = (v + TM - 1) / TM;
+    ls += v;
+    lt += tc[i];
   }
   int is = ls, it = lt;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
-    int o1 = __shfl_up(is, d, 64), o2 = __shfl_up(it, d, 64);
+    const int o1 = __shfl_up(is, d, 64), o2 = __shfl_up(it, d, 64);
     if (lane >= d) {
       is += o1;
       it += o2;
@@ -514,262 +543,297 @@ __global__ __launch_bounds__(1024) void pf_sort_kernel(PfArgs a) {
     wsum2[wv] = it;
   }
   __syncthreads();
-  int bs = 0, bt = 0, tot_t = 0;
-  for (int w2 = 0; w2 < 16; ++w2) {
-    if (w2 < wv) {
-      bs += wsum[w2];
-      bt += wsum2[w2];
-    }
-    tot_t += wsum2[w2];
+  int bs = 0, bt = 0;
+  for (int w = 0; w < wv; ++w) {
+    bs += wsum[w];
+    bt += wsum2[w];
   }
-  int es = bs + is - ls, et = bt + it - lt;
+  int es = bs + is - ls, et = bt + it - lt;   // exclusive prefix of this thread's first slot
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    int s = tid * 4 + i;
+    const int s = tid * 4 + i;
     if (s < S) {
-      base[s] = es;
-      a.off[s] = es;
       a.cnt[s] = c[i];
-      for (int q = 0; q < tcount[i]; ++q) {
-        if (et + q < a.max_tiles) {
-          a.tile_slot[et + q] = s;
-          a.tile_m0[et + q] = q * kBM;
+      a.off[s] = es;
+      a.mtoff[s] = et;
+      int col[kSortMaxChunks];
+#pragma unroll
+      for (int w = 0; w < kSortMaxChunks; ++w) col[w] = w < n_chunks ? a.hist[(size_t)w * S + s] : 0;
+      int b = es;
+#pragma unroll
+      for (int w = 0; w < kSortMaxChunks; ++w)
+        if (w < n_chunks) {
+          a.hist[(size_t)w * S + s] = b;
+          b += col[w];
         }
-      }
+      for (int q = 0; q < tc[i]; ++q)
+        if (et + q < a.max_mtiles) {
+          a.tile_slot[et + q] = s;
+          a.tile_m0[et + q] = q * TM;
+        }
     }
     es += c[i];
-    et += tcount[i];
+    et += tc[i];
   }
-  if (tid == 0) *a.n_tiles = tot_t < a.max_tiles ? tot_t : a.max_tiles;
+  if (tid == 1023) *a.n_mtiles = min(et, a.max_mtiles);
+}
+
+// pass 3: scatter each chunk's pairs to their sorted positions
+__global__ __launch_bounds__(256) void pf_scatter_kernel(PfArgs a) {
+  __shared__ int cur[kSortMaxSlots];
+  const int tid = threadIdx.x, S = a.n_slots;
+  const int32_t* row = a.hist + (size_t)blockIdx.x * S;
+  for (int s = tid; s < S; s += 256) cur[s] = row[s];
   __syncthreads();
-  for (int p = tid; p < a.P; p += 1024) {
-    int s = a.pick_slot[p];
+  const int p0 = blockIdx.x * a.chunk, p1 = min(a.P, p0 + a.chunk);
+  for (int p = p0 + tid; p < p1; p += 256) {
+    const int s = a.pick_slot[p];
     int pos = -1;
     if (s >= 0 && s < S) {
-      pos = atomicAdd(&base[s], 1);
+      pos = atomicAdd(&cur[s], 1);
       a.sorted_pair[pos] = p;
     }
     a.pair_pos[p] = pos;
   }
 }
 
-// Grouped GEMM tile C[128 pairs x 128 weight rows] over one slot's segment;
-// weights are bricks read as MFMA B operands.  GATEUP: A = gathered x rows,
-// B = gate/up brick rows (16 B-rows = 8 gate + 8 up of the same outputs),
-// epilogue h = silu(g) * u (BF16).  DOWN: A = h rows of the segment, B =
-// W_down bricks, epilogue o = w_pair * acc (FP32).  Global -> register ->
-// LDS staging is double-buffered: the next K step's loads are in flight while
-// the current one computes.  FP8 bricks are expanded exactly to BF16 when
-// read from LDS; the 128 x 128 scale multiplies the block partial once.
+// Grouped GEMM.  Tile = (M tile of one slot: TM sorted pairs) x (512 bank
+// rows).  Eight waves, two per SIMD so that one wave's barrier and load
+// latency hides under the other's MFMAs: wave (wr, wt) owns bank rows
+// [128 wr, 128 wr + 128) against pairs [TM/2 wt, TM/2 wt + TM/2).  K
+// advances one brick per step.  Every operand goes from memory straight
+// into LDS as 1 KB MFMA bricks (buffer loads with an LDS destination: 32
+// weight bricks + 8 token bricks per step, 5 per wave), three stages deep,
+// so two steps of loads are in flight while the MFMAs of the third run; one
+// barrier per step.  A token brick's lane (r, j) fetches 16 bytes of pair
+// row 16g + r at the brick's K offset for group j, so the LDS image is
+// already the MFMA operand.  FP8: two steps make one 128-K scale block; its
+// partial sums are scaled once and added (post-scaling).  Tiles are taken
+// in list order per XCD (workgroup b runs on XCD b % 8) and the list is
+// ordered (slot, bank-row block, M tile), so the M tiles that share a block
+// of weights run side by side and share it through that XCD's L2.
+typedef __attribute__((address_space(3))) void* lds_ptr;
+template <int AUX>
+__device__ __forceinline__ void bload_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, AUX);
+}
+constexpr int kPfWaves = 8;
+
 template <bool FP8, bool GATEUP>
-__global__ __launch_bounds__(kPfThreads) void pf_gemm_kernel(PfArgs a) {
-  constexpr int BK = FP8 ? 128 : 64;           // one FP8 scale block per step; 2 bricks per 16 B-rows
-  constexpr int KB = FP8 ? 64 : 32;            // brick K width
-  constexpr int ASTR = BK + 8;                 // A row stride in LDS (BF16 elements)
-  constexpr int A_ELEMS = kBM * ASTR;
-  constexpr int B_BYTES = 16 * 1024;           // 8 groups of 16 B-rows x 2 bricks
-  constexpr int ACH = kBM * BK / 16;           // 16-element A chunks per step
-  constexpr int ACT = ACH / kPfThreads;        // per thread
-  constexpr int BCT = (B_BYTES / 16) / kPfThreads;
-  __shared__ __attribute__((aligned(16))) uint16_t As[2][A_ELEMS];
-  __shared__ __attribute__((aligned(16))) char Bs[2][B_BYTES];
-  __shared__ int rowtok[kBM];
+__global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
+  constexpr int TM = FP8 ? 64 : 128;     // pairs per tile
+  constexpr int KS = FP8 ? 64 : 32;      // K per step = one weight brick
+  constexpr int NTG = TM / 32;           // token groups (MFMA N blocks) per wave
+  constexpr int TBW = FP8 ? 2 * NTG : NTG;   // token bricks a wave reads per step (FP8: lo and hi)
+  constexpr int SB = 32 + 8;             // bricks per stage: 32 weight + 8 token
+  __shared__ __attribute__((aligned(1024))) char Ls[3][SB * 1024];
+  __shared__ int rowsrc[TM];
 
-  const int tile = blockIdx.x;
-  if (tile >= *a.n_tiles) return;
-  const int slot = a.tile_slot[tile];
-  const int m0 = a.tile_m0[tile];
-  const int seg = a.off[slot];
-  const int mrows = min(kBM, a.cnt[slot] - m0);
   const int K = GATEUP ? a.H : a.I;
-  const int nkt = K / KB;
-  const int n0 = blockIdx.y * 128;             // first B row (gate/up rows or H rows)
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int wm = wv >> 1, wn = wv & 1;
+  const int NROWS = GATEUP ? 2 * a.I : a.H;          // bank rows
+  const int NB = (NROWS + kPfRows - 1) / kPfRows;
+  const int ntiles = *a.n_mtiles * NB;
+  const int Q = (ntiles + 7) / 8;
+  const int xcd = blockIdx.x & 7, sq = blockIdx.x >> 3;
+  if (sq >= Q) return;
+  const int tau = xcd * Q + sq;
+  if (tau >= ntiles) return;
+  // tau / NB falls inside the slot's run of M tiles because each slot's
+  // block of tiles is NB times its M tiles.
+  const int slot = a.tile_slot[tau / NB];
+  const int nm = (a.cnt[slot] + TM - 1) / TM;
+  const int lam = tau - a.mtoff[slot] * NB;
+  const int nb = lam / nm, mt = a.mtoff[slot] + (lam - nb * nm);
+  const int m0 = a.tile_m0[mt];
+  const int seg = a.off[slot];
+  const int mrows = min(TM, a.cnt[slot] - m0);
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wr = wv >> 1, wt = wv & 1;
   const int r = lane & 15, j = lane >> 4;
+  const int nkt = K / KS;                                // bricks per brick row = steps
+  const int t0 = (nb * kPfRows + 128 * wr) / 16;        // first brick row of this wave's rows
+  const bool rows_ok = nb * kPfRows + 128 * wr < NROWS;
 
-  if (tid < kBM) {
-    int pr = -1;
-    if (tid < mrows) pr = GATEUP ? a.sorted_pair[seg + m0 + tid] / a.k : seg + m0 + tid;
-    rowtok[tid] = pr;
-  }
-  const char* bbase = (const char*)(GATEUP ? a.w_gu : a.w_down) +
-                      (size_t)slot * (GATEUP ? 2 : 1) * a.I * a.H * (FP8 ? 1 : 2) + (size_t)(n0 / 16) * nkt * 1024;
-  float sc_lane = 1.f;
+  if (tid < TM) rowsrc[tid] = tid < mrows ? (GATEUP ? a.sorted_pair[seg + m0 + tid] / a.k : seg + m0 + tid) : -1;
+  const size_t bank_bytes = (size_t)(GATEUP ? 2 : 1) * a.I * a.H * (FP8 ? 1 : 2);
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc((const char*)(GATEUP ? a.w_gu : a.w_down) + (size_t)slot * bank_bytes +
+                                                   (size_t)(rows_ok ? t0 : 0) * nkt * 1024,
+                                               rows_ok ? (uint32_t)(8 * nkt * 1024) : 0u);
+  const uint16_t* tsrc = GATEUP ? a.x : a.h;
+  const uint32_t tbytes = (uint32_t)((size_t)(GATEUP ? a.T : a.P) * K * 2);
+  const __amdgpu_buffer_rsrc_t trs = make_rsrc(tsrc, tbytes);
   const float* scp = nullptr;
   if (FP8) {
     const int nbk = K / 128;
-    if (GATEUP)   // B column r of a 16-row group: gate (r < 8) or up; all 64 outputs share one scale row block
-      scp = (r < 8 ? a.s_gate : a.s_up) + ((size_t)slot * (a.I / 128) + (n0 / 2) / 128) * nbk;
+    if (GATEUP)   // lanes j < 2 hold gate rows, j >= 2 up rows; 64 features in one 128-block
+      scp = (j < 2 ? a.s_gate : a.s_up) + ((size_t)slot * (a.I / 128) + (8 * t0) / 128) * nbk;
     else
-      scp = a.s_down + ((size_t)slot * (a.H / 128) + n0 / 128) * nbk;
+      scp = a.s_down + ((size_t)slot * (a.H / 128) + (16 * t0) / 128) * nbk;
   }
-  const uint16_t* asrc = GATEUP ? a.x : a.h;
-  const int astride = GATEUP ? a.H : a.I;
   __syncthreads();
-
-  u32x4 ra[ACT][2], rb[BCT];
-  auto gload = [&](int k0) {
+  // Loads of one step, 5 per wave: weight bricks 4 wt .. 4 wt + 3 of row
+  // block wr (stage bricks 8 wr + ...), and token brick tb = wv (stage brick
+  // 32 + tb; BF16: token group tb, FP8: group tb / 2, low or high half).
+  const int tb = wv;
+  const int tg_of_tb = FP8 ? tb >> 1 : tb;
+  const int tsrc_row = rowsrc[16 * tg_of_tb + r];
+  const uint32_t tkoff = FP8 ? (uint32_t)(16 * j + 8 * (tb & 1)) : (uint32_t)(8 * j);
+  auto issue = [&](int st) {
+    char* stage = Ls[st % 3];
 #pragma unroll
-    for (int c = 0; c < ACT; ++c) {
-      const int ch = tid + c * kPfThreads;
-      const int row = ch / (BK / 16), kc = (ch % (BK / 16)) * 16;
-      const int src = rowtok[row];
-      if (src >= 0) {
-        const uint16_t* p = asrc + (size_t)src * astride + k0 + kc;
-        ra[c][0] = ld16(p);
-        ra[c][1] = ld16(p + 8);
-      } else {
-        ra[c][0] = u32x4{0, 0, 0, 0};
-        ra[c][1] = u32x4{0, 0, 0, 0};
-      }
+    for (int q = 0; q < 4; ++q) {
+      const int bi = 4 * wt + q;
+      bload_lds<0>(wrs, stage + (8 * wr + bi) * 1024, (uint32_t)((bi * nkt + st) * 1024 + lane * 16));
     }
-#pragma unroll
-    for (int c = 0; c < BCT; ++c) {
-      const int ch = tid + c * kPfThreads;     // brick bi = ch / 64 (group bi/2, sub bi%2), lane ch % 64
-      const int bi = ch >> 6, gi = bi >> 1, sub = bi & 1;
-      rb[c] = ld16_nt(bbase + ((size_t)gi * nkt + k0 / KB + sub) * 1024 + (ch & 63) * 16);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int c = 0; c < ACT; ++c) {
-      const int ch = tid + c * kPfThreads;
-      const int row = ch / (BK / 16), kc = (ch % (BK / 16)) * 16;
-      uint16_t* d = &As[buf][row * ASTR + kc];
-      if (FP8) {
-        u32x4 ev, od;
-        split_even_odd(ra[c][0], ra[c][1], ev, od);
-        *reinterpret_cast<u32x4*>(d) = ev;
-        *reinterpret_cast<u32x4*>(d + 8) = od;
-      } else {
-        *reinterpret_cast<u32x4*>(d) = ra[c][0];
-        *reinterpret_cast<u32x4*>(d + 8) = ra[c][1];
-      }
-    }
-#pragma unroll
-    for (int c = 0; c < BCT; ++c) {
-      const int ch = tid + c * kPfThreads;
-      *reinterpret_cast<u32x4*>(&Bs[buf][ch * 16]) = rb[c];
-    }
+    bload_lds<0>(trs, stage + (32 + tb) * 1024,
+                 oob_sel(tsrc_row >= 0, (uint32_t)(((size_t)tsrc_row * K + st * KS + tkoff) * 2)));
   };
 
-  f32x4 acc[4][4];
+  f32x4 acc[8][NTG];
+  f32x4 part[FP8 ? 8 : 1][FP8 ? NTG : 1];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
+  for (int bi = 0; bi < 8; ++bi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4{0, 0, 0, 0};
+    for (int tg = 0; tg < NTG; ++tg) acc[bi][tg] = f32x4{0, 0, 0, 0};
 
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int nsteps = K / BK;
+  // Operand reads from LDS are issued as asm so that the compiler, which
+  // cannot tell the stage being read from the stages still being filled by
+  // the LDS-destination loads, does not wait for every load in flight before
+  // them; the asm waits that follow tie the read registers.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)&Ls[0][0];
+  auto compute = [&](int st) {
+    const uint32_t stage = lds0 + (uint32_t)((st % 3) * SB * 1024);
+    const uint32_t wbase = stage + (8 * wr) * 1024 + lane * 16;
+    const uint32_t tbase = stage + (32 + wt * TBW) * 1024 + lane * 16;
+    u32x4 tf[TBW], wf[8];
+#pragma unroll
+    for (int q = 0; q < TBW; ++q) asm volatile("ds_read_b128 %0, %1" : "=v"(tf[q]) : "v"(tbase + q * 1024));
+#pragma unroll
+    for (int bi = 0; bi < 8; ++bi) asm volatile("ds_read_b128 %0, %1" : "=v"(wf[bi]) : "v"(wbase + bi * 1024));
+    // LDS returns in order: wait for the token bricks and weight brick 0,
+    // then for one more weight brick before each row of MFMAs.
+    if (TBW == 4)
+      asm volatile("s_waitcnt lgkmcnt(7)" : "+v"(tf[0]), "+v"(tf[1]), "+v"(tf[2]), "+v"(tf[3]), "+v"(wf[0]));
+    else
+      asm volatile("s_waitcnt lgkmcnt(7)" : "+v"(tf[0]), "+v"(tf[1]), "+v"(wf[0]));
+    if (FP8 && (st & 1) == 0)
+#pragma unroll
+      for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+        for (int tg = 0; tg < NTG; ++tg) part[bi][tg] = f32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int bi = 0; bi < 8; ++bi) {
+      if (bi == 1) asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(wf[1]));
+      if (bi == 2) asm volatile("s_waitcnt lgkmcnt(5)" : "+v"(wf[2]));
+      if (bi == 3) asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(wf[3]));
+      if (bi == 4) asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(wf[4]));
+      if (bi == 5) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(wf[5]));
+      if (bi == 6) asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(wf[6]));
+      if (bi == 7) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[7]));
+      if (!FP8) {
+#pragma unroll
+        for (int tg = 0; tg < NTG; ++tg) acc[bi][tg] = mfma16x16x32(wf[bi], tf[tg], acc[bi][tg]);
+      } else {
+        u32x4 lo, hi;
+        e4m3x16_to_bf16_nat(wf[bi], lo, hi);
+#pragma unroll
+        for (int tg = 0; tg < NTG; ++tg) {
+          part[bi][tg] = mfma16x16x32(lo, tf[2 * tg], part[bi][tg]);
+          part[bi][tg] = mfma16x16x32(hi, tf[2 * tg + 1], part[bi][tg]);
+        }
+      }
+    }
+    if (FP8 && (st & 1)) {
+      const float sc = scp[st >> 1];
+#pragma unroll
+      for (int bi = 0; bi < 8; ++bi)
+#pragma unroll
+        for (int tg = 0; tg < NTG; ++tg)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[bi][tg][i] += sc * part[bi][tg][i];
+    }
+  };
+
+  // Step st reads stage st % 3.  Before the barrier of step st each wave
+  // waits for its own loads of step st (only step st+1's 5 may remain); the
+  // barrier then also orders every wave's reads of step st-1 before the
+  // loads of step st+2 into the same stage.  A raw barrier: a fence would
+  // wait for all loads in flight.
+  const int nsteps = nkt;
+  issue(0);
+  if (nsteps > 1) issue(1);
   for (int st = 0; st < nsteps; ++st) {
-    const int buf = st & 1;
-    if (st + 1 < nsteps) gload((st + 1) * BK);
-    if (!FP8) {
-#pragma unroll
-      for (int ks = 0; ks < 2; ++ks) {
-        u32x4 af[4], bfr[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-          af[mi] = *reinterpret_cast<const u32x4*>(&As[buf][(wm * 64 + mi * 16 + r) * ASTR + ks * 32 + j * 8]);
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-          bfr[ni] = *reinterpret_cast<const u32x4*>(&Bs[buf][((wn * 4 + ni) * 2 + ks) * 1024 + lane * 16]);
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = mfma16x16x32(af[mi], bfr[ni], acc[mi][ni]);
-      }
-    } else {
-      f32x4 part[4][4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) part[mi][ni] = f32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        u32x4 ae[4], ao[4], be[4], bo[4];
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi) {
-          const uint16_t* p = &As[buf][(wm * 64 + mi * 16 + r) * ASTR + hh * 64 + j * 16];
-          ae[mi] = *reinterpret_cast<const u32x4*>(p);
-          ao[mi] = *reinterpret_cast<const u32x4*>(p + 8);
-        }
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
-          const u32x4 q = *reinterpret_cast<const u32x4*>(&Bs[buf][((wn * 4 + ni) * 2 + hh) * 1024 + lane * 16]);
-          e4m3x16_to_bf16(q, be[ni], bo[ni]);
-        }
-#pragma unroll
-        for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) {
-            part[mi][ni] = mfma16x16x32(ae[mi], be[ni], part[mi][ni]);
-            part[mi][ni] = mfma16x16x32(ao[mi], bo[ni], part[mi][ni]);
-          }
-      }
-      sc_lane = scp[st];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[mi][ni][i] += sc_lane * part[mi][ni][i];
-    }
-    if (st + 1 < nsteps) {
-      lstore(buf ^ 1);
-    }
-    __syncthreads();
+    if (st + 1 < nsteps)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5); expcnt, lgkmcnt not waited on
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (st + 2 < nsteps) issue(st + 2);
+    compute(st);
   }
+  if (!rows_ok) return;
 
-  // ---- epilogue.  Lane holds C[row = 4j + i][col = r] of each 16x16 tile.
+  // ---- epilogue.  acc[bi][tg][i] at lane (r, j): bank row 16 (t0 + bi) + 4 j + i,
+  // pair row TM/2 wt + 16 tg + r.
   if (GATEUP) {
-    // col r < 8: gate, r >= 8: up of output 8*(n0/16 + wn*4 + ni) + (r & 7)
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int tg = 0; tg < NTG; ++tg) {
+      const int row = (TM / 2) * wt + 16 * tg + r;
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni)
+      for (int bi = 0; bi < 8; ++bi) {
+        f32x4 u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float v = acc[mi][ni][i];
-          const float u = __shfl_xor(v, 8, 64);
-          const int row = wm * 64 + mi * 16 + 4 * j + i;
-          if (r < 8 && row < mrows) {
-            const int io = n0 / 2 + (wn * 4 + ni) * 8 + r;
-            a.h[(size_t)(seg + m0 + row) * a.I + io] = f32_to_bf16_rne(silu_f32(v) * u);
-          }
+        for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(acc[bi][tg][i], 32, 64);
+        if (j < 2 && row < mrows) {
+          const int f = 8 * (t0 + bi) + 4 * j;   // first of the lane's 4 features
+          const uint32_t h01 = f32_to_bf16_rne(silu_f32(acc[bi][tg][0]) * u[0]) |
+                               ((uint32_t)f32_to_bf16_rne(silu_f32(acc[bi][tg][1]) * u[1]) << 16);
+          const uint32_t h23 = f32_to_bf16_rne(silu_f32(acc[bi][tg][2]) * u[2]) |
+                               ((uint32_t)f32_to_bf16_rne(silu_f32(acc[bi][tg][3]) * u[3]) << 16);
+          *reinterpret_cast<u32x2*>(a.h + (size_t)(seg + m0 + row) * a.I + f) = u32x2{h01, h23};
         }
+      }
+    }
   } else {
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
+    for (int tg = 0; tg < NTG; ++tg) {
+      const int row = (TM / 2) * wt + 16 * tg + r;
+      if (row < mrows) {
+        const int pos = seg + m0 + row;
+        const float wp = a.w[a.sorted_pair[pos]];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int row = wm * 64 + mi * 16 + 4 * j + i;
-        if (row < mrows) {
-          const int pos = seg + m0 + row;
-          const float wp = a.w[a.sorted_pair[pos]];
-          float* orow = a.o + (size_t)pos * a.H + n0 + wn * 64;
-#pragma unroll
-          for (int ni = 0; ni < 4; ++ni) orow[ni * 16 + r] = wp * acc[mi][ni][i];
+        for (int bi = 0; bi < 8; ++bi) {
+          const int c = 16 * (t0 + bi) + 4 * j;
+          const uint32_t o01 = f32_to_bf16_rne(wp * acc[bi][tg][0]) | ((uint32_t)f32_to_bf16_rne(wp * acc[bi][tg][1]) << 16);
+          const uint32_t o23 = f32_to_bf16_rne(wp * acc[bi][tg][2]) | ((uint32_t)f32_to_bf16_rne(wp * acc[bi][tg][3]) << 16);
+          *reinterpret_cast<u32x2*>(a.o + (size_t)pos * a.H + c) = u32x2{o01, o23};
         }
       }
+    }
   }
 }
 
-// y[t] = sum_j o[pos(t, j)] in pick order (deterministic)
+// y[t] = sum_j o[pos(t, j)] in pick order (deterministic), 8 outputs per thread
 __global__ __launch_bounds__(256) void pf_combine_kernel(PfArgs a) {
   const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  const int per_row = a.H / 4;
+  const int per_row = a.H / 8;
   if (gid >= (size_t)a.T * per_row) return;
-  const int t = (int)(gid / per_row), c = (int)(gid % per_row) * 4;
-  f32x4 s = {0, 0, 0, 0};
+  const int t = (int)(gid / per_row), c = (int)(gid % per_row) * 8;
+  float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int jj = 0; jj < a.k; ++jj) {
     const int pos = a.pair_pos[(size_t)t * a.k + jj];
-    if (pos >= 0) s += *reinterpret_cast<const f32x4*>(a.o + (size_t)pos * a.H + c);
+    if (pos >= 0) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(a.o + (size_t)pos * a.H + c);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        s[2 * q] += __uint_as_float(v[q] << 16);
+        s[2 * q + 1] += __uint_as_float(v[q] & 0xFFFF0000u);
+      }
+    }
   }
-  *reinterpret_cast<f32x4*>(a.y + (size_t)t * a.H + c) = s;
+  float* yr = a.y + (size_t)t * a.H + c;
+  *reinterpret_cast<f32x4*>(yr) = f32x4{s[0], s[1], s[2], s[3]};
+  *reinterpret_cast<f32x4*>(yr + 4) = f32x4{s[4], s[5], s[6], s[7]};
 }
 
 // ================================================================ merge
@@ -865,23 +929,29 @@ static moe_status dec_occupancy(DecOcc* out) {
 }
 
 struct PfWs {
-  size_t cnt, off, nt, tslot, tm0, sp, pp, h, o, total;
-  int max_tiles;
+  size_t hist, cnt, off, mtoff, nt, tslot, tm0, sp, pp, h, o, total;
+  int max_mtiles, n_chunks, tm, chunk;
 };
-static PfWs pf_ws(int T_max, int k, int H, int I, int n_slots) {
+static PfWs pf_ws(int T_max, int k, int H, int I, int n_slots, bool fp8) {
   PfWs w{};
   size_t P = (size_t)T_max * k;
-  w.max_tiles = (int)((P + kBM - 1) / kBM) + n_slots;
+  w.tm = fp8 ? 64 : 128;
+  w.max_mtiles = (int)((P + w.tm - 1) / w.tm) + n_slots;
+  w.chunk = kSortChunk;
+  while ((P + w.chunk - 1) / w.chunk > (size_t)kSortMaxChunks) w.chunk *= 2;
+  w.n_chunks = (int)((P + w.chunk - 1) / w.chunk);
   size_t off = 0;
+  w.hist = off; off = align256(off + 4 * (size_t)w.n_chunks * n_slots);
   w.cnt = off; off = align256(off + 4 * (size_t)n_slots);
   w.off = off; off = align256(off + 4 * (size_t)n_slots);
+  w.mtoff = off; off = align256(off + 4 * (size_t)n_slots);
   w.nt = off; off = align256(off + 4);
-  w.tslot = off; off = align256(off + 4 * (size_t)w.max_tiles);
-  w.tm0 = off; off = align256(off + 4 * (size_t)w.max_tiles);
+  w.tslot = off; off = align256(off + 4 * (size_t)w.max_mtiles);
+  w.tm0 = off; off = align256(off + 4 * (size_t)w.max_mtiles);
   w.sp = off; off = align256(off + 4 * P);
   w.pp = off; off = align256(off + 4 * P);
   w.h = off; off = align256(off + 2 * P * I);
-  w.o = off; off = align256(off + 4 * P * H);
+  w.o = off; off = align256(off + 2 * P * H);
   w.total = off;
   return w;
 }
@@ -900,8 +970,9 @@ extern "C" moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int3
       MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T_max <= %d and T_max*k <= %d", kDecTok, kDecPmax);
     *bytes = dec_ws(T_max, k, H, I, n_slots).total;
   } else if (mode == MOE_FWD_PREFILL) {
-    if (n_slots > 4096) MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs n_slots <= 4096");
-    *bytes = pf_ws(T_max, k, H, I, n_slots).total;
+    if (n_slots > kSortMaxSlots) MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs n_slots <= %d", kSortMaxSlots);
+    const size_t b16 = pf_ws(T_max, k, H, I, n_slots, false).total, b8 = pf_ws(T_max, k, H, I, n_slots, true).total;
+    *bytes = b16 > b8 ? b16 : b8;
   } else {
     MOE_FAIL(MOE_ERR_ARG, "bad mode %u", mode);
   }
@@ -975,34 +1046,43 @@ extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t*
     return MOE_OK;
   }
   if (mode != MOE_FWD_PREFILL) MOE_FAIL(MOE_ERR_ARG, "bad mode %u", mode);
-  if (slots->n_slots > 4096) MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs n_slots <= 4096");
+  if (slots->n_slots > kSortMaxSlots) MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs n_slots <= %d", kSortMaxSlots);
   if (H % 128 || I % 64) MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs H %% 128 == 0 and I %% 64 == 0");
-  PfWs L = pf_ws(T, k, H, I, slots->n_slots);
+  PfWs L = pf_ws(T, k, H, I, slots->n_slots, fp8);
   if (ws_bytes < L.total) MOE_FAIL(MOE_ERR_NO_SPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  if ((size_t)T * H * 2 >= 0x80000000ull || (size_t)T * k * (size_t)(H > I ? H : I) * 2 >= 0x80000000ull)
+    MOE_FAIL(MOE_ERR_SHAPE, "prefill mode needs T*H*2 and T*k*max(H,I)*2 below 2^31 bytes");
   PfArgs a{};
   a.w_gu = slots->w_gate_up; a.w_down = slots->w_down;
   a.s_gate = slots->s_gate; a.s_up = slots->s_up; a.s_down = slots->s_down;
   a.H = H; a.I = I; a.n_slots = slots->n_slots; a.T = T; a.k = k; a.P = T * k;
-  a.max_tiles = L.max_tiles;
+  a.tm = L.tm; a.max_mtiles = L.max_mtiles; a.chunk = L.chunk;
   a.x = x; a.pick_slot = pick_slot; a.w = w; a.y = y;
+  a.hist = (int32_t*)(wsb + L.hist);
   a.cnt = (int32_t*)(wsb + L.cnt);
   a.off = (int32_t*)(wsb + L.off);
-  a.n_tiles = (int32_t*)(wsb + L.nt);
+  a.mtoff = (int32_t*)(wsb + L.mtoff);
+  a.n_mtiles = (int32_t*)(wsb + L.nt);
   a.tile_slot = (int32_t*)(wsb + L.tslot);
   a.tile_m0 = (int32_t*)(wsb + L.tm0);
   a.sorted_pair = (int32_t*)(wsb + L.sp);
   a.pair_pos = (int32_t*)(wsb + L.pp);
   a.h = (uint16_t*)(wsb + L.h);
-  a.o = (float*)(wsb + L.o);
-  pf_sort_kernel<<<1, 1024, 0, stream>>>(a);
-  const size_t ncomb = ((size_t)T * (H / 4) + 255) / 256;
+  a.o = (uint16_t*)(wsb + L.o);
+  pf_count_kernel<<<L.n_chunks, 256, 0, stream>>>(a);
+  pf_scan_kernel<<<1, 1024, 0, stream>>>(a, L.n_chunks);
+  pf_scatter_kernel<<<L.n_chunks, 256, 0, stream>>>(a);
+  const long gu_tiles = (long)L.max_mtiles * ((2 * I + kPfRows - 1) / kPfRows);
+  const long dn_tiles = (long)L.max_mtiles * ((H + kPfRows - 1) / kPfRows);
+  const unsigned g1 = (unsigned)(8 * ((gu_tiles + 7) / 8)), g2 = (unsigned)(8 * ((dn_tiles + 7) / 8));
   if (fp8) {
-    pf_gemm_kernel<true, true><<<dim3(L.max_tiles, I / 64), kPfThreads, 0, stream>>>(a);
-    pf_gemm_kernel<true, false><<<dim3(L.max_tiles, H / 128), kPfThreads, 0, stream>>>(a);
+    pf_gemm_kernel<true, true><<<g1, kPfWaves * 64, 0, stream>>>(a);
+    pf_gemm_kernel<true, false><<<g2, kPfWaves * 64, 0, stream>>>(a);
   } else {
-    pf_gemm_kernel<false, true><<<dim3(L.max_tiles, I / 64), kPfThreads, 0, stream>>>(a);
-    pf_gemm_kernel<false, false><<<dim3(L.max_tiles, H / 128), kPfThreads, 0, stream>>>(a);
+    pf_gemm_kernel<false, true><<<g1, kPfWaves * 64, 0, stream>>>(a);
+    pf_gemm_kernel<false, false><<<g2, kPfWaves * 64, 0, stream>>>(a);
   }
+  const size_t ncomb = ((size_t)T * (H / 8) + 255) / 256;
   pf_combine_kernel<<<(unsigned)ncomb, 256, 0, stream>>>(a);
   MOE_LAUNCHED();
   return MOE_OK;
