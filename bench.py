@@ -34,6 +34,105 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+ROOT = os.path.dirname(os.path.abspath(__file__))
+TRAFFIC_JSON = os.path.join(ROOT, "profiles", "traffic.json")
+COPY_BYTES = 1 << 30
+
+
+def forward_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("forward.hip", "common.h"):
+        with open(os.path.join(ROOT, "routed_expert_cache_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic(key, algorithmic_bytes=None):
+    """HBM bytes per launch of `key` from the committed counter summary, or
+    None when the kernels have changed since the counters were taken.  Where
+    the counted run's launches moved a different algorithmic byte count (the
+    decode trace sample differs), the counted traffic/algorithmic ratio is
+    applied to this run's algorithmic bytes per launch."""
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            t = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    if t.get("source_sha256") != forward_source_hash() or key not in t.get("launches", {}):
+        return None
+    e = t["launches"][key]
+    if algorithmic_bytes is not None and e.get("algorithmic_bytes"):
+        return e["bytes"] / e["algorithmic_bytes"] * algorithmic_bytes
+    return e["bytes"]
+
+
+# kernels that make up one launch of each measured entry point (name prefixes)
+PMC_LAUNCHES = {
+    "decode_bf16_forward": ["void moe::dec_gu_kernel<false", "void moe::dec_dn_kernel<false"],
+    "prefill_bf16_forward": ["moe::pf_count_kernel", "moe::pf_scan_kernel", "moe::pf_scatter_kernel",
+                             "void moe::pf_gemm_kernel<false, true>", "void moe::pf_gemm_kernel<false, false>",
+                             "moe::pf_combine_kernel"],
+}
+
+
+def pmc_summary(fetch_dir, write_dir, bench_json):
+    import csv
+    import glob
+    per = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+        assert files, "no counter_collection.csv under %s" % d
+        vals = {}
+        for r in csv.DictReader(open(files[0])):
+            if r["Counter_Name"] != counter:
+                continue
+            vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        # the calibration copy (a device-to-device copy of COPY_BYTES): the
+        # copy kernel with the largest count
+        copy = max((k for k in vals if "copybuffer" in k.lower()), key=lambda k: max(vals[k]))
+        factor = max(vals[copy]) * 1024.0 / COPY_BYTES      # counter KiB per true KiB
+        per[counter] = dict(vals=vals, factor=factor, copy_kernel=copy)
+    out = {"source_sha256": forward_source_hash(),
+           "calibration": {c: {"copy_kernel": per[c]["copy_kernel"], "copy_bytes": COPY_BYTES,
+                               "counter_kib_per_true_kib": round(per[c]["factor"], 4)} for c in per},
+           "launches": {}}
+    for key, prefixes in PMC_LAUNCHES.items():
+        tot, parts = 0.0, {}
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            v = per[c]["vals"]
+            for pre in prefixes:
+                ks = [k for k in v if k.startswith(pre)]
+                if not ks:
+                    continue
+                avg = sum(sum(v[k]) for k in ks) / sum(len(v[k]) for k in ks)   # KiB per dispatch
+                b = avg * 1024.0 / per[c]["factor"]
+                parts["%s %s" % (pre.replace("void ", "").replace("moe::", ""), c)] = round(b)
+                tot += b
+        if parts:
+            out["launches"][key] = {"bytes": round(tot), "parts": parts}
+    with open(bench_json) as fh:
+        run = json.loads([ln for ln in fh.read().splitlines() if ln.startswith('{"metric"')][-1])
+    if "decode_bf16_forward" in out["launches"]:
+        out["launches"]["decode_bf16_forward"]["algorithmic_bytes"] = run["roofline"]["bytes_per_launch"]
+    out["counted_run"] = {"trace_steps": run["config"]["trace_steps"]}
+    with open(TRAFFIC_JSON, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
+
+
+def calibrate_copy():
+    import torch
+    src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(4):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log("copy calibration: 4 copies of %d bytes" % COPY_BYTES)
+    del src, dst
+    torch.cuda.empty_cache()
+
+
 class HipEvents:
     """Timing events created with hipEventDisableSystemFence: a record on a busy
     stream costs far less GPU time than torch's default events (no
@@ -80,6 +179,12 @@ def parse():
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 decode and FP8 double-buffered prefill runs")
     p.add_argument("--fp8-steps", type=int, default=64)
     p.add_argument("--fp8-warmup", type=int, default=32)
+    p.add_argument("--no-prefill-fp8", action="store_true", help="skip the FP8 double-buffered prefill run")
+    p.add_argument("--calibrate-copy", action="store_true",
+                   help="first run a plain 1 GiB device-to-device copy 4 times (counter calibration)")
+    p.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
+                   help="no GPU run: turn two rocprofv3 --pmc output folders (FETCH_SIZE, WRITE_SIZE) of "
+                        "`bench.py --calibrate-copy ...` and that run's JSON line into profiles/traffic.json")
     return p.parse_args()
 
 
@@ -170,6 +275,7 @@ def run_decode(b, K, W):
         ),
     )
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_HBM_GBPS
+    res["roofline"]["traffic"] = measured_traffic("decode_bf16_forward", res["roofline"]["bytes_per_launch"])
     cache.destroy()
     return res
 
@@ -224,7 +330,8 @@ def run_prefill(b, reps):
         reps=reps, flops_per_layer=flops,
         roofline=dict(kernel="moe_expert_forward prefill (sort + gate/up GEMM + down GEMM + combine)",
                       bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                      frac=ach / PEAK_BF16_TFLOPS, avg_launch_us=fwd_s * 1e6, traffic=None),
+                      frac=ach / PEAK_BF16_TFLOPS, avg_launch_us=fwd_s * 1e6,
+                      traffic=measured_traffic("prefill_bf16_forward")),
     )
 
 
@@ -459,6 +566,9 @@ def cpu_baseline(budget_s):
 
 def main():
     a = parse()
+    if a.pmc_summary:
+        pmc_summary(*a.pmc_summary)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: the expert-slot cache path runs on a single MI355X "
@@ -468,6 +578,8 @@ def main():
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     import routed_expert_cache_amd.binding as b
     assert torch.cuda.is_available(), "needs a GPU"
+    if a.calibrate_copy:
+        calibrate_copy()
     dec = run_decode(b, a.steps, a.warmup)
     line = {
         "metric": METRIC, "value": round(dec["value"], 2), "unit": "GB/s", "n_gpus": 1,
@@ -486,7 +598,7 @@ def main():
     if not a.no_fp8:
         line["decode_fp8"] = run_decode_fp8(b, a.fp8_steps, a.fp8_warmup)
         torch.cuda.empty_cache()
-        if not a.no_prefill:
+        if not a.no_prefill and not a.no_prefill_fp8:
             line["prefill_fp8"] = run_prefill_fp8(b)
             torch.cuda.empty_cache()
     if not a.no_cpu_baseline:

@@ -253,7 +253,9 @@ moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int32_t H, int3
  * (decode: the gfx950 two-codes-per-instruction E4M3 -> BF16 conversion with
  * unit scale; prefill: integer bit operations) and each 128x128 tile's scale
  * is applied once to its block partial sum.  Accumulation is FP32; the
- * SwiGLU activations h are rounded to BF16 before the down projection.
+ * SwiGLU activations h are rounded to BF16 before the down projection, and
+ * in prefill mode each pick's gate-weighted row is rounded to BF16 before a
+ * token's k rows are summed (in FP32, pick order).
  *   mode MOE_FWD_DECODE: T <= 16 and T*k <= 256 (grouped GEMV streaming each
  *     slot once; y is the same bits on every run).
  *   mode MOE_FWD_PREFILL: any T (tokens sorted by slot, grouped GEMM).
