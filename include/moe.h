@@ -250,16 +250,23 @@ moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int32_t H, int3
  * x: device BF16 [T, H]; pick_slot: device int32 [T, k] (slot index in
  * `slots`, -1 = skip); w: device float32 [T, k]; y: device float32 [T, H],
  * fully overwritten.  FP8 weights are expanded exactly to BF16 in registers
- * (decode: the gfx950 two-codes-per-instruction E4M3 -> BF16 conversion with
- * unit scale; prefill: integer bit operations) and each 128x128 tile's scale
- * is applied once to its block partial sum.  Accumulation is FP32; the
+ * (the gfx950 two-codes-per-instruction E4M3 -> BF16 conversion with unit
+ * scale) and each 128x128 tile's scale is applied once to its block partial
+ * sum.  Accumulation is FP32; the
  * SwiGLU activations h are rounded to BF16 before the down projection, and
  * in prefill mode each pick's gate-weighted row is rounded to BF16 before a
  * token's k rows are summed (in FP32, pick order).
  *   mode MOE_FWD_DECODE: T <= 16 and T*k <= 256 (grouped GEMV streaming each
  *     slot once; y is the same bits on every run).
  *   mode MOE_FWD_PREFILL: any T (tokens sorted by slot, grouped GEMM).
- * ws: device workspace of moe_forward_workspace_bytes(T_max >= T, ...).
+ * ws: device workspace of moe_forward_workspace_bytes(T_max >= T, ...),
+ * owned by the caller, 256-byte aligned and ZERO-FILLED before its first
+ * use: decode mode keeps its hand-over counters there and leaves them at
+ * zero on exit, so the same workspace serves any later call on the same
+ * stream without clearing; calls that overlap on one workspace race.  A
+ * decode call whose internal wait timed out (only possible when its
+ * workgroups cannot all be resident, e.g. a shared GPU) sets the first
+ * 32-bit word of ws to a non-zero value and y is then not valid.
  * Requires H, I multiples of 128 (FP8) or of 32 (BF16).  Capturable.
  */
 moe_status moe_expert_forward(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,

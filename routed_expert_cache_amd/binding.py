@@ -251,7 +251,8 @@ def forward_workspace(T_max, k, H, I, n_slots, mode, device="cuda"):
     n = ctypes.c_size_t(0)
     _check(_lib.moe_forward_workspace_bytes(T_max, k, H, I, n_slots, mode, ctypes.byref(n)),
            "moe_forward_workspace_bytes")
-    return torch.empty((max(n.value, 256),), dtype=torch.uint8, device=device)
+    # zero-filled: decode mode keeps self-resetting counters in it
+    return torch.zeros((max(n.value, 256),), dtype=torch.uint8, device=device)
 
 
 def expert_forward(slots_c, x, pick_slot, w, mode, ws, y=None, stream=None):

@@ -203,139 +203,41 @@ __device__ void wave_plan(const int32_t* __restrict__ pick_slot, const float* __
   if (lane == 0) *s_G = base[kDecPPL];
 }
 
-// gate/up + SwiGLU.  Task (group g, brick row t): 16 rows of the gate/up bank
-// (gate rows 8t..8t+7 above the same up rows) over all H.  The NW waves take
-// 1/NW of the row's 2-brick steps each and meet in LDS, where wave 0 forms
-// h[g][token][8t..8t+7] = silu(gate) * up in BF16.  A workgroup's tasks form
-// one continuous step sequence per wave, so the loads of the next task are in
-// flight while the current one is reduced.  The first pass of workgroups also
-// zeroes y for the down launch.
-template <bool FP8, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void dec_gu_kernel(DecArgs a) {
-  __shared__ int s_gslot[kDecPmax];
-  __shared__ int s_G;
-  __shared__ unsigned long long s_tab[kPlanTab];
-  __shared__ f32x4 red[2][NW][64];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  const int r = lane & 15, j = lane >> 4;
-  const int H = a.H, I = a.I, T = a.T;
-  for (int i = blockIdx.x * NW * 64 + tid; i < T * H; i += gridDim.x * NW * 64) a.y[i] = 0.f;
-  if (wv == 0) wave_plan(a.pick_slot, a.w, T * a.k, a.k, a.n_slots, a.G_max, s_gslot, nullptr, &s_G, s_tab);
-  __syncthreads();
-  const int G = s_G;
-  const int RA = I / 8;
-  const int nkt = FP8 ? H / 64 : H / 32;     // bricks per row
-  const int S = (nkt + 1) >> 1;              // 2-brick steps per row
-  const int SW = (S + NW - 1) / NW;          // steps per wave per task
-  const int s_lo = wv * SW;
-  const size_t gu_bytes = (size_t)2 * I * H * (FP8 ? 1 : 2);
-  const int ntask = G * RA;
-  const int ntk = ntask > (int)blockIdx.x ? (ntask - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-  const int nsteps = ntk * SW;
-  const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)(T * H * 2));
-  const bool tok = r < T;
-  constexpr int XN = FP8 ? 4 : 2;
-  u32x4 wb[D][2], xb[D][XN];
-  float sb[D][2];
-  int i_tk = 0, i_l = 0;   // issue position: task of this workgroup, step within the wave's share
-  auto issue = [&](int d) {
-    const int task = (int)blockIdx.x + i_tk * (int)gridDim.x;
-    const int s = s_lo + i_l;
-    const bool ok = i_tk < ntk && s < S;
-    const int tt = ok ? task : 0;
-    const int g = tt / RA, t = tt - g * RA;
-    const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;   // slot 0 always exists
-    const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc((const char*)a.w_gu + (size_t)slot * gu_bytes + (size_t)t * nkt * 1024, (uint32_t)(nkt * 1024));
-    const uint32_t wo = oob_sel(ok, (uint32_t)s * 2048u + lane * 16u);
-    wb[d][0] = bload_nt(wr, wo);
-    wb[d][1] = bload_nt(wr, oob_sel(ok, wo + 1024u));
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int k0 = FP8 ? 128 * s + 64 * b : 64 * s + 32 * b;
-      const bool xo = ok && tok && k0 < H;
-      const uint32_t off = oob_sel(xo, (uint32_t)(r * H + k0 + (FP8 ? 16 : 8) * j) * 2u);
-      if (FP8) {
-        xb[d][2 * b] = bload(xr, off);
-        xb[d][2 * b + 1] = bload(xr, oob_sel(xo, off + 16u));
-      } else {
-        xb[d][b] = bload(xr, off);
-      }
-    }
-    if (FP8) {   // block scales of the gate rows and of the up rows at this K step (scalar loads)
-      const size_t si = ((size_t)slot * (I / 128) + (8 * t) / 128) * (H / 128) + (ok ? s : 0);
-      sb[d][0] = a.s_gate[si];
-      sb[d][1] = a.s_up[si];
-    }
-    if (++i_l == SW) {
-      i_l = 0;
-      ++i_tk;
-    }
-  };
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue(d);
-  f32x4 acc = {0, 0, 0, 0};
-  int c_tk = 0, c_l = 0;
-  for (int i0 = 0; i0 < nsteps; i0 += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (i0 + d < nsteps) {
-        if (!FP8) {
-          acc = mfma16x16x32(wb[d][0], xb[d][0], acc);
-          acc = mfma16x16x32(wb[d][1], xb[d][1], acc);
-        } else {
-          f32x4 p = {0, 0, 0, 0};
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            u32x4 lo, hi;
-            e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
-            p = mfma16x16x32(lo, xb[d][2 * b], p);
-            p = mfma16x16x32(hi, xb[d][2 * b + 1], p);
-          }
-          const float sc = j < 2 ? sb[d][0] : sb[d][1];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] += sc * p[q];
-        }
-        if (c_l == SW - 1) {   // end of a task: reduce over the waves, SwiGLU, h
-          const int task = (int)blockIdx.x + c_tk * (int)gridDim.x;
-          const int g = task / RA, t = task - g * RA;
-          f32x4(&rb)[NW][64] = red[c_tk & 1];
-          rb[wv][lane] = acc;
-          __syncthreads();
-          if (wv == 0 && j < 2 && tok) {
-            f32x4 Gv = rb[0][lane], Uv = rb[0][lane + 32];
-#pragma unroll
-            for (int w2 = 1; w2 < NW; ++w2) {
-              Gv += rb[w2][lane];
-              Uv += rb[w2][lane + 32];
-            }
-            uint16_t* hrow = a.h + ((size_t)g * kDecTok + r) * I + 8 * t + 4 * j;
-            const uint32_t h01 = f32_to_bf16_rne(silu_f32(Gv[0]) * Uv[0]) | ((uint32_t)f32_to_bf16_rne(silu_f32(Gv[1]) * Uv[1]) << 16);
-            const uint32_t h23 = f32_to_bf16_rne(silu_f32(Gv[2]) * Uv[2]) | ((uint32_t)f32_to_bf16_rne(silu_f32(Gv[3]) * Uv[3]) << 16);
-            *reinterpret_cast<u32x2*>(hrow) = u32x2{h01, h23};
-          }
-          acc = f32x4{0, 0, 0, 0};
-          c_l = 0;
-          ++c_tk;
-        } else {
-          ++c_l;
-        }
-      }
-      issue(d);
-    }
-  }
-}
+// ---------------------------------------------------------------- fused decode
+// One launch evaluates both projections: a grid of resident workgroups walks
+// one task list round-robin, first the gate/up tasks (group g, brick row t),
+// then the down tasks (16 output rows, half of the (group, K) steps).  A
+// workgroup takes its tasks in list order, so every gate/up task is finished
+// or in progress before any workgroup waits for one.
+//
+// Hand-over without a reset launch.  A gate/up task writes its h values with
+// device-coherent (write-through) stores, waits for them, and counts itself
+// in done[g]; the task that completes group g (old value I/8 - 1) clears
+// done[g] and counts the group in `all`; the task that completes the last
+// group clears `all` and raises go[b] for every workgroup b that holds a
+// down task.  A down workgroup first loads the weights of its first D steps,
+// then polls its own go[b] (one address per poller, so the polls stay off
+// the streams' memory channels), clears it, and only then loads h.  Every
+// control word is back at 0 when the launch ends, so a workspace that starts
+// zero-filled stays valid.  A poll is bounded: on time-out the workgroup
+// flags the workspace error word and goes on.  The gate/up tasks of group 0
+// zero y before they count themselves (workgroup 0 does it when no pick is
+// on the GPU); down sums are added into y with two float atomics per
+// element (one per half), which commute exactly: y has the same bits on
+// every run.
+constexpr int kCtrlStride = 16;                     // one control word per 64 bytes
+constexpr int kDecGridMax = 4096;                   // go flags
+constexpr uint32_t kPollLimit = 1u << 22;
 
-// down projection + gate weights.  Task (brick row t of H, half): the output
-// row's steps over (group, 2-brick K step) are split in two halves; the NW
-// waves take 1/NW of the half each, scale each step's sum by the token's gate
-// weight (and the FP8 block scale), meet in LDS, and wave 0 adds the 16 x T
-// partial into y, zeroed by the gate/up launch.  Exactly two additions land on
-// each y element and two additions into 0 commute exactly, so y has the same
-// bits whichever half lands first.  Continuous per-wave step sequence as in
-// the gate/up launch.
+struct DecWsDev {
+  uint32_t* err;          // [1] sticky error word
+  uint32_t* done;         // [kDecPmax * kCtrlStride] per-group count of finished gate/up tasks
+  uint32_t* all;          // [1] finished groups
+  uint32_t* go;           // [kDecGridMax * kCtrlStride] per-workgroup start signal of the down phase
+};
+
 template <bool FP8, int D, int NW>
-__global__ __launch_bounds__(NW * 64) void dec_dn_kernel(DecArgs a) {
+__global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev c) {
   __shared__ int s_gslot[kDecPmax];
   __shared__ float s_gw[kDecPmax * kDecTok];
   __shared__ int s_G;
@@ -347,103 +249,266 @@ __global__ __launch_bounds__(NW * 64) void dec_dn_kernel(DecArgs a) {
   if (wv == 0) wave_plan(a.pick_slot, a.w, T * a.k, a.k, a.n_slots, a.G_max, s_gslot, s_gw, &s_G, s_tab);
   __syncthreads();
   const int G = s_G;
-  const int nkt = FP8 ? I / 64 : I / 32;     // bricks per (row, slot)
-  const int SB = (nkt + 1) >> 1;             // steps per (row, group)
-  const int n = G * SB;                      // steps per output row
-  const int SWB = ((n + 1) / 2 + NW - 1) / NW;   // steps per wave per task (larger half)
-  const size_t dn_bytes = (size_t)H * I * (FP8 ? 1 : 2);
-  const int ntask = 2 * (H / 16);
-  const int ntk = ntask > (int)blockIdx.x ? (ntask - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x : 0;
-  const int nsteps = ntk * SWB;
-  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.h, (uint32_t)(2u * a.G_max * kDecTok * I));
+  if (G == 0 && blockIdx.x == 0)
+    for (int i = tid; i < T * H; i += NW * 64) a.y[i] = 0.f;
   const bool tok = r < T;
   constexpr int XN = FP8 ? 4 : 2;
-  u32x4 wb[D][2], hb[D][XN];
-  float fb[D];
-  int i_tk = 0, i_l = 0;
-  auto issue = [&](int d) {
-    const int task = (int)blockIdx.x + i_tk * (int)gridDim.x;
-    const int t = task >> 1, half = task & 1;
-    const int lo = half ? n / 2 : 0, hi = half ? n : n / 2;
-    const int q = lo + wv * SWB + i_l;
-    const bool ok = i_tk < ntk && i_l < SWB && wv * SWB + i_l < hi - lo;
-    (void)q;
-    const int qq = ok ? q : 0;
-    const int g = qq / SB, s = qq - g * SB;
-    const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;   // slot 0 always exists
-    const int tr = ok ? t : 0;
-    const __amdgpu_buffer_rsrc_t wr =
-        make_rsrc((const char*)a.w_down + (size_t)slot * dn_bytes + (size_t)tr * nkt * 1024, (uint32_t)(nkt * 1024));
-    const uint32_t wo = oob_sel(ok, (uint32_t)s * 2048u + lane * 16u);
-    wb[d][0] = bload_nt(wr, wo);
-    wb[d][1] = bload_nt(wr, oob_sel(ok, wo + 1024u));
-    const uint32_t hrow = (uint32_t)((g * kDecTok + r) * I);
+  const int RA = I / 8;
+  const int nA = G * RA, nB = 2 * (H / 16);
+  const int b0 = (int)blockIdx.x, gs = (int)gridDim.x;
+  const int myA = nA > b0 ? (nA - b0 + gs - 1) / gs : 0;                  // my tasks below nA
+  const int myAll = nA + nB > b0 ? (nA + nB - b0 + gs - 1) / gs : 0;
+  const int myB = myAll - myA;
+  u32x4 wb[D][2], ob[D][XN];   // weight bricks and the other operand (x or h) of D steps
+
+  // ================= phase A: gate/up + SwiGLU
+  {
+    const int nkt = FP8 ? H / 64 : H / 32;
+    const int S = (nkt + 1) >> 1;
+    const int SW = (S + NW - 1) / NW;
+    const int s_lo = wv * SW;
+    const size_t gu_bytes = (size_t)2 * I * H * (FP8 ? 1 : 2);
+    const int nsteps = myA * SW;
+    const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)(T * H * 2));
+    const __amdgpu_buffer_rsrc_t hw = make_rsrc(a.h, (uint32_t)(2u * a.G_max * kDecTok * I));
+    const __amdgpu_buffer_rsrc_t yw = make_rsrc(a.y, (uint32_t)(4u * T * H));
+    const __amdgpu_buffer_rsrc_t gow = make_rsrc(c.go, (uint32_t)(4u * kDecGridMax * kCtrlStride));
+    float sb[D][2];
+    int i_tk = 0, i_l = 0;
+    auto issue = [&](int d) {
+      const int task = b0 + i_tk * gs;
+      const int s = s_lo + i_l;
+      const bool ok = i_tk < myA && s < S;
+      const int tt = ok ? task : 0;
+      const int g = tt / RA, t = tt - g * RA;
+      const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;   // slot 0 always exists
+      const __amdgpu_buffer_rsrc_t wr =
+          make_rsrc((const char*)a.w_gu + (size_t)slot * gu_bytes + (size_t)t * nkt * 1024, (uint32_t)(nkt * 1024));
+      const uint32_t wo = oob_sel(ok, (uint32_t)s * 2048u + lane * 16u);
+      wb[d][0] = bload_nt(wr, wo);
+      wb[d][1] = bload_nt(wr, oob_sel(ok, wo + 1024u));
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int k0 = FP8 ? 128 * s + 64 * b : 64 * s + 32 * b;
-      const bool ho = ok && tok && k0 < I;
-      const uint32_t off = oob_sel(ho, (hrow + k0 + (FP8 ? 16 : 8) * j) * 2u);
-      if (FP8) {
-        hb[d][2 * b] = bload(hr, off);
-        hb[d][2 * b + 1] = bload(hr, oob_sel(ho, off + 16u));
-      } else {
-        hb[d][b] = bload(hr, off);
-      }
-    }
-    float f = ok ? s_gw[g * kDecTok + r] : 0.f;
-    if (FP8) f *= a.s_down[((size_t)slot * (H / 128) + (16 * tr) / 128) * (I / 128) + s];
-    fb[d] = f;
-    if (++i_l == SWB) {
-      i_l = 0;
-      ++i_tk;
-    }
-  };
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue(d);
-  f32x4 acc = {0, 0, 0, 0};
-  int c_tk = 0, c_l = 0;
-  for (int i0 = 0; i0 < nsteps; i0 += D) {
-#pragma unroll
-    for (int d = 0; d < D; ++d) {
-      if (i0 + d < nsteps) {
-        f32x4 p = {0, 0, 0, 0};
-        if (!FP8) {
-          p = mfma16x16x32(wb[d][0], hb[d][0], p);
-          p = mfma16x16x32(wb[d][1], hb[d][1], p);
+      for (int b = 0; b < 2; ++b) {
+        const int k0 = FP8 ? 128 * s + 64 * b : 64 * s + 32 * b;
+        const bool xo = ok && tok && k0 < H;
+        const uint32_t off = oob_sel(xo, (uint32_t)(r * H + k0 + (FP8 ? 16 : 8) * j) * 2u);
+        if (FP8) {
+          ob[d][2 * b] = bload(xr, off);
+          ob[d][2 * b + 1] = bload(xr, oob_sel(xo, off + 16u));
         } else {
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {
-            u32x4 lo, hi;
-            e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
-            p = mfma16x16x32(lo, hb[d][2 * b], p);
-            p = mfma16x16x32(hi, hb[d][2 * b + 1], p);
-          }
-        }
-        const float f = fb[d];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) acc[q] += f * p[q];
-        if (c_l == SWB - 1) {   // end of a task: reduce over the waves, add into y
-          const int task = (int)blockIdx.x + c_tk * (int)gridDim.x;
-          const int t = task >> 1;
-          f32x4(&rb)[NW][64] = red[c_tk & 1];
-          rb[wv][lane] = acc;
-          __syncthreads();
-          if (wv == 0 && tok) {
-            f32x4 Y = rb[0][lane];
-#pragma unroll
-            for (int w2 = 1; w2 < NW; ++w2) Y += rb[w2][lane];
-            float* yr = a.y + (size_t)r * H + 16 * t + 4 * j;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) atomicAdd(yr + q, Y[q]);
-          }
-          acc = f32x4{0, 0, 0, 0};
-          c_l = 0;
-          ++c_tk;
-        } else {
-          ++c_l;
+          ob[d][b] = bload(xr, off);
         }
       }
-      issue(d);
+      if (FP8) {   // block scales of the gate rows and of the up rows at this K step
+        const size_t si = ((size_t)slot * (I / 128) + (8 * t) / 128) * (H / 128) + (ok ? s : 0);
+        sb[d][0] = a.s_gate[si];
+        sb[d][1] = a.s_up[si];
+      }
+      if (++i_l == SW) {
+        i_l = 0;
+        ++i_tk;
+      }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue(d);
+    f32x4 acc = {0, 0, 0, 0};
+    int c_tk = 0, c_l = 0;
+    for (int i0 = 0; i0 < nsteps; i0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (i0 + d < nsteps) {
+          if (!FP8) {
+            acc = mfma16x16x32(wb[d][0], ob[d][0], acc);
+            acc = mfma16x16x32(wb[d][1], ob[d][1], acc);
+          } else {
+            f32x4 p = {0, 0, 0, 0};
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              u32x4 lo, hi;
+              e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
+              p = mfma16x16x32(lo, ob[d][2 * b], p);
+              p = mfma16x16x32(hi, ob[d][2 * b + 1], p);
+            }
+            const float sc = j < 2 ? sb[d][0] : sb[d][1];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] += sc * p[q];
+          }
+          if (c_l == SW - 1) {   // end of a task: reduce over the waves, SwiGLU, h, count
+            const int task = b0 + c_tk * gs;
+            const int g = task / RA, t = task - g * RA;
+            f32x4(&rb)[NW][64] = red[c_tk & 1];
+            rb[wv][lane] = acc;
+            __syncthreads();
+            if (wv == 0) {
+              if (j < 2 && tok) {
+                f32x4 Gv = rb[0][lane], Uv = rb[0][lane + 32];
+#pragma unroll
+                for (int w2 = 1; w2 < NW; ++w2) {
+                  Gv += rb[w2][lane];
+                  Uv += rb[w2][lane + 32];
+                }
+                const uint32_t h01 = f32_to_bf16_rne(silu_f32(Gv[0]) * Uv[0]) |
+                                     ((uint32_t)f32_to_bf16_rne(silu_f32(Gv[1]) * Uv[1]) << 16);
+                const uint32_t h23 = f32_to_bf16_rne(silu_f32(Gv[2]) * Uv[2]) |
+                                     ((uint32_t)f32_to_bf16_rne(silu_f32(Gv[3]) * Uv[3]) << 16);
+                // device-coherent store (written through to memory), so no L2 write-back is needed
+                __builtin_amdgcn_raw_buffer_store_b64(u32x2{h01, h23}, hw,
+                                                      (uint32_t)((((size_t)g * kDecTok + r) * I + 8 * t + 4 * j) * 2), 0, 16);
+              }
+              if (g == 0) {   // group 0's tasks zero y (device-coherent stores) before they count themselves
+                const int n = T * H, z = (n + RA - 1) / RA;
+                for (int i = t * z + lane; i < min(n, (t + 1) * z); i += 64)
+                  __builtin_amdgcn_raw_buffer_store_b32(0u, yw, (uint32_t)i * 4u, 0, 16);
+              }
+              __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores above have completed
+              __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // and stay before the count
+              bool last = false;
+              if (lane == 0 && atomicAdd(&c.done[g * kCtrlStride], 1u) == (uint32_t)RA - 1u) {
+                // no other task of g is left: clear its counter for the next launch
+                __hip_atomic_store(&c.done[g * kCtrlStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                last = atomicAdd(c.all, 1u) == (uint32_t)G - 1u;
+                if (last) __hip_atomic_store(c.all, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+              }
+              if (__ballot(last)) {   // every group is done: start the down phase
+                for (int tb = nA + lane; tb < nA + nB; tb += 64)
+                  __builtin_amdgcn_raw_buffer_store_b32(1u, gow, (uint32_t)((tb % gs) * kCtrlStride * 4), 0, 16);
+              }
+            }
+            acc = f32x4{0, 0, 0, 0};
+            c_l = 0;
+            ++c_tk;
+          } else {
+            ++c_l;
+          }
+        }
+        issue(d);
+      }
+    }
+  }
+
+  // ================= phase B: down projection + gate weights
+  if (myB > 0) {
+    const int nkt = FP8 ? I / 64 : I / 32;
+    const int SB = (nkt + 1) >> 1;
+    const int n = G * SB;
+    const int SWB = ((n + 1) / 2 + NW - 1) / NW;
+    const size_t dn_bytes = (size_t)H * I * (FP8 ? 1 : 2);
+    const int nsteps = myB * SWB;
+    const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.h, (uint32_t)(2u * a.G_max * kDecTok * I));
+    float fb[D];
+    int qg[D], qs[D];
+    bool qok[D];
+    int i_tk = 0, i_l = 0;
+    auto issue_w = [&](int d) {   // weights of the next step; remembers its (group, step)
+      const int task = b0 + (myA + i_tk) * gs - nA;
+      const int t = task >> 1, half = task & 1;
+      const int lo = half ? n / 2 : 0, hi = half ? n : n / 2;
+      const int q = lo + wv * SWB + i_l;
+      const bool ok = i_tk < myB && wv * SWB + i_l < hi - lo;
+      const int qq = ok ? q : 0;
+      const int g = qq / SB, s = qq - g * SB;
+      const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;
+      const int tr = ok ? t : 0;
+      const __amdgpu_buffer_rsrc_t wr =
+          make_rsrc((const char*)a.w_down + (size_t)slot * dn_bytes + (size_t)tr * nkt * 1024, (uint32_t)(nkt * 1024));
+      const uint32_t wo = oob_sel(ok, (uint32_t)s * 2048u + lane * 16u);
+      wb[d][0] = bload_nt(wr, wo);
+      wb[d][1] = bload_nt(wr, oob_sel(ok, wo + 1024u));
+      float f = ok ? s_gw[g * kDecTok + r] : 0.f;
+      if (FP8) f *= a.s_down[((size_t)slot * (H / 128) + (16 * tr) / 128) * (I / 128) + s];
+      fb[d] = f;
+      qg[d] = g;
+      qs[d] = s;
+      qok[d] = ok;
+      if (++i_l == SWB) {
+        i_l = 0;
+        ++i_tk;
+      }
+    };
+    auto issue_h = [&](int d) {   // the h operand of the step issue_w(d) took
+      const int g = qg[d], s = qs[d];
+      const uint32_t hrow = (uint32_t)((g * kDecTok + r) * I);
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        const int k0 = FP8 ? 128 * s + 64 * b : 64 * s + 32 * b;
+        const bool ho = qok[d] && tok && k0 < I;
+        const uint32_t off = oob_sel(ho, (hrow + k0 + (FP8 ? 16 : 8) * j) * 2u);
+        if (FP8) {
+          ob[d][2 * b] = bload(hr, off);
+          ob[d][2 * b + 1] = bload(hr, oob_sel(ho, off + 16u));
+        } else {
+          ob[d][b] = bload(hr, off);
+        }
+      }
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue_w(d);
+    // wait for the start signal of the down phase (bounded)
+    if (wv == 0 && G > 0) {
+      uint32_t* flag = c.go + (size_t)b0 * kCtrlStride;
+      uint32_t it = 0;
+      for (;;) {
+        uint32_t v = 0;
+        if (lane == 0) v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__shfl(v, 0, 64)) break;
+        if (++it >= kPollLimit) {
+          if (lane == 0) atomicOr(c.err, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(16);
+      }
+      if (lane == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // h written on other XCDs is read from memory
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < D; ++d) issue_h(d);
+    f32x4 acc = {0, 0, 0, 0};
+    int c_tk = 0, c_l = 0;
+    for (int i0 = 0; i0 < nsteps; i0 += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (i0 + d < nsteps) {
+          f32x4 p = {0, 0, 0, 0};
+          if (!FP8) {
+            p = mfma16x16x32(wb[d][0], ob[d][0], p);
+            p = mfma16x16x32(wb[d][1], ob[d][1], p);
+          } else {
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              u32x4 lo, hi;
+              e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
+              p = mfma16x16x32(lo, ob[d][2 * b], p);
+              p = mfma16x16x32(hi, ob[d][2 * b + 1], p);
+            }
+          }
+          const float f = fb[d];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) acc[q] += f * p[q];
+          if (c_l == SWB - 1) {   // end of a task: reduce over the waves, add into y
+            const int task = b0 + (myA + c_tk) * gs - nA;
+            const int t = task >> 1;
+            f32x4(&rb)[NW][64] = red[c_tk & 1];
+            rb[wv][lane] = acc;
+            __syncthreads();
+            if (wv == 0 && tok) {
+              f32x4 Y = rb[0][lane];
+#pragma unroll
+              for (int w2 = 1; w2 < NW; ++w2) Y += rb[w2][lane];
+              float* yr = a.y + (size_t)r * H + 16 * t + 4 * j;
+#pragma unroll
+              for (int q = 0; q < 4; ++q) atomicAdd(yr + q, Y[q]);
+            }
+            acc = f32x4{0, 0, 0, 0};
+            c_l = 0;
+            ++c_tk;
+          } else {
+            ++c_l;
+          }
+        }
+        issue_w(d);
+        issue_h(d);
+      }
     }
   }
 }
@@ -884,12 +949,16 @@ __global__ __launch_bounds__(256) void e4m3_expand_kernel(const uint8_t* __restr
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct DecWs {
-  size_t h, total;
+  size_t err, done, all, go, h, total;
 };
 static DecWs dec_ws(int T_max, int k, int H, int I, int n_slots) {
   DecWs w{};
   int G = T_max * k < n_slots ? T_max * k : n_slots;
   size_t off = 0;
+  w.err = off; off = align256(off + 4);
+  w.done = off; off = align256(off + 4 * (size_t)kDecPmax * kCtrlStride);
+  w.all = off; off = align256(off + 4);
+  w.go = off; off = align256(off + 4 * (size_t)kDecGridMax * kCtrlStride);
   w.h = off; off = align256(off + 2 * (size_t)G * kDecTok * I);
   w.total = off;
   return w;
@@ -898,11 +967,10 @@ static DecWs dec_ws(int T_max, int k, int H, int I, int n_slots) {
 // Resident workgroups per CU of each decode kernel, and the CU count, per device.
 struct DecOcc {
   int cus = 0;
-  int gu[2] = {0, 0}, dn[2] = {0, 0};
+  int fu[2] = {0, 0};
 };
-constexpr int kDecD_BF16 = 4, kDecD_FP8 = 4;   // register-ring depth in 2-brick steps (gate/up)
-constexpr int kDnD_BF16 = 4, kDnD_FP8 = 4;     // (down)
-constexpr int kGuW = 4, kDnW = 16;              // waves per workgroup
+constexpr int kDecD = 4;   // register-ring depth in 2-brick steps
+constexpr int kDecW = 4;   // waves per workgroup
 static std::mutex g_occ_mu;
 static DecOcc g_occ[64];
 static moe_status dec_occupancy(DecOcc* out) {
@@ -914,14 +982,10 @@ static moe_status dec_occupancy(DecOcc* out) {
   if (!o.cus) {
     int cus = 0;
     MOE_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.gu[0], dec_gu_kernel<false, kDecD_BF16, kGuW>, kGuW * 64, 0));
-    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.gu[1], dec_gu_kernel<true, kDecD_FP8, kGuW>, kGuW * 64, 0));
-    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.dn[0], dec_dn_kernel<false, kDnD_BF16, kDnW>, kDnW * 64, 0));
-    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.dn[1], dec_dn_kernel<true, kDnD_FP8, kDnW>, kDnW * 64, 0));
-    for (int i = 0; i < 2; ++i) {
-      if (o.gu[i] < 1) o.gu[i] = 1;
-      if (o.dn[i] < 1) o.dn[i] = 1;
-    }
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0], dec_fused_kernel<false, kDecD, kDecW>, kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1], dec_fused_kernel<true, kDecD, kDecW>, kDecW * 64, 0));
+    for (int i = 0; i < 2; ++i)
+      if (o.fu[i] < 1) o.fu[i] = 1;
     o.cus = cus > 0 ? cus : 1;
   }
   *out = o;
@@ -1031,17 +1095,18 @@ extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t*
     a.x = x; a.pick_slot = pick_slot; a.w = w; a.y = y;
     a.h = (uint16_t*)(wsb + L.h);
     a.G_max = T * k < slots->n_slots ? T * k : slots->n_slots;
+    DecWsDev c{};
+    c.err = (uint32_t*)(wsb + L.err);
+    c.done = (uint32_t*)(wsb + L.done);
+    c.all = (uint32_t*)(wsb + L.all);
+    c.go = (uint32_t*)(wsb + L.go);
     const int f = fp8 ? 1 : 0;
-    const long gu_tasks = (long)a.G_max * (I / 8), dn_tasks = 2L * (H / 16);
-    const unsigned g1 = (unsigned)std::min<long>(gu_tasks, (long)occ.cus * occ.gu[f]);
-    const unsigned g2 = (unsigned)std::min<long>(dn_tasks, (long)occ.cus * occ.dn[f]);
-    if (fp8) {
-      dec_gu_kernel<true, kDecD_FP8, kGuW><<<g1, kGuW * 64, 0, stream>>>(a);
-      dec_dn_kernel<true, kDnD_FP8, kDnW><<<g2, kDnW * 64, 0, stream>>>(a);
-    } else {
-      dec_gu_kernel<false, kDecD_BF16, kGuW><<<g1, kGuW * 64, 0, stream>>>(a);
-      dec_dn_kernel<false, kDnD_BF16, kDnW><<<g2, kDnW * 64, 0, stream>>>(a);
-    }
+    const long tasks = (long)a.G_max * (I / 8) + 2L * (H / 16);
+    const unsigned g1 = (unsigned)std::min<long>(std::min<long>(tasks, (long)occ.cus * occ.fu[f]), kDecGridMax);
+    if (fp8)
+      dec_fused_kernel<true, kDecD, kDecW><<<g1, kDecW * 64, 0, stream>>>(a, c);
+    else
+      dec_fused_kernel<false, kDecD, kDecW><<<g1, kDecW * 64, 0, stream>>>(a, c);
     MOE_LAUNCHED();
     return MOE_OK;
   }

@@ -22,9 +22,18 @@ def _slots_identity(b, bank, wtype):
 def _run_forward(b, pool, x_bits, pick_slot, w, mode, T_max=None):
     T, k = pick_slot.shape
     ws = b.forward_workspace(T_max or T, k, pool.H, pool.I, pool.n_slots, mode)
-    y = b.expert_forward(pool.c, dev(x_bits), dev(pick_slot.astype(np.int32)), dev(w.astype(np.float32)), mode, ws)
+    args = (pool.c, dev(x_bits), dev(pick_slot.astype(np.int32)), dev(w.astype(np.float32)), mode, ws)
+    y = b.expert_forward(*args)
     torch.cuda.synchronize()
-    return y.cpu().numpy()
+    out = y.cpu().numpy()
+    if mode == b.FWD_DECODE:
+        # the hand-over counters reset themselves: a second call on the same
+        # workspace gives the same bits, and the error word stays clear
+        y2 = b.expert_forward(*args)
+        torch.cuda.synchronize()
+        assert np.array_equal(y2.cpu().numpy().view(np.uint32), out.view(np.uint32))
+        assert int(ws[:4].view(torch.int32).item()) == 0
+    return out
 
 
 # ---------------------------------------------------------------- decode, BF16
