@@ -219,8 +219,7 @@ def run_decode(b, K, W):
     pick = out.pick_slot.view(1, k)
 
     def layer_step(cache, s, l, ev=None, i=0):
-        b.route_topk(lg[s, l], k, ids, w)
-        cache.step(l, ids, out, copy=False)
+        cache.route_step(l, lg[s, l], ids, w, out, copy=False)      # router + cache step, one launch
         if ev:
             ev.record(3 * i)
         cache.fill(out)
@@ -402,8 +401,7 @@ def run_decode_fp8(b, K, W, Ts=(1, 4, 16)):
 
         def step(s, i=None):
             for l in range(L):
-                b.route_topk(lg[s, l], k, ids, w)
-                cache.step(l, ids, out, copy=False)
+                cache.route_step(l, lg[s, l], ids, w, out, copy=False)
                 if l == 0:
                     flush.add_(1.0)                                  # evict the MALL (512 MB read + write)
                     if i is not None:

@@ -202,6 +202,20 @@ moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t* ids, int3
                           uint32_t flags, const moe_step_out* out, hipStream_t stream);
 
 /*
+ * Router and cache step in one launch: the same results as
+ * moe_route_topk(logits, T, E, k, ids, w) followed by
+ * moe_cache_step(c, layer, ids, T, flags, out) (bit for bit: the same
+ * selection and softmax code), with one kernel instead of two on the decode
+ * path ([FT] section "Device-side 缓存控制": routing feeds the one control
+ * kernel; [FTK] GPU-router paragraph).  logits: device float32 [T, E];
+ * ids: device int32 [T, k] and w: device float32 [T, k], both written.
+ * Needs E <= 1024 and k <= 32.  Capturable.
+ */
+moe_status moe_cache_route_step(moe_cache_t c, int32_t layer, const float* logits, int32_t T,
+                                int32_t* ids, float* w, uint32_t flags, const moe_step_out* out,
+                                hipStream_t stream);
+
+/*
  * The fused fill copy alone: copy every bank of the out->counts[MOE_CNT_FILL]
  * experts listed in out->fill_id / out->fill_slot from the pinned host pool
  * into their slots, with one fixed-grid launch masked by the device count

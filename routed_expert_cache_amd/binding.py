@@ -28,7 +28,7 @@ CNT_UNIQ, CNT_HIT, CNT_MISS, CNT_QSTAR, CNT_FILL, CNT_HOST, CNT_N = 0, 1, 2, 3, 
 
 EXPORTS = [
     "moe_last_error", "moe_route_topk", "moe_cache_workspace_bytes", "moe_cache_create",
-    "moe_cache_seed", "moe_cache_step", "moe_cache_fill", "moe_cache_read_state", "moe_cache_error",
+    "moe_cache_seed", "moe_cache_step", "moe_cache_route_step", "moe_cache_fill", "moe_cache_read_state", "moe_cache_error",
     "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_e4m3_to_bf16", "moe_pack_weights",
@@ -71,6 +71,7 @@ _sig = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_route_topk": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_cache_workspace_bytes": (_i32, [_P(CacheCfg), _P(_sz)]),
+    "moe_cache_route_step": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _u32, _P(StepOutC), _vp]),
     "moe_cache_create": (_i32, [_P(CacheCfg), _P(Slots), _P(HostPool), _vp, _sz, _vp, _P(_vp)]),
     "moe_cache_seed": (_i32, [_vp, _P(_i32), _i32, _u32, _vp]),
     "moe_cache_step": (_i32, [_vp, _i32, _vp, _i32, _u32, _P(StepOutC), _vp]),
@@ -219,6 +220,14 @@ class Cache:
         T = ids.shape[0]
         _check(_lib.moe_cache_step(self.h, layer, _ptr(ids), T, 0 if copy else STEP_NO_COPY,
                                    ctypes.byref(out.c), _stream(stream)), "moe_cache_step")
+
+    def route_step(self, layer, logits, ids, w, out: StepOut, copy=True, stream=None):
+        """Router + cache step in one launch; writes ids [T, k] and w [T, k]."""
+        T = logits.shape[0]
+        assert logits.is_cuda and logits.dtype == torch.float32 and logits.is_contiguous()
+        _check(_lib.moe_cache_route_step(self.h, layer, _ptr(logits), T, _ptr(ids), _ptr(w),
+                                         0 if copy else STEP_NO_COPY, ctypes.byref(out.c), _stream(stream)),
+               "moe_cache_route_step")
 
     def fill(self, out: StepOut, stream=None):
         _check(_lib.moe_cache_fill(self.h, ctypes.byref(out.c), _stream(stream)), "moe_cache_fill")

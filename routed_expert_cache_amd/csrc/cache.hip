@@ -56,6 +56,7 @@ moe_status check_slots(const moe_slots* s) {
 }
 
 constexpr int kDT = 256;              // decision kernel: one workgroup of 4 waves
+static_assert(kDT == 256, "the decision kernel's prefix sums read four wave counts as one int4");
 constexpr int kUMax = 1024;           // T_max * k <= 1024
 constexpr int kEMax = 4096;
 constexpr int kCMax = 16384;
@@ -78,7 +79,9 @@ struct CacheDev {
 };
 
 struct StepArgs {
-  const int32_t* ids;
+  const int32_t* ids;     // routed ids [T*k] (input, or written when routing in the kernel)
+  const float* logits;    // [T*E] when routing in the kernel
+  float* w;               // [T*k] gate weights when routing in the kernel
   int layer, T, k, U_max;
   moe_step_out out;
 };
@@ -89,38 +92,16 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
-// Ordered compaction over [0, N) by the 4 waves of the workgroup: each wave
-// walks a contiguous range in 64-element steps with ballots; pass 1 counts,
-// one barrier shares the wave totals, pass 2 emits (i, rank) in index order.
-// `pred` is evaluated twice and must be pure.  Ends with a barrier.
-template <class Pred, class Emit>
-__device__ int ordered_compact(int N, Pred pred, Emit emit, int* wtot) {
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
-  const int per = ((N + kDT - 1) / kDT) * 64;
-  const int beg = wv * per, end = min(N, beg + per);
-  int cnt = 0;
-  for (int i0 = beg; i0 < end; i0 += 64) {
-    const int i = i0 + lane;
-    cnt += __popcll(__ballot(i < end && pred(i)));
-  }
-  if (lane == 0) wtot[wv] = cnt;
-  __syncthreads();
-  int base = 0, total = 0;
-#pragma unroll
-  for (int w = 0; w < kDT / 64; ++w) {
-    const int t = wtot[w];
-    base += (w < wv) ? t : 0;
-    total += t;
-  }
-  for (int i0 = beg; i0 < end; i0 += 64) {
-    const int i = i0 + lane;
-    const bool f = i < end && pred(i);
-    const uint64_t b = __ballot(f);
-    if (f) emit(i, base + __popcll(b & lanemask_lt()));
-    base += __popcll(b);
-  }
-  __syncthreads();
-  return total;
+// Staging batch of the decision kernel: 8 words per thread.
+constexpr int kStageB = kDT * 8;
+__host__ __device__ constexpr int round_stage(int n) { return (n + kStageB - 1) / kStageB * kStageB; }
+
+// Dynamic LDS of the decision kernel (sizes rounded up to whole staging
+// batches, so the staging writes need no bounds test): slot_id [C] | LRU
+// order [C] as 16-bit slot numbers | id_slot row of the layer [E] | hit
+// bitmap [ceil(C/32)].
+__host__ __device__ inline int decide_lds_bytes(int C, int E) {
+  return 6 * round_stage(C) + 4 * round_stage(E) + 4 * ((C + 31) / 32);
 }
 
 // ---------------------------------------------------------------- decision kernel
@@ -129,63 +110,195 @@ __device__ int ordered_compact(int N, Pred pred, Emit emit, int* wtot) {
 // ordered scan; the new order is the other entries in place, then the hits
 // (rank order), then the filled victims: exactly the (stamp, slot) order after
 // the new stamps, since every new stamp exceeds all older ones.
+// Every table the decision reads (the order, slot_id, the layer's id_slot
+// row, the routed ids) is staged into LDS up front with all loads in flight
+// together; the rest of the kernel reads only LDS, so its barriers wait for
+// LDS traffic only and its global stores drain in the background.
+// VPL > 0: the kernel routes first (the router of route_topk_kernel, one
+// wave per token, VPL logits per lane) while the table loads are in flight,
+// and writes ids and gate weights as well.
+template <int VPL>
 __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs a) {
-  extern __shared__ int dyn[];                // ord [C] then hitbm [C/32]
+  extern __shared__ int dyn[];
   __shared__ uint32_t bm[kEMax / 32];         // routed experts of this layer
   __shared__ int uniq[kUMax];                 // local expert index, ascending
   __shared__ int uslot[kUMax];                // slot of uniq[i] after the step, -1 = host
   __shared__ int hit_list[kUMax];             // positions into uniq
   __shared__ int miss_list[kUMax];
   __shared__ int victims[kUMax];
-  __shared__ int wtot[kDT / 64];
-  __shared__ uint64_t s_tick;
-  __shared__ int s_nord;
+  __shared__ __align__(16) int s_cnt[kEMax / kDT][kDT / 64][2];   // per (row, wave): routed, hit
+  __shared__ __align__(16) int s_cc[2][kStageB / kDT][kDT / 64];   // per (row, wave): LRU candidates
 
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = cd.E, C = cd.C, layer = a.layer;
   const int P = a.T * a.k;
   const int lbase = layer * E;
-  int* ord = dyn;
-  uint32_t* hitbm = reinterpret_cast<uint32_t*>(dyn + C);
+  const int Cp = round_stage(C), Ep = round_stage(E);
+  int* sl = dyn;                                               // slot_id before the step
+  uint16_t* ord = reinterpret_cast<uint16_t*>(dyn + Cp);       // LRU order before the step
+  int* row = dyn + Cp + Cp / 2;                                // id_slot[lbase + e]
+  uint32_t* hitbm = reinterpret_cast<uint32_t*>(row + Ep);
 
+  // 0. stage: the loads of the first batch of every table are all issued
+  //    before the first is used (buffer loads past the end return 0, so no
+  //    branch separates them); entries of `order` past n_ord are not used.
+  const uint64_t tick = *cd.tick;      // uniform: scalar loads, consumed late
+  const int n_ord = *cd.n_ord;
+  uint64_t ctr[6];
+#pragma unroll
+  for (int i = 0; i < 6; ++i) ctr[i] = cd.counters[i];
+  const __amdgpu_buffer_rsrc_t r_ids = make_rsrc(a.ids, 4u * (uint32_t)P);
+  const __amdgpu_buffer_rsrc_t r_ord = make_rsrc(cd.order, 4u * (uint32_t)C);
+  const __amdgpu_buffer_rsrc_t r_sl = make_rsrc(cd.slot_id, 4u * (uint32_t)C);
+  const __amdgpu_buffer_rsrc_t r_row = make_rsrc(cd.id_slot + lbase, 4u * (uint32_t)E);
+  constexpr int V = kStageB / kDT, NP = kUMax / kDT;
+  int pid[NP];
+  int32_t vo[V], vs[V], vr[V];
+  if constexpr (VPL == 0) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) pid[j] = __builtin_amdgcn_raw_buffer_load_b32(r_ids, 4 * (j * kDT + tid), 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int o = 4 * (j * kDT + tid);
+    vo[j] = __builtin_amdgcn_raw_buffer_load_b32(r_ord, o, 0, 0);
+    vs[j] = __builtin_amdgcn_raw_buffer_load_b32(r_sl, o, 0, 0);
+    vr[j] = __builtin_amdgcn_raw_buffer_load_b32(r_row, o, 0, 0);
+  }
+  __shared__ int s_pid[VPL > 0 ? kUMax : 1];
+  if constexpr (VPL > 0) {
+    // wave wv routes tokens wv, wv+4, ...; the next token's logits load
+    // while this one is picked (a buffer of 0 bytes past the last token)
+    const int T = a.T, k = a.k;
+    auto row_of = [&](int t) {
+      return make_rsrc(a.logits + (size_t)(t < T ? t : 0) * E, t < T ? 4u * (uint32_t)E : 0u);
+    };
+    uint32_t kc[VPL], ac;
+    topk_keys<VPL>(row_of(wv), E, kc, ac);
+    for (int t = wv; t < T; t += kDT / 64) {
+      uint32_t kn[VPL], an;
+      topk_keys<VPL>(row_of(t + kDT / 64), E, kn, an);
+      int id;
+      float wt;
+      topk_pick<VPL>(kc, ac, k, id, wt);
+      if (lane < k) {
+        const_cast<int32_t*>(a.ids)[t * k + lane] = id;
+        a.w[t * k + lane] = wt;
+        s_pid[t * k + lane] = id;
+      }
+#pragma unroll
+      for (int v = 0; v < VPL; ++v) kc[v] = kn[v];
+      ac = an;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    const int i = j * kDT + tid;
+    ord[i] = (uint16_t)(i < n_ord ? vo[j] : 0);   // entries past n_ord read as slot 0
+    sl[i] = vs[j];
+    row[i] = vr[j];
+  }
+  for (int b0 = kStageB; b0 < Cp; b0 += kStageB) {   // pools of more than kStageB slots
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      const int o = 4 * (b0 + j * kDT + tid);
+      vo[j] = __builtin_amdgcn_raw_buffer_load_b32(r_ord, o, 0, 0);
+      vs[j] = __builtin_amdgcn_raw_buffer_load_b32(r_sl, o, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < V; ++j) {
+      ord[b0 + j * kDT + tid] = (uint16_t)(b0 + j * kDT + tid < n_ord ? vo[j] : 0);
+      sl[b0 + j * kDT + tid] = vs[j];
+    }
+  }
+  for (int b0 = kStageB; b0 < Ep; b0 += kStageB) {   // layers of more than kStageB experts
+#pragma unroll
+    for (int j = 0; j < V; ++j) vr[j] = __builtin_amdgcn_raw_buffer_load_b32(r_row, 4 * (b0 + j * kDT + tid), 0, 0);
+#pragma unroll
+    for (int j = 0; j < V; ++j) row[b0 + j * kDT + tid] = vr[j];
+  }
   for (int i = tid; i < (E + 31) / 32; i += kDT) bm[i] = 0;
   for (int i = tid; i < (C + 31) / 32; i += kDT) hitbm[i] = 0;
-  if (tid == 0) {
-    s_tick = *cd.tick;
-    s_nord = *cd.n_ord;
+  lds_barrier();
+  if constexpr (VPL > 0) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) pid[j] = j * kDT + tid < P ? s_pid[j * kDT + tid] : 0;
   }
-  __syncthreads();
-  const int n_ord = s_nord;
-  for (int i = tid; i < n_ord; i += kDT) ord[i] = cd.order[i];   // staged: the new order overwrites it
 
-  // 1. dedup: bitmap of the routed experts, compacted in ascending order
-  for (int p = tid; p < P; p += kDT) {
-    const int e = a.ids[p];
-    if (e < 0 || e >= E)
-      atomicOr(cd.error, 1 << ERR_BAD_ID);
-    else
-      atomicOr(&bm[e >> 5], 1u << (e & 31));
-  }
-  __syncthreads();
-  const int u = ordered_compact(
-      E, [&](int e) { return ((bm[e >> 5] >> (e & 31)) & 1u) != 0; }, [&](int e, int r) { uniq[r] = e; }, wtot);
-
-  // 2. classify against the residency table
-  for (int i = tid; i < u; i += kDT) {
-    int s = cd.id_slot[lbase + uniq[i]];
-    if (s >= C || (s >= 0 && cd.slot_id[s] != lbase + uniq[i])) {
-      atomicOr(cd.error, 1 << ERR_TABLE);
-      s = -1;
+  // 1. dedup: bitmap of the routed experts
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int p = j * kDT + tid;
+    const int e = pid[j];
+    if (p < P) {
+      if (e < 0 || e >= E)
+        atomicOr(cd.error, 1 << ERR_BAD_ID);
+      else
+        atomicOr(&bm[e >> 5], 1u << (e & 31));
     }
-    uslot[i] = s;
-    a.out.is_hit[i] = s >= 0 ? 1 : 0;
   }
+  lds_barrier();
+
+  // 2. one ordered pass over the layer's experts, e = j*kDT + tid: routed
+  //    (unique, ascending), and hit when the residency table holds it.  The
+  //    ranks among the unique, hit and missed experts come from ballots and
+  //    per-(row, wave) counts, with one barrier between counting and placing.
+  //    Every LDS read below is unconditional (indices clamped), so the
+  //    compiler keeps them in flight together instead of waiting per branch.
+  const int NE = (E + kDT - 1) / kDT;
+  const auto classify = [&](int e, bool& routed) {   // -> slot if hit, else -1
+    const int ee = e < E ? e : 0;
+    const uint32_t word = bm[ee >> 5];
+    const int s = row[ee];                             // row is padded: ee is in range
+    const int sc = (s >= 0 && s < C) ? s : 0;
+    const int owner = sl[sc];
+    routed = e < E && ((word >> (ee & 31)) & 1u) != 0;
+    const bool valid = s >= 0 && s < C && owner == lbase + e;
+    if (routed && s >= 0 && !valid) atomicOr(cd.error, 1 << ERR_TABLE);   // a broken entry counts as a miss
+    return routed && valid ? s : -1;
+  };
+  for (int j = 0; j < NE; ++j) {
+    bool rt;
+    const int s = classify(j * kDT + tid, rt);
+    const uint64_t bR = __ballot(rt), bH = __ballot(s >= 0);
+    s_cnt[j][wv][0] = __popcll(bR);   // every lane writes the same value: no branch
+    s_cnt[j][wv][1] = __popcll(bH);
+  }
+  lds_barrier();
+  int u = 0, h = 0;
+  {
+    int bu = 0, bh = 0;   // routed and hit experts before this thread's row and wave
+    for (int j = 0; j < NE; ++j) {
+      const int4 c01 = *reinterpret_cast<const int4*>(&s_cnt[j][0][0]);   // waves 0, 1
+      const int4 c23 = *reinterpret_cast<const int4*>(&s_cnt[j][2][0]);   // waves 2, 3
+      bool rt;
+      const int e = j * kDT + tid;
+      const int s = classify(e, rt);
+      const uint64_t bR = __ballot(rt), bH = __ballot(s >= 0);
+      const int pu = bu + (wv > 0 ? c01.x : 0) + (wv > 1 ? c01.z : 0) + (wv > 2 ? c23.x : 0);
+      const int ph = bh + (wv > 0 ? c01.y : 0) + (wv > 1 ? c01.w : 0) + (wv > 2 ? c23.y : 0);
+      if (rt) {
+        const int r = pu + __popcll(bR & lanemask_lt());
+        const int rh = ph + __popcll(bH & lanemask_lt());
+        uniq[r] = e;
+        uslot[r] = s;
+        a.out.is_hit[r] = s >= 0 ? 1 : 0;
+        if (s >= 0) {
+          hit_list[rh] = r;
+          atomicOr(&hitbm[s >> 5], 1u << (s & 31));
+        } else {
+          miss_list[r - rh] = r;
+        }
+      }
+      bu += c01.x + c01.z + c23.x + c23.z;
+      bh += c01.y + c01.w + c23.y + c23.w;
+    }
+    u = bu;
+    h = bh;
+  }
+  const int m = u - h;
   for (int i = u + tid; i < a.U_max; i += kDT) a.out.is_hit[i] = -1;
-  __syncthreads();
-  const int h = ordered_compact(
-      u, [&](int i) { return uslot[i] >= 0; }, [&](int i, int r) { hit_list[r] = i; }, wtot);
-  const int m = ordered_compact(
-      u, [&](int i) { return uslot[i] < 0; }, [&](int i, int r) { miss_list[r] = i; }, wtot);
 
   // 3. q* = clamp(round(m bp / bh), 1, m)
   int qs = 0;
@@ -193,63 +306,58 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
     const uint64_t q0 = (2ull * (uint64_t)m * cd.bp + cd.bh) / (2ull * cd.bh);
     qs = (int)(q0 < 1 ? 1 : (q0 > (uint64_t)m ? (uint64_t)m : q0));
   }
+  // every hit slot is in the order (it is occupied, so not reserved):
+  // the candidates are the other n_ord - h entries
+  const int n_cand = n_ord - h;
+  const int q = qs < n_cand ? qs : n_cand;
+  lds_barrier();   // hit bitmap and lists complete
 
   // 4. one ordered scan of the LRU order: the first q non-hit entries are the
   //    victims; the others keep their relative order in the new order.
-  for (int r = tid; r < h; r += kDT) {
-    const int s = uslot[hit_list[r]];
-    atomicOr(&hitbm[s >> 5], 1u << (s & 31));
-  }
-  __syncthreads();
-  const auto is_cand = [&](int i) {
-    const int s = ord[i];
-    return ((hitbm[s >> 5] >> (s & 31)) & 1u) == 0;
-  };
-  // pass 1 of the compaction is also the candidate count, needed for q
-  int n_cand;
+  //    Chunks of kStageB entries, i = b0 + j*kDT + tid, one barrier each.
   {
-    const int lane = tid & 63, wv = tid >> 6;
-    const int per = ((n_ord + kDT - 1) / kDT) * 64;
-    const int beg = wv * per, end = min(n_ord, beg + per);
-    int cnt = 0;
-    for (int i0 = beg; i0 < end; i0 += 64) {
-      const int i = i0 + lane;
-      cnt += __popcll(__ballot(i < end && is_cand(i)));
-    }
-    if (lane == 0) wtot[wv] = cnt;
-    __syncthreads();
-    int base = 0;
-    n_cand = 0;
+    constexpr int V = kStageB / kDT;
+    int before = 0;   // candidates before the current row
+    for (int b0 = 0; b0 < n_ord; b0 += kStageB) {
+      const int cb = (b0 / kStageB) & 1;   // count buffers alternate between chunks
+      int sv[V];
+      uint32_t hw[V];
+      uint64_t bc[V];
 #pragma unroll
-    for (int w = 0; w < kDT / 64; ++w) {
-      const int t = wtot[w];
-      base += (w < wv) ? t : 0;
-      n_cand += t;
-    }
-    const int q_ = qs < n_cand ? qs : n_cand;
-    for (int i0 = beg; i0 < end; i0 += 64) {
-      const int i = i0 + lane;
-      const bool f = i < end && is_cand(i);
-      const uint64_t b = __ballot(f);
-      if (f) {
-        const int r = base + __popcll(b & lanemask_lt());
-        if (r < q_)
-          victims[r] = ord[i];
-        else
-          cd.order[r - q_] = ord[i];
+      for (int j = 0; j < V; ++j) sv[j] = ord[b0 + j * kDT + tid];   // padded, 0 past n_ord
+#pragma unroll
+      for (int j = 0; j < V; ++j) hw[j] = hitbm[sv[j] >> 5];
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const bool cand = (b0 + j * kDT + tid < n_ord) & (((hw[j] >> (sv[j] & 31)) & 1u) == 0);
+        bc[j] = __ballot(cand);
+        s_cc[cb][j][wv] = __popcll(bc[j]);   // every lane writes the same value: no branch
       }
-      base += __popcll(b);
+      lds_barrier();
+      int4 cc[V];
+#pragma unroll
+      for (int j = 0; j < V; ++j) cc[j] = *reinterpret_cast<const int4*>(&s_cc[cb][j][0]);
+#pragma unroll
+      for (int j = 0; j < V; ++j) {
+        const int pre = before + (wv > 0 ? cc[j].x : 0) + (wv > 1 ? cc[j].y : 0) + (wv > 2 ? cc[j].z : 0);
+        if ((bc[j] >> lane) & 1ull) {
+          const int r = pre + __popcll(bc[j] & lanemask_lt());
+          if (r < q)
+            victims[r] = sv[j];
+          else
+            cd.order[r - q] = sv[j];
+        }
+        before += cc[j].x + cc[j].y + cc[j].z + cc[j].w;
+      }
     }
-    __syncthreads();
   }
-  const int q = qs < n_cand ? qs : n_cand;
+  lds_barrier();   // victims complete
 
   // 5. table update: fill i -> victim i; stamps; tail of the new order
-  const uint64_t tick = s_tick;
   for (int i = tid; i < q; i += kDT) {
     const int v = victims[i];
     const int f = lbase + uniq[miss_list[i]];
-    const int old = cd.slot_id[v];
+    const int old = sl[v];
     if (old >= 0) cd.id_slot[old] = -1;
     cd.slot_id[v] = f;
     cd.id_slot[f] = v;
@@ -265,21 +373,25 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
     cd.stamp[s] = (tick << 16) | (uint64_t)(1 + r);
     cd.order[n_cand - q + r] = s;
   }
-  __syncthreads();
+  lds_barrier();
 
   // 6. outputs: rewrite picks, lists, counts
-  for (int p = tid; p < P; p += kDT) {
-    const int e = a.ids[p];
-    int slot = -1;
-    if (e >= 0 && e < E) {
-      int lo = 0, hi = u - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (uniq[mid] < e) lo = mid + 1; else hi = mid;
+#pragma unroll
+  for (int j = 0; j < NP; ++j) {
+    const int p = j * kDT + tid;
+    if (p < P) {
+      const int e = pid[j];
+      int slot = -1;
+      if (e >= 0 && e < E) {
+        int lo = 0, hi = u - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (uniq[mid] < e) lo = mid + 1; else hi = mid;
+        }
+        slot = uslot[lo];
       }
-      slot = uslot[lo];
+      a.out.pick_slot[p] = slot;
     }
-    a.out.pick_slot[p] = slot;
   }
   for (int i = tid; i < a.U_max; i += kDT) {
     a.out.uniq[i] = i < u ? lbase + uniq[i] : -1;
@@ -303,12 +415,9 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
     cnt[7] = 0;
     *cd.tick = tick + 1;
     if (tick + 1 >= (1ull << 28)) atomicOr(cd.error, 1 << ERR_TICK);
-    cd.counters[0] += 1;
-    cd.counters[1] += (uint64_t)u;
-    cd.counters[2] += (uint64_t)h;
-    cd.counters[3] += (uint64_t)m;
-    cd.counters[4] += (uint64_t)q;
-    cd.counters[5] += (uint64_t)(m - q);
+    const uint64_t add[6] = {1, (uint64_t)u, (uint64_t)h, (uint64_t)m, (uint64_t)q, (uint64_t)(m - q)};
+#pragma unroll
+    for (int i = 0; i < 6; ++i) cd.counters[i] = ctr[i] + add[i];
   }
 }
 
@@ -510,7 +619,7 @@ extern "C" moe_status moe_cache_create(const moe_cache_cfg* cfg, const moe_slots
   int lds_max = 0;
   MOE_HIP(hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
   const int lds_static = 32 * 1024;   // bound on the kernel's static LDS (about 21 KB)
-  const int lds_dyn = 4 * cfg->C + 4 * ((cfg->C + 31) / 32);
+  const int lds_dyn = decide_lds_bytes(cfg->C, cfg->E);
   if (lds_dyn + lds_static > lds_max)
     MOE_FAIL(MOE_ERR_SHAPE, "C=%d needs %d B of LDS; device allows %d", cfg->C, lds_dyn + lds_static, lds_max);
 
@@ -588,8 +697,12 @@ extern "C" moe_status moe_cache_create(const moe_cache_cfg* cfg, const moe_slots
   d.bp = cfg->bp;
   d.bh = cfg->bh;
 
-  hipError_t e = hipFuncSetAttribute((const void*)cache_decide_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, lds_dyn);
+  const void* decide_fns[] = {(const void*)cache_decide_kernel<0>, (const void*)cache_decide_kernel<1>,
+                              (const void*)cache_decide_kernel<2>, (const void*)cache_decide_kernel<4>,
+                              (const void*)cache_decide_kernel<8>, (const void*)cache_decide_kernel<16>};
+  hipError_t e = hipSuccess;
+  for (const void* fn : decide_fns)
+    if (e == hipSuccess) e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_dyn);
   if (e != hipSuccess) {
     delete c;
     MOE_FAIL(MOE_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
@@ -660,23 +773,64 @@ extern "C" moe_status moe_cache_seed(moe_cache_t c, const int32_t* host_ids, int
   return MOE_OK;
 }
 
-extern "C" moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t* ids, int32_t T, uint32_t flags,
-                                     const moe_step_out* out, hipStream_t stream) {
-  clear_error();
-  if (!c || !ids || !out) MOE_FAIL(MOE_ERR_ARG, "null argument");
+static moe_status check_step(moe_cache_t c, int32_t layer, int32_t T, const moe_step_out* out) {
+  if (!c || !out) MOE_FAIL(MOE_ERR_ARG, "null argument");
   if (layer < 0 || layer >= c->cfg.L) MOE_FAIL(MOE_ERR_SHAPE, "layer %d outside [0, %d)", layer, c->cfg.L);
   if (T < 1 || T > c->cfg.T_max) MOE_FAIL(MOE_ERR_SHAPE, "T=%d outside [1, T_max=%d]", T, c->cfg.T_max);
   if (!out->pick_slot || !out->uniq || !out->is_hit || !out->fill_id || !out->fill_slot || !out->fill_evicted ||
       !out->host_id || !out->counts)
     MOE_FAIL(MOE_ERR_ARG, "a moe_step_out buffer is NULL");
-  StepArgs a;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t* ids, int32_t T, uint32_t flags,
+                                     const moe_step_out* out, hipStream_t stream) {
+  clear_error();
+  moe_status st = check_step(c, layer, T, out);
+  if (st) return st;
+  if (!ids) MOE_FAIL(MOE_ERR_ARG, "ids is NULL");
+  StepArgs a{};
   a.ids = ids;
   a.layer = layer;
   a.T = T;
   a.k = c->cfg.k;
   a.U_max = c->U_max;
   a.out = *out;
-  cache_decide_kernel<<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
+  cache_decide_kernel<0><<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
+  MOE_LAUNCHED();
+  if (!(flags & MOE_STEP_NO_COPY))
+    return launch_fill(c, out->fill_id, out->fill_slot, out->counts + MOE_CNT_FILL, stream);
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_route_step(moe_cache_t c, int32_t layer, const float* logits, int32_t T,
+                                           int32_t* ids, float* w, uint32_t flags, const moe_step_out* out,
+                                           hipStream_t stream) {
+  clear_error();
+  moe_status st = check_step(c, layer, T, out);
+  if (st) return st;
+  if (!logits || !ids || !w) MOE_FAIL(MOE_ERR_ARG, "null argument");
+  const int E = c->cfg.E, k = c->cfg.k;
+  if (E > 1024 || k > 32) MOE_FAIL(MOE_ERR_SHAPE, "routing in the step needs E <= 1024 and k <= 32 (E=%d k=%d)", E, k);
+  StepArgs a{};
+  a.ids = ids;
+  a.logits = logits;
+  a.w = w;
+  a.layer = layer;
+  a.T = T;
+  a.k = k;
+  a.U_max = c->U_max;
+  a.out = *out;
+  if (E <= 64)
+    cache_decide_kernel<1><<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
+  else if (E <= 128)
+    cache_decide_kernel<2><<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
+  else if (E <= 256)
+    cache_decide_kernel<4><<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
+  else if (E <= 512)
+    cache_decide_kernel<8><<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
+  else
+    cache_decide_kernel<16><<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
   MOE_LAUNCHED();
   if (!(flags & MOE_STEP_NO_COPY))
     return launch_fill(c, out->fill_id, out->fill_slot, out->counts + MOE_CNT_FILL, stream);

@@ -72,6 +72,22 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u & 0x7fffffffu) > 0x7f800000u ? nan : r);
 }
 
+// Workgroup barrier for LDS traffic only: each wave waits for its own LDS
+// operations, not for its global stores (which __syncthreads would also
+// wait for, a full memory round trip).  For code whose waves exchange data
+// through LDS only.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Raw buffer resource over [base, base + bytes): a load past the end returns
+// zero without a memory access, so masked loads need no branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
 
 __device__ __forceinline__ f32x4 mfma16x16x32(const u32x4& a, const u32x4& b, const f32x4& c) {
@@ -94,6 +110,92 @@ __device__ __forceinline__ void e4m3x16_to_bf16_nat(const u32x4& q, u32x4& lo, u
              e4m3x2_to_bf16x2<true>(q[1])};
   hi = u32x4{e4m3x2_to_bf16x2<false>(q[2]), e4m3x2_to_bf16x2<true>(q[2]), e4m3x2_to_bf16x2<false>(q[3]),
              e4m3x2_to_bf16x2<true>(q[3])};
+}
+
+// ---------------------------------------------------------------- wave top-k
+// Router selection for one token per wavefront ([FTK] routing and GPU-router
+// paragraphs: top-k of the logits, gate weights = softmax over the kept k).
+// Lane l holds the logits of experts l, l+64, ... as 32-bit keys whose
+// unsigned order is the float order (sign-magnitude folded, -0 ranks as +0).
+// Each of the k rounds takes the wave-wide maximum key (DPP exchanges inside
+// each row of 16 lanes, then the four row results through scalar registers),
+// finds the lowest expert index holding it with one ballot per key column
+// (ties go to the lower index), and retires that key.  Lane j < k ends with
+// pick j (rank order) and its weight.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <- 7-i within each 8
+constexpr int kDppMirror = 0x140;     // lane i <- 15-i within each 16
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppXor1>(v));
+  v = max(v, dpp_u32<kDppXor2>(v));
+  v = max(v, dpp_u32<kDppHalfMirror>(v));
+  v = max(v, dpp_u32<kDppMirror>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+__device__ __forceinline__ float wave_sum_f32(float v) {
+  v += __uint_as_float(dpp_u32<kDppXor1>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppXor2>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppHalfMirror>(__float_as_uint(v)));
+  v += __uint_as_float(dpp_u32<kDppMirror>(__float_as_uint(v)));
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+// Load one token's logits (row: buffer over its E floats) as ordered keys;
+// bit v of `alive` marks key[v] as a real expert (v*64 + lane < E).
+template <int VPL>
+__device__ __forceinline__ void topk_keys(__amdgpu_buffer_rsrc_t row, int E, uint32_t (&key)[VPL], uint32_t& alive) {
+  const int lane = threadIdx.x & 63;
+  alive = 0;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    const int e = v * 64 + lane;
+    uint32_t u = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(row, 4 * e, 0, 0);   // 0 past E
+    if ((u & 0x7fffffffu) == 0) u = 0;                                                 // -0 ranks as +0
+    key[v] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    alive |= (e < E ? 1u : 0u) << v;
+  }
+}
+
+template <int VPL>
+__device__ __forceinline__ void topk_pick(uint32_t (&key)[VPL], uint32_t alive, int k, int& my_id, float& my_w) {
+  const int lane = threadIdx.x & 63;
+  my_id = -1;
+  float my_z = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int v = 0; v < VPL; ++v) m = ((alive >> v) & 1u) ? max(m, key[v]) : m;
+    const uint32_t best = wave_max_u32(m);
+    int e = -1;
+#pragma unroll
+    for (int v = VPL - 1; v >= 0; --v) {   // the lowest column holding `best` wins
+      const uint64_t b = __ballot(((alive >> v) & 1u) && key[v] == best);
+      if (b) e = v * 64 + (int)__builtin_ctzll(b);
+    }
+    if ((e & 63) == lane) alive &= ~(1u << (e >> 6));
+    const uint32_t u = (best & 0x80000000u) ? (best & 0x7fffffffu) : ~best;
+    if (lane == j) {
+      my_id = e;
+      my_z = __uint_as_float(u);
+    }
+  }
+  // softmax over the k kept logits; pick 0 holds the maximum
+  const float zmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_z), 0));
+  const float ex = (lane < k) ? expf(my_z - zmax) : 0.f;
+  my_w = ex / wave_sum_f32(ex);
 }
 
 // a * sigmoid(a); the reciprocal is the hardware one (about 1 ulp), far

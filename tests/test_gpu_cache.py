@@ -91,6 +91,20 @@ class Harness:
         self.compare(r, T)
         return r
 
+    def route_step(self, layer, logits):
+        """Router + step in one launch; checks ids and weights against the
+        oracle router, then the step against the oracle cache."""
+        T = logits.shape[0]
+        ids = torch.empty((T, self.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((T, self.k), dtype=torch.float32, device="cuda")
+        self.cache.route_step(layer, dev(logits), ids, w, self.out, copy=self.copy)
+        rid, rw = route.topk_softmax(logits, self.k)
+        assert np.array_equal(ids.cpu().numpy(), rid)
+        assert np.abs(w.cpu().numpy() - rw).max() <= W_ABS
+        r = self.orc.step(layer, rid)
+        self.compare(r, T)
+        return ids, w
+
     def compare(self, r, T):
         b = self.b
         o = self.out
@@ -165,6 +179,8 @@ STRESS = [
     (2, 256, 300, 16, 8, 900, 475, 40),     # all misses filled: q up to 128 (radix select)
     (3, 64, 70, 16, 8, 900, 475, 40),       # q clamped by free victims
     (40, 128, 1894, 1, 8, 527, 773, 100),   # decode BF16 shape
+    (3, 64, 2500, 4, 8, 118, 475, 60),      # pool over two staging batches of the decision kernel
+    (2, 3000, 4100, 16, 8, 900, 475, 30),   # layer row over two batches, pool over three
 ]
 
 
@@ -193,6 +209,47 @@ def test_sticky_decode_trace_short():
             hz.step(l, ids)
             if s >= 10:
                 hz.compare_tables()
+    hz.compare_tables()
+
+
+ROUTE_STEP = [
+    # L, E, C, T, k, bp, bh, steps
+    (4, 8, 5, 3, 2, 118, 475, 60),
+    (40, 128, 1894, 1, 8, 527, 773, 80),    # decode BF16 shape
+    (3, 256, 200, 16, 8, 118, 475, 40),     # decode FP8 layer width, 4 tokens per wave
+    (2, 1000, 300, 5, 32, 900, 475, 20),    # 16 logits per lane
+    (2, 60, 2500, 9, 4, 118, 475, 30),      # pool over two staging batches
+]
+
+
+@pytest.mark.parametrize("case", ROUTE_STEP)
+def test_route_step_fused(case):
+    """moe_cache_route_step = moe_route_topk + moe_cache_step, bit for bit."""
+    L, E, C, T, k, bp, bh, steps = case
+    rng = np.random.default_rng(sum(case) + 5)
+    hz = Harness(L, E, C, T, k, bp, bh, copy=False)
+    b = hz.b
+    for s in range(steps):
+        layer = int(rng.integers(0, L))
+        Ts = int(rng.integers(1, T + 1))
+        lg = rng.standard_normal((Ts, E)).astype(np.float32)
+        if s % 3 == 0:
+            lg[:, ::5] = np.float32(0.25)          # ties across experts
+        ids, w = hz.route_step(layer, lg)
+        # the separate router gives the same bits
+        ids2, w2 = b.route_topk(dev(lg), k)
+        assert torch.equal(ids, ids2) and torch.equal(w, w2)
+    hz.compare_tables()
+
+
+def test_route_step_sticky_decode_trace():
+    """The decode BF16 workload's logits through the fused router + step."""
+    c = CONFIGS["decode_bf16"]
+    picks, logits = gen.decode_trace(c.cfg_id, c.L, 12, c.E, c.k, c.p_keep)
+    hz = Harness(c.L, c.E, c.C, 1, c.k, c.bp, c.bh, copy=False)
+    for s in range(12):
+        for l in range(c.L):
+            hz.route_step(l, logits[s, l])
     hz.compare_tables()
 
 
