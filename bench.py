@@ -214,7 +214,6 @@ def run_decode(b, K, W):
     w = torch.empty((1, k), dtype=torch.float32, device="cuda")
     out = b.StepOut(1, k, E)
     ws = b.forward_workspace(1, k, H, I, C, b.FWD_DECODE)
-    yg = torch.empty((1, H), dtype=torch.float32, device="cuda")
     y = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
     pick = out.pick_slot.view(1, k)
 
@@ -225,10 +224,9 @@ def run_decode(b, K, W):
         cache.fill(out)
         if ev:
             ev.record(3 * i + 1)
-        b.expert_forward(pool.c, x[s, l], pick, w, b.FWD_DECODE, ws, y=yg)
+        b.expert_forward_merge(pool.c, x[s, l], pick, w, b.FWD_DECODE, ws, yh[l], y_out=y[l])   # + merge
         if ev:
             ev.record(3 * i + 2)
-        b.merge_partial(yg, yh[l], y_out=y[l])
 
     def run_trace(ev):
         """Cold cache, W warm-up steps, then K timed steps; returns (wall s, counter deltas)."""
@@ -270,7 +268,7 @@ def run_decode(b, K, W):
     res = dict(
         value=gpu_bytes / hbm_s / 1e9,
         ms_per_step=hbm_s / K * 1e3,
-        roofline=dict(kernel="moe_expert_forward decode (grouped GEMV: gate/up + down launches)",
+        roofline=dict(kernel="moe_expert_forward_merge decode (one kernel: gate/up, down, merge)",
                       bound="hbm", achieved=gpu_bytes / fwd_s / 1e9, peak=PEAK_HBM_GBPS, unit="GB/s",
                       bytes_per_launch=gpu_bytes / (K * L), launches=K * L,
                       avg_launch_us=fwd_s / (K * L) * 1e6, traffic=None),
@@ -392,7 +390,6 @@ def run_decode_fp8(b, K, W, Ts=(1, 4, 16)):
         ids = torch.empty((T, k), dtype=torch.int32, device="cuda")
         w = torch.empty((T, k), dtype=torch.float32, device="cuda")
         ws = b.forward_workspace(T, k, H, I, C, b.FWD_DECODE)
-        yg = torch.empty((T, H), dtype=torch.float32, device="cuda")
         yh = torch.zeros((T, H), dtype=torch.float32, device="cuda")
         y = torch.empty((T, H), dtype=torch.float32, device="cuda")
         pick = out.pick_slot.view(T, k)
@@ -409,10 +406,9 @@ def run_decode_fp8(b, K, W, Ts=(1, 4, 16)):
                     cache.fill(out)
                     if i is not None:
                         ev.record(3 * i + 1)
-                    b.expert_forward(pool.c, x[s], pick, w, b.FWD_DECODE, ws, y=yg)
+                    b.expert_forward_merge(pool.c, x[s], pick, w, b.FWD_DECODE, ws, yh, y_out=y)
                     if i is not None:
                         ev.record(3 * i + 2)
-                    b.merge_partial(yg, yh, y_out=y)
                     if i is not None:
                         cnt = out.counts                                # read after the run
                         fwd_counts_dev.append(cnt.clone())

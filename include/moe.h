@@ -288,6 +288,21 @@ moe_status moe_expert_forward(const moe_slots* slots, const uint16_t* x, const i
                               void* ws, size_t ws_bytes, uint32_t mode, hipStream_t stream);
 
 /*
+ * moe_expert_forward followed by moe_merge_partial in one call, with the
+ * same bits: y_out = y_gpu + y_host and, if y_out_bf16 != NULL, its BF16
+ * ([FT] section "q* 策略": the GPU and host partial sums are added).  The
+ * sum is formed where the GPU partial sum leaves the expert kernels, so the
+ * merge needs no launch of its own.  y_gpu: device float32 [T, H], written
+ * if not NULL; y_host: device or pinned host float32 [T, H]; y_out: device
+ * float32 [T, H] (may not alias y_host).  Same modes, sizes and workspace as
+ * moe_expert_forward.  Capturable.
+ */
+moe_status moe_expert_forward_merge(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,
+                                    const float* w, int32_t T, int32_t k, float* y_gpu, const float* y_host,
+                                    float* y_out, uint16_t* y_out_bf16, void* ws, size_t ws_bytes, uint32_t mode,
+                                    hipStream_t stream);
+
+/*
  * Merge of the GPU and host partial sums ([FT] section "q* 策略": the two
  * partial sums are combined exactly; [FT] "Graph 内的 CPU 执行分支").
  * y_out[i] = y_gpu[i] + y_host[i] over T*H floats; if y_out_bf16 != NULL it

@@ -29,7 +29,8 @@ CNT_UNIQ, CNT_HIT, CNT_MISS, CNT_QSTAR, CNT_FILL, CNT_HOST, CNT_N = 0, 1, 2, 3, 
 EXPORTS = [
     "moe_last_error", "moe_route_topk", "moe_cache_workspace_bytes", "moe_cache_create",
     "moe_cache_seed", "moe_cache_step", "moe_cache_route_step", "moe_cache_fill", "moe_cache_read_state", "moe_cache_error",
-    "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_merge_partial",
+    "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_expert_forward_merge",
+    "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_e4m3_to_bf16", "moe_pack_weights",
 ]
@@ -81,6 +82,8 @@ _sig = {
     "moe_cache_destroy": (_i32, [_vp]),
     "moe_forward_workspace_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, _u32, _P(_sz)]),
     "moe_expert_forward": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _u32, _vp]),
+    "moe_expert_forward_merge": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
+                                        _u32, _vp]),
     "moe_merge_partial": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "moe_prefill_create": (_i32, [_vp, _P(_vp)]),
     "moe_prefill_prefetch": (_i32, [_vp, _i32, _vp]),
@@ -272,6 +275,19 @@ def expert_forward(slots_c, x, pick_slot, w, mode, ws, y=None, stream=None):
     _check(_lib.moe_expert_forward(ctypes.byref(slots_c), _ptr(x), _ptr(pick_slot), _ptr(w), T, k, _ptr(y),
                                    _ptr(ws), ws.numel(), mode, _stream(stream)), "moe_expert_forward")
     return y
+
+
+def expert_forward_merge(slots_c, x, pick_slot, w, mode, ws, y_host, y_out=None, y_gpu=None, y_out_bf16=None,
+                         stream=None):
+    """expert_forward then merge_partial in one call: y_out = y_gpu + y_host
+    (y_gpu, the GPU partial sum, is written only when given)."""
+    T, k = pick_slot.shape
+    if y_out is None:
+        y_out = torch.empty((T, slots_c.H), dtype=torch.float32, device=x.device)
+    _check(_lib.moe_expert_forward_merge(ctypes.byref(slots_c), _ptr(x), _ptr(pick_slot), _ptr(w), T, k,
+                                         _ptr(y_gpu), _ptr(y_host), _ptr(y_out), _ptr(y_out_bf16),
+                                         _ptr(ws), ws.numel(), mode, _stream(stream)), "moe_expert_forward_merge")
+    return y_out
 
 
 def merge_partial(y_gpu, y_host, y_out=None, y_out_bf16=None, stream=None):

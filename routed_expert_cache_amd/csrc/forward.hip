@@ -107,7 +107,10 @@ struct DecArgs {
   const uint16_t* x;         // [T][H]
   const int32_t* pick_slot;  // [T*k]
   const float* w;            // [T*k]
-  float* y;                  // [T][H]
+  float* y;                  // [T][H] GPU partial sum, or NULL
+  const float* y_host;       // [T][H] host partial sum (merge), or NULL
+  float* y_out;              // [T][H] y + y_host (merge), or NULL
+  uint16_t* y_bf16;          // [T][H] BF16 of y_out (merge), or NULL
   uint16_t* h;               // workspace [G_max][16][I] BF16
   int G_max;
 };
@@ -203,9 +206,14 @@ __device__ void wave_plan(const int32_t* __restrict__ pick_slot, const float* __
 // ---------------------------------------------------------------- fused decode
 // One launch evaluates both projections: a grid of resident workgroups walks
 // one task list round-robin, first the gate/up tasks (group g, brick row t),
-// then the down tasks (16 output rows, half of the (group, K) steps).  A
-// workgroup takes its tasks in list order, so every gate/up task is finished
-// or in progress before any workgroup waits for one.
+// then the down tasks (one 16-row block of y each, over every (group, K)
+// step).  A workgroup takes its tasks in list order, so every gate/up task is
+// finished or in progress before any workgroup waits for one.  The waves of a
+// workgroup split a task's K steps and meet in LDS at its end, so every
+// output element is summed by one workgroup in a fixed order: y is written
+// with plain stores and has the same bits on every run; the merge with the
+// host partial sum happens in the same place ([FT] section "q* 策略": the two
+// partial sums are added).
 //
 // Hand-over without a reset launch.  A gate/up task writes its h values with
 // device-coherent (write-through) stores, waits for them, and counts itself
@@ -217,11 +225,7 @@ __device__ void wave_plan(const int32_t* __restrict__ pick_slot, const float* __
 // the streams' memory channels), clears it, and only then loads h.  Every
 // control word is back at 0 when the launch ends, so a workspace that starts
 // zero-filled stays valid.  A poll is bounded: on time-out the workgroup
-// flags the workspace error word and goes on.  The gate/up tasks of group 0
-// zero y before they count themselves (workgroup 0 does it when no pick is
-// on the GPU); down sums are added into y with two float atomics per
-// element (one per half), which commute exactly: y has the same bits on
-// every run.
+// flags the workspace error word and goes on.
 constexpr int kCtrlStride = 16;                     // one control word per 64 bytes
 constexpr int kDecGridMax = 4096;                   // go flags
 constexpr uint32_t kPollLimit = 1u << 22;
@@ -246,12 +250,10 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   if (wv == 0) wave_plan(a.pick_slot, a.w, T * a.k, a.k, a.n_slots, a.G_max, s_gslot, s_gw, &s_G, s_tab);
   __syncthreads();
   const int G = s_G;
-  if (G == 0 && blockIdx.x == 0)
-    for (int i = tid; i < T * H; i += NW * 64) a.y[i] = 0.f;
   const bool tok = r < T;
   constexpr int XN = FP8 ? 4 : 2;
   const int RA = I / 8;
-  const int nA = G * RA, nB = 2 * (H / 16);
+  const int nA = G * RA, nB = H / 16;
   const int b0 = (int)blockIdx.x, gs = (int)gridDim.x;
   const int myA = nA > b0 ? (nA - b0 + gs - 1) / gs : 0;                  // my tasks below nA
   const int myAll = nA + nB > b0 ? (nA + nB - b0 + gs - 1) / gs : 0;
@@ -268,7 +270,6 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
     const int nsteps = myA * SW;
     const __amdgpu_buffer_rsrc_t xr = make_rsrc(a.x, (uint32_t)(T * H * 2));
     const __amdgpu_buffer_rsrc_t hw = make_rsrc(a.h, (uint32_t)(2u * a.G_max * kDecTok * I));
-    const __amdgpu_buffer_rsrc_t yw = make_rsrc(a.y, (uint32_t)(4u * T * H));
     const __amdgpu_buffer_rsrc_t gow = make_rsrc(c.go, (uint32_t)(4u * kDecGridMax * kCtrlStride));
     float sb[D][2];
     int i_tk = 0, i_l = 0;
@@ -352,11 +353,6 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
                 __builtin_amdgcn_raw_buffer_store_b64(u32x2{h01, h23}, hw,
                                                       (uint32_t)((((size_t)g * kDecTok + r) * I + 8 * t + 4 * j) * 2), 0, 16);
               }
-              if (g == 0) {   // group 0's tasks zero y (device-coherent stores) before they count themselves
-                const int n = T * H, z = (n + RA - 1) / RA;
-                for (int i = t * z + lane; i < min(n, (t + 1) * z); i += 64)
-                  __builtin_amdgcn_raw_buffer_store_b32(0u, yw, (uint32_t)i * 4u, 0, 16);
-              }
               __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores above have completed
               __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // and stay before the count
               bool last = false;
@@ -383,12 +379,12 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
     }
   }
 
-  // ================= phase B: down projection + gate weights
+  // ================= phase B: down projection + gate weights (+ merge)
   if (myB > 0) {
     const int nkt = FP8 ? I / 64 : I / 32;
     const int SB = (nkt + 1) >> 1;
-    const int n = G * SB;
-    const int SWB = ((n + 1) / 2 + NW - 1) / NW;
+    const int n = G * SB;                       // (group, K step) pairs of every task
+    const int SWB = (n + NW - 1) / NW;          // of one wave
     const size_t dn_bytes = (size_t)H * I * (FP8 ? 1 : 2);
     const int nsteps = myB * SWB;
     const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.h, (uint32_t)(2u * a.G_max * kDecTok * I));
@@ -397,11 +393,9 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
     bool qok[D];
     int i_tk = 0, i_l = 0;
     auto issue_w = [&](int d) {   // weights of the next step; remembers its (group, step)
-      const int task = b0 + (myA + i_tk) * gs - nA;
-      const int t = task >> 1, half = task & 1;
-      const int lo = half ? n / 2 : 0, hi = half ? n : n / 2;
-      const int q = lo + wv * SWB + i_l;
-      const bool ok = i_tk < myB && wv * SWB + i_l < hi - lo;
+      const int t = b0 + (myA + i_tk) * gs - nA;   // 16-row block of y
+      const int q = wv * SWB + i_l;
+      const bool ok = i_tk < myB && q < n;
       const int qq = ok ? q : 0;
       const int g = qq / SB, s = qq - g * SB;
       const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;
@@ -438,73 +432,101 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
         }
       }
     };
-#pragma unroll
-    for (int d = 0; d < D; ++d) issue_w(d);
-    // wait for the start signal of the down phase (bounded)
-    if (wv == 0 && G > 0) {
-      uint32_t* flag = c.go + (size_t)b0 * kCtrlStride;
-      uint32_t it = 0;
-      for (;;) {
-        uint32_t v = 0;
-        if (lane == 0) v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (__shfl(v, 0, 64)) break;
-        if (++it >= kPollLimit) {
-          if (lane == 0) atomicOr(c.err, 1u);
-          break;
-        }
-        __builtin_amdgcn_s_sleep(16);
+    // the end of a task: sum the waves' partials in wave order, store y
+    // and the merged output (lanes 16j + r: token r, rows 16t + 4j .. + 3)
+    f32x4 yh = {0, 0, 0, 0};   // host partial of the current task (wave 0)
+    auto load_yh = [&](int tk) {
+      if (wv == 0 && a.y_host && tok) {
+        const int t = b0 + (myA + tk) * gs - nA;
+        yh = *reinterpret_cast<const f32x4*>(a.y_host + (size_t)r * H + 16 * t + 4 * j);
       }
-      if (lane == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // h written on other XCDs is read from memory
-    }
-    __syncthreads();
+    };
+    auto finish = [&](int tk, const f32x4& acc) {
+      const int t = b0 + (myA + tk) * gs - nA;
+      f32x4(&rb)[NW][64] = red[tk & 1];
+      rb[wv][lane] = acc;
+      __syncthreads();
+      if (wv == 0 && tok) {
+        f32x4 Y = rb[0][lane];
 #pragma unroll
-    for (int d = 0; d < D; ++d) issue_h(d);
-    f32x4 acc = {0, 0, 0, 0};
-    int c_tk = 0, c_l = 0;
-    for (int i0 = 0; i0 < nsteps; i0 += D) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        if (i0 + d < nsteps) {
-          f32x4 p = {0, 0, 0, 0};
-          if (!FP8) {
-            p = mfma16x16x32(wb[d][0], ob[d][0], p);
-            p = mfma16x16x32(wb[d][1], ob[d][1], p);
-          } else {
-#pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              u32x4 lo, hi;
-              e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
-              p = mfma16x16x32(lo, ob[d][2 * b], p);
-              p = mfma16x16x32(hi, ob[d][2 * b + 1], p);
-            }
-          }
-          const float f = fb[d];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) acc[q] += f * p[q];
-          if (c_l == SWB - 1) {   // end of a task: reduce over the waves, add into y
-            const int task = b0 + (myA + c_tk) * gs - nA;
-            const int t = task >> 1;
-            f32x4(&rb)[NW][64] = red[c_tk & 1];
-            rb[wv][lane] = acc;
-            __syncthreads();
-            if (wv == 0 && tok) {
-              f32x4 Y = rb[0][lane];
-#pragma unroll
-              for (int w2 = 1; w2 < NW; ++w2) Y += rb[w2][lane];
-              float* yr = a.y + (size_t)r * H + 16 * t + 4 * j;
-#pragma unroll
-              for (int q = 0; q < 4; ++q) atomicAdd(yr + q, Y[q]);
-            }
-            acc = f32x4{0, 0, 0, 0};
-            c_l = 0;
-            ++c_tk;
-          } else {
-            ++c_l;
+        for (int w2 = 1; w2 < NW; ++w2) Y += rb[w2][lane];
+        const size_t o = (size_t)r * H + 16 * t + 4 * j;
+        if (a.y) *reinterpret_cast<f32x4*>(a.y + o) = Y;
+        if (a.y_out) {
+          const f32x4 M = Y + yh;
+          *reinterpret_cast<f32x4*>(a.y_out + o) = M;
+          if (a.y_bf16) {
+            const uint32_t lo = f32_to_bf16_rne(M[0]) | ((uint32_t)f32_to_bf16_rne(M[1]) << 16);
+            const uint32_t hi = f32_to_bf16_rne(M[2]) | ((uint32_t)f32_to_bf16_rne(M[3]) << 16);
+            *reinterpret_cast<u32x2*>(a.y_bf16 + o) = u32x2{lo, hi};
           }
         }
-        issue_w(d);
-        issue_h(d);
+      }
+    };
+    if (SWB == 0) {   // no pick on the GPU: y = 0, y_out = y_host
+      for (int tk = 0; tk < myB; ++tk) {
+        load_yh(tk);
+        finish(tk, f32x4{0, 0, 0, 0});
+      }
+    } else {
+#pragma unroll
+      for (int d = 0; d < D; ++d) issue_w(d);
+      load_yh(0);
+      // wait for the start signal of the down phase (bounded)
+      if (wv == 0) {
+        uint32_t* flag = c.go + (size_t)b0 * kCtrlStride;
+        uint32_t it = 0;
+        for (;;) {
+          uint32_t v = 0;
+          if (lane == 0) v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (__shfl(v, 0, 64)) break;
+          if (++it >= kPollLimit) {
+            if (lane == 0) atomicOr(c.err, 1u);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(16);
+        }
+        if (lane == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // h written on other XCDs is read from memory
+      }
+      __syncthreads();
+#pragma unroll
+      for (int d = 0; d < D; ++d) issue_h(d);
+      f32x4 acc = {0, 0, 0, 0};
+      int c_tk = 0, c_l = 0;
+      for (int i0 = 0; i0 < nsteps; i0 += D) {
+#pragma unroll
+        for (int d = 0; d < D; ++d) {
+          if (i0 + d < nsteps) {
+            f32x4 p = {0, 0, 0, 0};
+            if (!FP8) {
+              p = mfma16x16x32(wb[d][0], ob[d][0], p);
+              p = mfma16x16x32(wb[d][1], ob[d][1], p);
+            } else {
+#pragma unroll
+              for (int b = 0; b < 2; ++b) {
+                u32x4 lo, hi;
+                e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
+                p = mfma16x16x32(lo, ob[d][2 * b], p);
+                p = mfma16x16x32(hi, ob[d][2 * b + 1], p);
+              }
+            }
+            const float f = fb[d];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) acc[q] += f * p[q];
+            if (c_l == SWB - 1) {
+              finish(c_tk, acc);
+              acc = f32x4{0, 0, 0, 0};
+              c_l = 0;
+              ++c_tk;
+              if (c_tk < myB) load_yh(c_tk);
+            } else {
+              ++c_l;
+            }
+          }
+          issue_w(d);
+          issue_h(d);
+        }
       }
     }
   }
@@ -536,7 +558,10 @@ struct PfArgs {
   const uint16_t* x;
   const int32_t* pick_slot;
   const float* w;
-  float* y;
+  float* y;              // [T][H] GPU partial sum, or NULL
+  const float* y_host;   // merge: [T][H] host partial sum, or NULL
+  float* y_out;          // merge: y + y_host, or NULL
+  uint16_t* y_bf16;      // merge: BF16 of y_out, or NULL
   // workspace
   int32_t* hist;         // [n_chunks][n_slots] counts, then bases
   int32_t* cnt;          // [n_slots]
@@ -893,9 +918,25 @@ __global__ __launch_bounds__(256) void pf_combine_kernel(PfArgs a) {
       }
     }
   }
-  float* yr = a.y + (size_t)t * a.H + c;
-  *reinterpret_cast<f32x4*>(yr) = f32x4{s[0], s[1], s[2], s[3]};
-  *reinterpret_cast<f32x4*>(yr + 4) = f32x4{s[4], s[5], s[6], s[7]};
+  const size_t o = (size_t)t * a.H + c;
+  const f32x4 y0 = {s[0], s[1], s[2], s[3]}, y1 = {s[4], s[5], s[6], s[7]};
+  if (a.y) {
+    *reinterpret_cast<f32x4*>(a.y + o) = y0;
+    *reinterpret_cast<f32x4*>(a.y + o + 4) = y1;
+  }
+  if (a.y_out) {   // merge with the host partial sum
+    const f32x4 m0 = y0 + *reinterpret_cast<const f32x4*>(a.y_host + o);
+    const f32x4 m1 = y1 + *reinterpret_cast<const f32x4*>(a.y_host + o + 4);
+    *reinterpret_cast<f32x4*>(a.y_out + o) = m0;
+    *reinterpret_cast<f32x4*>(a.y_out + o + 4) = m1;
+    if (a.y_bf16) {
+      const uint32_t b0 = f32_to_bf16_rne(m0[0]) | ((uint32_t)f32_to_bf16_rne(m0[1]) << 16);
+      const uint32_t b1 = f32_to_bf16_rne(m0[2]) | ((uint32_t)f32_to_bf16_rne(m0[3]) << 16);
+      const uint32_t b2 = f32_to_bf16_rne(m1[0]) | ((uint32_t)f32_to_bf16_rne(m1[1]) << 16);
+      const uint32_t b3 = f32_to_bf16_rne(m1[2]) | ((uint32_t)f32_to_bf16_rne(m1[3]) << 16);
+      *reinterpret_cast<u32x4*>(a.y_bf16 + o) = u32x4{b0, b1, b2, b3};
+    }
+  }
 }
 
 // ================================================================ merge
@@ -967,7 +1008,7 @@ struct DecOcc {
   int fu[2] = {0, 0};
 };
 constexpr int kDecD = 4;   // register-ring depth in 2-brick steps
-constexpr int kDecW = 4;   // waves per workgroup
+constexpr int kDecW = 8;   // waves per workgroup
 static std::mutex g_occ_mu;
 static DecOcc g_occ[64];
 static moe_status dec_occupancy(DecOcc* out) {
@@ -1061,16 +1102,17 @@ extern "C" moe_status moe_pack_weights(int32_t wtype, int32_t H, int32_t I, int3
   return MOE_OK;
 }
 
-extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,
-                                         const float* w, int32_t T, int32_t k, float* y, void* ws, size_t ws_bytes,
-                                         uint32_t mode, hipStream_t stream) {
-  clear_error();
+static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot, const float* w,
+                              int32_t T, int32_t k, float* y, const float* y_host, float* y_out, uint16_t* y_bf16,
+                              void* ws, size_t ws_bytes, uint32_t mode, hipStream_t stream) {
   moe_status st = check_slots(slots);
   if (st) return st;
   if (T < 0 || k < 1) MOE_FAIL(MOE_ERR_SHAPE, "bad T=%d k=%d", T, k);
   if (T == 0) return MOE_OK;
-  if (!x || !pick_slot || !w || !y || !ws) MOE_FAIL(MOE_ERR_ARG, "null argument");
-  if (!aligned16(x) || !aligned16(y)) MOE_FAIL(MOE_ERR_ARG, "x and y must be 16-byte aligned");
+  if (!x || !pick_slot || !w || !ws) MOE_FAIL(MOE_ERR_ARG, "null argument");
+  if (!aligned16(x) || (y && !aligned16(y)) || (y_host && !aligned16(y_host)) || (y_out && !aligned16(y_out)) ||
+      (y_bf16 && !aligned16(y_bf16)))
+    MOE_FAIL(MOE_ERR_ARG, "x and the outputs must be 16-byte aligned");
   if (reinterpret_cast<uintptr_t>(ws) & 255) MOE_FAIL(MOE_ERR_ARG, "workspace must be 256-byte aligned");
   const bool fp8 = slots->wtype == MOE_W_FP8_B128;
   const int H = slots->H, I = slots->I;
@@ -1090,6 +1132,7 @@ extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t*
     a.s_gate = slots->s_gate; a.s_up = slots->s_up; a.s_down = slots->s_down;
     a.H = H; a.I = I; a.n_slots = slots->n_slots; a.T = T; a.k = k;
     a.x = x; a.pick_slot = pick_slot; a.w = w; a.y = y;
+    a.y_host = y_host; a.y_out = y_out; a.y_bf16 = y_bf16;
     a.h = (uint16_t*)(wsb + L.h);
     a.G_max = T * k < slots->n_slots ? T * k : slots->n_slots;
     DecWsDev c{};
@@ -1120,6 +1163,7 @@ extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t*
   a.H = H; a.I = I; a.n_slots = slots->n_slots; a.T = T; a.k = k; a.P = T * k;
   a.tm = L.tm; a.max_mtiles = L.max_mtiles; a.chunk = L.chunk;
   a.x = x; a.pick_slot = pick_slot; a.w = w; a.y = y;
+  a.y_host = y_host; a.y_out = y_out; a.y_bf16 = y_bf16;
   a.hist = (int32_t*)(wsb + L.hist);
   a.cnt = (int32_t*)(wsb + L.cnt);
   a.off = (int32_t*)(wsb + L.off);
@@ -1148,6 +1192,23 @@ extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t*
   pf_combine_kernel<<<(unsigned)ncomb, 256, 0, stream>>>(a);
   MOE_LAUNCHED();
   return MOE_OK;
+}
+
+extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,
+                                         const float* w, int32_t T, int32_t k, float* y, void* ws, size_t ws_bytes,
+                                         uint32_t mode, hipStream_t stream) {
+  clear_error();
+  if (T > 0 && !y) MOE_FAIL(MOE_ERR_ARG, "y is NULL");
+  return run_forward(slots, x, pick_slot, w, T, k, y, nullptr, nullptr, nullptr, ws, ws_bytes, mode, stream);
+}
+
+extern "C" moe_status moe_expert_forward_merge(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,
+                                               const float* w, int32_t T, int32_t k, float* y_gpu,
+                                               const float* y_host, float* y_out, uint16_t* y_out_bf16, void* ws,
+                                               size_t ws_bytes, uint32_t mode, hipStream_t stream) {
+  clear_error();
+  if (T > 0 && (!y_host || !y_out)) MOE_FAIL(MOE_ERR_ARG, "y_host and y_out are required");
+  return run_forward(slots, x, pick_slot, w, T, k, y_gpu, y_host, y_out, y_out_bf16, ws, ws_bytes, mode, stream);
 }
 
 extern "C" moe_status moe_merge_partial(const float* y_gpu, const float* y_host, int32_t T, int32_t H, float* y_out,

@@ -33,6 +33,17 @@ def _run_forward(b, pool, x_bits, pick_slot, w, mode, T_max=None):
         torch.cuda.synchronize()
         assert np.array_equal(y2.cpu().numpy().view(np.uint32), out.view(np.uint32))
         assert int(ws[:4].view(torch.int32).item()) == 0
+    # forward + merge in one call: the same bits as the two calls
+    yh = torch.randn((T, pool.H), dtype=torch.float32, device="cuda")
+    yg = torch.full((T, pool.H), float("nan"), dtype=torch.float32, device="cuda")
+    yb = torch.empty((T, pool.H), dtype=torch.uint16, device="cuda")
+    yo = b.expert_forward_merge(*args[:5], ws, yh, y_gpu=yg, y_out_bf16=yb)
+    ref_b = torch.empty_like(yb)
+    ref_o = b.merge_partial(y, yh, y_out_bf16=ref_b)
+    torch.cuda.synchronize()
+    assert np.array_equal(yg.cpu().numpy().view(np.uint32), out.view(np.uint32))
+    assert torch.equal(yo.view(torch.int32), ref_o.view(torch.int32))
+    assert torch.equal(yb, ref_b)
     return out
 
 
