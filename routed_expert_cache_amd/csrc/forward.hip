@@ -255,9 +255,12 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   const int RA = I / 8;
   const int nA = G * RA, nB = H / 16;
   const int b0 = (int)blockIdx.x, gs = (int)gridDim.x;
-  const int myA = nA > b0 ? (nA - b0 + gs - 1) / gs : 0;                  // my tasks below nA
-  const int myAll = nA + nB > b0 ? (nA + nB - b0 + gs - 1) / gs : 0;
-  const int myB = myAll - myA;
+  // the gate/up tasks go round-robin over the whole grid (the fewest per
+  // compute unit at most); the down tasks start at workgroup nA % gs, the
+  // first one with one gate/up task fewer
+  const int myA = nA > b0 ? (nA - b0 + gs - 1) / gs : 0;
+  const int tb0 = (b0 - nA % gs + gs) % gs;                               // my first down task
+  const int myB = nB > tb0 ? (nB - tb0 + gs - 1) / gs : 0;
   u32x4 wb[D][2], ob[D][XN];   // weight bricks and the other operand (x or h) of D steps
 
   // ================= phase A: gate/up + SwiGLU
@@ -393,7 +396,7 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
     bool qok[D];
     int i_tk = 0, i_l = 0;
     auto issue_w = [&](int d) {   // weights of the next step; remembers its (group, step)
-      const int t = b0 + (myA + i_tk) * gs - nA;   // 16-row block of y
+      const int t = tb0 + i_tk * gs;   // 16-row block of y
       const int q = wv * SWB + i_l;
       const bool ok = i_tk < myB && q < n;
       const int qq = ok ? q : 0;
@@ -437,12 +440,12 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
     f32x4 yh = {0, 0, 0, 0};   // host partial of the current task (wave 0)
     auto load_yh = [&](int tk) {
       if (wv == 0 && a.y_host && tok) {
-        const int t = b0 + (myA + tk) * gs - nA;
+        const int t = tb0 + tk * gs;
         yh = *reinterpret_cast<const f32x4*>(a.y_host + (size_t)r * H + 16 * t + 4 * j);
       }
     };
     auto finish = [&](int tk, const f32x4& acc) {
-      const int t = b0 + (myA + tk) * gs - nA;
+      const int t = tb0 + tk * gs;
       f32x4(&rb)[NW][64] = red[tk & 1];
       rb[wv][lane] = acc;
       __syncthreads();
@@ -1007,7 +1010,8 @@ struct DecOcc {
   int cus = 0;
   int fu[2] = {0, 0};
 };
-constexpr int kDecD = 4;   // register-ring depth in 2-brick steps
+constexpr int kDecD_BF16 = 4;   // register-ring depth in 2-brick steps
+constexpr int kDecD_FP8 = 3;    // (FP8 steps carry twice the x operand: a shallower ring keeps 2 workgroups per CU)
 constexpr int kDecW = 8;   // waves per workgroup
 static std::mutex g_occ_mu;
 static DecOcc g_occ[64];
@@ -1020,8 +1024,8 @@ static moe_status dec_occupancy(DecOcc* out) {
   if (!o.cus) {
     int cus = 0;
     MOE_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0], dec_fused_kernel<false, kDecD, kDecW>, kDecW * 64, 0));
-    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1], dec_fused_kernel<true, kDecD, kDecW>, kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0], dec_fused_kernel<false, kDecD_BF16, kDecW>, kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1], dec_fused_kernel<true, kDecD_FP8, kDecW>, kDecW * 64, 0));
     for (int i = 0; i < 2; ++i)
       if (o.fu[i] < 1) o.fu[i] = 1;
     o.cus = cus > 0 ? cus : 1;
@@ -1144,9 +1148,9 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     const long tasks = (long)a.G_max * (I / 8) + 2L * (H / 16);
     const unsigned g1 = (unsigned)std::min<long>(std::min<long>(tasks, (long)occ.cus * occ.fu[f]), kDecGridMax);
     if (fp8)
-      dec_fused_kernel<true, kDecD, kDecW><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      dec_fused_kernel<true, kDecD_FP8, kDecW><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else
-      dec_fused_kernel<false, kDecD, kDecW><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      dec_fused_kernel<false, kDecD_BF16, kDecW><<<g1, kDecW * 64, 0, stream>>>(a, c);
     MOE_LAUNCHED();
     return MOE_OK;
   }
