@@ -71,7 +71,7 @@ def measured_traffic(key, algorithmic_bytes=None):
 
 # kernels that make up one launch of each measured entry point (name prefixes)
 PMC_LAUNCHES = {
-    "decode_bf16_forward": ["void moe::dec_gu_kernel<false", "void moe::dec_dn_kernel<false"],
+    "decode_bf16_forward": ["void moe::dec_fused_kernel<false"],
     "prefill_bf16_forward": ["moe::pf_count_kernel", "moe::pf_scan_kernel", "moe::pf_scatter_kernel",
                              "void moe::pf_gemm_kernel<false, true>", "void moe::pf_gemm_kernel<false, false>",
                              "moe::pf_combine_kernel"],
@@ -190,6 +190,37 @@ def parse():
     return p.parse_args()
 
 
+# ---------------------------------------------------------------- read ceiling
+def read_ceiling(b, nbytes, reps=20):
+    """Context for the decode roofline: the same number of bytes read from HBM
+    (a 512 MB write before each rep evicts the caches), HIP-event timed like
+    the forward, by (1) moe_stream_read, one launch of plain wide loads and
+    nothing else: what a single launch streaming a working set this small
+    reaches, start-up and tail included; (2) a library reduction
+    (torch.sum over float32)."""
+    import torch
+    x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty((), dtype=torch.float32, device="cuda")
+    sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+    res = {"bytes": nbytes}
+    for name, fn in (("moe_stream_read", lambda: b.stream_read(x, sink)),
+                     ("torch_sum", lambda: torch.sum(x, dim=0, out=out))):
+        ev = HipEvents(2 * reps)
+        for r in range(reps):
+            flush.fill_(float(r))
+            ev.record(2 * r)
+            fn()
+            ev.record(2 * r + 1)
+        torch.cuda.synchronize()
+        us = sorted(ev.ms(2 * r, 2 * r + 1) * 1e3 for r in range(reps))
+        ev.close()
+        med = us[len(us) // 2]
+        res[name] = dict(median_us=med, best_us=us[0], GBps_median=nbytes / med / 1e3,
+                         frac_median=nbytes / med / 1e3 / PEAK_HBM_GBPS)
+    return res
+
+
 # ---------------------------------------------------------------- decode trace
 def run_decode(b, K, W):
     import torch
@@ -217,23 +248,29 @@ def run_decode(b, K, W):
     y = torch.empty((L, 1, H), dtype=torch.float32, device="cuda")
     pick = out.pick_slot.view(1, k)
 
-    def layer_step(cache, s, l, ev=None, i=0):
+    rec_pick = torch.empty((K * L, 1, k), dtype=torch.int32, device="cuda")
+    rec_w = torch.empty((K * L, 1, k), dtype=torch.float32, device="cuda")
+
+    def layer_step(cache, s, l, ev=None, i=0, fill=True):
         cache.route_step(l, lg[s, l], ids, w, out, copy=False)      # router + cache step, one launch
         if ev:
+            rec_pick[i].copy_(pick)                                  # for the forward-only burst below
+            rec_w[i].copy_(w)
             ev.record(3 * i)
-        cache.fill(out)
+        if fill:
+            cache.fill(out)                                          # PCIe: host pool -> filled slots
         if ev:
             ev.record(3 * i + 1)
         b.expert_forward_merge(pool.c, x[s, l], pick, w, b.FWD_DECODE, ws, yh[l], y_out=y[l])   # + merge
         if ev:
             ev.record(3 * i + 2)
 
-    def run_trace(ev):
+    def run_trace(ev, fill=True):
         """Cold cache, W warm-up steps, then K timed steps; returns (wall s, counter deltas)."""
         cache = b.Cache(L, E, k, 1, pool, host, c.bp, c.bh)
         for s in range(W):
             for l in range(L):
-                layer_step(cache, s, l)
+                layer_step(cache, s, l, fill=fill)
         torch.cuda.synchronize()
         c0 = cache.read_state()[4].astype(np.int64)
         torch.cuda.synchronize()
@@ -241,7 +278,7 @@ def run_decode(b, K, W):
         i = 0
         for s in range(W, W + K):
             for l in range(L):
-                layer_step(cache, s, l, ev, i)
+                layer_step(cache, s, l, ev, i, fill=fill)
                 i += 1
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
@@ -249,10 +286,14 @@ def run_decode(b, K, W):
         cache.destroy()
         return wall, d
 
-    # Two passes over the same trace from the same cold cache make the same
-    # decisions.  The first brackets every fill and forward with HIP events
-    # (fill time, forward time); the second runs without events, because each
-    # event record costs a few microseconds of GPU time, and gives the wall.
+    # Three passes over the same trace from the same cold cache make the same
+    # decisions (they do not depend on the copies).  Pass 1 brackets every
+    # fill and forward with HIP events (fill time, forward time).  Pass 2 runs
+    # the full path without events (each record costs GPU time): the
+    # PCIe-inclusive wall.  Pass 3 leaves out the PCIe fill copies, the one
+    # part that moves host memory: the filled slots then hold stale bytes but
+    # the forward streams the same slots, so its wall is the path with every
+    # input resident in HBM (`value`).
     log("decode: pass 1 (events): warmup %d steps, timing %d steps" % (W, K))
     ev = HipEvents(3 * K * L)
     wall_ev, d = run_trace(ev)
@@ -262,19 +303,39 @@ def run_decode(b, K, W):
     log("decode: pass 2 (no events)")
     wall, d2 = run_trace(None)
     assert np.array_equal(d, d2), "the two passes made different cache decisions"
+    log("decode: pass 3 (no events, no PCIe fill copies)")
+    wall_res, d3 = run_trace(None, fill=False)
+    assert np.array_equal(d, d3), "the passes made different cache decisions"
+    # Forward-only burst: the timed layer calls' forward launches again, back
+    # to back with the same picks (the slots now hold other experts: the same
+    # bytes), one event pair per step of 40 layers: the kernel's duration with
+    # no event between its launches.
+    log("decode: forward-only burst")
+    evb = HipEvents(2 * K)
+    for si in range(K):
+        evb.record(2 * si)
+        for l in range(L):
+            i = si * L + l
+            b.expert_forward_merge(pool.c, x[W + si, l], rec_pick[i], rec_w[i], b.FWD_DECODE, ws, yh[l], y_out=y[l])
+        evb.record(2 * si + 1)
+    torch.cuda.synchronize()
+    burst_s = sum(evb.ms(2 * si, 2 * si + 1) for si in range(K)) / 1e3
+    evb.close()
     n_g = int(d[2] + d[4])
     gpu_bytes = n_g * S
-    hbm_s = wall - fill_s
     res = dict(
-        value=gpu_bytes / hbm_s / 1e9,
-        ms_per_step=hbm_s / K * 1e3,
+        value=gpu_bytes / wall_res / 1e9,
+        ms_per_step=wall_res / K * 1e3,
         roofline=dict(kernel="moe_expert_forward_merge decode (one kernel: gate/up, down, merge)",
-                      bound="hbm", achieved=gpu_bytes / fwd_s / 1e9, peak=PEAK_HBM_GBPS, unit="GB/s",
+                      bound="hbm", achieved=gpu_bytes / burst_s / 1e9, peak=PEAK_HBM_GBPS, unit="GB/s",
                       bytes_per_launch=gpu_bytes / (K * L), launches=K * L,
-                      avg_launch_us=fwd_s / (K * L) * 1e6, traffic=None),
+                      avg_launch_us=burst_s / (K * L) * 1e6,
+                      timing="forward-only burst of the timed calls' launches, one HIP event pair per 40 launches",
+                      avg_launch_us_in_trace=fwd_s / (K * L) * 1e6, traffic=None),
         detail=dict(
             wall_ms_per_step_pcie_inclusive=wall / K * 1e3,
             pcie_inclusive_GBps=gpu_bytes / wall / 1e9,
+            wall_minus_fill_events_ms_per_step=(wall - fill_s) / K * 1e3,
             fill_ms_per_step=fill_s / K * 1e3,
             fill_GBps=(d[4] * S / fill_s / 1e9) if fill_s > 0 else None,
             miss_rate=float(d[3] / d[1]),
@@ -287,6 +348,7 @@ def run_decode(b, K, W):
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_HBM_GBPS
     res["roofline"]["traffic"] = measured_traffic("decode_bf16_forward", res["roofline"]["bytes_per_launch"])
     res["detail"]["wall_ms_per_step_with_events"] = wall_ev / K * 1e3
+    res["roofline"]["read_ceiling"] = read_ceiling(b, int(res["roofline"]["bytes_per_launch"]) // 4096 * 4096)
     return res
 
 

@@ -352,6 +352,17 @@ moe_status moe_prefill_destroy(moe_prefill_t p, hipStream_t stream);
  */
 moe_status moe_e4m3_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream);
 
+/*
+ * Measurement reference, not a step of the method: one launch that reads
+ * `bytes` from `src` with the decode kernels' wide non-temporal loads and
+ * does nothing else (each workgroup folds what it read into sink[0..255]
+ * with atomic XORs, so the loads stay).  Its duration bounds what any single
+ * launch streaming the same bytes can reach on this GPU, start-up and tail
+ * included.  src: device, 16-byte aligned; bytes a multiple of 16; sink:
+ * device uint32 [256].  Capturable.
+ */
+moe_status moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -32,7 +32,7 @@ EXPORTS = [
     "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_expert_forward_merge",
     "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
-    "moe_prefill_destroy", "moe_e4m3_to_bf16", "moe_pack_weights",
+    "moe_prefill_destroy", "moe_e4m3_to_bf16", "moe_pack_weights", "moe_stream_read",
 ]
 
 
@@ -85,6 +85,7 @@ _sig = {
     "moe_expert_forward_merge": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
                                         _u32, _vp]),
     "moe_merge_partial": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
+    "moe_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
     "moe_prefill_create": (_i32, [_vp, _P(_vp)]),
     "moe_prefill_prefetch": (_i32, [_vp, _i32, _vp]),
     "moe_prefill_acquire": (_i32, [_vp, _i32, _vp, _P(Slots)]),
@@ -297,6 +298,12 @@ def merge_partial(y_gpu, y_host, y_out=None, y_out_bf16=None, stream=None):
     _check(_lib.moe_merge_partial(_ptr(y_gpu), _ptr(y_host), T, H, _ptr(y_out), _ptr(y_out_bf16),
                                   _stream(stream)), "moe_merge_partial")
     return y_out
+
+
+def stream_read(src, sink, stream=None):
+    """One launch that only reads src (a measurement reference)."""
+    _check(_lib.moe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
+           "moe_stream_read")
 
 
 def e4m3_to_bf16(codes, out=None, stream=None):

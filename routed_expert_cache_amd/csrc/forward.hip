@@ -1230,6 +1230,39 @@ extern "C" moe_status moe_merge_partial(const float* y_gpu, const float* y_host,
   return MOE_OK;
 }
 
+namespace moe {
+// Plain streaming read: 4 non-temporal 16-byte loads per thread in flight,
+// grid-stride, folded with XOR and one atomic per workgroup.
+__global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, size_t n, uint32_t* sink) {
+  const size_t gsz = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + 3 * gsz < n; i += 4 * gsz) {
+    u32x4 v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p + i + u * gsz);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+  }
+  for (; i < n; i += gsz) {
+    const u32x4 v = __builtin_nontemporal_load(p + i);
+    acc ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+  }
+  for (int m = 32; m >= 1; m >>= 1) acc ^= (uint32_t)__shfl_xor((int)acc, m, 64);
+  if ((threadIdx.x & 63) == 0) atomicXor(sink + (blockIdx.x & 255), acc);
+}
+}  // namespace moe
+
+extern "C" moe_status moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  clear_error();
+  if (bytes == 0) return MOE_OK;
+  if (!src || !sink) MOE_FAIL(MOE_ERR_ARG, "null argument");
+  if (!aligned16(src) || (bytes & 15)) MOE_FAIL(MOE_ERR_ARG, "src must be 16-byte aligned and bytes a multiple of 16");
+  stream_read_kernel<<<512, 256, 0, stream>>>((const u32x4*)src, bytes / 16, sink);
+  MOE_LAUNCHED();
+  return MOE_OK;
+}
+
 extern "C" moe_status moe_e4m3_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream) {
   clear_error();
   if (n < 0) MOE_FAIL(MOE_ERR_SHAPE, "n < 0");

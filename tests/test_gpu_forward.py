@@ -320,3 +320,16 @@ def test_pack_matches_brick_format(wtype, H, I):
                 t, rr = row // 16, row % 16
                 kt, j, e = col // KB, (col % KB) // per, col % per
                 assert dp[ex, brick_elem(H, I, t, kt, 16 * j + rr, e)] == wd[ex, row, col]
+
+
+def test_stream_read_reads_every_word_once():
+    """The measurement reference read folds every 32-bit word exactly once."""
+    b = binding()
+    for n16 in (1, 1000, 3 * 512 * 256 * 4 + 77):
+        src = torch.randint(-2 ** 31, 2 ** 31 - 1, (n16 * 4,), dtype=torch.int32, device="cuda")
+        sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+        b.stream_read(src, sink)
+        torch.cuda.synchronize()
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        ref = np.bitwise_xor.reduce(src.cpu().numpy().view(np.uint32))
+        assert got == ref
