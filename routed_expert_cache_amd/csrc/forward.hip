@@ -550,6 +550,7 @@ constexpr int kSortChunk = 2048;   // least pairs per counting workgroup
 constexpr int kSortMaxChunks = 32; // counting workgroups at most
 constexpr int kSortMaxSlots = 4096;
 constexpr int kPfRows = 512;       // bank rows per tile (4 waves x 128)
+constexpr int kPfStages = 4;       // LDS stages of 40 KB (the whole 160 KB of a CU)
 
 struct PfArgs {
   const void* w_gu;
@@ -716,8 +717,8 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   constexpr int NTG = TM / 32;           // token groups (MFMA N blocks) per wave
   constexpr int TBW = FP8 ? 2 * NTG : NTG;   // token bricks a wave reads per step (FP8: lo and hi)
   constexpr int SB = 32 + 8;             // bricks per stage: 32 weight + 8 token
-  __shared__ __attribute__((aligned(1024))) char Ls[3][SB * 1024];
-  __shared__ int rowsrc[TM];
+  constexpr int NS = kPfStages;          // stages in flight
+  __shared__ __attribute__((aligned(1024))) char Ls[NS][SB * 1024];
 
   const int K = GATEUP ? a.H : a.I;
   const int NROWS = GATEUP ? 2 * a.I : a.H;          // bank rows
@@ -744,7 +745,6 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   const int t0 = (nb * kPfRows + 128 * wr) / 16;        // first brick row of this wave's rows
   const bool rows_ok = nb * kPfRows + 128 * wr < NROWS;
 
-  if (tid < TM) rowsrc[tid] = tid < mrows ? (GATEUP ? a.sorted_pair[seg + m0 + tid] / a.k : seg + m0 + tid) : -1;
   const size_t bank_bytes = (size_t)(GATEUP ? 2 : 1) * a.I * a.H * (FP8 ? 1 : 2);
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc((const char*)(GATEUP ? a.w_gu : a.w_down) + (size_t)slot * bank_bytes +
                                                    (size_t)(rows_ok ? t0 : 0) * nkt * 1024,
@@ -752,24 +752,33 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   const uint16_t* tsrc = GATEUP ? a.x : a.h;
   const uint32_t tbytes = (uint32_t)((size_t)(GATEUP ? a.T : a.P) * K * 2);
   const __amdgpu_buffer_rsrc_t trs = make_rsrc(tsrc, tbytes);
+  // FP8 block scales: wave-uniform pointers (scalar loads, so reading a scale
+  // never waits on the stage loads in flight); gate/up lanes j < 2 hold gate
+  // rows and j >= 2 up rows (64 features in one 128-block).
   const float* scp = nullptr;
+  const float* scq = nullptr;
   if (FP8) {
     const int nbk = K / 128;
-    if (GATEUP)   // lanes j < 2 hold gate rows, j >= 2 up rows; 64 features in one 128-block
-      scp = (j < 2 ? a.s_gate : a.s_up) + ((size_t)slot * (a.I / 128) + (8 * t0) / 128) * nbk;
-    else
-      scp = a.s_down + ((size_t)slot * (a.H / 128) + (16 * t0) / 128) * nbk;
+    if (GATEUP) {
+      const size_t o = ((size_t)slot * (a.I / 128) + (8 * t0) / 128) * nbk;
+      scp = a.s_gate + o;
+      scq = a.s_up + o;
+    } else {
+      scp = scq = a.s_down + ((size_t)slot * (a.H / 128) + (16 * t0) / 128) * nbk;
+    }
   }
-  __syncthreads();
   // Loads of one step, 5 per wave: weight bricks 4 wt .. 4 wt + 3 of row
   // block wr (stage bricks 8 wr + ...), and token brick tb = wv (stage brick
   // 32 + tb; BF16: token group tb, FP8: group tb / 2, low or high half).
+  // Lane r of the token brick fetches pair row 16 tg + r of the tile: a row
+  // of x (gate/up: the pair's token) or of h (down: the pair itself).
   const int tb = wv;
   const int tg_of_tb = FP8 ? tb >> 1 : tb;
-  const int tsrc_row = rowsrc[16 * tg_of_tb + r];
+  const int prow = 16 * tg_of_tb + r;
+  const int tsrc_row = prow < mrows ? (GATEUP ? a.sorted_pair[seg + m0 + prow] / a.k : seg + m0 + prow) : -1;
   const uint32_t tkoff = FP8 ? (uint32_t)(16 * j + 8 * (tb & 1)) : (uint32_t)(8 * j);
   auto issue = [&](int st) {
-    char* stage = Ls[st % 3];
+    char* stage = Ls[st % NS];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int bi = 4 * wt + q;
@@ -791,8 +800,16 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   // the LDS-destination loads, does not wait for every load in flight before
   // them; the asm waits that follow tie the read registers.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)&Ls[0][0];
+  // FP8: the two scales of a 128-K block are fetched by scalar loads issued at
+  // the end of its first step (after that step's LDS reads have all returned)
+  // and waited for at the start of its second, before any LDS read is in
+  // flight: the LDS waits below count LDS reads only while no scalar load is
+  // outstanding.  A vector load here would make the compiler wait for every
+  // stage load in flight.
+  float s_g = 0.f, s_u = 0.f;
   auto compute = [&](int st) {
-    const uint32_t stage = lds0 + (uint32_t)((st % 3) * SB * 1024);
+    if (FP8 && (st & 1)) asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(s_g), "+s"(s_u));
+    const uint32_t stage = lds0 + (uint32_t)((st % NS) * SB * 1024);
     const uint32_t wbase = stage + (8 * wr) * 1024 + lane * 16;
     const uint32_t tbase = stage + (32 + wt * TBW) * 1024 + lane * 16;
     u32x4 tf[TBW], wf[8];
@@ -834,7 +851,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
       }
     }
     if (FP8 && (st & 1)) {
-      const float sc = scp[st >> 1];
+      const float sc = j < 2 ? s_g : s_u;
 #pragma unroll
       for (int bi = 0; bi < 8; ++bi)
 #pragma unroll
@@ -842,23 +859,29 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[bi][tg][i] += sc * part[bi][tg][i];
     }
+    if (FP8 && !(st & 1)) {
+      asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_g) : "s"(scp + (st >> 1)));
+      asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_u) : "s"(scq + (st >> 1)));
+    }
   };
 
-  // Step st reads stage st % 3.  Before the barrier of step st each wave
-  // waits for its own loads of step st (only step st+1's 5 may remain); the
-  // barrier then also orders every wave's reads of step st-1 before the
-  // loads of step st+2 into the same stage.  A raw barrier: a fence would
-  // wait for all loads in flight.
+  // Step st reads stage st % NS.  Before the barrier of step st each wave
+  // waits for its own loads of step st (only the 5 of each later step in
+  // flight may remain); the barrier then also orders every wave's reads of
+  // step st-1 before the loads of step st+NS-1 into the same stage.  A raw
+  // barrier: a fence would wait for all loads in flight.
   const int nsteps = nkt;
-  issue(0);
-  if (nsteps > 1) issue(1);
+  for (int st = 0; st < NS - 1 && st < nsteps; ++st) issue(st);
   for (int st = 0; st < nsteps; ++st) {
-    if (st + 1 < nsteps)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5); expcnt, lgkmcnt not waited on
+    const int later = min(nsteps - 1 - st, NS - 2);   // steps issued after st still in flight
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10); expcnt, lgkmcnt not waited on
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
     else
       __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
     __builtin_amdgcn_s_barrier();
-    if (st + 2 < nsteps) issue(st + 2);
+    if (st + NS - 1 < nsteps) issue(st + NS - 1);
     compute(st);
   }
   if (!rows_ok) return;
