@@ -176,6 +176,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=64)
     p.add_argument("--prefill-reps", type=int, default=10)
     p.add_argument("--cpu-seconds", type=float, default=15.0)
+    p.add_argument("--cpu-prefill", type=int, default=0, metavar="ROWS",
+                   help="also time the oracle on ROWS tokens of the prefill BF16 chunk (about 40 s of host "
+                        "work for weight generation and decoding besides the timed FFN)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 decode and FP8 double-buffered prefill runs")
@@ -252,18 +255,21 @@ def run_decode(b, K, W):
     rec_w = torch.empty((K * L, 1, k), dtype=torch.float32, device="cuda")
 
     def layer_step(cache, s, l, ev=None, i=0, fill=True):
+        if ev:
+            ev.record(4 * i)
         cache.route_step(l, lg[s, l], ids, w, out, copy=False)      # router + cache step, one launch
         if ev:
+            ev.record(4 * i + 1)
             rec_pick[i].copy_(pick)                                  # for the forward-only burst below
             rec_w[i].copy_(w)
-            ev.record(3 * i)
+            ev.record(4 * i + 2)
         if fill:
             cache.fill(out)                                          # PCIe: host pool -> filled slots
         if ev:
-            ev.record(3 * i + 1)
+            ev.record(4 * i + 3)
         b.expert_forward_merge(pool.c, x[s, l], pick, w, b.FWD_DECODE, ws, yh[l], y_out=y[l])   # + merge
         if ev:
-            ev.record(3 * i + 2)
+            ev.record(4 * i + 4)
 
     def run_trace(ev, fill=True):
         """Cold cache, W warm-up steps, then K timed steps; returns (wall s, counter deltas)."""
@@ -295,10 +301,11 @@ def run_decode(b, K, W):
     # the forward streams the same slots, so its wall is the path with every
     # input resident in HBM (`value`).
     log("decode: pass 1 (events): warmup %d steps, timing %d steps" % (W, K))
-    ev = HipEvents(3 * K * L)
+    ev = HipEvents(4 * K * L + 1)
     wall_ev, d = run_trace(ev)
-    fill_s = sum(ev.ms(3 * i, 3 * i + 1) for i in range(K * L)) / 1e3
-    fwd_s = sum(ev.ms(3 * i + 1, 3 * i + 2) for i in range(K * L)) / 1e3
+    step_s = sum(ev.ms(4 * i, 4 * i + 1) for i in range(K * L)) / 1e3
+    fill_s = sum(ev.ms(4 * i + 2, 4 * i + 3) for i in range(K * L)) / 1e3
+    fwd_s = sum(ev.ms(4 * i + 3, 4 * i + 4) for i in range(K * L)) / 1e3
     ev.close()
     log("decode: pass 2 (no events)")
     wall, d2 = run_trace(None)
@@ -343,6 +350,7 @@ def run_decode(b, K, W):
             fills_per_layer_call=float(d[4] / (K * L)),
             host_experts_per_layer_call=float(d[5] / (K * L)),
             layer_calls=int(d[0]),
+            route_and_cache_step_us=step_s / (K * L) * 1e6,
         ),
     )
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_HBM_GBPS
@@ -588,6 +596,35 @@ def run_prefill_fp8(b):
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
+def cpu_prefill_oracle(rows):
+    """The oracle on a sample of the prefill BF16 chunk: the exact float64
+    FFN of `rows` tokens (each with its k picks), as oracle GFLOP/s (the
+    weights are decoded to float64 before the timed part)."""
+    from harness import gen, CONFIGS
+    from oracle import route, ffn, numerics
+    c = CONFIGS["prefill_bf16"]
+    T, H, I, E, k = c.T, c.H, c.I, c.E, c.k
+    wg, wu, wd = gen.bank_bf16(c.cfg_id, E, H, I, c.w_std)
+    xb = gen.activations_bf16(gen.np_rng(c.cfg_id, gen.S_ACT), T, H)
+    wr = gen.router_matrix(gen.np_rng(c.cfg_id, gen.S_ROUTER), H, E, c.router_std)
+    lg = gen.router_logits(xb[:rows], wr)
+    ids, w = route.topk_softmax(lg, k)
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            cache[e] = (numerics.bf16_to_f64(wg[e]), numerics.bf16_to_f64(wu[e]), numerics.bf16_to_f64(wd[e]))
+        return cache[e]
+    for e in range(E):
+        expert(e)                                           # decode the weights outside the timed part
+    t0 = time.perf_counter()
+    ffn.moe_output(numerics.bf16_to_f64(xb[:rows]), ids, w, expert)
+    el = time.perf_counter() - t0
+    fl = 6.0 * H * I * rows * k
+    return dict(value=fl / el / 1e9, unit="GFLOP/s", rows=rows, seconds=el, us_per_token=el / rows * 1e6,
+                sample="first %d tokens of the prefill BF16 chunk, float64 FFN of their %d picks" % (rows, k))
+
+
 def cpu_baseline(budget_s):
     """The oracle, as it stands, on the decode trace: route, LRU cache step and
     the exact FFN of every pick, layer call after layer call from a cold cache,
@@ -673,6 +710,8 @@ def main():
     if not a.no_cpu_baseline:
         log("cpu baseline: oracle for %.0f s" % a.cpu_seconds)
         line["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
+        if a.cpu_prefill:
+            line["cpu_baseline"]["prefill_bf16"] = cpu_prefill_oracle(a.cpu_prefill)
     print(json.dumps(line), flush=True)
 
 
