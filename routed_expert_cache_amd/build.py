@@ -3,12 +3,17 @@
     python -m routed_expert_cache_amd.build
 
 Every source is compiled on each call (the build is the "does it build"
-check); objects go to routed_expert_cache_amd/_build/.
+check); objects go to routed_expert_cache_amd/_build/.  The device assembly
+of every source is then checked for registers of hand-timed asm loads that
+the compiler touches before their wait (asm_check.py); the build fails on
+any.
 """
 import os
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
+
+from routed_expert_cache_amd import asm_check
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -39,6 +44,7 @@ def build(verbose=True):
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         results = list(ex.map(_compile, SOURCES))
+        list(ex.map(lambda s: asm_check.check_sources(CSRC, [s], HIPCC, FLAGS), SOURCES))
     for obj, warn in results:
         if warn.strip() and verbose:
             print(warn, file=sys.stderr)
