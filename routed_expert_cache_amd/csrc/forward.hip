@@ -366,8 +366,11 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
                 if (last) __hip_atomic_store(c.all, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
               }
               if (__ballot(last)) {   // every group is done: start the down phase
-                for (int tb = nA + lane; tb < nA + nB; tb += 64)
-                  __builtin_amdgcn_raw_buffer_store_b32(1u, gow, (uint32_t)((tb % gs) * kCtrlStride * 4), 0, 16);
+                // one store per workgroup holding a down task (a second store
+                // could land after that workgroup cleared its flag)
+                for (int bb = lane; bb < gs; bb += 64)
+                  if ((bb - nA % gs + gs) % gs < nB)
+                    __builtin_amdgcn_raw_buffer_store_b32(1u, gow, (uint32_t)(bb * kCtrlStride * 4), 0, 16);
               }
             }
             acc = f32x4{0, 0, 0, 0};

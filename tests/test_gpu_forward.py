@@ -68,6 +68,46 @@ def test_decode_bf16(T, E, k, H, I):
     check_layer(y, yg, "decode bf16")
 
 
+@pytest.mark.parametrize("n_gpu", [1, 2])
+def test_decode_few_groups_full_shape(n_gpu):
+    """One or two groups at the decode shape (H 2048, I 768): most of the grid
+    holds no gate/up task, and the down tasks start on workgroups that had
+    none."""
+    b = binding()
+    T, E, k, H, I = 2, 16, 8, 2048, 768
+    bank = Bf16Bank(70 + n_gpu, E, H, I)
+    pool = _slots_identity(b, bank, b.W_BF16)
+    rng = np.random.default_rng(40 + n_gpu)
+    x = gen.activations_bf16(rng, T, H)
+    ids = np.stack([rng.choice(E, size=k, replace=False) for _ in range(T)])
+    ids[:, :n_gpu] = np.arange(n_gpu)                    # the GPU picks: the same n_gpu experts
+    w = np.exp(rng.standard_normal((T, k)))
+    w /= w.sum(1, keepdims=True)
+    on_gpu = np.zeros(ids.shape, bool)
+    on_gpu[:, :n_gpu] = True
+    pick = np.where(on_gpu, ids, -1)
+    y = _run_forward(b, pool, x, pick, w, b.FWD_DECODE)
+    yg, _ = oracle_partials(x, ids, w, bank.expert64, on_gpu)
+    check_layer(y, yg, "decode few groups")
+
+
+def test_decode_more_down_tasks_than_workgroups():
+    """H 16384: 1024 down tasks, more than the resident workgroups, so some
+    workgroups hold two; each is started once per call, and two calls in a
+    row on one workspace give the same bits with the error word clear."""
+    b = binding()
+    T, E, k, H, I = 2, 4, 2, 16384, 128
+    bank = Bf16Bank(75, E, H, I)
+    pool = _slots_identity(b, bank, b.W_BF16)
+    rng = np.random.default_rng(75)
+    x = gen.activations_bf16(rng, T, H)
+    ids = np.array([[0, 1], [2, 1]])
+    w = np.array([[0.6, 0.4], [0.3, 0.7]])
+    y = _run_forward(b, pool, x, ids, w, b.FWD_DECODE)
+    yg, _ = oracle_partials(x, ids, w, bank.expert64, np.ones(ids.shape, bool))
+    check_layer(y, yg, "decode H 16384")
+
+
 def test_decode_shared_slots_across_tokens():
     """Several tokens routed to the same slots: each slot streamed once."""
     b = binding()
