@@ -256,6 +256,28 @@ def test_prefill_bf16_full_shape_sampled():
     check_layer(y[rows], ref, "prefill bf16 full")
 
 
+def test_prefill_fp8_full_shape_sampled():
+    """Prefill FP8 workload layer (8192 tokens, H 7168, E 256, top-8 of x.W_r,
+    I 2048, E4M3 with 128x128 scales), the first and the last token checked
+    against the oracle, every output finite."""
+    b = binding()
+    c = CONFIGS["prefill_fp8"]
+    bank = Fp8Bank(c.cfg_id, c.E, c.H, c.I, c.w_std, device="cuda", pin=False)
+    pool = _slots_identity(b, bank, b.W_FP8_B128)
+    x = gen.activations_bf16(gen.np_rng(c.cfg_id, gen.S_ACT), c.T, c.H)
+    wr = gen.router_matrix(gen.np_rng(c.cfg_id, gen.S_ROUTER), c.H, c.E, c.router_std)
+    lg = gen.router_logits(x, wr)
+    ids_d, w_d = b.route_topk(dev(lg), c.k)
+    ids, w = route.topk_softmax(lg, c.k)
+    assert np.array_equal(ids_d.cpu().numpy(), ids)
+    ws = b.forward_workspace(c.T, c.k, c.H, c.I, c.E, b.FWD_PREFILL)
+    y = b.expert_forward(pool.c, dev(x), ids_d, w_d, b.FWD_PREFILL, ws).cpu().numpy()
+    assert np.all(np.isfinite(y))
+    rows = [0, c.T - 1]
+    ref = ffn.moe_output(numerics.bf16_to_f64(x[rows]), ids[rows], w[rows], bank.expert64)
+    check_layer(y[rows], ref, "prefill fp8 full")
+
+
 def test_prefill_equals_decode_small_batch():
     b = binding()
     bank = Bf16Bank(43, 8, 256, 128)
