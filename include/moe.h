@@ -280,7 +280,9 @@ moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int32_t H, int3
  * stream without clearing; calls that overlap on one workspace race.  A
  * decode call whose internal wait timed out (only possible when its
  * workgroups cannot all be resident, e.g. a shared GPU) sets the first
- * 32-bit word of ws to a non-zero value and y is then not valid.
+ * 32-bit word of ws to a non-zero value; y is then not valid, and ws must be
+ * zero-filled again before its next use (a late hand-over store may leave a
+ * control word set).
  * Requires H, I multiples of 128 (FP8) or of 32 (BF16).  Capturable.
  */
 moe_status moe_expert_forward(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,

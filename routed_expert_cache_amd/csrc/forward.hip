@@ -12,8 +12,8 @@
 // wave is one contiguous 1 KB segment.
 // Decode (T <= 16): every slot in G is streamed once from HBM; the brick is
 // the MFMA A operand and the (up to 16) tokens are B, so one read of a slot
-// serves the whole batch.  Two launches: gate/up + SwiGLU into h, then down
-// with the per-token gate weights.
+// serves the whole batch.  One launch: gate/up + SwiGLU into h, then down
+// with the per-token gate weights (and the merge with the host partial sum).
 // Prefill (any T): (token, pick) pairs counting-sorted by slot, a grouped
 // MFMA GEMM for gate/up with the SwiGLU epilogue, a grouped MFMA GEMM for
 // down with the gate-weight epilogue into per-pair rows, and a combine that
@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void pack_kernel(int fp8, int H, int I, int n,
 }
 
 // ================================================================ decode
-// Both launches are grids of resident workgroups that walk a task list
+// The launch is a grid of resident workgroups that walk a task list
 // round-robin.  Every weight and activation load is a raw buffer load whose
 // offset is pushed past the buffer's end when the step does not exist, so the
 // hardware returns zeros without touching memory: each wave issues one fixed
@@ -542,9 +542,9 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
 // (token, pick) pairs are counting-sorted by slot in three launches (per
 // workgroup histograms, one scan, scatter), then two grouped GEMMs walk a
 // tile list: tile = (slot, 128 or 64 sorted pairs) x (512 bank rows).  The
-// weight bricks are the MFMA A operand, streamed from memory straight into
-// registers; the tokens' rows are the B operand, staged in LDS.  Each wave
-// owns 128 bank rows, so the accumulator of a lane holds 4 consecutive bank
+// weight bricks are the MFMA A operand and the tokens' rows the B operand;
+// both go from memory straight into LDS stages.  Each wave owns 128 bank
+// rows, so the accumulator of a lane holds 4 consecutive bank
 // rows of one token: SwiGLU pairs a gate lane with the up lane 32 away, and
 // the outputs leave registers as 8-byte stores.  Gate/up writes h [P][I]
 // (BF16); down writes the gate-weighted rows o [P][H] (BF16); a last launch
@@ -697,9 +697,9 @@ __global__ __launch_bounds__(256) void pf_scatter_kernel(PfArgs a) {
 // [128 wr, 128 wr + 128) against pairs [TM/2 wt, TM/2 wt + TM/2).  K
 // advances one brick per step.  Every operand goes from memory straight
 // into LDS as 1 KB MFMA bricks (buffer loads with an LDS destination: 32
-// weight bricks + 8 token bricks per step, 5 per wave), three stages deep,
-// so two steps of loads are in flight while the MFMAs of the third run; one
-// barrier per step.  A token brick's lane (r, j) fetches 16 bytes of pair
+// weight bricks + 8 token bricks per step, 5 per wave), kPfStages (4) stages
+// deep, so three steps of loads are in flight while the MFMAs of the fourth
+// run; one barrier per step.  A token brick's lane (r, j) fetches 16 bytes of pair
 // row 16g + r at the brick's K offset for group j, so the LDS image is
 // already the MFMA operand.  FP8: two steps make one 128-K scale block; its
 // partial sums are scaled once and added (post-scaling).  Tiles are taken
