@@ -874,18 +874,82 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   // step st-1 before the loads of step st+NS-1 into the same stage.  A raw
   // barrier: a fence would wait for all loads in flight.
   const int nsteps = nkt;
-  for (int st = 0; st < NS - 1 && st < nsteps; ++st) issue(st);
-  for (int st = 0; st < nsteps; ++st) {
-    const int later = min(nsteps - 1 - st, NS - 2);   // steps issued after st still in flight
-    if (later >= 2)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10); expcnt, lgkmcnt not waited on
-    else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
+  if constexpr (FP8) {
+    for (int st = 0; st < NS - 1 && st < nsteps; ++st) issue(st);
+    for (int st = 0; st < nsteps; ++st) {
+      const int later = min(nsteps - 1 - st, NS - 2);   // steps issued after st still in flight
+      if (later >= 2)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10); expcnt, lgkmcnt not waited on
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      if (st + NS - 1 < nsteps) issue(st + NS - 1);
+      compute(st);
+    }
+  } else {
+    // BF16: the operands of step st+1 are read from LDS while the MFMAs of
+    // step st run from registers.  Top of step st: every wave's reads of
+    // stage st are complete (lgkmcnt 0) and its loads of step st+1 have
+    // landed; the barrier then makes stage st+1 readable and stage st free,
+    // and the loads of step st+NS go into it.  Weight brick bi of step st+1
+    // is read right after the MFMAs of brick bi of step st are issued (the
+    // read returns long after they took their operands); the token bricks
+    // alternate between two register sets.  nsteps is even (K is a multiple
+    // of 64), so the loop runs in pairs with no branch around a read.
+    static_assert(TBW == 4, "BF16 layout");
+    const uint32_t wofs = (8 * wr) * 1024 + lane * 16, tofs = (32 + wt * TBW) * 1024 + lane * 16;
+    u32x4 wf[8], ta[TBW], tb2[TBW];
+    auto rd_t = [&](int st, u32x4 (&tf)[TBW]) {
+      const uint32_t base = lds0 + (uint32_t)((st % NS) * SB * 1024) + tofs;
+#pragma unroll
+      for (int q = 0; q < TBW; ++q) asm volatile("ds_read_b128 %0, %1" : "=v"(tf[q]) : "v"(base + q * 1024));
+    };
+    auto rd_w = [&](int st, int bi) {
+      const uint32_t base = lds0 + (uint32_t)((st % NS) * SB * 1024) + wofs;
+      asm volatile("ds_read_b128 %0, %1" : "=v"(wf[bi]) : "v"(base + bi * 1024));
+    };
+    auto wait_all = [&](u32x4 (&tf)[TBW]) {   // every read issued so far has returned
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(tf[0]), "+v"(tf[1]), "+v"(tf[2]), "+v"(tf[3]), "+v"(wf[0]), "+v"(wf[1]), "+v"(wf[2]),
+                     "+v"(wf[3]), "+v"(wf[4]), "+v"(wf[5]), "+v"(wf[6]), "+v"(wf[7]));
+    };
+    auto step = [&](int st, u32x4 (&tc)[TBW], u32x4 (&tn)[TBW]) {
+      wait_all(tc);
+      // loads issued so far: steps up to min(st + NS - 1, nsteps - 1); step st+1's must be in
+      const int later = min(nsteps - 1, st + NS - 1) - (st + 1);
+      if (later >= 2)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10)
+      else if (later == 1)
+        __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
+      else
+        __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+      __builtin_amdgcn_s_barrier();
+      if (st + NS < nsteps) issue(st + NS);
+      rd_t(st + 1, tn);   // past the last step this reads a stale stage: never used
+#pragma unroll
+      for (int bi = 0; bi < 8; ++bi) {
+#pragma unroll
+        for (int tg = 0; tg < NTG; ++tg) acc[bi][tg] = mfma16x16x32(wf[bi], tc[tg], acc[bi][tg]);
+        rd_w(st + 1, bi);
+      }
+    };
+    static_assert(NS == 4, "the waits below count 5 loads per step, NS - 1 steps behind");
+    for (int st = 0; st < NS && st < nsteps; ++st) issue(st);
+    if (nsteps >= 4)   // step 0's loads are in (nsteps is even: 2 or >= 4)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 15);   // vmcnt(15)
     else
-      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
     __builtin_amdgcn_s_barrier();
-    if (st + NS - 1 < nsteps) issue(st + NS - 1);
-    compute(st);
+    rd_t(0, ta);
+#pragma unroll
+    for (int bi = 0; bi < 8; ++bi) rd_w(0, bi);
+    for (int st = 0; st < nsteps; st += 2) {
+      step(st, ta, tb2);
+      step(st + 1, tb2, ta);
+    }
+    wait_all(ta);   // the reads past the last step land before their registers are reused
   }
   if (!rows_ok) return;
 

@@ -196,7 +196,8 @@ def test_decode_fp8_full_shape(T):
 
 
 # ---------------------------------------------------------------- prefill
-@pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 128), (300, 8, 2, 256, 128), (1000, 16, 4, 512, 192)])
+@pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 128), (300, 8, 2, 256, 128), (1000, 16, 4, 512, 192),
+                                       (257, 8, 2, 128, 64)])   # two K steps in the down GEMM
 def test_prefill_bf16(T, E, k, H, I):
     b = binding()
     bank = Bf16Bank(50 + E, E, H, I)
