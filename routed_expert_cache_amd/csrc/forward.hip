@@ -21,6 +21,7 @@
 #include "common.h"
 
 #include <algorithm>
+#include <type_traits>
 #include <mutex>
 
 namespace moe {
@@ -803,57 +804,84 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   // the LDS-destination loads, does not wait for every load in flight before
   // them; the asm waits that follow tie the read registers.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)&Ls[0][0];
-  // FP8: the two scales of a 128-K block are fetched by scalar loads issued at
-  // the end of its first step (after that step's LDS reads have all returned)
-  // and waited for at the start of its second, before any LDS read is in
-  // flight: the LDS waits below count LDS reads only while no scalar load is
-  // outstanding.  A vector load here would make the compiler wait for every
-  // stage load in flight.
+  // FP8: the two scales of a 128-K block are fetched by scalar loads (a vector
+  // load would make the compiler wait for every stage load in flight); the
+  // only LDS wait below is lgkmcnt(0), which a scalar load in flight cannot
+  // make return early.
   float s_g = 0.f, s_u = 0.f;
-  auto compute = [&](int st) {
-    if (FP8 && (st & 1)) asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(s_g), "+s"(s_u));
-    const uint32_t stage = lds0 + (uint32_t)((st % NS) * SB * 1024);
-    const uint32_t wbase = stage + (8 * wr) * 1024 + lane * 16;
-    const uint32_t tbase = stage + (32 + wt * TBW) * 1024 + lane * 16;
-    u32x4 tf[TBW], wf[8];
+
+  const int nsteps = nkt;
+  // The operands of step st+1 are read from LDS while the MFMAs of step st
+  // run from registers.  Top of step st: every wave's reads of stage st are
+  // complete (lgkmcnt 0, which also covers the FP8 scale loads) and its loads
+  // of step st+1 have landed; the barrier then makes stage st+1 readable and
+  // stage st free, and the loads of step st+NS go into it.  Weight brick bi
+  // of step st+1 is read right after the MFMAs of brick bi of step st are
+  // issued (the read returns long after they took their operands); the token
+  // bricks alternate between two register sets.  nsteps is even (BF16: K is
+  // a multiple of 64; FP8: of 128, one scale block per two steps), so the
+  // loop runs in pairs with no branch around a read.  FP8: the two scales
+  // of a block are loaded (scalar loads) on its first step and applied to
+  // the block's partial sums at the end of its second (post-scaling).
+  static_assert(TBW == 4, "two register sets of 4 token bricks");
+  static_assert(NS == 4, "the waits below count 5 loads per step, NS - 1 steps behind");
+  const uint32_t wofs = (8 * wr) * 1024 + lane * 16, tofs = (32 + wt * TBW) * 1024 + lane * 16;
+  u32x4 wf[8], ta[TBW], tb2[TBW];
+  auto rd_t = [&](int st, u32x4 (&tf)[TBW]) {
+    const uint32_t base = lds0 + (uint32_t)((st % NS) * SB * 1024) + tofs;
 #pragma unroll
-    for (int q = 0; q < TBW; ++q) asm volatile("ds_read_b128 %0, %1" : "=v"(tf[q]) : "v"(tbase + q * 1024));
-#pragma unroll
-    for (int bi = 0; bi < 8; ++bi) asm volatile("ds_read_b128 %0, %1" : "=v"(wf[bi]) : "v"(wbase + bi * 1024));
-    // LDS returns in order: wait for the token bricks and weight brick 0,
-    // then for one more weight brick before each row of MFMAs.
-    if (TBW == 4)
-      asm volatile("s_waitcnt lgkmcnt(7)" : "+v"(tf[0]), "+v"(tf[1]), "+v"(tf[2]), "+v"(tf[3]), "+v"(wf[0]));
+    for (int q = 0; q < TBW; ++q) asm volatile("ds_read_b128 %0, %1" : "=v"(tf[q]) : "v"(base + q * 1024));
+  };
+  auto rd_w = [&](int st, int bi) {
+    const uint32_t base = lds0 + (uint32_t)((st % NS) * SB * 1024) + wofs;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(wf[bi]) : "v"(base + bi * 1024));
+  };
+  auto wait_all = [&](u32x4 (&tf)[TBW]) {   // every LDS read and scale load issued so far has returned
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(tf[0]), "+v"(tf[1]), "+v"(tf[2]), "+v"(tf[3]), "+v"(wf[0]), "+v"(wf[1]), "+v"(wf[2]),
+                   "+v"(wf[3]), "+v"(wf[4]), "+v"(wf[5]), "+v"(wf[6]), "+v"(wf[7]));
+  };
+  // ODD: the step's parity, known at compile time because the loop runs in pairs
+  auto step = [&](int st, u32x4 (&tc)[TBW], u32x4 (&tn)[TBW], auto odd) {
+    constexpr bool ODD = decltype(odd)::value;
+    wait_all(tc);
+    if constexpr (FP8 && ODD) asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(s_g), "+s"(s_u));   // the block's scales
+    // loads issued so far: steps up to min(st + NS - 1, nsteps - 1); step st+1's must be in
+    const int later = min(nsteps - 1, st + NS - 1) - (st + 1);
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10)
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
     else
-      asm volatile("s_waitcnt lgkmcnt(7)" : "+v"(tf[0]), "+v"(tf[1]), "+v"(wf[0]));
-    if (FP8 && (st & 1) == 0)
+      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
+    __builtin_amdgcn_s_barrier();
+    if (st + NS < nsteps) issue(st + NS);
+    if constexpr (FP8 && !ODD) {
+      asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_g) : "s"(scp + (st >> 1)));
+      asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_u) : "s"(scq + (st >> 1)));
 #pragma unroll
       for (int bi = 0; bi < 8; ++bi)
 #pragma unroll
         for (int tg = 0; tg < NTG; ++tg) part[bi][tg] = f32x4{0, 0, 0, 0};
+    }
+    rd_t(st + 1, tn);   // past the last step this reads a stale stage: never used
 #pragma unroll
     for (int bi = 0; bi < 8; ++bi) {
-      if (bi == 1) asm volatile("s_waitcnt lgkmcnt(6)" : "+v"(wf[1]));
-      if (bi == 2) asm volatile("s_waitcnt lgkmcnt(5)" : "+v"(wf[2]));
-      if (bi == 3) asm volatile("s_waitcnt lgkmcnt(4)" : "+v"(wf[3]));
-      if (bi == 4) asm volatile("s_waitcnt lgkmcnt(3)" : "+v"(wf[4]));
-      if (bi == 5) asm volatile("s_waitcnt lgkmcnt(2)" : "+v"(wf[5]));
-      if (bi == 6) asm volatile("s_waitcnt lgkmcnt(1)" : "+v"(wf[6]));
-      if (bi == 7) asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(wf[7]));
       if (!FP8) {
 #pragma unroll
-        for (int tg = 0; tg < NTG; ++tg) acc[bi][tg] = mfma16x16x32(wf[bi], tf[tg], acc[bi][tg]);
+        for (int tg = 0; tg < NTG; ++tg) acc[bi][tg] = mfma16x16x32(wf[bi], tc[tg], acc[bi][tg]);
       } else {
         u32x4 lo, hi;
         e4m3x16_to_bf16_nat(wf[bi], lo, hi);
 #pragma unroll
         for (int tg = 0; tg < NTG; ++tg) {
-          part[bi][tg] = mfma16x16x32(lo, tf[2 * tg], part[bi][tg]);
-          part[bi][tg] = mfma16x16x32(hi, tf[2 * tg + 1], part[bi][tg]);
+          part[bi][tg] = mfma16x16x32(lo, tc[2 * tg], part[bi][tg]);
+          part[bi][tg] = mfma16x16x32(hi, tc[2 * tg + 1], part[bi][tg]);
         }
       }
+      rd_w(st + 1, bi);
     }
-    if (FP8 && (st & 1)) {
+    if constexpr (FP8 && ODD) {
       const float sc = j < 2 ? s_g : s_u;
 #pragma unroll
       for (int bi = 0; bi < 8; ++bi)
@@ -862,95 +890,21 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) acc[bi][tg][i] += sc * part[bi][tg][i];
     }
-    if (FP8 && !(st & 1)) {
-      asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_g) : "s"(scp + (st >> 1)));
-      asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_u) : "s"(scq + (st >> 1)));
-    }
   };
-
-  // Step st reads stage st % NS.  Before the barrier of step st each wave
-  // waits for its own loads of step st (only the 5 of each later step in
-  // flight may remain); the barrier then also orders every wave's reads of
-  // step st-1 before the loads of step st+NS-1 into the same stage.  A raw
-  // barrier: a fence would wait for all loads in flight.
-  const int nsteps = nkt;
-  if constexpr (FP8) {
-    for (int st = 0; st < NS - 1 && st < nsteps; ++st) issue(st);
-    for (int st = 0; st < nsteps; ++st) {
-      const int later = min(nsteps - 1 - st, NS - 2);   // steps issued after st still in flight
-      if (later >= 2)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10); expcnt, lgkmcnt not waited on
-      else if (later == 1)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      if (st + NS - 1 < nsteps) issue(st + NS - 1);
-      compute(st);
-    }
-  } else {
-    // BF16: the operands of step st+1 are read from LDS while the MFMAs of
-    // step st run from registers.  Top of step st: every wave's reads of
-    // stage st are complete (lgkmcnt 0) and its loads of step st+1 have
-    // landed; the barrier then makes stage st+1 readable and stage st free,
-    // and the loads of step st+NS go into it.  Weight brick bi of step st+1
-    // is read right after the MFMAs of brick bi of step st are issued (the
-    // read returns long after they took their operands); the token bricks
-    // alternate between two register sets.  nsteps is even (K is a multiple
-    // of 64), so the loop runs in pairs with no branch around a read.
-    static_assert(TBW == 4, "BF16 layout");
-    const uint32_t wofs = (8 * wr) * 1024 + lane * 16, tofs = (32 + wt * TBW) * 1024 + lane * 16;
-    u32x4 wf[8], ta[TBW], tb2[TBW];
-    auto rd_t = [&](int st, u32x4 (&tf)[TBW]) {
-      const uint32_t base = lds0 + (uint32_t)((st % NS) * SB * 1024) + tofs;
+  for (int st = 0; st < NS && st < nsteps; ++st) issue(st);
+  if (nsteps >= 4)   // step 0's loads are in (nsteps is even: 2 or >= 4)
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 15);   // vmcnt(15)
+  else
+    __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
+  __builtin_amdgcn_s_barrier();
+  rd_t(0, ta);
 #pragma unroll
-      for (int q = 0; q < TBW; ++q) asm volatile("ds_read_b128 %0, %1" : "=v"(tf[q]) : "v"(base + q * 1024));
-    };
-    auto rd_w = [&](int st, int bi) {
-      const uint32_t base = lds0 + (uint32_t)((st % NS) * SB * 1024) + wofs;
-      asm volatile("ds_read_b128 %0, %1" : "=v"(wf[bi]) : "v"(base + bi * 1024));
-    };
-    auto wait_all = [&](u32x4 (&tf)[TBW]) {   // every read issued so far has returned
-      asm volatile("s_waitcnt lgkmcnt(0)"
-                   : "+v"(tf[0]), "+v"(tf[1]), "+v"(tf[2]), "+v"(tf[3]), "+v"(wf[0]), "+v"(wf[1]), "+v"(wf[2]),
-                     "+v"(wf[3]), "+v"(wf[4]), "+v"(wf[5]), "+v"(wf[6]), "+v"(wf[7]));
-    };
-    auto step = [&](int st, u32x4 (&tc)[TBW], u32x4 (&tn)[TBW]) {
-      wait_all(tc);
-      // loads issued so far: steps up to min(st + NS - 1, nsteps - 1); step st+1's must be in
-      const int later = min(nsteps - 1, st + NS - 1) - (st + 1);
-      if (later >= 2)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10)
-      else if (later == 1)
-        __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
-      else
-        __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
-      __builtin_amdgcn_s_barrier();
-      if (st + NS < nsteps) issue(st + NS);
-      rd_t(st + 1, tn);   // past the last step this reads a stale stage: never used
-#pragma unroll
-      for (int bi = 0; bi < 8; ++bi) {
-#pragma unroll
-        for (int tg = 0; tg < NTG; ++tg) acc[bi][tg] = mfma16x16x32(wf[bi], tc[tg], acc[bi][tg]);
-        rd_w(st + 1, bi);
-      }
-    };
-    static_assert(NS == 4, "the waits below count 5 loads per step, NS - 1 steps behind");
-    for (int st = 0; st < NS && st < nsteps; ++st) issue(st);
-    if (nsteps >= 4)   // step 0's loads are in (nsteps is even: 2 or >= 4)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 15);   // vmcnt(15)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
-    __builtin_amdgcn_s_barrier();
-    rd_t(0, ta);
-#pragma unroll
-    for (int bi = 0; bi < 8; ++bi) rd_w(0, bi);
-    for (int st = 0; st < nsteps; st += 2) {
-      step(st, ta, tb2);
-      step(st + 1, tb2, ta);
-    }
-    wait_all(ta);   // the reads past the last step land before their registers are reused
+  for (int bi = 0; bi < 8; ++bi) rd_w(0, bi);
+  for (int st = 0; st < nsteps; st += 2) {
+    step(st, ta, tb2, std::false_type{});
+    step(st + 1, tb2, ta, std::true_type{});
   }
+  wait_all(ta);   // the reads past the last step land before their registers are reused
   if (!rows_ok) return;
 
   // ---- epilogue.  acc[bi][tg][i] at lane (r, j): bank row 16 (t0 + bi) + 4 j + i,
