@@ -603,19 +603,30 @@ __global__ __launch_bounds__(256) void pf_count_kernel(PfArgs a) {
 // pass 2 (one workgroup): slot totals and segment offsets, per-chunk bases
 // (hist is overwritten with the first sorted position of each chunk's pairs
 // of each slot), and the list of M tiles (slot, first row) in slot order.
-// A thread takes 4 slots; each slot's column of chunk counts is loaded into
-// registers at once (at most kSortMaxChunks), so no load waits on another.
+// Thread t takes the R = ceil(S / 1024) consecutive slots from t R; each
+// slot's column of chunk counts is read with raw buffer loads whose offset
+// leaves the buffer for a missing chunk (reading zero), so a column's loads
+// issue back to back.  n_chunks * S <= kSortMaxChunks * kSortMaxSlots keeps
+// every byte offset below the out-of-range one.
 __global__ __launch_bounds__(1024) void pf_scan_kernel(PfArgs a, int n_chunks) {
   __shared__ int wsum[16], wsum2[16];
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int S = a.n_slots, TM = a.tm;
+  static_assert(kSortMaxSlots <= 4 * 1024, "four slots per thread at most");
+  const int R = (S + 1023) / 1024;   // at most kSortMaxSlots / 1024 = 4
+  const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.hist, (uint32_t)(4u * n_chunks * S));
+  auto column = [&](int s, int (&col)[kSortMaxChunks]) {
+#pragma unroll
+    for (int w = 0; w < kSortMaxChunks; ++w)
+      col[w] = (int)__builtin_amdgcn_raw_buffer_load_b32(
+          hr, (int)oob_sel(s < S && w < n_chunks, (uint32_t)((w * S + s) * 4)), 0, 0);
+  };
   int c[4], tc[4], ls = 0, lt = 0;
-#pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int s = tid * 4 + i;
+    c[i] = tc[i] = 0;
+    if (i >= R) continue;
     int col[kSortMaxChunks];
-#pragma unroll
-    for (int w = 0; w < kSortMaxChunks; ++w) col[w] = (s < S && w < n_chunks) ? a.hist[(size_t)w * S + s] : 0;
+    column(tid * R + i, col);
     int v = 0;
 #pragma unroll
     for (int w = 0; w < kSortMaxChunks; ++w) v += col[w];
@@ -644,16 +655,14 @@ __global__ __launch_bounds__(1024) void pf_scan_kernel(PfArgs a, int n_chunks) {
     bt += wsum2[w];
   }
   int es = bs + is - ls, et = bt + it - lt;   // exclusive prefix of this thread's first slot
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int s = tid * 4 + i;
+  for (int i = 0; i < R; ++i) {
+    const int s = tid * R + i;
     if (s < S) {
       a.cnt[s] = c[i];
       a.off[s] = es;
       a.mtoff[s] = et;
       int col[kSortMaxChunks];
-#pragma unroll
-      for (int w = 0; w < kSortMaxChunks; ++w) col[w] = w < n_chunks ? a.hist[(size_t)w * S + s] : 0;
+      column(s, col);
       int b = es;
 #pragma unroll
       for (int w = 0; w < kSortMaxChunks; ++w)
