@@ -404,6 +404,7 @@ def run_prefill(b, reps):
     layer_s = sum(ev.ms(3 * r, 3 * r + 2) for r in range(reps)) / 1e3 / reps
     ev.close()
     ach = flops / fwd_s / 1e12
+    lib = library_gemm_reference(E, T * k // E, H, I, flops)
     return dict(
         workload="prefill_bf16: 8192 tokens, hidden 2048, 128 experts, top-8 of x.W_r, SwiGLU I 768, BF16, all experts resident",
         value=flops / layer_s / 1e12, unit="TFLOP/s", ms_per_layer=layer_s * 1e3, wall_ms_per_rep=wall / reps * 1e3,
@@ -411,8 +412,41 @@ def run_prefill(b, reps):
         roofline=dict(kernel="moe_expert_forward prefill (sort + gate/up GEMM + down GEMM + combine)",
                       bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                       frac=ach / PEAK_BF16_TFLOPS, avg_launch_us=fwd_s * 1e6,
-                      traffic=measured_traffic("prefill_bf16_forward")),
+                      traffic=measured_traffic("prefill_bf16_forward"), library_gemm=lib),
     )
+
+
+def library_gemm_reference(E, M, H, I, flops, reps=10):
+    """Vendor-library reference for the prefill GEMMs: torch.bmm (hipBLASLt) in
+    BF16 on the same per-expert shapes with every expert holding the mean M
+    pairs (no sort, gather, ragged segments or combine), contiguous operands.
+    A context figure beside the roofline, like the plain-read reference of
+    the decode kernel; not the product path."""
+    import torch
+    out = {}
+    tot = 0.0
+    for name, N, K in (("gate_up", 2 * I, H), ("down", H, I)):
+        a = torch.randn(E, M, K, device="cuda", dtype=torch.bfloat16)
+        bm = torch.randn(E, K, N, device="cuda", dtype=torch.bfloat16).contiguous()
+        c = torch.empty(E, M, N, device="cuda", dtype=torch.bfloat16)
+        for _ in range(3):
+            torch.bmm(a, bm, out=c)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            torch.bmm(a, bm, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        tot += ms
+        out[name] = dict(shape="%d x [%d x %d] . [%d x %d]" % (E, M, K, K, N), ms=ms,
+                         TFLOPs=2.0 * E * M * N * K / ms / 1e9)
+        del a, bm, c
+    out["total_ms"] = tot
+    out["TFLOPs_on_layer_flops"] = flops / tot / 1e9
+    out["frac"] = out["TFLOPs_on_layer_flops"] / PEAK_BF16_TFLOPS
+    return out
 
 
 # ---------------------------------------------------------------- FP8 pools
