@@ -365,6 +365,66 @@ moe_status moe_e4m3_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipS
  */
 moe_status moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
+/*
+ * Host executor for the host set C ([FT] section "q* 策略": the misses a step
+ * does not fill are computed by the CPU while the GPU evaluates G, and the two
+ * partial sums are added; [OSDI] section 4.2: FP8 codes expanded on the CPU,
+ * each 128-wide block dotted first and multiplied by its scale once;
+ * [OSDI] section 4.3: gate, up, SiLU(gate) * up, down).  This is the CPU side
+ * of the method, never a substitute for the GPU evaluation of G.
+ *
+ * moe_host_exec_create starts n_threads - 1 worker threads (the calling
+ * thread is the n-th); they sleep between calls.  The executor uses AVX-512
+ * where the CPU has it (AVX512F + AVX512BW), else portable C++; flags
+ * MOE_HOST_PORTABLE selects the portable path everywhere.  Both sum in the
+ * same order within a 16-row brick row but group the additions differently,
+ * so their results agree to FP32 rounding, not bitwise.
+ * moe_host_exec_destroy joins the threads; no call may be running.
+ * moe_host_exec_simd returns 512 for an executor on the AVX-512 path, else 0.
+ */
+#define MOE_HOST_PORTABLE 1u
+typedef struct moe_host_exec* moe_host_exec_t;
+moe_status moe_host_exec_create(int32_t n_threads, uint32_t flags, moe_host_exec_t* out);
+moe_status moe_host_exec_destroy(moe_host_exec_t h);
+int32_t moe_host_exec_simd(moe_host_exec_t h);
+
+/*
+ * y_host[t] = sum over picks j with pick_slot[t,j] < 0 of
+ *             w[t,j] * W_down (silu(W_gate x_t) * (W_up x_t))   (expert ids[t,j])
+ * computed on the executor's threads from the packed rows of `pool` (the
+ * rows fills copy: the brick format, gate/up interleaved; FP8 with its
+ * 128x128 scales).  All pointers are host memory: x BF16 [T, H]; ids int32
+ * [T, k] logical ids (indices into the pool's tables; must be >= 0 where
+ * pick_slot < 0); pick_slot int32 [T, k] as written by moe_cache_step (only
+ * its sign is read); w float32 [T, k]; y_host float32 [T, H], fully
+ * overwritten (0 for tokens with no host pick).  Accumulation is FP32 and h
+ * stays FP32; each output element is summed by one thread in a fixed order,
+ * so the result has the same bits on every call and for any thread count.
+ * Calls on one executor are serialised.  Requires H, I multiples of 32 (BF16)
+ * or 128 (FP8) and I % 8 == 0.  Returns MOE_ERR_ARG on a NULL pointer or a
+ * negative host id, MOE_ERR_SHAPE on bad sizes.  Synchronous; not a HIP call.
+ */
+moe_status moe_host_forward(moe_host_exec_t h, const moe_host_pool* pool, int32_t wtype, int32_t H, int32_t I,
+                            const uint16_t* x, const int32_t* ids, const int32_t* pick_slot, const float* w,
+                            int32_t T, int32_t k, float* y_host);
+
+/*
+ * moe_host_forward in stream order: records the arguments in the executor
+ * (one descriptor per executor, replaced by the next enqueue) and enqueues on
+ * `stream` a host function that runs the call when the stream reaches it;
+ * later work on `stream` waits for it.  The host arrays (x, ids, pick_slot,
+ * w: written by earlier copies on the stream; y_host: read by later work)
+ * must stay valid until then, pinned if the GPU reads or writes them.
+ * Capturable: the host function becomes a graph node, and replays run the
+ * recorded descriptor again, so capture one enqueue per executor per graph.
+ * The host function makes no HIP call.  A failure inside it is kept until
+ * moe_host_exec_status reads it (returns and clears the first failure).
+ */
+moe_status moe_host_forward_enqueue(moe_host_exec_t h, const moe_host_pool* pool, int32_t wtype, int32_t H,
+                                    int32_t I, const uint16_t* x, const int32_t* ids, const int32_t* pick_slot,
+                                    const float* w, int32_t T, int32_t k, float* y_host, hipStream_t stream);
+moe_status moe_host_exec_status(moe_host_exec_t h);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,6 +23,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_NO_S
           -4: "MOE_ERR_NOT_PINNED", -5: "MOE_ERR_HIP", -6: "MOE_ERR_STATE", -7: "MOE_ERR_DEVICE"}
 W_BF16, W_FP8_B128 = 0, 1
 STEP_NO_COPY = 1
+HOST_PORTABLE = 1
 FWD_DECODE, FWD_PREFILL = 0, 1
 CNT_UNIQ, CNT_HIT, CNT_MISS, CNT_QSTAR, CNT_FILL, CNT_HOST, CNT_N = 0, 1, 2, 3, 4, 5, 8
 
@@ -33,6 +34,8 @@ EXPORTS = [
     "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_e4m3_to_bf16", "moe_pack_weights", "moe_stream_read",
+    "moe_host_exec_create", "moe_host_exec_destroy", "moe_host_exec_simd", "moe_host_forward",
+    "moe_host_forward_enqueue", "moe_host_exec_status",
 ]
 
 
@@ -93,6 +96,13 @@ _sig = {
     "moe_prefill_destroy": (_i32, [_vp, _vp]),
     "moe_e4m3_to_bf16": (_i32, [_vp, _vp, ctypes.c_int64, _vp]),
     "moe_pack_weights": (_i32, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_host_exec_create": (_i32, [_i32, _u32, _P(_vp)]),
+    "moe_host_exec_destroy": (_i32, [_vp]),
+    "moe_host_exec_simd": (_i32, [_vp]),
+    "moe_host_forward": (_i32, [_vp, _P(HostPool), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
+    "moe_host_forward_enqueue": (_i32, [_vp, _P(HostPool), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
+                                        _vp]),
+    "moe_host_exec_status": (_i32, [_vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -168,14 +178,15 @@ class HostPoolTables:
 
     `banks` is a list (gate_up, down[, s_gate, s_up, s_down]) of pinned host
     tensors whose first dim indexes *base* experts; `base_of` maps a logical
-    id to its base expert row."""
+    id to its base expert row.  pinned=False allows pageable tensors, for the
+    host executor alone (fills need pinned memory)."""
 
-    def __init__(self, banks, base_of, n_ids):
+    def __init__(self, banks, base_of, n_ids, pinned=True):
         self.banks = banks
         self._arrays = []
         ptrs = []
         for t in banks:
-            assert t.is_pinned(), "host pool banks must be pinned"
+            assert t.is_pinned() or not pinned, "host pool banks must be pinned"
             row = t[0].numel() * t.element_size()
             arr = (ctypes.c_void_p * n_ids)(*[t.data_ptr() + int(base_of(i)) * row for i in range(n_ids)])
             self._arrays.append(arr)
@@ -335,4 +346,52 @@ class PrefillPool:
     def destroy(self, stream=None):
         if self.h:
             _check(_lib.moe_prefill_destroy(self.h, _stream(stream)), "moe_prefill_destroy")
+            self.h = None
+
+
+# ---------------------------------------------------------------- host executor
+class HostExec:
+    """The CPU executor of the host set (moe_host_forward): a persistent pool
+    of n_threads threads (the caller counts as one)."""
+
+    def __init__(self, n_threads, portable=False):
+        h = ctypes.c_void_p()
+        _check(_lib.moe_host_exec_create(n_threads, HOST_PORTABLE if portable else 0, ctypes.byref(h)),
+               "moe_host_exec_create")
+        self.h = h
+        self.n_threads = n_threads
+
+    def simd(self):
+        return _lib.moe_host_exec_simd(self.h)
+
+    def forward(self, pool, wtype, H, I, x, ids, pick_slot, w, y_host=None):
+        """Host tensors: x uint16 [T, H] (BF16 bits), ids / pick_slot int32
+        [T, k], w float32 [T, k]; returns y_host float32 [T, H] (host)."""
+        T, k = ids.shape
+        for t in (x, ids, pick_slot, w):
+            assert not t.is_cuda and t.is_contiguous()
+        if y_host is None:
+            y_host = torch.empty((T, H), dtype=torch.float32)
+        _check(_lib.moe_host_forward(self.h, ctypes.byref(pool.c), wtype, H, I, _ptr(x), _ptr(ids), _ptr(pick_slot),
+                                     _ptr(w), T, k, _ptr(y_host)), "moe_host_forward")
+        return y_host
+
+    def enqueue(self, pool, wtype, H, I, x, ids, pick_slot, w, y_host, stream=None):
+        """Stream-ordered forward: host tensors (pinned where the GPU copies
+        into or reads them) that must stay alive until the stream passes."""
+        T, k = ids.shape
+        for t in (x, ids, pick_slot, w, y_host):
+            assert not t.is_cuda and t.is_contiguous()
+        self._keep = (pool, x, ids, pick_slot, w, y_host)
+        _check(_lib.moe_host_forward_enqueue(self.h, ctypes.byref(pool.c), wtype, H, I, _ptr(x), _ptr(ids),
+                                             _ptr(pick_slot), _ptr(w), T, k, _ptr(y_host), _stream(stream)),
+               "moe_host_forward_enqueue")
+
+    def status(self):
+        """First failure of an enqueued run since the last call (0 if none)."""
+        return _lib.moe_host_exec_status(self.h)
+
+    def destroy(self):
+        if self.h:
+            _check(_lib.moe_host_exec_destroy(self.h), "moe_host_exec_destroy")
             self.h = None

@@ -19,7 +19,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_gfx950.so")
-SOURCES = ["route_topk.hip", "cache.hip", "forward.hip"]
+SOURCES = ["route_topk.hip", "cache.hip", "forward.hip", "host_exec.cpp"]
+GPU_SOURCES = [s for s in SOURCES if s.endswith(".hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950",
@@ -29,9 +30,15 @@ FLAGS = [
 ]
 
 
+HOST_FLAGS = ["-O3", "-std=c++17", "-fPIC", "-x", "c++", "-I" + os.path.join(os.path.dirname(os.path.dirname(HIPCC)), "include"),
+              "-D__HIP_PLATFORM_AMD__", "-Wall", "-Wno-unused-function", "-Wno-unused-variable"]
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    # host-only C++ (the CPU executor) is compiled as plain C++ against the HIP runtime headers
+    flags = FLAGS if src.endswith(".hip") else HOST_FLAGS
+    cmd = [HIPCC, *flags, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("compile failed: %s\n%s\n%s" % (" ".join(cmd), r.stdout, r.stderr))
@@ -44,7 +51,7 @@ def build(verbose=True):
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
         results = list(ex.map(_compile, SOURCES))
-        list(ex.map(lambda s: asm_check.check_sources(CSRC, [s], HIPCC, FLAGS), SOURCES))
+        list(ex.map(lambda s: asm_check.check_sources(CSRC, [s], HIPCC, FLAGS), GPU_SOURCES))
     for obj, warn in results:
         if warn.strip() and verbose:
             print(warn, file=sys.stderr)

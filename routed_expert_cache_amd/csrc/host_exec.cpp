@@ -1,0 +1,454 @@
+// Host executor for the host set C: the experts a cache step leaves to the
+// CPU are evaluated here, on a persistent pool of threads, from the same
+// packed rows of the pinned host pool that fills copy to the GPU.
+//
+// [FT] section "q* 策略": the misses not filled are computed by the CPU in
+// parallel with the GPU and the two partial sums are added.  [OSDI] section
+// 4.2: FP8 weights stay as stored; the CPU expands the codes with bit
+// operations, dots each 128-wide block first and multiplies it by its scale
+// once (post-scaling).  [OSDI] section 4.3: an expert is gate, up and down
+// projections, down reads SiLU(gate) * up.
+//
+// Packed rows (the brick format of the GPU slots): a matrix W [N][K] is a run
+// of 1 KB bricks of 16 rows x KB columns (KB = 32 BF16 or 64 E4M3), brick
+// (t, kt) at (t * (K / KB) + kt) KB; the 16-byte chunk c = 16 j + r of a
+// brick holds W[16 t + r][KB kt + (KB / 4) j + e].  Gate/up rows interleave:
+// packed row 16 t + r is gate row 8 t + r (r < 8) or up row 8 t + r - 8.
+//
+// Work of one call, in two passes over the thread pool: (1) every (host
+// expert, brick row) pair -> 8 features of h for every token that picked
+// the expert, in FP32; (2) every 16-row block of y_host -> for each token,
+// the gate-weighted down products of its host experts summed in pick order.
+// Each output is summed by one thread in a fixed order: the same bits on
+// every call, with any number of threads.
+#include "../../include/moe.h"
+
+#include <hip/hip_runtime_api.h>
+#include <immintrin.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <condition_variable>
+#include <cstdint>
+#include <cstring>
+#include <functional>
+#include <mutex>
+#include <new>
+#include <thread>
+#include <vector>
+
+namespace moe {
+void set_error(const char* fmt, ...);   // the library's per-thread error message
+void clear_error();
+}  // namespace moe
+
+#define HX_FAIL(code, ...)         \
+  do {                             \
+    ::moe::set_error(__VA_ARGS__); \
+    return code;                   \
+  } while (0)
+
+namespace {
+
+// ------------------------------------------------------------ E4M3 decoding
+// E4M3FN: sign, 4 exponent bits (bias 7), 3 mantissa bits; exponent 0 is
+// subnormal (m * 2^-9); 0x7F / 0xFF are NaN; there are no infinities.
+inline float e4m3_to_f32(uint8_t c) {
+  const uint32_t s = (uint32_t)(c >> 7) << 31, e = (c >> 3) & 15u, m = c & 7u;
+  float v;
+  if ((c & 0x7Fu) == 0x7Fu) {
+    uint32_t nan = s | 0x7FC00000u;
+    std::memcpy(&v, &nan, 4);
+    return v;
+  }
+  if (e == 0) {
+    v = (float)m * (1.0f / 512.0f);
+    return s ? -v : v;
+  }
+  const uint32_t bits = s | ((e + 120u) << 23) | (m << 20);
+  std::memcpy(&v, &bits, 4);
+  return v;
+}
+
+inline float bf16_to_f32(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return f;
+}
+
+inline float silu(float a) { return a / (1.0f + std::exp(-a)); }
+
+// ------------------------------------------------------------ brick-row dot
+// acc[r] (16 rows) += sum over the brick row's K of W[r][k] * v[k], for one
+// vector v (FP32, length K).  FP8: each 128-wide K block is dotted on its
+// own and multiplied by sc(row half, block) before it is added.
+struct RowScale {               // FP8 scale of a 16-row brick row at K block b
+  const float* lo;              // rows 0..7: lo[b]
+  const float* hi;              // rows 8..15: hi[b]
+};
+
+void dot_rows_bf16_scalar(const uint16_t* brow, int nkt, const float* v, float* acc) {
+  for (int kt = 0; kt < nkt; ++kt) {
+    const uint16_t* b = brow + (size_t)kt * 512;
+    for (int j = 0; j < 4; ++j)
+      for (int r = 0; r < 16; ++r) {
+        const uint16_t* w = b + (16 * j + r) * 8;
+        const float* x = v + 32 * kt + 8 * j;
+        float s = 0.f;
+        for (int e = 0; e < 8; ++e) s += bf16_to_f32(w[e]) * x[e];
+        acc[r] += s;
+      }
+  }
+}
+
+void dot_rows_fp8_scalar(const uint8_t* brow, int nkt, const float* v, RowScale sc, float* acc) {
+  float blk[16];
+  for (int kt = 0; kt < nkt; ++kt) {
+    if ((kt & 1) == 0) std::fill(blk, blk + 16, 0.f);
+    const uint8_t* b = brow + (size_t)kt * 1024;
+    for (int j = 0; j < 4; ++j)
+      for (int r = 0; r < 16; ++r) {
+        const uint8_t* w = b + (16 * j + r) * 16;
+        const float* x = v + 64 * kt + 16 * j;
+        float s = 0.f;
+        for (int e = 0; e < 16; ++e) s += e4m3_to_f32(w[e]) * x[e];
+        blk[r] += s;
+      }
+    if ((kt & 1) == 1 || kt == nkt - 1) {
+      const int bk = kt >> 1;
+      for (int r = 0; r < 16; ++r) acc[r] += (r < 8 ? sc.lo[bk] : sc.hi[bk]) * blk[r];
+    }
+  }
+}
+
+__attribute__((target("avx512f,avx512bw"))) inline __m512 bf16x16_to_f32(__m256i h) {
+  return _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(h), 16));
+}
+
+// 16 E4M3 codes -> 16 floats, by the same rule as e4m3_to_f32
+__attribute__((target("avx512f,avx512bw"))) inline __m512 e4m3x16_to_f32(__m128i c8) {
+  const __m512i c = _mm512_cvtepu8_epi32(c8);
+  const __m512i s = _mm512_slli_epi32(_mm512_srli_epi32(c, 7), 31);
+  const __m512i e = _mm512_and_si512(_mm512_srli_epi32(c, 3), _mm512_set1_epi32(15));
+  const __m512i m = _mm512_and_si512(c, _mm512_set1_epi32(7));
+  const __m512i normal = _mm512_or_si512(
+      s, _mm512_or_si512(_mm512_slli_epi32(_mm512_add_epi32(e, _mm512_set1_epi32(120)), 23), _mm512_slli_epi32(m, 20)));
+  const __m512 sub_mag = _mm512_mul_ps(_mm512_cvtepi32_ps(m), _mm512_set1_ps(1.0f / 512.0f));
+  const __m512i sub = _mm512_or_si512(_mm512_castps_si512(sub_mag), s);
+  const __mmask16 is_sub = _mm512_cmpeq_epi32_mask(e, _mm512_setzero_si512());
+  __m512i r = _mm512_mask_blend_epi32(is_sub, normal, sub);
+  const __mmask16 is_nan =
+      _mm512_cmpeq_epi32_mask(_mm512_and_si512(c, _mm512_set1_epi32(0x7F)), _mm512_set1_epi32(0x7F));
+  r = _mm512_mask_blend_epi32(is_nan, r, _mm512_or_si512(s, _mm512_set1_epi32(0x7FC00000)));
+  return _mm512_castsi512_ps(r);
+}
+
+// Lane layout of the AVX-512 accumulators: a[q] holds rows 2q, 2q + 1, one
+// 8-wide K chunk each (BF16), or rows q (FP8: 16-wide chunk); the horizontal
+// sums at the end give the row sums.
+__attribute__((target("avx512f,avx512bw"))) void dot_rows_bf16_avx512(const uint16_t* brow, int nkt, const float* v,
+                                                                       float* acc) {
+  __m512 a[8];
+  for (int q = 0; q < 8; ++q) a[q] = _mm512_setzero_ps();
+  for (int kt = 0; kt < nkt; ++kt) {
+    const uint16_t* b = brow + (size_t)kt * 512;
+    for (int j = 0; j < 4; ++j) {
+      const __m256 x8 = _mm256_loadu_ps(v + 32 * kt + 8 * j);
+      const __m512 x16 = _mm512_castpd_ps(
+          _mm512_insertf64x4(_mm512_castps_pd(_mm512_castps256_ps512(x8)), _mm256_castps_pd(x8), 1));
+      const uint16_t* w = b + 16 * j * 8;   // rows 0..15, 8 values each: 256 bytes
+      for (int q = 0; q < 8; ++q) {
+        const __m512 wf = bf16x16_to_f32(_mm256_loadu_si256((const __m256i*)(w + 16 * q)));
+        a[q] = _mm512_fmadd_ps(wf, x16, a[q]);
+      }
+    }
+  }
+  for (int q = 0; q < 8; ++q) {
+    const __m256 lo = _mm512_castps512_ps256(a[q]);
+    const __m256 hi = _mm256_castpd_ps(_mm512_extractf64x4_pd(_mm512_castps_pd(a[q]), 1));
+    float t0[8], t1[8];
+    _mm256_storeu_ps(t0, lo);
+    _mm256_storeu_ps(t1, hi);
+    float s0 = 0.f, s1 = 0.f;
+    for (int e = 0; e < 8; ++e) {
+      s0 += t0[e];
+      s1 += t1[e];
+    }
+    acc[2 * q] += s0;
+    acc[2 * q + 1] += s1;
+  }
+}
+
+__attribute__((target("avx512f,avx512bw"))) void dot_rows_fp8_avx512(const uint8_t* brow, int nkt, const float* v,
+                                                                      RowScale sc, float* acc) {
+  __m512 t[16], blk[16];
+  for (int r = 0; r < 16; ++r) t[r] = _mm512_setzero_ps();
+  for (int kt = 0; kt < nkt; ++kt) {
+    if ((kt & 1) == 0)
+      for (int r = 0; r < 16; ++r) blk[r] = _mm512_setzero_ps();
+    const uint8_t* b = brow + (size_t)kt * 1024;
+    for (int j = 0; j < 4; ++j) {
+      const __m512 x = _mm512_loadu_ps(v + 64 * kt + 16 * j);
+      for (int r = 0; r < 16; ++r) {
+        const __m512 wf = e4m3x16_to_f32(_mm_loadu_si128((const __m128i*)(b + (16 * j + r) * 16)));
+        blk[r] = _mm512_fmadd_ps(wf, x, blk[r]);
+      }
+    }
+    if ((kt & 1) == 1 || kt == nkt - 1) {
+      const int bk = kt >> 1;
+      const __m512 slo = _mm512_set1_ps(sc.lo[bk]), shi = _mm512_set1_ps(sc.hi[bk]);
+      for (int r = 0; r < 16; ++r) t[r] = _mm512_fmadd_ps(r < 8 ? slo : shi, blk[r], t[r]);
+    }
+  }
+  for (int r = 0; r < 16; ++r) acc[r] += _mm512_reduce_add_ps(t[r]);
+}
+
+bool have_avx512() {
+  static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
+  return ok;
+}
+
+// ------------------------------------------------------------ thread pool
+// run(n_items, f): f(item) for every item in [0, n_items), spread over the
+// pool threads and the caller; returns when all are done.
+class Pool {
+ public:
+  explicit Pool(int n) : n_(n) {
+    for (int i = 1; i < n_; ++i) th_.emplace_back([this] { loop(); });
+  }
+  ~Pool() {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      stop_ = true;
+      ++gen_;
+    }
+    cv_.notify_all();
+    for (auto& t : th_) t.join();
+  }
+  int size() const { return n_; }
+  void run(int n_items, const std::function<void(int)>& f) {
+    {
+      std::lock_guard<std::mutex> lk(mu_);
+      f_ = &f;
+      n_items_ = n_items;
+      next_.store(0);
+      busy_ = (int)th_.size();
+      ++gen_;
+    }
+    cv_.notify_all();
+    work();
+    std::unique_lock<std::mutex> lk(mu_);
+    done_cv_.wait(lk, [this] { return busy_ == 0; });
+    f_ = nullptr;
+  }
+
+ private:
+  void work() {
+    for (;;) {
+      const int i = next_.fetch_add(1);
+      if (i >= n_items_) break;
+      (*f_)(i);
+    }
+  }
+  void loop() {
+    uint64_t seen = 0;
+    for (;;) {
+      {
+        std::unique_lock<std::mutex> lk(mu_);
+        cv_.wait(lk, [&] { return gen_ != seen; });
+        seen = gen_;
+        if (stop_) return;
+      }
+      work();
+      {
+        std::lock_guard<std::mutex> lk(mu_);
+        if (--busy_ == 0) done_cv_.notify_one();
+      }
+    }
+  }
+  int n_;
+  std::vector<std::thread> th_;
+  std::mutex mu_;
+  std::condition_variable cv_, done_cv_;
+  uint64_t gen_ = 0;
+  bool stop_ = false;
+  int busy_ = 0;
+  int n_items_ = 0;
+  std::atomic<int> next_{0};
+  const std::function<void(int)>* f_ = nullptr;
+};
+
+}  // namespace
+
+struct HostCall {             // the arguments of one moe_host_forward
+  moe_host_pool pool;
+  int32_t wtype, H, I;
+  const uint16_t* x;
+  const int32_t* ids;
+  const int32_t* pick_slot;
+  const float* w;
+  int32_t T, k;
+  float* y_host;
+};
+
+struct moe_host_exec {
+  Pool pool;
+  bool simd;                   // the AVX-512 path
+  std::mutex call_mu;          // one call at a time per executor
+  std::vector<float> xs;       // [T][H] x in FP32
+  std::vector<float> hbuf;     // [n_pairs][I] h in FP32
+  HostCall queued{};           // the call an enqueued host function runs (persistent: graphs replay it)
+  std::atomic<int32_t> status{MOE_OK};   // first failure of an enqueued run
+  moe_host_exec(int n, bool s) : pool(n), simd(s) {}
+};
+
+extern "C" moe_status moe_host_exec_create(int32_t n_threads, uint32_t flags, moe_host_exec_t* out) {
+  ::moe::clear_error();
+  if (!out) HX_FAIL(MOE_ERR_ARG, "out is NULL");
+  *out = nullptr;
+  if (n_threads < 1 || n_threads > 1024) HX_FAIL(MOE_ERR_ARG, "n_threads %d not in [1, 1024]", n_threads);
+  if (flags & ~MOE_HOST_PORTABLE) HX_FAIL(MOE_ERR_ARG, "bad flags %u", flags);
+  moe_host_exec* h = new (std::nothrow) moe_host_exec(n_threads, have_avx512() && !(flags & MOE_HOST_PORTABLE));
+  if (!h) HX_FAIL(MOE_ERR_NO_SPACE, "out of host memory");
+  *out = h;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_host_exec_destroy(moe_host_exec_t h) {
+  ::moe::clear_error();
+  delete h;
+  return MOE_OK;
+}
+
+extern "C" int32_t moe_host_exec_simd(moe_host_exec_t h) { return h && h->simd ? 512 : 0; }
+
+extern "C" moe_status moe_host_forward(moe_host_exec_t h, const moe_host_pool* pool, int32_t wtype, int32_t H,
+                                       int32_t I, const uint16_t* x, const int32_t* ids, const int32_t* pick_slot,
+                                       const float* w, int32_t T, int32_t k, float* y_host) {
+  ::moe::clear_error();
+  if (!h || !pool || !y_host) HX_FAIL(MOE_ERR_ARG, "null executor, pool or y_host");
+  if (T < 0 || k < 1) HX_FAIL(MOE_ERR_SHAPE, "bad T=%d k=%d", T, k);
+  if (wtype != MOE_W_BF16 && wtype != MOE_W_FP8_B128) HX_FAIL(MOE_ERR_ARG, "bad wtype %d", wtype);
+  const bool fp8 = wtype == MOE_W_FP8_B128;
+  const int KB = fp8 ? 64 : 32;
+  if (H <= 0 || I <= 0 || H % KB || I % KB || I % 8 || (fp8 && (H % 128 || I % 128)))
+    HX_FAIL(MOE_ERR_SHAPE, "host executor needs H, I multiples of %d and I %% 8 == 0 (H=%d I=%d)", fp8 ? 128 : 32, H, I);
+  if (T == 0) return MOE_OK;
+  if (!x || !ids || !pick_slot || !w || !pool->w_gate_up || !pool->w_down) HX_FAIL(MOE_ERR_ARG, "null argument");
+  if (fp8 && (!pool->s_gate || !pool->s_up || !pool->s_down)) HX_FAIL(MOE_ERR_ARG, "FP8 pool without scales");
+  std::lock_guard<std::mutex> lk(h->call_mu);
+
+  // the host picks, token-major in pick order: pair p = (token, pick)
+  std::vector<int> pt, pj;
+  for (int t = 0; t < T; ++t)
+    for (int j = 0; j < k; ++j)
+      if (pick_slot[t * k + j] < 0) {
+        if (ids[t * k + j] < 0) HX_FAIL(MOE_ERR_ARG, "host pick (%d, %d) has id %d", t, j, ids[t * k + j]);
+        pt.push_back(t);
+        pj.push_back(j);
+      }
+  std::memset(y_host, 0, sizeof(float) * (size_t)T * H);
+  const int n_pairs = (int)pt.size();
+  if (n_pairs == 0) return MOE_OK;
+
+  h->xs.resize((size_t)T * H);
+  for (size_t i = 0; i < (size_t)T * H; ++i) h->xs[i] = bf16_to_f32(x[i]);
+  h->hbuf.resize((size_t)n_pairs * I);
+  const bool simd = h->simd;
+  const int nkt_gu = H / KB, nkt_dn = I / KB;
+  const size_t brick_row_gu = (size_t)nkt_gu * 1024, brick_row_dn = (size_t)nkt_dn * 1024;
+
+  // (1) gate/up: item = (pair, brick row t of I/8): gate/up rows 8t..8t+7
+  const int RA = I / 8;
+  h->pool.run(n_pairs * RA, [&](int item) {
+    const int p = item / RA, t = item - p * RA;
+    const int id = ids[pt[p] * k + pj[p]];
+    const char* brow = (const char*)pool->w_gate_up[id] + (size_t)t * brick_row_gu;
+    const float* v = h->xs.data() + (size_t)pt[p] * H;
+    float acc[16] = {0};
+    if (fp8) {
+      const int nbk = H / 128, rb = (8 * t) / 128;
+      const RowScale sc{pool->s_gate[id] + (size_t)rb * nbk, pool->s_up[id] + (size_t)rb * nbk};
+      if (simd)
+        dot_rows_fp8_avx512((const uint8_t*)brow, nkt_gu, v, sc, acc);
+      else
+        dot_rows_fp8_scalar((const uint8_t*)brow, nkt_gu, v, sc, acc);
+    } else {
+      if (simd)
+        dot_rows_bf16_avx512((const uint16_t*)brow, nkt_gu, v, acc);
+      else
+        dot_rows_bf16_scalar((const uint16_t*)brow, nkt_gu, v, acc);
+    }
+    float* hp = h->hbuf.data() + (size_t)p * I + 8 * t;
+    for (int r = 0; r < 8; ++r) hp[r] = silu(acc[r]) * acc[8 + r];
+  });
+
+  // (2) down: item = 16-row block of y_host; for each token, its host pairs in pick order
+  h->pool.run(H / 16, [&](int blk) {
+    float acc[16];
+    for (int p0 = 0; p0 < n_pairs;) {
+      const int t = pt[p0];
+      int p1 = p0;
+      while (p1 < n_pairs && pt[p1] == t) ++p1;
+      float yt[16] = {0};
+      for (int p = p0; p < p1; ++p) {
+        const int id = ids[t * k + pj[p]];
+        const char* brow = (const char*)pool->w_down[id] + (size_t)blk * brick_row_dn;
+        const float* v = h->hbuf.data() + (size_t)p * I;
+        std::fill(acc, acc + 16, 0.f);
+        if (fp8) {
+          const int nbk = I / 128;
+          const float* s = pool->s_down[id] + (size_t)((16 * blk) / 128) * nbk;
+          const RowScale sc{s, s};
+          if (simd)
+            dot_rows_fp8_avx512((const uint8_t*)brow, nkt_dn, v, sc, acc);
+          else
+            dot_rows_fp8_scalar((const uint8_t*)brow, nkt_dn, v, sc, acc);
+        } else {
+          if (simd)
+            dot_rows_bf16_avx512((const uint16_t*)brow, nkt_dn, v, acc);
+          else
+            dot_rows_bf16_scalar((const uint16_t*)brow, nkt_dn, v, acc);
+        }
+        const float wp = w[t * k + pj[p]];
+        for (int r = 0; r < 16; ++r) yt[r] += wp * acc[r];
+      }
+      std::memcpy(y_host + (size_t)t * H + 16 * blk, yt, sizeof(yt));
+      p0 = p1;
+    }
+  });
+  return MOE_OK;
+}
+
+// ------------------------------------------------------------ stream-ordered form
+namespace {
+void host_call_fn(void* p) {
+  moe_host_exec* h = static_cast<moe_host_exec*>(p);
+  const HostCall& c = h->queued;
+  const moe_status st = moe_host_forward(h, &c.pool, c.wtype, c.H, c.I, c.x, c.ids, c.pick_slot, c.w, c.T, c.k,
+                                         c.y_host);
+  if (st != MOE_OK) {
+    int32_t ok = MOE_OK;
+    h->status.compare_exchange_strong(ok, st);
+  }
+}
+}  // namespace
+
+extern "C" moe_status moe_host_forward_enqueue(moe_host_exec_t h, const moe_host_pool* pool, int32_t wtype, int32_t H,
+                                               int32_t I, const uint16_t* x, const int32_t* ids,
+                                               const int32_t* pick_slot, const float* w, int32_t T, int32_t k,
+                                               float* y_host, hipStream_t stream) {
+  ::moe::clear_error();
+  if (!h || !pool) HX_FAIL(MOE_ERR_ARG, "null executor or pool");
+  h->queued = HostCall{*pool, wtype, H, I, x, ids, pick_slot, w, T, k, y_host};
+  const hipError_t e = hipLaunchHostFunc(stream, host_call_fn, h);
+  if (e != hipSuccess) HX_FAIL(MOE_ERR_HIP, "hipLaunchHostFunc failed: %s", hipGetErrorString(e));
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_host_exec_status(moe_host_exec_t h) {
+  if (!h) return MOE_ERR_ARG;
+  return (moe_status)h->status.exchange(MOE_OK);
+}

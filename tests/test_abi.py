@@ -17,7 +17,7 @@ LIB = os.path.join(ROOT, "routed_expert_cache_amd", "libmoe_gfx950.so")
 def declared_functions():
     src = open(HEADER).read()
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
-    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*)\s+(moe_\w+)\s*\(", src, flags=re.M)))
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char\*|int32_t)\s+(moe_\w+)\s*\(", src, flags=re.M)))
 
 
 def test_header_is_valid_c():

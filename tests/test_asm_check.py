@@ -108,7 +108,7 @@ def test_compiler_reads_are_not_tracked():
 
 
 @pytest.mark.skipif(not os.path.exists(B.HIPCC) and shutil.which("hipcc") is None, reason="hipcc not installed")
-@pytest.mark.parametrize("src", B.SOURCES)
+@pytest.mark.parametrize("src", B.GPU_SOURCES)
 def test_library_kernels_are_clean(src):
     text = asm_check.device_asm(os.path.join(B.CSRC, src), B.HIPCC, B.FLAGS)
     assert ".amdhsa_kernel" in text
