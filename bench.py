@@ -180,6 +180,7 @@ def parse():
                    help="also time the oracle on ROWS tokens of the prefill BF16 chunk (about 40 s of host "
                         "work for weight generation and decoding besides the timed FFN)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-host-exec", action="store_true", help="skip the host executor (CPU) throughput run")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 decode and FP8 double-buffered prefill runs")
     p.add_argument("--fp8-steps", type=int, default=64)
@@ -704,6 +705,72 @@ def cpu_baseline(budget_s):
                        % (done, el, len(os.sched_getaffinity(0))))
 
 
+def run_host_exec(b, fill_GBps=None, seconds=3.0):
+    """Throughput of the host executor (moe_host_forward) on this machine's cores:
+    the B_H of the q* split.  Each call evaluates k = 8 host picks of one token,
+    each a different expert, cycling through a pinned pool larger than the CPU
+    caches, so the weights stream from host DRAM as the host set's do.  The
+    weights are random values in the packed layout (the rate does not depend
+    on them); parity is covered by the tests."""
+    import torch
+    threads = len(os.sched_getaffinity(0))
+    ex = b.HostExec(threads)
+    out = dict(threads=threads, simd=ex.simd(), picks_per_call=8)
+    for name, wtype, H, I, n_pool in (("decode_bf16", b.W_BF16, 2048, 768, 64),
+                                      ("decode_fp8", b.W_FP8_B128, 7168, 2048, 24)):
+        el = 2 if wtype == b.W_BF16 else 1
+        if wtype == b.W_BF16:
+            gu = (torch.randn((n_pool, 2 * I * H)) * 0.02).to(torch.bfloat16).view(torch.uint16).pin_memory()
+            dp = (torch.randn((n_pool, H * I)) * 0.02).to(torch.bfloat16).view(torch.uint16).pin_memory()
+            banks = [gu, dp]
+        else:
+            gu = torch.randint(0, 0x7F, (n_pool, 2 * I * H), dtype=torch.uint8).pin_memory()   # no NaN codes
+            dp = torch.randint(0, 0x7F, (n_pool, H * I), dtype=torch.uint8).pin_memory()
+            sg = (torch.rand((n_pool, I // 128, H // 128)) * 1e-3).pin_memory()
+            su = (torch.rand((n_pool, I // 128, H // 128)) * 1e-3).pin_memory()
+            sd = (torch.rand((n_pool, H // 128, I // 128)) * 1e-3).pin_memory()
+            banks = [gu, dp, sg, su, sd]
+        pool = b.HostPoolTables(banks, lambda i: i, n_pool)
+        expert_bytes = 3 * H * I * el + (3 * (I // 128) * (H // 128) * 4 if wtype != b.W_BF16 else 0)
+        x = (torch.randn((1, H))).to(torch.bfloat16).view(torch.uint16)
+        w = torch.full((1, 8), 0.125, dtype=torch.float32)
+        pick = torch.full((1, 8), -1, dtype=torch.int32)
+        y = torch.empty((1, H), dtype=torch.float32)
+        call = 0
+
+        def one(ids):
+            ex.forward(pool, wtype, H, I, x, ids, pick, w, y)
+
+        def ids_of(c):
+            return torch.tensor([[(8 * c + j) % n_pool for j in range(8)]], dtype=torch.int32)
+
+        for c in range(3):
+            one(ids_of(c))
+        t0 = time.perf_counter()
+        n = 0
+        while time.perf_counter() - t0 < seconds:
+            one(ids_of(call))
+            call += 1
+            n += 1
+        dt = time.perf_counter() - t0
+        one1 = torch.tensor([[call % n_pool] + [0] * 7], dtype=torch.int32)
+        pick1 = torch.tensor([[-1] + [5] * 7], dtype=torch.int32)
+        t1 = time.perf_counter()
+        for r in range(10):
+            one1[0, 0] = (call + 8 * r) % n_pool
+            ex.forward(pool, wtype, H, I, x, one1, pick1, w, y)
+        lat = (time.perf_counter() - t1) / 10
+        out[name] = dict(expert_bytes=expert_bytes, calls=n, GBps=8 * n * expert_bytes / dt / 1e9,
+                         ms_per_call_8_experts=dt / n * 1e3, ms_one_expert=lat * 1e3,
+                         pool_GB=n_pool * expert_bytes / 1e9)
+        del banks, pool, gu, dp
+    ex.destroy()
+    if fill_GBps:
+        out["fill_GBps"] = fill_GBps
+        out["B_P_over_B_H_measured"] = {k: fill_GBps / out[k]["GBps"] for k in ("decode_bf16", "decode_fp8")}
+    return out
+
+
 def main():
     a = parse()
     if a.pmc_summary:
@@ -741,6 +808,9 @@ def main():
         if not a.no_prefill and not a.no_prefill_fp8:
             line["prefill_fp8"] = run_prefill_fp8(b)
             torch.cuda.empty_cache()
+    if not a.no_host_exec:
+        log("host executor: expert GB/s on %d cores" % len(os.sched_getaffinity(0)))
+        line["host_exec"] = run_host_exec(b, dec["detail"].get("fill_GBps"))
     if not a.no_cpu_baseline:
         log("cpu baseline: oracle for %.0f s" % a.cpu_seconds)
         line["cpu_baseline"] = cpu_baseline(a.cpu_seconds)

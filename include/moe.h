@@ -375,7 +375,7 @@ moe_status moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStr
  *
  * moe_host_exec_create starts n_threads - 1 worker threads (the calling
  * thread is the n-th); they sleep between calls.  The executor uses AVX-512
- * where the CPU has it (AVX512F + AVX512BW), else portable C++; flags
+ * where the CPU has it (AVX512F, BW and VL), else portable C++; flags
  * MOE_HOST_PORTABLE selects the portable path everywhere.  Both sum in the
  * same order within a 16-row brick row but group the additions differently,
  * so their results agree to FP32 rounding, not bitwise.

@@ -127,22 +127,19 @@ __attribute__((target("avx512f,avx512bw"))) inline __m512 bf16x16_to_f32(__m256i
   return _mm512_castsi512_ps(_mm512_slli_epi32(_mm512_cvtepu16_epi32(h), 16));
 }
 
-// 16 E4M3 codes -> 16 floats, by the same rule as e4m3_to_f32
-__attribute__((target("avx512f,avx512bw"))) inline __m512 e4m3x16_to_f32(__m128i c8) {
-  const __m512i c = _mm512_cvtepu8_epi32(c8);
-  const __m512i s = _mm512_slli_epi32(_mm512_srli_epi32(c, 7), 31);
-  const __m512i e = _mm512_and_si512(_mm512_srli_epi32(c, 3), _mm512_set1_epi32(15));
-  const __m512i m = _mm512_and_si512(c, _mm512_set1_epi32(7));
-  const __m512i normal = _mm512_or_si512(
-      s, _mm512_or_si512(_mm512_slli_epi32(_mm512_add_epi32(e, _mm512_set1_epi32(120)), 23), _mm512_slli_epi32(m, 20)));
-  const __m512 sub_mag = _mm512_mul_ps(_mm512_cvtepi32_ps(m), _mm512_set1_ps(1.0f / 512.0f));
-  const __m512i sub = _mm512_or_si512(_mm512_castps_si512(sub_mag), s);
-  const __mmask16 is_sub = _mm512_cmpeq_epi32_mask(e, _mm512_setzero_si512());
-  __m512i r = _mm512_mask_blend_epi32(is_sub, normal, sub);
-  const __mmask16 is_nan =
-      _mm512_cmpeq_epi32_mask(_mm512_and_si512(c, _mm512_set1_epi32(0x7F)), _mm512_set1_epi32(0x7F));
-  r = _mm512_mask_blend_epi32(is_nan, r, _mm512_or_si512(s, _mm512_set1_epi32(0x7FC00000)));
-  return _mm512_castsi512_ps(r);
+// 16 E4M3 codes -> 16 floats equal to 2^-8 times their values.  With its
+// 7 magnitude bits shifted up by 7, an E4M3 code is the FP16 pattern of
+// value * 2^-8 (exponent bias 15 = 7 + 8; E4M3 subnormals land on FP16
+// subnormals with the same mantissa), so one FP16 -> FP32 conversion expands
+// 16 codes exactly; the callers fold the 2^8 into the block scale.  The NaN
+// codes (0x7F, 0xFF) are patched to NaN.
+__attribute__((target("avx512f,avx512bw,avx512vl"))) inline __m512 e4m3x16_to_f32_div256(__m128i c8) {
+  const __m256i c = _mm256_cvtepu8_epi16(c8);
+  const __m256i mag = _mm256_and_si256(c, _mm256_set1_epi16(0x7F));
+  const __m256i sign = _mm256_slli_epi16(_mm256_and_si256(c, _mm256_set1_epi16(0x80)), 8);
+  const __m256i h = _mm256_or_si256(sign, _mm256_slli_epi16(mag, 7));
+  const __mmask16 nan = _mm256_cmpeq_epi16_mask(mag, _mm256_set1_epi16(0x7F));
+  return _mm512_mask_blend_ps(nan, _mm512_cvtph_ps(h), _mm512_set1_ps(__builtin_nanf("")));
 }
 
 // Lane layout of the AVX-512 accumulators: a[q] holds rows 2q, 2q + 1, one
@@ -181,8 +178,8 @@ __attribute__((target("avx512f,avx512bw"))) void dot_rows_bf16_avx512(const uint
   }
 }
 
-__attribute__((target("avx512f,avx512bw"))) void dot_rows_fp8_avx512(const uint8_t* brow, int nkt, const float* v,
-                                                                      RowScale sc, float* acc) {
+__attribute__((target("avx512f,avx512bw,avx512vl"))) void dot_rows_fp8_avx512(const uint8_t* brow, int nkt,
+                                                                               const float* v, RowScale sc, float* acc) {
   __m512 t[16], blk[16];
   for (int r = 0; r < 16; ++r) t[r] = _mm512_setzero_ps();
   for (int kt = 0; kt < nkt; ++kt) {
@@ -192,13 +189,14 @@ __attribute__((target("avx512f,avx512bw"))) void dot_rows_fp8_avx512(const uint8
     for (int j = 0; j < 4; ++j) {
       const __m512 x = _mm512_loadu_ps(v + 64 * kt + 16 * j);
       for (int r = 0; r < 16; ++r) {
-        const __m512 wf = e4m3x16_to_f32(_mm_loadu_si128((const __m128i*)(b + (16 * j + r) * 16)));
+        const __m512 wf = e4m3x16_to_f32_div256(_mm_loadu_si128((const __m128i*)(b + (16 * j + r) * 16)));
         blk[r] = _mm512_fmadd_ps(wf, x, blk[r]);
       }
     }
     if ((kt & 1) == 1 || kt == nkt - 1) {
       const int bk = kt >> 1;
-      const __m512 slo = _mm512_set1_ps(sc.lo[bk]), shi = _mm512_set1_ps(sc.hi[bk]);
+      // the codes were expanded as 2^-8 times their values: scale by 2^8 too (exact)
+      const __m512 slo = _mm512_set1_ps(256.0f * sc.lo[bk]), shi = _mm512_set1_ps(256.0f * sc.hi[bk]);
       for (int r = 0; r < 16; ++r) t[r] = _mm512_fmadd_ps(r < 8 ? slo : shi, blk[r], t[r]);
     }
   }
@@ -206,7 +204,8 @@ __attribute__((target("avx512f,avx512bw"))) void dot_rows_fp8_avx512(const uint8
 }
 
 bool have_avx512() {
-  static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
+  static const bool ok = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+                         __builtin_cpu_supports("avx512vl");
   return ok;
 }
 

@@ -190,3 +190,25 @@ def test_no_host_pick_gives_zero_and_errors():
         ex.destroy()
     with pytest.raises(b.MoeError, match="MOE_ERR_ARG"):
         b.HostExec(0)
+
+
+@pytest.mark.parametrize("portable", [False, True])
+def test_fp8_nan_code_propagates(portable):
+    """E4M3FN has NaN codes (0x7F, 0xFF) and no infinities: one NaN weight of
+    an expert's gate matrix makes every output of the tokens that picked it
+    NaN, and no other output."""
+    b = binding()
+    bank = BankFP8(206, 3, 128, 128)
+    bank.t["gate"][1].view(-1)[5] = 0xFF              # repack with the NaN code
+    g, u, d = (bank.t[n].numpy() for n in ("gate", "up", "down"))
+    bank.banks[0] = torch.from_numpy(np.stack([pack_rows(gate_up_rows(g[e], u[e]), 64) for e in range(3)]))
+    x = gen.activations_bf16(np.random.default_rng(7), 3, 128)
+    ids = np.array([[1, 0], [2, 0], [0, 1]], np.int32)
+    w = np.full((3, 2), 0.5, np.float32)
+    pick = np.array([[-1, -1], [-1, -1], [-1, 5]], np.int32)   # token 2's pick of expert 1 is on the GPU
+    ex = b.HostExec(2, portable=portable)
+    try:
+        y = _run(b, ex, bank, x, ids, pick, w)
+    finally:
+        ex.destroy()
+    assert np.all(np.isnan(y[0])) and np.all(np.isfinite(y[1])) and np.all(np.isfinite(y[2]))
