@@ -243,7 +243,7 @@ def run_decode(b, K, W):
     pool = b.SlotPool(C, H, I, b.W_BF16)
     x = torch.from_numpy(gen.activations_bf16(gen.np_rng(c.cfg_id, gen.S_ACT), n * L, H)).cuda().view(n, L, 1, H)
     lg = torch.from_numpy(logits).cuda()                # [n, L, 1, E]
-    # host partial sums are inputs of the merge (the host branch is not on this path)
+    # host partial sums are inputs of the merge in passes 1-3; pass 4 computes them with the host executor
     yh = torch.randn((L, 1, H), dtype=torch.float32, device="cuda") * 0.01
     ids = torch.empty((1, k), dtype=torch.int32, device="cuda")
     w = torch.empty((1, k), dtype=torch.float32, device="cuda")
@@ -314,6 +314,59 @@ def run_decode(b, K, W):
     log("decode: pass 3 (no events, no PCIe fill copies)")
     wall_res, d3 = run_trace(None, fill=False)
     assert np.array_equal(d, d3), "the passes made different cache decisions"
+    # Pass 4: the path as the pages run it, with the host branch.  Per layer
+    # call: router + cache step; the logical ids, picks, gate weights and x
+    # copied to pinned host buffers, then a pinned `ready` word written in
+    # stream order; the host executor's dispatcher thread, waiting for that
+    # word, evaluates the host set (moe_host_forward_signal) while the stream
+    # runs the fill copies and the GPU evaluation of G; the merge waits for
+    # the executor's `done` word and adds its y_host.  Reported beside pass 2
+    # (the same path with the harness's y_host).
+    log("decode: pass 4 (with the host branch on the CPU)")
+    n_cores = len(os.sched_getaffinity(0))
+    ex = b.HostExec(max(1, n_cores - 1))    # one core left to the thread launching GPU work
+    ids_log = torch.empty((1, k), dtype=torch.int32, device="cuda")
+    h_ids = torch.empty((1, k), dtype=torch.int32).pin_memory()
+    h_pick = torch.empty((1, k), dtype=torch.int32).pin_memory()
+    h_w = torch.empty((1, k), dtype=torch.float32).pin_memory()
+    h_x = torch.empty((1, H), dtype=torch.uint16).pin_memory()
+    h_y = torch.empty((1, H), dtype=torch.float32).pin_memory()
+    ready = torch.zeros(1, dtype=torch.int32).pin_memory()
+    done = torch.zeros(1, dtype=torch.int32).pin_memory()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    y_gpu = torch.empty((1, H), dtype=torch.float32, device="cuda")
+    seq = [0]
+
+    def layer_step_host(cache, s, l):
+        seq[0] += 1
+        cache.route_step(l, lg[s, l], ids, w, out, copy=False)
+        torch.add(ids, l * E, out=ids_log)                           # logical ids index the host pool
+        for hd, dd in ((h_ids, ids_log), (h_pick, pick), (h_w, w), (h_x, x[s, l])):
+            hd.copy_(dd, non_blocking=True)
+        b.host_signal(ready, seq[0])
+        ex.forward_signal(host, b.W_BF16, H, I, h_x, h_ids, h_pick, h_w, h_y, ready, done, seq[0])
+        cache.fill(out)
+        b.expert_forward(pool.c, x[s, l], pick, w, b.FWD_DECODE, ws, y=y_gpu)
+        b.merge_partial_after(y_gpu, h_y, done, seq[0], y_out=y[l], err=err)
+
+    cache4 = b.Cache(L, E, k, 1, pool, host, c.bp, c.bh)
+    for s in range(W):
+        for l in range(L):
+            layer_step_host(cache4, s, l)
+    torch.cuda.synchronize()
+    c0 = cache4.read_state()[4].astype(np.int64)
+    t0 = time.perf_counter()
+    for s in range(W, W + K):
+        for l in range(L):
+            layer_step_host(cache4, s, l)
+    torch.cuda.synchronize()
+    wall_host = time.perf_counter() - t0
+    d4 = cache4.read_state()[4].astype(np.int64) - c0
+    cache4.destroy()
+    assert np.array_equal(d, d4), "the passes made different cache decisions"
+    assert ex.status() == 0 and int(err.item()) == 0, "the host branch failed"
+    host_calls, host_s = ex.stats()
+    ex.destroy()
     # Forward-only burst: the timed layer calls' forward launches again, back
     # to back with the same picks (the slots now hold other experts: the same
     # bytes), one event pair per step of 40 layers: the kernel's duration with
@@ -350,6 +403,13 @@ def run_decode(b, K, W):
             experts_on_gpu_per_layer_call=n_g / (K * L),
             fills_per_layer_call=float(d[4] / (K * L)),
             host_experts_per_layer_call=float(d[5] / (K * L)),
+            host_branch=dict(
+                wall_ms_per_step=wall_host / K * 1e3,
+                host_compute_us_per_call_with_host_picks=host_s / max(host_calls, 1) * 1e6,
+                calls_with_host_picks=host_calls,
+                note="pass 4: the full path with the host set evaluated by moe_host_forward on %d host threads, "
+                     "handed over through pinned words while the GPU fills and evaluates G, beside "
+                     "wall_ms_per_step_pcie_inclusive (pass 2: the harness's y_host)" % max(1, n_cores - 1)),
             layer_calls=int(d[0]),
             route_and_cache_step_us=step_s / (K * L) * 1e6,
         ),

@@ -374,7 +374,8 @@ moe_status moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStr
  * of the method, never a substitute for the GPU evaluation of G.
  *
  * moe_host_exec_create starts n_threads - 1 worker threads (the calling
- * thread is the n-th); they sleep between calls.  The executor uses AVX-512
+ * thread is the n-th); after a call they spin for a quarter of a
+ * millisecond, so calls one layer apart find them awake, then sleep.  The executor uses AVX-512
  * where the CPU has it (AVX512F, BW and VL), else portable C++; flags
  * MOE_HOST_PORTABLE selects the portable path everywhere.  Both sum in the
  * same order within a 16-row brick row but group the additions differently,
@@ -424,6 +425,43 @@ moe_status moe_host_forward_enqueue(moe_host_exec_t h, const moe_host_pool* pool
                                     int32_t I, const uint16_t* x, const int32_t* ids, const int32_t* pick_slot,
                                     const float* w, int32_t T, int32_t k, float* y_host, hipStream_t stream);
 moe_status moe_host_exec_status(moe_host_exec_t h);
+
+/*
+ * The host branch of a decode step without host callbacks: pinned words hand
+ * the step over between a GPU stream and the executor's dispatcher thread.
+ *   moe_host_signal: in stream order, store seq into *word (pinned host
+ *     memory) at system scope: put after the copies of the step's inputs.
+ *   moe_host_forward_signal: queue moe_host_forward on the executor's
+ *     dispatcher thread (started by the first call; calls run in order):
+ *     it waits until *ready - seq >= 0 (serial numbers modulo 2^32; at most
+ *     2 s, then the call is skipped and its failure kept for
+ *     moe_host_exec_status), runs the call, and stores seq into *done after
+ *     y_host.  Returns at once; the host arrays must stay valid until *done
+ *     reaches seq.  ready, done: pinned host words, zero before the first
+ *     seq (seq = 1, 2, ...).
+ *   moe_merge_partial_after: moe_merge_partial whose workgroups first wait
+ *     until *done - seq >= 0 (a bounded poll, seconds; on time-out
+ *     *err |= 1 and the merge goes on with whatever y_host holds).  y_host
+ *     is pinned host memory read after the wait; err: device or pinned word,
+ *     or NULL.
+ * Not capturable (the dispatcher is fed per call); moe_host_forward_enqueue
+ * is the capturable form.
+ */
+moe_status moe_host_signal(uint32_t* word, uint32_t seq, hipStream_t stream);
+moe_status moe_host_forward_signal(moe_host_exec_t h, const moe_host_pool* pool, int32_t wtype, int32_t H,
+                                   int32_t I, const uint16_t* x, const int32_t* ids, const int32_t* pick_slot,
+                                   const float* w, int32_t T, int32_t k, float* y_host, const uint32_t* ready,
+                                   uint32_t* done, uint32_t seq);
+moe_status moe_merge_partial_after(const float* y_gpu, const float* y_host, const uint32_t* done, uint32_t seq,
+                                   int32_t T, int32_t H, float* y_out, uint16_t* y_out_bf16, uint32_t* err,
+                                   hipStream_t stream);
+
+/*
+ * Measurement: the calls of moe_host_forward (direct or enqueued) that had
+ * host picks, and the wall time spent in them (ns), since the executor was
+ * created.
+ */
+moe_status moe_host_exec_stats(moe_host_exec_t h, uint64_t* calls, uint64_t* ns);
 
 #ifdef __cplusplus
 }

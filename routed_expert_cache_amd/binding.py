@@ -35,7 +35,8 @@ EXPORTS = [
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_e4m3_to_bf16", "moe_pack_weights", "moe_stream_read",
     "moe_host_exec_create", "moe_host_exec_destroy", "moe_host_exec_simd", "moe_host_forward",
-    "moe_host_forward_enqueue", "moe_host_exec_status",
+    "moe_host_forward_enqueue", "moe_host_exec_status", "moe_host_exec_stats",
+    "moe_host_signal", "moe_host_forward_signal", "moe_merge_partial_after",
 ]
 
 
@@ -103,6 +104,11 @@ _sig = {
     "moe_host_forward_enqueue": (_i32, [_vp, _P(HostPool), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                                         _vp]),
     "moe_host_exec_status": (_i32, [_vp]),
+    "moe_host_exec_stats": (_i32, [_vp, _P(ctypes.c_uint64), _P(ctypes.c_uint64)]),
+    "moe_host_signal": (_i32, [_vp, _u32, _vp]),
+    "moe_host_forward_signal": (_i32, [_vp, _P(HostPool), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
+                                       _vp, _vp, _u32]),
+    "moe_merge_partial_after": (_i32, [_vp, _vp, _vp, _u32, _i32, _i32, _vp, _vp, _vp, _vp]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -311,6 +317,21 @@ def merge_partial(y_gpu, y_host, y_out=None, y_out_bf16=None, stream=None):
     return y_out
 
 
+def host_signal(word, seq, stream=None):
+    """In stream order, store seq into the pinned uint32 word."""
+    _check(_lib.moe_host_signal(_ptr(word), seq & 0xFFFFFFFF, _stream(stream)), "moe_host_signal")
+
+
+def merge_partial_after(y_gpu, y_host, done, seq, y_out=None, y_out_bf16=None, err=None, stream=None):
+    """moe_merge_partial after waiting (bounded) for done >= seq."""
+    T, H = y_gpu.shape
+    if y_out is None:
+        y_out = torch.empty_like(y_gpu)
+    _check(_lib.moe_merge_partial_after(_ptr(y_gpu), _ptr(y_host), _ptr(done), seq & 0xFFFFFFFF, T, H, _ptr(y_out),
+                                        _ptr(y_out_bf16), _ptr(err), _stream(stream)), "moe_merge_partial_after")
+    return y_out
+
+
 def stream_read(src, sink, stream=None):
     """One launch that only reads src (a measurement reference)."""
     _check(_lib.moe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
@@ -387,9 +408,26 @@ class HostExec:
                                              _ptr(pick_slot), _ptr(w), T, k, _ptr(y_host), _stream(stream)),
                "moe_host_forward_enqueue")
 
+    def forward_signal(self, pool, wtype, H, I, x, ids, pick_slot, w, y_host, ready, done, seq):
+        """Queue a call on the dispatcher thread: it waits for ready >= seq,
+        computes y_host, then stores seq into done (pinned uint32 words)."""
+        T, k = ids.shape
+        for t in (x, ids, pick_slot, w, y_host, ready, done):
+            assert not t.is_cuda and t.is_contiguous()
+        self._keep_sig = (pool, x, ids, pick_slot, w, y_host, ready, done)
+        _check(_lib.moe_host_forward_signal(self.h, ctypes.byref(pool.c), wtype, H, I, _ptr(x), _ptr(ids),
+                                            _ptr(pick_slot), _ptr(w), T, k, _ptr(y_host), _ptr(ready), _ptr(done),
+                                            seq & 0xFFFFFFFF), "moe_host_forward_signal")
+
     def status(self):
         """First failure of an enqueued run since the last call (0 if none)."""
         return _lib.moe_host_exec_status(self.h)
+
+    def stats(self):
+        """(calls with host picks, seconds spent in them) since creation."""
+        c, ns = ctypes.c_uint64(0), ctypes.c_uint64(0)
+        _check(_lib.moe_host_exec_stats(self.h, ctypes.byref(c), ctypes.byref(ns)), "moe_host_exec_stats")
+        return c.value, ns.value / 1e9
 
     def destroy(self):
         if self.h:

@@ -19,7 +19,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmoe_gfx950.so")
-SOURCES = ["route_topk.hip", "cache.hip", "forward.hip", "host_exec.cpp"]
+SOURCES = ["route_topk.hip", "cache.hip", "forward.hip", "host_signal.hip", "host_exec.cpp"]
 GPU_SOURCES = [s for s in SOURCES if s.endswith(".hip")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

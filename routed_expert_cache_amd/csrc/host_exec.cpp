@@ -28,6 +28,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <condition_variable>
 #include <cstdint>
@@ -222,6 +223,7 @@ class Pool {
       std::lock_guard<std::mutex> lk(mu_);
       stop_ = true;
       ++gen_;
+      gen_seen_.store(gen_, std::memory_order_release);
     }
     cv_.notify_all();
     for (auto& t : th_) t.join();
@@ -235,6 +237,7 @@ class Pool {
       next_.store(0);
       busy_ = (int)th_.size();
       ++gen_;
+      gen_seen_.store(gen_, std::memory_order_release);
     }
     cv_.notify_all();
     work();
@@ -251,9 +254,17 @@ class Pool {
       (*f_)(i);
     }
   }
+  // A worker spins for about kSpin before it sleeps, so calls that come one
+  // layer apart find it awake (a sleeping thread takes tens of microseconds
+  // to wake).
+  static constexpr auto kSpin = std::chrono::microseconds(250);
   void loop() {
     uint64_t seen = 0;
     for (;;) {
+      const auto t0 = std::chrono::steady_clock::now();
+      while (gen_seen_.load(std::memory_order_acquire) == seen &&
+             std::chrono::steady_clock::now() - t0 < kSpin)
+        _mm_pause();
       {
         std::unique_lock<std::mutex> lk(mu_);
         cv_.wait(lk, [&] { return gen_ != seen; });
@@ -272,6 +283,7 @@ class Pool {
   std::mutex mu_;
   std::condition_variable cv_, done_cv_;
   uint64_t gen_ = 0;
+  std::atomic<uint64_t> gen_seen_{0};   // gen_, readable without the lock (the spin)
   bool stop_ = false;
   int busy_ = 0;
   int n_items_ = 0;
@@ -292,6 +304,13 @@ struct HostCall {             // the arguments of one moe_host_forward
   float* y_host;
 };
 
+struct SignalJob {             // a call that waits for `ready`, then publishes `done`
+  HostCall call;
+  const volatile uint32_t* ready;
+  volatile uint32_t* done;
+  uint32_t seq;
+};
+
 struct moe_host_exec {
   Pool pool;
   bool simd;                   // the AVX-512 path
@@ -300,7 +319,24 @@ struct moe_host_exec {
   std::vector<float> hbuf;     // [n_pairs][I] h in FP32
   HostCall queued{};           // the call an enqueued host function runs (persistent: graphs replay it)
   std::atomic<int32_t> status{MOE_OK};   // first failure of an enqueued run
+  uint64_t n_calls = 0, ns = 0;          // calls with host picks, time spent in them
+  // the dispatcher thread of moe_host_forward_signal (started by its first call)
+  std::thread dispatcher;
+  std::mutex q_mu;
+  std::condition_variable q_cv;
+  std::vector<SignalJob> q;
+  bool q_stop = false;
   moe_host_exec(int n, bool s) : pool(n), simd(s) {}
+  ~moe_host_exec() {
+    if (dispatcher.joinable()) {
+      {
+        std::lock_guard<std::mutex> lk(q_mu);
+        q_stop = true;
+      }
+      q_cv.notify_all();
+      dispatcher.join();
+    }
+  }
 };
 
 extern "C" moe_status moe_host_exec_create(int32_t n_threads, uint32_t flags, moe_host_exec_t* out) {
@@ -352,6 +388,7 @@ extern "C" moe_status moe_host_forward(moe_host_exec_t h, const moe_host_pool* p
   const int n_pairs = (int)pt.size();
   if (n_pairs == 0) return MOE_OK;
 
+  const auto t_start = std::chrono::steady_clock::now();
   h->xs.resize((size_t)T * H);
   for (size_t i = 0; i < (size_t)T * H; ++i) h->xs[i] = bf16_to_f32(x[i]);
   h->hbuf.resize((size_t)n_pairs * I);
@@ -418,6 +455,18 @@ extern "C" moe_status moe_host_forward(moe_host_exec_t h, const moe_host_pool* p
       p0 = p1;
     }
   });
+  h->n_calls += 1;
+  h->ns += (uint64_t)std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t_start)
+               .count();
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_host_exec_stats(moe_host_exec_t h, uint64_t* calls, uint64_t* ns) {
+  ::moe::clear_error();
+  if (!h || !calls || !ns) HX_FAIL(MOE_ERR_ARG, "null argument");
+  std::lock_guard<std::mutex> lk(h->call_mu);
+  *calls = h->n_calls;
+  *ns = h->ns;
   return MOE_OK;
 }
 
@@ -450,4 +499,62 @@ extern "C" moe_status moe_host_forward_enqueue(moe_host_exec_t h, const moe_host
 extern "C" moe_status moe_host_exec_status(moe_host_exec_t h) {
   if (!h) return MOE_ERR_ARG;
   return (moe_status)h->status.exchange(MOE_OK);
+}
+
+// ------------------------------------------------------------ signalled form
+namespace {
+constexpr auto kReadyTimeout = std::chrono::seconds(2);
+
+void dispatch_loop(moe_host_exec* h) {
+  for (;;) {
+    SignalJob job;
+    bool stopping;
+    {
+      std::unique_lock<std::mutex> lk(h->q_mu);
+      h->q_cv.wait(lk, [&] { return h->q_stop || !h->q.empty(); });
+      if (h->q.empty()) return;   // stopping with nothing queued
+      job = h->q.front();
+      h->q.erase(h->q.begin());
+      stopping = h->q_stop;
+    }
+    // wait (bounded) until the stream has written this call's inputs; a
+    // stopping executor abandons the call but still releases the GPU
+    const auto t0 = std::chrono::steady_clock::now();
+    bool ready = !stopping;
+    while (ready && (int32_t)(*job.ready - job.seq) < 0) {
+      if (std::chrono::steady_clock::now() - t0 > kReadyTimeout) {
+        ready = false;
+        break;
+      }
+      _mm_pause();
+    }
+    std::atomic_thread_fence(std::memory_order_acquire);
+    moe_status st = MOE_ERR_STATE;
+    if (ready) {
+      const HostCall& c = job.call;
+      st = moe_host_forward(h, &c.pool, c.wtype, c.H, c.I, c.x, c.ids, c.pick_slot, c.w, c.T, c.k, c.y_host);
+    }
+    if (st != MOE_OK) {
+      int32_t ok = MOE_OK;
+      h->status.compare_exchange_strong(ok, st);
+    }
+    std::atomic_thread_fence(std::memory_order_release);   // y_host before `done`
+    *job.done = job.seq;
+  }
+}
+}  // namespace
+
+extern "C" moe_status moe_host_forward_signal(moe_host_exec_t h, const moe_host_pool* pool, int32_t wtype, int32_t H,
+                                              int32_t I, const uint16_t* x, const int32_t* ids,
+                                              const int32_t* pick_slot, const float* w, int32_t T, int32_t k,
+                                              float* y_host, const uint32_t* ready, uint32_t* done, uint32_t seq) {
+  ::moe::clear_error();
+  if (!h || !pool || !ready || !done) HX_FAIL(MOE_ERR_ARG, "null executor, pool or signal word");
+  {
+    std::lock_guard<std::mutex> lk(h->q_mu);
+    if (!h->dispatcher.joinable()) h->dispatcher = std::thread(dispatch_loop, h);
+    h->q.push_back(SignalJob{HostCall{*pool, wtype, H, I, x, ids, pick_slot, w, T, k, y_host}, ready, done, seq});
+  }
+  h->q_cv.notify_one();
+  return MOE_OK;
 }

@@ -102,3 +102,51 @@ def test_host_node_in_captured_graph():
     _, ref = ffn.moe_partials(numerics.bf16_to_f64(x), ids, w, bank.expert64, on_gpu=np.zeros((T, k), bool))
     check_layer(eager.numpy(), ref, "host branch")
     ex.destroy()
+
+
+def test_decode_steps_with_signalled_host_branch():
+    """The same decode steps with the host branch handed over through pinned
+    words (moe_host_signal, moe_host_forward_signal, moe_merge_partial_after)
+    instead of a stream host function."""
+    b = binding()
+    E, H, I, k, T, C, steps = 16, 256, 128, 4, 3, 6, 12
+    bank, pool, host, cache = _setup(b, E, H, I, k, T, C, 83)
+    ex = b.HostExec(4)
+    out = b.StepOut(T, k, E)
+    ws = b.forward_workspace(T, k, H, I, C, b.FWD_DECODE)
+    h_ids = torch.empty((T, k), dtype=torch.int32).pin_memory()
+    h_pick = torch.empty((T, k), dtype=torch.int32).pin_memory()
+    h_w = torch.empty((T, k), dtype=torch.float32).pin_memory()
+    h_x = torch.empty((T, H), dtype=torch.uint16).pin_memory()
+    h_y = torch.empty((T, H), dtype=torch.float32).pin_memory()
+    ready = torch.zeros(1, dtype=torch.int32).pin_memory()
+    done = torch.zeros(1, dtype=torch.int32).pin_memory()
+    err = torch.zeros(1, dtype=torch.int32, device="cuda")
+    ids_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    y_gpu = torch.empty((T, H), dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(7)
+    xs, lgs, ys = [], [], []
+    for s in range(steps):                       # launched back to back: one sync at the end
+        x = gen.activations_bf16(rng, T, H)
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        xs.append(x)
+        lgs.append(lg)
+        x_d, lg_d = dev(x), dev(lg)
+        cache.route_step(0, lg_d, ids_d, w_d, out, copy=True)
+        pick_d = out.pick_slot.view(T, k)
+        for hd, d in ((h_ids, ids_d), (h_pick, pick_d), (h_w, w_d), (h_x, x_d)):
+            hd.copy_(d, non_blocking=True)
+        b.host_signal(ready, s + 1)
+        ex.forward_signal(host, b.W_BF16, H, I, h_x, h_ids, h_pick, h_w, h_y, ready, done, s + 1)
+        b.expert_forward(pool.c, x_d, pick_d, w_d, b.FWD_DECODE, ws, y=y_gpu)
+        ys.append(b.merge_partial_after(y_gpu, h_y, done, s + 1, err=err))
+        del x_d, lg_d
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and ex.status() == 0 and int(done[0]) == steps
+    for s in range(steps):
+        ids, w = route.topk_softmax(lgs[s], k)
+        ref = ffn.moe_output(numerics.bf16_to_f64(xs[s]), ids, w, bank.expert64)
+        check_layer(ys[s].cpu().numpy(), ref, "step %d" % s)
+    ex.destroy()
+    cache.destroy()

@@ -212,3 +212,41 @@ def test_fp8_nan_code_propagates(portable):
     finally:
         ex.destroy()
     assert np.all(np.isnan(y[0])) and np.all(np.isfinite(y[1])) and np.all(np.isfinite(y[2]))
+
+
+def test_signalled_calls_wait_for_ready_and_publish_done():
+    """moe_host_forward_signal without a GPU: the ready word is written from
+    the host.  Calls run in order once ready reaches their number, done is
+    stored after y_host; a call whose ready never comes is skipped after the
+    bounded wait, still publishes done, and leaves its failure in the status."""
+    import time
+    b = binding()
+    bank = BankBF16(207, 4, 64, 32)
+    pool = b.HostPoolTables(bank.banks, lambda i: i, bank.E, pinned=False)
+    x, ids, w, host, pick = _case(bank, 2, 2, 1.0, 6)
+    ready = torch.zeros(1, dtype=torch.int32)
+    done = torch.zeros(1, dtype=torch.int32)
+    ys = [torch.zeros((2, 64), dtype=torch.float32) for _ in range(2)]
+    args = [torch.from_numpy(a) for a in (x, ids, pick, w)]
+    ex = b.HostExec(2)
+    try:
+        ex.forward_signal(pool, 0, 64, 32, *args, ys[0], ready, done, 1)
+        ex.forward_signal(pool, 0, 64, 32, *args, ys[1], ready, done, 2)
+        time.sleep(0.05)
+        assert int(done[0]) == 0 and np.all(ys[0].numpy() == 0)   # nothing runs before ready
+        ready[0] = 2                                              # both calls' inputs are in
+        t0 = time.time()
+        while int(done[0]) != 2 and time.time() - t0 < 5:
+            time.sleep(0.001)
+        assert int(done[0]) == 2 and ex.status() == 0
+        ref = _run(b, ex, bank, x, ids, pick, w)
+        assert np.array_equal(ys[0].numpy(), ref) and np.array_equal(ys[1].numpy(), ref)
+        ex.forward_signal(pool, 0, 64, 32, *args, ys[0], ready, done, 3)   # ready never reaches 3
+        t0 = time.time()
+        while int(done[0]) != 3 and time.time() - t0 < 10:
+            time.sleep(0.01)
+        assert int(done[0]) == 3 and time.time() - t0 >= 1.5
+        assert ex.status() == -6                                  # MOE_ERR_STATE, then cleared
+        assert ex.status() == 0
+    finally:
+        ex.destroy()
