@@ -226,7 +226,7 @@ def read_ceiling(b, nbytes, reps=20):
 
 
 # ---------------------------------------------------------------- decode trace
-def run_decode(b, K, W):
+def run_decode(b, K, W, host_GBps=None):
     import torch
     from harness import gen, CONFIGS
     c = CONFIGS["decode_bf16"]
@@ -349,23 +349,40 @@ def run_decode(b, K, W):
         b.expert_forward(pool.c, x[s, l], pick, w, b.FWD_DECODE, ws, y=y_gpu)
         b.merge_partial_after(y_gpu, h_y, done, seq[0], y_out=y[l], err=err)
 
-    cache4 = b.Cache(L, E, k, 1, pool, host, c.bp, c.bh)
-    for s in range(W):
-        for l in range(L):
-            layer_step_host(cache4, s, l)
-    torch.cuda.synchronize()
-    c0 = cache4.read_state()[4].astype(np.int64)
-    t0 = time.perf_counter()
-    for s in range(W, W + K):
-        for l in range(L):
-            layer_step_host(cache4, s, l)
-    torch.cuda.synchronize()
-    wall_host = time.perf_counter() - t0
-    d4 = cache4.read_state()[4].astype(np.int64) - c0
-    cache4.destroy()
+    def run_host_trace(bp, bh):
+        """Pass 4 (and 5): cold cache with this B_P:B_H, W warm-up and K timed steps."""
+        cache4 = b.Cache(L, E, k, 1, pool, host, bp, bh)
+        for s in range(W):
+            for l in range(L):
+                layer_step_host(cache4, s, l)
+        torch.cuda.synchronize()
+        c0 = cache4.read_state()[4].astype(np.int64)
+        t0 = time.perf_counter()
+        for s in range(W, W + K):
+            for l in range(L):
+                layer_step_host(cache4, s, l)
+        torch.cuda.synchronize()
+        wall_h = time.perf_counter() - t0
+        dh = cache4.read_state()[4].astype(np.int64) - c0
+        cache4.destroy()
+        assert ex.status() == 0 and int(err.item()) == 0, "the host branch failed"
+        return wall_h, dh
+
+    wall_host, d4 = run_host_trace(c.bp, c.bh)
     assert np.array_equal(d, d4), "the passes made different cache decisions"
-    assert ex.status() == 0 and int(err.item()) == 0, "the host branch failed"
     host_calls, host_s = ex.stats()
+    calibrated = None
+    fill_rate = (d[4] * S / fill_s / 1e9) if fill_s > 0 else None
+    if host_GBps and fill_rate:
+        # Pass 5: q* from this machine's rates (B_P: the fill copies above, B_H:
+        # the host executor) instead of the quoted ratio; the same trace.
+        bp_c, bh_c = max(1, round(fill_rate * 10)), max(1, round(host_GBps * 10))   # units of 0.1 GB/s
+        log("decode: pass 5 (host branch, calibrated B_P:B_H %.1f:%.1f)" % (bp_c / 10, bh_c / 10))
+        wall5, d5 = run_host_trace(bp_c, bh_c)
+        calibrated = dict(B_P_GBps=bp_c / 10, B_H_GBps=bh_c / 10, wall_ms_per_step=wall5 / K * 1e3,
+                          miss_rate=float(d5[3] / d5[1]), fills_per_layer_call=float(d5[4] / (K * L)),
+                          host_experts_per_layer_call=float(d5[5] / (K * L)),
+                          experts_on_gpu_per_layer_call=float((d5[2] + d5[4]) / (K * L)))
     ex.destroy()
     # Forward-only burst: the timed layer calls' forward launches again, back
     # to back with the same picks (the slots now hold other experts: the same
@@ -407,6 +424,7 @@ def run_decode(b, K, W):
                 wall_ms_per_step=wall_host / K * 1e3,
                 host_compute_us_per_call_with_host_picks=host_s / max(host_calls, 1) * 1e6,
                 calls_with_host_picks=host_calls,
+                calibrated_split=calibrated,
                 note="pass 4: the full path with the host set evaluated by moe_host_forward on %d host threads, "
                      "handed over through pinned words while the GPU fills and evaluates G, beside "
                      "wall_ms_per_step_pcie_inclusive (pass 2: the harness's y_host)" % max(1, n_cores - 1)),
@@ -765,7 +783,7 @@ def cpu_baseline(budget_s):
                        % (done, el, len(os.sched_getaffinity(0))))
 
 
-def run_host_exec(b, fill_GBps=None, seconds=3.0):
+def run_host_exec(b, seconds=3.0):
     """Throughput of the host executor (moe_host_forward) on this machine's cores:
     the B_H of the q* split.  Each call evaluates k = 8 host picks of one token,
     each a different expert, cycling through a pinned pool larger than the CPU
@@ -825,9 +843,6 @@ def run_host_exec(b, fill_GBps=None, seconds=3.0):
                          pool_GB=n_pool * expert_bytes / 1e9)
         del banks, pool, gu, dp
     ex.destroy()
-    if fill_GBps:
-        out["fill_GBps"] = fill_GBps
-        out["B_P_over_B_H_measured"] = {k: fill_GBps / out[k]["GBps"] for k in ("decode_bf16", "decode_fp8")}
     return out
 
 
@@ -847,7 +862,16 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
     if a.calibrate_copy:
         calibrate_copy()
-    dec = run_decode(b, a.steps, a.warmup)
+    host_exec = None
+    if not a.no_host_exec:
+        log("host executor: expert GB/s on %d cores" % len(os.sched_getaffinity(0)))
+        host_exec = run_host_exec(b)
+    dec = run_decode(b, a.steps, a.warmup, host_exec["decode_bf16"]["GBps"] if host_exec else None)
+    if host_exec:
+        fr = dec["detail"].get("fill_GBps")
+        if fr:
+            host_exec["fill_GBps"] = fr
+            host_exec["B_P_over_B_H_measured"] = {k: fr / host_exec[k]["GBps"] for k in ("decode_bf16", "decode_fp8")}
     line = {
         "metric": METRIC, "value": round(dec["value"], 2), "unit": "GB/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(dec["ms_per_step"], 4),
@@ -868,9 +892,8 @@ def main():
         if not a.no_prefill and not a.no_prefill_fp8:
             line["prefill_fp8"] = run_prefill_fp8(b)
             torch.cuda.empty_cache()
-    if not a.no_host_exec:
-        log("host executor: expert GB/s on %d cores" % len(os.sched_getaffinity(0)))
-        line["host_exec"] = run_host_exec(b, dec["detail"].get("fill_GBps"))
+    if host_exec:
+        line["host_exec"] = host_exec
     if not a.no_cpu_baseline:
         log("cpu baseline: oracle for %.0f s" % a.cpu_seconds)
         line["cpu_baseline"] = cpu_baseline(a.cpu_seconds)
