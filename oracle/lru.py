@@ -27,7 +27,11 @@ Readings adopted where the pages are silent (all listed in the design notes):
   by the grouped evaluation after the copy), so q = min(q*, #non-hit slots);
 * victims: ascending (stamp, slot) among non-hit, non-reserved slots; F is
   the first q misses by ascending id and fill i goes to victim i;
-* slots reserved by the prefill double buffer are outside the LRU.
+* slots reserved by the prefill double buffer are outside the LRU;
+* on-demand loading (no room for the full-layer buffers) fills every miss
+  that finds a non-hit slot: q* = m instead of the bandwidth split;
+* at the end of prefill the experts the buffers hold become residents (see
+  finish_prefill for the order of their stamps).
 """
 import numpy as np
 
@@ -86,8 +90,43 @@ class ExpertCache:
             self.slot_id[s] = EMPTY
             self.ts[s] = 0
 
+    def finish_prefill(self, first: int, n_buf: int, loaded):
+        """End of prefill: the full-layer buffers hand what they hold to the
+        decode cache.
+
+        [FT] "全层双缓冲" and [FTK] (prefill paragraph): the buffers are slots
+        of the one shared pool, so the experts they hold when prefill ends are
+        the decode cache's first residents, with no copy and no separate
+        hand-over phase.  Buffer b spans slots [first + b*E, first + b*E + E).
+        loaded: (b, layer) for each buffer holding a complete layer, least
+        recently loaded first.  Readings: a later load is more recent; inside
+        a buffer, ascending expert index; expert e of the buffer at position
+        pos of `loaded` gets stamp (tick << 16) | (1 + pos*E + e); an expert
+        already resident in a decode slot keeps that slot, takes the new
+        stamp, and its buffer slot is left empty; every other buffer slot is
+        left empty; the tick then advances by one.
+        """
+        E = self.E
+        self.release(first, n_buf * E)
+        for pos, (b, layer) in enumerate(loaded):
+            for e in range(E):
+                lid = layer * E + e
+                stamp = (self.tick << 16) | (1 + pos * E + e)
+                old = self.id_slot[lid]
+                if old >= 0:
+                    self.ts[old] = stamp
+                    continue
+                s = first + b * E + e
+                self.slot_id[s] = lid
+                self.id_slot[lid] = s
+                self.ts[s] = stamp
+        self.tick += 1
+
     # -- one layer call --------------------------------------------------------
-    def step(self, layer: int, ids, copy: bool = True) -> StepResult:
+    def step(self, layer: int, ids, copy: bool = True, fill_all: bool = False) -> StepResult:
+        """One layer call.  fill_all: on-demand loading ([FT] "全层双缓冲",
+        the fallback when two full layers do not fit): every miss is a fill
+        candidate, q* = m; q is still capped by the non-hit slots."""
         ids = np.asarray(ids, dtype=np.int64)
         T, k = ids.shape
         E = self.E
@@ -99,7 +138,7 @@ class ExpertCache:
         hits = [i for i in uniq if self.id_slot[i] >= 0]
         misses = [i for i in uniq if self.id_slot[i] < 0]
         m = len(misses)
-        qs = _q_star(m, self.bp, self.bh)
+        qs = m if fill_all else _q_star(m, self.bp, self.bh)
 
         hit_slots = set(self.id_slot[i] for i in hits)
         cand = [s for s in range(self.C) if s not in hit_slots and self.slot_id[s] != RESERVED]

@@ -173,3 +173,111 @@ def test_tiny_config_all_hit_consequence():
     r = oc.step(0, ids)
     assert r.hits == [0, 1, 2, 3] and r.q_star == 1 and r.q == 0
     assert r.host_id == [4, 5, 6, 7]
+
+
+# ---------------------------------------------------------------- prefill hand-over and on-demand loading
+@pytest.mark.parametrize("seed", range(8))
+def test_fill_all_matches_textbook(seed):
+    """On-demand loading fills every miss that has room: the textbook LRU
+    with q capped only by the free or evictable slots, whatever the
+    bandwidth ratio (here one that would keep most misses on the host)."""
+    rng = np.random.default_rng(300 + seed)
+    L, E, C, T, k = 2, 6, int(rng.integers(2, 9)), 3, 2
+    oc = lru.ExpertCache(L, E, C, 1, 1000)
+    tb = TextbookLRU(C, [])
+    for layer, ids in _random_trace(rng, 120, L, E, T, k):
+        r = oc.step(layer, ids, fill_all=True)
+        uniq = sorted(set((layer * E + ids).reshape(-1).tolist()))
+        hits, fills, host, evicted = tb.step(uniq, lambda m: m)
+        assert r.q_star == len(r.misses)
+        assert (r.hits, r.fill_id, r.host_id, r.fill_evicted) == (hits, fills, host, evicted)
+
+
+def _prefill_then_textbook(rng, L, E, C, n_buf, n_layers_run, pre_resident):
+    """Reserve n_buf full-layer buffers, run prefill over layers
+    0..n_layers_run-1 (layer l in buffer l % n_buf), finish; return the
+    oracle cache and the textbook LRU that must agree with it from there."""
+    first = C - n_buf * E
+    oc = lru.ExpertCache(L, E, C, 900, 475)
+    oc.seed(pre_resident)
+    oc.reserve(first, n_buf * E)
+    held = {}
+    order = []
+    for l in range(n_layers_run):
+        b = l % n_buf
+        held[b] = l
+        if b in order:
+            order.remove(b)
+        order.append(b)
+    loaded = [(b, held[b]) for b in order]
+    oc.finish_prefill(first, n_buf, loaded)
+    # textbook: the decode residents that kept their slots (seeded order),
+    # then the buffers' experts, least recently loaded first, ascending e
+    od = OrderedDict((int(i), None) for i in pre_resident)
+    for b, l in loaded:
+        for e in range(E):
+            od.pop(l * E + e, None)
+            od[l * E + e] = None
+    tb = TextbookLRU(C, [])
+    tb.od = od
+    return oc, tb, loaded
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_prefill_survivors_seed_the_lru(seed):
+    rng = np.random.default_rng(400 + seed)
+    E = int(rng.integers(2, 5))
+    L = int(rng.integers(2, 6))
+    n_buf = int(rng.integers(1, 4))
+    C = n_buf * E + int(rng.integers(0, 5))
+    run = int(rng.integers(0, L + 1))
+    first = C - n_buf * E
+    pre = list(rng.choice(L * E, size=min(first, L * E), replace=False))
+    oc, tb, loaded = _prefill_then_textbook(rng, L, E, C, n_buf, run, pre)
+    slot_id, ts, id_slot, _ = oc.tables()
+    assert set(i for i in slot_id if i >= 0) == set(tb.od.keys())
+    for b, l in loaded:                              # every held expert is resident
+        for e in range(E):
+            s = id_slot[l * E + e]
+            assert s >= 0 and slot_id[s] == l * E + e
+            assert s == first + b * E + e or s < first  # its buffer slot, or the decode slot it had
+    assert not (slot_id == lru.RESERVED).any()
+    for s, i in enumerate(slot_id):
+        if i >= 0:
+            assert id_slot[i] == s
+    # the recency order the stamps give is the textbook's
+    occ = sorted((int(ts[s]), s) for s in range(C) if slot_id[s] >= 0)
+    assert [int(slot_id[s]) for _, s in occ] == list(tb.od.keys())
+    # and decode from there behaves as the textbook LRU
+    for layer, ids in _random_trace(rng, 80, L, E, 2, min(2, E)):
+        r = oc.step(layer, ids, fill_all=True)
+        uniq = sorted(set((layer * E + ids).reshape(-1).tolist()))
+        hits, fills, host, evicted = tb.step(uniq, lambda m: m)
+        assert (r.hits, r.fill_id, r.host_id, r.fill_evicted) == (hits, fills, host, evicted)
+
+
+def test_prefill_survivor_already_resident_keeps_its_slot():
+    """Worked by hand: slot 0 holds id 9 (layer 2, expert 1), slot 1 holds
+    id 2 (layer 0, expert 2); buffers at slots 2-5 (layer 0) and 6-9
+    (layer 2, loaded last)."""
+    L, E, C = 3, 4, 10
+    oc = lru.ExpertCache(L, E, C, 900, 475)
+    oc.seed([9, 2])
+    oc.reserve(2, 8)
+    t0 = oc.tick
+    oc.finish_prefill(2, 2, [(0, 0), (1, 2)])
+    slot_id, ts, id_slot, tick = oc.tables()
+    assert slot_id.tolist() == [9, 2, 0, 1, -1, 3, 8, -1, 10, 11]
+    assert id_slot[2] == 1 and id_slot[9] == 0
+    base = t0 << 16
+    assert ts.tolist() == [base | 6, base | 3, base | 1, base | 2, 0, base | 4, base | 5, 0, base | 7, base | 8]
+    assert tick == t0 + 1
+
+
+def test_finish_with_nothing_loaded_releases_the_buffers():
+    oc = lru.ExpertCache(2, 4, 9, 900, 475)
+    oc.seed([5])
+    oc.reserve(1, 8)
+    oc.finish_prefill(1, 2, [])
+    slot_id, ts, _, _ = oc.tables()
+    assert slot_id.tolist() == [5] + [-1] * 8 and ts.tolist() == [1] + [0] * 8
