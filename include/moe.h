@@ -143,6 +143,9 @@ typedef struct moe_step_out {
 } moe_step_out;
 
 #define MOE_STEP_NO_COPY 1u   /* decisions and tables only; skip the fill copy  */
+#define MOE_STEP_FILL_ALL 2u  /* q* = m: fill every miss that finds a non-hit
+                                 slot (on-demand loading, see
+                                 moe_cache_prefill_load)                        */
 
 #define MOE_FWD_DECODE 0u     /* grouped GEMV, T <= 16                           */
 #define MOE_FWD_PREFILL 1u    /* sorted grouped GEMM on MFMA                     */
@@ -224,6 +227,27 @@ moe_status moe_cache_route_step(moe_cache_t c, int32_t layer, const float* logit
  * flag.  Capturable.
  */
 moe_status moe_cache_fill(moe_cache_t c, const moe_step_out* out, hipStream_t stream);
+
+/*
+ * On-demand loading of one layer for a prefill batch, the fallback when the
+ * pool has no room for the full-layer buffers ([FT] section "全层双缓冲";
+ * [FTK] prefill paragraph: without two whole-layer buffers prefill loads
+ * what the layer needs instead of oversubscribing memory).  One layer call
+ * of the cache over the batch's routed experts with MOE_STEP_FILL_ALL: the
+ * dedup, hit/miss, victim scan, table update and stamps of moe_cache_step
+ * with q* = m (every miss is filled while non-hit slots remain; the rest
+ * stay on the host), then pick_slot[p] = slot of the expert of pick p, or -1
+ * for a pick left to the host, then (unless MOE_STEP_NO_COPY) the fused fill
+ * copy.  Decisions, tables and counts equal moe_cache_step(c, layer, ids, T,
+ * flags | MOE_STEP_FILL_ALL, out) would give for a T within T_max.
+ * ids: device int32 [T, k], any T >= 1; pick_slot: device int32 [T, k],
+ * written (out->pick_slot is not used).  Needs ceil(E/k) <= T_max (the
+ * layer's expert set goes to the decision kernel as rows of k).  Ids outside
+ * [0, E) set the device error word and go to the host.  Capturable.
+ */
+moe_status moe_cache_prefill_load(moe_cache_t c, int32_t layer, const int32_t* ids, int32_t T,
+                                  uint32_t flags, const moe_step_out* out, int32_t* pick_slot,
+                                  hipStream_t stream);
 
 /*
  * Copy the residency tables to HOST arrays (any pointer may be NULL):
@@ -318,12 +342,22 @@ moe_status moe_merge_partial(const float* y_gpu, const float* y_host, int32_t T,
  * Full-layer double buffer for prefill ([FT] section "全层双缓冲"; [FTK]
  * prefill paragraph).  Reserves the last 2E slots of the cache's pool as two
  * full-layer buffers (evicting what they held; they leave the LRU), else
- * MOE_ERR_NO_SPACE.  Layer l uses buffer l % 2.
+ * MOE_ERR_NO_SPACE (then prefill falls back to moe_cache_prefill_load).
+ * Layer l uses buffer l % 2.  Synchronises the device.
  */
 moe_status moe_prefill_create(moe_cache_t c, moe_prefill_t* out);
 
 /*
- * Enqueue on copy_stream: wait until buffer (layer % 2) is released, copy ALL
+ * The same with `depth` full-layer buffers (2 <= depth <= 64) in a ring:
+ * reserves the last depth*E slots, layer l uses buffer l % depth, so up to
+ * depth - 1 layers load ahead of the one computing ([OSDI] section 3.2,
+ * the expert ring of stream-loading prefill: deep while transfer is the
+ * bottleneck, two buffers once compute is).  MOE_ERR_NO_SPACE if depth*E > C.
+ */
+moe_status moe_prefill_create_ring(moe_cache_t c, int32_t depth, moe_prefill_t* out);
+
+/*
+ * Enqueue on copy_stream: wait until buffer (layer % depth) is released, copy ALL
  * E experts of `layer` (every bank) from the pinned host pool into it
  * (without waiting for routing), then mark it ready.
  */
@@ -341,7 +375,21 @@ moe_status moe_prefill_acquire(moe_prefill_t p, int32_t layer, hipStream_t compu
 /* Record on `compute` that layer's buffer may be overwritten by a later prefetch. */
 moe_status moe_prefill_release(moe_prefill_t p, int32_t layer, hipStream_t compute);
 
-/* Return the 2E slots to the LRU as empty slots and free the events. */
+/*
+ * End prefill and seed decode with what the buffers hold ([FT] section
+ * "全层双缓冲" and [FTK] prefill paragraph: the buffers are slots of the
+ * shared pool, so the experts that survive prefill are decode's first
+ * residents, with no copy).  Waits for the device, then every expert of a
+ * layer a buffer holds becomes resident in its buffer slot, more recent than
+ * every earlier entry: buffers in load order (least recent first), experts
+ * ascending, stamps (tick << 16) | (1 + rank); an expert already resident in
+ * a decode slot keeps that slot and takes the new stamp, its buffer slot and
+ * every buffer that holds nothing return empty; the tick advances by one.
+ * Frees the pool.  Not capturable.
+ */
+moe_status moe_prefill_finish(moe_prefill_t p, hipStream_t stream);
+
+/* End prefill discarding the buffers: their slots return to the LRU empty. */
 moe_status moe_prefill_destroy(moe_prefill_t p, hipStream_t stream);
 
 

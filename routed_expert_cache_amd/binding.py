@@ -23,6 +23,7 @@ STATUS = {0: "MOE_OK", -1: "MOE_ERR_ARG", -2: "MOE_ERR_SHAPE", -3: "MOE_ERR_NO_S
           -4: "MOE_ERR_NOT_PINNED", -5: "MOE_ERR_HIP", -6: "MOE_ERR_STATE", -7: "MOE_ERR_DEVICE"}
 W_BF16, W_FP8_B128 = 0, 1
 STEP_NO_COPY = 1
+STEP_FILL_ALL = 2
 HOST_PORTABLE = 1
 FWD_DECODE, FWD_PREFILL = 0, 1
 CNT_UNIQ, CNT_HIT, CNT_MISS, CNT_QSTAR, CNT_FILL, CNT_HOST, CNT_N = 0, 1, 2, 3, 4, 5, 8
@@ -33,7 +34,8 @@ EXPORTS = [
     "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_expert_forward_merge",
     "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
-    "moe_prefill_destroy", "moe_e4m3_to_bf16", "moe_pack_weights", "moe_stream_read",
+    "moe_prefill_destroy", "moe_prefill_create_ring", "moe_prefill_finish", "moe_cache_prefill_load",
+    "moe_e4m3_to_bf16", "moe_pack_weights", "moe_stream_read",
     "moe_host_exec_create", "moe_host_exec_destroy", "moe_host_exec_simd", "moe_host_forward",
     "moe_host_forward_enqueue", "moe_host_exec_status", "moe_host_exec_stats",
     "moe_host_signal", "moe_host_forward_signal", "moe_merge_partial_after",
@@ -95,6 +97,9 @@ _sig = {
     "moe_prefill_acquire": (_i32, [_vp, _i32, _vp, _P(Slots)]),
     "moe_prefill_release": (_i32, [_vp, _i32, _vp]),
     "moe_prefill_destroy": (_i32, [_vp, _vp]),
+    "moe_prefill_create_ring": (_i32, [_vp, _i32, _P(_vp)]),
+    "moe_prefill_finish": (_i32, [_vp, _vp]),
+    "moe_cache_prefill_load": (_i32, [_vp, _i32, _vp, _i32, _u32, _P(StepOutC), _vp, _vp]),
     "moe_e4m3_to_bf16": (_i32, [_vp, _vp, ctypes.c_int64, _vp]),
     "moe_pack_weights": (_i32, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_host_exec_create": (_i32, [_i32, _u32, _P(_vp)]),
@@ -237,10 +242,21 @@ class Cache:
         _check(_lib.moe_cache_seed(self.h, arr, len(ids), 0 if copy else STEP_NO_COPY, _stream(stream)),
                "moe_cache_seed")
 
-    def step(self, layer, ids, out: StepOut, copy=True, stream=None):
+    def step(self, layer, ids, out: StepOut, copy=True, fill_all=False, stream=None):
         T = ids.shape[0]
-        _check(_lib.moe_cache_step(self.h, layer, _ptr(ids), T, 0 if copy else STEP_NO_COPY,
-                                   ctypes.byref(out.c), _stream(stream)), "moe_cache_step")
+        flags = (0 if copy else STEP_NO_COPY) | (STEP_FILL_ALL if fill_all else 0)
+        _check(_lib.moe_cache_step(self.h, layer, _ptr(ids), T, flags, ctypes.byref(out.c), _stream(stream)),
+               "moe_cache_step")
+
+    def prefill_load(self, layer, ids, out: StepOut, pick_slot=None, copy=True, stream=None):
+        """On-demand loading of a prefill batch (any T): returns pick_slot [T, k]."""
+        assert ids.is_cuda and ids.dtype == torch.int32 and ids.is_contiguous()
+        if pick_slot is None:
+            pick_slot = torch.empty(ids.shape, dtype=torch.int32, device=ids.device)
+        _check(_lib.moe_cache_prefill_load(self.h, layer, _ptr(ids), ids.shape[0], 0 if copy else STEP_NO_COPY,
+                                           ctypes.byref(out.c), _ptr(pick_slot), _stream(stream)),
+               "moe_cache_prefill_load")
+        return pick_slot
 
     def route_step(self, layer, logits, ids, w, out: StepOut, copy=True, stream=None):
         """Router + cache step in one launch; writes ids [T, k] and w [T, k]."""
@@ -348,10 +364,15 @@ def e4m3_to_bf16(codes, out=None, stream=None):
 
 # ---------------------------------------------------------------- prefill double buffer
 class PrefillPool:
-    def __init__(self, cache: Cache):
+    """depth full-layer buffers (2: the double buffer) reserved from the cache's slots."""
+
+    def __init__(self, cache: Cache, depth=2):
         h = ctypes.c_void_p()
-        _check(_lib.moe_prefill_create(cache.h, ctypes.byref(h)), "moe_prefill_create")
-        self.h, self.cache = h, cache
+        if depth == 2:
+            _check(_lib.moe_prefill_create(cache.h, ctypes.byref(h)), "moe_prefill_create")
+        else:
+            _check(_lib.moe_prefill_create_ring(cache.h, depth, ctypes.byref(h)), "moe_prefill_create_ring")
+        self.h, self.cache, self.depth = h, cache, depth
 
     def prefetch(self, layer, copy_stream):
         _check(_lib.moe_prefill_prefetch(self.h, layer, _stream(copy_stream)), "moe_prefill_prefetch")
@@ -365,8 +386,15 @@ class PrefillPool:
         _check(_lib.moe_prefill_release(self.h, layer, _stream(compute)), "moe_prefill_release")
 
     def destroy(self, stream=None):
+        """End prefill discarding the buffers (their slots return empty)."""
         if self.h:
             _check(_lib.moe_prefill_destroy(self.h, _stream(stream)), "moe_prefill_destroy")
+            self.h = None
+
+    def finish(self, stream=None):
+        """End prefill keeping what the buffers hold as decode's residents."""
+        if self.h:
+            _check(_lib.moe_prefill_finish(self.h, _stream(stream)), "moe_prefill_finish")
             self.h = None
 
 

@@ -21,6 +21,8 @@
 #include <stdarg.h>
 #include <string.h>
 
+#include <algorithm>
+#include <utility>
 #include <vector>
 
 #include "common.h"
@@ -73,6 +75,7 @@ struct CacheDev {
   uint64_t* counters;   // [8]
   int32_t* error;       // [1]
   int32_t* seed_list;   // [2*C + 8] scratch for seeding: ids, slots, counts
+  int32_t* set_list;    // [2*kUMax] scratch of on-demand loading: expert set, its picks
   const uint64_t* host_tab;  // [nb][L*E] device-visible host pointers
   int L, E, C;
   uint32_t bp, bh;
@@ -83,6 +86,7 @@ struct StepArgs {
   const float* logits;    // [T*E] when routing in the kernel
   float* w;               // [T*k] gate weights when routing in the kernel
   int layer, T, k, U_max;
+  int fill_all;           // q* = m (on-demand loading) instead of the bandwidth split
   moe_step_out out;
 };
 
@@ -300,9 +304,11 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
   const int m = u - h;
   for (int i = u + tid; i < a.U_max; i += kDT) a.out.is_hit[i] = -1;
 
-  // 3. q* = clamp(round(m bp / bh), 1, m)
+  // 3. q* = clamp(round(m bp / bh), 1, m), or m when every miss is to be filled
   int qs = 0;
-  if (m > 0) {
+  if (m > 0 && a.fill_all) {
+    qs = m;
+  } else if (m > 0) {
     const uint64_t q0 = (2ull * (uint64_t)m * cd.bp + cd.bh) / (2ull * cd.bh);
     qs = (int)(q0 < 1 ? 1 : (q0 > (uint64_t)m ? (uint64_t)m : q0));
   }
@@ -537,6 +543,104 @@ __global__ void cache_mark_kernel(CacheDev cd, int first, int n, int mark) {
   }
 }
 
+// On-demand loading of a prefill batch: the set of experts the batch routes
+// to, written as n_set ids (whole rows of k for the decision kernel): the
+// routed experts ascending, then the first of them repeated (the decision's
+// dedup removes repeats; a set with no valid id is all -1).
+__global__ __launch_bounds__(1024) void prefill_set_kernel(CacheDev cd, const int32_t* __restrict__ ids, int64_t P,
+                                                           int n_set) {
+  __shared__ uint32_t bm[kEMax / 32];
+  __shared__ int wpre[kEMax / 32 + 1];
+  const int E = cd.E, nw = (E + 31) / 32, tid = threadIdx.x;
+  for (int i = tid; i < nw; i += 1024) bm[i] = 0;
+  __syncthreads();
+  for (int64_t p = tid; p < P; p += 1024) {
+    const int e = ids[p];
+    if (e < 0 || e >= E)
+      atomicOr(cd.error, 1 << ERR_BAD_ID);
+    else
+      atomicOr(&bm[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  if (tid == 0) {   // at most 128 words
+    int acc = 0;
+    for (int w = 0; w < nw; ++w) {
+      wpre[w] = acc;
+      acc += __popc(bm[w]);
+    }
+    wpre[nw] = acc;
+  }
+  __syncthreads();
+  int* set = cd.set_list;
+  const int U = wpre[nw];
+  int first = -1;
+  for (int w = 0; w < nw && first < 0; ++w)
+    if (bm[w]) first = 32 * w + __builtin_ctz(bm[w]);
+  for (int w = tid; w < nw; w += 1024) {
+    uint32_t bits = bm[w];
+    int r = wpre[w];
+    while (bits) {
+      set[r++] = 32 * w + __builtin_ctz(bits);
+      bits &= bits - 1;
+    }
+  }
+  for (int i = U + tid; i < n_set; i += 1024) set[i] = first;
+}
+
+// After the decision: each pick of the batch goes to its expert's slot if the
+// expert is now resident (it is then in G = H u F), else to the host (-1).
+__global__ __launch_bounds__(256) void prefill_pick_kernel(CacheDev cd, const int32_t* __restrict__ ids, int64_t P,
+                                                           int layer, int32_t* __restrict__ pick_slot) {
+  const int E = cd.E;
+  const int32_t* row = cd.id_slot + (size_t)layer * E;
+  for (int64_t p = (int64_t)blockIdx.x * 256 + threadIdx.x; p < P; p += (int64_t)gridDim.x * 256) {
+    const int e = ids[p];
+    pick_slot[p] = (e >= 0 && e < E) ? row[e] : -1;
+  }
+}
+
+// End of prefill: slot first + b*E + e of buffer b takes expert e of layer
+// lay[b] (-1: the buffer holds nothing) with stamp (tick << 16) | (1 + pos[b]*E
+// + e), pos[b] being the buffer's rank in load order; an expert already
+// resident elsewhere keeps its slot and takes the stamp, leaving the buffer
+// slot empty.  The tick then advances by one.
+constexpr int kMaxRing = 64;
+struct AdoptArgs {
+  int first, n_buf;
+  int lay[kMaxRing], pos[kMaxRing];
+};
+
+__global__ __launch_bounds__(1024) void cache_adopt_kernel(CacheDev cd, AdoptArgs a) {
+  const uint64_t tick = *cd.tick;
+  const int E = cd.E;
+  for (int i = threadIdx.x; i < a.n_buf * E; i += 1024) {
+    const int b = i / E, e = i - b * E, s = a.first + i;
+    const int layer = a.lay[b];
+    if (layer < 0) {
+      cd.slot_id[s] = -1;
+      cd.stamp[s] = 0;
+      continue;
+    }
+    const int lid = layer * E + e;
+    const uint64_t st = (tick << 16) | (uint64_t)(1 + a.pos[b] * E + e);
+    const int old = cd.id_slot[lid];
+    if (old >= 0 && old < cd.C && cd.slot_id[old] == lid) {
+      cd.stamp[old] = st;
+      cd.slot_id[s] = -1;
+      cd.stamp[s] = 0;
+    } else {
+      cd.slot_id[s] = lid;
+      cd.id_slot[lid] = s;
+      cd.stamp[s] = st;
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    *cd.tick = tick + 1;
+    if (tick + 1 >= (1ull << 28)) atomicOr(cd.error, 1 << ERR_TICK);
+  }
+}
+
 }  // namespace moe
 
 // ================================================================ host side
@@ -557,7 +661,7 @@ using namespace moe;
 static size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t id_slot, slot_id, stamp, order, n_ord, tick, counters, error, seed, host_tab, total;
+  size_t id_slot, slot_id, stamp, order, n_ord, tick, counters, error, seed, set, host_tab, total;
 };
 static WsLayout ws_layout(const moe_cache_cfg* c, int nb) {
   WsLayout w{};
@@ -572,6 +676,7 @@ static WsLayout ws_layout(const moe_cache_cfg* c, int nb) {
   w.counters = off; off = align_up(off + 64, 256);
   w.error = off; off = align_up(off + 4, 256);
   w.seed = off; off = align_up(off + 4 * (2 * (size_t)c->C + 8), 256);
+  w.set = off; off = align_up(off + 4 * 2 * (size_t)kUMax, 256);
   w.host_tab = off; off = align_up(off + 8 * (size_t)nb * LE, 256);
   w.total = off;
   return w;
@@ -690,6 +795,7 @@ extern "C" moe_status moe_cache_create(const moe_cache_cfg* cfg, const moe_slots
   d.counters = (uint64_t*)(ws + L.counters);
   d.error = (int32_t*)(ws + L.error);
   d.seed_list = (int32_t*)(ws + L.seed);
+  d.set_list = (int32_t*)(ws + L.set);
   d.host_tab = (const uint64_t*)(ws + L.host_tab);
   d.L = cfg->L;
   d.E = cfg->E;
@@ -795,6 +901,7 @@ extern "C" moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t
   a.T = T;
   a.k = c->cfg.k;
   a.U_max = c->U_max;
+  a.fill_all = (flags & MOE_STEP_FILL_ALL) != 0;
   a.out = *out;
   cache_decide_kernel<0><<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
   MOE_LAUNCHED();
@@ -820,6 +927,7 @@ extern "C" moe_status moe_cache_route_step(moe_cache_t c, int32_t layer, const f
   a.T = T;
   a.k = k;
   a.U_max = c->U_max;
+  a.fill_all = (flags & MOE_STEP_FILL_ALL) != 0;
   a.out = *out;
   if (E <= 64)
     cache_decide_kernel<1><<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
@@ -841,6 +949,43 @@ extern "C" moe_status moe_cache_fill(moe_cache_t c, const moe_step_out* out, hip
   clear_error();
   if (!c || !out || !out->fill_id || !out->fill_slot || !out->counts) MOE_FAIL(MOE_ERR_ARG, "null argument");
   return launch_fill(c, out->fill_id, out->fill_slot, out->counts + MOE_CNT_FILL, stream);
+}
+
+extern "C" moe_status moe_cache_prefill_load(moe_cache_t c, int32_t layer, const int32_t* ids, int32_t T,
+                                             uint32_t flags, const moe_step_out* out, int32_t* pick_slot,
+                                             hipStream_t stream) {
+  clear_error();
+  if (!c || !out || !ids || !pick_slot) MOE_FAIL(MOE_ERR_ARG, "null argument");
+  if (layer < 0 || layer >= c->cfg.L) MOE_FAIL(MOE_ERR_SHAPE, "layer %d outside [0, %d)", layer, c->cfg.L);
+  if (T < 1) MOE_FAIL(MOE_ERR_SHAPE, "T=%d < 1", T);
+  const int E = c->cfg.E, k = c->cfg.k;
+  const int rows = (E + k - 1) / k;
+  if (rows > c->cfg.T_max)
+    MOE_FAIL(MOE_ERR_SHAPE, "on-demand loading passes a layer's expert set as %d rows of k; T_max is %d", rows,
+             c->cfg.T_max);
+  if (!out->uniq || !out->is_hit || !out->fill_id || !out->fill_slot || !out->fill_evicted || !out->host_id ||
+      !out->counts)
+    MOE_FAIL(MOE_ERR_ARG, "a moe_step_out buffer is NULL");
+  const int64_t P = (int64_t)T * k;
+  prefill_set_kernel<<<1, 1024, 0, stream>>>(c->dev, ids, P, rows * k);
+  MOE_LAUNCHED();
+  StepArgs a{};
+  a.ids = c->dev.set_list;
+  a.layer = layer;
+  a.T = rows;
+  a.k = k;
+  a.U_max = c->U_max;
+  a.fill_all = 1;
+  a.out = *out;
+  a.out.pick_slot = c->dev.set_list + kUMax;   // picks of the set itself: not the caller's
+  cache_decide_kernel<0><<<1, kDT, c->lds_bytes, stream>>>(c->dev, a);
+  MOE_LAUNCHED();
+  const int64_t blocks = (P + 255) / 256 < 2048 ? (P + 255) / 256 : 2048;
+  prefill_pick_kernel<<<(unsigned)blocks, 256, 0, stream>>>(c->dev, ids, P, layer, pick_slot);
+  MOE_LAUNCHED();
+  if (!(flags & MOE_STEP_NO_COPY))
+    return launch_fill(c, out->fill_id, out->fill_slot, out->counts + MOE_CNT_FILL, stream);
+  return MOE_OK;
 }
 
 extern "C" moe_status moe_cache_read_state(moe_cache_t c, int32_t* slot_id, uint64_t* stamp, int32_t* id_slot,
@@ -876,30 +1021,45 @@ extern "C" moe_status moe_cache_destroy(moe_cache_t c) {
   return MOE_OK;
 }
 
-// ================================================================ prefill double buffer
+// ================================================================ prefill full-layer buffers
 struct moe_prefill {
   moe_cache* c;
   int first;               // first reserved slot
   int E;
-  int buf_layer[2];
-  hipEvent_t ready[2], released[2];
-  bool released_recorded[2];
+  int D;                   // buffers: layer l uses buffer l % D
+  uint64_t n_loads;        // prefetches so far (load order of the buffers)
+  std::vector<int> buf_layer;
+  std::vector<uint64_t> buf_load;
+  std::vector<hipEvent_t> ready, released;
+  std::vector<char> released_recorded;
+  ~moe_prefill() {
+    for (hipEvent_t e : ready) if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : released) if (e) (void)hipEventDestroy(e);
+  }
 };
 
-extern "C" moe_status moe_prefill_create(moe_cache_t c, moe_prefill_t* out) {
+extern "C" moe_status moe_prefill_create_ring(moe_cache_t c, int32_t depth, moe_prefill_t* out) {
   clear_error();
   if (!c || !out) MOE_FAIL(MOE_ERR_ARG, "null argument");
   *out = nullptr;
+  if (depth < 2 || depth > kMaxRing) MOE_FAIL(MOE_ERR_SHAPE, "ring depth %d outside [2, %d]", depth, kMaxRing);
   if (c->has_prefill) MOE_FAIL(MOE_ERR_STATE, "the cache already has a prefill pool");
   const int E = c->cfg.E;
-  if (2 * E > c->cfg.C) MOE_FAIL(MOE_ERR_NO_SPACE, "two full-layer buffers need %d slots; the pool has %d", 2 * E, c->cfg.C);
+  if ((int64_t)depth * E > c->cfg.C)
+    MOE_FAIL(MOE_ERR_NO_SPACE, "%d full-layer buffers need %lld slots; the pool has %d", depth,
+             (long long)depth * E, c->cfg.C);
   moe_prefill* p = new moe_prefill();
   p->c = c;
   p->E = E;
-  p->first = c->cfg.C - 2 * E;
-  for (int b = 0; b < 2; ++b) {
-    p->buf_layer[b] = -1;
-    p->released_recorded[b] = false;
+  p->D = depth;
+  p->n_loads = 0;
+  p->first = c->cfg.C - depth * E;
+  p->buf_layer.assign(depth, -1);
+  p->buf_load.assign(depth, 0);
+  p->ready.assign(depth, nullptr);
+  p->released.assign(depth, nullptr);
+  p->released_recorded.assign(depth, 0);
+  for (int b = 0; b < depth; ++b) {
     hipError_t e1 = hipEventCreateWithFlags(&p->ready[b], hipEventDisableTiming);
     hipError_t e2 = hipEventCreateWithFlags(&p->released[b], hipEventDisableTiming);
     if (e1 != hipSuccess || e2 != hipSuccess) {
@@ -907,13 +1067,21 @@ extern "C" moe_status moe_prefill_create(moe_cache_t c, moe_prefill_t* out) {
       MOE_FAIL(MOE_ERR_HIP, "hipEventCreate failed");
     }
   }
-  cache_mark_kernel<<<(2 * E + 255) / 256, 256, 0, 0>>>(c->dev, p->first, 2 * E, -2);
+  cache_mark_kernel<<<(depth * E + 255) / 256, 256, 0, 0>>>(c->dev, p->first, depth * E, -2);
   cache_order_kernel<<<1, 1024, 0, 0>>>(c->dev);
-  MOE_LAUNCHED();
-  MOE_HIP(hipDeviceSynchronize());
+  hipError_t e = hipGetLastError();
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e != hipSuccess) {
+    delete p;
+    MOE_FAIL(MOE_ERR_HIP, "reserving the buffers: %s", hipGetErrorString(e));
+  }
   c->has_prefill = true;
   *out = p;
   return MOE_OK;
+}
+
+extern "C" moe_status moe_prefill_create(moe_cache_t c, moe_prefill_t* out) {
+  return moe_prefill_create_ring(c, 2, out);
 }
 
 extern "C" moe_status moe_prefill_prefetch(moe_prefill_t p, int32_t layer, hipStream_t copy_stream) {
@@ -921,7 +1089,7 @@ extern "C" moe_status moe_prefill_prefetch(moe_prefill_t p, int32_t layer, hipSt
   if (!p) MOE_FAIL(MOE_ERR_ARG, "pool is NULL");
   moe_cache* c = p->c;
   if (layer < 0 || layer >= c->cfg.L) MOE_FAIL(MOE_ERR_SHAPE, "layer %d outside [0, %d)", layer, c->cfg.L);
-  const int b = layer & 1;
+  const int b = layer % p->D;
   if (p->released_recorded[b]) MOE_HIP(hipStreamWaitEvent(copy_stream, p->released[b], 0));
   const int E = p->E;
   const int slot0 = p->first + b * E;
@@ -942,15 +1110,16 @@ extern "C" moe_status moe_prefill_prefetch(moe_prefill_t p, int32_t layer, hipSt
   }
   MOE_HIP(hipEventRecord(p->ready[b], copy_stream));
   p->buf_layer[b] = layer;
+  p->buf_load[b] = ++p->n_loads;
   return MOE_OK;
 }
 
 extern "C" moe_status moe_prefill_acquire(moe_prefill_t p, int32_t layer, hipStream_t compute, moe_slots* view) {
   clear_error();
   if (!p || !view) MOE_FAIL(MOE_ERR_ARG, "null argument");
-  const int b = layer & 1;
-  if (layer < 0 || p->buf_layer[b] != layer)
-    MOE_FAIL(MOE_ERR_STATE, "layer %d was not prefetched into buffer %d", layer, b);
+  if (layer < 0) MOE_FAIL(MOE_ERR_STATE, "layer %d was not prefetched", layer);
+  const int b = layer % p->D;
+  if (p->buf_layer[b] != layer) MOE_FAIL(MOE_ERR_STATE, "layer %d was not prefetched into buffer %d", layer, b);
   MOE_HIP(hipStreamWaitEvent(compute, p->ready[b], 0));
   moe_cache* c = p->c;
   const int slot0 = p->first + b * p->E;
@@ -970,27 +1139,50 @@ extern "C" moe_status moe_prefill_acquire(moe_prefill_t p, int32_t layer, hipStr
 extern "C" moe_status moe_prefill_release(moe_prefill_t p, int32_t layer, hipStream_t compute) {
   clear_error();
   if (!p) MOE_FAIL(MOE_ERR_ARG, "pool is NULL");
-  const int b = layer & 1;
-  if (layer < 0 || p->buf_layer[b] != layer) MOE_FAIL(MOE_ERR_STATE, "layer %d does not own buffer %d", layer, b);
+  if (layer < 0) MOE_FAIL(MOE_ERR_STATE, "layer %d does not own a buffer", layer);
+  const int b = layer % p->D;
+  if (p->buf_layer[b] != layer) MOE_FAIL(MOE_ERR_STATE, "layer %d does not own buffer %d", layer, b);
   MOE_HIP(hipEventRecord(p->released[b], compute));
-  p->released_recorded[b] = true;
+  p->released_recorded[b] = 1;
   return MOE_OK;
+}
+
+// Ends the pool: keep = the buffers' layers become residents, else the
+// buffers return to the LRU empty.
+static moe_status prefill_end(moe_prefill_t p, bool keep, hipStream_t stream) {
+  moe_cache* c = p->c;
+  MOE_HIP(hipDeviceSynchronize());   // every prefetch has landed and no kernel reads the buffers
+  AdoptArgs a{};
+  a.first = p->first;
+  a.n_buf = p->D;
+  std::vector<std::pair<uint64_t, int>> loads;
+  for (int b = 0; b < p->D; ++b) {
+    a.lay[b] = keep ? p->buf_layer[b] : -1;
+    if (a.lay[b] >= 0) loads.push_back({p->buf_load[b], b});
+  }
+  std::sort(loads.begin(), loads.end());
+  for (size_t i = 0; i < loads.size(); ++i) a.pos[loads[i].second] = (int)i;
+  if (keep) {
+    cache_adopt_kernel<<<1, 1024, 0, stream>>>(c->dev, a);
+  } else {
+    cache_mark_kernel<<<(p->D * p->E + 255) / 256, 256, 0, stream>>>(c->dev, p->first, p->D * p->E, -1);
+  }
+  cache_order_kernel<<<1, 1024, 0, stream>>>(c->dev);
+  MOE_LAUNCHED();
+  MOE_HIP(hipStreamSynchronize(stream));
+  c->has_prefill = false;
+  delete p;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_prefill_finish(moe_prefill_t p, hipStream_t stream) {
+  clear_error();
+  if (!p) MOE_FAIL(MOE_ERR_ARG, "pool is NULL");
+  return prefill_end(p, true, stream);
 }
 
 extern "C" moe_status moe_prefill_destroy(moe_prefill_t p, hipStream_t stream) {
   clear_error();
   if (!p) return MOE_OK;
-  moe_cache* c = p->c;
-  MOE_HIP(hipDeviceSynchronize());
-  cache_mark_kernel<<<(2 * p->E + 255) / 256, 256, 0, stream>>>(c->dev, p->first, 2 * p->E, -1);
-  cache_order_kernel<<<1, 1024, 0, stream>>>(c->dev);
-  MOE_LAUNCHED();
-  MOE_HIP(hipStreamSynchronize(stream));
-  for (int b = 0; b < 2; ++b) {
-    (void)hipEventDestroy(p->ready[b]);
-    (void)hipEventDestroy(p->released[b]);
-  }
-  c->has_prefill = false;
-  delete p;
-  return MOE_OK;
+  return prefill_end(p, false, stream);
 }

@@ -84,12 +84,21 @@ class Harness:
             self.orc.seed(list(seed_ids))
         self.copy = copy
 
-    def step(self, layer, ids):
+    def step(self, layer, ids, fill_all=False):
         T = ids.shape[0]
-        self.cache.step(layer, dev(ids.astype(np.int32)), self.out, copy=self.copy)
-        r = self.orc.step(layer, ids)
+        self.cache.step(layer, dev(ids.astype(np.int32)), self.out, copy=self.copy, fill_all=fill_all)
+        r = self.orc.step(layer, ids, fill_all=fill_all)
         self.compare(r, T)
         return r
+
+    def prefill_load(self, layer, ids):
+        """On-demand loading of a batch of any size: the same decisions as a
+        step with every miss filled; the picks come back in their own array."""
+        pick = self.cache.prefill_load(layer, dev(ids.astype(np.int32)), self.out, copy=self.copy)
+        r = self.orc.step(layer, ids, fill_all=True)
+        self.compare(r, 0)
+        assert np.array_equal(pick.cpu().numpy(), r.pick_slot)
+        return r, pick
 
     def route_step(self, layer, logits):
         """Router + step in one launch; checks ids and weights against the
@@ -121,7 +130,8 @@ class Harness:
         assert list(o.fill_evicted.cpu().numpy()[:q]) == r.fill_evicted
         assert np.all(o.fill_id.cpu().numpy()[q:U] == -1)
         assert list(o.host_id.cpu().numpy()[:m - q]) == r.host_id
-        assert np.array_equal(o.pick_slot.cpu().numpy()[:T * self.k], r.pick_slot.reshape(-1))
+        if T:
+            assert np.array_equal(o.pick_slot.cpu().numpy()[:T * self.k], r.pick_slot.reshape(-1))
 
     def compare_tables(self):
         slot_id, stamp, id_slot, tick, counters = self.cache.read_state()
