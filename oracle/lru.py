@@ -31,7 +31,8 @@ Readings adopted where the pages are silent (all listed in the design notes):
 * on-demand loading (no room for the full-layer buffers) fills every miss
   that finds a non-hit slot: q* = m instead of the bandwidth split;
 * at the end of prefill the experts the buffers hold become residents (see
-  finish_prefill for the order of their stamps).
+  finish_prefill for the order of their stamps);
+* a resize keeps the most recent residents that fit (see resize).
 """
 import numpy as np
 
@@ -121,6 +122,43 @@ class ExpertCache:
                 self.id_slot[lid] = s
                 self.ts[s] = stamp
         self.tick += 1
+
+    def resize(self, new_C: int):
+        """Change the number of slots at a safe point between layer calls.
+
+        [FTK] (safe-point paragraph) and [FT] (third challenge): the memory
+        budget is re-split at run time without a restart; the host pool is
+        the ground truth, so a smaller GPU cache changes no output.  Readings:
+        no slot may be reserved; the cache keeps its min(residents, new_C)
+        most recent residents (largest (stamp, slot)) with their stamps; a
+        kept resident whose slot is below new_C stays in it; the other kept
+        residents move, in ascending order of their old slots, to the free
+        slots below new_C (empty, or holding a resident that is dropped), in
+        ascending order; slots added by growth are empty; tick and counters
+        are unchanged.  Returns the moves as [(old slot, new slot)].
+        """
+        if new_C <= 0:
+            raise ValueError("bad size")
+        if RESERVED in self.slot_id:
+            raise ValueError("slots are reserved")
+        res = sorted((self.ts[s], s) for s in range(self.C) if self.slot_id[s] >= 0)
+        keep = set(s for _, s in res[len(res) - min(len(res), new_C):])
+        stay = [s for s in range(min(self.C, new_C)) if s in keep]
+        movers = sorted(s for s in keep if s >= new_C)
+        free = [s for s in range(new_C) if s not in keep]
+        moves = list(zip(movers, free))
+        slot_id = [EMPTY] * new_C
+        ts = [0] * new_C
+        for s in stay:
+            slot_id[s], ts[s] = self.slot_id[s], self.ts[s]
+        for src, dst in moves:
+            slot_id[dst], ts[dst] = self.slot_id[src], self.ts[src]
+        self.id_slot = [EMPTY] * (self.L * self.E)
+        for s, lid in enumerate(slot_id):
+            if lid >= 0:
+                self.id_slot[lid] = s
+        self.slot_id, self.ts, self.C = slot_id, ts, new_C
+        return moves
 
     # -- one layer call --------------------------------------------------------
     def step(self, layer: int, ids, copy: bool = True, fill_all: bool = False) -> StepResult:

@@ -281,3 +281,57 @@ def test_finish_with_nothing_loaded_releases_the_buffers():
     oc.finish_prefill(1, 2, [])
     slot_id, ts, _, _ = oc.tables()
     assert slot_id.tolist() == [5] + [-1] * 8 and ts.tolist() == [1] + [0] * 8
+
+
+# ---------------------------------------------------------------- resize at a safe point
+@pytest.mark.parametrize("seed", range(12))
+def test_resize_matches_textbook(seed):
+    """Shrinking keeps the most recent residents that fit, growing adds room;
+    the recency order survives, and steps after it agree with a textbook
+    LRU of the new capacity holding the same entries in the same order."""
+    rng = np.random.default_rng(500 + seed)
+    L, E, T, k = 2, 5, 2, 2
+    C = int(rng.integers(2, 9))
+    oc = lru.ExpertCache(L, E, C, 1, 1)
+    tb = TextbookLRU(C, [])
+    for n_resize in range(4):
+        for layer, ids in _random_trace(rng, 30, L, E, T, k):
+            r = oc.step(layer, ids, fill_all=True)
+            uniq = sorted(set((layer * E + ids).reshape(-1).tolist()))
+            hits, fills, host, evicted = tb.step(uniq, lambda m: m)
+            assert (r.hits, r.fill_id, r.host_id, r.fill_evicted) == (hits, fills, host, evicted)
+        new_C = int(rng.integers(1, 10))
+        moves = oc.resize(new_C)
+        keys = list(tb.od.keys())
+        tb = TextbookLRU(new_C, keys[max(0, len(keys) - new_C):])
+        slot_id, ts, id_slot, _ = oc.tables()
+        assert len(slot_id) == new_C
+        occ = sorted((int(ts[s]), s) for s in range(new_C) if slot_id[s] >= 0)
+        assert [int(slot_id[s]) for _, s in occ] == list(tb.od.keys())
+        for s, i in enumerate(slot_id):
+            if i >= 0:
+                assert id_slot[i] == s
+        assert (id_slot >= 0).sum() == (slot_id >= 0).sum()
+        assert all(dst < new_C <= src for src, dst in moves)
+
+
+def test_resize_by_hand():
+    """Slots 0-5 hold ids 10..15 with recency 12 < 14 < 10 < 15 < 11 < 13
+    (stamps 3, 5, 1, 6, 2, 4 in slot order); shrink to 3 keeps the three most
+    recent: 15 (slot 5), 11 (slot 1), 13 (slot 3) -> 11 stays in slot 1,
+    13 moves to slot 0, 15 to slot 2."""
+    oc = lru.ExpertCache(2, 8, 6, 1, 1)
+    oc.slot_id = [10, 11, 12, 13, 14, 15]
+    oc.ts = [3, 5, 1, 6, 2, 4]
+    oc.id_slot = [-1] * 16
+    for s, i in enumerate(oc.slot_id):
+        oc.id_slot[i] = s
+    moves = oc.resize(3)
+    assert moves == [(3, 0), (5, 2)]
+    slot_id, ts, id_slot, _ = oc.tables()
+    assert slot_id.tolist() == [13, 11, 15] and ts.tolist() == [6, 5, 4]
+    moves = oc.resize(5)                             # grow: nothing moves, two empty slots
+    assert moves == [] and oc.slot_id == [13, 11, 15, -1, -1] and oc.ts == [6, 5, 4, 0, 0]
+    with pytest.raises(ValueError):
+        oc.reserve(3, 2)
+        oc.resize(4)
