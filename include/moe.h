@@ -266,6 +266,29 @@ moe_status moe_cache_error(moe_cache_t c, int32_t* code, hipStream_t stream);
 moe_status moe_cache_destroy(moe_cache_t c);
 
 /*
+ * Change the cache's slot count at a safe point (between layer calls, no
+ * prefill pool alive) ([FTK] safe-point paragraph: the memory budget between
+ * KV cache and expert cache is re-split at run time, and since the host pool
+ * is the ground truth a smaller GPU cache changes no output; [FT] third
+ * challenge: the budget shrinks or grows without a restart).  The new
+ * capacity is slots->n_slots (same weight type, H and I).  The cache keeps
+ * its min(residents, new C) most recent residents with their stamps: one in
+ * a slot below the new C stays there, the others move, in ascending order of
+ * their old slots, to the free slots below the new C in ascending order
+ * (evicting the least recently used); slots added by growth are empty; tick
+ * and counters carry over.  slots: either every bank at the same address as
+ * now (in place: shrink, or grow into banks allocated that large) or every
+ * bank in new memory that does not overlap the old (kept experts are copied
+ * there).  dev_ws: a new workspace of moe_cache_workspace_bytes for the new
+ * configuration, not overlapping the current one; afterwards the cache uses
+ * it and the old workspace (and old banks, if moved) may be freed.
+ * Synchronises `stream`; not capturable.  On MOE_ERR_HIP the cache must be
+ * destroyed.
+ */
+moe_status moe_cache_resize(moe_cache_t c, const moe_slots* slots, void* dev_ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/*
  * Pack n experts from row-major device matrices into the brick format of the
  * slot pool (see moe_slots): w_gate, w_up [n][I][H] and w_down [n][H][I]
  * (BF16 bits or E4M3 codes) -> w_gate_up [n][2*I*H], w_down_packed [n][H*I].

@@ -35,6 +35,7 @@ EXPORTS = [
     "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_prefill_create_ring", "moe_prefill_finish", "moe_cache_prefill_load",
+    "moe_cache_resize",
     "moe_e4m3_to_bf16", "moe_pack_weights", "moe_stream_read",
     "moe_host_exec_create", "moe_host_exec_destroy", "moe_host_exec_simd", "moe_host_forward",
     "moe_host_forward_enqueue", "moe_host_exec_status", "moe_host_exec_stats",
@@ -100,6 +101,7 @@ _sig = {
     "moe_prefill_create_ring": (_i32, [_vp, _i32, _P(_vp)]),
     "moe_prefill_finish": (_i32, [_vp, _vp]),
     "moe_cache_prefill_load": (_i32, [_vp, _i32, _vp, _i32, _u32, _P(StepOutC), _vp, _vp]),
+    "moe_cache_resize": (_i32, [_vp, _P(Slots), _vp, _sz, _vp]),
     "moe_e4m3_to_bf16": (_i32, [_vp, _vp, ctypes.c_int64, _vp]),
     "moe_pack_weights": (_i32, [_i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_host_exec_create": (_i32, [_i32, _u32, _P(_vp)]),
@@ -164,6 +166,17 @@ class SlotPool:
             self.s_gate = self.s_up = self.s_down = None
         self.c = Slots(wtype, H, I, n_slots, *[None if t is None else t.data_ptr() for t in
                                                 (self.w_gu, self.w_down, self.s_gate, self.s_up, self.s_down)])
+
+    def prefix(self, n):
+        """The first n slots of this pool, same memory (an in-place shrink)."""
+        v = SlotPool.__new__(SlotPool)
+        v.n_slots, v.H, v.I, v.wtype = n, self.H, self.I, self.wtype
+        v.w_gu, v.w_down = self.w_gu[:n], self.w_down[:n]
+        v.s_gate, v.s_up, v.s_down = [None if t is None else t[:n] for t in (self.s_gate, self.s_up, self.s_down)]
+        v.c = Slots(self.wtype, self.H, self.I, n, *[None if t is None else t.data_ptr() for t in
+                                                    (v.w_gu, v.w_down, v.s_gate, v.s_up, v.s_down)])
+        v.base = getattr(self, "base", self)
+        return v
 
     def banks(self):
         out = [self.w_gu, self.w_down]
@@ -285,6 +298,16 @@ class Cache:
         code = ctypes.c_int32(0)
         _check(_lib.moe_cache_error(self.h, ctypes.byref(code), _stream(stream)), "moe_cache_error")
         return code.value
+
+    def resize(self, slots: SlotPool, stream=None):
+        """Safe-point resize to slots.n_slots slots (same memory or new banks)."""
+        cfg = CacheCfg(self.cfg.L, self.cfg.E, self.cfg.k, self.cfg.T_max, slots.n_slots, self.cfg.bp, self.cfg.bh)
+        nbytes = ctypes.c_size_t(0)
+        _check(_lib.moe_cache_workspace_bytes(ctypes.byref(cfg), ctypes.byref(nbytes)), "workspace_bytes")
+        ws = torch.empty((nbytes.value,), dtype=torch.uint8, device="cuda")
+        _check(_lib.moe_cache_resize(self.h, ctypes.byref(slots.c), _ptr(ws), nbytes.value, _stream(stream)),
+               "moe_cache_resize")
+        self.cfg, self.ws, self.slots = cfg, ws, slots
 
     def destroy(self):
         if self.h:

@@ -22,6 +22,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 #include <utility>
 #include <vector>
 
@@ -641,6 +642,128 @@ __global__ __launch_bounds__(1024) void cache_adopt_kernel(CacheDev cd, AdoptArg
   }
 }
 
+// ---------------------------------------------------------------- resize
+// Tables of the resized cache `nd` (Cn slots, fresh workspace) from those of
+// `od` (C slots; no slot reserved): the min(residents, Cn) most recent
+// residents (the tail of od's LRU order, where every resident follows every
+// empty slot) are kept with their stamps; one below Cn stays in its slot, the
+// others move, ascending by old slot, to the free slots below Cn, ascending.
+// The copies to make are listed in nd.seed_list: sources [0, Cn),
+// destinations [Cn, 2Cn), count at 2Cn; every kept resident when copy_all (the
+// banks move to new memory), else only the movers.  One workgroup; each
+// thread owns a contiguous chunk of slot numbers, so ranks are chunk prefix
+// sums.
+__global__ __launch_bounds__(1024) void cache_resize_kernel(CacheDev od, CacheDev nd, int copy_all) {
+  __shared__ uint8_t keep[kCMax];
+  __shared__ uint16_t free_list[kCMax];
+  __shared__ int c_free[1024], c_list[1024], c_move[1024];
+  __shared__ int n_res;
+  const int tid = threadIdx.x, C = od.C, Cn = nd.C;
+  const int S = C > Cn ? C : Cn;
+  const int ch = (S + 1023) / 1024;
+  const int s0 = tid * ch < S ? tid * ch : S;
+  const int s1 = s0 + ch < S ? s0 + ch : S;
+  if (tid == 0) n_res = 0;
+  for (int x = tid; x < S; x += 1024) keep[x] = 0;
+  __syncthreads();
+  int nr = 0;
+  for (int x = tid; x < C; x += 1024) nr += od.slot_id[x] >= 0 ? 1 : 0;
+  atomicAdd(&n_res, nr);
+  __syncthreads();
+  const int n_ord = *od.n_ord;
+  const int n_keep = n_res < Cn ? n_res : Cn;
+  for (int i = n_ord - n_keep + tid; i < n_ord; i += 1024) keep[od.order[i]] = 1;
+  __syncthreads();
+  int nf = 0, nl = 0, nm = 0;
+  for (int x = s0; x < s1; ++x) {
+    const bool kp = x < C && keep[x];
+    nf += (x < Cn && !kp) ? 1 : 0;
+    nm += (kp && x >= Cn) ? 1 : 0;
+    nl += (kp && (copy_all || x >= Cn)) ? 1 : 0;
+  }
+  c_free[tid] = nf;
+  c_list[tid] = nl;
+  c_move[tid] = nm;
+  __syncthreads();
+  if (tid == 0) {
+    int af = 0, al = 0, am = 0;
+    for (int t = 0; t < 1024; ++t) {
+      const int f = c_free[t], l = c_list[t], m = c_move[t];
+      c_free[t] = af;
+      c_list[t] = al;
+      c_move[t] = am;
+      af += f;
+      al += l;
+      am += m;
+    }
+    nd.seed_list[2 * Cn] = al;
+  }
+  __syncthreads();
+  int rf = c_free[tid];
+  for (int x = s0; x < s1; ++x)
+    if (x < Cn && !(x < C && keep[x])) free_list[rf++] = (uint16_t)x;
+  for (int x = tid; x < Cn; x += 1024) {
+    nd.slot_id[x] = -1;
+    nd.stamp[x] = 0;
+  }
+  for (size_t i = tid; i < (size_t)od.L * od.E; i += 1024) nd.id_slot[i] = -1;
+  __syncthreads();
+  int rl = c_list[tid], rm = c_move[tid];
+  for (int x = s0; x < s1; ++x) {
+    if (!(x < C && keep[x])) continue;
+    const int dst = x < Cn ? x : (int)free_list[rm++];
+    const int id = od.slot_id[x];
+    nd.slot_id[dst] = id;
+    nd.stamp[dst] = od.stamp[x];
+    nd.id_slot[id] = dst;
+    if (copy_all || x >= Cn) {
+      nd.seed_list[rl] = x;
+      nd.seed_list[Cn + rl] = dst;
+      ++rl;
+    }
+  }
+  if (tid == 0) {
+    *nd.tick = *od.tick;
+    for (int i = 0; i < 8; ++i) nd.counters[i] = od.counters[i];
+    *nd.error = *od.error;
+  }
+}
+
+// Copy every bank of each listed slot from the old banks to the new ones.
+// Sources and destinations are distinct slots (destinations were free), so
+// the copies are independent.
+struct MoveArgs {
+  const int32_t* src;
+  const int32_t* dst;
+  const int32_t* n;
+  int nb;
+  const char* from[5];
+  char* to[5];
+  uint64_t bytes[5];
+};
+
+__global__ __launch_bounds__(256) void slot_move_kernel(MoveArgs a) {
+  const int n = *a.n;
+  const size_t gtid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const size_t gsz = (size_t)gridDim.x * blockDim.x;
+  for (int f = 0; f < n; ++f) {
+    const size_t s = (size_t)a.src[f], d = (size_t)a.dst[f];
+    for (int b = 0; b < a.nb; ++b) {
+      const char* src = a.from[b] + s * a.bytes[b];
+      char* dst = a.to[b] + d * a.bytes[b];
+      if ((a.bytes[b] & 15) == 0) {
+        const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
+        u32x4* d4 = reinterpret_cast<u32x4*>(dst);
+        for (size_t i = gtid; i < (a.bytes[b] >> 4); i += gsz) d4[i] = __builtin_nontemporal_load(s4 + i);
+      } else {
+        const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src);
+        uint32_t* d1 = reinterpret_cast<uint32_t*>(dst);
+        for (size_t i = gtid; i < (a.bytes[b] >> 2); i += gsz) d1[i] = s1[i];
+      }
+    }
+  }
+}
+
 }  // namespace moe
 
 // ================================================================ host side
@@ -654,6 +777,8 @@ struct moe_cache {
   int lds_bytes;
   int U_max;
   bool has_prefill;
+  char* ws;                // the caller's workspace and its used bytes
+  size_t ws_used;
 };
 
 using namespace moe;
@@ -680,6 +805,45 @@ static WsLayout ws_layout(const moe_cache_cfg* c, int nb) {
   w.host_tab = off; off = align_up(off + 8 * (size_t)nb * LE, 256);
   w.total = off;
   return w;
+}
+
+static CacheDev make_dev(char* ws, const WsLayout& L, const moe_cache_cfg* cfg) {
+  CacheDev d{};
+  d.id_slot = (int32_t*)(ws + L.id_slot);
+  d.slot_id = (int32_t*)(ws + L.slot_id);
+  d.stamp = (uint64_t*)(ws + L.stamp);
+  d.order = (int32_t*)(ws + L.order);
+  d.n_ord = (int32_t*)(ws + L.n_ord);
+  d.tick = (uint64_t*)(ws + L.tick);
+  d.counters = (uint64_t*)(ws + L.counters);
+  d.error = (int32_t*)(ws + L.error);
+  d.seed_list = (int32_t*)(ws + L.seed);
+  d.set_list = (int32_t*)(ws + L.set);
+  d.host_tab = (const uint64_t*)(ws + L.host_tab);
+  d.L = cfg->L;
+  d.E = cfg->E;
+  d.C = cfg->C;
+  d.bp = cfg->bp;
+  d.bh = cfg->bh;
+  return d;
+}
+
+// The decision kernels' dynamic-LDS limit is a per-function attribute shared
+// by every cache of the process: raise it to the largest size asked for.
+static std::mutex g_lds_mu;
+static int g_decide_lds = 0;
+static hipError_t ensure_decide_lds(int bytes) {
+  std::lock_guard<std::mutex> lk(g_lds_mu);
+  if (bytes <= g_decide_lds) return hipSuccess;
+  const void* fns[] = {(const void*)cache_decide_kernel<0>, (const void*)cache_decide_kernel<1>,
+                       (const void*)cache_decide_kernel<2>, (const void*)cache_decide_kernel<4>,
+                       (const void*)cache_decide_kernel<8>, (const void*)cache_decide_kernel<16>};
+  for (const void* fn : fns) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e != hipSuccess) return e;
+  }
+  g_decide_lds = bytes;
+  return hipSuccess;
 }
 
 static moe_status check_cfg(const moe_cache_cfg* c) {
@@ -785,30 +949,11 @@ extern "C" moe_status moe_cache_create(const moe_cache_cfg* cfg, const moe_slots
   c->lds_bytes = lds_dyn;
   c->U_max = cfg->T_max * cfg->k < cfg->E ? cfg->T_max * cfg->k : cfg->E;
   c->has_prefill = false;
-  CacheDev& d = c->dev;
-  d.id_slot = (int32_t*)(ws + L.id_slot);
-  d.slot_id = (int32_t*)(ws + L.slot_id);
-  d.stamp = (uint64_t*)(ws + L.stamp);
-  d.order = (int32_t*)(ws + L.order);
-  d.n_ord = (int32_t*)(ws + L.n_ord);
-  d.tick = (uint64_t*)(ws + L.tick);
-  d.counters = (uint64_t*)(ws + L.counters);
-  d.error = (int32_t*)(ws + L.error);
-  d.seed_list = (int32_t*)(ws + L.seed);
-  d.set_list = (int32_t*)(ws + L.set);
-  d.host_tab = (const uint64_t*)(ws + L.host_tab);
-  d.L = cfg->L;
-  d.E = cfg->E;
-  d.C = cfg->C;
-  d.bp = cfg->bp;
-  d.bh = cfg->bh;
-
-  const void* decide_fns[] = {(const void*)cache_decide_kernel<0>, (const void*)cache_decide_kernel<1>,
-                              (const void*)cache_decide_kernel<2>, (const void*)cache_decide_kernel<4>,
-                              (const void*)cache_decide_kernel<8>, (const void*)cache_decide_kernel<16>};
-  hipError_t e = hipSuccess;
-  for (const void* fn : decide_fns)
-    if (e == hipSuccess) e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds_dyn);
+  c->ws = ws;
+  c->ws_used = L.total;
+  c->dev = make_dev(ws, L, cfg);
+  const CacheDev& d = c->dev;
+  hipError_t e = ensure_decide_lds(lds_dyn);
   if (e != hipSuccess) {
     delete c;
     MOE_FAIL(MOE_ERR_HIP, "hipFuncSetAttribute: %s", hipGetErrorString(e));
@@ -1018,6 +1163,76 @@ extern "C" moe_status moe_cache_destroy(moe_cache_t c) {
   if (!c) return MOE_OK;
   if (c->has_prefill) MOE_FAIL(MOE_ERR_STATE, "destroy the prefill pool first");
   delete c;
+  return MOE_OK;
+}
+
+extern "C" moe_status moe_cache_resize(moe_cache_t c, const moe_slots* slots, void* dev_ws, size_t ws_bytes,
+                                       hipStream_t stream) {
+  clear_error();
+  if (!c || !dev_ws) MOE_FAIL(MOE_ERR_ARG, "null argument");
+  moe_status st = check_slots(slots);
+  if (st) return st;
+  if (c->has_prefill) MOE_FAIL(MOE_ERR_STATE, "cannot resize while a prefill pool holds slots");
+  if (slots->wtype != c->slots.wtype || slots->H != c->slots.H || slots->I != c->slots.I)
+    MOE_FAIL(MOE_ERR_ARG, "the new slots must have the cache's weight type, H and I");
+  moe_cache_cfg ncfg = c->cfg;
+  ncfg.C = slots->n_slots;
+  if ((st = check_cfg(&ncfg))) return st;
+  if (reinterpret_cast<uintptr_t>(dev_ws) & 255) MOE_FAIL(MOE_ERR_ARG, "workspace must be 256-byte aligned");
+  const WsLayout L = ws_layout(&ncfg, 5);
+  if (ws_bytes < L.total) MOE_FAIL(MOE_ERR_NO_SPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
+  char* nws = (char*)dev_ws;
+  if (nws < c->ws + c->ws_used && c->ws < nws + L.total)
+    MOE_FAIL(MOE_ERR_ARG, "the new workspace overlaps the cache's current one");
+  int dev = 0, lds_max = 0;
+  MOE_HIP(hipGetDevice(&dev));
+  MOE_HIP(hipDeviceGetAttribute(&lds_max, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
+  const int lds_dyn = decide_lds_bytes(ncfg.C, ncfg.E);
+  if (lds_dyn + 32 * 1024 > lds_max)
+    MOE_FAIL(MOE_ERR_SHAPE, "C=%d needs %d B of LDS; device allows %d", ncfg.C, lds_dyn + 32 * 1024, lds_max);
+  // banks: all in place (same base) or all in new memory that does not overlap the old
+  const void* ob[5] = {c->slots.w_gate_up, c->slots.w_down, c->slots.s_gate, c->slots.s_up, c->slots.s_down};
+  const void* nbk[5] = {slots->w_gate_up, slots->w_down, slots->s_gate, slots->s_up, slots->s_down};
+  int same = 0;
+  for (int b = 0; b < c->nb; ++b) {
+    const char* o = (const char*)ob[b];
+    const char* n = (const char*)nbk[b];
+    if (o == n) {
+      ++same;
+      continue;
+    }
+    const size_t bo = (size_t)c->cfg.C * c->bb.b[b], bn = (size_t)ncfg.C * c->bb.b[b];
+    if (n < o + bo && o < n + bn) MOE_FAIL(MOE_ERR_ARG, "bank %d of the new slots overlaps the old one", b);
+  }
+  if (same != 0 && same != c->nb) MOE_FAIL(MOE_ERR_ARG, "move every bank or none");
+  const int copy_all = same == 0;
+
+  CacheDev nd = make_dev(nws, L, &ncfg);
+  MOE_HIP(ensure_decide_lds(lds_dyn));
+  const size_t LE = (size_t)c->cfg.L * c->cfg.E;
+  MOE_HIP(hipMemcpyAsync((void*)nd.host_tab, c->dev.host_tab, 8 * (size_t)c->nb * LE, hipMemcpyDeviceToDevice,
+                         stream));
+  cache_resize_kernel<<<1, 1024, 0, stream>>>(c->dev, nd, copy_all);
+  cache_order_kernel<<<1, 1024, 0, stream>>>(nd);
+  MoveArgs m{};
+  m.src = nd.seed_list;
+  m.dst = nd.seed_list + ncfg.C;
+  m.n = nd.seed_list + 2 * ncfg.C;
+  m.nb = c->nb;
+  for (int b = 0; b < c->nb; ++b) {
+    m.from[b] = (const char*)ob[b];
+    m.to[b] = (char*)nbk[b];
+    m.bytes[b] = c->bb.b[b];
+  }
+  slot_move_kernel<<<512, 256, 0, stream>>>(m);
+  MOE_LAUNCHED();
+  MOE_HIP(hipStreamSynchronize(stream));
+  c->cfg = ncfg;
+  c->slots = *slots;
+  c->dev = nd;
+  c->lds_bytes = lds_dyn;
+  c->ws = nws;
+  c->ws_used = L.total;
   return MOE_OK;
 }
 

@@ -1,0 +1,130 @@
+"""GPU tests of resizing the shared cache at a safe point (moe_cache_resize):
+tables and slot bytes bit for bit against the oracle cache across shrinks and
+growths, in place and into new memory, with decode steps between them; the
+layer output (GPU part plus the host executor's part) stays the float64
+oracle's MoE output before, across and after a resize."""
+import numpy as np
+import pytest
+import torch
+
+from harness import gen
+from oracle import ffn, numerics, route
+from tests.layer_setup import binding, dev, check_layer, Bf16Bank
+from tests.test_gpu_cache import Harness
+
+pytestmark = pytest.mark.gpu
+
+
+def _steps(h, rng, n, fill_all):
+    for _ in range(n):
+        layer = int(rng.integers(0, h.L))
+        T = int(rng.integers(1, h.T_max + 1))
+        ids = np.stack([rng.choice(h.E, size=h.k, replace=False) for _ in range(T)])
+        h.step(layer, ids, fill_all=fill_all)
+
+
+def _resize(h, pool):
+    h.cache.resize(pool)
+    moves = h.orc.resize(pool.n_slots)
+    h.pool = pool
+    h.compare_tables()
+    h.check_slot_bytes()
+    return moves
+
+
+@pytest.mark.parametrize("fill_all", [False, True])
+def test_resize_sequence(fill_all):
+    b = binding()
+    h = Harness(3, 8, 12, 3, 2, 900, 475, seed_ids=(3, 17), copy=True)
+    rng = np.random.default_rng(21 + fill_all)
+    H, I = h.pool.H, h.pool.I
+    _steps(h, rng, 30, fill_all)
+    moves = _resize(h, h.pool.prefix(7))                 # shrink in place
+    assert moves, "the shrink moved nothing: the case does not test moves"
+    _steps(h, rng, 30, fill_all)
+    _resize(h, b.SlotPool(15, H, I, b.W_BF16))           # grow into new memory
+    _steps(h, rng, 30, fill_all)
+    _resize(h, b.SlotPool(4, H, I, b.W_BF16))            # shrink into new memory
+    _steps(h, rng, 20, fill_all)
+    big = b.SlotPool(20, H, I, b.W_BF16)
+    _resize(h, big.prefix(9))                            # grow into new memory ...
+    _steps(h, rng, 20, fill_all)
+    _resize(h, big)                                      # ... then in place
+    _steps(h, rng, 30, fill_all)
+    _resize(h, big.prefix(20))                           # same size: nothing changes
+    h.compare_tables()
+    assert h.cache.error() == 0
+    h.cache.destroy()
+
+
+def test_resize_to_one_slot_and_back():
+    b = binding()
+    h = Harness(2, 8, 6, 2, 2, 900, 475, copy=True)
+    rng = np.random.default_rng(5)
+    _steps(h, rng, 10, True)
+    _resize(h, h.pool.prefix(1))
+    _steps(h, rng, 10, True)
+    _resize(h, b.SlotPool(9, h.pool.H, h.pool.I, b.W_BF16))
+    _steps(h, rng, 10, True)
+    h.cache.destroy()
+
+
+def test_resize_errors():
+    b = binding()
+    h = Harness(2, 8, 2 * 8 + 2, 2, 2, 900, 475)
+    H, I = h.pool.H, h.pool.I
+    pf = b.PrefillPool(h.cache)
+    with pytest.raises(b.MoeError) as ei:
+        h.cache.resize(h.pool.prefix(4))
+    assert ei.value.status == -6                          # MOE_ERR_STATE: prefill pool alive
+    pf.destroy()
+    with pytest.raises(b.MoeError) as ei:
+        h.cache.resize(b.SlotPool(4, H + 32, I, b.W_BF16))
+    assert ei.value.status == -1                          # MOE_ERR_ARG: other shape
+    mixed = b.SlotPool(4, H, I, b.W_BF16)
+    mixed.w_gu = h.pool.w_gu[:4]
+    mixed.c = b.Slots(b.W_BF16, H, I, 4, mixed.w_gu.data_ptr(), mixed.w_down.data_ptr(), None, None, None)
+    with pytest.raises(b.MoeError) as ei:
+        h.cache.resize(mixed)
+    assert ei.value.status == -1                          # MOE_ERR_ARG: one bank moved, one not
+    h.compare_tables()                                    # a refused resize leaves the cache as it was
+    h.cache.destroy()
+
+
+def test_outputs_unchanged_across_resizes():
+    """Decode steps with the host branch computing the host set: the layer
+    output is the oracle's at every step while the cache shrinks to two
+    slots and grows to fourteen."""
+    b = binding()
+    E, H, I, k, T = 16, 256, 128, 4, 3
+    bank = Bf16Bank(84, E, H, I)
+    pool = b.SlotPool(10, H, I, b.W_BF16)
+    host = b.HostPoolTables(bank.host, lambda i: i, E)
+    cache = b.Cache(1, E, k, T, pool, host, 527, 773)
+    ex = b.HostExec(4)
+    out = b.StepOut(T, k, E)
+    ws = b.forward_workspace(T, k, H, I, 14, b.FWD_DECODE)
+    rng = np.random.default_rng(9)
+    ids_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
+    w_d = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    big = b.SlotPool(14, H, I, b.W_BF16)
+    plan = {8: pool.prefix(2), 16: big, 24: big.prefix(5)}
+    n_host = 0
+    for s in range(32):
+        if s in plan:
+            cache.resize(plan[s])
+        x = gen.activations_bf16(rng, T, H)
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        cache.route_step(0, dev(lg), ids_d, w_d, out)
+        pick = out.pick_slot.view(T, k)
+        y_gpu = b.expert_forward(cache.slots.c, dev(x), pick, w_d, b.FWD_DECODE, ws)
+        pick_h, ids_h, w_h = pick.cpu(), ids_d.cpu(), w_d.cpu()
+        n_host += int((pick_h < 0).sum())
+        y_host = ex.forward(host, b.W_BF16, H, I, torch.from_numpy(x), ids_h, pick_h, w_h)
+        ids, w = route.topk_softmax(lg, k)
+        ref = ffn.moe_output(numerics.bf16_to_f64(x), ids, w, bank.expert64)
+        check_layer((y_gpu.cpu() + y_host).numpy(), ref, "step %d (C=%d)" % (s, cache.cfg.C))
+    assert n_host > 0
+    assert cache.error() == 0
+    ex.destroy()
+    cache.destroy()
