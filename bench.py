@@ -182,6 +182,7 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-host-exec", action="store_true", help="skip the host executor (CPU) throughput run")
     p.add_argument("--no-prefill", action="store_true")
+    p.add_argument("--no-resize", action="store_true", help="skip the safe-point resize timing")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 decode and FP8 double-buffered prefill runs")
     p.add_argument("--fp8-steps", type=int, default=64)
     p.add_argument("--fp8-warmup", type=int, default=32)
@@ -666,13 +667,14 @@ def run_prefill_fp8(b):
     compute = torch.cuda.current_stream()
     copy = torch.cuda.Stream()
 
-    def run(serial):
+    def run(serial, pf=pf, depth=2):
+        """One pass over the NL layers through `depth` full-layer buffers
+        (serial: each layer's copy waits for the previous layer's compute)."""
         ev = HipEvents(2 * NL)
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        pf.prefetch(0, copy)
-        if not serial:
-            pf.prefetch(1, copy)
+        for l in range(1 if serial else min(depth, NL)):
+            pf.prefetch(l, copy)
         for l in range(NL):
             if serial and l > 0:
                 copy.wait_stream(compute)
@@ -683,8 +685,8 @@ def run_prefill_fp8(b):
             b.expert_forward(view, xs[l], ids, w, b.FWD_PREFILL, ws, y=y)
             ev.record(2 * l + 1)
             pf.release(l, compute)
-            if not serial and l + 2 < NL:
-                pf.prefetch(l + 2, copy)
+            if not serial and l + depth < NL:
+                pf.prefetch(l + depth, copy)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         fwd = [ev.ms(2 * l, 2 * l + 1) / 1e3 for l in range(NL)]
@@ -694,18 +696,120 @@ def run_prefill_fp8(b):
     run(False)                                                       # warm-up
     wall_o, fwd_o = run(False)
     wall_s, fwd_s = run(True)
-    pf.destroy()
+    # hand-over: the two buffers' layers become the decode cache's residents
+    t0 = time.perf_counter()
+    pf.finish()
+    handover_ms = (time.perf_counter() - t0) * 1e3
+    survivors = int((cache.read_state()[0] >= 0).sum())
     cache.destroy()
+    del pool, cache, pf
+    torch.cuda.empty_cache()
+    variants = dict(handover=dict(ms=handover_ms, survivors=survivors,
+                                  what="moe_prefill_finish after the 4-layer pass: 2 x 256 experts registered"))
+    # a ring of three full-layer buffers
+    log("prefill fp8: ring of three buffers")
+    pool3 = b.SlotPool(3 * E, H, I, b.W_FP8_B128)
+    cache3 = b.Cache(NL, E, k, 1, pool3, host, 118, 475)
+    pf3 = b.PrefillPool(cache3, 3)
+    run(False, pf3, 3)
+    wall_r, fwd_r = run(False, pf3, 3)
+    pf3.destroy()
+    cache3.destroy()
+    del pool3, cache3, pf3
+    torch.cuda.empty_cache()
+    variants["ring3"] = dict(ms_per_layer=wall_r / NL * 1e3, forward_ms_per_layer=sum(fwd_r) / NL * 1e3)
+    # on-demand loading: a pool of 1.5 layers cannot hold two full-layer buffers
+    log("prefill fp8: on-demand loading into %d slots" % (3 * E // 2))
+    pool_d = b.SlotPool(3 * E // 2, H, I, b.W_FP8_B128)
+    cache_d = b.Cache(NL, E, k, (E + k - 1) // k, pool_d, host, 118, 475)
+    out_d = b.StepOut((E + k - 1) // k, k, E)
+    ws_d = b.forward_workspace(T, k, H, I, pool_d.n_slots, b.FWD_PREFILL)
+    pick_d = torch.empty((T, k), dtype=torch.int32, device="cuda")
+
+    def run_on_demand():
+        ev = HipEvents(3 * NL)
+        fills, host_picks = 0, 0
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for l in range(NL):
+            b.route_topk(lgs[l], k, ids, w)
+            ev.record(3 * l)
+            cache_d.prefill_load(l, ids, out_d, pick_slot=pick_d)
+            ev.record(3 * l + 1)
+            b.expert_forward(pool_d.c, xs[l], pick_d, w, b.FWD_PREFILL, ws_d, y=y)
+            ev.record(3 * l + 2)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        load = [ev.ms(3 * l, 3 * l + 1) / 1e3 for l in range(NL)]
+        fwd = [ev.ms(3 * l + 1, 3 * l + 2) / 1e3 for l in range(NL)]
+        ev.close()
+        return wall, load, fwd
+
+    run_on_demand()                                                  # warm-up (the cache then holds layer 3)
+    c0 = cache_d.read_state()[4].astype(np.int64)
+    wall_d, load_d, fwd_d = run_on_demand()
+    dd = cache_d.read_state()[4].astype(np.int64) - c0
+    host_left = int((pick_d < 0).sum())
+    cache_d.destroy()
+    del pool_d, cache_d
+    torch.cuda.empty_cache()
+    variants["on_demand"] = dict(
+        slots=3 * E // 2, ms_per_layer=wall_d / NL * 1e3, load_ms_per_layer=sum(load_d) / NL * 1e3,
+        forward_ms_per_layer=sum(fwd_d) / NL * 1e3, fills_per_layer=float(dd[4]) / NL,
+        load_GBps=float(dd[4]) * (layer_bytes / E) / sum(load_d) / 1e9, host_picks_last_layer=host_left,
+        what="moe_cache_prefill_load (every miss filled by the fused fill kernel from mapped pinned memory) then "
+             "the grouped GEMM over the whole pool; no overlap of load and compute")
     ach = flops / (sum(fwd_o) / NL) / 1e12
     return dict(workload="prefill_fp8: 8192 tokens x 4 layers, H 7168, E 256, top-8 of x.W_r, I 2048, FP8 E4M3 + "
                          "128x128 scales, pinned host pool, two full-layer slot buffers",
                 ms_per_layer_overlapped=wall_o / NL * 1e3, ms_per_layer_serial=wall_s / NL * 1e3,
                 overlap_gain=wall_s / wall_o, h2d_bytes_per_layer=layer_bytes,
                 h2d_GBps_bound=layer_bytes / (wall_o / NL) / 1e9,
-                forward_ms_per_layer=sum(fwd_o) / NL * 1e3,
+                forward_ms_per_layer=sum(fwd_o) / NL * 1e3, variants=variants,
                 roofline=dict(kernel="moe_expert_forward prefill FP8 (sort + gate/up GEMM + down GEMM + combine)",
                               bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                               frac=ach / PEAK_BF16_TFLOPS))
+
+
+def run_resize(b):
+    """Cost of a safe-point resize at the decode BF16 shapes: a full cache of
+    1894 slots (seeded so that its most recent half sits in the upper half of
+    the slots: every kept expert has to move) shrinks in place to 947 slots,
+    then grows into new banks of 1894 slots (every kept expert is copied)."""
+    import torch
+    from harness import gen, CONFIGS
+    c = CONFIGS["decode_bf16"]
+    L, E, k, H, I, C = c.L, c.E, c.k, c.H, c.I, c.C
+    S = 3 * H * I * 2
+    wg, wu, wd = gen.bank_bf16(c.cfg_id, E, H, I, c.w_std)
+    host_banks = [t.cpu().pin_memory() for t in
+                  b.pack_weights(b.W_BF16, *[torch.from_numpy(a).cuda() for a in (wg, wu, wd)])]
+    host = b.HostPoolTables(host_banks, lambda i: gen.alias_base_expert(i // E, i % E, E, c.alias_stride), L * E)
+    pool = b.SlotPool(C, H, I, b.W_BF16)
+    cache = b.Cache(L, E, k, 1, pool, host, c.bp, c.bh)
+    ids = np.random.default_rng(0).permutation(L * E)[:C]
+    cache.seed([int(i) for i in ids], copy=True)
+    torch.cuda.synchronize()
+    half = C // 2
+    t0 = time.perf_counter()
+    cache.resize(pool.prefix(half))
+    shrink_ms = (time.perf_counter() - t0) * 1e3
+    moved = half                                             # the kept half all sat at slots >= C/2
+    ok = int((cache.read_state()[0] >= 0).sum()) == half
+    pool2 = b.SlotPool(C, H, I, b.W_BF16)
+    t0 = time.perf_counter()
+    cache.resize(pool2)
+    grow_ms = (time.perf_counter() - t0) * 1e3
+    cache.destroy()
+    del pool, pool2, cache, host, host_banks
+    torch.cuda.empty_cache()
+    return dict(workload="decode_bf16 cache: %d slots of %d B, full, shrink in place to %d then grow into new "
+                         "banks of %d slots" % (C, S, half, C),
+                shrink_ms=shrink_ms, shrink_moved_experts=moved, shrink_tables_ok=ok,
+                shrink_copy_GBps=moved * S / (shrink_ms / 1e3) / 1e9,
+                grow_ms=grow_ms, grow_copied_experts=half, grow_copy_GBps=half * S / (grow_ms / 1e3) / 1e9,
+                note="wall of the synchronous call (tables kernel, order rebuild, bank copies); GB/s counts the "
+                     "expert bytes copied (each read once and written once in HBM)")
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
@@ -892,6 +996,9 @@ def main():
         if not a.no_prefill and not a.no_prefill_fp8:
             line["prefill_fp8"] = run_prefill_fp8(b)
             torch.cuda.empty_cache()
+    if not a.no_resize:
+        log("resize: shrink and grow of the decode cache")
+        line["resize"] = run_resize(b)
     if host_exec:
         line["host_exec"] = host_exec
     if not a.no_cpu_baseline:
