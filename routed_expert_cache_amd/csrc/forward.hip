@@ -119,6 +119,10 @@ struct DecArgs {
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
+// device scope (sc1): sees the write-through stores of other XCDs without an L2 invalidate
+__device__ __forceinline__ u32x4 bload_dev(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 16));
+}
 __device__ __forceinline__ u32x4 bload_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
 }
@@ -238,14 +242,33 @@ struct DecWsDev {
   uint32_t* go;           // [kDecGridMax * kCtrlStride] per-workgroup start signal of the down phase
 };
 
-template <bool FP8, int D, int NW>
+// DR: rows of y per down task.
+//  16: one brick row per task; each wave streams its (group, K step) pairs
+//      through a register ring D steps deep, weights before the start signal
+//      and h after it.
+//   8: half a brick row per task (the task's slice of a brick is one 128-byte
+//      line per K chunk), for calls whose down work is small: every wave
+//      loads ALL of its weights into registers before it waits for the start
+//      signal (at most kDecResSteps steps of 4 bricks), and after it the
+//      workgroup copies h into LDS in one round trip, so the only memory
+//      latency left between the signal and y is that copy.  Each of a step's
+//      two 16-byte loads per lane holds the 8-row slices of two bricks (lanes
+//      16j + r, r < 8: the first, r >= 8: the second); MFMAs with the other
+//      half masked to zero put the first bricks' sums in rows 0-7 of the
+//      accumulator and the second bricks' in rows 8-15, added at the end.
+constexpr int kDecResSteps = 6;          // down steps per wave held in registers (DR = 8)
+constexpr int kDecResH = 32 * 1024;      // bytes of LDS for h (DR = 8): G * T * I * 2 at most
+
+template <bool FP8, int D, int NW, int DR>
 __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev c) {
+  static_assert(DR == 8 || DR == 16, "down tasks of 8 or 16 rows");
+  __shared__ __align__(16) uint16_t s_h[DR == 8 ? kDecResH / 2 : 8];
   __shared__ int s_gslot[kDecPmax];
   __shared__ float s_gw[kDecPmax * kDecTok];
   __shared__ int s_G;
   __shared__ unsigned long long s_tab[kPlanTab];
   __shared__ f32x4 red[2][NW][64];
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int H = a.H, I = a.I, T = a.T;
   if (wv == 0) wave_plan(a.pick_slot, a.w, T * a.k, a.k, a.n_slots, a.G_max, s_gslot, s_gw, &s_G, s_tab);
@@ -254,7 +277,7 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   const bool tok = r < T;
   constexpr int XN = FP8 ? 4 : 2;
   const int RA = I / 8;
-  const int nA = G * RA, nB = H / 16;
+  const int nA = G * RA, nB = H / DR;
   const int b0 = (int)blockIdx.x, gs = (int)gridDim.x;
   // the gate/up tasks go round-robin over the whole grid (the fewest per
   // compute unit at most); the down tasks start at workgroup nA % gs, the
@@ -262,10 +285,47 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   const int myA = nA > b0 ? (nA - b0 + gs - 1) / gs : 0;
   const int tb0 = (b0 - nA % gs + gs) % gs;                               // my first down task
   const int myB = nB > tb0 ? (nB - tb0 + gs - 1) / gs : 0;
-  u32x4 wb[D][2], ob[D][XN];   // weight bricks and the other operand (x or h) of D steps
+
+  // DR == 8: the down task's weights (every step of every wave) are loaded
+  // into registers before phase A, so they stream with the gate/up bricks
+  const int rnkt = FP8 ? I / 64 : I / 32;
+  const int rSB = (rnkt + 3) >> 2;               // down steps of 4 bricks
+  const int rn = G * rSB;                        // 0: no pick on the GPU, no start signal comes
+  const int rSWB = (rn + NW - 1) / NW;           // <= kDecResSteps (checked by the host)
+  u32x4 wv2[DR == 8 ? kDecResSteps : 1][2];
+  float f1[DR == 8 ? kDecResSteps : 1], f2[DR == 8 ? kDecResSteps : 1];
+  if constexpr (DR == 8) {
+    const size_t dn_bytes = (size_t)H * I * (FP8 ? 1 : 2);
+    const int t = tb0;
+    const int t16 = t >> 1;
+    const uint32_t lo = (uint32_t)(r >> 3) * 1024u + (uint32_t)(16 * j + 8 * (t & 1) + (r & 7)) * 16u;
+#pragma unroll
+    for (int d = 0; d < kDecResSteps; ++d) {
+      const int q = wv * rSWB + d;
+      const bool ok = myB > 0 && d < rSWB && q < rn;
+      const int qq = ok ? q : 0;
+      const int g = qq / rSB, s = qq - g * rSB;
+      const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;
+      const __amdgpu_buffer_rsrc_t wr =
+          make_rsrc((const char*)a.w_down + (size_t)slot * dn_bytes + (size_t)t16 * rnkt * 1024, (uint32_t)(rnkt * 1024));
+      const uint32_t wo = oob_sel(ok, (uint32_t)s * 4096u + lo);
+      wv2[d][0] = bload_nt(wr, wo);
+      wv2[d][1] = bload_nt(wr, oob_sel(ok, wo + 2048u));
+      float f = ok ? s_gw[g * kDecTok + r] : 0.f;
+      float f_2 = f;
+      if (FP8) {   // 128-wide scale blocks: bricks 4s, 4s+1 and 4s+2, 4s+3
+        const float* sr = a.s_down + ((size_t)slot * (H / 128) + (8 * t) / 128) * (I / 128);
+        f_2 = f * (ok && 2 * s + 1 < I / 128 ? sr[2 * s + 1] : 0.f);
+        f *= sr[2 * s];
+      }
+      f1[d] = f;
+      f2[d] = f_2;
+    }
+  }
 
   // ================= phase A: gate/up + SwiGLU
   {
+    u32x4 wb[D][2], ob[D][XN];   // weight bricks and x of D steps
     const int nkt = FP8 ? H / 64 : H / 32;
     const int S = (nkt + 1) >> 1;
     const int SW = (S + NW - 1) / NW;
@@ -387,7 +447,132 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   }
 
   // ================= phase B: down projection + gate weights (+ merge)
-  if (myB > 0) {
+  if (DR == 8 && myB > 0) {
+    // one 8-row task (myB == 1): rows 8t .. 8t+7 of y; its weights are in wv2
+    const int t = tb0;
+    f32x4 yh = {0, 0, 0, 0};
+    if (wv == 0 && a.y_host && tok && j < 2)
+      yh = *reinterpret_cast<const f32x4*>(a.y_host + (size_t)r * H + 8 * t + 4 * j);
+    if (wv == 0 && rn > 0) {   // wait for the start signal of the down phase (bounded)
+      uint32_t* flag = c.go + (size_t)b0 * kCtrlStride;
+      uint32_t it = 0;
+      for (;;) {
+        uint32_t v = 0;
+        if (lane == 0) v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (__shfl(v, 0, 64)) break;
+        if (++it >= kPollLimit) {
+          if (lane == 0) atomicOr(c.err, 1u);
+          break;
+        }
+        __builtin_amdgcn_s_sleep(8);
+      }
+      if (lane == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      // no acquire fence (on gfx950 an L2 invalidate): h is read below with
+      // device-scope loads, which see the write-through h stores of other XCDs
+    }
+    __syncthreads();
+    // h rows of the T tokens of every group -> LDS [g][t][I]: every load of a
+    // thread (16 bytes each, at most kHL) is issued before the first LDS write
+    {
+      constexpr int kHL = kDecResH / 16 / (NW * 64);
+      const int n16 = G * T * (I / 8);
+      const __amdgpu_buffer_rsrc_t hr = make_rsrc(a.h, (uint32_t)(2u * a.G_max * kDecTok * I));
+      u32x4 hv[kHL];
+#pragma unroll
+      for (int u = 0; u < kHL; ++u) {
+        const int i = tid + u * NW * 64;
+        const int row = i / (I / 8), k8 = i - row * (I / 8);
+        const int g = row / T, tt = row - g * T;
+        hv[u] = bload_dev(hr, oob_sel(i < n16, (uint32_t)(((g * kDecTok + tt) * I + 8 * k8) * 2)));
+      }
+#pragma unroll
+      for (int u = 0; u < kHL; ++u) {
+        const int i = tid + u * NW * 64;
+        if (i < n16) *reinterpret_cast<u32x4*>(&s_h[(size_t)i * 8]) = hv[u];
+      }
+    }
+    __syncthreads();
+    // A 16-byte load of a step holds the 8-row slices of two bricks (the first
+    // in the accumulator's rows 0-7, the second in rows 8-15).  Against the h
+    // of the first brick, rows 0-7 of the product are that brick's sums (rows
+    // 8-15 are unused products); against the h of the second, rows 8-15 are.
+    // acc_e and acc_o collect the two, and the valid halves are added at the
+    // end.  Lanes of tokens >= T read token 0's h: their columns are never
+    // stored.  Missing steps and bricks past I are skipped by uniform branches.
+    f32x4 acc_e = {0, 0, 0, 0}, acc_o = {0, 0, 0, 0};
+    const u32x4 z = {0, 0, 0, 0};
+    const int hl = (tok ? r : 0) * I + (FP8 ? 16 : 8) * j;
+#pragma unroll
+    for (int d = 0; d < kDecResSteps; ++d) {
+      const int q = wv * rSWB + d;
+      if (d < rSWB && q < rn) {
+        const int g = q / rSB, s = q - g * rSB;
+        const uint16_t* hg = s_h + (size_t)g * T * I + hl;
+        u32x4 hb[XN * 4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const int k0 = (FP8 ? 64 : 32) * (4 * s + b);
+          constexpr int HP = FP8 ? 2 : 1;   // h registers per brick
+          if (k0 < I) {
+            hb[HP * b] = *reinterpret_cast<const u32x4*>(hg + k0);
+            if (FP8) hb[HP * b + 1] = *reinterpret_cast<const u32x4*>(hg + k0 + 8);
+          } else {
+            hb[HP * b] = z;
+            if (FP8) hb[HP * b + 1] = z;
+          }
+        }
+        if (!FP8) {
+          f32x4 pe = mfma16x16x32(wv2[d][0], hb[0], f32x4{0, 0, 0, 0});
+          f32x4 po = mfma16x16x32(wv2[d][0], hb[1], f32x4{0, 0, 0, 0});
+          pe = mfma16x16x32(wv2[d][1], hb[2], pe);
+          po = mfma16x16x32(wv2[d][1], hb[3], po);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc_e[e] += f1[d] * pe[e];
+            acc_o[e] += f1[d] * po[e];
+          }
+        } else {
+          f32x4 pe[2], po[2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {   // bricks 4s + 2 h2 (even) and 4s + 2 h2 + 1 (odd): one scale block
+            u32x4 lo8, hi8;
+            e4m3x16_to_bf16_nat(wv2[d][h2], lo8, hi8);
+            pe[h2] = mfma16x16x32(lo8, hb[4 * h2], f32x4{0, 0, 0, 0});
+            po[h2] = mfma16x16x32(lo8, hb[4 * h2 + 2], f32x4{0, 0, 0, 0});
+            pe[h2] = mfma16x16x32(hi8, hb[4 * h2 + 1], pe[h2]);
+            po[h2] = mfma16x16x32(hi8, hb[4 * h2 + 3], po[h2]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            acc_e[e] += f1[d] * pe[0][e] + f2[d] * pe[1][e];
+            acc_o[e] += f1[d] * po[0][e] + f2[d] * po[1][e];
+          }
+        }
+      }
+    }
+    const f32x4 acc = j < 2 ? acc_e : acc_o;   // rows 0-7 of acc_e, rows 8-15 of acc_o
+    // sum the waves' partials (rows 0-7 and 8-15 of each) in a fixed order, store y
+    f32x4(&rb)[NW][64] = red[0];
+    rb[wv][lane] = acc;
+    __syncthreads();
+    if (wv == 0 && tok && j < 2) {
+      f32x4 Y = rb[0][lane] + rb[0][lane + 32];
+#pragma unroll
+      for (int w2 = 1; w2 < NW; ++w2) Y += rb[w2][lane] + rb[w2][lane + 32];
+      const size_t o = (size_t)r * H + 8 * t + 4 * j;
+      if (a.y) *reinterpret_cast<f32x4*>(a.y + o) = Y;
+      if (a.y_out) {
+        const f32x4 M = Y + yh;
+        *reinterpret_cast<f32x4*>(a.y_out + o) = M;
+        if (a.y_bf16) {
+          const uint32_t lo2 = f32_to_bf16_rne(M[0]) | ((uint32_t)f32_to_bf16_rne(M[1]) << 16);
+          const uint32_t hi2 = f32_to_bf16_rne(M[2]) | ((uint32_t)f32_to_bf16_rne(M[3]) << 16);
+          *reinterpret_cast<u32x2*>(a.y_bf16 + o) = u32x2{lo2, hi2};
+        }
+      }
+    }
+  } else if (myB > 0) {
+    u32x4 wb[D][2], ob[D][XN];   // weight bricks and h of D steps
     const int nkt = FP8 ? I / 64 : I / 32;
     const int SB = (nkt + 1) >> 1;
     const int n = G * SB;                       // (group, K step) pairs of every task
@@ -494,7 +679,11 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
           __builtin_amdgcn_s_sleep(16);
         }
         if (lane == 0) __hip_atomic_store(flag, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");   // h written on other XCDs is read from memory
+        // h written on other XCDs is read from memory: one L2 invalidate per
+        // workgroup, then ordinary loads that the XCD's L2 serves to every
+        // down workgroup on it (device-scope loads re-read h from memory each
+        // time, which costs more than the invalidate once T is large)
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       __syncthreads();
 #pragma unroll
@@ -1061,9 +1250,10 @@ static DecWs dec_ws(int T_max, int k, int H, int I, int n_slots) {
 // Resident workgroups per CU of each decode kernel, and the CU count, per device.
 struct DecOcc {
   int cus = 0;
-  int fu[2] = {0, 0};
+  int fu[2][2] = {{0, 0}, {0, 0}};   // [FP8][8-row down tasks]
 };
 constexpr int kDecD_BF16 = 4;   // register-ring depth in 2-brick steps
+constexpr int kDecD_RES = 2;    // the same with the down weights held in registers through phase A (DR = 8)
 constexpr int kDecD_FP8 = 3;    // (FP8 steps carry twice the x operand: a shallower ring keeps 2 workgroups per CU)
 constexpr int kDecW = 8;   // waves per workgroup
 static std::mutex g_occ_mu;
@@ -1077,10 +1267,13 @@ static moe_status dec_occupancy(DecOcc* out) {
   if (!o.cus) {
     int cus = 0;
     MOE_HIP(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
-    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0], dec_fused_kernel<false, kDecD_BF16, kDecW>, kDecW * 64, 0));
-    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1], dec_fused_kernel<true, kDecD_FP8, kDecW>, kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0][0], dec_fused_kernel<false, kDecD_BF16, kDecW, 16>, kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1][0], dec_fused_kernel<true, kDecD_FP8, kDecW, 16>, kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0][1], dec_fused_kernel<false, kDecD_RES, kDecW, 8>, kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1][1], dec_fused_kernel<true, kDecD_RES, kDecW, 8>, kDecW * 64, 0));
     for (int i = 0; i < 2; ++i)
-      if (o.fu[i] < 1) o.fu[i] = 1;
+      for (int v = 0; v < 2; ++v)
+        if (o.fu[i][v] < 1) o.fu[i][v] = 1;
     o.cus = cus > 0 ? cus : 1;
   }
   *out = o;
@@ -1199,11 +1392,21 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     c.go = (uint32_t*)(wsb + L.go);
     const int f = fp8 ? 1 : 0;
     const long tasks = (long)a.G_max * (I / 8) + 2L * (H / 16);
-    const unsigned g1 = (unsigned)std::min<long>(std::min<long>(tasks, (long)occ.cus * occ.fu[f]), kDecGridMax);
-    if (fp8)
-      dec_fused_kernel<true, kDecD_FP8, kDecW><<<g1, kDecW * 64, 0, stream>>>(a, c);
+    const unsigned g1 = (unsigned)std::min<long>(std::min<long>(tasks, (long)occ.cus * occ.fu[f][0]), kDecGridMax);
+    // 8-row down tasks with register-resident weights and h in LDS when every
+    // task fits in one round of the grid, a wave's steps fit its registers,
+    // h fits the LDS, and the occupancy stays
+    const long res_steps = ((long)a.G_max * ((I / (fp8 ? 64 : 32) + 3) / 4) + kDecW - 1) / kDecW;
+    const bool dr8 = (long)(H / 8) <= (long)g1 && res_steps <= kDecResSteps &&
+                     (long)a.G_max * T * I * 2 <= kDecResH && occ.fu[f][1] >= occ.fu[f][0];
+    if (fp8 && dr8)
+      dec_fused_kernel<true, kDecD_RES, kDecW, 8><<<g1, kDecW * 64, 0, stream>>>(a, c);
+    else if (fp8)
+      dec_fused_kernel<true, kDecD_FP8, kDecW, 16><<<g1, kDecW * 64, 0, stream>>>(a, c);
+    else if (dr8)
+      dec_fused_kernel<false, kDecD_RES, kDecW, 8><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else
-      dec_fused_kernel<false, kDecD_BF16, kDecW><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      dec_fused_kernel<false, kDecD_BF16, kDecW, 16><<<g1, kDecW * 64, 0, stream>>>(a, c);
     MOE_LAUNCHED();
     return MOE_OK;
   }
