@@ -181,6 +181,8 @@ def parse():
                         "work for weight generation and decoding besides the timed FFN)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-host-exec", action="store_true", help="skip the host executor (CPU) throughput run")
+    p.add_argument("--no-host-branch", action="store_true",
+                   help="skip decode passes 4 and 5 (the host branch on the CPU), e.g. under counter collection")
     p.add_argument("--no-prefill", action="store_true")
     p.add_argument("--no-resize", action="store_true", help="skip the safe-point resize timing")
     p.add_argument("--no-fp8", action="store_true", help="skip the FP8 decode and FP8 double-buffered prefill runs")
@@ -227,7 +229,7 @@ def read_ceiling(b, nbytes, reps=20):
 
 
 # ---------------------------------------------------------------- decode trace
-def run_decode(b, K, W, host_GBps=None):
+def run_decode(b, K, W, host_GBps=None, host_branch=True):
     import torch
     from harness import gen, CONFIGS
     c = CONFIGS["decode_bf16"]
@@ -323,68 +325,70 @@ def run_decode(b, K, W, host_GBps=None):
     # runs the fill copies and the GPU evaluation of G; the merge waits for
     # the executor's `done` word and adds its y_host.  Reported beside pass 2
     # (the same path with the harness's y_host).
-    log("decode: pass 4 (with the host branch on the CPU)")
-    n_cores = len(os.sched_getaffinity(0))
-    ex = b.HostExec(max(1, n_cores - 1))    # one core left to the thread launching GPU work
-    ids_log = torch.empty((1, k), dtype=torch.int32, device="cuda")
-    h_ids = torch.empty((1, k), dtype=torch.int32).pin_memory()
-    h_pick = torch.empty((1, k), dtype=torch.int32).pin_memory()
-    h_w = torch.empty((1, k), dtype=torch.float32).pin_memory()
-    h_x = torch.empty((1, H), dtype=torch.uint16).pin_memory()
-    h_y = torch.empty((1, H), dtype=torch.float32).pin_memory()
-    ready = torch.zeros(1, dtype=torch.int32).pin_memory()
-    done = torch.zeros(1, dtype=torch.int32).pin_memory()
-    err = torch.zeros(1, dtype=torch.int32, device="cuda")
-    y_gpu = torch.empty((1, H), dtype=torch.float32, device="cuda")
-    seq = [0]
+    wall_host, host_calls, host_s, calibrated, n_cores = None, 0, 0.0, None, len(os.sched_getaffinity(0))
+    if host_branch:
+        log("decode: pass 4 (with the host branch on the CPU)")
+        n_cores = len(os.sched_getaffinity(0))
+        ex = b.HostExec(max(1, n_cores - 1))    # one core left to the thread launching GPU work
+        ids_log = torch.empty((1, k), dtype=torch.int32, device="cuda")
+        h_ids = torch.empty((1, k), dtype=torch.int32).pin_memory()
+        h_pick = torch.empty((1, k), dtype=torch.int32).pin_memory()
+        h_w = torch.empty((1, k), dtype=torch.float32).pin_memory()
+        h_x = torch.empty((1, H), dtype=torch.uint16).pin_memory()
+        h_y = torch.empty((1, H), dtype=torch.float32).pin_memory()
+        ready = torch.zeros(1, dtype=torch.int32).pin_memory()
+        done = torch.zeros(1, dtype=torch.int32).pin_memory()
+        err = torch.zeros(1, dtype=torch.int32, device="cuda")
+        y_gpu = torch.empty((1, H), dtype=torch.float32, device="cuda")
+        seq = [0]
 
-    def layer_step_host(cache, s, l):
-        seq[0] += 1
-        cache.route_step(l, lg[s, l], ids, w, out, copy=False)
-        torch.add(ids, l * E, out=ids_log)                           # logical ids index the host pool
-        for hd, dd in ((h_ids, ids_log), (h_pick, pick), (h_w, w), (h_x, x[s, l])):
-            hd.copy_(dd, non_blocking=True)
-        b.host_signal(ready, seq[0])
-        ex.forward_signal(host, b.W_BF16, H, I, h_x, h_ids, h_pick, h_w, h_y, ready, done, seq[0])
-        cache.fill(out)
-        b.expert_forward(pool.c, x[s, l], pick, w, b.FWD_DECODE, ws, y=y_gpu)
-        b.merge_partial_after(y_gpu, h_y, done, seq[0], y_out=y[l], err=err)
+        def layer_step_host(cache, s, l):
+            seq[0] += 1
+            cache.route_step(l, lg[s, l], ids, w, out, copy=False)
+            torch.add(ids, l * E, out=ids_log)                           # logical ids index the host pool
+            for hd, dd in ((h_ids, ids_log), (h_pick, pick), (h_w, w), (h_x, x[s, l])):
+                hd.copy_(dd, non_blocking=True)
+            b.host_signal(ready, seq[0])
+            ex.forward_signal(host, b.W_BF16, H, I, h_x, h_ids, h_pick, h_w, h_y, ready, done, seq[0])
+            cache.fill(out)
+            b.expert_forward(pool.c, x[s, l], pick, w, b.FWD_DECODE, ws, y=y_gpu)
+            b.merge_partial_after(y_gpu, h_y, done, seq[0], y_out=y[l], err=err)
 
-    def run_host_trace(bp, bh):
-        """Pass 4 (and 5): cold cache with this B_P:B_H, W warm-up and K timed steps."""
-        cache4 = b.Cache(L, E, k, 1, pool, host, bp, bh)
-        for s in range(W):
-            for l in range(L):
-                layer_step_host(cache4, s, l)
-        torch.cuda.synchronize()
-        c0 = cache4.read_state()[4].astype(np.int64)
-        t0 = time.perf_counter()
-        for s in range(W, W + K):
-            for l in range(L):
-                layer_step_host(cache4, s, l)
-        torch.cuda.synchronize()
-        wall_h = time.perf_counter() - t0
-        dh = cache4.read_state()[4].astype(np.int64) - c0
-        cache4.destroy()
-        assert ex.status() == 0 and int(err.item()) == 0, "the host branch failed"
-        return wall_h, dh
+        def run_host_trace(bp, bh):
+            """Pass 4 (and 5): cold cache with this B_P:B_H, W warm-up and K timed steps."""
+            cache4 = b.Cache(L, E, k, 1, pool, host, bp, bh)
+            for s in range(W):
+                for l in range(L):
+                    layer_step_host(cache4, s, l)
+            torch.cuda.synchronize()
+            c0 = cache4.read_state()[4].astype(np.int64)
+            t0 = time.perf_counter()
+            for s in range(W, W + K):
+                for l in range(L):
+                    layer_step_host(cache4, s, l)
+            torch.cuda.synchronize()
+            wall_h = time.perf_counter() - t0
+            dh = cache4.read_state()[4].astype(np.int64) - c0
+            cache4.destroy()
+            assert ex.status() == 0 and int(err.item()) == 0, "the host branch failed"
+            return wall_h, dh
 
-    wall_host, d4 = run_host_trace(c.bp, c.bh)
-    assert np.array_equal(d, d4), "the passes made different cache decisions"
-    host_calls, host_s = ex.stats()
-    calibrated = None
-    fill_rate = (d[4] * S / fill_s / 1e9) if fill_s > 0 else None
-    if host_GBps and fill_rate:
-        # Pass 5: q* from this machine's rates (B_P: the fill copies above, B_H:
-        # the host executor) instead of the quoted ratio; the same trace.
-        bp_c, bh_c = max(1, round(fill_rate * 10)), max(1, round(host_GBps * 10))   # units of 0.1 GB/s
-        log("decode: pass 5 (host branch, calibrated B_P:B_H %.1f:%.1f)" % (bp_c / 10, bh_c / 10))
-        wall5, d5 = run_host_trace(bp_c, bh_c)
-        calibrated = dict(B_P_GBps=bp_c / 10, B_H_GBps=bh_c / 10, wall_ms_per_step=wall5 / K * 1e3,
-                          miss_rate=float(d5[3] / d5[1]), fills_per_layer_call=float(d5[4] / (K * L)),
-                          host_experts_per_layer_call=float(d5[5] / (K * L)),
-                          experts_on_gpu_per_layer_call=float((d5[2] + d5[4]) / (K * L)))
-    ex.destroy()
+        wall_host, d4 = run_host_trace(c.bp, c.bh)
+        assert np.array_equal(d, d4), "the passes made different cache decisions"
+        host_calls, host_s = ex.stats()
+        calibrated = None
+        fill_rate = (d[4] * S / fill_s / 1e9) if fill_s > 0 else None
+        if host_GBps and fill_rate:
+            # Pass 5: q* from this machine's rates (B_P: the fill copies above, B_H:
+            # the host executor) instead of the quoted ratio; the same trace.
+            bp_c, bh_c = max(1, round(fill_rate * 10)), max(1, round(host_GBps * 10))   # units of 0.1 GB/s
+            log("decode: pass 5 (host branch, calibrated B_P:B_H %.1f:%.1f)" % (bp_c / 10, bh_c / 10))
+            wall5, d5 = run_host_trace(bp_c, bh_c)
+            calibrated = dict(B_P_GBps=bp_c / 10, B_H_GBps=bh_c / 10, wall_ms_per_step=wall5 / K * 1e3,
+                              miss_rate=float(d5[3] / d5[1]), fills_per_layer_call=float(d5[4] / (K * L)),
+                              host_experts_per_layer_call=float(d5[5] / (K * L)),
+                              experts_on_gpu_per_layer_call=float((d5[2] + d5[4]) / (K * L)))
+        ex.destroy()
     # Forward-only burst: the timed layer calls' forward launches again, back
     # to back with the same picks (the slots now hold other experts: the same
     # bytes), one event pair per step of 40 layers: the kernel's duration with
@@ -421,7 +425,7 @@ def run_decode(b, K, W, host_GBps=None):
             experts_on_gpu_per_layer_call=n_g / (K * L),
             fills_per_layer_call=float(d[4] / (K * L)),
             host_experts_per_layer_call=float(d[5] / (K * L)),
-            host_branch=dict(
+            host_branch=None if wall_host is None else dict(
                 wall_ms_per_step=wall_host / K * 1e3,
                 host_compute_us_per_call_with_host_picks=host_s / max(host_calls, 1) * 1e6,
                 calls_with_host_picks=host_calls,
@@ -970,7 +974,8 @@ def main():
     if not a.no_host_exec:
         log("host executor: expert GB/s on %d cores" % len(os.sched_getaffinity(0)))
         host_exec = run_host_exec(b)
-    dec = run_decode(b, a.steps, a.warmup, host_exec["decode_bf16"]["GBps"] if host_exec else None)
+    dec = run_decode(b, a.steps, a.warmup, host_exec["decode_bf16"]["GBps"] if host_exec else None,
+                     host_branch=not a.no_host_branch)
     if host_exec:
         fr = dec["detail"].get("fill_GBps")
         if fr:
