@@ -261,7 +261,7 @@ constexpr int kDecResH = 32 * 1024;      // bytes of LDS for h (DR = 8): G * T *
 
 template <bool FP8, int D, int NW, int DR>
 __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev c) {
-  static_assert(DR == 8 || DR == 16, "down tasks of 8 or 16 rows");
+  static_assert(DR == 16 || (DR == 8 && !FP8), "down tasks of 16 rows, or 8 (BF16 only)");
   __shared__ __align__(16) uint16_t s_h[DR == 8 ? kDecResH / 2 : 8];
   __shared__ int s_gslot[kDecPmax];
   __shared__ float s_gw[kDecPmax * kDecTok];
@@ -288,14 +288,14 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
 
   // DR == 8: the down task's weights (every step of every wave) are loaded
   // into registers before phase A, so they stream with the gate/up bricks
-  const int rnkt = FP8 ? I / 64 : I / 32;
+  const int rnkt = I / 32;
   const int rSB = (rnkt + 3) >> 2;               // down steps of 4 bricks
   const int rn = G * rSB;                        // 0: no pick on the GPU, no start signal comes
   const int rSWB = (rn + NW - 1) / NW;           // <= kDecResSteps (checked by the host)
   u32x4 wv2[DR == 8 ? kDecResSteps : 1][2];
-  float f1[DR == 8 ? kDecResSteps : 1], f2[DR == 8 ? kDecResSteps : 1];
+  float f1[DR == 8 ? kDecResSteps : 1];
   if constexpr (DR == 8) {
-    const size_t dn_bytes = (size_t)H * I * (FP8 ? 1 : 2);
+    const size_t dn_bytes = (size_t)H * I * 2;
     const int t = tb0;
     const int t16 = t >> 1;
     const uint32_t lo = (uint32_t)(r >> 3) * 1024u + (uint32_t)(16 * j + 8 * (t & 1) + (r & 7)) * 16u;
@@ -311,15 +311,7 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
       const uint32_t wo = oob_sel(ok, (uint32_t)s * 4096u + lo);
       wv2[d][0] = bload_nt(wr, wo);
       wv2[d][1] = bload_nt(wr, oob_sel(ok, wo + 2048u));
-      float f = ok ? s_gw[g * kDecTok + r] : 0.f;
-      float f_2 = f;
-      if (FP8) {   // 128-wide scale blocks: bricks 4s, 4s+1 and 4s+2, 4s+3
-        const float* sr = a.s_down + ((size_t)slot * (H / 128) + (8 * t) / 128) * (I / 128);
-        f_2 = f * (ok && 2 * s + 1 < I / 128 ? sr[2 * s + 1] : 0.f);
-        f *= sr[2 * s];
-      }
-      f1[d] = f;
-      f2[d] = f_2;
+      f1[d] = ok ? s_gw[g * kDecTok + r] : 0.f;
     }
   }
 
@@ -501,52 +493,28 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
     // stored.  Missing steps and bricks past I are skipped by uniform branches.
     f32x4 acc_e = {0, 0, 0, 0}, acc_o = {0, 0, 0, 0};
     const u32x4 z = {0, 0, 0, 0};
-    const int hl = (tok ? r : 0) * I + (FP8 ? 16 : 8) * j;
+    const int hl = (tok ? r : 0) * I + 8 * j;
 #pragma unroll
     for (int d = 0; d < kDecResSteps; ++d) {
       const int q = wv * rSWB + d;
       if (d < rSWB && q < rn) {
         const int g = q / rSB, s = q - g * rSB;
         const uint16_t* hg = s_h + (size_t)g * T * I + hl;
-        u32x4 hb[XN * 4];
+        u32x4 hb[4];   // h of bricks 4s .. 4s+3 (zero past I)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-          const int k0 = (FP8 ? 64 : 32) * (4 * s + b);
-          constexpr int HP = FP8 ? 2 : 1;   // h registers per brick
-          if (k0 < I) {
-            hb[HP * b] = *reinterpret_cast<const u32x4*>(hg + k0);
-            if (FP8) hb[HP * b + 1] = *reinterpret_cast<const u32x4*>(hg + k0 + 8);
-          } else {
-            hb[HP * b] = z;
-            if (FP8) hb[HP * b + 1] = z;
-          }
+          const int k0 = 32 * (4 * s + b);
+          const u32x4 v = *reinterpret_cast<const u32x4*>(hg + (k0 < I ? k0 : 0));   // in the row either way
+          hb[b] = k0 < I ? v : z;
         }
-        if (!FP8) {
-          f32x4 pe = mfma16x16x32(wv2[d][0], hb[0], f32x4{0, 0, 0, 0});
-          f32x4 po = mfma16x16x32(wv2[d][0], hb[1], f32x4{0, 0, 0, 0});
-          pe = mfma16x16x32(wv2[d][1], hb[2], pe);
-          po = mfma16x16x32(wv2[d][1], hb[3], po);
+        f32x4 pe = mfma16x16x32(wv2[d][0], hb[0], f32x4{0, 0, 0, 0});
+        f32x4 po = mfma16x16x32(wv2[d][0], hb[1], f32x4{0, 0, 0, 0});
+        pe = mfma16x16x32(wv2[d][1], hb[2], pe);
+        po = mfma16x16x32(wv2[d][1], hb[3], po);
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc_e[e] += f1[d] * pe[e];
-            acc_o[e] += f1[d] * po[e];
-          }
-        } else {
-          f32x4 pe[2], po[2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {   // bricks 4s + 2 h2 (even) and 4s + 2 h2 + 1 (odd): one scale block
-            u32x4 lo8, hi8;
-            e4m3x16_to_bf16_nat(wv2[d][h2], lo8, hi8);
-            pe[h2] = mfma16x16x32(lo8, hb[4 * h2], f32x4{0, 0, 0, 0});
-            po[h2] = mfma16x16x32(lo8, hb[4 * h2 + 2], f32x4{0, 0, 0, 0});
-            pe[h2] = mfma16x16x32(hi8, hb[4 * h2 + 1], pe[h2]);
-            po[h2] = mfma16x16x32(hi8, hb[4 * h2 + 3], po[h2]);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            acc_e[e] += f1[d] * pe[0][e] + f2[d] * pe[1][e];
-            acc_o[e] += f1[d] * po[0][e] + f2[d] * po[1][e];
-          }
+        for (int e = 0; e < 4; ++e) {
+          acc_e[e] += f1[d] * pe[e];
+          acc_o[e] += f1[d] * po[e];
         }
       }
     }
@@ -1270,10 +1238,9 @@ static moe_status dec_occupancy(DecOcc* out) {
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0][0], dec_fused_kernel<false, kDecD_BF16, kDecW, 16>, kDecW * 64, 0));
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1][0], dec_fused_kernel<true, kDecD_FP8, kDecW, 16>, kDecW * 64, 0));
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0][1], dec_fused_kernel<false, kDecD_RES, kDecW, 8>, kDecW * 64, 0));
-    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1][1], dec_fused_kernel<true, kDecD_RES, kDecW, 8>, kDecW * 64, 0));
+    o.fu[1][1] = 0;   // the register-resident form is BF16 only (FP8 steps need more registers than it has)
     for (int i = 0; i < 2; ++i)
-      for (int v = 0; v < 2; ++v)
-        if (o.fu[i][v] < 1) o.fu[i][v] = 1;
+      if (o.fu[i][0] < 1) o.fu[i][0] = 1;
     o.cus = cus > 0 ? cus : 1;
   }
   *out = o;
@@ -1397,11 +1364,9 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     // task fits in one round of the grid, a wave's steps fit its registers,
     // h fits the LDS, and the occupancy stays
     const long res_steps = ((long)a.G_max * ((I / (fp8 ? 64 : 32) + 3) / 4) + kDecW - 1) / kDecW;
-    const bool dr8 = (long)(H / 8) <= (long)g1 && res_steps <= kDecResSteps &&
+    const bool dr8 = !fp8 && (long)(H / 8) <= (long)g1 && res_steps <= kDecResSteps &&
                      (long)a.G_max * T * I * 2 <= kDecResH && occ.fu[f][1] >= occ.fu[f][0];
-    if (fp8 && dr8)
-      dec_fused_kernel<true, kDecD_RES, kDecW, 8><<<g1, kDecW * 64, 0, stream>>>(a, c);
-    else if (fp8)
+    if (fp8)
       dec_fused_kernel<true, kDecD_FP8, kDecW, 16><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (dr8)
       dec_fused_kernel<false, kDecD_RES, kDecW, 8><<<g1, kDecW * 64, 0, stream>>>(a, c);
