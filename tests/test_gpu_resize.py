@@ -128,3 +128,46 @@ def test_outputs_unchanged_across_resizes():
     assert cache.error() == 0
     ex.destroy()
     cache.destroy()
+
+
+def test_resize_fp8_pool_moves_every_bank():
+    """FP8 slots carry five banks, the scale banks in 4-byte multiples that
+    are not 16-byte multiples (128x128 blocks of a 256x128 expert: 8 bytes):
+    after an in-place shrink and a grow into new banks every resident slot
+    holds its expert's bytes in all five banks, and the tables match the
+    oracle."""
+    from oracle import lru
+    from tests.layer_setup import Fp8Bank
+    b = binding()
+    E, H, I, k, C = 12, 256, 128, 2, 10
+    bank = Fp8Bank(86, E, H, I)
+    pool = b.SlotPool(C, H, I, b.W_FP8_B128)
+    host = b.HostPoolTables(bank.host, lambda i: i, E)
+    cache = b.Cache(1, E, k, 2, pool, host, 900, 475)
+    orc = lru.ExpertCache(1, E, C, 900, 475)
+    seeded = [int(i) for i in np.random.default_rng(3).permutation(E)[:C]]
+    cache.seed(seeded, copy=True)
+    orc.seed(seeded)
+    host_rows = [bank.host[0], bank.host[1], bank.t["s_gate"], bank.t["s_up"], bank.t["s_down"]]
+
+    def check(p):
+        slot_id, stamp, id_slot, tick, _ = cache.read_state()
+        rs, rt, ri, rtick = orc.tables()
+        assert np.array_equal(slot_id, rs) and np.array_equal(stamp, rt) and np.array_equal(id_slot, ri)
+        for s, lid in enumerate(slot_id):
+            if lid >= 0:
+                for dev_bank, hb in zip(p.banks(), host_rows):
+                    assert torch.equal(dev_bank[s].cpu().reshape(-1).view(torch.uint8),
+                                       hb[lid].reshape(-1).view(torch.uint8)), (s, lid)
+
+    check(pool)
+    small = pool.prefix(4)
+    cache.resize(small)
+    assert orc.resize(4), "nothing moved"
+    check(small)
+    grown = b.SlotPool(7, H, I, b.W_FP8_B128)
+    cache.resize(grown)
+    orc.resize(7)
+    check(grown)
+    assert cache.error() == 0
+    cache.destroy()
