@@ -29,6 +29,7 @@ import numpy as np
 
 PEAK_HBM_GBPS = 8000.0          # MI355X HBM3E
 PEAK_BF16_TFLOPS = 2500.0       # MI355X dense BF16 MFMA
+PEAK_PCIE_GBPS = 63.0           # PCIe 5.0 x16, one direction: 32 GT/s x 16 lanes, 128b/130b
 METRIC = "decode MoE-layer expert GB/s (%HBM peak); prefill MoE TFLOP/s (%MFMA peak)"
 
 
@@ -708,8 +709,15 @@ def run_prefill_fp8(b):
     cache.destroy()
     del pool, cache, pf
     torch.cuda.empty_cache()
-    variants = dict(handover=dict(ms=handover_ms, survivors=survivors,
-                                  what="moe_prefill_finish after the 4-layer pass: 2 x 256 experts registered"))
+    from oracle import lru
+    orc = lru.ExpertCache(NL, E, 2 * E, 118, 475)
+    orc.reserve(0, 2 * E)
+    t0 = time.perf_counter()
+    orc.finish_prefill(0, 2, [(0, NL - 2), (1, NL - 1)])
+    oracle_ho_ms = (time.perf_counter() - t0) * 1e3
+    variants = dict(handover=dict(ms=handover_ms, survivors=survivors, cpu_oracle_ms=oracle_ho_ms,
+                                  what="moe_prefill_finish after the 4-layer pass: 2 x 256 experts registered "
+                                       "(tables only: a device sync, one kernel, the order rebuild)"))
     # a ring of three full-layer buffers
     log("prefill fp8: ring of three buffers")
     pool3 = b.SlotPool(3 * E, H, I, b.W_FP8_B128)
@@ -761,6 +769,10 @@ def run_prefill_fp8(b):
         slots=3 * E // 2, ms_per_layer=wall_d / NL * 1e3, load_ms_per_layer=sum(load_d) / NL * 1e3,
         forward_ms_per_layer=sum(fwd_d) / NL * 1e3, fills_per_layer=float(dd[4]) / NL,
         load_GBps=float(dd[4]) * (layer_bytes / E) / sum(load_d) / 1e9, host_picks_last_layer=host_left,
+        roofline=dict(bound="pcie", achieved=float(dd[4]) * (layer_bytes / E) / sum(load_d) / 1e9,
+                      peak=PEAK_PCIE_GBPS, unit="GB/s",
+                      frac=float(dd[4]) * (layer_bytes / E) / sum(load_d) / 1e9 / PEAK_PCIE_GBPS,
+                      what="the fill copies of moe_cache_prefill_load against PCIe 5.0 x16 (one direction)"),
         what="moe_cache_prefill_load (every miss filled by the fused fill kernel from mapped pinned memory) then "
              "the grouped GEMM over the whole pool; no overlap of load and compute")
     ach = flops / (sum(fwd_o) / NL) / 1e12
@@ -807,13 +819,26 @@ def run_resize(b):
     cache.destroy()
     del pool, pool2, cache, host, host_banks
     torch.cuda.empty_cache()
+    # the oracle's resize of the same table state (test infrastructure, timed beside)
+    from oracle import lru
+    orc = lru.ExpertCache(L, E, C, c.bp, c.bh)
+    orc.seed([int(i) for i in ids])
+    t0 = time.perf_counter()
+    orc.resize(half)
+    orc.resize(C)
+    oracle_ms = (time.perf_counter() - t0) * 1e3
+    hbm = 2 * moved * S / (shrink_ms / 1e3) / 1e9     # each moved byte read and written once
     return dict(workload="decode_bf16 cache: %d slots of %d B, full, shrink in place to %d then grow into new "
                          "banks of %d slots" % (C, S, half, C),
                 shrink_ms=shrink_ms, shrink_moved_experts=moved, shrink_tables_ok=ok,
                 shrink_copy_GBps=moved * S / (shrink_ms / 1e3) / 1e9,
                 grow_ms=grow_ms, grow_copied_experts=half, grow_copy_GBps=half * S / (grow_ms / 1e3) / 1e9,
+                roofline=dict(bound="hbm", achieved=hbm, peak=PEAK_HBM_GBPS, unit="GB/s", frac=hbm / PEAK_HBM_GBPS,
+                              what="in-place shrink: moved expert bytes read + written over the call's wall time"),
+                cpu_oracle_tables_ms=oracle_ms,
                 note="wall of the synchronous call (tables kernel, order rebuild, bank copies); GB/s counts the "
-                     "expert bytes copied (each read once and written once in HBM)")
+                     "expert bytes copied (each read once and written once in HBM); cpu_oracle_tables_ms: the "
+                     "oracle's shrink and grow of the same tables (no bytes)")
 
 
 # ---------------------------------------------------------------- CPU oracle baseline
