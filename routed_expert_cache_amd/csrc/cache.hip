@@ -429,25 +429,55 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
 }
 
 // Rebuild the LRU order from the stamps (set-up paths only: reset, seed,
-// reserve, release): rank of each non-reserved slot by (stamp, slot).
+// reserve, release, hand-over, resize): rank of each non-reserved slot by
+// (stamp, slot).  The keys are staged through LDS a tile at a time, so each
+// thread compares its slots against every other slot from LDS; a reserved
+// slot's key is the maximum and never counts.
+constexpr int kOrdTile = 2048;
 __global__ __launch_bounds__(1024) void cache_order_kernel(CacheDev cd) {
+  __shared__ uint64_t key[kOrdTile];
   __shared__ int cnt;
-  if (threadIdx.x == 0) cnt = 0;
-  __syncthreads();
-  for (int s = threadIdx.x; s < cd.C; s += 1024) {
-    if (cd.slot_id[s] == -2) continue;
-    const uint64_t ks = cd.stamp[s];
-    int rank = 0;
-    for (int t = 0; t < cd.C; ++t) {
-      if (cd.slot_id[t] == -2) continue;
-      const uint64_t kt = cd.stamp[t];
-      rank += (kt < ks) || (kt == ks && t < s);
+  constexpr uint64_t kNone = ~0ull;
+  const int C = cd.C, tid = threadIdx.x;
+  if (tid == 0) cnt = 0;
+  constexpr int kPer = kCMax / 1024;   // slots per thread at most
+  uint64_t ks[kPer];
+  int rank[kPer];
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int sidx = tid + u * 1024;
+    ks[u] = (sidx < C && cd.slot_id[sidx] != -2) ? cd.stamp[sidx] : kNone;
+    rank[u] = 0;
+  }
+  for (int t0 = 0; t0 < C; t0 += kOrdTile) {
+    __syncthreads();
+    for (int t = tid; t < kOrdTile; t += 1024) {
+      const int ti = t0 + t;
+      key[t] = (ti < C && cd.slot_id[ti] != -2) ? cd.stamp[ti] : kNone;
     }
-    cd.order[rank] = s;
-    atomicAdd(&cnt, 1);
+    __syncthreads();
+    const int nt = C - t0 < kOrdTile ? C - t0 : kOrdTile;
+    for (int t = 0; t < nt; ++t) {
+      const uint64_t kt = key[t];
+      const int ti = t0 + t;
+#pragma unroll
+      for (int u = 0; u < kPer; ++u) {
+        if (u * 1024 >= C) break;   // uniform: only the slot columns that exist
+        const int sidx = tid + u * 1024;
+        rank[u] += (kt < ks[u]) || (kt == ks[u] && ti < sidx);
+      }
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kPer; ++u) {
+    const int sidx = tid + u * 1024;
+    if (sidx < C && ks[u] != kNone) {
+      cd.order[rank[u]] = sidx;
+      atomicAdd(&cnt, 1);
+    }
   }
   __syncthreads();
-  if (threadIdx.x == 0) *cd.n_ord = cnt;
+  if (tid == 0) *cd.n_ord = cnt;
 }
 
 // ---------------------------------------------------------------- fused fill copy
@@ -731,7 +761,9 @@ __global__ __launch_bounds__(1024) void cache_resize_kernel(CacheDev od, CacheDe
 
 // Copy every bank of each listed slot from the old banks to the new ones.
 // Sources and destinations are distinct slots (destinations were free), so
-// the copies are independent.
+// the copies are independent: each workgroup copies whole experts, with
+// eight 16-byte loads per thread in flight, and every workgroup streams at
+// once.
 struct MoveArgs {
   const int32_t* src;
   const int32_t* dst;
@@ -744,9 +776,7 @@ struct MoveArgs {
 
 __global__ __launch_bounds__(256) void slot_move_kernel(MoveArgs a) {
   const int n = *a.n;
-  const size_t gtid = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const size_t gsz = (size_t)gridDim.x * blockDim.x;
-  for (int f = 0; f < n; ++f) {
+  for (int f = blockIdx.x; f < n; f += gridDim.x) {
     const size_t s = (size_t)a.src[f], d = (size_t)a.dst[f];
     for (int b = 0; b < a.nb; ++b) {
       const char* src = a.from[b] + s * a.bytes[b];
@@ -754,11 +784,20 @@ __global__ __launch_bounds__(256) void slot_move_kernel(MoveArgs a) {
       if ((a.bytes[b] & 15) == 0) {
         const u32x4* s4 = reinterpret_cast<const u32x4*>(src);
         u32x4* d4 = reinterpret_cast<u32x4*>(dst);
-        for (size_t i = gtid; i < (a.bytes[b] >> 4); i += gsz) d4[i] = __builtin_nontemporal_load(s4 + i);
+        const size_t n16 = a.bytes[b] >> 4;
+        size_t i = threadIdx.x;
+        for (; i + 7 * 256 < n16; i += 8 * 256) {
+          u32x4 v[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) v[u] = __builtin_nontemporal_load(s4 + i + u * 256);
+#pragma unroll
+          for (int u = 0; u < 8; ++u) d4[i + u * 256] = v[u];
+        }
+        for (; i < n16; i += 256) d4[i] = __builtin_nontemporal_load(s4 + i);
       } else {
         const uint32_t* s1 = reinterpret_cast<const uint32_t*>(src);
         uint32_t* d1 = reinterpret_cast<uint32_t*>(dst);
-        for (size_t i = gtid; i < (a.bytes[b] >> 2); i += gsz) d1[i] = s1[i];
+        for (size_t i = threadIdx.x; i < (a.bytes[b] >> 2); i += 256) d1[i] = s1[i];
       }
     }
   }
