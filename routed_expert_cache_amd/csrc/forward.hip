@@ -246,16 +246,19 @@ struct DecWsDev {
 //  16: one brick row per task; each wave streams its (group, K step) pairs
 //      through a register ring D steps deep, weights before the start signal
 //      and h after it.
-//   8: half a brick row per task (the task's slice of a brick is one 128-byte
-//      line per K chunk), for calls whose down work is small: every wave
-//      loads ALL of its weights into registers before it waits for the start
-//      signal (at most kDecResSteps steps of 4 bricks), and after it the
-//      workgroup copies h into LDS in one round trip, so the only memory
-//      latency left between the signal and y is that copy.  Each of a step's
-//      two 16-byte loads per lane holds the 8-row slices of two bricks (lanes
-//      16j + r, r < 8: the first, r >= 8: the second); MFMAs with the other
-//      half masked to zero put the first bricks' sums in rows 0-7 of the
-//      accumulator and the second bricks' in rows 8-15, added at the end.
+//   8: (BF16) half a brick row per task (the task's slice of a brick is one
+//      128-byte line per K chunk), for calls whose down work is small: every
+//      wave issues ALL of its down weights into registers right after the
+//      plan, before its gate/up task (at most kDecResSteps steps of 4
+//      bricks), so they stream with the gate/up bricks; after the start
+//      signal the workgroup copies h into LDS in one round trip of
+//      device-scope loads (no L2 invalidate), so the only memory latency left
+//      between the signal and y is that copy.  Each of a step's two 16-byte
+//      loads per lane holds the 8-row slices of two bricks (lanes 16j + r,
+//      r < 8: the first, r >= 8: the second): against the first brick's h the
+//      product's rows 0-7 are that brick's sums, against the second's its
+//      rows 8-15 are; two accumulators collect them and the valid halves are
+//      added at the end.
 constexpr int kDecResSteps = 6;          // down steps per wave held in registers (DR = 8)
 constexpr int kDecResH = 32 * 1024;      // bytes of LDS for h (DR = 8): G * T * I * 2 at most
 
