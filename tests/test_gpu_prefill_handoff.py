@@ -208,3 +208,40 @@ def test_on_demand_prefill_outputs():
     assert cache.error() == 0
     ex.destroy()
     cache.destroy()
+
+
+def test_on_demand_load_full_shape_decisions():
+    """The on-demand loading of the FP8 prefill workload's shape (8192 tokens,
+    256 experts, top-8, a 384-slot pool: no room for two full layers), four
+    layers in a row: decisions, picks and tables bit-exact against the oracle
+    (tiny weight rows: the decisions do not read them)."""
+    L, E, k, T, C = 4, 256, 8, 8192, 384
+    h = Harness(L, E, C, (E + k - 1) // k, k, 118, 475, copy=False)
+    rng = np.random.default_rng(17)
+    for layer in range(L):
+        lg = rng.standard_normal((T, E)).astype(np.float32)
+        ids, _ = route.topk_softmax(lg, k)
+        r, _ = h.prefill_load(layer, ids)
+        assert len(r.uniq) == E and r.q == min(len(r.misses), C - len(r.hits))
+    h.compare_tables()
+    assert h.cache.error() == 0
+    h.cache.destroy()
+
+
+def test_finish_full_shape_tables():
+    """Hand-over at the FP8 prefill workload's shape: 4 layers of 256 experts
+    through two full-layer buffers of a 1633-slot pool holding earlier decode
+    residents; tables and slot bytes against the oracle afterwards."""
+    L, E, k, C = 4, 256, 8, 1633
+    rng = np.random.default_rng(18)
+    pre = [int(i) for i in rng.choice(L * E, size=600, replace=False)]
+    h = Harness(L, E, C, 1, k, 118, 475, seed_ids=pre, copy=True)
+    first = C - 2 * E
+    pf = h.b.PrefillPool(h.cache)
+    h.orc.reserve(first, 2 * E)
+    _prefill_layers(pf, 2, L, torch.cuda.current_stream(), torch.cuda.Stream())
+    pf.finish()
+    h.orc.finish_prefill(first, 2, _loaded(2, L))
+    h.compare_tables()
+    h.check_slot_bytes()
+    h.cache.destroy()
