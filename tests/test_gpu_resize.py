@@ -171,3 +171,35 @@ def test_resize_fp8_pool_moves_every_bank():
     check(grown)
     assert cache.error() == 0
     cache.destroy()
+
+
+def test_resize_full_shape_decode_cache():
+    """The decode BF16 workload's cache (40 layers x 128 experts, top-8, 1894
+    slots, 52.7:77.3) driven by its sticky trace, shrunk in place to 947
+    slots and grown back into new banks of 1894, with trace steps between:
+    tables against the oracle after every phase, slot bytes at the end (tiny
+    weight rows: the tables and copies do not depend on their size)."""
+    from harness import CONFIGS
+    from oracle import route
+    b = binding()
+    c = CONFIGS["decode_bf16"]
+    h = Harness(c.L, c.E, c.C, 1, c.k, c.bp, c.bh, copy=True)
+    picks, logits = gen.decode_trace(c.cfg_id, c.L, 12, c.E, c.k, c.p_keep)
+
+    def run(steps):
+        for s in steps:
+            for l in range(c.L):
+                ids, _ = route.topk_softmax(logits[s, l], c.k)
+                h.step(l, ids)
+
+    run(range(0, 4))
+    h.compare_tables()
+    _resize(h, h.pool.prefix(c.C // 2))
+    run(range(4, 8))
+    h.compare_tables()
+    _resize(h, b.SlotPool(c.C, h.pool.H, h.pool.I, b.W_BF16))
+    run(range(8, 12))
+    h.compare_tables()
+    h.check_slot_bytes()
+    assert h.cache.error() == 0
+    h.cache.destroy()
