@@ -248,9 +248,9 @@ struct DecWsDev {
 //      and h after it.
 //   8: (BF16) half a brick row per task (the task's slice of a brick is one
 //      128-byte line per K chunk), for calls whose down work is small: every
-//      wave issues ALL of its down weights into registers right after the
-//      plan, before its gate/up task (at most kDecResSteps steps of 4
-//      bricks), so they stream with the gate/up bricks; after the start
+//      wave issues ALL of its down weights into registers when its gate/up
+//      tasks are done (at most kDecResSteps steps of 4 bricks), so they stream
+//      while the second round of gate/up tasks runs; after the start
 //      signal the workgroup copies h into LDS in one round trip of
 //      device-scope loads (no L2 invalidate), so the only memory latency left
 //      between the signal and y is that copy.  Each of a step's two 16-byte
@@ -289,35 +289,14 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   const int tb0 = (b0 - nA % gs + gs) % gs;                               // my first down task
   const int myB = nB > tb0 ? (nB - tb0 + gs - 1) / gs : 0;
 
-  // DR == 8: the down task's weights (every step of every wave) are loaded
-  // into registers before phase A, so they stream with the gate/up bricks
+  // DR == 8: the down task's weights (every step of every wave) go into
+  // registers when phase A is done, before the wait for the start signal
   const int rnkt = I / 32;
   const int rSB = (rnkt + 3) >> 2;               // down steps of 4 bricks
   const int rn = G * rSB;                        // 0: no pick on the GPU, no start signal comes
   const int rSWB = (rn + NW - 1) / NW;           // <= kDecResSteps (checked by the host)
   u32x4 wv2[DR == 8 ? kDecResSteps : 1][2];
   float f1[DR == 8 ? kDecResSteps : 1];
-  if constexpr (DR == 8) {
-    const size_t dn_bytes = (size_t)H * I * 2;
-    const int t = tb0;
-    const int t16 = t >> 1;
-    const uint32_t lo = (uint32_t)(r >> 3) * 1024u + (uint32_t)(16 * j + 8 * (t & 1) + (r & 7)) * 16u;
-#pragma unroll
-    for (int d = 0; d < kDecResSteps; ++d) {
-      const int q = wv * rSWB + d;
-      const bool ok = myB > 0 && d < rSWB && q < rn;
-      const int qq = ok ? q : 0;
-      const int g = qq / rSB, s = qq - g * rSB;
-      const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;
-      const __amdgpu_buffer_rsrc_t wr =
-          make_rsrc((const char*)a.w_down + (size_t)slot * dn_bytes + (size_t)t16 * rnkt * 1024, (uint32_t)(rnkt * 1024));
-      const uint32_t wo = oob_sel(ok, (uint32_t)s * 4096u + lo);
-      wv2[d][0] = bload_nt(wr, wo);
-      wv2[d][1] = bload_nt(wr, oob_sel(ok, wo + 2048u));
-      f1[d] = ok ? s_gw[g * kDecTok + r] : 0.f;
-    }
-  }
-
   // ================= phase A: gate/up + SwiGLU
   {
     u32x4 wb[D][2], ob[D][XN];   // weight bricks and x of D steps
@@ -438,6 +417,27 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
         }
         issue(d);
       }
+    }
+  }
+
+  if constexpr (DR == 8) {
+    const size_t dn_bytes = (size_t)H * I * 2;
+    const int t = tb0;
+    const int t16 = t >> 1;
+    const uint32_t lo = (uint32_t)(r >> 3) * 1024u + (uint32_t)(16 * j + 8 * (t & 1) + (r & 7)) * 16u;
+#pragma unroll
+    for (int d = 0; d < kDecResSteps; ++d) {
+      const int q = wv * rSWB + d;
+      const bool ok = myB > 0 && d < rSWB && q < rn;
+      const int qq = ok ? q : 0;
+      const int g = qq / rSB, s = qq - g * rSB;
+      const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;
+      const __amdgpu_buffer_rsrc_t wr =
+          make_rsrc((const char*)a.w_down + (size_t)slot * dn_bytes + (size_t)t16 * rnkt * 1024, (uint32_t)(rnkt * 1024));
+      const uint32_t wo = oob_sel(ok, (uint32_t)s * 4096u + lo);
+      wv2[d][0] = bload_nt(wr, wo);
+      wv2[d][1] = bload_nt(wr, oob_sel(ok, wo + 2048u));
+      f1[d] = ok ? s_gw[g * kDecTok + r] : 0.f;
     }
   }
 
@@ -1224,7 +1224,7 @@ struct DecOcc {
   int fu[2][2] = {{0, 0}, {0, 0}};   // [FP8][8-row down tasks]
 };
 constexpr int kDecD_BF16 = 4;   // register-ring depth in 2-brick steps
-constexpr int kDecD_RES = 2;    // the same with the down weights held in registers through phase A (DR = 8)
+constexpr int kDecD_RES = 4;    // the same for the form with register-resident down weights (DR = 8)
 constexpr int kDecD_FP8 = 3;    // (FP8 steps carry twice the x operand: a shallower ring keeps 2 workgroups per CU)
 constexpr int kDecW = 8;   // waves per workgroup
 static std::mutex g_occ_mu;
