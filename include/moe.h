@@ -269,8 +269,8 @@ moe_status moe_cache_destroy(moe_cache_t c);
  * Change the cache's slot count at a safe point (between layer calls, no
  * prefill pool alive) ([FTK] safe-point paragraph: the memory budget between
  * KV cache and expert cache is re-split at run time, and since the host pool
- * is the ground truth a smaller GPU cache changes no output; [FT] third
- * challenge: the budget shrinks or grows without a restart).  The new
+ * is the ground truth a smaller GPU cache changes no output; [FT] section
+ * "挑战三": the budget shrinks or grows without a restart).  The new
  * capacity is slots->n_slots (same weight type, H and I).  The cache keeps
  * its min(residents, new C) most recent residents with their stamps: one in
  * a slot below the new C stays there, the others move, in ascending order of

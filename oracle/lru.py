@@ -126,7 +126,7 @@ class ExpertCache:
     def resize(self, new_C: int):
         """Change the number of slots at a safe point between layer calls.
 
-        [FTK] (safe-point paragraph) and [FT] (third challenge): the memory
+        [FTK] (safe-point paragraph) and [FT] (section "挑战三"): the memory
         budget is re-split at run time without a restart; the host pool is
         the ground truth, so a smaller GPU cache changes no output.  Readings:
         no slot may be reserved; the cache keeps its min(residents, new_C)
