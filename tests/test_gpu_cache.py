@@ -310,3 +310,20 @@ def test_argument_errors():
     with pytest.raises(b.MoeError) as ei:
         b.Cache(1, 8, 2, 2, hz.pool, tabs, 118, 475)
     assert ei.value.status == -4                          # MOE_ERR_NOT_PINNED
+
+
+@pytest.mark.parametrize("T", [1, 4, 16])
+def test_route_step_fp8_decode_trace_full_shape(T):
+    """The FP8 decode workload's cache: 58 layers x 256 experts, top-8, a
+    1633-slot pool (11%), 118:475, its sticky trace at T tokens per step,
+    through the fused router + step as the benchmark runs it: ids, weights,
+    decisions and tables bit-exact against the oracle (metadata only)."""
+    c = CONFIGS["decode_fp8"]
+    C = c.C
+    steps = 6 if T < 16 else 3
+    picks, logits = gen.decode_trace(c.cfg_id, c.L, steps, c.E, c.k, c.p_keep, T=T, salt=T)
+    hz = Harness(c.L, c.E, C, T, c.k, c.bp, c.bh, copy=False)
+    for s in range(steps):
+        for l in range(c.L):
+            hz.route_step(l, logits[s, l])
+    hz.compare_tables()
