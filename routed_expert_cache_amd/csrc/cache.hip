@@ -1221,7 +1221,12 @@ extern "C" moe_status moe_cache_resize(moe_cache_t c, const moe_slots* slots, vo
   const WsLayout L = ws_layout(&ncfg, 5);
   if (ws_bytes < L.total) MOE_FAIL(MOE_ERR_NO_SPACE, "workspace %zu < %zu bytes", ws_bytes, L.total);
   char* nws = (char*)dev_ws;
-  if (nws < c->ws + c->ws_used && c->ws < nws + L.total)
+  // address ranges as integers: the two allocations are unrelated objects
+  const auto overlap = [](const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
+    return x < y + nb && y < x + na;
+  };
+  if (overlap(nws, L.total, c->ws, c->ws_used))
     MOE_FAIL(MOE_ERR_ARG, "the new workspace overlaps the cache's current one");
   int dev = 0, lds_max = 0;
   MOE_HIP(hipGetDevice(&dev));
@@ -1234,14 +1239,12 @@ extern "C" moe_status moe_cache_resize(moe_cache_t c, const moe_slots* slots, vo
   const void* nbk[5] = {slots->w_gate_up, slots->w_down, slots->s_gate, slots->s_up, slots->s_down};
   int same = 0;
   for (int b = 0; b < c->nb; ++b) {
-    const char* o = (const char*)ob[b];
-    const char* n = (const char*)nbk[b];
-    if (o == n) {
+    if (ob[b] == nbk[b]) {
       ++same;
       continue;
     }
     const size_t bo = (size_t)c->cfg.C * c->bb.b[b], bn = (size_t)ncfg.C * c->bb.b[b];
-    if (n < o + bo && o < n + bn) MOE_FAIL(MOE_ERR_ARG, "bank %d of the new slots overlaps the old one", b);
+    if (overlap(nbk[b], bn, ob[b], bo)) MOE_FAIL(MOE_ERR_ARG, "bank %d of the new slots overlaps the old one", b);
   }
   if (same != 0 && same != c->nb) MOE_FAIL(MOE_ERR_ARG, "move every bank or none");
   const int copy_all = same == 0;
