@@ -422,6 +422,10 @@ def run_decode(b, K, W, host_GBps=None, host_branch=True):
             wall_minus_fill_events_ms_per_step=(wall - fill_s) / K * 1e3,
             fill_ms_per_step=fill_s / K * 1e3,
             fill_GBps=(d[4] * S / fill_s / 1e9) if fill_s > 0 else None,
+            fill_roofline=dict(bound="pcie", achieved=(d[4] * S / fill_s / 1e9) if fill_s > 0 else None,
+                               peak=PEAK_PCIE_GBPS, unit="GB/s",
+                               frac=(d[4] * S / fill_s / 1e9 / PEAK_PCIE_GBPS) if fill_s > 0 else None,
+                               what="cache_fill_kernel: mapped pinned host memory -> slots, per fill event"),
             miss_rate=float(d[3] / d[1]),
             experts_on_gpu_per_layer_call=n_g / (K * L),
             fills_per_layer_call=float(d[4] / (K * L)),
