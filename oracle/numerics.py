@@ -41,7 +41,16 @@ def e4m3_to_f64(codes) -> np.ndarray:
 
 
 def dequant_b128(codes, scales, block: int = 128) -> np.ndarray:
-    """[R, Cc] codes with [R/b, Cc/b] float32 scales -> float64 weights."""
-    v = e4m3_to_f64(codes)
-    s = np.asarray(scales, dtype=np.float32).astype(np.float64)
-    return v * np.repeat(np.repeat(s, block, axis=0), block, axis=1)
+    """[R, Cc] codes with [R/b, Cc/b] float32 scales -> float64 weights:
+    element (r, c) is the code's value times the scale of tile (r//b, c//b).
+
+    The table lookup and the product run as torch CPU ops (multi-threaded;
+    numpy's gather takes seconds per expert matrix at full size); each
+    element is still the one float64 product of the exact code value and its
+    tile's scale, so the result is bit for bit the same as numpy's."""
+    import torch
+    c = torch.from_numpy(np.ascontiguousarray(codes, dtype=np.uint8))
+    R, Cc = c.shape
+    v = torch.from_numpy(E4M3_VALUES)[c.long()]
+    s = torch.from_numpy(np.asarray(scales, dtype=np.float32).astype(np.float64))
+    return (v.view(R // block, block, Cc // block, block) * s[:, None, :, None]).reshape(R, Cc).numpy()

@@ -304,3 +304,66 @@ def test_partition_invariance():
         assert np.allclose(yg + yh, y_all, rtol=1e-12, atol=1e-13)
     yg, yh = ffn.moe_partials(x, ids, w, lambda e: Ws[e], on_gpu=np.zeros(ids.shape, bool))
     assert np.all(yg == 0)
+
+
+def test_moe_partials_hand_worked_two_picks():
+    """[FT] q* policy and [FT] "Graph 内的 CPU 执行分支": each pick carries its
+    own gate weight and its own GPU/host route, and the gate weight scales
+    that expert's output.  Two tokens x two picks of scalar experts
+    (H = I = 1) with a gate weight of 100, so that for x > 0 silu(100 x) =
+    100 x exactly in float64 (e^-100 x is below half an ulp) and
+    FFN_e(x) = c_e * (100 x) * (b_e x) = 100 b_e c_e x^2 by hand:
+      expert 0: b = 0.5, c = 0.01  ->  FFN_0(x) = 0.5 x^2
+      expert 1: b = 2,   c = -0.03 ->  FFN_1(x) = -6 x^2
+    Token 0 (x = 1): pick 0 = expert 1, w 0.75, on the GPU; pick 1 = expert
+    0, w 0.25, on the host.  Token 1 (x = 2): pick 0 = expert 0, w 0.6, on
+    the GPU; pick 1 = expert 1, w 0.4, on the host.  A weight or a route
+    attached to the wrong pick (transposed, or taken from the other token)
+    changes every one of the four values."""
+    Ws = {0: (np.array([[100.0]]), np.array([[0.5]]), np.array([[0.01]])),
+          1: (np.array([[100.0]]), np.array([[2.0]]), np.array([[-0.03]]))}
+    x = np.array([[1.0], [2.0]])
+    ids = np.array([[1, 0], [0, 1]])
+    w = np.array([[0.75, 0.25], [0.6, 0.4]])
+    on_gpu = np.array([[True, False], [True, False]])
+    yg, yh = ffn.moe_partials(x, ids, w, lambda e: Ws[e], on_gpu=on_gpu)
+    # by hand: 0.75 * -6 * 1, 0.25 * 0.5 * 1, 0.6 * 0.5 * 4, 0.4 * -6 * 4
+    assert yg[0, 0] == pytest.approx(-4.5, rel=1e-15)
+    assert yh[0, 0] == pytest.approx(0.125, rel=1e-15)
+    assert yg[1, 0] == pytest.approx(1.2, rel=1e-15)
+    assert yh[1, 0] == pytest.approx(-9.6, rel=1e-15)
+    # the other split of the same picks: both of token 0 on the host, both of token 1 on the GPU
+    yg2, yh2 = ffn.moe_partials(x, ids, w, lambda e: Ws[e], on_gpu=np.array([[False, False], [True, True]]))
+    assert yg2[0, 0] == 0 and yh2[1, 0] == 0
+    assert yh2[0, 0] == pytest.approx(-4.5 + 0.125, rel=1e-15)
+    assert yg2[1, 0] == pytest.approx(1.2 - 9.6, rel=1e-15)
+    # all on the GPU: the layer output
+    y = ffn.moe_output(x, ids, w, lambda e: Ws[e])
+    assert y[0, 0] == pytest.approx(-4.375, rel=1e-15) and y[1, 0] == pytest.approx(-8.4, rel=1e-15)
+
+
+def test_moe_partials_hand_worked_vector_rows():
+    """The same association with H = 2, I = 1 and the picks' order reversed
+    in token 1, so the output rows are distinct vectors: expert e has gate
+    row [100, 0], up row [b_e, 0] and down column [c_e, d_e]; for x = (s, t)
+    with s > 0, FFN_e(x) = 100 b_e s^2 (c_e, d_e)."""
+    Ws = {0: (np.array([[100.0, 0.0]]), np.array([[0.5, 0.0]]), np.array([[0.01], [0.02]])),
+          1: (np.array([[100.0, 0.0]]), np.array([[2.0, 0.0]]), np.array([[-0.03], [0.01]])),
+          2: (np.array([[100.0, 0.0]]), np.array([[1.0, 0.0]]), np.array([[0.0], [-0.01]]))}
+    # 100 b c s^2 and 100 b d s^2 per expert at s = 1 and s = 2
+    ffn0 = lambda s: np.array([0.5, 1.0]) * s * s
+    ffn1 = lambda s: np.array([-6.0, 2.0]) * s * s
+    ffn2 = lambda s: np.array([0.0, -1.0]) * s * s
+    x = np.array([[1.0, 5.0], [2.0, -3.0]])
+    ids = np.array([[2, 0, 1], [1, 2, 0]])
+    w = np.array([[0.5, 0.3, 0.2], [0.1, 0.7, 0.2]])
+    on_gpu = np.array([[True, False, True], [False, True, True]])
+    yg, yh = ffn.moe_partials(x, ids, w, lambda e: Ws[e], on_gpu=on_gpu)
+    exp_g0 = 0.5 * ffn2(1.0) + 0.2 * ffn1(1.0)
+    exp_h0 = 0.3 * ffn0(1.0)
+    exp_g1 = 0.7 * ffn2(2.0) + 0.2 * ffn0(2.0)
+    exp_h1 = 0.1 * ffn1(2.0)
+    np.testing.assert_allclose(yg[0], exp_g0, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(yh[0], exp_h0, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(yg[1], exp_g1, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(yh[1], exp_h1, rtol=1e-14, atol=1e-15)
