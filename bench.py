@@ -124,6 +124,20 @@ def pmc_summary(fetch_dir, write_dir, bench_json):
     print(json.dumps(out, indent=1))
 
 
+def assert_clean(what, cache=None, ws=None):
+    """After a pass: the decode forward's hand-over word (first word of its
+    workspace: non-zero when a bounded wait gave up and y is invalid) and the
+    cache's device error word must both be clear, else the pass is not timed."""
+    import torch
+    torch.cuda.synchronize()
+    if ws is not None:
+        word = int(ws[:4].view(torch.int32).item())
+        assert word == 0, "%s: the decode forward's hand-over timed out (ws word %d); y is invalid" % (what, word)
+    if cache is not None:
+        code = cache.error()
+        assert code == 0, "%s: the cache kernels flagged bad data (error word %d)" % (what, code)
+
+
 def calibrate_copy():
     import torch
     src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
@@ -294,6 +308,7 @@ def run_decode(b, K, W, host_GBps=None, host_branch=True):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         d = cache.read_state()[4].astype(np.int64) - c0    # calls, uniq, hits, misses, fills, host
+        assert_clean("decode pass", cache, ws)
         cache.destroy()
         return wall, d
 
@@ -370,6 +385,7 @@ def run_decode(b, K, W, host_GBps=None, host_branch=True):
             torch.cuda.synchronize()
             wall_h = time.perf_counter() - t0
             dh = cache4.read_state()[4].astype(np.int64) - c0
+            assert_clean("decode host-branch pass", cache4, ws)
             cache4.destroy()
             assert ex.status() == 0 and int(err.item()) == 0, "the host branch failed"
             return wall_h, dh
@@ -405,6 +421,7 @@ def run_decode(b, K, W, host_GBps=None, host_branch=True):
     torch.cuda.synchronize()
     burst_s = sum(evb.ms(2 * si, 2 * si + 1) for si in range(K)) / 1e3
     evb.close()
+    assert_clean("decode forward-only burst", None, ws)
     n_g = int(d[2] + d[4])
     gpu_bytes = n_g * S
     res = dict(
@@ -618,6 +635,7 @@ def run_decode_fp8(b, K, W, Ts=(1, 4, 16)):
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
         c1 = cache.read_state()[4].astype(np.int64)
+        assert_clean("decode fp8 T=%d" % T, cache, ws)
         cnts = torch.stack(fwd_counts_dev).cpu().numpy()
         n_g = int(cnts[:, 1].sum() + cnts[:, 4].sum())                  # layer-0 hits + fills
         fill_s = sum(ev.ms(3 * i, 3 * i + 1) for i in range(K)) / 1e3
@@ -705,6 +723,7 @@ def run_prefill_fp8(b):
     run(False)                                                       # warm-up
     wall_o, fwd_o = run(False)
     wall_s, fwd_s = run(True)
+    assert_clean("prefill fp8 double buffer", cache)
     # hand-over: the two buffers' layers become the decode cache's residents
     t0 = time.perf_counter()
     pf.finish()
@@ -765,6 +784,7 @@ def run_prefill_fp8(b):
     c0 = cache_d.read_state()[4].astype(np.int64)
     wall_d, load_d, fwd_d = run_on_demand()
     dd = cache_d.read_state()[4].astype(np.int64) - c0
+    assert_clean("prefill fp8 on-demand loading", cache_d)
     host_left = int((pick_d < 0).sum())
     cache_d.destroy()
     del pool_d, cache_d

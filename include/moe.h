@@ -197,24 +197,32 @@ moe_status moe_cache_seed(moe_cache_t c, const int32_t* host_ids, int32_t n,
  * fixed-grid copy kernel moves every bank of each filled expert from the
  * pinned host pool into its slot, masked by the device fill count ([FT]
  * section "Device-side 缓存控制": one fused transfer over all banks).
- * ids: device int32 [T, k] expert indices of `layer` (0 <= layer < L).
- * 1 <= T <= T_max.  An id outside [0, E) sets the cache's device error word
- * and is treated as routed to the host.  Capturable.
+ * d_layer: DEVICE int32 scalar holding the layer (0 <= layer < L), read by
+ * the kernel when it runs, so one captured graph of a layer call serves
+ * every layer ([FT] section "执行顺序与工程细节": the per-layer control flow is
+ * captured once and replayed; [FT] section "Device-side 缓存控制": no host
+ * decision per layer).  A layer outside [0, L) sets the device error word
+ * (moe_cache_error) and the call decides nothing: tables unchanged, every
+ * pick -1, lists -1, counts 0 (counts[6] = the bad layer), no fill.
+ * ids: device int32 [T, k] expert indices of that layer.  1 <= T <= T_max.
+ * An id outside [0, E) sets the device error word and is treated as routed
+ * to the host.  Capturable.
  */
-moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t* ids, int32_t T,
+moe_status moe_cache_step(moe_cache_t c, const int32_t* d_layer, const int32_t* ids, int32_t T,
                           uint32_t flags, const moe_step_out* out, hipStream_t stream);
 
 /*
  * Router and cache step in one launch: the same results as
  * moe_route_topk(logits, T, E, k, ids, w) followed by
- * moe_cache_step(c, layer, ids, T, flags, out) (bit for bit: the same
+ * moe_cache_step(c, d_layer, ids, T, flags, out) (bit for bit: the same
  * selection and softmax code), with one kernel instead of two on the decode
  * path ([FT] section "Device-side 缓存控制": routing feeds the one control
- * kernel; [FTK] GPU-router paragraph).  logits: device float32 [T, E];
- * ids: device int32 [T, k] and w: device float32 [T, k], both written.
- * Needs E <= 1024 and k <= 32.  Capturable.
+ * kernel; [FTK] GPU-router paragraph).  d_layer: device int32 scalar, as
+ * for moe_cache_step (a bad layer also leaves ids and w unwritten).
+ * logits: device float32 [T, E]; ids: device int32 [T, k] and w: device
+ * float32 [T, k], both written.  Needs E <= 1024 and k <= 32.  Capturable.
  */
-moe_status moe_cache_route_step(moe_cache_t c, int32_t layer, const float* logits, int32_t T,
+moe_status moe_cache_route_step(moe_cache_t c, const int32_t* d_layer, const float* logits, int32_t T,
                                 int32_t* ids, float* w, uint32_t flags, const moe_step_out* out,
                                 hipStream_t stream);
 
@@ -382,7 +390,10 @@ moe_status moe_prefill_create_ring(moe_cache_t c, int32_t depth, moe_prefill_t* 
 /*
  * Enqueue on copy_stream: wait until buffer (layer % depth) is released, copy ALL
  * E experts of `layer` (every bank) from the pinned host pool into it
- * (without waiting for routing), then mark it ready.
+ * (without waiting for routing), then mark it ready.  MOE_ERR_STATE (nothing
+ * enqueued) if the layer the buffer holds has not been released by
+ * moe_prefill_release since its own prefetch: the copy would overwrite
+ * weights that compute may still be reading.
  */
 moe_status moe_prefill_prefetch(moe_prefill_t p, int32_t layer, hipStream_t copy_stream);
 
@@ -455,10 +466,26 @@ moe_status moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStr
  * moe_host_exec_simd returns 512 for an executor on the AVX-512 path, else 0.
  */
 #define MOE_HOST_PORTABLE 1u
+#define MOE_HOST_PIN 2u
 typedef struct moe_host_exec* moe_host_exec_t;
 moe_status moe_host_exec_create(int32_t n_threads, uint32_t flags, moe_host_exec_t* out);
 moe_status moe_host_exec_destroy(moe_host_exec_t h);
 int32_t moe_host_exec_simd(moe_host_exec_t h);
+
+/*
+ * Core placement ([FT] section "Graph 内的 CPU 执行分支": a resident pool of
+ * worker threads pinned to physical cores).  With MOE_HOST_PIN in the flags
+ * of moe_host_exec_create, thread i is pinned to entry i (modulo its length)
+ * of this list: the CPUs of the process's affinity set, one per physical
+ * core first (the lowest allowed SMT sibling of each core), the cores of the
+ * NUMA node the current HIP device is attached to before the others, then
+ * the remaining siblings in the same order.  Thread 0 is the caller's
+ * thread in moe_host_forward (left alone) and the dispatcher thread in the
+ * signalled form (pinned).  Without the flag the threads are not pinned.
+ * moe_host_exec_cpus writes the CPU of threads 0 .. n-1 (-1: not pinned, or
+ * beyond the pool) and the device's NUMA node (-1 if unknown).
+ */
+moe_status moe_host_exec_cpus(moe_host_exec_t h, int32_t* cpus, int32_t n, int32_t* numa_node);
 
 /*
  * y_host[t] = sum over picks j with pick_slot[t,j] < 0 of
@@ -526,6 +553,37 @@ moe_status moe_host_forward_signal(moe_host_exec_t h, const moe_host_pool* pool,
 moe_status moe_merge_partial_after(const float* y_gpu, const float* y_host, const uint32_t* done, uint32_t seq,
                                    int32_t T, int32_t H, float* y_out, uint16_t* y_out_bf16, uint32_t* err,
                                    hipStream_t stream);
+
+/*
+ * Bandwidth calibration for the q* split ([FT] section "q* 策略": B_P and B_H
+ * are measured on the deployed machine at the deployed tensor shapes before
+ * serving; [FT] section "挑战二": the right split is machine-specific).
+ * Copies the n experts `ids` (host array of logical ids of the cache's host
+ * pool) into scratch slots 0 .. n-1, once untimed and then `reps` times
+ * timed with HIP events on `stream`, through
+ *   - the fused fill kernel (mapped pinned host memory; the decode fill path):
+ *     fill_GBps, and bp = round(10 * fill_GBps), the cache's B_P unit;
+ *   - hipMemcpyAsync per bank (the DMA engines; the prefill buffers' path):
+ *     dma_GBps;
+ * and, if hx is not NULL, evaluates them on the host executor as the host
+ * set of decode-shaped calls (one token, min(8, n) host picks per call,
+ * cycling through the ids), once untimed and then `reps` times:
+ * host_GBps and bh = round(10 * host_GBps) (else 0).  Rates count every
+ * bank's bytes (expert_bytes per expert).  The cache's tables and slots are
+ * not touched; the fill list uses the cache's seed scratch.  scratch:
+ * device slots of the cache's weight type, H and I with n_slots >= n
+ * (caller-owned; overwritten).  1 <= n <= C, 1 <= reps <= 1000.
+ * Synchronises `stream`; not capturable.
+ */
+typedef struct moe_bandwidth {
+  uint32_t bp, bh;         /* B_P (fill kernel) and B_H (host executor) in 0.1 GB/s */
+  double fill_GBps;        /* fused fill kernel, pinned host -> device       */
+  double dma_GBps;         /* hipMemcpyAsync, pinned host -> device           */
+  double host_GBps;        /* host executor, expert bytes evaluated per second */
+  double expert_bytes;     /* bytes of one expert over every bank            */
+} moe_bandwidth;
+moe_status moe_calibrate_bandwidth(moe_cache_t c, moe_host_exec_t hx, const int32_t* ids, int32_t n,
+                                   const moe_slots* scratch, int32_t reps, hipStream_t stream, moe_bandwidth* out);
 
 /*
  * Measurement: the calls of moe_host_forward (direct or enqueued) that had

@@ -25,6 +25,7 @@ W_BF16, W_FP8_B128 = 0, 1
 STEP_NO_COPY = 1
 STEP_FILL_ALL = 2
 HOST_PORTABLE = 1
+HOST_PIN = 2
 FWD_DECODE, FWD_PREFILL = 0, 1
 CNT_UNIQ, CNT_HIT, CNT_MISS, CNT_QSTAR, CNT_FILL, CNT_HOST, CNT_N = 0, 1, 2, 3, 4, 5, 8
 
@@ -37,9 +38,9 @@ EXPORTS = [
     "moe_prefill_destroy", "moe_prefill_create_ring", "moe_prefill_finish", "moe_cache_prefill_load",
     "moe_cache_resize",
     "moe_e4m3_to_bf16", "moe_pack_weights", "moe_stream_read",
-    "moe_host_exec_create", "moe_host_exec_destroy", "moe_host_exec_simd", "moe_host_forward",
+    "moe_host_exec_create", "moe_host_exec_destroy", "moe_host_exec_simd", "moe_host_exec_cpus", "moe_host_forward",
     "moe_host_forward_enqueue", "moe_host_exec_status", "moe_host_exec_stats",
-    "moe_host_signal", "moe_host_forward_signal", "moe_merge_partial_after",
+    "moe_host_signal", "moe_host_forward_signal", "moe_merge_partial_after", "moe_calibrate_bandwidth",
 ]
 
 
@@ -73,16 +74,21 @@ class StepOutC(ctypes.Structure):
                 ("pick_slot", "uniq", "is_hit", "fill_id", "fill_slot", "fill_evicted", "host_id", "counts")]
 
 
+class Bandwidth(ctypes.Structure):
+    _fields_ = [("bp", ctypes.c_uint32), ("bh", ctypes.c_uint32), ("fill_GBps", ctypes.c_double),
+                ("dma_GBps", ctypes.c_double), ("host_GBps", ctypes.c_double), ("expert_bytes", ctypes.c_double)]
+
+
 _vp, _i32, _u32, _sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_size_t
 _P = ctypes.POINTER
 _sig = {
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_route_topk": (_i32, [_vp, _i32, _i32, _i32, _vp, _vp, _vp]),
     "moe_cache_workspace_bytes": (_i32, [_P(CacheCfg), _P(_sz)]),
-    "moe_cache_route_step": (_i32, [_vp, _i32, _vp, _i32, _vp, _vp, _u32, _P(StepOutC), _vp]),
+    "moe_cache_route_step": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp, _u32, _P(StepOutC), _vp]),
     "moe_cache_create": (_i32, [_P(CacheCfg), _P(Slots), _P(HostPool), _vp, _sz, _vp, _P(_vp)]),
     "moe_cache_seed": (_i32, [_vp, _P(_i32), _i32, _u32, _vp]),
-    "moe_cache_step": (_i32, [_vp, _i32, _vp, _i32, _u32, _P(StepOutC), _vp]),
+    "moe_cache_step": (_i32, [_vp, _vp, _vp, _i32, _u32, _P(StepOutC), _vp]),
     "moe_cache_fill": (_i32, [_vp, _P(StepOutC), _vp]),
     "moe_cache_read_state": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "moe_cache_error": (_i32, [_vp, _P(_i32), _vp]),
@@ -107,6 +113,7 @@ _sig = {
     "moe_host_exec_create": (_i32, [_i32, _u32, _P(_vp)]),
     "moe_host_exec_destroy": (_i32, [_vp]),
     "moe_host_exec_simd": (_i32, [_vp]),
+    "moe_host_exec_cpus": (_i32, [_vp, _vp, _i32, _P(_i32)]),
     "moe_host_forward": (_i32, [_vp, _P(HostPool), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp]),
     "moe_host_forward_enqueue": (_i32, [_vp, _P(HostPool), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                                         _vp]),
@@ -116,6 +123,7 @@ _sig = {
     "moe_host_forward_signal": (_i32, [_vp, _P(HostPool), _i32, _i32, _i32, _vp, _vp, _vp, _vp, _i32, _i32, _vp,
                                        _vp, _vp, _u32]),
     "moe_merge_partial_after": (_i32, [_vp, _vp, _vp, _u32, _i32, _i32, _vp, _vp, _vp, _vp]),
+    "moe_calibrate_bandwidth": (_i32, [_vp, _vp, _P(_i32), _i32, _P(Slots), _i32, _vp, _P(Bandwidth)]),
 }
 for _name, (_res, _args) in _sig.items():
     _f = getattr(_lib, _name)
@@ -249,6 +257,20 @@ class Cache:
                                      _ptr(self.ws), nbytes.value, _stream(stream), ctypes.byref(h)),
                "moe_cache_create")
         self.h = h
+        # device scalars 0 .. L-1: a host layer index is passed as a pointer into this table
+        self.layer_tab = torch.arange(L, dtype=torch.int32, device="cuda")
+
+    def _layer_ptr(self, layer):
+        """A device int32 scalar holding the layer: a 1-element int32 cuda
+        tensor is passed as is, an int through the resident table (an int
+        outside [0, L) goes through a fresh scalar, which the kernel rejects)."""
+        if isinstance(layer, torch.Tensor):
+            assert layer.is_cuda and layer.dtype == torch.int32 and layer.numel() == 1
+            return _ptr(layer)
+        if 0 <= layer < self.cfg.L:
+            return ctypes.c_void_p(self.layer_tab.data_ptr() + 4 * int(layer))
+        self._bad_layer = torch.tensor([int(layer)], dtype=torch.int32, device="cuda")
+        return _ptr(self._bad_layer)
 
     def seed(self, ids, copy=True, stream=None):
         arr = (ctypes.c_int32 * max(1, len(ids)))(*[int(i) for i in ids])
@@ -258,7 +280,8 @@ class Cache:
     def step(self, layer, ids, out: StepOut, copy=True, fill_all=False, stream=None):
         T = ids.shape[0]
         flags = (0 if copy else STEP_NO_COPY) | (STEP_FILL_ALL if fill_all else 0)
-        _check(_lib.moe_cache_step(self.h, layer, _ptr(ids), T, flags, ctypes.byref(out.c), _stream(stream)),
+        _check(_lib.moe_cache_step(self.h, self._layer_ptr(layer), _ptr(ids), T, flags, ctypes.byref(out.c),
+                                   _stream(stream)),
                "moe_cache_step")
 
     def prefill_load(self, layer, ids, out: StepOut, pick_slot=None, copy=True, stream=None):
@@ -275,7 +298,7 @@ class Cache:
         """Router + cache step in one launch; writes ids [T, k] and w [T, k]."""
         T = logits.shape[0]
         assert logits.is_cuda and logits.dtype == torch.float32 and logits.is_contiguous()
-        _check(_lib.moe_cache_route_step(self.h, layer, _ptr(logits), T, _ptr(ids), _ptr(w),
+        _check(_lib.moe_cache_route_step(self.h, self._layer_ptr(layer), _ptr(logits), T, _ptr(ids), _ptr(w),
                                          0 if copy else STEP_NO_COPY, ctypes.byref(out.c), _stream(stream)),
                "moe_cache_route_step")
 
@@ -308,6 +331,17 @@ class Cache:
         _check(_lib.moe_cache_resize(self.h, ctypes.byref(slots.c), _ptr(ws), nbytes.value, _stream(stream)),
                "moe_cache_resize")
         self.cfg, self.ws, self.slots = cfg, ws, slots
+
+    def calibrate(self, ids, scratch: SlotPool, reps=5, host_exec=None, stream=None):
+        """moe_calibrate_bandwidth: B_P through the fill kernel (and the DMA
+        engines) and B_H through the host executor, on experts `ids` of the
+        host pool copied into `scratch`; returns a dict (bp, bh in 0.1 GB/s)."""
+        arr = (ctypes.c_int32 * len(ids))(*[int(i) for i in ids])
+        r = Bandwidth()
+        _check(_lib.moe_calibrate_bandwidth(self.h, host_exec.h if host_exec is not None else None, arr, len(ids),
+                                            ctypes.byref(scratch.c), reps, _stream(stream), ctypes.byref(r)),
+               "moe_calibrate_bandwidth")
+        return {f: getattr(r, f) for f, _ in Bandwidth._fields_}
 
     def destroy(self):
         if self.h:
@@ -426,15 +460,22 @@ class HostExec:
     """The CPU executor of the host set (moe_host_forward): a persistent pool
     of n_threads threads (the caller counts as one)."""
 
-    def __init__(self, n_threads, portable=False):
+    def __init__(self, n_threads, portable=False, pin=False):
         h = ctypes.c_void_p()
-        _check(_lib.moe_host_exec_create(n_threads, HOST_PORTABLE if portable else 0, ctypes.byref(h)),
-               "moe_host_exec_create")
+        flags = (HOST_PORTABLE if portable else 0) | (HOST_PIN if pin else 0)
+        _check(_lib.moe_host_exec_create(n_threads, flags, ctypes.byref(h)), "moe_host_exec_create")
         self.h = h
         self.n_threads = n_threads
 
     def simd(self):
         return _lib.moe_host_exec_simd(self.h)
+
+    def cpus(self):
+        """(CPU of each thread, -1 where not pinned; the GPU's NUMA node or -1)."""
+        arr = (ctypes.c_int32 * self.n_threads)()
+        node = ctypes.c_int32(-1)
+        _check(_lib.moe_host_exec_cpus(self.h, arr, self.n_threads, ctypes.byref(node)), "moe_host_exec_cpus")
+        return list(arr), node.value
 
     def forward(self, pool, wtype, H, I, x, ids, pick_slot, w, y_host=None):
         """Host tensors: x uint16 [T, H] (BF16 bits), ids / pick_slot int32

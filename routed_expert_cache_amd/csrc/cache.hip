@@ -28,6 +28,10 @@
 
 #include "common.h"
 
+#include <chrono>
+#include <cmath>
+#include <functional>
+
 namespace moe {
 
 // ---------------------------------------------------------------- errors
@@ -64,7 +68,7 @@ constexpr int kUMax = 1024;           // T_max * k <= 1024
 constexpr int kEMax = 4096;
 constexpr int kCMax = 16384;
 
-enum { ERR_BAD_ID = 1, ERR_TICK = 2, ERR_TABLE = 3 };
+enum { ERR_BAD_ID = 1, ERR_TICK = 2, ERR_TABLE = 3, ERR_LAYER = 4 };
 
 struct CacheDev {
   int32_t* id_slot;     // [L*E]
@@ -86,6 +90,7 @@ struct StepArgs {
   const int32_t* ids;     // routed ids [T*k] (input, or written when routing in the kernel)
   const float* logits;    // [T*E] when routing in the kernel
   float* w;               // [T*k] gate weights when routing in the kernel
+  const int32_t* d_layer; // device scalar holding the layer, or NULL: `layer` below
   int layer, T, k, U_max;
   int fill_all;           // q* = m (on-demand loading) instead of the bandwidth split
   moe_step_out out;
@@ -136,8 +141,20 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int E = cd.E, C = cd.C, layer = a.layer;
+  const int E = cd.E, C = cd.C;
   const int P = a.T * a.k;
+  // the layer comes from device memory, so one captured step serves any layer
+  const int layer = a.d_layer ? __builtin_amdgcn_readfirstlane(*a.d_layer) : a.layer;
+  if (layer < 0 || layer >= cd.L) {   // uniform: nothing is decided, every pick goes to the host
+    if (tid == 0) atomicOr(cd.error, 1 << ERR_LAYER);
+    for (int p = tid; p < P; p += kDT) a.out.pick_slot[p] = -1;
+    for (int i = tid; i < a.U_max; i += kDT) {
+      a.out.uniq[i] = a.out.is_hit[i] = a.out.host_id[i] = -1;
+      a.out.fill_id[i] = a.out.fill_slot[i] = a.out.fill_evicted[i] = -1;
+    }
+    if (tid < MOE_CNT_N) a.out.counts[tid] = tid == 6 ? layer : 0;
+    return;
+  }
   const int lbase = layer * E;
   const int Cp = round_stage(C), Ep = round_stage(E);
   int* sl = dyn;                                               // slot_id before the step
@@ -1012,17 +1029,17 @@ extern "C" moe_status moe_cache_create(const moe_cache_cfg* cfg, const moe_slots
   return MOE_OK;
 }
 
-static moe_status launch_fill(moe_cache* c, const int32_t* fill_id, const int32_t* fill_slot,
-                              const int32_t* n_fill, hipStream_t stream) {
+static moe_status launch_fill_to(moe_cache* c, const moe_slots& dst, const int32_t* fill_id,
+                                 const int32_t* fill_slot, const int32_t* n_fill, hipStream_t stream) {
   FillArgs f{};
   f.fill_id = fill_id;
   f.fill_slot = fill_slot;
   f.n_fill = n_fill;
   f.host_tab = c->dev.host_tab;
   f.LE = c->cfg.L * c->cfg.E;
-  f.C = c->cfg.C;
+  f.C = dst.n_slots;
   f.nb = c->nb;
-  void* bases[5] = {c->slots.w_gate_up, c->slots.w_down, c->slots.s_gate, c->slots.s_up, c->slots.s_down};
+  void* bases[5] = {dst.w_gate_up, dst.w_down, dst.s_gate, dst.s_up, dst.s_down};
   for (int b = 0; b < c->nb; ++b) {
     f.dst[b] = (char*)bases[b];
     f.bytes[b] = c->bb.b[b];
@@ -1030,6 +1047,11 @@ static moe_status launch_fill(moe_cache* c, const int32_t* fill_id, const int32_
   cache_fill_kernel<<<512, 256, 0, stream>>>(f);
   MOE_LAUNCHED();
   return MOE_OK;
+}
+
+static moe_status launch_fill(moe_cache* c, const int32_t* fill_id, const int32_t* fill_slot,
+                              const int32_t* n_fill, hipStream_t stream) {
+  return launch_fill_to(c, c->slots, fill_id, fill_slot, n_fill, stream);
 }
 
 extern "C" moe_status moe_cache_seed(moe_cache_t c, const int32_t* host_ids, int32_t n, uint32_t flags,
@@ -1063,9 +1085,9 @@ extern "C" moe_status moe_cache_seed(moe_cache_t c, const int32_t* host_ids, int
   return MOE_OK;
 }
 
-static moe_status check_step(moe_cache_t c, int32_t layer, int32_t T, const moe_step_out* out) {
-  if (!c || !out) MOE_FAIL(MOE_ERR_ARG, "null argument");
-  if (layer < 0 || layer >= c->cfg.L) MOE_FAIL(MOE_ERR_SHAPE, "layer %d outside [0, %d)", layer, c->cfg.L);
+static moe_status check_step(moe_cache_t c, const int32_t* d_layer, int32_t T, const moe_step_out* out) {
+  if (!c || !out || !d_layer) MOE_FAIL(MOE_ERR_ARG, "null argument");
+  if (reinterpret_cast<uintptr_t>(d_layer) & 3) MOE_FAIL(MOE_ERR_ARG, "d_layer must be 4-byte aligned");
   if (T < 1 || T > c->cfg.T_max) MOE_FAIL(MOE_ERR_SHAPE, "T=%d outside [1, T_max=%d]", T, c->cfg.T_max);
   if (!out->pick_slot || !out->uniq || !out->is_hit || !out->fill_id || !out->fill_slot || !out->fill_evicted ||
       !out->host_id || !out->counts)
@@ -1073,15 +1095,15 @@ static moe_status check_step(moe_cache_t c, int32_t layer, int32_t T, const moe_
   return MOE_OK;
 }
 
-extern "C" moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t* ids, int32_t T, uint32_t flags,
-                                     const moe_step_out* out, hipStream_t stream) {
+extern "C" moe_status moe_cache_step(moe_cache_t c, const int32_t* d_layer, const int32_t* ids, int32_t T,
+                                     uint32_t flags, const moe_step_out* out, hipStream_t stream) {
   clear_error();
-  moe_status st = check_step(c, layer, T, out);
+  moe_status st = check_step(c, d_layer, T, out);
   if (st) return st;
   if (!ids) MOE_FAIL(MOE_ERR_ARG, "ids is NULL");
   StepArgs a{};
   a.ids = ids;
-  a.layer = layer;
+  a.d_layer = d_layer;
   a.T = T;
   a.k = c->cfg.k;
   a.U_max = c->U_max;
@@ -1094,11 +1116,11 @@ extern "C" moe_status moe_cache_step(moe_cache_t c, int32_t layer, const int32_t
   return MOE_OK;
 }
 
-extern "C" moe_status moe_cache_route_step(moe_cache_t c, int32_t layer, const float* logits, int32_t T,
+extern "C" moe_status moe_cache_route_step(moe_cache_t c, const int32_t* d_layer, const float* logits, int32_t T,
                                            int32_t* ids, float* w, uint32_t flags, const moe_step_out* out,
                                            hipStream_t stream) {
   clear_error();
-  moe_status st = check_step(c, layer, T, out);
+  moe_status st = check_step(c, d_layer, T, out);
   if (st) return st;
   if (!logits || !ids || !w) MOE_FAIL(MOE_ERR_ARG, "null argument");
   const int E = c->cfg.E, k = c->cfg.k;
@@ -1107,7 +1129,7 @@ extern "C" moe_status moe_cache_route_step(moe_cache_t c, int32_t layer, const f
   a.ids = ids;
   a.logits = logits;
   a.w = w;
-  a.layer = layer;
+  a.d_layer = d_layer;
   a.T = T;
   a.k = k;
   a.U_max = c->U_max;
@@ -1288,7 +1310,8 @@ struct moe_prefill {
   std::vector<int> buf_layer;
   std::vector<uint64_t> buf_load;
   std::vector<hipEvent_t> ready, released;
-  std::vector<char> released_recorded;
+  std::vector<char> released_recorded;   // released[b] has been recorded at least once
+  std::vector<char> buf_free;            // the layer buffer b holds (if any) has been released since its prefetch
   ~moe_prefill() {
     for (hipEvent_t e : ready) if (e) (void)hipEventDestroy(e);
     for (hipEvent_t e : released) if (e) (void)hipEventDestroy(e);
@@ -1316,6 +1339,7 @@ extern "C" moe_status moe_prefill_create_ring(moe_cache_t c, int32_t depth, moe_
   p->ready.assign(depth, nullptr);
   p->released.assign(depth, nullptr);
   p->released_recorded.assign(depth, 0);
+  p->buf_free.assign(depth, 1);
   for (int b = 0; b < depth; ++b) {
     hipError_t e1 = hipEventCreateWithFlags(&p->ready[b], hipEventDisableTiming);
     hipError_t e2 = hipEventCreateWithFlags(&p->released[b], hipEventDisableTiming);
@@ -1347,6 +1371,11 @@ extern "C" moe_status moe_prefill_prefetch(moe_prefill_t p, int32_t layer, hipSt
   moe_cache* c = p->c;
   if (layer < 0 || layer >= c->cfg.L) MOE_FAIL(MOE_ERR_SHAPE, "layer %d outside [0, %d)", layer, c->cfg.L);
   const int b = layer % p->D;
+  // the copy may only overwrite the buffer once the layer it holds is released:
+  // waiting on an older release would let the copy overwrite weights that
+  // the compute stream is still reading
+  if (!p->buf_free[b])
+    MOE_FAIL(MOE_ERR_STATE, "buffer %d still holds layer %d, which has not been released", b, p->buf_layer[b]);
   if (p->released_recorded[b]) MOE_HIP(hipStreamWaitEvent(copy_stream, p->released[b], 0));
   const int E = p->E;
   const int slot0 = p->first + b * E;
@@ -1368,6 +1397,7 @@ extern "C" moe_status moe_prefill_prefetch(moe_prefill_t p, int32_t layer, hipSt
   MOE_HIP(hipEventRecord(p->ready[b], copy_stream));
   p->buf_layer[b] = layer;
   p->buf_load[b] = ++p->n_loads;
+  p->buf_free[b] = 0;
   return MOE_OK;
 }
 
@@ -1401,6 +1431,7 @@ extern "C" moe_status moe_prefill_release(moe_prefill_t p, int32_t layer, hipStr
   if (p->buf_layer[b] != layer) MOE_FAIL(MOE_ERR_STATE, "layer %d does not own buffer %d", layer, b);
   MOE_HIP(hipEventRecord(p->released[b], compute));
   p->released_recorded[b] = 1;
+  p->buf_free[b] = 1;
   return MOE_OK;
 }
 
@@ -1442,4 +1473,114 @@ extern "C" moe_status moe_prefill_destroy(moe_prefill_t p, hipStream_t stream) {
   clear_error();
   if (!p) return MOE_OK;
   return prefill_end(p, false, stream);
+}
+
+// ================================================================ bandwidth calibration
+// [FT] section "q* 策略": B_P and B_H are measured on the deployed machine,
+// with the deployed tensor shapes, and feed the split; [FT] section "挑战二":
+// the right split between transfer and host execution is a property of the
+// machine.  B_P is measured through the path decode fills take (the fused
+// fill kernel reading mapped pinned memory) and through the DMA engines
+// (hipMemcpyAsync, the path of the prefill buffers); B_H through the host
+// executor evaluating experts of the pool as a decode step's host set.
+extern "C" moe_status moe_calibrate_bandwidth(moe_cache_t c, moe_host_exec_t hx, const int32_t* ids, int32_t n,
+                                              const moe_slots* scratch, int32_t reps, hipStream_t stream,
+                                              moe_bandwidth* out) {
+  clear_error();
+  if (!c || !ids || !scratch || !out) MOE_FAIL(MOE_ERR_ARG, "null argument");
+  if (n < 1 || n > c->cfg.C || reps < 1 || reps > 1000)
+    MOE_FAIL(MOE_ERR_SHAPE, "calibration needs 1 <= n <= C (%d) and 1 <= reps <= 1000 (n=%d reps=%d)", c->cfg.C, n,
+             reps);
+  moe_status st = check_slots(scratch);
+  if (st) return st;
+  if (scratch->wtype != c->slots.wtype || scratch->H != c->slots.H || scratch->I != c->slots.I ||
+      scratch->n_slots < n)
+    MOE_FAIL(MOE_ERR_SHAPE, "scratch slots must match the cache's weight type, H and I and hold n = %d experts", n);
+  const int LE = c->cfg.L * c->cfg.E;
+  for (int i = 0; i < n; ++i)
+    if (ids[i] < 0 || ids[i] >= LE) MOE_FAIL(MOE_ERR_ARG, "id %d out of range", ids[i]);
+  *out = moe_bandwidth{};
+  size_t expert_bytes = 0;
+  for (int b = 0; b < c->nb; ++b) expert_bytes += c->bb.b[b];
+  out->expert_bytes = (double)expert_bytes;
+  const double bytes = (double)expert_bytes * n;
+
+  // the fill list: ids -> scratch slots 0 .. n-1, in the cache's seed scratch
+  std::vector<int32_t> list(2 * (size_t)n + 1);
+  for (int i = 0; i < n; ++i) {
+    list[i] = ids[i];
+    list[n + i] = i;
+  }
+  list[2 * n] = n;
+  int32_t* dl = c->dev.seed_list;
+  MOE_HIP(hipMemcpyAsync(dl, list.data(), 4 * list.size(), hipMemcpyHostToDevice, stream));
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  MOE_HIP(hipEventCreate(&e0));
+  if (hipEventCreate(&e1) != hipSuccess) {
+    (void)hipEventDestroy(e0);
+    MOE_FAIL(MOE_ERR_HIP, "hipEventCreate failed");
+  }
+  auto timed = [&](const std::function<moe_status()>& body, double* ms) -> moe_status {
+    moe_status s1 = body();   // warm-up
+    if (s1) return s1;
+    if (hipEventRecord(e0, stream) != hipSuccess) MOE_FAIL(MOE_ERR_HIP, "hipEventRecord failed");
+    for (int r = 0; r < reps; ++r)
+      if ((s1 = body())) return s1;
+    if (hipEventRecord(e1, stream) != hipSuccess || hipEventSynchronize(e1) != hipSuccess)
+      MOE_FAIL(MOE_ERR_HIP, "event wait failed");
+    float f = 0.f;
+    if (hipEventElapsedTime(&f, e0, e1) != hipSuccess) MOE_FAIL(MOE_ERR_HIP, "hipEventElapsedTime failed");
+    *ms = f;
+    return MOE_OK;
+  };
+  double ms_fill = 0, ms_dma = 0;
+  st = timed([&] { return launch_fill_to(c, *scratch, dl, dl + n, dl + 2 * n, stream); }, &ms_fill);
+  void* bases[5] = {scratch->w_gate_up, scratch->w_down, scratch->s_gate, scratch->s_up, scratch->s_down};
+  if (!st)
+    st = timed(
+        [&]() -> moe_status {
+          for (int i = 0; i < n; ++i)
+            for (int b = 0; b < c->nb; ++b)
+              MOE_HIP(hipMemcpyAsync((char*)bases[b] + (size_t)i * c->bb.b[b], c->host_ptr[b][ids[i]], c->bb.b[b],
+                                     hipMemcpyHostToDevice, stream));
+          return MOE_OK;
+        },
+        &ms_dma);
+  (void)hipEventDestroy(e0);
+  (void)hipEventDestroy(e1);
+  if (st) return st;
+  out->fill_GBps = bytes * reps / (ms_fill * 1e-3) / 1e9;
+  out->dma_GBps = bytes * reps / (ms_dma * 1e-3) / 1e9;
+  out->bp = (uint32_t)std::max(1.0, std::floor(out->fill_GBps * 10.0 + 0.5));
+
+  if (hx) {
+    // the host executor on decode-shaped calls: one token, k = min(8, n) host
+    // picks per call, cycling through the ids
+    const int H = c->slots.H, I = c->slots.I;
+    const int k = n < 8 ? n : 8;
+    moe_host_pool pool{};
+    pool.w_gate_up = c->host_ptr[0].data();
+    pool.w_down = c->host_ptr[1].data();
+    if (c->nb == 5) {
+      pool.s_gate = (const float* const*)c->host_ptr[2].data();
+      pool.s_up = (const float* const*)c->host_ptr[3].data();
+      pool.s_down = (const float* const*)c->host_ptr[4].data();
+    }
+    std::vector<uint16_t> x((size_t)H, 0x3f80);   // 1.0 in BF16
+    std::vector<int32_t> pid(k), pick(k, -1);
+    std::vector<float> w(k, 1.0f / k), y((size_t)H);
+    auto one = [&](int call) -> moe_status {
+      for (int j = 0; j < k; ++j) pid[j] = ids[(call * k + j) % n];
+      return moe_host_forward(hx, &pool, c->slots.wtype, H, I, x.data(), pid.data(), pick.data(), w.data(), 1, k,
+                              y.data());
+    };
+    if ((st = one(0))) return st;
+    const auto t0 = std::chrono::steady_clock::now();
+    for (int r = 0; r < reps; ++r)
+      if ((st = one(r + 1))) return st;
+    const double sec = std::chrono::duration<double>(std::chrono::steady_clock::now() - t0).count();
+    out->host_GBps = (double)expert_bytes * k * reps / sec / 1e9;
+    out->bh = (uint32_t)std::max(1.0, std::floor(out->host_GBps * 10.0 + 0.5));
+  }
+  return MOE_OK;
 }

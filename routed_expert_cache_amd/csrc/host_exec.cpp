@@ -39,6 +39,14 @@
 #include <thread>
 #include <vector>
 
+#include <pthread.h>
+#include <sched.h>
+
+#include <cctype>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
 namespace moe {
 void set_error(const char* fmt, ...);   // the library's per-thread error message
 void clear_error();
@@ -210,13 +218,107 @@ bool have_avx512() {
   return ok;
 }
 
+// ------------------------------------------------------------ core placement
+// The pages run the host set on a resident pool of threads pinned to
+// physical cores ([FT] section "Graph 内的 CPU 执行分支").  The plan: the
+// CPUs this process may use, one per physical core first (the lowest CPU of
+// each core's SMT siblings), cores on the GPU's NUMA node before the others,
+// then the remaining SMT siblings in the same order; thread i takes entry
+// i (modulo the list).
+std::vector<int> parse_cpulist(const std::string& s) {
+  std::vector<int> out;
+  size_t i = 0;
+  while (i < s.size()) {
+    while (i < s.size() && (s[i] < '0' || s[i] > '9')) ++i;
+    if (i >= s.size()) break;
+    int a = 0;
+    while (i < s.size() && s[i] >= '0' && s[i] <= '9') a = 10 * a + (s[i++] - '0');
+    int b = a;
+    if (i < s.size() && s[i] == '-') {
+      ++i;
+      b = 0;
+      while (i < s.size() && s[i] >= '0' && s[i] <= '9') b = 10 * b + (s[i++] - '0');
+    }
+    for (int c = a; c <= b && c < 65536; ++c) out.push_back(c);
+  }
+  return out;
+}
+
+std::string read_line(const std::string& path) {
+  std::string out;
+  if (FILE* f = std::fopen(path.c_str(), "r")) {
+    char buf[4096];
+    if (std::fgets(buf, sizeof buf, f)) out = buf;
+    std::fclose(f);
+  }
+  return out;
+}
+
+int gpu_numa_node() {
+  int dev = 0;
+  char bus[64] = {0};
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetPCIBusId(bus, sizeof bus, dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return -1;
+  }
+  std::string id(bus);
+  for (char& ch : id) ch = (char)std::tolower((unsigned char)ch);
+  const std::string v = read_line("/sys/bus/pci/devices/" + id + "/numa_node");
+  return v.empty() ? -1 : std::atoi(v.c_str());
+}
+
+std::vector<int> core_plan(int* node_out) {
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  std::vector<int> allowed;
+  if (sched_getaffinity(0, sizeof set, &set) == 0)
+    for (int c = 0; c < CPU_SETSIZE; ++c)
+      if (CPU_ISSET(c, &set)) allowed.push_back(c);
+  const int node = gpu_numa_node();
+  *node_out = node;
+  std::vector<int> local;
+  if (node >= 0) local = parse_cpulist(read_line("/sys/devices/system/node/node" + std::to_string(node) + "/cpulist"));
+  auto is_local = [&](int c) { return std::find(local.begin(), local.end(), c) != local.end(); };
+  // rank 0: the first allowed sibling of its core; rank r: the r-th
+  std::vector<std::pair<int, int>> keyed;   // (sibling rank * 2 + remote, cpu)
+  for (int c : allowed) {
+    std::vector<int> sib = parse_cpulist(
+        read_line("/sys/devices/system/cpu/cpu" + std::to_string(c) + "/topology/thread_siblings_list"));
+    int rank = 0;
+    for (int s2 : sib)
+      if (s2 < c && std::find(allowed.begin(), allowed.end(), s2) != allowed.end()) ++rank;
+    keyed.push_back({rank * 2 + (is_local(c) ? 0 : 1), c});
+  }
+  std::stable_sort(keyed.begin(), keyed.end(),
+                   [](const std::pair<int, int>& a, const std::pair<int, int>& b) { return a.first < b.first; });
+  std::vector<int> out;
+  for (auto& kc : keyed) out.push_back(kc.second);
+  return out;
+}
+
+void pin_self(int cpu) {
+  if (cpu < 0) return;
+  cpu_set_t set;
+  CPU_ZERO(&set);
+  CPU_SET(cpu, &set);
+  (void)pthread_setaffinity_np(pthread_self(), sizeof set, &set);
+}
+
 // ------------------------------------------------------------ thread pool
 // run(n_items, f): f(item) for every item in [0, n_items), spread over the
-// pool threads and the caller; returns when all are done.
+// pool threads and the caller; returns when all are done.  cpus[i], if
+// given, is the CPU worker i (1 <= i < n) is pinned to (entry 0 belongs to
+// the calling thread, which the pool leaves alone).
 class Pool {
  public:
-  explicit Pool(int n) : n_(n) {
-    for (int i = 1; i < n_; ++i) th_.emplace_back([this] { loop(); });
+  Pool(int n, const std::vector<int>& cpus) : n_(n) {
+    for (int i = 1; i < n_; ++i) {
+      const int cpu = cpus.empty() ? -1 : cpus[(size_t)i % cpus.size()];
+      th_.emplace_back([this, cpu] {
+        pin_self(cpu);
+        loop();
+      });
+    }
   }
   ~Pool() {
     {
@@ -326,7 +428,10 @@ struct moe_host_exec {
   std::condition_variable q_cv;
   std::vector<SignalJob> q;
   bool q_stop = false;
-  moe_host_exec(int n, bool s) : pool(n), simd(s) {}
+  std::vector<int> cpus;       // CPU of thread i (0: the dispatcher), empty when not pinned
+  int numa_node = -1;
+  moe_host_exec(int n, bool s, const std::vector<int>& c, int node)
+      : pool(n, c), simd(s), cpus(c), numa_node(node) {}
   ~moe_host_exec() {
     if (dispatcher.joinable()) {
       {
@@ -344,8 +449,18 @@ extern "C" moe_status moe_host_exec_create(int32_t n_threads, uint32_t flags, mo
   if (!out) HX_FAIL(MOE_ERR_ARG, "out is NULL");
   *out = nullptr;
   if (n_threads < 1 || n_threads > 1024) HX_FAIL(MOE_ERR_ARG, "n_threads %d not in [1, 1024]", n_threads);
-  if (flags & ~MOE_HOST_PORTABLE) HX_FAIL(MOE_ERR_ARG, "bad flags %u", flags);
-  moe_host_exec* h = new (std::nothrow) moe_host_exec(n_threads, have_avx512() && !(flags & MOE_HOST_PORTABLE));
+  if (flags & ~(MOE_HOST_PORTABLE | MOE_HOST_PIN)) HX_FAIL(MOE_ERR_ARG, "bad flags %u", flags);
+  std::vector<int> cpus;
+  int node = -1;
+  if (flags & MOE_HOST_PIN) {
+    cpus = core_plan(&node);
+    if (cpus.empty()) HX_FAIL(MOE_ERR_STATE, "no CPU in this process's affinity set");
+    std::vector<int> per_thread;
+    for (int i = 0; i < n_threads; ++i) per_thread.push_back(cpus[(size_t)i % cpus.size()]);
+    cpus.swap(per_thread);
+  }
+  moe_host_exec* h =
+      new (std::nothrow) moe_host_exec(n_threads, have_avx512() && !(flags & MOE_HOST_PORTABLE), cpus, node);
   if (!h) HX_FAIL(MOE_ERR_NO_SPACE, "out of host memory");
   *out = h;
   return MOE_OK;
@@ -358,6 +473,14 @@ extern "C" moe_status moe_host_exec_destroy(moe_host_exec_t h) {
 }
 
 extern "C" int32_t moe_host_exec_simd(moe_host_exec_t h) { return h && h->simd ? 512 : 0; }
+
+extern "C" moe_status moe_host_exec_cpus(moe_host_exec_t h, int32_t* cpus, int32_t n, int32_t* numa_node) {
+  ::moe::clear_error();
+  if (!h || (n > 0 && !cpus)) HX_FAIL(MOE_ERR_ARG, "null argument");
+  for (int i = 0; i < n; ++i) cpus[i] = (i < h->pool.size() && !h->cpus.empty()) ? h->cpus[(size_t)i] : -1;
+  if (numa_node) *numa_node = h->numa_node;
+  return MOE_OK;
+}
 
 extern "C" moe_status moe_host_forward(moe_host_exec_t h, const moe_host_pool* pool, int32_t wtype, int32_t H,
                                        int32_t I, const uint16_t* x, const int32_t* ids, const int32_t* pick_slot,
@@ -506,6 +629,7 @@ namespace {
 constexpr auto kReadyTimeout = std::chrono::seconds(2);
 
 void dispatch_loop(moe_host_exec* h) {
+  if (!h->cpus.empty()) pin_self(h->cpus[0]);   // the calling thread of the signalled form
   for (;;) {
     SignalJob job;
     bool stopping;

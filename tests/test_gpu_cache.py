@@ -84,10 +84,11 @@ class Harness:
             self.orc.seed(list(seed_ids))
         self.copy = copy
 
-    def step(self, layer, ids, fill_all=False):
+    def step(self, layer, ids, fill_all=False, oracle_layer=None):
+        """layer: an int, or a device int32 scalar (then oracle_layer names it)."""
         T = ids.shape[0]
         self.cache.step(layer, dev(ids.astype(np.int32)), self.out, copy=self.copy, fill_all=fill_all)
-        r = self.orc.step(layer, ids, fill_all=fill_all)
+        r = self.orc.step(layer if oracle_layer is None else oracle_layer, ids, fill_all=fill_all)
         self.compare(r, T)
         return r
 
@@ -298,8 +299,6 @@ def test_argument_errors():
     b = binding()
     hz = Harness(1, 8, 4, 2, 2, 118, 475)
     with pytest.raises(b.MoeError):
-        hz.cache.step(1, dev(np.zeros((1, 2), np.int32)), hz.out)        # layer out of range
-    with pytest.raises(b.MoeError):
         hz.cache.step(0, dev(np.zeros((3, 2), np.int32)), hz.out)        # T > T_max
     pageable = [torch.zeros((8, 2 * 32 * 32), dtype=torch.uint16), torch.zeros((8, 32 * 32), dtype=torch.uint16)]
     tabs = b.HostPoolTables.__new__(b.HostPoolTables)
@@ -326,4 +325,35 @@ def test_route_step_fp8_decode_trace_full_shape(T):
     for s in range(steps):
         for l in range(c.L):
             hz.route_step(l, logits[s, l])
+    hz.compare_tables()
+
+
+def test_device_layer_index():
+    """The layer is a device scalar read by the kernel: the same call with the
+    scalar changed in between serves two layers (what one captured graph of a
+    layer call relies on); a layer outside [0, L) sets the device error word
+    and decides nothing (tables unchanged, every pick to the host)."""
+    b = binding()
+    hz = Harness(3, 8, 5, 2, 2, 118, 475, copy=False)
+    d_layer = torch.zeros(1, dtype=torch.int32, device="cuda")
+    rng = np.random.default_rng(12)
+    for s in range(12):
+        layer = int(rng.integers(0, 3))
+        d_layer.fill_(layer)
+        ids = np.stack([rng.choice(8, size=2, replace=False) for _ in range(2)])
+        hz.step(d_layer, ids, oracle_layer=layer)
+    hz.compare_tables()
+    before = hz.cache.read_state()
+    for bad in (3, -1, 1 << 30):
+        d_layer.fill_(bad)
+        hz.cache.step(d_layer, dev(np.array([[0, 1], [2, 3]], np.int32)), hz.out, copy=False)
+        assert np.all(hz.out.pick_slot.cpu().numpy() == -1)
+        cnt = hz.out.counts.cpu().numpy()
+        assert np.all(cnt[:6] == 0) and cnt[6] == bad
+        assert hz.cache.error() != 0
+        assert hz.cache.error() == 0                      # cleared by the read
+    after = hz.cache.read_state()
+    for u, v in zip(before[:3], after[:3]):
+        assert np.array_equal(u, v)
+    assert before[3] == after[3]
     hz.compare_tables()

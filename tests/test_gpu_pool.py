@@ -89,6 +89,23 @@ def test_prefill_pool_errors():
     with pytest.raises(b.MoeError) as ei:
         pf.acquire(1)
     assert ei.value.status == -6                  # MOE_ERR_STATE
+    # a buffer is overwritten only after the layer it holds was released
+    copy = torch.cuda.Stream()
+    pf.prefetch(0, copy)
+    with pytest.raises(b.MoeError) as ei:
+        pf.prefetch(0, copy)                      # layer 0 still holds buffer 0
+    assert ei.value.status == -6
+    pf.acquire(0)
+    with pytest.raises(b.MoeError) as ei:
+        pf.prefetch(0, copy)                      # acquired, not released
+    assert ei.value.status == -6
+    pf.release(0)
+    pf.prefetch(0, copy)                          # released: the buffer may be loaded again
+    pf.prefetch(1, copy)                          # the other buffer is empty
+    with pytest.raises(b.MoeError) as ei:
+        pf.prefetch(1, copy)
+    assert ei.value.status == -6
+    torch.cuda.synchronize()
     pf.destroy()
 
 
@@ -187,3 +204,74 @@ def test_forward_deterministic():
         y1 = b.expert_forward(pool.c, x, ids, w, mode, ws).clone()
         y2 = b.expert_forward(pool.c, x, ids, w, mode, ws)
         assert torch.equal(y1, y2)
+
+
+def test_one_graph_serves_every_layer():
+    """The layer index is a device scalar, so ONE captured graph of a layer
+    call (route + cache step with fills, grouped evaluation, merge) serves
+    every layer: before each replay the layer scalar and the inputs are
+    written, and the replays equal eager calls of the same layers bit for
+    bit (ids, weights, picks, counts, y, tables and slot bytes).  Eager work
+    and synchronisations run between the replays."""
+    b = binding()
+    A = _decode_setup(b)
+    B = _decode_setup(b)
+    L, E, k, H = A["L"], A["E"], A["k"], A["H"]
+    steps = 10
+    rng = np.random.default_rng(5)
+    picks = [np.stack([gen.sticky_trace(gen.np_rng(9, 3, l), steps, E, k, 0.5)[s] for l in range(L)])
+             for s in range(steps)]
+    logits = np.zeros((steps, L, 1, E), np.float32)
+    for s in range(steps):
+        for l in range(L):
+            logits[s, l] = gen.synth_logits(rng, picks[s][l][None], E)
+    xs = gen.to_bf16_bits(rng.standard_normal((steps, L, 1, H)).astype(np.float32))
+    yh = rng.standard_normal((steps, L, 1, H)).astype(np.float32)
+
+    def make_bufs():
+        return dict(layer=torch.zeros(1, dtype=torch.int32, device="cuda"),
+                    lg=torch.zeros((1, E), dtype=torch.float32, device="cuda"),
+                    x=torch.zeros((1, H), dtype=torch.uint16, device="cuda"),
+                    yh=torch.zeros((1, H), dtype=torch.float32, device="cuda"),
+                    ids=torch.zeros((1, k), dtype=torch.int32, device="cuda"),
+                    w=torch.zeros((1, k), dtype=torch.float32, device="cuda"),
+                    out=b.StepOut(1, k, E),
+                    ws=b.forward_workspace(1, k, H, A["I"], A["C"], b.FWD_DECODE),
+                    y=torch.zeros((1, H), dtype=torch.float32, device="cuda"))
+
+    def layer_call(S, bufs):
+        S["cache"].route_step(bufs["layer"], bufs["lg"], bufs["ids"], bufs["w"], bufs["out"], copy=True)
+        b.expert_forward_merge(S["pool"].c, bufs["x"], bufs["out"].pick_slot.view(1, k), bufs["w"], b.FWD_DECODE,
+                               bufs["ws"], bufs["yh"], y_out=bufs["y"])
+
+    ea, gb = make_bufs(), make_bufs()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            layer_call(B, gb)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    assert np.all(B["cache"].read_state()[0] == -1)       # capture ran nothing
+    for st in range(steps):
+        for l in range(L):
+            for bufs in (ea, gb):
+                bufs["layer"].fill_(l)
+                bufs["lg"].copy_(torch.from_numpy(logits[st, l]))
+                bufs["x"].copy_(torch.from_numpy(xs[st, l]))
+                bufs["yh"].copy_(torch.from_numpy(yh[st, l]))
+            layer_call(A, ea)
+            g.replay()
+            torch.cuda.synchronize()
+            for key in ("ids", "w", "y"):
+                assert torch.equal(ea[key], gb[key]), (st, l, key)
+            assert torch.equal(ea["out"].pick_slot, gb["out"].pick_slot)
+            assert torch.equal(ea["out"].counts, gb["out"].counts)
+            assert int(gb["out"].counts[6].item()) == l
+    sa, sb = A["cache"].read_state(), B["cache"].read_state()
+    for u, v in zip(sa[:3], sb[:3]):
+        assert np.array_equal(u, v)
+    assert sa[3] == sb[3] == 1 + steps * L
+    assert torch.equal(A["pool"].w_gu, B["pool"].w_gu) and torch.equal(A["pool"].w_down, B["pool"].w_down)
+    assert A["cache"].error() == 0 and B["cache"].error() == 0

@@ -156,6 +156,36 @@ def test_same_bits_for_any_thread_count():
         assert np.array_equal(o.view(np.uint32), outs[0].view(np.uint32))
 
 
+def test_pinned_workers_same_bits_and_distinct_cores():
+    """MOE_HOST_PIN: worker threads pinned to the allowed CPUs, one per
+    physical core before any SMT sibling, and the results bit for bit those
+    of an unpinned pool."""
+    import os
+    b = binding()
+    bank = BankBF16(204, 5, 128, 64)
+    x, ids, w, host, pick = _case(bank, 9, 4, 0.5, 3)
+    allowed = sorted(os.sched_getaffinity(0))
+    n = min(4, len(allowed))
+    ref_ex, ex = b.HostExec(n), b.HostExec(n, pin=True)
+    try:
+        cpus, node = ex.cpus()
+        assert all(c in allowed for c in cpus)
+        cores = set()
+        for c in allowed:
+            with open("/sys/devices/system/cpu/cpu%d/topology/core_id" % c) as f1, \
+                    open("/sys/devices/system/cpu/cpu%d/topology/physical_package_id" % c) as f2:
+                cores.add((f2.read().strip(), f1.read().strip()))
+        if len(cores) >= n:
+            assert len(set(cpus)) == n                # distinct CPUs while cores last
+        assert ref_ex.cpus()[0] == [-1] * n            # not pinned without the flag
+        y1 = _run(b, ex, bank, x, ids, pick, w)
+        y0 = _run(b, ref_ex, bank, x, ids, pick, w)
+        assert np.array_equal(y1.view(np.uint32), y0.view(np.uint32))
+    finally:
+        ex.destroy()
+        ref_ex.destroy()
+
+
 def test_portable_and_simd_paths_agree():
     b = binding()
     bank = BankFP8(204, 3, 256, 128)
