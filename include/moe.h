@@ -360,6 +360,29 @@ moe_status moe_expert_forward_merge(const moe_slots* slots, const uint16_t* x, c
                                     hipStream_t stream);
 
 /*
+ * For callers that cannot allocate device memory: code under hipGraph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
+ * as moe_expert_forward_merge in MOE_FWD_DECODE mode (the same kernels, the
+ * same bits), with the workspace taken from a static device array of the
+ * library (8.5 MiB per GPU, held until the process ends) instead of a
+ * caller buffer.  The library allocates nothing in this call (no hipMalloc,
+ * hipFree or allocating library routine).  Limit: the call needs
+ * min(T*k, n_slots) * 16 * I * 2 bytes of h within 8 MiB (for example T*k
+ * <= 128 at I = 2048, or <= 256 at I = 1024), else MOE_ERR_NO_SPACE with
+ * nothing enqueued; T <= 16 and T*k <= 256 as in decode mode.  Every call
+ * clears the array's hand-over words with a small kernel before the
+ * forward, so a call that timed out leaves nothing behind.  Every call on
+ * one GPU shares that GPU's array: calls that overlap on one GPU (other
+ * streams, other threads) race and must be serialised by the caller.  The
+ * first call on a device looks up the array's address (hipGetSymbolAddress):
+ * make it outside graph capture.  Capturable after that.
+ */
+moe_status moe_expert_forward_merge_static(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,
+                                           const float* w, int32_t T, int32_t k, float* y_gpu,
+                                           const float* y_host, float* y_out, uint16_t* y_out_bf16,
+                                           hipStream_t stream);
+
+/*
  * Merge of the GPU and host partial sums ([FT] section "q* 策略": the two
  * partial sums are combined exactly; [FT] "Graph 内的 CPU 执行分支").
  * y_out[i] = y_gpu[i] + y_host[i] over T*H floats; if y_out_bf16 != NULL it

@@ -33,6 +33,7 @@ EXPORTS = [
     "moe_last_error", "moe_route_topk", "moe_cache_workspace_bytes", "moe_cache_create",
     "moe_cache_seed", "moe_cache_step", "moe_cache_route_step", "moe_cache_fill", "moe_cache_read_state", "moe_cache_error",
     "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_expert_forward_merge",
+    "moe_expert_forward_merge_static",
     "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_prefill_create_ring", "moe_prefill_finish", "moe_cache_prefill_load",
@@ -97,6 +98,7 @@ _sig = {
     "moe_expert_forward": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _u32, _vp]),
     "moe_expert_forward_merge": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
                                         _u32, _vp]),
+    "moe_expert_forward_merge_static": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_merge_partial": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "moe_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
     "moe_prefill_create": (_i32, [_vp, _P(_vp)]),
@@ -378,6 +380,19 @@ def expert_forward_merge(slots_c, x, pick_slot, w, mode, ws, y_host, y_out=None,
     _check(_lib.moe_expert_forward_merge(ctypes.byref(slots_c), _ptr(x), _ptr(pick_slot), _ptr(w), T, k,
                                          _ptr(y_gpu), _ptr(y_host), _ptr(y_out), _ptr(y_out_bf16),
                                          _ptr(ws), ws.numel(), mode, _stream(stream)), "moe_expert_forward_merge")
+    return y_out
+
+
+def expert_forward_merge_static(slots_c, x, pick_slot, w, y_host, y_out=None, y_gpu=None, y_out_bf16=None,
+                                stream=None):
+    """expert_forward_merge in decode mode with the library's static device
+    scratch as its workspace (no allocation by the library)."""
+    T, k = pick_slot.shape
+    if y_out is None:
+        y_out = torch.empty((T, slots_c.H), dtype=torch.float32, device=x.device)
+    _check(_lib.moe_expert_forward_merge_static(ctypes.byref(slots_c), _ptr(x), _ptr(pick_slot), _ptr(w), T, k,
+                                                _ptr(y_gpu), _ptr(y_host), _ptr(y_out), _ptr(y_out_bf16),
+                                                _stream(stream)), "moe_expert_forward_merge_static")
     return y_out
 
 

@@ -1439,6 +1439,69 @@ extern "C" moe_status moe_expert_forward_merge(const moe_slots* slots, const uin
   return run_forward(slots, x, pick_slot, w, T, k, y_gpu, y_host, y_out, y_out_bf16, ws, ws_bytes, mode, stream);
 }
 
+// ================================================================ allocation-free decode
+// For callers that cannot allocate (hipGraph capture, serving loops, harnesses
+// that forbid hipMalloc): the decode workspace lives in this file-scope
+// device array.  Each GPU the library runs on holds its own copy until the
+// process ends; its device address is looked up once per device and kept.
+namespace moe {
+constexpr size_t kStaticCtrlBytes = 512u << 10;                       // error word, counters, start flags
+constexpr size_t kStaticScratchBytes = (8u << 20) + kStaticCtrlBytes;  // + h: 8 MiB
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[64];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) p[i] = 0u;
+}
+
+static moe_status scratch_ptr(void** out) {
+  int dev = 0;
+  MOE_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= 64) MOE_FAIL(MOE_ERR_ARG, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    MOE_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) MOE_FAIL(MOE_ERR_HIP, "hipGetSymbolAddress returned NULL for the static scratch");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+}  // namespace moe
+
+extern "C" moe_status moe_expert_forward_merge_static(const moe_slots* slots, const uint16_t* x,
+                                                      const int32_t* pick_slot, const float* w, int32_t T, int32_t k,
+                                                      float* y_gpu, const float* y_host, float* y_out,
+                                                      uint16_t* y_out_bf16, hipStream_t stream) {
+  clear_error();
+  moe_status st = check_slots(slots);
+  if (st) return st;
+  if (T < 0 || k < 1) MOE_FAIL(MOE_ERR_SHAPE, "bad T=%d k=%d", T, k);
+  if (T == 0) return MOE_OK;
+  if (!y_host || !y_out) MOE_FAIL(MOE_ERR_ARG, "y_host and y_out are required");
+  if (T > kDecTok || T * k > kDecPmax)
+    MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T <= %d and T*k <= %d (T=%d k=%d)", kDecTok, kDecPmax, T, k);
+  const DecWs L = dec_ws(T, k, slots->H, slots->I, slots->n_slots);
+  if (L.h > kStaticCtrlBytes || L.total > kStaticScratchBytes)
+    MOE_FAIL(MOE_ERR_NO_SPACE,
+             "this call needs %zu bytes of workspace; the static scratch holds %zu (h of min(T*k, n_slots) * 16 * I "
+             "BF16 values must fit 8 MiB)",
+             L.total, kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws))) return st;
+  // the hand-over words must start at zero: a call whose wait timed out may
+  // have left one set, so they are cleared (a kernel, not a memset, so that
+  // the call can be captured) before every call
+  const size_t ctrl_words = L.h / 4;
+  zero_words_kernel<<<(unsigned)std::min<size_t>((ctrl_words + 255) / 256, 256), 256, 0, stream>>>((uint32_t*)ws,
+                                                                                                  ctrl_words);
+  MOE_LAUNCHED();
+  return run_forward(slots, x, pick_slot, w, T, k, y_gpu, y_host, y_out, y_out_bf16, ws, kStaticScratchBytes,
+                     MOE_FWD_DECODE, stream);
+}
+
 extern "C" moe_status moe_merge_partial(const float* y_gpu, const float* y_host, int32_t T, int32_t H, float* y_out,
                                         uint16_t* y_out_bf16, hipStream_t stream) {
   clear_error();
