@@ -713,8 +713,7 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
 constexpr int kSortChunk = 2048;   // least pairs per counting workgroup
 constexpr int kSortMaxChunks = 32; // counting workgroups at most
 constexpr int kSortMaxSlots = 4096;
-constexpr int kPfRows = 512;       // bank rows per tile (4 waves x 128)
-constexpr int kPfStages = 4;       // LDS stages of 40 KB (the whole 160 KB of a CU)
+constexpr int kPfRows = 512;       // bank rows per tile (8 waves x 64)
 
 struct PfArgs {
   const void* w_gu;
@@ -862,39 +861,56 @@ __global__ __launch_bounds__(256) void pf_scatter_kernel(PfArgs a) {
 }
 
 // Grouped GEMM.  Tile = (M tile of one slot: TM sorted pairs) x (512 bank
-// rows).  Eight waves, two per SIMD so that one wave's barrier and load
-// latency hides under the other's MFMAs: wave (wr, wt) owns bank rows
-// [128 wr, 128 wr + 128) against pairs [TM/2 wt, TM/2 wt + TM/2).  K
-// advances one brick per step.  Every operand goes from memory straight
-// into LDS as 1 KB MFMA bricks (buffer loads with an LDS destination: 32
-// weight bricks + 8 token bricks per step, 5 per wave), kPfStages (4) stages
-// deep, so three steps of loads are in flight while the MFMAs of the fourth
-// run; one barrier per step.  A token brick's lane (r, j) fetches 16 bytes of pair
-// row 16g + r at the brick's K offset for group j, so the LDS image is
-// already the MFMA operand.  FP8: two steps make one 128-K scale block; its
-// partial sums are scaled once and added (post-scaling).  Tiles are taken
-// in list order per XCD (workgroup b runs on XCD b % 8) and the list is
-// ordered (slot, bank-row block, M tile), so the M tiles that share a block
-// of weights run side by side and share it through that XCD's L2.
+// rows).  Eight waves, two per SIMD; wave w owns bank rows [64 w, 64 w + 64)
+// of the tile (four brick rows) against every pair of the tile, so no two
+// waves need the same weights.  K advances one weight brick per step.
+// The weight bricks are already MFMA A-operand images: each wave streams its
+// four bricks of a step from memory straight into registers (one contiguous
+// 1 KB wave load each), D steps ahead of the MFMAs in a register ring.  Only
+// the token operand goes through LDS: the token bricks of SPS steps form a
+// stage, loaded from memory straight into LDS (buffer loads with an LDS
+// destination; lane (r, j) of a token brick fetches 16 bytes of its pair's
+// row, so the LDS image is the B operand), NSTG stages deep, one barrier per
+// stage.  A wave reads the token bricks of step st+1 from LDS while the
+// MFMAs of step st run (each brick's register is re-read right after the
+// MFMAs that take it are issued).  FP8: a weight brick is 64 K of E4M3
+// codes, expanded exactly to two BF16 operands in registers; the partial
+// sums of a 128-K scale block (two steps) are multiplied by the block's
+// scale once (post-scaling).  Every load past the last step, or of a pair
+// row past the tile's, is a buffer load pushed out of range: it returns
+// zeros without touching memory, so each wave issues the same loads on every
+// step and the waits are constants.  Tiles are ordered (slot, bank-row
+// block, M tile) and taken in order per XCD (workgroup b runs on XCD b % 8),
+// so the M tiles sharing a block of weights run side by side and share it
+// through that XCD's L2.
 typedef __attribute__((address_space(3))) void* lds_ptr;
 template <int AUX>
 __device__ __forceinline__ void bload_lds(__amdgpu_buffer_rsrc_t r, void* lds, uint32_t off) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr)lds, 16, off, 0, 0, AUX);
 }
 constexpr int kPfWaves = 8;
+constexpr int kPfWaveRows = kPfRows / kPfWaves;   // 64 bank rows (four brick rows) per wave
+
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 template <bool FP8, bool GATEUP>
 __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
-  constexpr int TM = FP8 ? 64 : 128;     // pairs per tile
-  constexpr int KS = FP8 ? 64 : 32;      // K per step = one weight brick
-  constexpr int NTG = TM / 32;           // token groups (MFMA N blocks) per wave
-  constexpr int TBW = FP8 ? 2 * NTG : NTG;   // token bricks a wave reads per step (FP8: lo and hi)
-  constexpr int SB = 32 + 8;             // bricks per stage: 32 weight + 8 token
-  constexpr int NS = kPfStages;          // stages in flight
-  __shared__ __attribute__((aligned(1024))) char Ls[NS][SB * 1024];
+  constexpr int TM = FP8 ? 64 : 128;         // pairs per tile
+  constexpr int NTG = TM / 16;               // token groups (MFMA N blocks)
+  constexpr int TBS = FP8 ? 2 * NTG : NTG;   // token bricks per step (FP8: K halves of 32)
+  constexpr int KS = FP8 ? 64 : 32;          // K per step = one weight brick
+  constexpr int WB = kPfWaveRows / 16;       // weight brick rows per wave
+  constexpr int SPS = 2;                     // steps per LDS stage (one barrier each)
+  constexpr int NSTG = 4;                    // stages in LDS
+  constexpr int D = FP8 ? 2 : 4;             // weight register ring, in steps (FP8 also holds the block sums)
+  constexpr int SB = SPS * TBS;              // token bricks per stage
+  static_assert(TBS == kPfWaves, "each wave loads one token brick per step: SPS per stage");
+  static_assert(D % SPS == 0, "a loop body of D steps holds whole stages");
+  __shared__ __attribute__((aligned(1024))) char Ls[NSTG][SB * 1024];
 
   const int K = GATEUP ? a.H : a.I;
-  const int NROWS = GATEUP ? 2 * a.I : a.H;          // bank rows
+  const int NROWS = GATEUP ? 2 * a.I : a.H;           // bank rows
   const int NB = (NROWS + kPfRows - 1) / kPfRows;
   const int ntiles = *a.n_mtiles * NB;
   const int Q = (ntiles + 7) / 8;
@@ -912,22 +928,43 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   const int seg = a.off[slot];
   const int mrows = min(TM, a.cnt[slot] - m0);
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wr = wv >> 1, wt = wv & 1;
   const int r = lane & 15, j = lane >> 4;
-  const int nkt = K / KS;                                // bricks per brick row = steps
-  const int t0 = (nb * kPfRows + 128 * wr) / 16;        // first brick row of this wave's rows
-  const bool rows_ok = nb * kPfRows + 128 * wr < NROWS;
+  const int nkt = K / KS;                                  // steps
+  const int row0 = nb * kPfRows + kPfWaveRows * wv;        // first bank row of this wave
+  const bool rows_ok = row0 < NROWS;                       // NROWS is a multiple of 128
+  const int t0 = rows_ok ? row0 / 16 : 0;                  // first brick row of this wave
 
   const size_t bank_bytes = (size_t)(GATEUP ? 2 : 1) * a.I * a.H * (FP8 ? 1 : 2);
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc((const char*)(GATEUP ? a.w_gu : a.w_down) + (size_t)slot * bank_bytes +
-                                                   (size_t)(rows_ok ? t0 : 0) * nkt * 1024,
-                                               rows_ok ? (uint32_t)(8 * nkt * 1024) : 0u);
+                                                   (size_t)t0 * nkt * 1024,
+                                               rows_ok ? (uint32_t)(WB * nkt * 1024) : 0u);
   const uint16_t* tsrc = GATEUP ? a.x : a.h;
-  const uint32_t tbytes = (uint32_t)((size_t)(GATEUP ? a.T : a.P) * K * 2);
-  const __amdgpu_buffer_rsrc_t trs = make_rsrc(tsrc, tbytes);
-  // FP8 block scales: wave-uniform pointers (scalar loads, so reading a scale
-  // never waits on the stage loads in flight); gate/up lanes j < 2 hold gate
-  // rows and j >= 2 up rows (64 features in one 128-block).
+  const __amdgpu_buffer_rsrc_t trs = make_rsrc(tsrc, (uint32_t)((size_t)(GATEUP ? a.T : a.P) * K * 2));
+  // This wave's token brick of every step: brick q = wv (BF16: token group
+  // wv; FP8: group wv / 2, K half wv & 1).  Lane (r, j) fetches 16 bytes of
+  // pair row 16 g + r: a row of x (gate/up: the pair's token) or of h (down:
+  // the pair itself).  FP8 halves follow the expansion of a weight brick:
+  // lane j of the low operand holds K 16 j .. 16 j + 7 of the step, of the
+  // high one 16 j + 8 .. 16 j + 15.
+  const int prow = 16 * (FP8 ? wv >> 1 : wv) + r;
+  const int srow = prow < mrows ? (GATEUP ? a.sorted_pair[seg + m0 + prow] / a.k : seg + m0 + prow) : -1;
+  const uint32_t tkoff = FP8 ? (uint32_t)(16 * j + 8 * (wv & 1)) : (uint32_t)(8 * j);
+  auto issue_tok = [&](int sg) {   // stage sg -> LDS buffer sg % NSTG
+    char* stage = Ls[sg % NSTG];
+#pragma unroll
+    for (int s = 0; s < SPS; ++s) {
+      const int st = sg * SPS + s;
+      bload_lds<0>(trs, stage + (s * TBS + wv) * 1024,
+                   oob_sel(srow >= 0 && st < nkt, (uint32_t)(((size_t)(srow < 0 ? 0 : srow) * K + st * KS + tkoff) * 2)));
+    }
+  };
+  u32x4 wr[D][WB];
+  auto issue_w = [&](int st, u32x4 (&dst)[WB]) {   // weight bricks of step st (zeros past the last)
+#pragma unroll
+    for (int i = 0; i < WB; ++i) dst[i] = bload(wrs, oob_sel(st < nkt, (uint32_t)((i * nkt + st) * 1024 + lane * 16)));
+  };
+  // FP8 block scales: wave-uniform pointers read with scalar loads; gate/up
+  // lanes j < 2 hold gate rows and j >= 2 up rows (32 features in one block)
   const float* scp = nullptr;
   const float* scq = nullptr;
   if (FP8) {
@@ -940,159 +977,150 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
       scp = scq = a.s_down + ((size_t)slot * (a.H / 128) + (16 * t0) / 128) * nbk;
     }
   }
-  // Loads of one step, 5 per wave: weight bricks 4 wt .. 4 wt + 3 of row
-  // block wr (stage bricks 8 wr + ...), and token brick tb = wv (stage brick
-  // 32 + tb; BF16: token group tb, FP8: group tb / 2, low or high half).
-  // Lane r of the token brick fetches pair row 16 tg + r of the tile: a row
-  // of x (gate/up: the pair's token) or of h (down: the pair itself).
-  const int tb = wv;
-  const int tg_of_tb = FP8 ? tb >> 1 : tb;
-  const int prow = 16 * tg_of_tb + r;
-  const int tsrc_row = prow < mrows ? (GATEUP ? a.sorted_pair[seg + m0 + prow] / a.k : seg + m0 + prow) : -1;
-  const uint32_t tkoff = FP8 ? (uint32_t)(16 * j + 8 * (tb & 1)) : (uint32_t)(8 * j);
-  auto issue = [&](int st) {
-    char* stage = Ls[st % NS];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int bi = 4 * wt + q;
-      bload_lds<0>(wrs, stage + (8 * wr + bi) * 1024, (uint32_t)((bi * nkt + st) * 1024 + lane * 16));
-    }
-    bload_lds<0>(trs, stage + (32 + tb) * 1024,
-                 oob_sel(tsrc_row >= 0, (uint32_t)(((size_t)tsrc_row * K + st * KS + tkoff) * 2)));
-  };
-
-  f32x4 acc[8][NTG];
-  f32x4 part[FP8 ? 8 : 1][FP8 ? NTG : 1];
-#pragma unroll
-  for (int bi = 0; bi < 8; ++bi)
-#pragma unroll
-    for (int tg = 0; tg < NTG; ++tg) acc[bi][tg] = f32x4{0, 0, 0, 0};
-
-  // Operand reads from LDS are issued as asm so that the compiler, which
-  // cannot tell the stage being read from the stages still being filled by
-  // the LDS-destination loads, does not wait for every load in flight before
-  // them; the asm waits that follow tie the read registers.
-  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)&Ls[0][0];
-  // FP8: the two scales of a 128-K block are fetched by scalar loads (a vector
-  // load would make the compiler wait for every stage load in flight); the
-  // only LDS wait below is lgkmcnt(0), which a scalar load in flight cannot
-  // make return early.
   float s_g = 0.f, s_u = 0.f;
 
-  const int nsteps = nkt;
-  // The operands of step st+1 are read from LDS while the MFMAs of step st
-  // run from registers.  Top of step st: every wave's reads of stage st are
-  // complete (lgkmcnt 0, which also covers the FP8 scale loads) and its loads
-  // of step st+1 have landed; the barrier then makes stage st+1 readable and
-  // stage st free, and the loads of step st+NS go into it.  Weight brick bi
-  // of step st+1 is read right after the MFMAs of brick bi of step st are
-  // issued (the read returns long after they took their operands); the token
-  // bricks alternate between two register sets.  nsteps is even (BF16: K is
-  // a multiple of 64; FP8: of 128, one scale block per two steps), so the
-  // loop runs in pairs with no branch around a read.  FP8: the two scales
-  // of a block are loaded (scalar loads) on its first step and applied to
-  // the block's partial sums at the end of its second (post-scaling).
-  static_assert(TBW == 4, "two register sets of 4 token bricks");
-  static_assert(NS == 4, "the waits below count 5 loads per step, NS - 1 steps behind");
-  const uint32_t wofs = (8 * wr) * 1024 + lane * 16, tofs = (32 + wt * TBW) * 1024 + lane * 16;
-  u32x4 wf[8], ta[TBW], tb2[TBW];
-  auto rd_t = [&](int st, u32x4 (&tf)[TBW]) {
-    const uint32_t base = lds0 + (uint32_t)((st % NS) * SB * 1024) + tofs;
+  f32x4 acc[WB][NTG];
+  f32x4 part[FP8 ? WB : 1][FP8 ? NTG : 1];
 #pragma unroll
-    for (int q = 0; q < TBW; ++q) asm volatile("ds_read_b128 %0, %1" : "=v"(tf[q]) : "v"(base + q * 1024));
+  for (int i = 0; i < WB; ++i)
+#pragma unroll
+    for (int tg = 0; tg < NTG; ++tg) acc[i][tg] = f32x4{0, 0, 0, 0};
+
+  // Token operands are read from LDS with asm so that the compiler, which
+  // cannot tell the stage being read from the stages still being filled by
+  // the LDS-destination loads, does not wait for every load in flight; the
+  // asm wait that follows ties the registers.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)&Ls[0][0];
+  u32x4 tk[TBS];
+  auto rd_tok = [&](int st, int q) {
+    const uint32_t addr =
+        lds0 + (uint32_t)(((st / SPS) % NSTG) * SB * 1024 + ((st % SPS) * TBS + q) * 1024) + (uint32_t)lane * 16u;
+    asm volatile("ds_read_b128 %0, %1" : "=v"(tk[q]) : "v"(addr));
   };
-  auto rd_w = [&](int st, int bi) {
-    const uint32_t base = lds0 + (uint32_t)((st % NS) * SB * 1024) + wofs;
-    asm volatile("ds_read_b128 %0, %1" : "=v"(wf[bi]) : "v"(base + bi * 1024));
-  };
-  auto wait_all = [&](u32x4 (&tf)[TBW]) {   // every LDS read and scale load issued so far has returned
+  auto wait_tok = [&]() {   // every LDS read and scalar load issued so far has returned
     asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(tf[0]), "+v"(tf[1]), "+v"(tf[2]), "+v"(tf[3]), "+v"(wf[0]), "+v"(wf[1]), "+v"(wf[2]),
-                   "+v"(wf[3]), "+v"(wf[4]), "+v"(wf[5]), "+v"(wf[6]), "+v"(wf[7]));
+                 : "+v"(tk[0]), "+v"(tk[1]), "+v"(tk[2]), "+v"(tk[3]), "+v"(tk[4]), "+v"(tk[5]), "+v"(tk[6]),
+                   "+v"(tk[7]));
   };
-  // ODD: the step's parity, known at compile time because the loop runs in pairs
-  auto step = [&](int st, u32x4 (&tc)[TBW], u32x4 (&tn)[TBW], auto odd) {
-    constexpr bool ODD = decltype(odd)::value;
-    wait_all(tc);
+  // Loads issued after the token loads of stage e + 1, at the end of stage e
+  // (the wait may not exceed it): in the steady state the weights of
+  // (NSTG - 1) SPS steps and the token loads of NSTG - 2 stages; at the
+  // first stage ends, whose next stages came with the prologue, the
+  // prologue's later token and weight loads plus WB per step run so far and
+  // SPS per earlier stage end (that count grows by WB SPS per stage end).
+  constexpr int kWaitSS = WB * SPS * (NSTG - 1) + SPS * (NSTG - 2);
+  constexpr int kWait0 = SPS * (NSTG - 2) + WB * D + WB * (SPS - 1);
+  constexpr int kWait1 = kWait0 + WB * SPS < kWaitSS ? kWait0 + WB * SPS : kWaitSS;
+  constexpr int kWait2 = kWait1 + WB * SPS < kWaitSS ? kWait1 + WB * SPS : kWaitSS;
+  static_assert(kWaitSS < 64, "vmcnt counts to 63");
+
+  auto step = [&](int st, auto dc) {
+    constexpr int d = decltype(dc)::value;                  // st % D
+    constexpr bool ODD = (d & 1) != 0;                      // st % 2 (D is even)
+    constexpr bool STAGE_END = (d % SPS) == SPS - 1;        // step st + 1 starts a new stage
+    wait_tok();
     if constexpr (FP8 && ODD) asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(s_g), "+s"(s_u));   // the block's scales
-    // loads issued so far: steps up to min(st + NS - 1, nsteps - 1); step st+1's must be in
-    const int later = min(nsteps - 1, st + NS - 1) - (st + 1);
-    if (later >= 2)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 10);   // vmcnt(10)
-    else if (later == 1)
-      __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
-    __builtin_amdgcn_s_barrier();
-    if (st + NS < nsteps) issue(st + NS);
-    if constexpr (FP8 && !ODD) {
-      asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_g) : "s"(scp + (st >> 1)));
-      asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_u) : "s"(scq + (st >> 1)));
-#pragma unroll
-      for (int bi = 0; bi < 8; ++bi)
-#pragma unroll
-        for (int tg = 0; tg < NTG; ++tg) part[bi][tg] = f32x4{0, 0, 0, 0};
+    if constexpr (STAGE_END) {
+      // the wait counts assume the loads stay in program order around it:
+      // nothing is scheduled across this block
+      __builtin_amdgcn_sched_barrier(0);
+      const int e = st / SPS;                               // stage ending; stage e + 1 must be in
+      if (e == 0)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWait0));
+      else if (e == 1)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWait1));
+      else if (e == 2)
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWait2));
+      else
+        __builtin_amdgcn_s_waitcnt(vmcnt_imm(kWaitSS));
+      __builtin_amdgcn_s_barrier();
+      issue_tok(e + NSTG);                                   // into the buffer of stage e, now free
+      __builtin_amdgcn_sched_barrier(0);
     }
-    rd_t(st + 1, tn);   // past the last step this reads a stale stage: never used
+    if (st < nkt) {
+      if constexpr (!FP8) {
 #pragma unroll
-    for (int bi = 0; bi < 8; ++bi) {
-      if (!FP8) {
+        for (int q = 0; q < TBS; ++q) {
 #pragma unroll
-        for (int tg = 0; tg < NTG; ++tg) acc[bi][tg] = mfma16x16x32(wf[bi], tc[tg], acc[bi][tg]);
+          for (int i = 0; i < WB; ++i) acc[i][q] = mfma16x16x32(wr[d][i], tk[q], acc[i][q]);
+          rd_tok(st + 1, q);
+        }
       } else {
-        u32x4 lo, hi;
-        e4m3x16_to_bf16_nat(wf[bi], lo, hi);
+        if constexpr (!ODD) {   // first step of a 128-K block: its two scales, zero partial sums
+          asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_g) : "s"(scp + (st >> 1)));
+          asm volatile("s_load_dword %0, %1, 0x0" : "=s"(s_u) : "s"(scq + (st >> 1)));
 #pragma unroll
-        for (int tg = 0; tg < NTG; ++tg) {
-          part[bi][tg] = mfma16x16x32(lo, tc[2 * tg], part[bi][tg]);
-          part[bi][tg] = mfma16x16x32(hi, tc[2 * tg + 1], part[bi][tg]);
+          for (int i = 0; i < WB; ++i)
+#pragma unroll
+            for (int tg = 0; tg < NTG; ++tg) part[i][tg] = f32x4{0, 0, 0, 0};
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {   // the low K halves of the step, then the high ones
+          u32x4 op[WB];
+#pragma unroll
+          for (int i = 0; i < WB; ++i) {
+            u32x4 lo, hi;
+            e4m3x16_to_bf16_nat(wr[d][i], lo, hi);
+            op[i] = h ? hi : lo;
+          }
+#pragma unroll
+          for (int tg = 0; tg < NTG; ++tg) {
+#pragma unroll
+            for (int i = 0; i < WB; ++i) part[i][tg] = mfma16x16x32(op[i], tk[2 * tg + h], part[i][tg]);
+            rd_tok(st + 1, 2 * tg + h);
+          }
+        }
+        if constexpr (ODD) {
+          const float sc = j < 2 ? s_g : s_u;
+#pragma unroll
+          for (int i = 0; i < WB; ++i)
+#pragma unroll
+            for (int tg = 0; tg < NTG; ++tg)
+#pragma unroll
+              for (int e = 0; e < 4; ++e) acc[i][tg][e] += sc * part[i][tg][e];
         }
       }
-      rd_w(st + 1, bi);
     }
-    if constexpr (FP8 && ODD) {
-      const float sc = j < 2 ? s_g : s_u;
-#pragma unroll
-      for (int bi = 0; bi < 8; ++bi)
-#pragma unroll
-        for (int tg = 0; tg < NTG; ++tg)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) acc[bi][tg][i] += sc * part[bi][tg][i];
-    }
+    issue_w(st + D, wr[d]);
   };
-  for (int st = 0; st < NS && st < nsteps; ++st) issue(st);
-  if (nsteps >= 4)   // step 0's loads are in (nsteps is even: 2 or >= 4)
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 15);   // vmcnt(15)
-  else
-    __builtin_amdgcn_s_waitcnt(0x0F70 | 5);    // vmcnt(5)
-  __builtin_amdgcn_s_barrier();
-  rd_t(0, ta);
+
+  for (int sg = 0; sg < NSTG; ++sg) issue_tok(sg);
 #pragma unroll
-  for (int bi = 0; bi < 8; ++bi) rd_w(0, bi);
-  for (int st = 0; st < nsteps; st += 2) {
-    step(st, ta, tb2, std::false_type{});
-    step(st + 1, tb2, ta, std::true_type{});
+  for (int d = 0; d < D; ++d) issue_w(d, wr[d]);
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(SPS * (NSTG - 1) + WB * D));   // stage 0 is in
+  __builtin_amdgcn_s_barrier();
+#pragma unroll
+  for (int q = 0; q < TBS; ++q) rd_tok(0, q);
+  const int nloop = (nkt + D - 1) / D * D;
+  for (int st0 = 0; st0 < nloop; st0 += D) {
+    step(st0, std::integral_constant<int, 0>{});
+    step(st0 + 1, std::integral_constant<int, 1>{});
+    if constexpr (D == 4) {
+      step(st0 + 2, std::integral_constant<int, 2>{});
+      step(st0 + 3, std::integral_constant<int, 3 % D>{});
+    }
   }
-  wait_all(ta);   // the reads past the last step land before their registers are reused
+  wait_tok();
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));   // no load into LDS or registers outlives the loop
   if (!rows_ok) return;
 
-  // ---- epilogue.  acc[bi][tg][i] at lane (r, j): bank row 16 (t0 + bi) + 4 j + i,
-  // pair row TM/2 wt + 16 tg + r.
+  // ---- epilogue.  acc[i][tg][e] at lane (r, j): bank row 16 (t0 + i) + 4 j + e,
+  // pair row 16 tg + r.
   if (GATEUP) {
 #pragma unroll
     for (int tg = 0; tg < NTG; ++tg) {
-      const int row = (TM / 2) * wt + 16 * tg + r;
+      const int row = 16 * tg + r;
 #pragma unroll
-      for (int bi = 0; bi < 8; ++bi) {
+      for (int i = 0; i < WB; ++i) {
         f32x4 u;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) u[i] = __shfl_xor(acc[bi][tg][i], 32, 64);
+        for (int e = 0; e < 4; ++e) u[e] = __shfl_xor(acc[i][tg][e], 32, 64);
         if (j < 2 && row < mrows) {
-          const int f = 8 * (t0 + bi) + 4 * j;   // first of the lane's 4 features
-          const uint32_t h01 = f32_to_bf16_rne(silu_f32(acc[bi][tg][0]) * u[0]) |
-                               ((uint32_t)f32_to_bf16_rne(silu_f32(acc[bi][tg][1]) * u[1]) << 16);
-          const uint32_t h23 = f32_to_bf16_rne(silu_f32(acc[bi][tg][2]) * u[2]) |
-                               ((uint32_t)f32_to_bf16_rne(silu_f32(acc[bi][tg][3]) * u[3]) << 16);
+          const int f = 8 * (t0 + i) + 4 * j;   // first of the lane's 4 features
+          const uint32_t h01 = f32_to_bf16_rne(silu_f32(acc[i][tg][0]) * u[0]) |
+                               ((uint32_t)f32_to_bf16_rne(silu_f32(acc[i][tg][1]) * u[1]) << 16);
+          const uint32_t h23 = f32_to_bf16_rne(silu_f32(acc[i][tg][2]) * u[2]) |
+                               ((uint32_t)f32_to_bf16_rne(silu_f32(acc[i][tg][3]) * u[3]) << 16);
           *reinterpret_cast<u32x2*>(a.h + (size_t)(seg + m0 + row) * a.I + f) = u32x2{h01, h23};
         }
       }
@@ -1100,15 +1128,15 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   } else {
 #pragma unroll
     for (int tg = 0; tg < NTG; ++tg) {
-      const int row = (TM / 2) * wt + 16 * tg + r;
+      const int row = 16 * tg + r;
       if (row < mrows) {
         const int pos = seg + m0 + row;
         const float wp = a.w[a.sorted_pair[pos]];
 #pragma unroll
-        for (int bi = 0; bi < 8; ++bi) {
-          const int c = 16 * (t0 + bi) + 4 * j;
-          const uint32_t o01 = f32_to_bf16_rne(wp * acc[bi][tg][0]) | ((uint32_t)f32_to_bf16_rne(wp * acc[bi][tg][1]) << 16);
-          const uint32_t o23 = f32_to_bf16_rne(wp * acc[bi][tg][2]) | ((uint32_t)f32_to_bf16_rne(wp * acc[bi][tg][3]) << 16);
+        for (int i = 0; i < WB; ++i) {
+          const int c = 16 * (t0 + i) + 4 * j;
+          const uint32_t o01 = f32_to_bf16_rne(wp * acc[i][tg][0]) | ((uint32_t)f32_to_bf16_rne(wp * acc[i][tg][1]) << 16);
+          const uint32_t o23 = f32_to_bf16_rne(wp * acc[i][tg][2]) | ((uint32_t)f32_to_bf16_rne(wp * acc[i][tg][3]) << 16);
           *reinterpret_cast<u32x2*>(a.o + (size_t)pos * a.H + c) = u32x2{o01, o23};
         }
       }
