@@ -262,15 +262,17 @@ struct DecWsDev {
 constexpr int kDecResSteps = 6;          // down steps per wave held in registers (DR = 8)
 constexpr int kDecResH = 32 * 1024;      // bytes of LDS for h (DR = 8): G * T * I * 2 at most
 
-template <bool FP8, int D, int NW, int DR>
+template <bool FP8, int D, int NW, int DR, int RG = 1>
 __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev c) {
   static_assert(DR == 16 || (DR == 8 && !FP8), "down tasks of 16 rows, or 8 (BF16 only)");
+  static_assert(RG == 1 || (RG == 2 && DR == 16), "gate/up tasks of one brick row, or two (16-row down tasks)");
   __shared__ __align__(16) uint16_t s_h[DR == 8 ? kDecResH / 2 : 8];
   __shared__ int s_gslot[kDecPmax];
   __shared__ float s_gw[kDecPmax * kDecTok];
   __shared__ int s_G;
   __shared__ unsigned long long s_tab[kPlanTab];
   __shared__ f32x4 red[2][NW][64];
+  __shared__ f32x4 redB[RG > 1 ? 2 : 1][NW][RG > 1 ? 64 : 1];   // the second brick row of a gate/up task
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int H = a.H, I = a.I, T = a.T;
@@ -279,8 +281,9 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   const int G = s_G;
   const bool tok = r < T;
   constexpr int XN = FP8 ? 4 : 2;
-  const int RA = I / 8;
-  const int nA = G * RA, nB = H / DR;
+  const int RA = I / 8;                          // gate/up brick rows
+  const int RAT = RA / RG;                       // gate/up tasks per group (the host checks RG | RA)
+  const int nA = G * RAT, nB = H / DR;
   const int b0 = (int)blockIdx.x, gs = (int)gridDim.x;
   // the gate/up tasks go round-robin over the whole grid (the fewest per
   // compute unit at most); the down tasks start at workgroup nA % gs, the
@@ -298,8 +301,11 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   u32x4 wv2[DR == 8 ? kDecResSteps : 1][2];
   float f1[DR == 8 ? kDecResSteps : 1];
   // ================= phase A: gate/up + SwiGLU
+  // A task is RG brick rows (RG x 16 gate/up rows) of one group: each step
+  // loads the x operand once for all RG rows, so x is re-read from the
+  // caches once per RG rows (it is as large as the weights at T = 8).
   {
-    u32x4 wb[D][2], ob[D][XN];   // weight bricks and x of D steps
+    u32x4 wb[D][RG][2], ob[D][XN];   // weight bricks and x of D steps
     const int nkt = FP8 ? H / 64 : H / 32;
     const int S = (nkt + 1) >> 1;
     const int SW = (S + NW - 1) / NW;
@@ -316,13 +322,17 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
       const int s = s_lo + i_l;
       const bool ok = i_tk < myA && s < S;
       const int tt = ok ? task : 0;
-      const int g = tt / RA, t = tt - g * RA;
+      const int g = tt / RAT, t = (tt - g * RAT) * RG;   // first brick row of the task
       const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;   // slot 0 always exists
       const __amdgpu_buffer_rsrc_t wr =
-          make_rsrc((const char*)a.w_gu + (size_t)slot * gu_bytes + (size_t)t * nkt * 1024, (uint32_t)(nkt * 1024));
+          make_rsrc((const char*)a.w_gu + (size_t)slot * gu_bytes + (size_t)t * nkt * 1024,
+                    (uint32_t)(RG * nkt * 1024));
       const uint32_t wo = oob_sel(ok, (uint32_t)s * 2048u + lane * 16u);
-      wb[d][0] = bload_nt(wr, wo);
-      wb[d][1] = bload_nt(wr, oob_sel(ok, wo + 1024u));
+#pragma unroll
+      for (int rr = 0; rr < RG; ++rr) {
+        wb[d][rr][0] = bload_nt(wr, oob_sel(ok, wo + (uint32_t)(rr * nkt * 1024)));
+        wb[d][rr][1] = bload_nt(wr, oob_sel(ok, wo + (uint32_t)(rr * nkt * 1024) + 1024u));
+      }
 #pragma unroll
       for (int b = 0; b < 2; ++b) {
         const int k0 = FP8 ? 128 * s + 64 * b : 64 * s + 32 * b;
@@ -335,7 +345,8 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
           ob[d][b] = bload(xr, off);
         }
       }
-      if (FP8) {   // block scales of the gate rows and of the up rows at this K step
+      if (FP8) {   // block scales of the gate rows and of the up rows at this K step (one 128-row
+                   // block holds every row of the task: 16 brick rows share it and RG divides 16)
         const size_t si = ((size_t)slot * (I / 128) + (8 * t) / 128) * (H / 128) + (ok ? s : 0);
         sb[d][0] = a.s_gate[si];
         sb[d][1] = a.s_up[si];
@@ -347,54 +358,65 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
     };
 #pragma unroll
     for (int d = 0; d < D; ++d) issue(d);
-    f32x4 acc = {0, 0, 0, 0};
+    f32x4 acc[RG];
+#pragma unroll
+    for (int rr = 0; rr < RG; ++rr) acc[rr] = f32x4{0, 0, 0, 0};
     int c_tk = 0, c_l = 0;
     for (int i0 = 0; i0 < nsteps; i0 += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
         if (i0 + d < nsteps) {
-          if (!FP8) {
-            acc = mfma16x16x32(wb[d][0], ob[d][0], acc);
-            acc = mfma16x16x32(wb[d][1], ob[d][1], acc);
-          } else {
-            f32x4 p = {0, 0, 0, 0};
 #pragma unroll
-            for (int b = 0; b < 2; ++b) {
-              u32x4 lo, hi;
-              e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
-              p = mfma16x16x32(lo, ob[d][2 * b], p);
-              p = mfma16x16x32(hi, ob[d][2 * b + 1], p);
+          for (int rr = 0; rr < RG; ++rr) {
+            if (!FP8) {
+              acc[rr] = mfma16x16x32(wb[d][rr][0], ob[d][0], acc[rr]);
+              acc[rr] = mfma16x16x32(wb[d][rr][1], ob[d][1], acc[rr]);
+            } else {
+              f32x4 p = {0, 0, 0, 0};
+#pragma unroll
+              for (int b = 0; b < 2; ++b) {
+                u32x4 lo, hi;
+                e4m3x16_to_bf16_nat(wb[d][rr][b], lo, hi);
+                p = mfma16x16x32(lo, ob[d][2 * b], p);
+                p = mfma16x16x32(hi, ob[d][2 * b + 1], p);
+              }
+              const float sc = j < 2 ? sb[d][0] : sb[d][1];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[rr][q] += sc * p[q];
             }
-            const float sc = j < 2 ? sb[d][0] : sb[d][1];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] += sc * p[q];
           }
           if (c_l == SW - 1) {   // end of a task: reduce over the waves, SwiGLU, h, count
             const int task = b0 + c_tk * gs;
-            const int g = task / RA, t = task - g * RA;
+            const int g = task / RAT, t = (task - g * RAT) * RG;
             f32x4(&rb)[NW][64] = red[c_tk & 1];
-            rb[wv][lane] = acc;
+            rb[wv][lane] = acc[0];
+            if constexpr (RG > 1) redB[c_tk & 1][wv][lane] = acc[RG - 1];
             __syncthreads();
             if (wv == 0) {
-              if (j < 2 && tok) {
-                f32x4 Gv = rb[0][lane], Uv = rb[0][lane + 32];
+              // sum one brick row's partials over the waves, SwiGLU, store its h
+              auto row_out = [&](auto& rx, int rr) {
+                f32x4 Gv = rx[0][lane], Uv = rx[0][lane + 32];
 #pragma unroll
                 for (int w2 = 1; w2 < NW; ++w2) {
-                  Gv += rb[w2][lane];
-                  Uv += rb[w2][lane + 32];
+                  Gv += rx[w2][lane];
+                  Uv += rx[w2][lane + 32];
                 }
                 const uint32_t h01 = f32_to_bf16_rne(silu_f32(Gv[0]) * Uv[0]) |
                                      ((uint32_t)f32_to_bf16_rne(silu_f32(Gv[1]) * Uv[1]) << 16);
                 const uint32_t h23 = f32_to_bf16_rne(silu_f32(Gv[2]) * Uv[2]) |
                                      ((uint32_t)f32_to_bf16_rne(silu_f32(Gv[3]) * Uv[3]) << 16);
                 // device-coherent store (written through to memory), so no L2 write-back is needed
-                __builtin_amdgcn_raw_buffer_store_b64(u32x2{h01, h23}, hw,
-                                                      (uint32_t)((((size_t)g * kDecTok + r) * I + 8 * t + 4 * j) * 2), 0, 16);
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{h01, h23}, hw, (uint32_t)((((size_t)g * kDecTok + r) * I + 8 * (t + rr) + 4 * j) * 2), 0, 16);
+              };
+              if (j < 2 && tok) {
+                row_out(red[c_tk & 1], 0);
+                if constexpr (RG > 1) row_out(redB[c_tk & 1], 1);
               }
               __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores above have completed
               __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // and stay before the count
               bool last = false;
-              if (lane == 0 && atomicAdd(&c.done[g * kCtrlStride], 1u) == (uint32_t)RA - 1u) {
+              if (lane == 0 && atomicAdd(&c.done[g * kCtrlStride], 1u) == (uint32_t)RAT - 1u) {
                 // no other task of g is left: clear its counter for the next launch
                 __hip_atomic_store(&c.done[g * kCtrlStride], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 last = atomicAdd(c.all, 1u) == (uint32_t)G - 1u;
@@ -408,7 +430,8 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
                     __builtin_amdgcn_raw_buffer_store_b32(1u, gow, (uint32_t)(bb * kCtrlStride * 4), 0, 16);
               }
             }
-            acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+            for (int rr = 0; rr < RG; ++rr) acc[rr] = f32x4{0, 0, 0, 0};
             c_l = 0;
             ++c_tk;
           } else {
@@ -419,7 +442,6 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
       }
     }
   }
-
   if constexpr (DR == 8) {
     const size_t dn_bytes = (size_t)H * I * 2;
     const int t = tb0;
@@ -1250,10 +1272,12 @@ static DecWs dec_ws(int T_max, int k, int H, int I, int n_slots) {
 struct DecOcc {
   int cus = 0;
   int fu[2][2] = {{0, 0}, {0, 0}};   // [FP8][8-row down tasks]
+  int fu_rg2 = 0;                    // FP8 with two brick rows per gate/up task
 };
 constexpr int kDecD_BF16 = 4;   // register-ring depth in 2-brick steps
 constexpr int kDecD_RES = 4;    // the same for the form with register-resident down weights (DR = 8)
 constexpr int kDecD_FP8 = 3;    // (FP8 steps carry twice the x operand: a shallower ring keeps 2 workgroups per CU)
+constexpr int kDecD_FP8_RG2 = 2;   // FP8, two brick rows per gate/up task: 2 steps of 2 rows in flight
 constexpr int kDecW = 8;   // waves per workgroup
 static std::mutex g_occ_mu;
 static DecOcc g_occ[64];
@@ -1269,6 +1293,8 @@ static moe_status dec_occupancy(DecOcc* out) {
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0][0], dec_fused_kernel<false, kDecD_BF16, kDecW, 16>, kDecW * 64, 0));
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1][0], dec_fused_kernel<true, kDecD_FP8, kDecW, 16>, kDecW * 64, 0));
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0][1], dec_fused_kernel<false, kDecD_RES, kDecW, 8>, kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu_rg2, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2>,
+                                                         kDecW * 64, 0));
     o.fu[1][1] = 0;   // the register-resident form is BF16 only (FP8 steps need more registers than it has)
     for (int i = 0; i < 2; ++i)
       if (o.fu[i][0] < 1) o.fu[i][0] = 1;
@@ -1389,7 +1415,11 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     c.all = (uint32_t*)(wsb + L.all);
     c.go = (uint32_t*)(wsb + L.go);
     const int f = fp8 ? 1 : 0;
-    const long tasks = (long)a.G_max * (I / 8) + 2L * (H / 16);
+    // FP8: two brick rows per gate/up task, so each x load serves both (x is
+    // 2 B x T per K against 1 B per weight row); measured faster at T = 1, 4
+    // and 16 (at T = 1 it also halves the task ends)
+    const bool rg2 = fp8 && (I / 8) % 2 == 0 && occ.fu_rg2 >= occ.fu[1][0];
+    const long tasks = (long)a.G_max * (I / 8) / (rg2 ? 2 : 1) + 2L * (H / 16);
     const unsigned g1 = (unsigned)std::min<long>(std::min<long>(tasks, (long)occ.cus * occ.fu[f][0]), kDecGridMax);
     // 8-row down tasks with register-resident weights and h in LDS when every
     // task fits in one round of the grid, a wave's steps fit its registers,
@@ -1397,7 +1427,9 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     const long res_steps = ((long)a.G_max * ((I / (fp8 ? 64 : 32) + 3) / 4) + kDecW - 1) / kDecW;
     const bool dr8 = !fp8 && (long)(H / 8) <= (long)g1 && res_steps <= kDecResSteps &&
                      (long)a.G_max * T * I * 2 <= kDecResH && occ.fu[f][1] >= occ.fu[f][0];
-    if (fp8)
+    if (rg2)
+      dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
+    else if (fp8)
       dec_fused_kernel<true, kDecD_FP8, kDecW, 16><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (dr8)
       dec_fused_kernel<false, kDecD_RES, kDecW, 8><<<g1, kDecW * 64, 0, stream>>>(a, c);
