@@ -331,8 +331,68 @@ def run_decode(b, K, W, host_GBps=None, host_branch=True):
     wall, d2 = run_trace(None)
     assert np.array_equal(d, d2), "the two passes made different cache decisions"
     log("decode: pass 3 (no events, no PCIe fill copies)")
+    y_eager_last = {}
     wall_res, d3 = run_trace(None, fill=False)
     assert np.array_equal(d, d3), "the passes made different cache decisions"
+    y_eager_last["nofill"] = y.clone()
+
+    # Pass 6: one hipGraph per 40-layer step.  The 40 layer calls (router +
+    # decision with the layer read from a device scalar, fill, forward +
+    # merge) are captured once; each step copies its logits and x into the
+    # graph's input buffers and replays it.  With and without the fill copies.
+    def run_graph(fill):
+        cache = b.Cache(L, E, k, 1, pool, host, c.bp, c.bh)
+        lg_s = torch.empty((L, 1, E), dtype=torch.float32, device="cuda")
+        x_s = torch.empty((L, 1, H), dtype=torch.uint16, device="cuda")
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(g, stream=side):
+                for l in range(L):
+                    cache.route_step(l, lg_s[l], ids, w, out, copy=False)
+                    if fill:
+                        cache.fill(out)
+                    b.expert_forward_merge(pool.c, x_s[l], pick, w, b.FWD_DECODE, ws, yh[l], y_out=y[l])
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+
+        def one(s):
+            lg_s.copy_(lg[s])
+            x_s.copy_(x[s])
+            g.replay()
+
+        for s in range(W):
+            one(s)
+        torch.cuda.synchronize()
+        c0 = cache.read_state()[4].astype(np.int64)
+        t0 = time.perf_counter()
+        for s in range(W, W + K):
+            one(s)
+        torch.cuda.synchronize()
+        wall_g = time.perf_counter() - t0
+        dg = cache.read_state()[4].astype(np.int64) - c0
+        assert_clean("decode graph pass", cache, ws)
+        cache.destroy()
+        del g
+        return wall_g, dg
+
+    log("decode: pass 6 (one captured graph per 40-layer step, replayed)")
+    wall_g_nofill, dg1 = run_graph(False)
+    assert np.array_equal(d, dg1), "the graph pass made different cache decisions"
+    assert torch.equal(y.view(torch.int32), y_eager_last["nofill"].view(torch.int32)), \
+        "the replayed graph's last step differs from the eager pass"
+    wall_g_fill, dg2 = run_graph(True)
+    assert np.array_equal(d, dg2), "the graph pass made different cache decisions"
+    graph_info = dict(
+        ms_per_step=wall_g_nofill / K * 1e3, ms_per_step_eager=wall_res / K * 1e3,
+        ms_per_step_pcie_inclusive=wall_g_fill / K * 1e3, ms_per_step_pcie_inclusive_eager=wall / K * 1e3,
+        GBps=int(d[2] + d[4]) * S / wall_g_nofill / 1e9,
+        what="one hipGraph holding a whole 40-layer step (router + decision reading the layer from a device "
+             "scalar, fill copy, forward + merge with the host partial), replayed once per token step after "
+             "copying the step's logits and x into its input buffers; beside the same work launched eagerly "
+             "(pass 3 without fills: `value`; pass 2 with fills); the replay's last y equals the eager pass's "
+             "bit for bit")
     # Pass 4: the path as the pages run it, with the host branch.  Per layer
     # call: router + cache step; the logical ids, picks, gate weights and x
     # copied to pinned host buffers, then a pinned `ready` word written in
@@ -345,7 +405,23 @@ def run_decode(b, K, W, host_GBps=None, host_branch=True):
     if host_branch:
         log("decode: pass 4 (with the host branch on the CPU)")
         n_cores = len(os.sched_getaffinity(0))
-        ex = b.HostExec(max(1, n_cores - 1))    # one core left to the thread launching GPU work
+        n_thr = max(1, n_cores - 1)              # one core left to the thread launching GPU work
+        # B_P and B_H of this machine at this expert shape (moe_calibrate_bandwidth):
+        # the fill kernel and the DMA engines for B_P, the host executor with its
+        # threads unpinned and pinned to physical cores for B_H
+        log("decode: bandwidth calibration (fill kernel, DMA, host executor unpinned / pinned)")
+        cal_scratch = b.SlotPool(16, H, I, b.W_BF16)
+        cal_cache = b.Cache(L, E, k, 1, pool, host, c.bp, c.bh)
+        cal_ids = list(range(16))                                    # layer 0: base experts 0..15
+        ex_u = b.HostExec(n_thr)
+        cal_unpinned = cal_cache.calibrate(cal_ids, cal_scratch, reps=5, host_exec=ex_u)
+        ex_u.destroy()
+        ex = b.HostExec(n_thr, pin=True)
+        cal_pinned = cal_cache.calibrate(cal_ids, cal_scratch, reps=5, host_exec=ex)
+        pin_cpus, pin_node = ex.cpus()
+        assert_clean("calibration", cal_cache)
+        cal_cache.destroy()
+        del cal_scratch
         ids_log = torch.empty((1, k), dtype=torch.int32, device="cuda")
         h_ids = torch.empty((1, k), dtype=torch.int32).pin_memory()
         h_pick = torch.empty((1, k), dtype=torch.int32).pin_memory()
@@ -394,14 +470,21 @@ def run_decode(b, K, W, host_GBps=None, host_branch=True):
         assert np.array_equal(d, d4), "the passes made different cache decisions"
         host_calls, host_s = ex.stats()
         calibrated = None
-        fill_rate = (d[4] * S / fill_s / 1e9) if fill_s > 0 else None
-        if host_GBps and fill_rate:
-            # Pass 5: q* from this machine's rates (B_P: the fill copies above, B_H:
-            # the host executor) instead of the quoted ratio; the same trace.
-            bp_c, bh_c = max(1, round(fill_rate * 10)), max(1, round(host_GBps * 10))   # units of 0.1 GB/s
+        if True:
+            # Pass 5: q* from this machine's rates as moe_calibrate_bandwidth
+            # measured them (B_P: the fill kernel, B_H: the pinned executor)
+            # instead of the quoted ratio; the same trace.
+            bp_c, bh_c = cal_pinned["bp"], cal_pinned["bh"]                    # units of 0.1 GB/s
             log("decode: pass 5 (host branch, calibrated B_P:B_H %.1f:%.1f)" % (bp_c / 10, bh_c / 10))
             wall5, d5 = run_host_trace(bp_c, bh_c)
             calibrated = dict(B_P_GBps=bp_c / 10, B_H_GBps=bh_c / 10, wall_ms_per_step=wall5 / K * 1e3,
+                              calibration=dict(
+                                  pinned=cal_pinned, unpinned=cal_unpinned, cpus=pin_cpus, numa_node=pin_node,
+                                  fill_events_GBps=(d[4] * S / fill_s / 1e9) if fill_s > 0 else None,
+                                  what="moe_calibrate_bandwidth on 16 experts of the pool (9437184 B each), 5 "
+                                       "reps: fill kernel and hipMemcpyAsync from pinned host memory, host "
+                                       "executor on %d threads with decode-shaped calls; fill_events_GBps: "
+                                       "pass 1's fill copies for comparison" % n_thr),
                               miss_rate=float(d5[3] / d5[1]), fills_per_layer_call=float(d5[4] / (K * L)),
                               host_experts_per_layer_call=float(d5[5] / (K * L)),
                               experts_on_gpu_per_layer_call=float((d5[2] + d5[4]) / (K * L)))
@@ -457,6 +540,7 @@ def run_decode(b, K, W, host_GBps=None, host_branch=True):
                      "wall_ms_per_step_pcie_inclusive (pass 2: the harness's y_host)" % max(1, n_cores - 1)),
             layer_calls=int(d[0]),
             route_and_cache_step_us=step_s / (K * L) * 1e6,
+            graph=graph_info,
         ),
     )
     res["roofline"]["frac"] = res["roofline"]["achieved"] / PEAK_HBM_GBPS

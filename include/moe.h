@@ -498,15 +498,16 @@ int32_t moe_host_exec_simd(moe_host_exec_t h);
 /*
  * Core placement ([FT] section "Graph 内的 CPU 执行分支": a resident pool of
  * worker threads pinned to physical cores).  With MOE_HOST_PIN in the flags
- * of moe_host_exec_create, thread i is pinned to entry i (modulo its length)
- * of this list: the CPUs of the process's affinity set, one per physical
- * core first (the lowest allowed SMT sibling of each core), the cores of the
- * NUMA node the current HIP device is attached to before the others, then
- * the remaining siblings in the same order.  Thread 0 is the caller's
- * thread in moe_host_forward (left alone) and the dispatcher thread in the
- * signalled form (pinned).  Without the flag the threads are not pinned.
- * moe_host_exec_cpus writes the CPU of threads 0 .. n-1 (-1: not pinned, or
- * beyond the pool) and the device's NUMA node (-1 if unknown).
+ * of moe_host_exec_create, the pool is n_threads worker threads, worker i
+ * pinned to entry i (modulo its length) of this list: the CPUs of the
+ * process's affinity set, one per physical core first (the lowest allowed
+ * SMT sibling of each core), the cores of the NUMA node the current HIP
+ * device is attached to before the others, then the remaining siblings in
+ * the same order; the calling thread (or the signalled form's dispatcher)
+ * then only waits for them.  Without the flag the pool is n_threads - 1
+ * unpinned workers plus the calling thread.  moe_host_exec_cpus writes the
+ * CPU of workers 0 .. n-1 (-1: not pinned, or beyond the pool) and the
+ * device's NUMA node (-1 if unknown).
  */
 moe_status moe_host_exec_cpus(moe_host_exec_t h, int32_t* cpus, int32_t n, int32_t* numa_node);
 

@@ -306,13 +306,15 @@ void pin_self(int cpu) {
 
 // ------------------------------------------------------------ thread pool
 // run(n_items, f): f(item) for every item in [0, n_items), spread over the
-// pool threads and the caller; returns when all are done.  cpus[i], if
-// given, is the CPU worker i (1 <= i < n) is pinned to (entry 0 belongs to
-// the calling thread, which the pool leaves alone).
+// pool; returns when all are done.  Unpinned, the pool is n - 1 worker
+// threads plus the calling thread.  Pinned (cpus given), it is n worker
+// threads, worker i on cpus[i], and the calling thread only waits: a caller
+// that also took items would run wherever the OS put it, possibly on a
+// pinned worker's core, and every pass would wait for the two sharing it.
 class Pool {
  public:
-  Pool(int n, const std::vector<int>& cpus) : n_(n) {
-    for (int i = 1; i < n_; ++i) {
+  Pool(int n, const std::vector<int>& cpus) : n_(n), caller_works_(cpus.empty()) {
+    for (int i = caller_works_ ? 1 : 0; i < n_; ++i) {
       const int cpu = cpus.empty() ? -1 : cpus[(size_t)i % cpus.size()];
       th_.emplace_back([this, cpu] {
         pin_self(cpu);
@@ -342,7 +344,7 @@ class Pool {
       gen_seen_.store(gen_, std::memory_order_release);
     }
     cv_.notify_all();
-    work();
+    if (caller_works_) work();
     std::unique_lock<std::mutex> lk(mu_);
     done_cv_.wait(lk, [this] { return busy_ == 0; });
     f_ = nullptr;
@@ -381,6 +383,7 @@ class Pool {
     }
   }
   int n_;
+  bool caller_works_;
   std::vector<std::thread> th_;
   std::mutex mu_;
   std::condition_variable cv_, done_cv_;
@@ -629,7 +632,6 @@ namespace {
 constexpr auto kReadyTimeout = std::chrono::seconds(2);
 
 void dispatch_loop(moe_host_exec* h) {
-  if (!h->cpus.empty()) pin_self(h->cpus[0]);   // the calling thread of the signalled form
   for (;;) {
     SignalJob job;
     bool stopping;
