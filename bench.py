@@ -70,37 +70,60 @@ def measured_traffic(key, algorithmic_bytes=None):
     return e["bytes"]
 
 
-# kernels that make up one launch of each measured entry point (name prefixes)
+# kernels that make up one launch of each measured entry point (name prefixes);
+# the BF16 counter run (--no-fp8) holds the first two, the FP8 one (--only-fp8)
+# the others.  The FP8 decode launches of T = 1, 4 and 16 share a kernel name:
+# they are told apart by order (the run does T = 1, 4, 16 in turn, the same
+# number of launches each).
 PMC_LAUNCHES = {
     "decode_bf16_forward": ["void moe::dec_fused_kernel<false"],
     "prefill_bf16_forward": ["moe::pf_count_kernel", "moe::pf_scan_kernel", "moe::pf_scatter_kernel",
                              "void moe::pf_gemm_kernel<false, true>", "void moe::pf_gemm_kernel<false, false>",
                              "moe::pf_combine_kernel"],
+    "decode_fp8_forward": ["void moe::dec_fused_kernel<true"],
+    "prefill_fp8_forward": ["moe::pf_count_kernel", "moe::pf_scan_kernel", "moe::pf_scatter_kernel",
+                            "void moe::pf_gemm_kernel<true, true>", "void moe::pf_gemm_kernel<true, false>",
+                            "moe::pf_combine_kernel"],
 }
+FP8_TS = (1, 4, 16)
 
 
 def pmc_summary(fetch_dir, write_dir, bench_json):
     import csv
     import glob
+    with open(bench_json) as fh:
+        run = json.loads([ln for ln in fh.read().splitlines() if ln.startswith('{"metric"')][-1])
+    fp8_run = "decode_fp8" in run and "roofline" not in run
     per = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
         assert files, "no counter_collection.csv under %s" % d
         vals = {}
-        for r in csv.DictReader(open(files[0])):
-            if r["Counter_Name"] != counter:
-                continue
+        rows = sorted((r for r in csv.DictReader(open(files[0])) if r["Counter_Name"] == counter),
+                      key=lambda r: int(r["Dispatch_Id"]))
+        for r in rows:
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
         # the calibration copy (a device-to-device copy of COPY_BYTES): the
         # copy kernel with the largest count
         copy = max((k for k in vals if "copybuffer" in k.lower()), key=lambda k: max(vals[k]))
         factor = max(vals[copy]) * 1024.0 / COPY_BYTES      # counter KiB per true KiB
         per[counter] = dict(vals=vals, factor=factor, copy_kernel=copy)
-    out = {"source_sha256": forward_source_hash(),
-           "calibration": {c: {"copy_kernel": per[c]["copy_kernel"], "copy_bytes": COPY_BYTES,
-                               "counter_kib_per_true_kib": round(per[c]["factor"], 4)} for c in per},
-           "launches": {}}
-    for key, prefixes in PMC_LAUNCHES.items():
+    # merge into the committed summary when it describes the same sources
+    try:
+        with open(TRAFFIC_JSON) as fh:
+            out = json.load(fh)
+        if out.get("source_sha256") != forward_source_hash():
+            out = None
+    except (OSError, ValueError):
+        out = None
+    if out is None:
+        out = {"source_sha256": forward_source_hash(), "launches": {}, "counted_runs": {}}
+    out.setdefault("calibration", {})
+    out["calibration"]["fp8_run" if fp8_run else "bf16_run"] = {
+        c: {"copy_kernel": per[c]["copy_kernel"], "copy_bytes": COPY_BYTES,
+            "counter_kib_per_true_kib": round(per[c]["factor"], 4)} for c in per}
+
+    def launch_bytes(prefixes, select=None):
         tot, parts = 0.0, {}
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
             v = per[c]["vals"]
@@ -108,17 +131,32 @@ def pmc_summary(fetch_dir, write_dir, bench_json):
                 ks = [k for k in v if k.startswith(pre)]
                 if not ks:
                     continue
-                avg = sum(sum(v[k]) for k in ks) / sum(len(v[k]) for k in ks)   # KiB per dispatch
-                b = avg * 1024.0 / per[c]["factor"]
+                xs = [x for k in ks for x in (select(v[k]) if select else v[k])]
+                b = sum(xs) / len(xs) * 1024.0 / per[c]["factor"]   # bytes per dispatch
                 parts["%s %s" % (pre.replace("void ", "").replace("moe::", ""), c)] = round(b)
                 tot += b
+        return tot, parts
+
+    keys = ("decode_fp8_forward", "prefill_fp8_forward") if fp8_run else ("decode_bf16_forward", "prefill_bf16_forward")
+    for key in keys:
+        if key == "decode_fp8_forward":
+            K = run["decode_fp8"]["steps"]
+            for i, T in enumerate(FP8_TS):
+                tot, parts = launch_bytes(PMC_LAUNCHES[key], lambda xs, i=i: xs[i * K:(i + 1) * K])
+                byT = run["decode_fp8"]["by_T"]["T%d" % T]
+                out["launches"]["decode_fp8_T%d_forward" % T] = {
+                    "bytes": round(tot), "parts": parts,
+                    "algorithmic_bytes": byT["experts_per_forward"] * byT["bytes_per_expert"]}
+            continue
+        tot, parts = launch_bytes(PMC_LAUNCHES[key])
         if parts:
             out["launches"][key] = {"bytes": round(tot), "parts": parts}
-    with open(bench_json) as fh:
-        run = json.loads([ln for ln in fh.read().splitlines() if ln.startswith('{"metric"')][-1])
-    if "decode_bf16_forward" in out["launches"]:
+    if "decode_bf16_forward" in out["launches"] and not fp8_run:
         out["launches"]["decode_bf16_forward"]["algorithmic_bytes"] = run["roofline"]["bytes_per_launch"]
-    out["counted_run"] = {"trace_steps": run["config"]["trace_steps"]}
+    out.setdefault("counted_runs", {})
+    out["counted_runs"]["fp8_run" if fp8_run else "bf16_run"] = (
+        {"fp8_steps": run["decode_fp8"]["steps"], "fp8_warmup": run["decode_fp8"]["warmup"]} if fp8_run
+        else {"trace_steps": run["config"]["trace_steps"]})
     with open(TRAFFIC_JSON, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
@@ -204,6 +242,8 @@ def parse():
     p.add_argument("--fp8-steps", type=int, default=64)
     p.add_argument("--fp8-warmup", type=int, default=32)
     p.add_argument("--no-prefill-fp8", action="store_true", help="skip the FP8 double-buffered prefill run")
+    p.add_argument("--only-fp8", action="store_true",
+                   help="only the FP8 decode and FP8 prefill runs (the FP8 counter runs); no BF16 headline line")
     p.add_argument("--calibrate-copy", action="store_true",
                    help="first run a plain 1 GiB device-to-device copy 4 times (counter calibration)")
     p.add_argument("--pmc-summary", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "BENCH_JSON"),
@@ -727,7 +767,9 @@ def run_decode_fp8(b, K, W, Ts=(1, 4, 16)):
         ev.close()
         d = c1 - c0
         ach = n_g * S / fwd_s / 1e9
+        tr = measured_traffic("decode_fp8_T%d_forward" % T, n_g * S / K)
         out_all["T%d" % T] = dict(
+            traffic=tr, traffic_over_algorithmic=(tr / (n_g * S / K)) if tr else None,
             expert_GBps=ach, frac_hbm=ach / PEAK_HBM_GBPS, experts_per_forward=n_g / K,
             avg_forward_us=fwd_s / K * 1e6, bytes_per_expert=S,
             layer0_fill_GBps=(cnts[:, 4].sum() * S / fill_s / 1e9) if fill_s > 0 else None,
@@ -892,7 +934,7 @@ def run_prefill_fp8(b):
                 forward_ms_per_layer=sum(fwd_o) / NL * 1e3, variants=variants,
                 roofline=dict(kernel="moe_expert_forward prefill FP8 (sort + gate/up GEMM + down GEMM + combine)",
                               bound="mfma", achieved=ach, peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                              frac=ach / PEAK_BF16_TFLOPS))
+                              frac=ach / PEAK_BF16_TFLOPS, traffic=measured_traffic("prefill_fp8_forward")))
 
 
 def run_resize(b):
@@ -1103,6 +1145,15 @@ def main():
     assert torch.cuda.is_available(), "needs a GPU"
     if a.calibrate_copy:
         calibrate_copy()
+    if a.only_fp8:
+        line = {"metric": METRIC, "value": None, "unit": "GB/s", "n_gpus": 1, "data": "synthetic",
+                "note": "FP8 runs only (counter collection); not a headline line"}
+        line["decode_fp8"] = run_decode_fp8(b, a.fp8_steps, a.fp8_warmup)
+        torch.cuda.empty_cache()
+        if not a.no_prefill_fp8:
+            line["prefill_fp8"] = run_prefill_fp8(b)
+        print(json.dumps(line), flush=True)
+        return
     host_exec = None
     if not a.no_host_exec:
         log("host executor: expert GB/s on %d cores" % len(os.sched_getaffinity(0)))
