@@ -258,16 +258,18 @@ def read_ceiling(b, nbytes, reps=20):
     (a 512 MB write before each rep evicts the caches), HIP-event timed like
     the forward, by (1) moe_stream_read, one launch of plain wide loads and
     nothing else: what a single launch streaming a working set this small
-    reaches, start-up and tail included; (2) a library reduction
-    (torch.sum over float32)."""
+    reaches, start-up and tail included; (2) the same read kernel over a sweep
+    of grid sizes and loads in flight per thread (moe_stream_read_cfg), the
+    best median kept: the fastest single read-only launch of this many bytes
+    found; (3) a library reduction (torch.sum over float32)."""
     import torch
     x = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     flush = torch.empty((512 << 20) // 4, dtype=torch.float32, device="cuda")
     out = torch.empty((), dtype=torch.float32, device="cuda")
     sink = torch.zeros(256, dtype=torch.int32, device="cuda")
     res = {"bytes": nbytes}
-    for name, fn in (("moe_stream_read", lambda: b.stream_read(x, sink)),
-                     ("torch_sum", lambda: torch.sum(x, dim=0, out=out))):
+
+    def timed(fn):
         ev = HipEvents(2 * reps)
         for r in range(reps):
             flush.fill_(float(r))
@@ -278,8 +280,20 @@ def read_ceiling(b, nbytes, reps=20):
         us = sorted(ev.ms(2 * r, 2 * r + 1) * 1e3 for r in range(reps))
         ev.close()
         med = us[len(us) // 2]
-        res[name] = dict(median_us=med, best_us=us[0], GBps_median=nbytes / med / 1e3,
-                         frac_median=nbytes / med / 1e3 / PEAK_HBM_GBPS)
+        return dict(median_us=med, best_us=us[0], GBps_median=nbytes / med / 1e3,
+                    frac_median=nbytes / med / 1e3 / PEAK_HBM_GBPS)
+
+    res["moe_stream_read"] = timed(lambda: b.stream_read(x, sink))
+    sweep = []
+    for n_wg in (256, 512, 1024, 2048, 4096, 8192):
+        for unroll in (1, 2, 4, 8, 16):
+            r = timed(lambda: b.stream_read_cfg(x, sink, n_wg, unroll))
+            sweep.append(dict(n_wg=n_wg, unroll=unroll, median_us=r["median_us"]))
+    best = min(sweep, key=lambda d: d["median_us"])
+    res["stream_read_sweep_best"] = dict(best, GBps_median=nbytes / best["median_us"] / 1e3,
+                                         frac_median=nbytes / best["median_us"] / 1e3 / PEAK_HBM_GBPS)
+    res["stream_read_sweep"] = sweep
+    res["torch_sum"] = timed(lambda: torch.sum(x, dim=0, out=out))
     return res
 
 

@@ -471,6 +471,16 @@ moe_status moe_e4m3_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipS
 moe_status moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
 
 /*
+ * moe_stream_read with its launch shape chosen: n_wg workgroups of 256
+ * threads (1 <= n_wg <= 65536), each thread keeping `unroll` 16-byte loads
+ * in flight (1, 2, 4, 8 or 16); moe_stream_read is n_wg 512, unroll 4.  A
+ * sweep of the two gives the fastest single launch that only reads a given
+ * byte count.  Capturable.
+ */
+moe_status moe_stream_read_cfg(const void* src, size_t bytes, uint32_t* sink, int32_t n_wg, int32_t unroll,
+                               hipStream_t stream);
+
+/*
  * Host executor for the host set C ([FT] section "q* 策略": the misses a step
  * does not fill are computed by the CPU while the GPU evaluates G, and the two
  * partial sums are added; [OSDI] section 4.2: FP8 codes expanded on the CPU,

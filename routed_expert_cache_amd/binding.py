@@ -38,7 +38,7 @@ EXPORTS = [
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_prefill_create_ring", "moe_prefill_finish", "moe_cache_prefill_load",
     "moe_cache_resize",
-    "moe_e4m3_to_bf16", "moe_pack_weights", "moe_stream_read",
+    "moe_e4m3_to_bf16", "moe_pack_weights", "moe_stream_read", "moe_stream_read_cfg",
     "moe_host_exec_create", "moe_host_exec_destroy", "moe_host_exec_simd", "moe_host_exec_cpus", "moe_host_forward",
     "moe_host_forward_enqueue", "moe_host_exec_status", "moe_host_exec_stats",
     "moe_host_signal", "moe_host_forward_signal", "moe_merge_partial_after", "moe_calibrate_bandwidth",
@@ -101,6 +101,7 @@ _sig = {
     "moe_expert_forward_merge_static": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_merge_partial": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "moe_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
+    "moe_stream_read_cfg": (_i32, [_vp, _sz, _vp, _i32, _i32, _vp]),
     "moe_prefill_create": (_i32, [_vp, _P(_vp)]),
     "moe_prefill_prefetch": (_i32, [_vp, _i32, _vp]),
     "moe_prefill_acquire": (_i32, [_vp, _i32, _vp, _P(Slots)]),
@@ -424,6 +425,12 @@ def stream_read(src, sink, stream=None):
     """One launch that only reads src (a measurement reference)."""
     _check(_lib.moe_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink), _stream(stream)),
            "moe_stream_read")
+
+
+def stream_read_cfg(src, sink, n_wg, unroll, stream=None):
+    """moe_stream_read with n_wg workgroups and `unroll` loads in flight per thread."""
+    _check(_lib.moe_stream_read_cfg(_ptr(src), src.numel() * src.element_size(), _ptr(sink), n_wg, unroll,
+                                    _stream(stream)), "moe_stream_read_cfg")
 
 
 def e4m3_to_bf16(codes, out=None, stream=None):

@@ -62,9 +62,10 @@ moe_status check_slots(const moe_slots* s) {
   return MOE_OK;
 }
 
-constexpr int kDT = 256;              // decision kernel: one workgroup of 4 waves
-static_assert(kDT == 256, "the decision kernel's prefix sums read four wave counts as one int4");
+constexpr int kDT = 1024;             // decision kernel: one workgroup of 16 waves
+constexpr int kDW = kDT / 64;
 constexpr int kUMax = 1024;           // T_max * k <= 1024
+static_assert(kUMax == kDT, "the decision kernel holds one routed pick per thread");
 constexpr int kEMax = 4096;
 constexpr int kCMax = 16384;
 
@@ -102,8 +103,23 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
   return lane ? (~0ull >> (64 - lane)) : 0ull;
 }
 
-// Staging batch of the decision kernel: 8 words per thread.
-constexpr int kStageB = kDT * 8;
+// Staging batch of the decision kernel: 2 words per thread.
+constexpr int kStageB = 2048;
+static_assert(kStageB % kDT == 0, "whole staging rows");
+
+// Exclusive prefix (for wave wv) and total of the 16 per-wave counts cnt[0..15]
+// in LDS: lane l reads cnt[l & 15], four DPP row shifts inside each row of 16
+// lanes make the inclusive prefix, and two lane reads pick out the results.
+__device__ __forceinline__ void wave_counts_prefix(const int* cnt, int wv, int& excl, int& total) {
+  static_assert(kDW == 16, "one count per lane of a DPP row");
+  int v = cnt[threadIdx.x & 15];
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);   // row_shr:8
+  total = __builtin_amdgcn_readlane(v, 15);
+  excl = wv ? __builtin_amdgcn_readlane(v, wv - 1) : 0;
+}
 __host__ __device__ constexpr int round_stage(int n) { return (n + kStageB - 1) / kStageB * kStageB; }
 
 // Dynamic LDS of the decision kernel (sizes rounded up to whole staging
@@ -124,87 +140,90 @@ __host__ __device__ inline int decide_lds_bytes(int C, int E) {
 // row, the routed ids) is staged into LDS up front with all loads in flight
 // together; the rest of the kernel reads only LDS, so its barriers wait for
 // LDS traffic only and its global stores drain in the background.
+// One workgroup of 16 waves: with one wave per SIMD the kernel's dependent
+// LDS and ballot chains left the SIMDs idle; four waves per SIMD overlap them.
 // VPL > 0: the kernel routes first (the router of route_topk_kernel, one
 // wave per token, VPL logits per lane) while the table loads are in flight,
 // and writes ids and gate weights as well.
 template <int VPL>
 __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs a) {
   extern __shared__ int dyn[];
-  __shared__ uint32_t bm[kEMax / 32];         // routed experts of this layer
-  __shared__ int uniq[kUMax];                 // local expert index, ascending
-  __shared__ int uslot[kUMax];                // slot of uniq[i] after the step, -1 = host
-  __shared__ int hit_list[kUMax];             // positions into uniq
+  __shared__ uint32_t bm[kEMax / 32];          // routed experts of this layer
+  __shared__ int uniq[kUMax];                  // local expert index, ascending
+  __shared__ int uslot[kUMax];                 // slot of uniq[i] when hit, else -1
+  __shared__ int hit_list[kUMax];              // positions into uniq
   __shared__ int miss_list[kUMax];
   __shared__ int victims[kUMax];
-  __shared__ __align__(16) int s_cnt[kEMax / kDT][kDT / 64][2];   // per (row, wave): routed, hit
-  __shared__ __align__(16) int s_cc[2][kStageB / kDT][kDT / 64];   // per (row, wave): LRU candidates
+  __shared__ int s_cnt[kEMax / kDT][2][kDW];   // per (row, kind, wave): routed, hit
+  __shared__ int s_cc[2][kStageB / kDT][kDW];  // per (chunk parity, row, wave): LRU candidates
+  __shared__ int s_pid[VPL > 0 ? kUMax : 1];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int E = cd.E, C = cd.C;
-  const int P = a.T * a.k;
-  // the layer comes from device memory, so one captured step serves any layer
-  const int layer = a.d_layer ? __builtin_amdgcn_readfirstlane(*a.d_layer) : a.layer;
-  if (layer < 0 || layer >= cd.L) {   // uniform: nothing is decided, every pick goes to the host
-    if (tid == 0) atomicOr(cd.error, 1 << ERR_LAYER);
-    for (int p = tid; p < P; p += kDT) a.out.pick_slot[p] = -1;
-    for (int i = tid; i < a.U_max; i += kDT) {
-      a.out.uniq[i] = a.out.is_hit[i] = a.out.host_id[i] = -1;
-      a.out.fill_id[i] = a.out.fill_slot[i] = a.out.fill_evicted[i] = -1;
-    }
-    if (tid < MOE_CNT_N) a.out.counts[tid] = tid == 6 ? layer : 0;
-    return;
-  }
-  const int lbase = layer * E;
+  const int T = a.T, k = a.k, P = T * k;
+  constexpr int V = kStageB / kDT, NEM = kEMax / kDT;
   const int Cp = round_stage(C), Ep = round_stage(E);
   int* sl = dyn;                                               // slot_id before the step
   uint16_t* ord = reinterpret_cast<uint16_t*>(dyn + Cp);       // LRU order before the step
-  int* row = dyn + Cp + Cp / 2;                                // id_slot[lbase + e]
+  int* row = dyn + Cp + Cp / 2;                                // id_slot[lbase + e]; after step 5 the new slot
   uint32_t* hitbm = reinterpret_cast<uint32_t*>(row + Ep);
 
-  // 0. stage: the loads of the first batch of every table are all issued
-  //    before the first is used (buffer loads past the end return 0, so no
-  //    branch separates them); entries of `order` past n_ord are not used.
-  const uint64_t tick = *cd.tick;      // uniform: scalar loads, consumed late
+  // 0. stage.  The layer scalar is loaded first (a load of 0 bytes when the
+  //    layer comes as an argument), then what does not depend on the layer:
+  //    the router's logits (or the routed ids) ahead of the tables, so that
+  //    routing can run while the table loads are in flight, then the LRU
+  //    order and the slot table; the layer's id_slot row is issued as soon
+  //    as the layer has arrived.  An invalid layer reads no row and is
+  //    handled after the staging (the loads stay unconditional).  Buffer
+  //    loads past the end return 0; entries of `order` past n_ord are not
+  //    used.  All loads are vector loads, so each wait below is for a
+  //    prefix of them in issue order.
+  const int layer_ld = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.d_layer, a.d_layer ? 4u : 0u), 0, 0, 0);
+  __builtin_amdgcn_sched_barrier(0);
+  auto row_of = [&](int t) {
+    return make_rsrc(a.logits + (size_t)(t < T ? t : 0) * E, t < T ? 4u * (uint32_t)E : 0u);
+  };
+  uint32_t kraw[VPL > 0 ? VPL : 1], kc[VPL > 0 ? VPL : 1], ac = 0;
+  int pid = 0;
+  if constexpr (VPL > 0)
+    topk_load<VPL>(row_of(wv), kraw);
+  else
+    pid = __builtin_amdgcn_raw_buffer_load_b32(make_rsrc(a.ids, 4u * (uint32_t)P), 4 * tid, 0, 0);
+  const __amdgpu_buffer_rsrc_t r_ord = make_rsrc(cd.order, 4u * (uint32_t)C);
+  const __amdgpu_buffer_rsrc_t r_sl = make_rsrc(cd.slot_id, 4u * (uint32_t)C);
+  int32_t vo[V], vs[V], vr[V];
+#pragma unroll
+  for (int j = 0; j < V; ++j) {
+    vo[j] = __builtin_amdgcn_raw_buffer_load_b32(r_ord, 4 * (j * kDT + tid), 0, 0);
+    vs[j] = __builtin_amdgcn_raw_buffer_load_b32(r_sl, 4 * (j * kDT + tid), 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+  const uint64_t tick = *cd.tick;      // uniform, consumed late
   const int n_ord = *cd.n_ord;
   uint64_t ctr[6];
 #pragma unroll
   for (int i = 0; i < 6; ++i) ctr[i] = cd.counters[i];
-  const __amdgpu_buffer_rsrc_t r_ids = make_rsrc(a.ids, 4u * (uint32_t)P);
-  const __amdgpu_buffer_rsrc_t r_ord = make_rsrc(cd.order, 4u * (uint32_t)C);
-  const __amdgpu_buffer_rsrc_t r_sl = make_rsrc(cd.slot_id, 4u * (uint32_t)C);
-  const __amdgpu_buffer_rsrc_t r_row = make_rsrc(cd.id_slot + lbase, 4u * (uint32_t)E);
-  constexpr int V = kStageB / kDT, NP = kUMax / kDT;
-  int pid[NP];
-  int32_t vo[V], vs[V], vr[V];
-  if constexpr (VPL == 0) {
+  // the layer comes from device memory, so one captured step serves any
+  // layer (layer_ld is 0 when it comes as an argument: no branch on the load)
+  const int layer = __builtin_amdgcn_readfirstlane(layer_ld) + (a.d_layer ? 0 : a.layer);
+  const bool bad_layer = layer < 0 || layer >= cd.L;
+  const int lbase = bad_layer ? 0 : layer * E;
+  const __amdgpu_buffer_rsrc_t r_row = make_rsrc(cd.id_slot + lbase, bad_layer ? 0u : 4u * (uint32_t)E);
 #pragma unroll
-    for (int j = 0; j < NP; ++j) pid[j] = __builtin_amdgcn_raw_buffer_load_b32(r_ids, 4 * (j * kDT + tid), 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < V; ++j) {
-    const int o = 4 * (j * kDT + tid);
-    vo[j] = __builtin_amdgcn_raw_buffer_load_b32(r_ord, o, 0, 0);
-    vs[j] = __builtin_amdgcn_raw_buffer_load_b32(r_sl, o, 0, 0);
-    vr[j] = __builtin_amdgcn_raw_buffer_load_b32(r_row, o, 0, 0);
-  }
-  __shared__ int s_pid[VPL > 0 ? kUMax : 1];
+  for (int j = 0; j < V; ++j) vr[j] = __builtin_amdgcn_raw_buffer_load_b32(r_row, 4 * (j * kDT + tid), 0, 0);
+  __builtin_amdgcn_sched_barrier(0);   // nothing below moves above the row loads
   if constexpr (VPL > 0) {
-    // wave wv routes tokens wv, wv+4, ...; the next token's logits load
+    topk_keys_of<VPL>(kraw, E, kc, ac);
+    // wave wv routes tokens wv, wv + 16, ...; the next token's logits load
     // while this one is picked (a buffer of 0 bytes past the last token)
-    const int T = a.T, k = a.k;
-    auto row_of = [&](int t) {
-      return make_rsrc(a.logits + (size_t)(t < T ? t : 0) * E, t < T ? 4u * (uint32_t)E : 0u);
-    };
-    uint32_t kc[VPL], ac;
-    topk_keys<VPL>(row_of(wv), E, kc, ac);
-    for (int t = wv; t < T; t += kDT / 64) {
+    for (int t = wv; t < T; t += kDW) {
       uint32_t kn[VPL], an;
-      topk_keys<VPL>(row_of(t + kDT / 64), E, kn, an);
+      topk_keys<VPL>(row_of(t + kDW), E, kn, an);
       int id;
       float wt;
       topk_pick<VPL>(kc, ac, k, id, wt);
-      if (lane < k) {
+      if (lane < k && !bad_layer) {   // a bad layer leaves ids and w unwritten
         const_cast<int32_t*>(a.ids)[t * k + lane] = id;
         a.w[t * k + lane] = wt;
         s_pid[t * k + lane] = id;
@@ -240,69 +259,69 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
 #pragma unroll
     for (int j = 0; j < V; ++j) row[b0 + j * kDT + tid] = vr[j];
   }
+  if (bad_layer) {   // uniform: nothing is decided, every pick goes to the host
+    if (tid == 0) atomicOr(cd.error, 1 << ERR_LAYER);
+    for (int p = tid; p < P; p += kDT) a.out.pick_slot[p] = -1;
+    for (int i = tid; i < a.U_max; i += kDT) {
+      a.out.uniq[i] = a.out.is_hit[i] = a.out.host_id[i] = -1;
+      a.out.fill_id[i] = a.out.fill_slot[i] = a.out.fill_evicted[i] = -1;
+    }
+    if (tid < MOE_CNT_N) a.out.counts[tid] = tid == 6 ? layer : 0;
+    return;
+  }
   for (int i = tid; i < (E + 31) / 32; i += kDT) bm[i] = 0;
   for (int i = tid; i < (C + 31) / 32; i += kDT) hitbm[i] = 0;
   lds_barrier();
-  if constexpr (VPL > 0) {
-#pragma unroll
-    for (int j = 0; j < NP; ++j) pid[j] = j * kDT + tid < P ? s_pid[j * kDT + tid] : 0;
-  }
+  if constexpr (VPL > 0) pid = tid < P ? s_pid[tid] : 0;
 
-  // 1. dedup: bitmap of the routed experts
-#pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    const int p = j * kDT + tid;
-    const int e = pid[j];
-    if (p < P) {
-      if (e < 0 || e >= E)
-        atomicOr(cd.error, 1 << ERR_BAD_ID);
-      else
-        atomicOr(&bm[e >> 5], 1u << (e & 31));
-    }
+  // 1. dedup: bitmap of the routed experts (one pick per thread)
+  if (tid < P) {
+    if (pid < 0 || pid >= E)
+      atomicOr(cd.error, 1 << ERR_BAD_ID);
+    else
+      atomicOr(&bm[pid >> 5], 1u << (pid & 31));
   }
   lds_barrier();
 
   // 2. one ordered pass over the layer's experts, e = j*kDT + tid: routed
   //    (unique, ascending), and hit when the residency table holds it.  The
   //    ranks among the unique, hit and missed experts come from ballots and
-  //    per-(row, wave) counts, with one barrier between counting and placing.
-  //    Every LDS read below is unconditional (indices clamped), so the
-  //    compiler keeps them in flight together instead of waiting per branch.
+  //    per-(row, wave) counts, with one barrier between counting and placing;
+  //    the classification of each thread's experts stays in registers.
   const int NE = (E + kDT - 1) / kDT;
-  const auto classify = [&](int e, bool& routed) {   // -> slot if hit, else -1
-    const int ee = e < E ? e : 0;
-    const uint32_t word = bm[ee >> 5];
-    const int s = row[ee];                             // row is padded: ee is in range
-    const int sc = (s >= 0 && s < C) ? s : 0;
-    const int owner = sl[sc];
-    routed = e < E && ((word >> (ee & 31)) & 1u) != 0;
-    const bool valid = s >= 0 && s < C && owner == lbase + e;
-    if (routed && s >= 0 && !valid) atomicOr(cd.error, 1 << ERR_TABLE);   // a broken entry counts as a miss
-    return routed && valid ? s : -1;
-  };
-  for (int j = 0; j < NE; ++j) {
-    bool rt;
-    const int s = classify(j * kDT + tid, rt);
-    const uint64_t bR = __ballot(rt), bH = __ballot(s >= 0);
-    s_cnt[j][wv][0] = __popcll(bR);   // every lane writes the same value: no branch
-    s_cnt[j][wv][1] = __popcll(bH);
+  int cs[NEM];
+  uint64_t cbR[NEM], cbH[NEM];
+#pragma unroll
+  for (int j = 0; j < NEM; ++j) {
+    if (j < NE) {
+      const int e = j * kDT + tid;
+      const int ee = e < E ? e : 0;
+      const uint32_t word = bm[ee >> 5];
+      const int s = row[ee];                           // row is padded: ee is in range
+      const int owner = sl[(s >= 0 && s < C) ? s : 0];
+      const bool rt = e < E && ((word >> (ee & 31)) & 1u) != 0;
+      const bool valid = s >= 0 && s < C && owner == lbase + e;
+      if (rt && s >= 0 && !valid) atomicOr(cd.error, 1 << ERR_TABLE);   // a broken entry counts as a miss
+      cs[j] = rt ? (valid ? s : -1) : -2;
+      cbR[j] = __ballot(rt);
+      cbH[j] = __ballot(rt && valid);
+      s_cnt[j][0][wv] = __popcll(cbR[j]);   // every lane writes the same value: no branch
+      s_cnt[j][1][wv] = __popcll(cbH[j]);
+    }
   }
   lds_barrier();
-  int u = 0, h = 0;
-  {
-    int bu = 0, bh = 0;   // routed and hit experts before this thread's row and wave
-    for (int j = 0; j < NE; ++j) {
-      const int4 c01 = *reinterpret_cast<const int4*>(&s_cnt[j][0][0]);   // waves 0, 1
-      const int4 c23 = *reinterpret_cast<const int4*>(&s_cnt[j][2][0]);   // waves 2, 3
-      bool rt;
+  int u = 0, h = 0;   // routed and hit experts before the current row
+#pragma unroll
+  for (int j = 0; j < NEM; ++j) {
+    if (j < NE) {
+      int pu, tu, ph, th;
+      wave_counts_prefix(&s_cnt[j][0][0], wv, pu, tu);
+      wave_counts_prefix(&s_cnt[j][1][0], wv, ph, th);
       const int e = j * kDT + tid;
-      const int s = classify(e, rt);
-      const uint64_t bR = __ballot(rt), bH = __ballot(s >= 0);
-      const int pu = bu + (wv > 0 ? c01.x : 0) + (wv > 1 ? c01.z : 0) + (wv > 2 ? c23.x : 0);
-      const int ph = bh + (wv > 0 ? c01.y : 0) + (wv > 1 ? c01.w : 0) + (wv > 2 ? c23.y : 0);
-      if (rt) {
-        const int r = pu + __popcll(bR & lanemask_lt());
-        const int rh = ph + __popcll(bH & lanemask_lt());
+      const int s = cs[j];
+      if (s != -2) {
+        const int r = u + pu + __popcll(cbR[j] & lanemask_lt());
+        const int rh = h + ph + __popcll(cbH[j] & lanemask_lt());
         uniq[r] = e;
         uslot[r] = s;
         a.out.is_hit[r] = s >= 0 ? 1 : 0;
@@ -311,13 +330,12 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
           atomicOr(&hitbm[s >> 5], 1u << (s & 31));
         } else {
           miss_list[r - rh] = r;
+          row[e] = -1;   // host unless step 5 fills it
         }
       }
-      bu += c01.x + c01.z + c23.x + c23.z;
-      bh += c01.y + c01.w + c23.y + c23.w;
+      u += tu;
+      h += th;
     }
-    u = bu;
-    h = bh;
   }
   const int m = u - h;
   for (int i = u + tid; i < a.U_max; i += kDT) a.out.is_hit[i] = -1;
@@ -340,7 +358,6 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
   //    victims; the others keep their relative order in the new order.
   //    Chunks of kStageB entries, i = b0 + j*kDT + tid, one barrier each.
   {
-    constexpr int V = kStageB / kDT;
     int before = 0;   // candidates before the current row
     for (int b0 = 0; b0 < n_ord; b0 += kStageB) {
       const int cb = (b0 / kStageB) & 1;   // count buffers alternate between chunks
@@ -358,20 +375,18 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
         s_cc[cb][j][wv] = __popcll(bc[j]);   // every lane writes the same value: no branch
       }
       lds_barrier();
-      int4 cc[V];
-#pragma unroll
-      for (int j = 0; j < V; ++j) cc[j] = *reinterpret_cast<const int4*>(&s_cc[cb][j][0]);
 #pragma unroll
       for (int j = 0; j < V; ++j) {
-        const int pre = before + (wv > 0 ? cc[j].x : 0) + (wv > 1 ? cc[j].y : 0) + (wv > 2 ? cc[j].z : 0);
+        int pre, tot;
+        wave_counts_prefix(&s_cc[cb][j][0], wv, pre, tot);
         if ((bc[j] >> lane) & 1ull) {
-          const int r = pre + __popcll(bc[j] & lanemask_lt());
+          const int r = before + pre + __popcll(bc[j] & lanemask_lt());
           if (r < q)
             victims[r] = sv[j];
           else
             cd.order[r - q] = sv[j];
         }
-        before += cc[j].x + cc[j].y + cc[j].z + cc[j].w;
+        before += tot;
       }
     }
   }
@@ -380,12 +395,13 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
   // 5. table update: fill i -> victim i; stamps; tail of the new order
   for (int i = tid; i < q; i += kDT) {
     const int v = victims[i];
-    const int f = lbase + uniq[miss_list[i]];
+    const int e = uniq[miss_list[i]];
+    const int f = lbase + e;
     const int old = sl[v];
     if (old >= 0) cd.id_slot[old] = -1;
     cd.slot_id[v] = f;
     cd.id_slot[f] = v;
-    uslot[miss_list[i]] = v;
+    row[e] = v;
     a.out.fill_id[i] = f;
     a.out.fill_slot[i] = v;
     a.out.fill_evicted[i] = old;
@@ -399,24 +415,9 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
   }
   lds_barrier();
 
-  // 6. outputs: rewrite picks, lists, counts
-#pragma unroll
-  for (int j = 0; j < NP; ++j) {
-    const int p = j * kDT + tid;
-    if (p < P) {
-      const int e = pid[j];
-      int slot = -1;
-      if (e >= 0 && e < E) {
-        int lo = 0, hi = u - 1;
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (uniq[mid] < e) lo = mid + 1; else hi = mid;
-        }
-        slot = uslot[lo];
-      }
-      a.out.pick_slot[p] = slot;
-    }
-  }
+  // 6. outputs: rewrite picks (row holds each routed expert's slot after the
+  //    step, -1 for the host), lists, counts
+  if (tid < P) a.out.pick_slot[tid] = (pid >= 0 && pid < E) ? row[pid] : -1;
   for (int i = tid; i < a.U_max; i += kDT) {
     a.out.uniq[i] = i < u ? lbase + uniq[i] : -1;
     if (i >= q) {

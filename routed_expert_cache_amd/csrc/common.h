@@ -155,18 +155,32 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
 
 // Load one token's logits (row: buffer over its E floats) as ordered keys;
 // bit v of `alive` marks key[v] as a real expert (v*64 + lane < E).
+// topk_load issues the loads, topk_keys_of turns them into keys: callers that
+// want other loads issued in between call the two halves.
 template <int VPL>
-__device__ __forceinline__ void topk_keys(__amdgpu_buffer_rsrc_t row, int E, uint32_t (&key)[VPL], uint32_t& alive) {
+__device__ __forceinline__ void topk_load(__amdgpu_buffer_rsrc_t row, uint32_t (&raw)[VPL]) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) raw[v] = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(row, 4 * (v * 64 + lane), 0, 0);
+}
+template <int VPL>
+__device__ __forceinline__ void topk_keys_of(const uint32_t (&raw)[VPL], int E, uint32_t (&key)[VPL], uint32_t& alive) {
   const int lane = threadIdx.x & 63;
   alive = 0;
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = v * 64 + lane;
-    uint32_t u = (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(row, 4 * e, 0, 0);   // 0 past E
-    if ((u & 0x7fffffffu) == 0) u = 0;                                                 // -0 ranks as +0
+    uint32_t u = raw[v];                            // 0 past E
+    if ((u & 0x7fffffffu) == 0) u = 0;              // -0 ranks as +0
     key[v] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
     alive |= (e < E ? 1u : 0u) << v;
   }
+}
+template <int VPL>
+__device__ __forceinline__ void topk_keys(__amdgpu_buffer_rsrc_t row, int E, uint32_t (&key)[VPL], uint32_t& alive) {
+  uint32_t raw[VPL];
+  topk_load<VPL>(row, raw);
+  topk_keys_of<VPL>(raw, E, key, alive);
 }
 
 template <int VPL>

@@ -1578,18 +1578,19 @@ extern "C" moe_status moe_merge_partial(const float* y_gpu, const float* y_host,
 }
 
 namespace moe {
-// Plain streaming read: 4 non-temporal 16-byte loads per thread in flight,
+// Plain streaming read: U non-temporal 16-byte loads per thread in flight,
 // grid-stride, folded with XOR and one atomic per workgroup.
+template <int U>
 __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restrict__ p, size_t n, uint32_t* sink) {
   const size_t gsz = (size_t)gridDim.x * 256;
   size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   uint32_t acc = 0;
-  for (; i + 3 * gsz < n; i += 4 * gsz) {
-    u32x4 v[4];
+  for (; i + (U - 1) * gsz < n; i += U * gsz) {
+    u32x4 v[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) v[u] = __builtin_nontemporal_load(p + i + u * gsz);
+    for (int u = 0; u < U; ++u) v[u] = __builtin_nontemporal_load(p + i + u * gsz);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
+    for (int u = 0; u < U; ++u) acc ^= v[u][0] ^ v[u][1] ^ v[u][2] ^ v[u][3];
   }
   for (; i < n; i += gsz) {
     const u32x4 v = __builtin_nontemporal_load(p + i);
@@ -1600,14 +1601,29 @@ __global__ __launch_bounds__(256) void stream_read_kernel(const u32x4* __restric
 }
 }  // namespace moe
 
-extern "C" moe_status moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+extern "C" moe_status moe_stream_read_cfg(const void* src, size_t bytes, uint32_t* sink, int32_t n_wg, int32_t unroll,
+                                          hipStream_t stream) {
   clear_error();
   if (bytes == 0) return MOE_OK;
   if (!src || !sink) MOE_FAIL(MOE_ERR_ARG, "null argument");
   if (!aligned16(src) || (bytes & 15)) MOE_FAIL(MOE_ERR_ARG, "src must be 16-byte aligned and bytes a multiple of 16");
-  stream_read_kernel<<<512, 256, 0, stream>>>((const u32x4*)src, bytes / 16, sink);
+  if (n_wg < 1 || n_wg > 65536) MOE_FAIL(MOE_ERR_SHAPE, "n_wg %d outside [1, 65536]", n_wg);
+  const u32x4* p = (const u32x4*)src;
+  const size_t n = bytes / 16;
+  switch (unroll) {
+    case 1: stream_read_kernel<1><<<n_wg, 256, 0, stream>>>(p, n, sink); break;
+    case 2: stream_read_kernel<2><<<n_wg, 256, 0, stream>>>(p, n, sink); break;
+    case 4: stream_read_kernel<4><<<n_wg, 256, 0, stream>>>(p, n, sink); break;
+    case 8: stream_read_kernel<8><<<n_wg, 256, 0, stream>>>(p, n, sink); break;
+    case 16: stream_read_kernel<16><<<n_wg, 256, 0, stream>>>(p, n, sink); break;
+    default: MOE_FAIL(MOE_ERR_ARG, "unroll %d not in {1, 2, 4, 8, 16}", unroll);
+  }
   MOE_LAUNCHED();
   return MOE_OK;
+}
+
+extern "C" moe_status moe_stream_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream) {
+  return moe_stream_read_cfg(src, bytes, sink, 512, 4, stream);
 }
 
 extern "C" moe_status moe_e4m3_to_bf16(const uint8_t* codes, uint16_t* out, int64_t n, hipStream_t stream) {
