@@ -149,14 +149,19 @@ template <int VPL>
 __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs a) {
   extern __shared__ int dyn[];
   __shared__ uint32_t bm[kEMax / 32];          // routed experts of this layer
-  __shared__ int uniq[kUMax];                  // local expert index, ascending
-  __shared__ int uslot[kUMax];                 // slot of uniq[i] when hit, else -1
-  __shared__ int hit_list[kUMax];              // positions into uniq
-  __shared__ int miss_list[kUMax];
-  __shared__ int victims[kUMax];
+  // uniq: local expert index, ascending; uslot: slot of uniq[i] when hit,
+  // else -1; hit_list, miss_list: positions into uniq; victims.  Before the
+  // classification the same memory is the router's per-wave scratch.
+  __shared__ __align__(16) int s_lists[5 * kUMax];
+  static_assert(5 * kUMax * 4 >= kDW * 96 * 8, "router scratch fits the lists");
+  int* const uniq = s_lists;
+  int* const uslot = s_lists + kUMax;
+  int* const hit_list = s_lists + 2 * kUMax;
+  int* const miss_list = s_lists + 3 * kUMax;
+  int* const victims = s_lists + 4 * kUMax;
   __shared__ int s_cnt[kEMax / kDT][2][kDW];   // per (row, kind, wave): routed, hit
   __shared__ int s_cc[2][kStageB / kDT][kDW];  // per (chunk parity, row, wave): LRU candidates
-  __shared__ int s_pid[VPL > 0 ? kUMax : 1];
+  __shared__ int s_pid[VPL > 0 ? kUMax : 1];   // the router's picks
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -216,21 +221,22 @@ __global__ __launch_bounds__(kDT) void cache_decide_kernel(CacheDev cd, StepArgs
   if constexpr (VPL > 0) {
     topk_keys_of<VPL>(kraw, E, kc, ac);
     // wave wv routes tokens wv, wv + 16, ...; the next token's logits load
-    // while this one is picked (a buffer of 0 bytes past the last token)
+    // while this one is picked (a buffer of 0 bytes past the last token) and
+    // are waited for only when there is a next token: that wait also covers
+    // the stores issued in between, which a last token need not wait for.
     for (int t = wv; t < T; t += kDW) {
-      uint32_t kn[VPL], an;
-      topk_keys<VPL>(row_of(t + kDW), E, kn, an);
+      const bool more = t + kDW < T;   // uniform
+      uint32_t rn[VPL];
+      topk_load<VPL>(row_of(more ? t + kDW : T), rn);
       int id;
       float wt;
-      topk_pick<VPL>(kc, ac, k, id, wt);
+      topk_pick_fast<VPL>(kc, ac, E, k, reinterpret_cast<uint2*>(s_lists) + 96 * wv, id, wt);
       if (lane < k && !bad_layer) {   // a bad layer leaves ids and w unwritten
         const_cast<int32_t*>(a.ids)[t * k + lane] = id;
         a.w[t * k + lane] = wt;
         s_pid[t * k + lane] = id;
       }
-#pragma unroll
-      for (int v = 0; v < VPL; ++v) kc[v] = kn[v];
-      ac = an;
+      if (more) topk_keys_of<VPL>(rn, E, kc, ac);
     }
   }
 #pragma unroll

@@ -153,6 +153,13 @@ __device__ __forceinline__ float wave_sum_f32(float v) {
   return (a + b) + (c + d);
 }
 
+// Ordered key of a float32 logit's bits: unsigned order of keys is the order
+// of the values, -0 ranks as +0.
+__device__ __forceinline__ uint32_t topk_key_of(uint32_t u) {
+  if ((u & 0x7fffffffu) == 0) u = 0;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
 // Load one token's logits (row: buffer over its E floats) as ordered keys;
 // bit v of `alive` marks key[v] as a real expert (v*64 + lane < E).
 // topk_load issues the loads, topk_keys_of turns them into keys: callers that
@@ -170,9 +177,7 @@ __device__ __forceinline__ void topk_keys_of(const uint32_t (&raw)[VPL], int E, 
 #pragma unroll
   for (int v = 0; v < VPL; ++v) {
     const int e = v * 64 + lane;
-    uint32_t u = raw[v];                            // 0 past E
-    if ((u & 0x7fffffffu) == 0) u = 0;              // -0 ranks as +0
-    key[v] = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    key[v] = topk_key_of(raw[v]);                   // 0 past E
     alive |= (e < E ? 1u : 0u) << v;
   }
 }
@@ -181,6 +186,20 @@ __device__ __forceinline__ void topk_keys(__amdgpu_buffer_rsrc_t row, int E, uin
   uint32_t raw[VPL];
   topk_load<VPL>(row, raw);
   topk_keys_of<VPL>(raw, E, key, alive);
+}
+
+// Logit value of an ordered key (the inverse of the map in topk_keys_of).
+__device__ __forceinline__ float topk_key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// Softmax over the k kept logits, lane j < k holding pick j (pick 0 the
+// maximum); the weight of this lane's pick.
+__device__ __forceinline__ float topk_softmax(float my_z, int k) {
+  const int lane = threadIdx.x & 63;
+  const float zmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_z), 0));
+  const float ex = (lane < k) ? expf(my_z - zmax) : 0.f;
+  return ex / wave_sum_f32(ex);
 }
 
 template <int VPL>
@@ -200,16 +219,81 @@ __device__ __forceinline__ void topk_pick(uint32_t (&key)[VPL], uint32_t alive, 
       if (b) e = v * 64 + (int)__builtin_ctzll(b);
     }
     if ((e & 63) == lane) alive &= ~(1u << (e >> 6));
-    const uint32_t u = (best & 0x80000000u) ? (best & 0x7fffffffu) : ~best;
     if (lane == j) {
       my_id = e;
-      my_z = __uint_as_float(u);
+      my_z = topk_key_value(best);
     }
   }
-  // softmax over the k kept logits; pick 0 holds the maximum
-  const float zmax = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_z), 0));
-  const float ex = (lane < k) ? expf(my_z - zmax) : 0.f;
-  my_w = ex / wave_sum_f32(ex);
+  my_w = topk_softmax(my_z, k);
+}
+
+// Top-k through a threshold, the same picks and weights as topk_pick.  tau is
+// the smallest of the maxima of the ceil(E/16) groups of 16 experts (one DPP
+// row of one key column); each group's maximum reaches tau, so at least that
+// many keys do, and with at least k groups every pick is a key >= tau (a
+// candidate).  The candidates are compacted into this wave's LDS scratch
+// (key, expert) and each ranks itself against the others (higher key, or
+// the same key and a lower index, is ahead: the order of topk_pick); ranks
+// below k are the picks.  Fewer than k groups or more than 64 candidates
+// (heavy ties) take the k-round selection.  scratch: 96 uint2 of this wave,
+// 16-byte aligned.
+template <int VPL>
+__device__ __forceinline__ void topk_pick_fast(uint32_t (&key)[VPL], uint32_t alive, int E, int k, uint2* scratch,
+                                               int& my_id, float& my_w) {
+  const int lane = threadIdx.x & 63;
+  const int r16 = lane >> 4;
+  uint32_t tl = 0xFFFFFFFFu;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    uint32_t m = ((alive >> v) & 1u) ? key[v] : 0u;
+    m = max(m, dpp_u32<kDppXor1>(m));
+    m = max(m, dpp_u32<kDppXor2>(m));
+    m = max(m, dpp_u32<kDppHalfMirror>(m));
+    m = max(m, dpp_u32<kDppMirror>(m));   // every lane of the row: the row's maximum
+    if (v * 64 + r16 * 16 < E) tl = min(tl, m);
+  }
+  const uint32_t t0 = (uint32_t)__builtin_amdgcn_readlane((int)tl, 0), t1 = (uint32_t)__builtin_amdgcn_readlane((int)tl, 16);
+  const uint32_t t2 = (uint32_t)__builtin_amdgcn_readlane((int)tl, 32), t3 = (uint32_t)__builtin_amdgcn_readlane((int)tl, 48);
+  const uint32_t tau = min(min(t0, t1), min(t2, t3));
+  uint64_t b[VPL];
+  int c = 0;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    b[v] = __ballot(((alive >> v) & 1u) && key[v] >= tau);
+    c += __popcll(b[v]);
+  }
+  if (c > 64 || (E + 15) / 16 < k) {   // uniform
+    topk_pick<VPL>(key, alive, k, my_id, my_w);
+    return;
+  }
+  const uint64_t lt = lane ? (~0ull >> (64 - lane)) : 0ull;
+  int base = 0;
+#pragma unroll
+  for (int v = 0; v < VPL; ++v) {
+    if ((b[v] >> lane) & 1ull) scratch[base + __popcll(b[v] & lt)] = make_uint2(key[v], (uint32_t)(v * 64 + lane));
+    base += __popcll(b[v]);
+  }
+  __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): the wave's LDS writes are done
+  const uint2 mine = lane < c ? scratch[lane] : make_uint2(0u, 0u);
+  // eight candidates per round, read together; entries past c are masked
+  // (the 64-entry buffer holds every read)
+  int rank = 0;
+  const auto ahead = [&](uint32_t kj, uint32_t ej, int j) {
+    return ((kj > mine.x) | ((kj == mine.x) & (ej < mine.y))) & (j < c);
+  };
+  for (int j = 0; j < c; j += 8) {
+    uint4 q[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) q[u] = *reinterpret_cast<const uint4*>(scratch + j + 2 * u);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) rank += ahead(q[u].x, q[u].y, j + 2 * u) + ahead(q[u].z, q[u].w, j + 2 * u + 1);
+  }
+  uint2* pk = scratch + 64;
+  if (lane < c && rank < k) pk[rank] = mine;
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  const uint2 p = lane < k ? pk[lane] : make_uint2(0u, 0u);
+  my_id = lane < k ? (int)p.y : -1;
+  my_w = topk_softmax(lane < k ? topk_key_value(p.x) : 0.f, k);
 }
 
 // a * sigmoid(a); the reciprocal is the hardware one (about 1 ulp), far

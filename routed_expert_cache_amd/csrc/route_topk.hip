@@ -1,6 +1,6 @@
 // Top-k router: one wavefront per token (the selection itself is
-// topk_keys / topk_pick in common.h, shared with the fused router + cache
-// step).  [FTK] routing and GPU-router paragraphs.
+// topk_keys / topk_pick_fast in common.h, shared with the fused router +
+// cache step).  [FTK] routing and GPU-router paragraphs.
 #include "common.h"
 
 namespace moe {
@@ -9,6 +9,7 @@ template <int VPL>
 __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict__ logits, int T, int E,
                                                          int k, int32_t* __restrict__ ids,
                                                          float* __restrict__ w) {
+  __shared__ __align__(16) uint2 scratch[4][96];
   const int lane = threadIdx.x & 63;
   const int t = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));   // one token per wave
   if (t >= T) return;
@@ -16,7 +17,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const float* __restrict
   topk_keys<VPL>(make_rsrc(logits + (size_t)t * E, 4u * (uint32_t)E), E, key, alive);
   int my_id;
   float my_w;
-  topk_pick<VPL>(key, alive, k, my_id, my_w);
+  topk_pick_fast<VPL>(key, alive, E, k, scratch[threadIdx.x >> 6], my_id, my_w);
   if (lane < k) {
     ids[(size_t)t * k + lane] = my_id;
     w[(size_t)t * k + lane] = my_w;

@@ -27,8 +27,12 @@ def test_e4m3_expansion_all_codes():
 
 
 # ---------------------------------------------------------------- router
-@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (33, 8, 2), (64, 128, 8), (300, 256, 8), (17, 1000, 32), (5, 64, 32)])
+@pytest.mark.parametrize("T,E,k", [(1, 8, 2), (33, 8, 2), (64, 128, 8), (300, 256, 8), (17, 1000, 32), (5, 64, 32),
+                                   (9, 100, 8), (40, 120, 4), (50, 512, 8)])
 def test_route_topk(T, E, k):
+    """Against the oracle router; the rows cover the threshold selection (a
+    few candidates), its fallback (fewer groups of 16 than picks, or more than
+    64 candidates when everything ties), ties and signed zeros."""
     b = binding()
     rng = np.random.default_rng(T * 1000 + E)
     lg = rng.standard_normal((T, E)).astype(np.float32)
@@ -230,6 +234,8 @@ ROUTE_STEP = [
     (3, 256, 200, 16, 8, 118, 475, 40),     # decode FP8 layer width, 4 tokens per wave
     (2, 1000, 300, 5, 32, 900, 475, 20),    # 16 logits per lane
     (2, 60, 2500, 9, 4, 118, 475, 30),      # pool over two staging batches
+    (3, 64, 150, 16, 8, 118, 475, 40),      # up to 1024 (token, expert) pairs: routing by ranks
+    (2, 128, 300, 12, 8, 527, 773, 30),     # ranks up to 4 tokens, one wave per token beyond
 ]
 
 
@@ -248,6 +254,27 @@ def test_route_step_fused(case):
             lg[:, ::5] = np.float32(0.25)          # ties across experts
         ids, w = hz.route_step(layer, lg)
         # the separate router gives the same bits
+        ids2, w2 = b.route_topk(dev(lg), k)
+        assert torch.equal(ids, ids2) and torch.equal(w, w2)
+    hz.compare_tables()
+
+
+@pytest.mark.parametrize("E,T", [(64, 16), (128, 1), (256, 1), (256, 3), (8, 32)])
+def test_route_step_ties_and_signed_zeros(E, T):
+    """Logits drawn from five values (+0 and -0 among them): most experts tie,
+    so the pick order rests on the lower-index rule; the fused router (ranks
+    or one wave per token, by T and E) against the oracle router and the
+    separate router kernel."""
+    b = binding()
+    k = 8 if E >= 8 else 2
+    hz = Harness(2, E, max(k, E // 2), T, k, 118, 475, copy=False)
+    rng = np.random.default_rng(E * 100 + T)
+    vals = np.array([-0.0, 0.0, 1.0, -1.0, 0.5], np.float32)
+    for s in range(12):
+        lg = vals[rng.integers(0, 5, size=(T, E))]
+        if s == 0:
+            lg[:] = np.float32(-0.0)               # every expert tied
+        ids, w = hz.route_step(int(rng.integers(0, 2)), lg)
         ids2, w2 = b.route_topk(dev(lg), k)
         assert torch.equal(ids, ids2) and torch.equal(w, w2)
     hz.compare_tables()
