@@ -234,8 +234,8 @@ ROUTE_STEP = [
     (3, 256, 200, 16, 8, 118, 475, 40),     # decode FP8 layer width, 4 tokens per wave
     (2, 1000, 300, 5, 32, 900, 475, 20),    # 16 logits per lane
     (2, 60, 2500, 9, 4, 118, 475, 30),      # pool over two staging batches
-    (3, 64, 150, 16, 8, 118, 475, 40),      # up to 1024 (token, expert) pairs: routing by ranks
-    (2, 128, 300, 12, 8, 527, 773, 30),     # ranks up to 4 tokens, one wave per token beyond
+    (3, 64, 150, 16, 8, 118, 475, 40),      # every wave routes a token
+    (2, 128, 300, 12, 8, 527, 773, 30),     # decode BF16 layer width, 12 tokens
 ]
 
 
@@ -262,9 +262,9 @@ def test_route_step_fused(case):
 @pytest.mark.parametrize("E,T", [(64, 16), (128, 1), (256, 1), (256, 3), (8, 32)])
 def test_route_step_ties_and_signed_zeros(E, T):
     """Logits drawn from five values (+0 and -0 among them): most experts tie,
-    so the pick order rests on the lower-index rule; the fused router (ranks
-    or one wave per token, by T and E) against the oracle router and the
-    separate router kernel."""
+    so the pick order rests on the lower-index rule and the candidate count
+    often passes 64 (the k-round fallback); the fused router against the
+    oracle router and the separate router kernel."""
     b = binding()
     k = 8 if E >= 8 else 2
     hz = Harness(2, E, max(k, E // 2), T, k, 118, 475, copy=False)
