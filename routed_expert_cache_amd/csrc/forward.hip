@@ -1274,10 +1274,16 @@ struct DecOcc {
   int fu[2][2] = {{0, 0}, {0, 0}};   // [FP8][8-row down tasks]
   int fu_rg2 = 0;                    // FP8 with two brick rows per gate/up task
 };
-constexpr int kDecD_BF16 = 4;   // register-ring depth in 2-brick steps
-constexpr int kDecD_RES = 4;    // the same for the form with register-resident down weights (DR = 8)
-constexpr int kDecD_FP8 = 3;    // (FP8 steps carry twice the x operand: a shallower ring keeps 2 workgroups per CU)
-constexpr int kDecD_FP8_RG2 = 2;   // FP8, two brick rows per gate/up task: 2 steps of 2 rows in flight
+// Register-ring depths in 2-brick steps.  Deeper rings put more bytes in
+// flight per wave, but past a few KB per wave the launch as a whole streams
+// slower (measured: BF16 T = 16 2 steps 83.5 us against 4 steps 87.4 us;
+// BF16 T = 1 with resident down weights 3 steps 19.5 us against 4 steps
+// 20.5 us; FP8 two-row tasks 1 step 41.9 / 120.1 / 338.5 us at T = 1 / 4 /
+// 16 against 2 steps 48.4 / 134.9 / 352.0 us).
+constexpr int kDecD_BF16 = 2;      // 16-row down tasks
+constexpr int kDecD_RES = 3;       // register-resident down weights (DR = 8)
+constexpr int kDecD_FP8 = 3;       // FP8, one brick row per gate/up task (steps carry twice the x operand)
+constexpr int kDecD_FP8_RG2 = 1;   // FP8, two brick rows per gate/up task
 constexpr int kDecW = 8;   // waves per workgroup
 static std::mutex g_occ_mu;
 static DecOcc g_occ[64];
@@ -1420,13 +1426,21 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     // and 16 (at T = 1 it also halves the task ends)
     const bool rg2 = fp8 && (I / 8) % 2 == 0 && occ.fu_rg2 >= occ.fu[1][0];
     const long tasks = (long)a.G_max * (I / 8) / (rg2 ? 2 : 1) + 2L * (H / 16);
-    const unsigned g1 = (unsigned)std::min<long>(std::min<long>(tasks, (long)occ.cus * occ.fu[f][0]), kDecGridMax);
+    // the grid: every workgroup resident at once (the down phase waits for
+    // the last gate/up task), at most one workgroup per task
+    const auto grid = [&](int per_cu) {
+      return (unsigned)std::min<long>(std::min<long>(tasks, (long)occ.cus * per_cu), kDecGridMax);
+    };
     // 8-row down tasks with register-resident weights and h in LDS when every
-    // task fits in one round of the grid, a wave's steps fit its registers,
-    // h fits the LDS, and the occupancy stays
+    // down task fits in one round of that form's grid, a wave's steps fit its
+    // registers and h fits the LDS
     const long res_steps = ((long)a.G_max * ((I / (fp8 ? 64 : 32) + 3) / 4) + kDecW - 1) / kDecW;
-    const bool dr8 = !fp8 && (long)(H / 8) <= (long)g1 && res_steps <= kDecResSteps &&
-                     (long)a.G_max * T * I * 2 <= kDecResH && occ.fu[f][1] >= occ.fu[f][0];
+    const bool dr8 = !fp8 && (long)(H / 8) <= (long)grid(occ.fu[0][1]) && res_steps <= kDecResSteps &&
+                     (long)a.G_max * T * I * 2 <= kDecResH;
+    // (FP8 two-row tasks: two workgroups per CU, the one-row form's
+    // occupancy, although three fit: measured 120 / 339 us at T = 4 / 16
+    // against 125 / 364 us with three)
+    const unsigned g1 = grid(rg2 ? occ.fu[1][0] : dr8 ? occ.fu[0][1] : occ.fu[f][0]);
     if (rg2)
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (fp8)
