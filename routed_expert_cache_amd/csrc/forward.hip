@@ -152,10 +152,12 @@ __device__ void wave_plan(const int32_t* __restrict__ pick_slot, const float* __
   const int lane = threadIdx.x & 63;
   constexpr unsigned long long kEmpty = ~0ull;
   int sl[kDecPPL], hs[kDecPPL];
+  float pw[kDecPPL];   // gate weights, loaded with the slots: one memory round trip for both
 #pragma unroll
   for (int h = 0; h < kDecPPL; ++h) {
     const int p = lane + 64 * h;
     const int s = p < P ? pick_slot[p] : -1;
+    pw[h] = (s_gw && p < P) ? w[p] : 0.f;
     sl[h] = (s >= 0 && s < n_slots) ? s : -1;
   }
   for (int i = lane; i < kPlanTab; i += 64) s_tab[i] = kEmpty;
@@ -203,7 +205,7 @@ __device__ void wave_plan(const int32_t* __restrict__ pick_slot, const float* __
     for (int h2 = 0; h2 < kDecPPL; ++h2)
       if ((f >> 6) == h2) g = base[h2] + __popcll(m[h2] & ((1ull << (f & 63)) - 1ull));
     if (first[h]) s_gslot[g] = sl[h];
-    if (s_gw) s_gw[g * kDecTok + (lane + 64 * h) / k] = w[lane + 64 * h];
+    if (s_gw) s_gw[g * kDecTok + (lane + 64 * h) / k] = pw[h];
   }
   if (lane == 0) *s_G = base[kDecPPL];
 }
