@@ -78,11 +78,11 @@ def measured_traffic(key, algorithmic_bytes=None):
 PMC_LAUNCHES = {
     "decode_bf16_forward": ["void moe::dec_fused_kernel<false"],
     "prefill_bf16_forward": ["moe::pf_count_kernel", "moe::pf_scan_kernel", "moe::pf_scatter_kernel",
-                             "void moe::pf_gemm_kernel<false, true>", "void moe::pf_gemm_kernel<false, false>",
+                             "void moe::pf_gemm_kernel<false, true>", "void moe::pf_down_kernel<false>",
                              "moe::pf_combine_kernel"],
     "decode_fp8_forward": ["void moe::dec_fused_kernel<true"],
     "prefill_fp8_forward": ["moe::pf_count_kernel", "moe::pf_scan_kernel", "moe::pf_scatter_kernel",
-                            "void moe::pf_gemm_kernel<true, true>", "void moe::pf_gemm_kernel<true, false>",
+                            "void moe::pf_gemm_kernel<true, true>", "void moe::pf_down_kernel<true>",
                             "moe::pf_combine_kernel"],
 }
 FP8_TS = (1, 4, 16)
