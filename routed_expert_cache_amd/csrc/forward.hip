@@ -248,6 +248,8 @@ struct DecWsDev {
 //  16: one brick row per task; each wave streams its (group, K step) pairs
 //      through a register ring D steps deep, weights before the start signal
 //      and h after it.
+//  32: (FP8, larger T) the same with two brick rows per task, each h load
+//      serving both.
 //   8: (BF16) half a brick row per task (the task's slice of a brick is one
 //      128-byte line per K chunk), for calls whose down work is small: every
 //      wave issues ALL of its down weights into registers when its gate/up
@@ -266,15 +268,17 @@ constexpr int kDecResH = 32 * 1024;      // bytes of LDS for h (DR = 8): G * T *
 
 template <bool FP8, int D, int NW, int DR, int RG = 1>
 __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev c) {
-  static_assert(DR == 16 || (DR == 8 && !FP8), "down tasks of 16 rows, or 8 (BF16 only)");
-  static_assert(RG == 1 || (RG == 2 && DR == 16), "gate/up tasks of one brick row, or two (16-row down tasks)");
+  static_assert(DR == 16 || DR == 32 || (DR == 8 && !FP8), "down tasks of 16 or 32 rows, or 8 (BF16 only)");
+  static_assert(RG == 1 || (RG == 2 && DR != 8), "gate/up tasks of one brick row, or two (16-row down tasks)");
+  constexpr int NRB = DR == 32 ? 2 : 1;   // brick rows per down task (DR >= 16)
   __shared__ __align__(16) uint16_t s_h[DR == 8 ? kDecResH / 2 : 8];
   __shared__ int s_gslot[kDecPmax];
   __shared__ float s_gw[kDecPmax * kDecTok];
   __shared__ int s_G;
   __shared__ unsigned long long s_tab[kPlanTab];
   __shared__ f32x4 red[2][NW][64];
-  __shared__ f32x4 redB[RG > 1 ? 2 : 1][NW][RG > 1 ? 64 : 1];   // the second brick row of a gate/up task
+  // the second brick row of a gate/up or down task
+  __shared__ f32x4 redB[RG > 1 || NRB > 1 ? 2 : 1][NW][RG > 1 || NRB > 1 ? 64 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int H = a.H, I = a.I, T = a.T;
@@ -567,7 +571,9 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
       }
     }
   } else if (myB > 0) {
-    u32x4 wb[D][2], ob[D][XN];   // weight bricks and h of D steps
+    // A down task is NRB brick rows of y: each step loads the h operand once
+    // for all of them (at T = 16, h is twice the FP8 weight bytes per row).
+    u32x4 wb[D][NRB][2], ob[D][XN];   // weight bricks and h of D steps
     const int nkt = FP8 ? I / 64 : I / 32;
     const int SB = (nkt + 1) >> 1;
     const int n = G * SB;                       // (group, K step) pairs of every task
@@ -580,20 +586,24 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
     bool qok[D];
     int i_tk = 0, i_l = 0;
     auto issue_w = [&](int d) {   // weights of the next step; remembers its (group, step)
-      const int t = tb0 + i_tk * gs;   // 16-row block of y
+      const int t = tb0 + i_tk * gs;   // DR-row block of y
       const int q = wv * SWB + i_l;
       const bool ok = i_tk < myB && q < n;
       const int qq = ok ? q : 0;
       const int g = qq / SB, s = qq - g * SB;
       const int slot = ok ? __builtin_amdgcn_readfirstlane(s_gslot[g]) : 0;
       const int tr = ok ? t : 0;
-      const __amdgpu_buffer_rsrc_t wr =
-          make_rsrc((const char*)a.w_down + (size_t)slot * dn_bytes + (size_t)tr * nkt * 1024, (uint32_t)(nkt * 1024));
+      const __amdgpu_buffer_rsrc_t wr = make_rsrc(
+          (const char*)a.w_down + (size_t)slot * dn_bytes + (size_t)tr * NRB * nkt * 1024, (uint32_t)(NRB * nkt * 1024));
       const uint32_t wo = oob_sel(ok, (uint32_t)s * 2048u + lane * 16u);
-      wb[d][0] = bload_nt(wr, wo);
-      wb[d][1] = bload_nt(wr, oob_sel(ok, wo + 1024u));
+#pragma unroll
+      for (int rr = 0; rr < NRB; ++rr) {
+        wb[d][rr][0] = bload_nt(wr, oob_sel(ok, wo + (uint32_t)(rr * nkt * 1024)));
+        wb[d][rr][1] = bload_nt(wr, oob_sel(ok, wo + (uint32_t)(rr * nkt * 1024) + 1024u));
+      }
       float f = ok ? s_gw[g * kDecTok + r] : 0.f;
-      if (FP8) f *= a.s_down[((size_t)slot * (H / 128) + (16 * tr) / 128) * (I / 128) + s];
+      // (the NRB brick rows lie in one 128-row scale block: 16 NRB divides 128)
+      if (FP8) f *= a.s_down[((size_t)slot * (H / 128) + (16 * NRB * tr) / 128) * (I / 128) + s];
       fb[d] = f;
       qg[d] = g;
       qs[d] = s;
@@ -620,27 +630,31 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
       }
     };
     // the end of a task: sum the waves' partials in wave order, store y
-    // and the merged output (lanes 16j + r: token r, rows 16t + 4j .. + 3)
-    f32x4 yh = {0, 0, 0, 0};   // host partial of the current task (wave 0)
+    // and the merged output (lanes 16j + r: token r, rows DR t + 16 rr + 4j .. + 3)
+    f32x4 yh[NRB];   // host partial of the current task (wave 0)
+#pragma unroll
+    for (int rr = 0; rr < NRB; ++rr) yh[rr] = f32x4{0, 0, 0, 0};
     auto load_yh = [&](int tk) {
       if (wv == 0 && a.y_host && tok) {
         const int t = tb0 + tk * gs;
-        yh = *reinterpret_cast<const f32x4*>(a.y_host + (size_t)r * H + 16 * t + 4 * j);
+#pragma unroll
+        for (int rr = 0; rr < NRB; ++rr)
+          yh[rr] = *reinterpret_cast<const f32x4*>(a.y_host + (size_t)r * H + DR * t + 16 * rr + 4 * j);
       }
     };
-    auto finish = [&](int tk, const f32x4& acc) {
+    auto finish = [&](int tk, const f32x4 (&acc)[NRB]) {
       const int t = tb0 + tk * gs;
-      f32x4(&rb)[NW][64] = red[tk & 1];
-      rb[wv][lane] = acc;
+      red[tk & 1][wv][lane] = acc[0];
+      if constexpr (NRB > 1) redB[tk & 1][wv][lane] = acc[NRB - 1];
       __syncthreads();
-      if (wv == 0 && tok) {
+      auto out_row = [&](auto& rb, int rr) {
         f32x4 Y = rb[0][lane];
 #pragma unroll
         for (int w2 = 1; w2 < NW; ++w2) Y += rb[w2][lane];
-        const size_t o = (size_t)r * H + 16 * t + 4 * j;
+        const size_t o = (size_t)r * H + DR * t + 16 * rr + 4 * j;
         if (a.y) *reinterpret_cast<f32x4*>(a.y + o) = Y;
         if (a.y_out) {
-          const f32x4 M = Y + yh;
+          const f32x4 M = Y + yh[rr];
           *reinterpret_cast<f32x4*>(a.y_out + o) = M;
           if (a.y_bf16) {
             const uint32_t lo = f32_to_bf16_rne(M[0]) | ((uint32_t)f32_to_bf16_rne(M[1]) << 16);
@@ -648,12 +662,19 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
             *reinterpret_cast<u32x2*>(a.y_bf16 + o) = u32x2{lo, hi};
           }
         }
+      };
+      if (wv == 0 && tok) {
+        out_row(red[tk & 1], 0);
+        if constexpr (NRB > 1) out_row(redB[tk & 1], 1);
       }
     };
     if (SWB == 0) {   // no pick on the GPU: y = 0, y_out = y_host
+      f32x4 z[NRB];
+#pragma unroll
+      for (int rr = 0; rr < NRB; ++rr) z[rr] = f32x4{0, 0, 0, 0};
       for (int tk = 0; tk < myB; ++tk) {
         load_yh(tk);
-        finish(tk, f32x4{0, 0, 0, 0});
+        finish(tk, z);
       }
     } else {
 #pragma unroll
@@ -683,31 +704,37 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
       __syncthreads();
 #pragma unroll
       for (int d = 0; d < D; ++d) issue_h(d);
-      f32x4 acc = {0, 0, 0, 0};
+      f32x4 acc[NRB];
+#pragma unroll
+      for (int rr = 0; rr < NRB; ++rr) acc[rr] = f32x4{0, 0, 0, 0};
       int c_tk = 0, c_l = 0;
       for (int i0 = 0; i0 < nsteps; i0 += D) {
 #pragma unroll
         for (int d = 0; d < D; ++d) {
           if (i0 + d < nsteps) {
-            f32x4 p = {0, 0, 0, 0};
-            if (!FP8) {
-              p = mfma16x16x32(wb[d][0], ob[d][0], p);
-              p = mfma16x16x32(wb[d][1], ob[d][1], p);
-            } else {
-#pragma unroll
-              for (int b = 0; b < 2; ++b) {
-                u32x4 lo, hi;
-                e4m3x16_to_bf16_nat(wb[d][b], lo, hi);
-                p = mfma16x16x32(lo, ob[d][2 * b], p);
-                p = mfma16x16x32(hi, ob[d][2 * b + 1], p);
-              }
-            }
             const float f = fb[d];
 #pragma unroll
-            for (int q = 0; q < 4; ++q) acc[q] += f * p[q];
+            for (int rr = 0; rr < NRB; ++rr) {
+              f32x4 p = {0, 0, 0, 0};
+              if (!FP8) {
+                p = mfma16x16x32(wb[d][rr][0], ob[d][0], p);
+                p = mfma16x16x32(wb[d][rr][1], ob[d][1], p);
+              } else {
+#pragma unroll
+                for (int b = 0; b < 2; ++b) {
+                  u32x4 lo, hi;
+                  e4m3x16_to_bf16_nat(wb[d][rr][b], lo, hi);
+                  p = mfma16x16x32(lo, ob[d][2 * b], p);
+                  p = mfma16x16x32(hi, ob[d][2 * b + 1], p);
+                }
+              }
+#pragma unroll
+              for (int q = 0; q < 4; ++q) acc[rr][q] += f * p[q];
+            }
             if (c_l == SWB - 1) {
               finish(c_tk, acc);
-              acc = f32x4{0, 0, 0, 0};
+#pragma unroll
+              for (int rr = 0; rr < NRB; ++rr) acc[rr] = f32x4{0, 0, 0, 0};
               c_l = 0;
               ++c_tk;
               if (c_tk < myB) load_yh(c_tk);
@@ -1609,6 +1636,7 @@ struct DecOcc {
   int cus = 0;
   int fu[2][2] = {{0, 0}, {0, 0}};   // [FP8][8-row down tasks]
   int fu_rg2 = 0;                    // FP8 with two brick rows per gate/up task
+  int fu_rb2 = 0;                    // ... and per down task
 };
 // Register-ring depths in 2-brick steps.  Deeper rings put more bytes in
 // flight per wave, but past a few KB per wave the launch as a whole streams
@@ -1636,6 +1664,8 @@ static moe_status dec_occupancy(DecOcc* out) {
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[1][0], dec_fused_kernel<true, kDecD_FP8, kDecW, 16>, kDecW * 64, 0));
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu[0][1], dec_fused_kernel<false, kDecD_RES, kDecW, 8>, kDecW * 64, 0));
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu_rg2, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2>,
+                                                         kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu_rb2, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2>,
                                                          kDecW * 64, 0));
     o.fu[1][1] = 0;   // the register-resident form is BF16 only (FP8 steps need more registers than it has)
     for (int i = 0; i < 2; ++i)
@@ -1761,6 +1791,10 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     // 2 B x T per K against 1 B per weight row); measured faster at T = 1, 4
     // and 16 (at T = 1 it also halves the task ends)
     const bool rg2 = fp8 && (I / 8) % 2 == 0 && occ.fu_rg2 >= occ.fu[1][0];
+    // FP8 from T = 8 on: two brick rows per down task too, so each h load
+    // serves both (h is 2 B x T per K against 1 B per weight row; measured
+    // at T = 16: 333 -> 281 us, at T = 4 unchanged)
+    const bool rb2 = rg2 && T >= 8 && occ.fu_rb2 >= occ.fu[1][0];
     const long tasks = (long)a.G_max * (I / 8) / (rg2 ? 2 : 1) + 2L * (H / 16);
     // the grid: every workgroup resident at once (the down phase waits for
     // the last gate/up task), at most one workgroup per task
@@ -1777,7 +1811,9 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     // occupancy, although three fit: measured 120 / 339 us at T = 4 / 16
     // against 125 / 364 us with three)
     const unsigned g1 = grid(rg2 ? occ.fu[1][0] : dr8 ? occ.fu[0][1] : occ.fu[f][0]);
-    if (rg2)
+    if (rb2)
+      dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
+    else if (rg2)
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (fp8)
       dec_fused_kernel<true, kDecD_FP8, kDecW, 16><<<g1, kDecW * 64, 0, stream>>>(a, c);

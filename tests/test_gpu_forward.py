@@ -51,7 +51,8 @@ def _run_forward(b, pool, x_bits, pick_slot, w, mode, T_max=None):
 @pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 128), (3, 8, 2, 256, 128), (16, 32, 4, 512, 256),
                                        (1, 128, 8, 2048, 768), (5, 24, 8, 1024, 384),
                                        (16, 24, 16, 256, 128),      # 256 picks, many shared slots
-                                       (2, 8, 2, 96, 96)])          # odd brick counts along H and I
+                                       (2, 8, 2, 96, 96),           # odd brick counts along H and I
+                                       (16, 64, 8, 2048, 768)])     # several gate/up tasks per workgroup
 def test_decode_bf16(T, E, k, H, I):
     b = binding()
     bank = Bf16Bank(90 + T, E, H, I)
@@ -143,7 +144,9 @@ def test_decode_all_host_gives_zero():
 
 
 # ---------------------------------------------------------------- decode, FP8
-@pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 256), (4, 16, 4, 512, 384), (16, 24, 8, 1024, 256)])
+@pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 256), (4, 16, 4, 512, 384), (16, 24, 8, 1024, 256),
+                                       (8, 16, 8, 512, 256),        # two brick rows per down task from T = 8
+                                       (12, 40, 4, 768, 1024)])     # ... ragged T
 def test_decode_fp8(T, E, k, H, I):
     b = binding()
     bank = Fp8Bank(60 + T, E, H, I)
