@@ -198,6 +198,27 @@ def test_decode_fp8_full_shape(T):
     check_layer(y[tok], yg, "decode fp8 full")
 
 
+@pytest.mark.parametrize("T,n_gpu", [(1, 1), (1, 4), (2, 3), (2, 4)])
+def test_decode_fp8_few_groups_full_shape(T, n_gpu):
+    """Decode FP8 workload shape with one to four groups on the GPU (the rest
+    of each token's picks on the host, as in most calls of the FP8 decode
+    trace).  Every token is checked."""
+    b = binding()
+    c = CONFIGS["decode_fp8"]
+    E, k = 8, c.k
+    bank = Fp8Bank(c.cfg_id, E, c.H, c.I, layer=20 + 4 * T + n_gpu, device="cuda")
+    pool = _slots_identity(b, bank, b.W_FP8_B128)
+    rng = np.random.default_rng(200 + 10 * T + n_gpu)
+    x = gen.activations_bf16(rng, T, c.H)
+    ids = np.stack([rng.permutation(E)[:k] for _ in range(T)])
+    on_gpu = ids < n_gpu                                  # experts 0 .. n_gpu-1 are the GPU set
+    w = np.exp(rng.standard_normal((T, k)))
+    w /= w.sum(1, keepdims=True)
+    y = _run_forward(b, pool, x, np.where(on_gpu, ids, -1), w, b.FWD_DECODE)
+    yg, _ = oracle_partials(x, ids, w, bank.expert64, on_gpu)
+    check_layer(y, yg, "decode fp8 few groups")
+
+
 # ---------------------------------------------------------------- prefill
 @pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 128), (300, 8, 2, 256, 128), (1000, 16, 4, 512, 192),
                                        (257, 8, 2, 128, 64)])   # two K steps in the down GEMM
