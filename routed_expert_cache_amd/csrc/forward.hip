@@ -266,10 +266,13 @@ struct DecWsDev {
 constexpr int kDecResSteps = 6;          // down steps per wave held in registers (DR = 8)
 constexpr int kDecResH = 32 * 1024;      // bytes of LDS for h (DR = 8): G * T * I * 2 at most
 
+// (RG = 4: the register budget of two workgroups per CU is asked for
+// explicitly; left to itself the compiler takes 134 VGPRs, one per CU)
 template <bool FP8, int D, int NW, int DR, int RG = 1>
-__global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev c) {
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RG == 4 ? 4 : 1)))
+void dec_fused_kernel(DecArgs a, DecWsDev c) {
   static_assert(DR == 16 || DR == 32 || (DR == 8 && !FP8), "down tasks of 16 or 32 rows, or 8 (BF16 only)");
-  static_assert(RG == 1 || (RG == 2 && DR != 8), "gate/up tasks of one brick row, or two (16-row down tasks)");
+  static_assert(RG == 1 || ((RG == 2 || RG == 4) && DR != 8), "gate/up tasks of one, two or four brick rows");
   constexpr int NRB = DR == 32 ? 2 : 1;   // brick rows per down task (DR >= 16)
   __shared__ __align__(16) uint16_t s_h[DR == 8 ? kDecResH / 2 : 8];
   __shared__ int s_gslot[kDecPmax];
@@ -279,6 +282,9 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   __shared__ f32x4 red[2][NW][64];
   // the second brick row of a gate/up or down task
   __shared__ f32x4 redB[RG > 1 || NRB > 1 ? 2 : 1][NW][RG > 1 || NRB > 1 ? 64 : 1];
+  // the third and fourth brick rows of a gate/up task (RG = 4), one buffer:
+  // wave 0 sums them before a second barrier releases it
+  __shared__ f32x4 red4[RG == 4 ? 2 : 1][NW][RG == 4 ? 64 : 1];
   const int tid = threadIdx.x, lane = tid & 63, wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int r = lane & 15, j = lane >> 4;
   const int H = a.H, I = a.I, T = a.T;
@@ -309,7 +315,8 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
   // ================= phase A: gate/up + SwiGLU
   // A task is RG brick rows (RG x 16 gate/up rows) of one group: each step
   // loads the x operand once for all RG rows, so x is re-read from the
-  // caches once per RG rows (it is as large as the weights at T = 8).
+  // caches once per RG rows (it is as large as the FP8 weights of two rows
+  // at T = 16; FP8 uses RG = 2, and RG = 4 from T = 8 on).
   {
     u32x4 wb[D][RG][2], ob[D][XN];   // weight bricks and x of D steps
     const int nkt = FP8 ? H / 64 : H / 32;
@@ -396,17 +403,34 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
             const int g = task / RAT, t = (task - g * RAT) * RG;
             f32x4(&rb)[NW][64] = red[c_tk & 1];
             rb[wv][lane] = acc[0];
-            if constexpr (RG > 1) redB[c_tk & 1][wv][lane] = acc[RG - 1];
+            if constexpr (RG > 1) redB[c_tk & 1][wv][lane] = acc[1];
+            if constexpr (RG == 4) {
+              red4[0][wv][lane] = acc[2];
+              red4[1][wv][lane] = acc[3];
+            }
             __syncthreads();
-            if (wv == 0) {
-              // sum one brick row's partials over the waves, SwiGLU, store its h
-              auto row_out = [&](auto& rx, int rr) {
-                f32x4 Gv = rx[0][lane], Uv = rx[0][lane + 32];
+            // a brick row's partials summed over the waves (gate lanes j < 2,
+            // the up value of the same feature at lane + 32)
+            auto row_sum = [&](auto& rx, f32x4& Gv, f32x4& Uv) {
+              Gv = rx[0][lane];
+              Uv = rx[0][lane + 32];
 #pragma unroll
-                for (int w2 = 1; w2 < NW; ++w2) {
-                  Gv += rx[w2][lane];
-                  Uv += rx[w2][lane + 32];
-                }
+              for (int w2 = 1; w2 < NW; ++w2) {
+                Gv += rx[w2][lane];
+                Uv += rx[w2][lane + 32];
+              }
+            };
+            f32x4 G4[RG == 4 ? 2 : 1], U4[RG == 4 ? 2 : 1];
+            if constexpr (RG == 4) {
+              if (wv == 0 && j < 2) {
+                row_sum(red4[0], G4[0], U4[0]);
+                row_sum(red4[1], G4[1], U4[1]);
+              }
+              __syncthreads();   // red4 is free for the next task's partials
+            }
+            if (wv == 0) {
+              // SwiGLU of one brick row's sums, store its h
+              auto row_emit = [&](const f32x4& Gv, const f32x4& Uv, int rr) {
                 const uint32_t h01 = f32_to_bf16_rne(silu_f32(Gv[0]) * Uv[0]) |
                                      ((uint32_t)f32_to_bf16_rne(silu_f32(Gv[1]) * Uv[1]) << 16);
                 const uint32_t h23 = f32_to_bf16_rne(silu_f32(Gv[2]) * Uv[2]) |
@@ -415,9 +439,18 @@ __global__ __launch_bounds__(NW * 64) void dec_fused_kernel(DecArgs a, DecWsDev 
                 __builtin_amdgcn_raw_buffer_store_b64(
                     u32x2{h01, h23}, hw, (uint32_t)((((size_t)g * kDecTok + r) * I + 8 * (t + rr) + 4 * j) * 2), 0, 16);
               };
+              auto row_out = [&](auto& rx, int rr) {
+                f32x4 Gv, Uv;
+                row_sum(rx, Gv, Uv);
+                row_emit(Gv, Uv, rr);
+              };
               if (j < 2 && tok) {
                 row_out(red[c_tk & 1], 0);
                 if constexpr (RG > 1) row_out(redB[c_tk & 1], 1);
+                if constexpr (RG == 4) {
+                  row_emit(G4[0], U4[0], 2);
+                  row_emit(G4[1], U4[1], 3);
+                }
               }
               __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0): the stores above have completed
               __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");   // and stay before the count
@@ -1637,6 +1670,7 @@ struct DecOcc {
   int fu[2][2] = {{0, 0}, {0, 0}};   // [FP8][8-row down tasks]
   int fu_rg2 = 0;                    // FP8 with two brick rows per gate/up task
   int fu_rb2 = 0;                    // ... and per down task
+  int fu_rg4 = 0;                    // FP8, four brick rows per gate/up task, two per down task
 };
 // Register-ring depths in 2-brick steps.  Deeper rings put more bytes in
 // flight per wave, but past a few KB per wave the launch as a whole streams
@@ -1666,6 +1700,8 @@ static moe_status dec_occupancy(DecOcc* out) {
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu_rg2, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2>,
                                                          kDecW * 64, 0));
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu_rb2, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2>,
+                                                         kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu_rg4, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 4>,
                                                          kDecW * 64, 0));
     o.fu[1][1] = 0;   // the register-resident form is BF16 only (FP8 steps need more registers than it has)
     for (int i = 0; i < 2; ++i)
@@ -1795,7 +1831,10 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     // serves both (h is 2 B x T per K against 1 B per weight row; measured
     // at T = 16: 333 -> 281 us, at T = 4 unchanged)
     const bool rb2 = rg2 && T >= 8 && occ.fu_rb2 >= occ.fu[1][0];
-    const long tasks = (long)a.G_max * (I / 8) / (rg2 ? 2 : 1) + 2L * (H / 16);
+    // ... and four brick rows per gate/up task, so x is re-read once per
+    // four rows (measured at T = 16: 285 -> 247 us)
+    const bool rg4 = rb2 && (I / 8) % 4 == 0 && occ.fu_rg4 >= occ.fu[1][0];
+    const long tasks = (long)a.G_max * (I / 8) / (rg4 ? 4 : rg2 ? 2 : 1) + 2L * (H / 16);
     // the grid: every workgroup resident at once (the down phase waits for
     // the last gate/up task), at most one workgroup per task
     const auto grid = [&](int per_cu) {
@@ -1811,7 +1850,9 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     // occupancy, although three fit: measured 120 / 339 us at T = 4 / 16
     // against 125 / 364 us with three)
     const unsigned g1 = grid(rg2 ? occ.fu[1][0] : dr8 ? occ.fu[0][1] : occ.fu[f][0]);
-    if (rb2)
+    if (rg4)
+      dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 4><<<g1, kDecW * 64, 0, stream>>>(a, c);
+    else if (rb2)
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (rg2)
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
