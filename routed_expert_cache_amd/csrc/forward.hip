@@ -268,7 +268,9 @@ constexpr int kDecResH = 32 * 1024;      // bytes of LDS for h (DR = 8): G * T *
 
 // (RG = 4: the register budget of two workgroups per CU is asked for
 // explicitly; left to itself the compiler takes 134 VGPRs, one per CU)
-template <bool FP8, int D, int NW, int DR, int RG = 1>
+// HDEV: the down phase reads h with device-scope loads instead of one L2
+// invalidate per workgroup and ordinary loads (cheaper when h is small: T <= 2).
+template <bool FP8, int D, int NW, int DR, int RG = 1, bool HDEV = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RG == 4 ? 4 : 1)))
 void dec_fused_kernel(DecArgs a, DecWsDev c) {
   static_assert(DR == 16 || DR == 32 || (DR == 8 && !FP8), "down tasks of 16 or 32 rows, or 8 (BF16 only)");
@@ -654,7 +656,10 @@ void dec_fused_kernel(DecArgs a, DecWsDev c) {
         const int k0 = FP8 ? 128 * s + 64 * b : 64 * s + 32 * b;
         const bool ho = qok[d] && tok && k0 < I;
         const uint32_t off = oob_sel(ho, (hrow + k0 + (FP8 ? 16 : 8) * j) * 2u);
-        if (FP8) {
+        if (FP8 && HDEV) {
+          ob[d][2 * b] = bload_dev(hr, off);
+          ob[d][2 * b + 1] = bload_dev(hr, oob_sel(ho, off + 16u));
+        } else if (FP8) {
           ob[d][2 * b] = bload(hr, off);
           ob[d][2 * b + 1] = bload(hr, oob_sel(ho, off + 16u));
         } else {
@@ -731,8 +736,9 @@ void dec_fused_kernel(DecArgs a, DecWsDev c) {
         // h written on other XCDs is read from memory: one L2 invalidate per
         // workgroup, then ordinary loads that the XCD's L2 serves to every
         // down workgroup on it (device-scope loads re-read h from memory each
-        // time, which costs more than the invalidate once T is large)
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+        // time, which costs more than the invalidate once T is large; HDEV
+        // takes them instead)
+        if constexpr (!HDEV) __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       __syncthreads();
 #pragma unroll
@@ -1671,6 +1677,7 @@ struct DecOcc {
   int fu_rg2 = 0;                    // FP8 with two brick rows per gate/up task
   int fu_rb2 = 0;                    // ... and per down task
   int fu_rg4 = 0;                    // FP8, four brick rows per gate/up task, two per down task
+  int fu_rg2h = 0;                   // FP8 two-row gate/up tasks, device-scope h loads
 };
 // Register-ring depths in 2-brick steps.  Deeper rings put more bytes in
 // flight per wave, but past a few KB per wave the launch as a whole streams
@@ -1703,6 +1710,8 @@ static moe_status dec_occupancy(DecOcc* out) {
                                                          kDecW * 64, 0));
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(&o.fu_rg4, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 4>,
                                                          kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &o.fu_rg2h, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2, true>, kDecW * 64, 0));
     o.fu[1][1] = 0;   // the register-resident form is BF16 only (FP8 steps need more registers than it has)
     for (int i = 0; i < 2; ++i)
       if (o.fu[i][0] < 1) o.fu[i][0] = 1;
@@ -1854,6 +1863,9 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 4><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (rb2)
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
+    else if (rg2 && T <= 2 && occ.fu_rg2h >= occ.fu[1][0])   // (device-scope h loads: T = 1 41.8 -> 40.2 us,
+                                                             // T = 4 119.6 -> 121.3 us)
+      dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2, true><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (rg2)
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (fp8)
