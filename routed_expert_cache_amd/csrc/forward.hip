@@ -248,7 +248,7 @@ struct DecWsDev {
 //  16: one brick row per task; each wave streams its (group, K step) pairs
 //      through a register ring D steps deep, weights before the start signal
 //      and h after it.
-//  32: (FP8, larger T) the same with two brick rows per task, each h load
+//  32: (FP8, T >= 2) the same with two brick rows per task, each h load
 //      serving both.
 //   8: (BF16) half a brick row per task (the task's slice of a brick is one
 //      128-byte line per K chunk), for calls whose down work is small: every
@@ -269,7 +269,7 @@ constexpr int kDecResH = 32 * 1024;      // bytes of LDS for h (DR = 8): G * T *
 // (RG = 4: the register budget of two workgroups per CU is asked for
 // explicitly; left to itself the compiler takes 134 VGPRs, one per CU)
 // HDEV: the down phase reads h with device-scope loads instead of one L2
-// invalidate per workgroup and ordinary loads (cheaper when h is small: T <= 2).
+// invalidate per workgroup and ordinary loads (cheaper when h is small: T = 1).
 template <bool FP8, int D, int NW, int DR, int RG = 1, bool HDEV = false>
 __global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(RG == 4 ? 4 : 1)))
 void dec_fused_kernel(DecArgs a, DecWsDev c) {
@@ -1836,13 +1836,13 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     // 2 B x T per K against 1 B per weight row); measured faster at T = 1, 4
     // and 16 (at T = 1 it also halves the task ends)
     const bool rg2 = fp8 && (I / 8) % 2 == 0 && occ.fu_rg2 >= occ.fu[1][0];
-    // FP8 from T = 8 on: two brick rows per down task too, so each h load
+    // FP8 from T = 2 on: two brick rows per down task too, so each h load
     // serves both (h is 2 B x T per K against 1 B per weight row; measured
-    // at T = 16: 333 -> 281 us, at T = 4 unchanged)
-    const bool rb2 = rg2 && T >= 8 && occ.fu_rb2 >= occ.fu[1][0];
-    // ... and four brick rows per gate/up task, so x is re-read once per
-    // four rows (measured at T = 16: 285 -> 247 us)
-    const bool rg4 = rb2 && (I / 8) % 4 == 0 && occ.fu_rg4 >= occ.fu[1][0];
+    // at T = 16: 333 -> 281 us, T = 4: 121 -> 111 us, T = 2: 67.5 -> 64.4 us)
+    const bool rb2 = rg2 && T >= 2 && occ.fu_rb2 >= occ.fu[1][0];
+    // from T = 8 on, also four brick rows per gate/up task, so x is re-read
+    // once per four rows (measured at T = 16: 285 -> 247 us; at T = 4 slower)
+    const bool rg4 = rb2 && T >= 8 && (I / 8) % 4 == 0 && occ.fu_rg4 >= occ.fu[1][0];
     const long tasks = (long)a.G_max * (I / 8) / (rg4 ? 4 : rg2 ? 2 : 1) + 2L * (H / 16);
     // the grid: every workgroup resident at once (the down phase waits for
     // the last gate/up task), at most one workgroup per task
@@ -1863,7 +1863,7 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 4><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (rb2)
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
-    else if (rg2 && T <= 2 && occ.fu_rg2h >= occ.fu[1][0])   // (device-scope h loads: T = 1 41.8 -> 40.2 us,
+    else if (rg2 && T == 1 && occ.fu_rg2h >= occ.fu[1][0])   // (device-scope h loads: T = 1 41.8 -> 40.2 us,
                                                              // T = 4 119.6 -> 121.3 us)
       dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2, true><<<g1, kDecW * 64, 0, stream>>>(a, c);
     else if (rg2)
