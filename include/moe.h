@@ -149,6 +149,7 @@ typedef struct moe_step_out {
 
 #define MOE_FWD_DECODE 0u     /* grouped GEMV, T <= 16                           */
 #define MOE_FWD_PREFILL 1u    /* sorted grouped GEMM on MFMA                     */
+#define MOE_FWD_DECODE_SPLIT 2u /* MOE_FWD_DECODE in two launches (see below)    */
 
 /* Message of the last failed call on this thread ("" if none). */
 const char* moe_last_error(void);
@@ -327,13 +328,22 @@ moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int32_t H, int3
  * token's k rows are summed (in FP32, pick order).
  *   mode MOE_FWD_DECODE: T <= 16 and T*k <= 256 (grouped GEMV streaming each
  *     slot once; y is the same bits on every run).
+ *   mode MOE_FWD_DECODE_SPLIT: the decode evaluation in two launches of the
+ *     same kernel (gate/up + SwiGLU, then down + gate weight), the same
+ *     bits.  MOE_FWD_DECODE hands h from the gate/up to the down work inside
+ *     one launch, so its down workgroups wait for gate/up work of the same
+ *     grid: it needs the whole grid resident at once (the grid is sized to
+ *     the compute units' capacity; a GPU whose units are shared with other
+ *     work can break that, and the bounded wait then reports it, below).
+ *     The split form waits for nothing and completes on any share of the
+ *     GPU, at the cost of a second launch.
  *   mode MOE_FWD_PREFILL: any T (tokens sorted by slot, grouped GEMM).
  * ws: device workspace of moe_forward_workspace_bytes(T_max >= T, ...),
  * owned by the caller, 256-byte aligned and ZERO-FILLED before its first
  * use: decode mode keeps its hand-over counters there and leaves them at
  * zero on exit, so the same workspace serves any later call on the same
  * stream without clearing; calls that overlap on one workspace race.  A
- * decode call whose internal wait timed out (only possible when its
+ * MOE_FWD_DECODE call whose internal wait timed out (only possible when its
  * workgroups cannot all be resident, e.g. a shared GPU) sets the first
  * 32-bit word of ws to a non-zero value; y is then not valid, and ws must be
  * zero-filled again before its next use (a late hand-over store may leave a
@@ -358,6 +368,20 @@ moe_status moe_expert_forward_merge(const moe_slots* slots, const uint16_t* x, c
                                     const float* w, int32_t T, int32_t k, float* y_gpu, const float* y_host,
                                     float* y_out, uint16_t* y_out_bf16, void* ws, size_t ws_bytes, uint32_t mode,
                                     hipStream_t stream);
+
+/*
+ * Launch shape of the decode forward (MOE_FWD_DECODE and _SPLIT in
+ * moe_expert_forward and _merge): n_workgroups > 0 fixes the grid of every
+ * later decode launch in this process, 0 restores the automatic grid (as
+ * many workgroups as the compute units hold at once).  For tests and
+ * tuning: in MOE_FWD_DECODE_SPLIT mode every grid completes, with the same
+ * bits for every grid that keeps the kernel form (BF16 small batches take
+ * 8-row down tasks only on grids of at least H/8 workgroups; smaller grids
+ * sum in another order); MOE_FWD_DECODE with more workgroups than the GPU
+ * holds at once times out (see moe_expert_forward).  Host only, takes effect at the next launch;
+ * MOE_ERR_ARG outside [0, 4096].
+ */
+moe_status moe_decode_grid_override(int32_t n_workgroups);
 
 /*
  * For callers that cannot allocate device memory: code under hipGraph

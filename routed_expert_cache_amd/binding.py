@@ -26,14 +26,14 @@ STEP_NO_COPY = 1
 STEP_FILL_ALL = 2
 HOST_PORTABLE = 1
 HOST_PIN = 2
-FWD_DECODE, FWD_PREFILL = 0, 1
+FWD_DECODE, FWD_PREFILL, FWD_DECODE_SPLIT = 0, 1, 2
 CNT_UNIQ, CNT_HIT, CNT_MISS, CNT_QSTAR, CNT_FILL, CNT_HOST, CNT_N = 0, 1, 2, 3, 4, 5, 8
 
 EXPORTS = [
     "moe_last_error", "moe_route_topk", "moe_cache_workspace_bytes", "moe_cache_create",
     "moe_cache_seed", "moe_cache_step", "moe_cache_route_step", "moe_cache_fill", "moe_cache_read_state", "moe_cache_error",
     "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_expert_forward_merge",
-    "moe_expert_forward_merge_static",
+    "moe_expert_forward_merge_static", "moe_decode_grid_override",
     "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_prefill_create_ring", "moe_prefill_finish", "moe_cache_prefill_load",
@@ -99,6 +99,7 @@ _sig = {
     "moe_expert_forward_merge": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp, _sz,
                                         _u32, _vp]),
     "moe_expert_forward_merge_static": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
+    "moe_decode_grid_override": (_i32, [_i32]),
     "moe_merge_partial": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "moe_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
     "moe_stream_read_cfg": (_i32, [_vp, _sz, _vp, _i32, _i32, _vp]),
@@ -395,6 +396,12 @@ def expert_forward_merge_static(slots_c, x, pick_slot, w, y_host, y_out=None, y_
                                                 _ptr(y_gpu), _ptr(y_host), _ptr(y_out), _ptr(y_out_bf16),
                                                 _stream(stream)), "moe_expert_forward_merge_static")
     return y_out
+
+
+def decode_grid_override(n_workgroups):
+    """Fix the decode forward's grid to n_workgroups for later launches in this
+    process (0: automatic)."""
+    _check(_lib.moe_decode_grid_override(int(n_workgroups)), "moe_decode_grid_override")
 
 
 def merge_partial(y_gpu, y_host, y_out=None, y_out_bf16=None, stream=None):

@@ -22,6 +22,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <atomic>
 #include <mutex>
 
 namespace moe {
@@ -114,6 +115,7 @@ struct DecArgs {
   uint16_t* y_bf16;          // [T][H] BF16 of y_out (merge), or NULL
   uint16_t* h;               // workspace [G_max][16][I] BF16
   int G_max;
+  int phase;                 // 0: both projections in one launch; a split pair: 1 gate/up only, then 2 down only
 };
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -297,7 +299,9 @@ void dec_fused_kernel(DecArgs a, DecWsDev c) {
   constexpr int XN = FP8 ? 4 : 2;
   const int RA = I / 8;                          // gate/up brick rows
   const int RAT = RA / RG;                       // gate/up tasks per group (the host checks RG | RA)
-  const int nA = G * RAT, nB = H / DR;
+  // (a split pair: the first launch takes only the gate/up tasks, the
+  // second only the down tasks, which then find h complete and wait for nothing)
+  const int nA = a.phase == 2 ? 0 : G * RAT, nB = a.phase == 1 ? 0 : H / DR;
   const int b0 = (int)blockIdx.x, gs = (int)gridDim.x;
   // the gate/up tasks go round-robin over the whole grid (the fewest per
   // compute unit at most); the down tasks start at workgroup nA % gs, the
@@ -511,7 +515,7 @@ void dec_fused_kernel(DecArgs a, DecWsDev c) {
     f32x4 yh = {0, 0, 0, 0};
     if (wv == 0 && a.y_host && tok && j < 2)
       yh = *reinterpret_cast<const f32x4*>(a.y_host + (size_t)r * H + 8 * t + 4 * j);
-    if (wv == 0 && rn > 0) {   // wait for the start signal of the down phase (bounded)
+    if (wv == 0 && rn > 0 && a.phase == 0) {   // wait for the start signal of the down phase (bounded)
       uint32_t* flag = c.go + (size_t)b0 * kCtrlStride;
       uint32_t it = 0;
       for (;;) {
@@ -719,7 +723,7 @@ void dec_fused_kernel(DecArgs a, DecWsDev c) {
       for (int d = 0; d < D; ++d) issue_w(d);
       load_yh(0);
       // wait for the start signal of the down phase (bounded)
-      if (wv == 0) {
+      if (wv == 0 && a.phase == 0) {
         uint32_t* flag = c.go + (size_t)b0 * kCtrlStride;
         uint32_t it = 0;
         for (;;) {
@@ -1690,6 +1694,7 @@ constexpr int kDecD_RES = 3;       // register-resident down weights (DR = 8)
 constexpr int kDecD_FP8 = 3;       // FP8, one brick row per gate/up task (steps carry twice the x operand)
 constexpr int kDecD_FP8_RG2 = 1;   // FP8, two brick rows per gate/up task
 constexpr int kDecW = 8;   // waves per workgroup
+static std::atomic<int> g_dec_grid_override{0};   // decode forward grid, 0: automatic
 static std::mutex g_occ_mu;
 static DecOcc g_occ[64];
 static moe_status dec_occupancy(DecOcc* out) {
@@ -1758,7 +1763,7 @@ extern "C" moe_status moe_forward_workspace_bytes(int32_t T_max, int32_t k, int3
   clear_error();
   if (!bytes) MOE_FAIL(MOE_ERR_ARG, "bytes is NULL");
   if (T_max < 1 || k < 1 || H < 1 || I < 1 || n_slots < 1) MOE_FAIL(MOE_ERR_SHAPE, "bad sizes");
-  if (mode == MOE_FWD_DECODE) {
+  if (mode == MOE_FWD_DECODE || mode == MOE_FWD_DECODE_SPLIT) {
     if (T_max > kDecTok || T_max * k > kDecPmax)
       MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T_max <= %d and T_max*k <= %d", kDecTok, kDecPmax);
     *bytes = dec_ws(T_max, k, H, I, n_slots).total;
@@ -1809,7 +1814,7 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
   const int H = slots->H, I = slots->I;
   char* wsb = (char*)ws;
 
-  if (mode == MOE_FWD_DECODE) {
+  if (mode == MOE_FWD_DECODE || mode == MOE_FWD_DECODE_SPLIT) {
     if (T > kDecTok || T * k > kDecPmax)
       MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T <= %d and T*k <= %d (T=%d k=%d)", kDecTok, kDecPmax, T, k);
     if (fp8 && H > 16384) MOE_FAIL(MOE_ERR_SHAPE, "FP8 decode mode needs H <= 16384 (H=%d)", H);
@@ -1853,28 +1858,33 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     // down task fits in one round of that form's grid, a wave's steps fit its
     // registers and h fits the LDS
     const long res_steps = ((long)a.G_max * ((I / (fp8 ? 64 : 32) + 3) / 4) + kDecW - 1) / kDecW;
-    const bool dr8 = !fp8 && (long)(H / 8) <= (long)grid(occ.fu[0][1]) && res_steps <= kDecResSteps &&
-                     (long)a.G_max * T * I * 2 <= kDecResH;
+    const int ov = g_dec_grid_override.load(std::memory_order_relaxed);
+    const bool dr8 = !fp8 && (long)(H / 8) <= (ov > 0 ? (long)ov : (long)grid(occ.fu[0][1])) &&
+                     res_steps <= kDecResSteps && (long)a.G_max * T * I * 2 <= kDecResH;
     // (FP8 two-row tasks: two workgroups per CU, the one-row form's
     // occupancy, although three fit: measured 120 / 339 us at T = 4 / 16
     // against 125 / 364 us with three)
-    const unsigned g1 = grid(rg2 ? occ.fu[1][0] : dr8 ? occ.fu[0][1] : occ.fu[f][0]);
-    if (rg4)
-      dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 4><<<g1, kDecW * 64, 0, stream>>>(a, c);
-    else if (rb2)
-      dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
-    else if (rg2 && T == 1 && occ.fu_rg2h >= occ.fu[1][0])   // (device-scope h loads: T = 1 41.8 -> 40.2 us,
-                                                             // T = 4 119.6 -> 121.3 us)
-      dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2, true><<<g1, kDecW * 64, 0, stream>>>(a, c);
-    else if (rg2)
-      dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
-    else if (fp8)
-      dec_fused_kernel<true, kDecD_FP8, kDecW, 16><<<g1, kDecW * 64, 0, stream>>>(a, c);
-    else if (dr8)
-      dec_fused_kernel<false, kDecD_RES, kDecW, 8><<<g1, kDecW * 64, 0, stream>>>(a, c);
-    else
-      dec_fused_kernel<false, kDecD_BF16, kDecW, 16><<<g1, kDecW * 64, 0, stream>>>(a, c);
-    MOE_LAUNCHED();
+    const unsigned g1 = ov > 0 ? (unsigned)ov : grid(rg2 ? occ.fu[1][0] : dr8 ? occ.fu[0][1] : occ.fu[f][0]);
+    // MOE_FWD_DECODE_SPLIT: the same kernel twice (gate/up, then down)
+    for (int ph = mode == MOE_FWD_DECODE ? 0 : 1; ph <= (mode == MOE_FWD_DECODE ? 0 : 2); ++ph) {
+      a.phase = ph;
+      if (rg4)
+        dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 4><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      else if (rb2)
+        dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      else if (rg2 && T == 1 && occ.fu_rg2h >= occ.fu[1][0])   // (device-scope h loads: T = 1 41.8 -> 40.2 us,
+                                                               // T = 4 119.6 -> 121.3 us)
+        dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2, true><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      else if (rg2)
+        dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      else if (fp8)
+        dec_fused_kernel<true, kDecD_FP8, kDecW, 16><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      else if (dr8)
+        dec_fused_kernel<false, kDecD_RES, kDecW, 8><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      else
+        dec_fused_kernel<false, kDecD_BF16, kDecW, 16><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      MOE_LAUNCHED();
+    }
     return MOE_OK;
   }
   if (mode != MOE_FWD_PREFILL) MOE_FAIL(MOE_ERR_ARG, "bad mode %u", mode);
@@ -1955,6 +1965,14 @@ extern "C" moe_status moe_expert_forward_merge(const moe_slots* slots, const uin
   clear_error();
   if (T > 0 && (!y_host || !y_out)) MOE_FAIL(MOE_ERR_ARG, "y_host and y_out are required");
   return run_forward(slots, x, pick_slot, w, T, k, y_gpu, y_host, y_out, y_out_bf16, ws, ws_bytes, mode, stream);
+}
+
+extern "C" moe_status moe_decode_grid_override(int32_t n_workgroups) {
+  clear_error();
+  if (n_workgroups < 0 || n_workgroups > kDecGridMax)
+    MOE_FAIL(MOE_ERR_ARG, "n_workgroups %d outside [0, %d]", n_workgroups, kDecGridMax);
+  g_dec_grid_override.store(n_workgroups, std::memory_order_relaxed);
+  return MOE_OK;
 }
 
 // ================================================================ allocation-free decode
