@@ -101,13 +101,15 @@ def pmc_summary(fetch_dir, write_dir, bench_json):
         vals = {}
         rows = sorted((r for r in csv.DictReader(open(files[0])) if r["Counter_Name"] == counter),
                       key=lambda r: int(r["Dispatch_Id"]))
+        seq = []   # (kernel, value) in dispatch order
         for r in rows:
             vals.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+            seq.append((r["Kernel_Name"], float(r["Counter_Value"])))
         # the calibration copy (a device-to-device copy of COPY_BYTES): the
         # copy kernel with the largest count
         copy = max((k for k in vals if "copybuffer" in k.lower()), key=lambda k: max(vals[k]))
         factor = max(vals[copy]) * 1024.0 / COPY_BYTES      # counter KiB per true KiB
-        per[counter] = dict(vals=vals, factor=factor, copy_kernel=copy)
+        per[counter] = dict(vals=vals, seq=seq, factor=factor, copy_kernel=copy)
     # merge into the committed summary when it describes the same sources
     try:
         with open(TRAFFIC_JSON) as fh:
@@ -124,14 +126,16 @@ def pmc_summary(fetch_dir, write_dir, bench_json):
             "counter_kib_per_true_kib": round(per[c]["factor"], 4)} for c in per}
 
     def launch_bytes(prefixes, select=None):
+        # the dispatches of each prefix in dispatch order, across every kernel
+        # it matches (the FP8 decode forms of T = 1, 4, 16 are different kernels)
         tot, parts = 0.0, {}
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
-            v = per[c]["vals"]
             for pre in prefixes:
-                ks = [k for k in v if k.startswith(pre)]
-                if not ks:
+                xs = [x for k, x in per[c]["seq"] if k.startswith(pre)]
+                if not xs:
                     continue
-                xs = [x for k in ks for x in (select(v[k]) if select else v[k])]
+                if select:
+                    xs = select(xs)
                 b = sum(xs) / len(xs) * 1024.0 / per[c]["factor"]   # bytes per dispatch
                 parts["%s %s" % (pre.replace("void ", "").replace("moe::", ""), c)] = round(b)
                 tot += b
