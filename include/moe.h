@@ -374,11 +374,11 @@ moe_status moe_expert_forward_merge(const moe_slots* slots, const uint16_t* x, c
  * moe_expert_forward and _merge): n_workgroups > 0 fixes the grid of every
  * later decode launch in this process, 0 restores the automatic grid (as
  * many workgroups as the compute units hold at once).  For tests and
- * tuning: in MOE_FWD_DECODE_SPLIT mode every grid completes, with the same
- * bits for every grid that keeps the kernel form (BF16 small batches take
- * 8-row down tasks only on grids of at least H/8 workgroups; smaller grids
- * sum in another order); MOE_FWD_DECODE with more workgroups than the GPU
- * holds at once times out (see moe_expert_forward).  Host only, takes effect at the next launch;
+ * tuning: in MOE_FWD_DECODE_SPLIT mode every grid completes, with the bits
+ * of MOE_FWD_DECODE on the same grid (the grid decides which workgroup sums
+ * which terms, so other grids may round differently, within the layer
+ * tolerance); MOE_FWD_DECODE with more workgroups than the GPU holds at once
+ * times out (see moe_expert_forward).  Host only, takes effect at the next launch;
  * MOE_ERR_ARG outside [0, 4096].
  */
 moe_status moe_decode_grid_override(int32_t n_workgroups);
