@@ -73,3 +73,14 @@ def test_status_codes_match_header():
     src = open(HEADER).read()
     for name, val in re.findall(r"(MOE_(?:OK|ERR_\w+))\s*=\s*(-?\d+)", src):
         assert b.STATUS[int(val)] == name
+
+
+def test_decode_grid_override_arguments():
+    """The decode launch-shape override is host state: checked without a GPU."""
+    import routed_expert_cache_amd.binding as b
+    for bad in (-1, 4097):
+        with pytest.raises(b.MoeError) as ei:
+            b.decode_grid_override(bad)
+        assert ei.value.status == -1                     # MOE_ERR_ARG
+    b.decode_grid_override(4096)
+    b.decode_grid_override(0)
