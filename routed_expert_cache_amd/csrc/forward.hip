@@ -250,7 +250,7 @@ struct DecWsDev {
 //  16: one brick row per task; each wave streams its (group, K step) pairs
 //      through a register ring D steps deep, weights before the start signal
 //      and h after it.
-//  32: (FP8, T >= 2) the same with two brick rows per task, each h load
+//  32: (FP8) the same with two brick rows per task, each h load
 //      serving both.
 //   8: (BF16) half a brick row per task (the task's slice of a brick is one
 //      128-byte line per K chunk), for calls whose down work is small: every
@@ -1682,6 +1682,7 @@ struct DecOcc {
   int fu_rb2 = 0;                    // ... and per down task
   int fu_rg4 = 0;                    // FP8, four brick rows per gate/up task, two per down task
   int fu_rg2h = 0;                   // FP8 two-row gate/up tasks, device-scope h loads
+  int fu_rb2h = 0;                   // ... and two-row down tasks
 };
 // Register-ring depths in 2-brick steps.  Deeper rings put more bytes in
 // flight per wave, but past a few KB per wave the launch as a whole streams
@@ -1717,6 +1718,8 @@ static moe_status dec_occupancy(DecOcc* out) {
                                                          kDecW * 64, 0));
     MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
         &o.fu_rg2h, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2, true>, kDecW * 64, 0));
+    MOE_HIP(hipOccupancyMaxActiveBlocksPerMultiprocessor(
+        &o.fu_rb2h, dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2, true>, kDecW * 64, 0));
     o.fu[1][1] = 0;   // the register-resident form is BF16 only (FP8 steps need more registers than it has)
     for (int i = 0; i < 2; ++i)
       if (o.fu[i][0] < 1) o.fu[i][0] = 1;
@@ -1870,8 +1873,14 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
       a.phase = ph;
       if (rg4)
         dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 4><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      else if (rb2 && T <= 4 && occ.fu_rb2h >= occ.fu[1][0])   // (device-scope h loads: T = 2 63.7 -> 62.6 us,
+                                                                // T = 4 98.6 -> 98.1 us, 8 and 13 groups)
+        dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2, true><<<g1, kDecW * 64, 0, stream>>>(a, c);
       else if (rb2)
         dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2><<<g1, kDecW * 64, 0, stream>>>(a, c);
+      else if (rg2 && T == 1 && occ.fu_rb2h >= occ.fu[1][0])   // T = 1: two-row down tasks too, device-scope h
+                                                               // loads (4 groups: 36.9 -> 35.5 us; 3: 31.7 -> 30.8)
+        dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 2, true><<<g1, kDecW * 64, 0, stream>>>(a, c);
       else if (rg2 && T == 1 && occ.fu_rg2h >= occ.fu[1][0])   // (device-scope h loads: T = 1 41.8 -> 40.2 us,
                                                                // T = 4 119.6 -> 121.3 us)
         dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 16, 2, true><<<g1, kDecW * 64, 0, stream>>>(a, c);
