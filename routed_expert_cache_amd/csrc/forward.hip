@@ -1691,7 +1691,7 @@ struct DecOcc {
 // 20.5 us; FP8 two-row tasks 1 step 41.9 / 120.1 / 338.5 us at T = 1 / 4 /
 // 16 against 2 steps 48.4 / 134.9 / 352.0 us).
 constexpr int kDecD_BF16 = 2;      // 16-row down tasks
-constexpr int kDecD_RES = 3;       // register-resident down weights (DR = 8)
+constexpr int kDecD_RES = 2;       // register-resident down weights (DR = 8; 3: 17.9 -> 17.5 us at 7 groups back to back)
 constexpr int kDecD_FP8 = 3;       // FP8, one brick row per gate/up task (steps carry twice the x operand)
 constexpr int kDecD_FP8_RG2 = 1;   // FP8, two brick rows per gate/up task
 constexpr int kDecW = 8;   // waves per workgroup
