@@ -963,9 +963,10 @@ __global__ __launch_bounds__(256) void pf_scatter_kernel(PfArgs a) {
 // 1 KB wave load each), D steps ahead of the MFMAs in a register ring.  Only
 // the token operand goes through LDS: the token bricks of SPS steps form a
 // stage, loaded from memory straight into LDS (buffer loads with an LDS
-// destination; lane (r, j) of a token brick fetches 16 bytes of its pair's
-// row, so the LDS image is the B operand), NSTG stages deep, one barrier per
-// stage.  A wave reads the token bricks of step st+1 from LDS while the
+// destination; FP8: lane (r, j) of a token brick fetches 16 bytes of its
+// pair's row, so the LDS image is the B operand; BF16: a stage's loads
+// fetch whole 128-byte lines of the rows into a swizzled image, described
+// at pf_line_row), NSTG stages deep, one barrier per stage.  A wave reads the token bricks of step st+1 from LDS while the
 // MFMAs of step st run (each brick's register is re-read right after the
 // MFMAs that take it are issued).  FP8: a weight brick is 64 K of E4M3
 // codes, expanded exactly to two BF16 operands in registers; the partial
@@ -985,6 +986,23 @@ __device__ __forceinline__ void bload_lds(__amdgpu_buffer_rsrc_t r, void* lds, u
 constexpr int kPfWaves = 8;
 constexpr int kPfWaveRows = kPfRows / kPfWaves;   // 64 bank rows (four brick rows) per wave
 
+// BF16 token stages in whole lines.  The two steps of a stage take 64 K of
+// each pair row: one 128-byte line.  A token brick with lane (r, j) fetching
+// 16 bytes per step would ask for 16 half lines per load; instead load s of
+// a stage brings rows 8 s .. 8 s + 7 of the wave's token group, eight lanes
+// a row and every line whole.  Such a load writes its 1 KB of LDS in lane
+// order, so the lane -> (row, chunk) map sets the image, and the 16-byte
+// chunks are XOR-swizzled by the row so that the operand reads of one step
+// (lane (r, j) takes chunk 4 s + j of row r) fall on distinct banks in every
+// 8 and every 16 lanes: chunk c of row 8 u + q sits in 16-byte slot
+// 64 u + 8 (q ^ u) + (c ^ q) of the group's 2 KB.
+__device__ __forceinline__ int pf_line_row(int lane, int u) { return 8 * u + ((lane >> 3) ^ u); }
+__device__ __forceinline__ int pf_line_chunk(int lane, int u) { return (lane & 7) ^ ((lane >> 3) ^ u); }
+__device__ __forceinline__ uint32_t pf_line_slot(int lane, int s) {   // the operand slot of lane (r, j) at step s
+  const int r = lane & 15, j = lane >> 4, u = r >> 3, q = r & 7;
+  return (uint32_t)(64 * u + 8 * (q ^ u) + ((4 * s + j) ^ q));
+}
+
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
@@ -1000,6 +1018,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   constexpr int D = FP8 ? 2 : 4;             // weight register ring, in steps (FP8 also holds the block sums)
   constexpr int SB = SPS * TBS;              // token bricks per stage
   static_assert(TBS == kPfWaves, "each wave loads one token brick per step: SPS per stage");
+  static_assert(SPS == 2 && (FP8 || SPS * KS * 2 == 128), "a BF16 stage spans one 128-byte line of each row");
   static_assert(D % SPS == 0, "a loop body of D steps holds whole stages");
   __shared__ __attribute__((aligned(1024))) char Ls[NSTG][SB * 1024];
 
@@ -1040,16 +1059,24 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   // the pair itself).  FP8 halves follow the expansion of a weight brick:
   // lane j of the low operand holds K 16 j .. 16 j + 7 of the step, of the
   // high one 16 j + 8 .. 16 j + 15.
-  const int prow = 16 * (FP8 ? wv >> 1 : wv) + r;
-  const int srow = prow < mrows ? (GATEUP ? a.sorted_pair[seg + m0 + prow] / a.k : seg + m0 + prow) : -1;
-  const uint32_t tkoff = FP8 ? (uint32_t)(16 * j + 8 * (wv & 1)) : (uint32_t)(8 * j);
+  // BF16 stages hold whole lines instead (pf_line_row and the notes above
+  // it): load s of a stage brings rows 8 s .. 8 s + 7 of group wv.
+  int srow[SPS];
+  uint32_t tkoff[SPS];
+#pragma unroll
+  for (int s = 0; s < SPS; ++s) {
+    const int prow = 16 * (FP8 ? wv >> 1 : wv) + (FP8 ? r : pf_line_row(lane, s));
+    srow[s] = prow < mrows ? (GATEUP ? a.sorted_pair[seg + m0 + prow] / a.k : seg + m0 + prow) : -1;
+    tkoff[s] = FP8 ? (uint32_t)(16 * j + 8 * (wv & 1)) : (uint32_t)(8 * pf_line_chunk(lane, s));
+  }
   auto issue_tok = [&](int sg) {   // stage sg -> LDS buffer sg % NSTG
     char* stage = Ls[sg % NSTG];
 #pragma unroll
     for (int s = 0; s < SPS; ++s) {
-      const int st = sg * SPS + s;
-      bload_lds<0>(trs, stage + (s * TBS + wv) * 1024,
-                   oob_sel(srow >= 0 && st < nkt, (uint32_t)(((size_t)(srow < 0 ? 0 : srow) * K + st * KS + tkoff) * 2)));
+      const int st = FP8 ? sg * SPS + s : sg * SPS;   // BF16: the stage's first step (the line spans both)
+      bload_lds<0>(trs, stage + (FP8 ? s * TBS + wv : 2 * wv + s) * 1024,
+                   oob_sel(srow[s] >= 0 && st < nkt,
+                           (uint32_t)(((size_t)(srow[s] < 0 ? 0 : srow[s]) * K + st * KS + tkoff[s]) * 2)));
     }
   };
   u32x4 wr[D][WB];
@@ -1086,9 +1113,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   // asm wait that follows ties the registers.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)&Ls[0][0];
   u32x4 tk[TBS];
+  const uint32_t rofs[2] = {FP8 ? (uint32_t)lane * 16u : pf_line_slot(lane, 0) * 16u,
+                            FP8 ? (uint32_t)lane * 16u : pf_line_slot(lane, 1) * 16u};
   auto rd_tok = [&](int st, int q) {
-    const uint32_t addr =
-        lds0 + (uint32_t)(((st / SPS) % NSTG) * SB * 1024 + ((st % SPS) * TBS + q) * 1024) + (uint32_t)lane * 16u;
+    const uint32_t addr = lds0 + (uint32_t)(((st / SPS) % NSTG) * SB * 1024 +
+                                            (FP8 ? ((st % SPS) * TBS + q) * 1024 : q * 2048)) + rofs[st % SPS];
     asm volatile("ds_read_b128 %0, %1" : "=v"(tk[q]) : "v"(addr));
   };
   auto wait_tok = [&]() {   // every LDS read and scalar load issued so far has returned
@@ -1276,6 +1305,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_down_kernel(PfArgs a) {
   constexpr int SB = SPS * TBS;              // token bricks per stage
   constexpr int MT = PfMeta<FP8>::kTiles;    // tiles per workgroup at most
   static_assert(TBS == kPfWaves, "each wave loads one token brick per step: SPS per stage");
+  static_assert(SPS == 2 && (FP8 || SPS * KS * 2 == 128), "a BF16 stage spans one 128-byte line of each row");
   static_assert(D % SPS == 0, "a loop body of D steps holds whole stages");
   __shared__ __attribute__((aligned(1024))) char Ls[NSTG][SB * 1024];
   __shared__ int4 s_desc[MT];                // per tile: slot, first sorted pair, pair rows, bank-row block
@@ -1334,23 +1364,35 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_down_kernel(PfArgs a) {
   // Token stream: this wave's token brick of every step (brick q = wv; BF16:
   // token group wv, FP8: group wv / 2, K half wv & 1); lane (r, j) fetches 16
   // bytes of the h row of pair row 16 g + r.
-  const int prow = 16 * (FP8 ? wv >> 1 : wv) + r;
-  const uint32_t tkoff = FP8 ? (uint32_t)(16 * j + 8 * (wv & 1)) : (uint32_t)(8 * j);
-  int t_i = -1, t_k = 0, t_st = 0, srow = -1;   // tile, its K step and the step overall of the next token step
+  // BF16 stages hold whole lines (pf_line_row): load s of a stage brings
+  // rows 8 s .. 8 s + 7 of group wv, for both steps of the stage.
+  int prow[SPS];
+  uint32_t tkoff[SPS];
+#pragma unroll
+  for (int s = 0; s < SPS; ++s) {
+    prow[s] = 16 * (FP8 ? wv >> 1 : wv) + (FP8 ? r : pf_line_row(lane, s));
+    tkoff[s] = FP8 ? (uint32_t)(16 * j + 8 * (wv & 1)) : (uint32_t)(8 * pf_line_chunk(lane, s));
+  }
+  int t_i = -1, t_k = 0, t_st = 0;   // tile, its K step and the step overall of the next token step
+  int srow[SPS] = {-1, -1};
   auto t_enter = [&](int i) __attribute__((always_inline)) {
     t_i = i;
     t_k = 0;
     const int4 d4 = desc(i);
-    srow = prow < d4.z ? d4.y + prow : -1;
+#pragma unroll
+    for (int s = 0; s < SPS; ++s) srow[s] = prow[s] < d4.z ? d4.y + prow[s] : -1;
   };
   auto issue_tok = [&](int sg) __attribute__((always_inline)) {   // stage sg -> LDS buffer sg % NSTG
     char* stage = Ls[sg % NSTG];
 #pragma unroll
     for (int s = 0; s < SPS; ++s) {
+      // a stage never spans two tiles (nkp is a multiple of SPS), so the
+      // tile changes only at s = 0
       if (t_k == nkp && t_i + 1 < nt_w) t_enter(t_i + 1);   // past the last tile: loads nothing
-      const bool live = t_st < nt_w * nkp && t_k < nkt && srow >= 0;
-      bload_lds<0>(trs, stage + (s * TBS + wv) * 1024,
-                   oob_sel(live, (uint32_t)(((size_t)(srow < 0 ? 0 : srow) * K + t_k * KS + tkoff) * 2)));
+      const int kst = FP8 ? t_k : t_k - s;                   // BF16: the stage's first step (the line spans both)
+      const bool live = t_st < nt_w * nkp && kst < nkt && srow[s] >= 0;
+      bload_lds<0>(trs, stage + (FP8 ? s * TBS + wv : 2 * wv + s) * 1024,
+                   oob_sel(live, (uint32_t)(((size_t)(srow[s] < 0 ? 0 : srow[s]) * K + kst * KS + tkoff[s]) * 2)));
       ++t_k;
       ++t_st;
     }
@@ -1410,9 +1452,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_down_kernel(PfArgs a) {
   // asm wait that follows ties the registers.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)&Ls[0][0];
   u32x4 tk[TBS];
+  const uint32_t rofs[2] = {FP8 ? (uint32_t)lane * 16u : pf_line_slot(lane, 0) * 16u,
+                            FP8 ? (uint32_t)lane * 16u : pf_line_slot(lane, 1) * 16u};
   auto rd_tok = [&](int st, int q) __attribute__((always_inline)) {
-    const uint32_t addr =
-        lds0 + (uint32_t)(((st / SPS) % NSTG) * SB * 1024 + ((st % SPS) * TBS + q) * 1024) + (uint32_t)lane * 16u;
+    const uint32_t addr = lds0 + (uint32_t)(((st / SPS) % NSTG) * SB * 1024 +
+                                            (FP8 ? ((st % SPS) * TBS + q) * 1024 : q * 2048)) + rofs[st % SPS];
     asm volatile("ds_read_b128 %0, %1" : "=v"(tk[q]) : "v"(addr));
   };
   auto wait_tok = [&]() __attribute__((always_inline)) {   // every LDS read and scalar load issued so far has returned
