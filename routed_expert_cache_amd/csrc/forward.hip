@@ -1235,16 +1235,18 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
       const int row = 16 * tg + r;
 #pragma unroll
       for (int i = 0; i < WB; ++i) {
-        f32x4 u;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) u[e] = __shfl_xor(acc[i][tg][e], 32, 64);
-        if (j < 2 && row < mrows) {
-          const int f = 8 * (t0 + i) + 4 * j;   // first of the lane's 4 features
-          const uint32_t h01 = f32_to_bf16_rne(silu_f32(acc[i][tg][0]) * u[0]) |
-                               ((uint32_t)f32_to_bf16_rne(silu_f32(acc[i][tg][1]) * u[1]) << 16);
-          const uint32_t h23 = f32_to_bf16_rne(silu_f32(acc[i][tg][2]) * u[2]) |
-                               ((uint32_t)f32_to_bf16_rne(silu_f32(acc[i][tg][3]) * u[3]) << 16);
-          *reinterpret_cast<u32x2*>(a.h + (size_t)(seg + m0 + row) * a.I + f) = u32x2{h01, h23};
+        // lanes j and j ^ 2 (32 apart) hold the gate and the up rows of the
+        // same 4 features; each computes two of them: j < 2 the first two
+        // (sending its gate of the last two), j >= 2 the last two (sending
+        // its up of the first two), so every lane evaluates 2 SiLUs, not 4
+        const f32x4 v = acc[i][tg];
+        const bool lo = j < 2;
+        const float r0 = __shfl_xor(lo ? v[2] : v[0], 32, 64), r1 = __shfl_xor(lo ? v[3] : v[1], 32, 64);
+        const float g0 = lo ? v[0] : r0, g1 = lo ? v[1] : r1, u0 = lo ? r0 : v[2], u1 = lo ? r1 : v[3];
+        if (row < mrows) {
+          const int f = 8 * (t0 + i) + 4 * (j & 1) + (lo ? 0 : 2);   // the lane's first feature
+          const uint32_t h01 = f32_to_bf16_rne(silu_f32(g0) * u0) | ((uint32_t)f32_to_bf16_rne(silu_f32(g1) * u1) << 16);
+          *reinterpret_cast<uint32_t*>(a.h + (size_t)(seg + m0 + row) * a.I + f) = h01;
         }
       }
     }
