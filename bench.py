@@ -152,7 +152,17 @@ def pmc_summary(fetch_dir, write_dir, bench_json):
                     "bytes": round(tot), "parts": parts,
                     "algorithmic_bytes": byT["experts_per_forward"] * byT["bytes_per_expert"]}
             continue
-        tot, parts = launch_bytes(PMC_LAUNCHES[key])
+        select = None
+        if key == "decode_bf16_forward":
+            # the forward-only burst (n launches replaying the timed calls,
+            # whose algorithmic bytes are known), which the split-form burst
+            # (2 n launches, the last of this kernel in the run) follows
+            n = run["roofline"]["launches"]
+
+            def select(xs, n=n):
+                assert len(xs) >= 3 * n, "fewer decode dispatches than the two bursts"
+                return xs[len(xs) - 3 * n:len(xs) - 2 * n]
+        tot, parts = launch_bytes(PMC_LAUNCHES[key], select)
         if parts:
             out["launches"][key] = {"bytes": round(tot), "parts": parts}
     if "decode_bf16_forward" in out["launches"] and not fp8_run:
