@@ -384,6 +384,24 @@ moe_status moe_expert_forward_merge(const moe_slots* slots, const uint16_t* x, c
 moe_status moe_decode_grid_override(int32_t n_workgroups);
 
 /*
+ * Exercises the bounded wait of MOE_FWD_DECODE (for tests of its error path,
+ * which otherwise needs a GPU shared with other work).  Same arguments as
+ * moe_expert_forward in MOE_FWD_DECODE mode (T <= 16, the same workspace),
+ * except that it launches only the down phase, with the waits of the
+ * one-launch form for the start signal that the gate/up phase would raise;
+ * nothing in this launch raises it, so each waiting workgroup gives up after
+ * `polls` polls (in [1, 4194304]; the one-launch form allows 4194304, about
+ * 1-2 s), sets the first 32-bit word of ws non-zero and finishes its work on
+ * whatever h the workspace holds.  Every workgroup exits; y is written but
+ * not valid, and ws must be zero-filled again before its next use, as after a
+ * time-out of moe_expert_forward.  MOE_ERR_ARG for polls outside the range,
+ * otherwise the errors of moe_expert_forward.  Capturable.
+ */
+moe_status moe_decode_wait_test(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,
+                                const float* w, int32_t T, int32_t k, float* y, void* ws, size_t ws_bytes,
+                                uint32_t polls, hipStream_t stream);
+
+/*
  * For callers that cannot allocate device memory: code under hipGraph
  * capture, tight serving loops, harnesses that forbid hipMalloc.  The same
  * as moe_expert_forward_merge in MOE_FWD_DECODE mode (the same kernels, the

@@ -33,7 +33,7 @@ EXPORTS = [
     "moe_last_error", "moe_route_topk", "moe_cache_workspace_bytes", "moe_cache_create",
     "moe_cache_seed", "moe_cache_step", "moe_cache_route_step", "moe_cache_fill", "moe_cache_read_state", "moe_cache_error",
     "moe_cache_destroy", "moe_forward_workspace_bytes", "moe_expert_forward", "moe_expert_forward_merge",
-    "moe_expert_forward_merge_static", "moe_decode_grid_override",
+    "moe_expert_forward_merge_static", "moe_decode_grid_override", "moe_decode_wait_test",
     "moe_merge_partial",
     "moe_prefill_create", "moe_prefill_prefetch", "moe_prefill_acquire", "moe_prefill_release",
     "moe_prefill_destroy", "moe_prefill_create_ring", "moe_prefill_finish", "moe_cache_prefill_load",
@@ -100,6 +100,7 @@ _sig = {
                                         _u32, _vp]),
     "moe_expert_forward_merge_static": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _vp, _vp, _vp]),
     "moe_decode_grid_override": (_i32, [_i32]),
+    "moe_decode_wait_test": (_i32, [_P(Slots), _vp, _vp, _vp, _i32, _i32, _vp, _vp, _sz, _u32, _vp]),
     "moe_merge_partial": (_i32, [_vp, _vp, _i32, _i32, _vp, _vp, _vp]),
     "moe_stream_read": (_i32, [_vp, _sz, _vp, _vp]),
     "moe_stream_read_cfg": (_i32, [_vp, _sz, _vp, _i32, _i32, _vp]),
@@ -402,6 +403,18 @@ def decode_grid_override(n_workgroups):
     """Fix the decode forward's grid to n_workgroups for later launches in this
     process (0: automatic)."""
     _check(_lib.moe_decode_grid_override(int(n_workgroups)), "moe_decode_grid_override")
+
+
+def decode_wait_test(slots_c, x, pick_slot, w, ws, polls, y=None, stream=None):
+    """The down phase of the decode forward alone, with the one-launch form's
+    bounded waits and at most `polls` polls: every waiting workgroup gives up
+    and sets ws's first word (y is then not valid)."""
+    T, k = pick_slot.shape
+    if y is None:
+        y = torch.empty((T, slots_c.H), dtype=torch.float32, device=x.device)
+    _check(_lib.moe_decode_wait_test(ctypes.byref(slots_c), _ptr(x), _ptr(pick_slot), _ptr(w), T, k, _ptr(y),
+                                     _ptr(ws), ws.numel(), int(polls), _stream(stream)), "moe_decode_wait_test")
+    return y
 
 
 def merge_partial(y_gpu, y_host, y_out=None, y_out_bf16=None, stream=None):

@@ -115,7 +115,9 @@ struct DecArgs {
   uint16_t* y_bf16;          // [T][H] BF16 of y_out (merge), or NULL
   uint16_t* h;               // workspace [G_max][16][I] BF16
   int G_max;
-  int phase;                 // 0: both projections in one launch; a split pair: 1 gate/up only, then 2 down only
+  int phase;                 // 0: both projections in one launch; a split pair: 1 gate/up only, then 2 down only;
+                             // 3: down only, with the waits of 0 (nothing raises their signal: a test of the bound)
+  uint32_t poll_limit;       // polls of a bounded wait before it gives up
 };
 
 __device__ __forceinline__ u32x4 bload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
@@ -301,7 +303,8 @@ void dec_fused_kernel(DecArgs a, DecWsDev c) {
   const int RAT = RA / RG;                       // gate/up tasks per group (the host checks RG | RA)
   // (a split pair: the first launch takes only the gate/up tasks, the
   // second only the down tasks, which then find h complete and wait for nothing)
-  const int nA = a.phase == 2 ? 0 : G * RAT, nB = a.phase == 1 ? 0 : H / DR;
+  const int nA = a.phase >= 2 ? 0 : G * RAT, nB = a.phase == 1 ? 0 : H / DR;
+  const bool waits = a.phase == 0 || a.phase == 3;   // the down phase waits for the start signal
   const int b0 = (int)blockIdx.x, gs = (int)gridDim.x;
   // the gate/up tasks go round-robin over the whole grid (the fewest per
   // compute unit at most); the down tasks start at workgroup nA % gs, the
@@ -515,14 +518,14 @@ void dec_fused_kernel(DecArgs a, DecWsDev c) {
     f32x4 yh = {0, 0, 0, 0};
     if (wv == 0 && a.y_host && tok && j < 2)
       yh = *reinterpret_cast<const f32x4*>(a.y_host + (size_t)r * H + 8 * t + 4 * j);
-    if (wv == 0 && rn > 0 && a.phase == 0) {   // wait for the start signal of the down phase (bounded)
+    if (wv == 0 && rn > 0 && waits) {   // wait for the start signal of the down phase (bounded)
       uint32_t* flag = c.go + (size_t)b0 * kCtrlStride;
       uint32_t it = 0;
       for (;;) {
         uint32_t v = 0;
         if (lane == 0) v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         if (__shfl(v, 0, 64)) break;
-        if (++it >= kPollLimit) {
+        if (++it >= a.poll_limit) {
           if (lane == 0) atomicOr(c.err, 1u);
           break;
         }
@@ -723,14 +726,14 @@ void dec_fused_kernel(DecArgs a, DecWsDev c) {
       for (int d = 0; d < D; ++d) issue_w(d);
       load_yh(0);
       // wait for the start signal of the down phase (bounded)
-      if (wv == 0 && a.phase == 0) {
+      if (wv == 0 && waits) {
         uint32_t* flag = c.go + (size_t)b0 * kCtrlStride;
         uint32_t it = 0;
         for (;;) {
           uint32_t v = 0;
           if (lane == 0) v = __hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           if (__shfl(v, 0, 64)) break;
-          if (++it >= kPollLimit) {
+          if (++it >= a.poll_limit) {
             if (lane == 0) atomicOr(c.err, 1u);
             break;
           }
@@ -1847,9 +1850,13 @@ extern "C" moe_status moe_pack_weights(int32_t wtype, int32_t H, int32_t I, int3
   return MOE_OK;
 }
 
+// run_forward's mode for moe_decode_wait_test (not a public mode)
+constexpr uint32_t kFwdDecodeWaitTest = 0x80000000u;
+
 static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot, const float* w,
                               int32_t T, int32_t k, float* y, const float* y_host, float* y_out, uint16_t* y_bf16,
-                              void* ws, size_t ws_bytes, uint32_t mode, hipStream_t stream) {
+                              void* ws, size_t ws_bytes, uint32_t mode, hipStream_t stream,
+                              uint32_t polls = kPollLimit) {
   moe_status st = check_slots(slots);
   if (st) return st;
   if (T < 0 || k < 1) MOE_FAIL(MOE_ERR_SHAPE, "bad T=%d k=%d", T, k);
@@ -1863,7 +1870,7 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
   const int H = slots->H, I = slots->I;
   char* wsb = (char*)ws;
 
-  if (mode == MOE_FWD_DECODE || mode == MOE_FWD_DECODE_SPLIT) {
+  if (mode == MOE_FWD_DECODE || mode == MOE_FWD_DECODE_SPLIT || mode == kFwdDecodeWaitTest) {
     if (T > kDecTok || T * k > kDecPmax)
       MOE_FAIL(MOE_ERR_SHAPE, "decode mode needs T <= %d and T*k <= %d (T=%d k=%d)", kDecTok, kDecPmax, T, k);
     if (fp8 && H > 16384) MOE_FAIL(MOE_ERR_SHAPE, "FP8 decode mode needs H <= 16384 (H=%d)", H);
@@ -1880,6 +1887,7 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     a.y_host = y_host; a.y_out = y_out; a.y_bf16 = y_bf16;
     a.h = (uint16_t*)(wsb + L.h);
     a.G_max = T * k < slots->n_slots ? T * k : slots->n_slots;
+    a.poll_limit = polls;
     DecWsDev c{};
     c.err = (uint32_t*)(wsb + L.err);
     c.done = (uint32_t*)(wsb + L.done);
@@ -1915,7 +1923,9 @@ static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const i
     // against 125 / 364 us with three)
     const unsigned g1 = ov > 0 ? (unsigned)ov : grid(rg2 ? occ.fu[1][0] : dr8 ? occ.fu[0][1] : occ.fu[f][0]);
     // MOE_FWD_DECODE_SPLIT: the same kernel twice (gate/up, then down)
-    for (int ph = mode == MOE_FWD_DECODE ? 0 : 1; ph <= (mode == MOE_FWD_DECODE ? 0 : 2); ++ph) {
+    const int ph0 = mode == MOE_FWD_DECODE ? 0 : mode == kFwdDecodeWaitTest ? 3 : 1;
+    const int ph1 = mode == MOE_FWD_DECODE_SPLIT ? 2 : ph0;
+    for (int ph = ph0; ph <= ph1; ++ph) {
       a.phase = ph;
       if (rg4)
         dec_fused_kernel<true, kDecD_FP8_RG2, kDecW, 32, 4><<<g1, kDecW * 64, 0, stream>>>(a, c);
@@ -2020,6 +2030,16 @@ extern "C" moe_status moe_expert_forward_merge(const moe_slots* slots, const uin
   clear_error();
   if (T > 0 && (!y_host || !y_out)) MOE_FAIL(MOE_ERR_ARG, "y_host and y_out are required");
   return run_forward(slots, x, pick_slot, w, T, k, y_gpu, y_host, y_out, y_out_bf16, ws, ws_bytes, mode, stream);
+}
+
+extern "C" moe_status moe_decode_wait_test(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot,
+                                           const float* w, int32_t T, int32_t k, float* y, void* ws, size_t ws_bytes,
+                                           uint32_t polls, hipStream_t stream) {
+  clear_error();
+  if (polls < 1 || polls > kPollLimit) MOE_FAIL(MOE_ERR_ARG, "polls %u outside [1, %u]", polls, kPollLimit);
+  if (T > 0 && !y) MOE_FAIL(MOE_ERR_ARG, "y is NULL");
+  return run_forward(slots, x, pick_slot, w, T, k, y, nullptr, nullptr, nullptr, ws, ws_bytes, kFwdDecodeWaitTest,
+                     stream, polls);
 }
 
 extern "C" moe_status moe_decode_grid_override(int32_t n_workgroups) {

@@ -75,6 +75,13 @@ def test_status_codes_match_header():
         assert b.STATUS[int(val)] == name
 
 
+def test_decode_wait_test_arguments():
+    """The wait test's poll count is checked before anything else: no GPU needed."""
+    import routed_expert_cache_amd.binding as b
+    for bad in (0, (1 << 22) + 1):
+        assert b._lib.moe_decode_wait_test(None, None, None, None, 1, 1, None, None, 0, bad, None) == -1   # MOE_ERR_ARG
+
+
 def test_decode_grid_override_arguments():
     """The decode launch-shape override is host state: checked without a GPU."""
     import routed_expert_cache_amd.binding as b

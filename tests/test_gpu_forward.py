@@ -262,6 +262,41 @@ def test_decode_split_any_grid(wtype, T, E, k, H, I):
         b.decode_grid_override(0)
 
 
+# ---------------------------------------------------------------- decode, the bounded wait's give-up path
+@pytest.mark.parametrize("wtype,T,E,k,H,I", [
+    ("bf16", 1, 128, 8, 2048, 768),    # 8-row register-resident down tasks (their own wait)
+    ("bf16", 4, 32, 8, 1024, 256),     # 16-row down tasks
+    ("fp8", 1, 16, 8, 1024, 512),      # device-scope h loads
+    ("fp8", 4, 16, 8, 1024, 512)])     # two brick rows per down task
+def test_decode_wait_gives_up(wtype, T, E, k, H, I):
+    """The one-launch decode's down workgroups wait, bounded, for the start
+    signal of the gate/up phase.  The wait test launches the down phase alone
+    with those waits, so nothing raises the signal: every waiting workgroup
+    gives up after `polls` polls, sets the workspace's error word and exits
+    (the launch ends; no fault).  Zero-filled again, the same workspace then
+    serves a normal call, which matches the oracle and leaves the word clear."""
+    b = binding()
+    bank = (Bf16Bank if wtype == "bf16" else Fp8Bank)(320 + T, E, H, I)
+    pool = _slots_identity(b, bank, b.W_BF16 if wtype == "bf16" else b.W_FP8_B128)
+    rng = np.random.default_rng(320 + T)
+    x = gen.activations_bf16(rng, T, H)
+    ids, w = route.topk_softmax(rng.standard_normal((T, E)).astype(np.float32), k)
+    pick = np.where(rng.random(ids.shape) < 0.8, ids, -1)
+    ws = b.forward_workspace(T, k, H, I, pool.n_slots, b.FWD_DECODE)
+    args = (pool.c, dev(x), dev(pick.astype(np.int32)), dev(w.astype(np.float32)))
+    yg, _ = oracle_partials(x, ids, w, bank.expert64, pick >= 0)
+    for polls in (1, 64):
+        print("wait test, polls", polls, flush=True)
+        b.decode_wait_test(*args, ws, polls)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) != 0, polls
+        ws.zero_()
+        y = b.expert_forward(*args, b.FWD_DECODE, ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0, polls
+        check_layer(y.cpu().numpy(), yg, "decode after a wait test, polls %d" % polls)
+
+
 # ---------------------------------------------------------------- prefill
 @pytest.mark.parametrize("T,E,k,H,I", [(1, 8, 2, 256, 128), (300, 8, 2, 256, 128), (1000, 16, 4, 512, 192),
                                        (257, 8, 2, 128, 64)])   # two K steps in the down GEMM
