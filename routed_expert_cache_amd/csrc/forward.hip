@@ -966,9 +966,10 @@ __global__ __launch_bounds__(256) void pf_scatter_kernel(PfArgs a) {
 // 1 KB wave load each), D steps ahead of the MFMAs in a register ring.  Only
 // the token operand goes through LDS: the token bricks of SPS steps form a
 // stage, loaded from memory straight into LDS (buffer loads with an LDS
-// destination, which fetch whole 128-byte lines of the pair rows into a
-// swizzled image of the B operands, described at pf_line_row), NSTG stages
-// deep, one barrier per stage.  A wave reads the token bricks of step st+1 from LDS while the
+// destination; FP8: lane (r, j) of a token brick fetches 16 bytes of its
+// pair's row, so the LDS image is the B operand; BF16: a stage's loads
+// fetch whole 128-byte lines of the rows into a swizzled image, described
+// at pf_line_row), NSTG stages deep, one barrier per stage.  A wave reads the token bricks of step st+1 from LDS while the
 // MFMAs of step st run (each brick's register is re-read right after the
 // MFMAs that take it are issued).  FP8: a weight brick is 64 K of E4M3
 // codes, expanded exactly to two BF16 operands in registers; the partial
@@ -1000,13 +1001,9 @@ constexpr int kPfWaveRows = kPfRows / kPfWaves;   // 64 bank rows (four brick ro
 // 64 u + 8 (q ^ u) + (c ^ q) of the group's 2 KB.
 __device__ __forceinline__ int pf_line_row(int lane, int u) { return 8 * u + ((lane >> 3) ^ u); }
 __device__ __forceinline__ int pf_line_chunk(int lane, int u) { return (lane & 7) ^ ((lane >> 3) ^ u); }
-// FP8: one step (64 K) is the whole line, and a load brings 8 rows of one
-// step: wave w takes rows 8 (w & 1) .. of group w >> 1, both K halves, into
-// the two bricks of that group and step; brick h's operand read takes chunk
-// 2 j + h of row r.
-__device__ __forceinline__ uint32_t pf_line_slot(int lane, int c) {   // the slot of chunk c of lane (r, j)'s row
-  const int r = lane & 15, u = r >> 3, q = r & 7;
-  return (uint32_t)(64 * u + 8 * (q ^ u) + (c ^ q));
+__device__ __forceinline__ uint32_t pf_line_slot(int lane, int s) {   // the operand slot of lane (r, j) at step s
+  const int r = lane & 15, j = lane >> 4, u = r >> 3, q = r & 7;
+  return (uint32_t)(64 * u + 8 * (q ^ u) + ((4 * s + j) ^ q));
 }
 
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt <= n only
@@ -1024,7 +1021,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   constexpr int D = FP8 ? 2 : 4;             // weight register ring, in steps (FP8 also holds the block sums)
   constexpr int SB = SPS * TBS;              // token bricks per stage
   static_assert(TBS == kPfWaves, "each wave loads one token brick per step: SPS per stage");
-  static_assert(SPS == 2 && (FP8 ? KS : SPS * KS) * 2 == 128, "a BF16 stage, an FP8 step spans one line of each row");
+  static_assert(SPS == 2 && (FP8 || SPS * KS * 2 == 128), "a BF16 stage spans one 128-byte line of each row");
   static_assert(D % SPS == 0, "a loop body of D steps holds whole stages");
   __shared__ __attribute__((aligned(1024))) char Ls[NSTG][SB * 1024];
 
@@ -1059,20 +1056,21 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
                                                rows_ok ? (uint32_t)(WB * nkt * 1024) : 0u);
   const uint16_t* tsrc = GATEUP ? a.x : a.h;
   const __amdgpu_buffer_rsrc_t trs = make_rsrc(tsrc, (uint32_t)((size_t)(GATEUP ? a.T : a.P) * K * 2));
-  // Token rows: of x (gate/up: the pair's token) or of h (down: the pair
-  // itself), fetched as whole lines (pf_line_row and the notes above it).
-  // BF16: load s of a stage brings rows 8 s .. 8 s + 7 of group wv for both
-  // steps; FP8: load s brings step s of rows 8 (wv & 1) .. of group wv / 2,
-  // both K halves.  FP8 halves follow the expansion of a weight brick: lane
-  // j of the low operand holds K 16 j .. 16 j + 7 of the step, of the high
-  // one 16 j + 8 .. 16 j + 15.
+  // This wave's token brick of every step: brick q = wv (BF16: token group
+  // wv; FP8: group wv / 2, K half wv & 1).  Lane (r, j) fetches 16 bytes of
+  // pair row 16 g + r: a row of x (gate/up: the pair's token) or of h (down:
+  // the pair itself).  FP8 halves follow the expansion of a weight brick:
+  // lane j of the low operand holds K 16 j .. 16 j + 7 of the step, of the
+  // high one 16 j + 8 .. 16 j + 15.
+  // BF16 stages hold whole lines instead (pf_line_row and the notes above
+  // it): load s of a stage brings rows 8 s .. 8 s + 7 of group wv.
   int srow[SPS];
   uint32_t tkoff[SPS];
 #pragma unroll
   for (int s = 0; s < SPS; ++s) {
-    const int prow = 16 * (FP8 ? wv >> 1 : wv) + pf_line_row(lane, FP8 ? wv & 1 : s);
+    const int prow = 16 * (FP8 ? wv >> 1 : wv) + (FP8 ? r : pf_line_row(lane, s));
     srow[s] = prow < mrows ? (GATEUP ? a.sorted_pair[seg + m0 + prow] / a.k : seg + m0 + prow) : -1;
-    tkoff[s] = (uint32_t)(8 * pf_line_chunk(lane, FP8 ? wv & 1 : s));
+    tkoff[s] = FP8 ? (uint32_t)(16 * j + 8 * (wv & 1)) : (uint32_t)(8 * pf_line_chunk(lane, s));
   }
   auto issue_tok = [&](int sg) {   // stage sg -> LDS buffer sg % NSTG
     char* stage = Ls[sg % NSTG];
@@ -1118,12 +1116,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_gemm_kernel(PfArgs a) {
   // asm wait that follows ties the registers.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)&Ls[0][0];
   u32x4 tk[TBS];
-  // the lane's operand slots: BF16 by step of the stage (chunk 4 s + j), FP8 by K half (chunk 2 j + h)
-  const uint32_t rofs[2] = {pf_line_slot(lane, FP8 ? 2 * j : j) * 16u, pf_line_slot(lane, FP8 ? 2 * j + 1 : 4 + j) * 16u};
+  const uint32_t rofs[2] = {FP8 ? (uint32_t)lane * 16u : pf_line_slot(lane, 0) * 16u,
+                            FP8 ? (uint32_t)lane * 16u : pf_line_slot(lane, 1) * 16u};
   auto rd_tok = [&](int st, int q) {
     const uint32_t addr = lds0 + (uint32_t)(((st / SPS) % NSTG) * SB * 1024 +
-                                            (FP8 ? ((st % SPS) * TBS + (q & ~1)) * 1024 : q * 2048)) +
-                          rofs[FP8 ? q & 1 : st % SPS];
+                                            (FP8 ? ((st % SPS) * TBS + q) * 1024 : q * 2048)) + rofs[st % SPS];
     asm volatile("ds_read_b128 %0, %1" : "=v"(tk[q]) : "v"(addr));
   };
   auto wait_tok = [&]() {   // every LDS read and scalar load issued so far has returned
@@ -1313,7 +1310,7 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_down_kernel(PfArgs a) {
   constexpr int SB = SPS * TBS;              // token bricks per stage
   constexpr int MT = PfMeta<FP8>::kTiles;    // tiles per workgroup at most
   static_assert(TBS == kPfWaves, "each wave loads one token brick per step: SPS per stage");
-  static_assert(SPS == 2 && (FP8 ? KS : SPS * KS) * 2 == 128, "a BF16 stage, an FP8 step spans one line of each row");
+  static_assert(SPS == 2 && (FP8 || SPS * KS * 2 == 128), "a BF16 stage spans one 128-byte line of each row");
   static_assert(D % SPS == 0, "a loop body of D steps holds whole stages");
   __shared__ __attribute__((aligned(1024))) char Ls[NSTG][SB * 1024];
   __shared__ int4 s_desc[MT];                // per tile: slot, first sorted pair, pair rows, bank-row block
@@ -1369,15 +1366,17 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_down_kernel(PfArgs a) {
   // row): the token loads NSTG stages ahead, the weight loads D steps ahead,
   // and the MFMAs.  Each keeps its own tile, advanced when it crosses into
   // the next; loads of padding steps (k >= nkt) are pushed out of range.
-  // Token stream: rows of h as whole lines (pf_line_row), as in
-  // pf_gemm_kernel: BF16 load s of a stage brings rows 8 s .. of group wv
-  // for both steps, FP8 load s step s of rows 8 (wv & 1) .. of group wv / 2.
+  // Token stream: this wave's token brick of every step (brick q = wv; BF16:
+  // token group wv, FP8: group wv / 2, K half wv & 1); lane (r, j) fetches 16
+  // bytes of the h row of pair row 16 g + r.
+  // BF16 stages hold whole lines (pf_line_row): load s of a stage brings
+  // rows 8 s .. 8 s + 7 of group wv, for both steps of the stage.
   int prow[SPS];
   uint32_t tkoff[SPS];
 #pragma unroll
   for (int s = 0; s < SPS; ++s) {
-    prow[s] = 16 * (FP8 ? wv >> 1 : wv) + pf_line_row(lane, FP8 ? wv & 1 : s);
-    tkoff[s] = (uint32_t)(8 * pf_line_chunk(lane, FP8 ? wv & 1 : s));
+    prow[s] = 16 * (FP8 ? wv >> 1 : wv) + (FP8 ? r : pf_line_row(lane, s));
+    tkoff[s] = FP8 ? (uint32_t)(16 * j + 8 * (wv & 1)) : (uint32_t)(8 * pf_line_chunk(lane, s));
   }
   int t_i = -1, t_k = 0, t_st = 0;   // tile, its K step and the step overall of the next token step
   int srow[SPS] = {-1, -1};
@@ -1458,12 +1457,11 @@ __global__ __launch_bounds__(kPfWaves * 64, 1) void pf_down_kernel(PfArgs a) {
   // asm wait that follows ties the registers.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_ptr)&Ls[0][0];
   u32x4 tk[TBS];
-  // the lane's operand slots: BF16 by step of the stage (chunk 4 s + j), FP8 by K half (chunk 2 j + h)
-  const uint32_t rofs[2] = {pf_line_slot(lane, FP8 ? 2 * j : j) * 16u, pf_line_slot(lane, FP8 ? 2 * j + 1 : 4 + j) * 16u};
+  const uint32_t rofs[2] = {FP8 ? (uint32_t)lane * 16u : pf_line_slot(lane, 0) * 16u,
+                            FP8 ? (uint32_t)lane * 16u : pf_line_slot(lane, 1) * 16u};
   auto rd_tok = [&](int st, int q) __attribute__((always_inline)) {
     const uint32_t addr = lds0 + (uint32_t)(((st / SPS) % NSTG) * SB * 1024 +
-                                            (FP8 ? ((st % SPS) * TBS + (q & ~1)) * 1024 : q * 2048)) +
-                          rofs[FP8 ? q & 1 : st % SPS];
+                                            (FP8 ? ((st % SPS) * TBS + q) * 1024 : q * 2048)) + rofs[st % SPS];
     asm volatile("ds_read_b128 %0, %1" : "=v"(tk[q]) : "v"(addr));
   };
   auto wait_tok = [&]() __attribute__((always_inline)) {   // every LDS read and scalar load issued so far has returned
