@@ -969,7 +969,8 @@ __global__ __launch_bounds__(256) void pf_scatter_kernel(PfArgs a) {
 // destination; FP8: lane (r, j) of a token brick fetches 16 bytes of its
 // pair's row, so the LDS image is the B operand; BF16: a stage's loads
 // fetch whole 128-byte lines of the rows into a swizzled image, described
-// at pf_line_row), NSTG stages deep, one barrier per stage.  A wave reads the token bricks of step st+1 from LDS while the
+// at pf_line_row), NSTG stages deep, one barrier per stage.  A wave reads
+// the token bricks of step st+1 from LDS while the
 // MFMAs of step st run (each brick's register is re-read right after the
 // MFMAs that take it are issued).  FP8: a weight brick is 64 K of E4M3
 // codes, expanded exactly to two BF16 operands in registers; the partial
@@ -1850,8 +1851,12 @@ extern "C" moe_status moe_pack_weights(int32_t wtype, int32_t H, int32_t I, int3
   return MOE_OK;
 }
 
-// run_forward's mode for moe_decode_wait_test (not a public mode)
+// run_forward's mode for moe_decode_wait_test (not a public mode: the public
+// calls take only these)
 constexpr uint32_t kFwdDecodeWaitTest = 0x80000000u;
+static bool public_mode(uint32_t mode) {
+  return mode == MOE_FWD_DECODE || mode == MOE_FWD_PREFILL || mode == MOE_FWD_DECODE_SPLIT;
+}
 
 static moe_status run_forward(const moe_slots* slots, const uint16_t* x, const int32_t* pick_slot, const float* w,
                               int32_t T, int32_t k, float* y, const float* y_host, float* y_out, uint16_t* y_bf16,
@@ -2019,6 +2024,7 @@ extern "C" moe_status moe_expert_forward(const moe_slots* slots, const uint16_t*
                                          const float* w, int32_t T, int32_t k, float* y, void* ws, size_t ws_bytes,
                                          uint32_t mode, hipStream_t stream) {
   clear_error();
+  if (!public_mode(mode)) MOE_FAIL(MOE_ERR_ARG, "bad mode %u", mode);
   if (T > 0 && !y) MOE_FAIL(MOE_ERR_ARG, "y is NULL");
   return run_forward(slots, x, pick_slot, w, T, k, y, nullptr, nullptr, nullptr, ws, ws_bytes, mode, stream);
 }
@@ -2028,6 +2034,7 @@ extern "C" moe_status moe_expert_forward_merge(const moe_slots* slots, const uin
                                                const float* y_host, float* y_out, uint16_t* y_out_bf16, void* ws,
                                                size_t ws_bytes, uint32_t mode, hipStream_t stream) {
   clear_error();
+  if (!public_mode(mode)) MOE_FAIL(MOE_ERR_ARG, "bad mode %u", mode);
   if (T > 0 && (!y_host || !y_out)) MOE_FAIL(MOE_ERR_ARG, "y_host and y_out are required");
   return run_forward(slots, x, pick_slot, w, T, k, y_gpu, y_host, y_out, y_out_bf16, ws, ws_bytes, mode, stream);
 }

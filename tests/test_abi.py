@@ -75,6 +75,17 @@ def test_status_codes_match_header():
         assert b.STATUS[int(val)] == name
 
 
+def test_forward_rejects_internal_modes():
+    """The public forward calls take only the three public modes (the wait
+    test's internal launch mode among the refused): checked before anything
+    else, so no GPU is needed."""
+    import routed_expert_cache_amd.binding as b
+    for mode in (3, 0x80000000):
+        assert b._lib.moe_expert_forward(None, None, None, None, 1, 1, None, None, 0, mode, None) == -1
+        assert b._lib.moe_expert_forward_merge(None, None, None, None, 1, 1, None, None, None, None, None, 0,
+                                               mode, None) == -1
+
+
 def test_decode_wait_test_arguments():
     """The wait test's poll count is checked before anything else: no GPU needed."""
     import routed_expert_cache_amd.binding as b
